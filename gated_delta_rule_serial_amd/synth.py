@@ -1,0 +1,125 @@
+"""Seeded synthetic workloads for the gated delta-rule recurrence.
+
+This module only draws random numbers and lays them out; it holds none of the
+recurrence's or the gate prologue's arithmetic.  The test suite feeds the same
+tensors to the oracle and to the HIP library; the benchmark uses it for its
+inputs.
+
+Recipe (one ``torch.Generator`` on the CPU per workload, seed 1234 + index,
+values drawn in float32 in this order):
+  1. sequence lengths (packed workload only): ``randint(lo, hi + 1, (N,))``
+  2. q, k ~ N(0, 1), each (token, head) row divided by its L2 norm
+  3. v ~ N(0, 1)
+  4. b ~ N(0, 1)                 (beta = sigmoid(b))
+  5. a ~ N(0, 1)                 (log-decay g = -exp(A_log) softplus(a + dt_bias))
+  6. A_log ~ U(0, 1)  [h_v]
+  7. dt_bias ~ U(-1, 1)  [h_v]
+  8. initial state ~ N(0, 0.05^2)  [N, h_v, d_k, d_v]  (when the workload has one)
+Then q, k, v, a, b are cast to the I/O dtype (round to nearest even for
+bfloat16); A_log, dt_bias and the state stay float32.  The key normalisation
+is a data-preparation step: the recurrence itself never normalises.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    """Geometry of one workload."""
+    name: str
+    kind: str               # "prefill" or "decode"
+    io_dtype: torch.dtype   # torch.float32 or torch.bfloat16
+    h_qk: int
+    h_v: int
+    d_k: int
+    d_v: int
+    gate_mode: str          # "precomputed" (g, beta given) or "raw" (a, b, A_log, dt_bias)
+    num_seqs: int
+    seqlen: Optional[int]   # fixed length per sequence, or None for drawn lengths
+    len_range: Optional[tuple] = None  # (lo, hi) inclusive, drawn lengths
+    init_state: bool = False
+    seed_index: int = 0
+
+
+# The five workloads, in order.
+WORKLOADS: List[Shape] = [
+    Shape("tiny_prefill", "prefill", torch.float32, 2, 2, 16, 16, "precomputed",
+          num_seqs=1, seqlen=64, seed_index=0),
+    Shape("decode_b64", "decode", torch.bfloat16, 16, 32, 128, 128, "precomputed",
+          num_seqs=64, seqlen=1, init_state=True, seed_index=1),
+    Shape("prefill_t4096_fused_gates", "prefill", torch.bfloat16, 16, 32, 128, 128, "raw",
+          num_seqs=1, seqlen=4096, seed_index=2),
+    Shape("varlen_prefill_8seq", "prefill", torch.bfloat16, 16, 32, 128, 128, "precomputed",
+          num_seqs=8, seqlen=None, len_range=(512, 8192), init_state=True, seed_index=3),
+    Shape("wide_prefill_t32768_d256", "prefill", torch.float32, 8, 8, 256, 256, "precomputed",
+          num_seqs=1, seqlen=32768, seed_index=4),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+@dataclasses.dataclass
+class Inputs:
+    shape: Shape
+    seqlens: List[int]
+    cu_seqlens: torch.Tensor     # int32 [N+1]
+    q: torch.Tensor              # [T, h_qk, d_k] io dtype
+    k: torch.Tensor              # [T, h_qk, d_k] io dtype
+    v: torch.Tensor              # [T, h_v, d_v] io dtype
+    a: torch.Tensor              # [T, h_v] io dtype
+    b: torch.Tensor              # [T, h_v] io dtype
+    A_log: torch.Tensor          # [h_v] float32
+    dt_bias: torch.Tensor        # [h_v] float32
+    initial_state: Optional[torch.Tensor]  # [N, h_v, d_k, d_v] float32
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def _unit_rows(x: torch.Tensor) -> torch.Tensor:
+    return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+
+
+def generate(shape: Shape, *, seqlen: Optional[int] = None, num_seqs: Optional[int] = None,
+             seqlens: Optional[List[int]] = None, seed: Optional[int] = None) -> Inputs:
+    """Draw a workload's inputs on the CPU.
+
+    ``seqlen`` / ``num_seqs`` / ``seqlens`` shrink or override the geometry
+    (for parity cases the oracle finishes in seconds); ``seed`` overrides
+    1234 + index.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(1234 + shape.seed_index if seed is None else seed)
+    n = shape.num_seqs if num_seqs is None else num_seqs
+    if seqlens is not None:
+        lens = [int(x) for x in seqlens]
+        n = len(lens)
+    elif shape.seqlen is None and seqlen is None:
+        lo, hi = shape.len_range
+        lens = torch.randint(lo, hi + 1, (n,), generator=gen).tolist()
+    else:
+        lens = [shape.seqlen if seqlen is None else seqlen] * n
+    T = sum(lens)
+    cu = torch.zeros(n + 1, dtype=torch.int32)
+    if n:
+        cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+
+    f32 = torch.float32
+    q = _unit_rows(torch.randn(T, shape.h_qk, shape.d_k, generator=gen, dtype=f32))
+    k = _unit_rows(torch.randn(T, shape.h_qk, shape.d_k, generator=gen, dtype=f32))
+    v = torch.randn(T, shape.h_v, shape.d_v, generator=gen, dtype=f32)
+    b = torch.randn(T, shape.h_v, generator=gen, dtype=f32)
+    a = torch.randn(T, shape.h_v, generator=gen, dtype=f32)
+    A_log = torch.rand(shape.h_v, generator=gen, dtype=f32)
+    dt_bias = torch.rand(shape.h_v, generator=gen, dtype=f32) * 2.0 - 1.0
+    s0 = None
+    if shape.init_state:
+        s0 = torch.randn(n, shape.h_v, shape.d_k, shape.d_v, generator=gen, dtype=f32) * 0.05
+    dt = shape.io_dtype
+    return Inputs(shape, lens, cu, q.to(dt), k.to(dt), v.to(dt), a.to(dt), b.to(dt),
+                  A_log, dt_bias, s0)

@@ -1,0 +1,155 @@
+"""Reference (test-infrastructure) implementation of the gated delta-rule recurrence.
+
+TEST INFRASTRUCTURE ONLY.  The arithmetic lives in ``gdn_oracle.c`` (plain C,
+IEEE double); this module builds it with gcc and marshals numpy arrays into it
+with ctypes.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import it.  It imports nothing from the HIP library and
+the HIP library imports nothing from it.
+
+Sources are cited in ``gdn_oracle.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gdn_oracle.c")
+LIB_PATH = os.path.join(HERE, "libgdn_oracle.so")
+
+RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3}
+
+# -ffp-contract=off keeps every multiply and add a separately rounded IEEE
+# double operation, exactly as written in the C source.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-Wall", "-Wextra"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one oracle C source file into a shared library at ``out``."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *CFLAGS, "-I", HERE, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile ``gdn_oracle.c`` into ``oracle/libgdn_oracle.so``."""
+    if not force and os.path.exists(LIB_PATH) and os.path.getmtime(LIB_PATH) >= os.path.getmtime(SRC):
+        return LIB_PATH
+    return compile_source(SRC, LIB_PATH)
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor on the CPU
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a, ctype=ctypes.c_double):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+class Oracle:
+    """numpy front end over one compiled copy of the oracle."""
+
+    def __init__(self, lib_path: str = LIB_PATH):
+        lib = ctypes.CDLL(lib_path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.gdnref_sigmoid.argtypes = [f64]
+        lib.gdnref_sigmoid.restype = f64
+        lib.gdnref_softplus.argtypes = [f64]
+        lib.gdnref_softplus.restype = f64
+        lib.gdnref_gates.argtypes = [i64, i32, dp, dp, dp, dp, dp, dp]
+        lib.gdnref_gates.restype = None
+        lib.gdnref_prefill.argtypes = [i32, i32, i32, i32, i32, f64, i32, ip,
+                                       dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.gdnref_prefill.restype = ctypes.c_int
+        lib.gdnref_decode_step.argtypes = [i32, i32, i32, i32, i32, f64, i32,
+                                           dp, dp, dp, dp, dp, dp, dp]
+        lib.gdnref_decode_step.restype = ctypes.c_int
+        lib.gdnref_max_threads.argtypes = []
+        lib.gdnref_max_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = lib_path
+
+    def sigmoid(self, x: float) -> float:
+        return self.lib.gdnref_sigmoid(float(x))
+
+    def softplus(self, x: float) -> float:
+        return self.lib.gdnref_softplus(float(x))
+
+    def max_threads(self) -> int:
+        return int(self.lib.gdnref_max_threads())
+
+    def gates(self, a, b, A_log, dt_bias):
+        """(g, beta) = (-exp(A_log) softplus(a + dt_bias), sigmoid(b)), shaped like ``a``."""
+        a, b, A_log, dt_bias = _f64(a), _f64(b), _f64(A_log), _f64(dt_bias)
+        h_v = A_log.shape[-1]
+        rows = a.size // h_v
+        g = np.empty(a.shape, np.float64)
+        beta = np.empty(b.shape, np.float64)
+        self.lib.gdnref_gates(rows, h_v, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                              _ptr(g), _ptr(beta))
+        return g, beta
+
+    def prefill(self, q, k, v, g, beta, cu_seqlens, initial_state=None, *,
+                rule="gated_delta", scale=0.0, want_out=True):
+        """Serial scan over packed sequences.
+
+        q, k: [T, h_qk, d_k]; v: [T, h_v, d_v]; g, beta: [T, h_v] (None when the
+        rule does not use them); cu_seqlens: ints [N+1]; initial_state:
+        [N, h_v, d_k, d_v] or None.  Returns (out [T, h_v, d_v], final
+        [N, h_v, d_k, d_v]) as float64 arrays.
+        """
+        q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
+        s0 = _f64(initial_state)
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        T, h_qk, d_k = q.shape
+        h_v, d_v = v.shape[1], v.shape[2]
+        n = cu.size - 1
+        out = np.empty((T, h_v, d_v), np.float64) if want_out else None
+        fin = np.empty((n, h_v, d_k, d_v), np.float64)
+        rc = self.lib.gdnref_prefill(RULES[rule], h_qk, h_v, d_k, d_v, float(scale), n,
+                                     _ptr(cu, ctypes.c_int32), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(g), _ptr(beta), _ptr(s0), _ptr(out), _ptr(fin))
+        if rc != 0:
+            raise ValueError("gdnref_prefill rejected its arguments")
+        return out, fin
+
+    def decode_step(self, q, k, v, g, beta, state, *, rule="gated_delta", scale=0.0):
+        """One token per sequence; ``state`` (float64 [B, h_v, d_k, d_v]) is updated in place."""
+        q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
+        if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+                and state.flags.c_contiguous):
+            raise TypeError("state must be a C-contiguous float64 numpy array")
+        B, h_qk, d_k = q.shape
+        h_v, d_v = v.shape[1], v.shape[2]
+        out = np.empty((B, h_v, d_v), np.float64)
+        rc = self.lib.gdnref_decode_step(RULES[rule], h_qk, h_v, d_k, d_v, float(scale), B,
+                                         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(state), _ptr(out))
+        if rc != 0:
+            raise ValueError("gdnref_decode_step rejected its arguments")
+        return out
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``gdn_oracle.c`` (compiled on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _default = Oracle(LIB_PATH)
+    return _default

@@ -1,0 +1,184 @@
+/*
+ * gdn_oracle.c -- reference (test-infrastructure) implementation of the gated
+ * delta-rule recurrence.  Plain C, IEEE double, one serial scan per
+ * (sequence, value head).  See gdn_oracle.h for layouts and sources.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark; never by the library's own path.
+ */
+#include "gdn_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* [P4] `la_sigmoid`: two branches so that exp only sees arguments <= 0. */
+double gdnref_sigmoid(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  const double e = exp(x);
+  return e / (1.0 + e);
+}
+
+/* [P4] `la_softplus`: log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}). */
+double gdnref_softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+
+/* [P4] fused decay branch of `linear_attention_core` (neg_exp_A times the
+ * softplus of a + dt_bias, with neg_exp_A = -exp(A_log) folded in) and the
+ * fused beta = sigmoid(b); [P1] `linear_attention_gate_op` computes the same
+ * decay as softplus(a + bias) times a per-head scale.  No intermediate
+ * rounding: everything stays in double. */
+void gdnref_gates(int64_t rows, int32_t h_v, const double* a, const double* b,
+                  const double* A_log, const double* dt_bias, double* g,
+                  double* beta) {
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t h = 0; h < h_v; ++h) {
+      const int64_t idx = r * h_v + h;
+      if (g) g[idx] = -exp(A_log[h]) * gdnref_softplus(a[idx] + dt_bias[h]);
+      if (beta) beta[idx] = gdnref_sigmoid(b[idx]);
+    }
+  }
+}
+
+static int rule_decays(int32_t rule) {
+  return rule == GDNREF_RULE_GATED || rule == GDNREF_RULE_GATED_DELTA;
+}
+static int rule_deltas(int32_t rule) {
+  return rule == GDNREF_RULE_DELTA || rule == GDNREF_RULE_GATED_DELTA;
+}
+
+/* Scan of one (sequence, value head) unit over tokens [t0, t1).
+ * S is the d_k x d_v state, row i / column j at S[i*d_v + j]; it holds the
+ * initial state on entry and the final state on return.  r and d are
+ * d_v-long scratch vectors.
+ *
+ * The four steps and their order follow [P4] `linear_attention_core`
+ * (step 1 decay, step 2 retrieval, step 3 delta update, step 4 readout of the
+ * UPDATED state), which [P1]'s stable unroll and [P3] `gated_delta_graph`
+ * also take. */
+static void scan_unit(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                      int32_t d_v, double scale, int64_t t0, int64_t t1,
+                      int32_t h, const double* q, const double* k,
+                      const double* v, const double* g, const double* beta,
+                      double* S, double* r, double* d, double* out) {
+  const int32_t hq = h / (h_v / h_qk); /* consecutive value heads share q/k */
+  for (int64_t t = t0; t < t1; ++t) {
+    const double* kt = k + (t * h_qk + hq) * d_k;
+    const double* qt = q + (t * h_qk + hq) * d_k;
+    const double* vt = v + (t * h_v + h) * d_v;
+
+    /* decay: S <- exp(g) S */
+    if (rule_decays(rule)) {
+      const double alpha = exp(g[t * h_v + h]);
+      for (int32_t i = 0; i < d_k; ++i)
+        for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] *= alpha;
+    }
+
+    /* retrieval r = S^T k and delta d = beta (v - r); plain rules use d = v */
+    if (rule_deltas(rule)) {
+      const double bt = beta[t * h_v + h];
+      for (int32_t j = 0; j < d_v; ++j) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < d_k; ++i) acc += S[i * d_v + j] * kt[i];
+        r[j] = acc;
+      }
+      for (int32_t j = 0; j < d_v; ++j) d[j] = bt * (vt[j] - r[j]);
+    } else {
+      for (int32_t j = 0; j < d_v; ++j) d[j] = vt[j];
+    }
+
+    /* rank-1 update S <- S + k d^T */
+    for (int32_t i = 0; i < d_k; ++i)
+      for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] += kt[i] * d[j];
+
+    /* readout of the updated state: out = scale * S^T q */
+    if (out) {
+      double* ot = out + (t * h_v + h) * d_v;
+      for (int32_t j = 0; j < d_v; ++j) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < d_k; ++i) acc += S[i * d_v + j] * qt[i];
+        ot[j] = scale * acc;
+      }
+    }
+  }
+}
+
+static int valid_geometry(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                          int32_t d_v) {
+  if (rule < GDNREF_RULE_LINEAR || rule > GDNREF_RULE_GATED_DELTA) return 0;
+  if (h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0) return 0;
+  if (h_v % h_qk != 0) return 0;
+  return 1;
+}
+
+int gdnref_prefill(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                   int32_t d_v, double scale, int32_t num_seqs,
+                   const int32_t* cu_seqlens, const double* q,
+                   const double* k, const double* v, const double* g,
+                   const double* beta, const double* initial_state,
+                   double* out, double* final_state) {
+  if (!valid_geometry(rule, h_qk, h_v, d_k, d_v) || num_seqs < 0) return -1;
+  if (num_seqs > 0 && !cu_seqlens) return -1;
+  if (rule_decays(rule) && !g && num_seqs > 0) return -1;
+  if (rule_deltas(rule) && !beta && num_seqs > 0) return -1;
+  if (num_seqs > 0 && cu_seqlens[0] != 0) return -1;
+  for (int32_t n = 0; n < num_seqs; ++n)
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+
+  if (scale == 0.0) scale = 1.0 / sqrt((double)d_k);
+  const int64_t state_elems = (int64_t)d_k * d_v;
+  const int64_t units = (int64_t)num_seqs * h_v;
+  int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    const int32_t n = (int32_t)(u / h_v);
+    const int32_t h = (int32_t)(u % h_v);
+    double* S = (double*)malloc(sizeof(double) * (size_t)(state_elems + 2 * d_v));
+    if (!S) {
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    double* r = S + state_elems;
+    double* d = r + d_v;
+    if (initial_state)
+      memcpy(S, initial_state + u * state_elems, sizeof(double) * (size_t)state_elems);
+    else
+      memset(S, 0, sizeof(double) * (size_t)state_elems);
+    scan_unit(rule, h_qk, h_v, d_k, d_v, scale, cu_seqlens[n], cu_seqlens[n + 1], h,
+              q, k, v, g, beta, S, r, d, out);
+    if (final_state)
+      memcpy(final_state + u * state_elems, S, sizeof(double) * (size_t)state_elems);
+    free(S);
+  }
+  return failed ? -1 : 0;
+}
+
+int gdnref_decode_step(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                       int32_t d_v, double scale, int32_t batch,
+                       const double* q, const double* k, const double* v,
+                       const double* g, const double* beta, double* state,
+                       double* out) {
+  if (batch < 0 || !state) return -1;
+  int32_t* cu = (int32_t*)malloc(sizeof(int32_t) * (size_t)(batch + 1));
+  if (!cu) return -1;
+  for (int32_t n = 0; n <= batch; ++n) cu[n] = n;
+  /* initial and final state are the same buffer: each unit copies its slice
+   * in before scanning and back out after, so the in-place call is safe. */
+  const int rc = gdnref_prefill(rule, h_qk, h_v, d_k, d_v, scale, batch, cu, q, k,
+                                v, g, beta, state, out, state);
+  free(cu);
+  return rc;
+}
+
+int gdnref_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

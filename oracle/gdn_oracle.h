@@ -1,0 +1,107 @@
+/*
+ * gdn_oracle.h -- reference (test-infrastructure) implementation of the gated
+ * delta-rule recurrence, in plain C and IEEE double.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This code is the slow, obviously-correct CPU
+ * definition that the HIP library is checked against.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it; the
+ * library's own path never does.  It shares no source with the HIP library.
+ *
+ * Sources (web pages; cited by page and section, no line numbers):
+ *   [P1] onnxruntime-ep-mlx 0.31.1, src/ops/ssm.rs
+ *        -- `linear_attention_op` (stable unroll, T = 0 handling),
+ *           `linear_attention_gate_op`, the wide-BF16 working-state test.
+ *   [P3] nuvec-core 0.6.1, fast/imp.rs -- `gated_delta_graph`.
+ *   [P4] onnx-runtime-ep-cuda 0.1.0-dev.6, src/kernels/linear_attention.rs
+ *        -- module doc "Parallelization", `linear_attention_core` steps
+ *           1-4, the gate helpers `la_sigmoid` / `la_softplus`,
+ *           `LinearAttentionFactory::create` (default scale),
+ *           `UpdateRule` (rule family).
+ *
+ * Layouts (all row-major, contiguous, double):
+ *   q, k          [T_total, h_qk, d_k]
+ *   v, out        [T_total, h_v,  d_v]
+ *   g, beta       [T_total, h_v]          g is the log-decay, alpha = exp(g)
+ *   a, b          [T_total, h_v]          raw gate inputs
+ *   A_log,dt_bias [h_v]
+ *   states        [num_seqs, h_v, d_k, d_v]
+ * Sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 (host int32).
+ * Value head h reads query/key head h / (h_v / h_qk): each q/k head serves a
+ * run of consecutive value heads ([P4] `linear_attention_core`, inverse-GQA
+ * branch; [P3] `gated_delta_graph`).
+ *
+ * Parity status: every function here is pinned by the CPU test suite
+ * (tests/test_oracle_*.py) against brute force, closed forms, library
+ * routines or values printed on [P1]; none is "parity unpinned".
+ */
+#ifndef GDN_ORACLE_H
+#define GDN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Update-rule family of [P4] `UpdateRule` / [P1] `is_known_rule`. */
+enum {
+  GDNREF_RULE_LINEAR = 0,      /* S += k v^T                     */
+  GDNREF_RULE_GATED = 1,       /* S = exp(g) S + k v^T           */
+  GDNREF_RULE_DELTA = 2,       /* S += k (beta (v - S^T k))^T    */
+  GDNREF_RULE_GATED_DELTA = 3  /* decay, then the delta update   */
+};
+
+/* Logistic function, evaluated so that exp never sees a large positive
+ * argument ([P4] `la_sigmoid`). */
+double gdnref_sigmoid(double x);
+
+/* softplus(x) = log(1 + e^x) in the overflow-free form
+ * max(x, 0) + log1p(exp(-|x|)) ([P4] `la_softplus`). */
+double gdnref_softplus(double x);
+
+/* Gate prologue ([P4] `linear_attention_core` fused decay/beta branch;
+ * [P1] `linear_attention_gate_op`):
+ *   g[r,h]    = -exp(A_log[h]) * softplus(a[r,h] + dt_bias[h])
+ *   beta[r,h] = sigmoid(b[r,h])
+ * for r < rows, h < h_v.  Either output pointer may be NULL. */
+void gdnref_gates(int64_t rows, int32_t h_v, const double* a, const double* b,
+                  const double* A_log, const double* dt_bias, double* g,
+                  double* beta);
+
+/* Serial scan over packed sequences.  For each sequence n and value head h,
+ * starting from initial_state[n,h] (zeros if NULL), every token t runs
+ *   decay     S <- exp(g[t,h]) S                       (gated rules)
+ *   retrieval r  = S^T k_t                             (delta rules)
+ *   delta     d  = beta[t,h] (v_t - r)  (delta rules; v_t otherwise)
+ *   update    S <- S + k_t d^T
+ *   readout   out[t,h] = scale * S^T q_t   on the updated S
+ * ([P4] `linear_attention_core` steps 1-4; [P1] stable unroll; [P3]
+ * `gated_delta_graph`).  scale == 0 selects 1/sqrt(d_k) ([P4]
+ * `LinearAttentionFactory::create`).  g / beta may be NULL when the rule does
+ * not use them.  final_state may be NULL.  A sequence with no tokens leaves
+ * its final state equal to its initial state ([P1] zero-length time axis).
+ *
+ * Returns 0, or -1 on an invalid argument (nothing written). */
+int gdnref_prefill(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                   int32_t d_v, double scale, int32_t num_seqs,
+                   const int32_t* cu_seqlens, const double* q,
+                   const double* k, const double* v, const double* g,
+                   const double* beta, const double* initial_state,
+                   double* out, double* final_state);
+
+/* One token per sequence, state read and written in place:
+ * identical to gdnref_prefill with cu_seqlens = {0, 1, ..., batch}. */
+int gdnref_decode_step(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                       int32_t d_v, double scale, int32_t batch,
+                       const double* q, const double* k, const double* v,
+                       const double* g, const double* beta, double* state,
+                       double* out);
+
+/* Threads the parallel loop over independent (sequence, head) units uses. */
+int gdnref_max_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_ORACLE_H */

@@ -1,0 +1,50 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require
+the pin suite to catch every one of them: a dropped term, a flipped sign, a
+wrong operand or index, a wrong default."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+# (label, text in gdn_oracle.c, replacement)
+MUTANTS = [
+    ("dropped decay", "S[i * d_v + j] *= alpha;", ";"),
+    ("decay applied as g, not exp(g)", "const double alpha = exp(g[t * h_v + h]);",
+     "const double alpha = g[t * h_v + h];"),
+    ("delta sign flipped", "d[j] = bt * (vt[j] - r[j]);", "d[j] = bt * (r[j] - vt[j]);"),
+    ("beta ignored", "d[j] = bt * (vt[j] - r[j]);", "d[j] = (vt[j] - r[j]);"),
+    ("retrieval against the query", "acc += S[i * d_v + j] * kt[i];\n        r[j] = acc;",
+     "acc += S[i * d_v + j] * qt[i];\n        r[j] = acc;"),
+    ("update with the query", "S[i * d_v + j] += kt[i] * d[j];", "S[i * d_v + j] += qt[i] * d[j];"),
+    ("scale dropped", "ot[j] = scale * acc;", "ot[j] = acc;"),
+    ("interleaved head map", "const int32_t hq = h / (h_v / h_qk);", "const int32_t hq = h % h_qk;"),
+    ("initial state ignored",
+     "memcpy(S, initial_state + u * state_elems, sizeof(double) * (size_t)state_elems);",
+     "memset(S, 0, sizeof(double) * (size_t)state_elems);"),
+    ("default scale from d_v", "scale = 1.0 / sqrt((double)d_k);", "scale = 1.0 / sqrt((double)d_v);"),
+    ("softplus tail sign", "log1p(exp(-fabs(x)))", "log1p(exp(fabs(x)))"),
+    ("sigmoid negative branch", "return e / (1.0 + e);", "return 1.0 / (1.0 + e);"),
+    ("decay sign", "g[idx] = -exp(A_log[h])", "g[idx] = exp(A_log[h])"),
+    ("dt_bias dropped", "gdnref_softplus(a[idx] + dt_bias[h])", "gdnref_softplus(a[idx])"),
+]
+
+
+@pytest.mark.parametrize("label,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, label, old, new):
+    with open(oracle.SRC) as fh:
+        src = fh.read()
+    assert src.count(old) == 1, f"mutation anchor for '{label}' not unique in gdn_oracle.c"
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as fh:
+        fh.write(src.replace(old, new))
+    lib = oracle.compile_source(path, os.path.join(tmp_path, "libmutant.so"))
+    m = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(m)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake '{label}'"
