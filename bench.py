@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of libgdn on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Default workload: the decode step at B = 64 (H_qk 16, H_v 32, d_k = d_v = 128,
+bfloat16 q/k/v/gates, float32 state updated in place).  One step = one
+gdn_decode_step over the whole batch.  The state rotates over 4 buffers
+(4 x 128 MiB, more than the 256 MB Infinity Cache) so each step streams its
+state from HBM.  W untimed steps, then K steps timed back to back between HIP
+events on the stream the kernel runs on.  Prints ONE JSON line.
+
+Other workloads (--workload prefill_t4096_fused_gates, varlen_prefill_8seq,
+wide_prefill_t32768_d256, tiny_prefill) time one gdn_prefill per step, each
+between its own events, with a 1 GiB write in between that flushes the L2 and
+the Infinity Cache.
+
+Inputs are synthetic and seeded (gated_delta_rule_serial_amd.synth); they are
+resident in device memory before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gated_delta_rule_serial_amd import gdn, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+# FP32 vector FMA without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
+FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12  # 78.64
+DECODE_STATE_BUFFERS = 4
+METRIC = "GDN prefill tokens/s + decode-step \u00b5s (B=64), % of HBM peak on 1 MI355X"
+
+
+def algorithmic_bytes(shape: synth.Shape, inp: synth.Inputs) -> int:
+    """Inputs read once, outputs written once, state read (if given) and written once."""
+    es = 2 if shape.io_dtype == torch.bfloat16 else 4
+    T = inp.total_tokens
+    n = len(inp.seqlens)
+    qk = 2 * T * shape.h_qk * shape.d_k * es
+    v = T * shape.h_v * shape.d_v * es
+    o = T * shape.h_v * shape.d_v * es
+    gates = 2 * T * shape.h_v * es
+    params = 2 * shape.h_v * 4 if shape.gate_mode == "raw" else 0
+    state = n * shape.h_v * shape.d_k * shape.d_v * 4
+    state_io = state * (2 if inp.initial_state is not None else 1)
+    cu = (n + 1) * 4 if shape.kind == "prefill" else 0
+    return qk + v + o + gates + params + state_io + cu
+
+
+def flops_serial(shape: synth.Shape, T: int) -> int:
+    """decay 1 + retrieval 2 + update 2 + readout 2 flops per state element per token."""
+    return 7 * T * shape.h_v * shape.d_k * shape.d_v
+
+
+def _kernel_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "gated_delta_rule_serial_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(name: str, kernel_files) -> float | None:
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/<name>_traffic.json),
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256_16") != _kernel_hash(kernel_files):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline_decode(shape, inp, budget_s=10.0):
+    """The oracle (as it stands) on a bounded sample of the decode workload:
+    whole B = 64 decode steps on the host cores until ~budget_s has passed."""
+    import numpy as np
+
+    import oracle
+    orc = oracle.default()
+    q, k, v = inp.q.double().numpy(), inp.k.double().numpy(), inp.v.double().numpy()
+    gg, bb = orc.gates(inp.a, inp.b, inp.A_log, inp.dt_bias)
+    st = inp.initial_state.double().numpy().copy()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.decode_step(q, k, v, gg, bb, st)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and steps >= 2:
+            break
+    assert np.isfinite(st).all()
+    return dict(value=round(shape.num_seqs * steps / el, 3), unit="tokens/s", cores=orc.max_threads(),
+                kind="oracle", sample=f"{steps} full decode steps (B={shape.num_seqs}, all heads) in {el:.1f} s")
+
+
+def cpu_baseline_prefill(shape, inp, budget_s=10.0):
+    """The oracle on a bounded sample of a prefill workload: one q/k head group
+    (its value heads) over the leading tokens of every sequence, sized to ~budget_s."""
+    import oracle
+    orc = oracle.default()
+    ratio = shape.h_v // shape.h_qk
+    hv = slice(0, ratio)
+    # probe speed on a short prefix, then size the sample
+    def run(ntok):
+        lens = [min(l, ntok) for l in inp.seqlens]
+        idx = torch.cat([torch.arange(int(inp.cu_seqlens[i]), int(inp.cu_seqlens[i]) + lens[i])
+                         for i in range(len(lens))]) if lens else torch.zeros(0, dtype=torch.long)
+        cu = [0]
+        for l in lens:
+            cu.append(cu[-1] + l)
+        gg, bb = orc.gates(inp.a[idx][:, hv], inp.b[idx][:, hv], inp.A_log[hv], inp.dt_bias[hv])
+        s0 = None if inp.initial_state is None else inp.initial_state[:, hv].double().numpy()
+        t0 = time.perf_counter()
+        orc.prefill(inp.q[idx][:, 0:1].double().numpy(), inp.k[idx][:, 0:1].double().numpy(),
+                    inp.v[idx][:, hv].double().numpy(), gg, bb, cu, s0)
+        return time.perf_counter() - t0, cu[-1]
+    el, tok = run(64)
+    ntok = max(64, int(64 * budget_s / max(el, 1e-6)))
+    el, tok = run(ntok)
+    heads_frac = ratio / shape.h_v
+    return dict(value=round(tok * heads_frac / el, 3), unit="tokens/s", cores=orc.max_threads(),
+                kind="oracle",
+                sample=f"q/k head group 0 ({ratio} of {shape.h_v} value heads), first {ntok} tokens of each "
+                       f"sequence ({tok} tokens) in {el:.1f} s; scaled to all heads")
+
+
+def bench_decode(shape, steps, warmup, want_cpu):
+    dev = "cuda"
+    inp = synth.generate(shape)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    # gates: the library's own gate prologue (bf16 g, beta from the raw draws)
+    g, beta = gdn.gate_prologue(inp.a.to(dev), inp.b.to(dev), inp.A_log.to(dev), inp.dt_bias.to(dev))
+    states = [inp.initial_state.to(dev).clone() for _ in range(DECODE_STATE_BUFFERS)]
+    out = torch.empty(shape.num_seqs, shape.h_v, shape.d_v, dtype=shape.io_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        gdn.gdn_decode_step(q, k, v, states[i % len(states)], out, g=g, beta=beta)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        gdn.gdn_decode_step(q, k, v, states[i % len(states)], out, g=g, beta=beta)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    assert torch.isfinite(out.float()).all()
+    nbytes = algorithmic_bytes(shape, inp)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    kernel_files = ["decode_step.hip", "gdn_device.hpp"]
+    traffic = _traffic(shape.name, kernel_files)
+    line = {
+        "metric": METRIC,
+        "value": round(shape.num_seqs / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "decode_step_us": round(ms * 1e3, 3),
+        "ms_per_step": round(ms, 6),
+        "wall_s": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel<bf16, 128, precomputed gates>",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "config": {"workload": shape.name, "batch": shape.num_seqs, "h_qk": shape.h_qk, "h_v": shape.h_v,
+                   "d_k": shape.d_k, "d_v": shape.d_v, "io_dtype": "bf16", "state_dtype": "f32",
+                   "gates": "precomputed bf16", "state_buffers_rotated": DECODE_STATE_BUFFERS},
+    }
+    if want_cpu:
+        line["cpu_baseline"] = cpu_baseline_decode(shape, inp)
+    return line
+
+
+def _flush(buf):
+    buf.fill_(1.0)
+
+
+def bench_prefill(shape, steps, warmup, want_cpu):
+    dev = "cuda"
+    inp = synth.generate(shape)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cu = inp.cu_seqlens.to(dev)
+    cu_host = inp.cu_seqlens.tolist()
+    raw = shape.gate_mode == "raw"
+    if raw:
+        gates = dict(a=inp.a.to(dev), b=inp.b.to(dev), A_log=inp.A_log.to(dev), dt_bias=inp.dt_bias.to(dev))
+        g = beta = None
+    else:
+        g, beta = gdn.gate_prologue(inp.a.to(dev), inp.b.to(dev), inp.A_log.to(dev), inp.dt_bias.to(dev))
+        gates = dict(g=g, beta=beta)
+    s0 = None if inp.initial_state is None else inp.initial_state.to(dev)
+    T = inp.total_tokens
+    n = len(inp.seqlens)
+    out = torch.empty(T, shape.h_v, shape.d_v, dtype=shape.io_dtype, device=dev)
+    fin = torch.empty(n, shape.h_v, shape.d_k, shape.d_v, dtype=torch.float32, device=dev)
+    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream()
+
+    def one():
+        gdn.gdn_prefill(q, k, v, cu, out=out, final_state=fin, initial_state=s0, cu_seqlens_host=cu_host,
+                        **gates)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    times = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        _flush(flush)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        one()
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_list = sorted(a.elapsed_time(b) for a, b in times)
+    ms = sum(ms_list) / len(ms_list)
+    assert torch.isfinite(out.float()).all()
+    nbytes = algorithmic_bytes(shape, inp)
+    fl = flops_serial(shape, T)
+    achieved_tf = fl / (ms * 1e-3) / 1e12
+    kernel_files = ["prefill_scan.hip", "gdn_device.hpp"]
+    line = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(ms, 6),
+        "ms_median": round(ms_list[len(ms_list) // 2], 6),
+        "wall_s": round(wall, 3),
+        "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(FP32_VALU_PEAK_TFLOPS, 2),
+                     "unit": "TFLOP/s", "frac": round(achieved_tf / FP32_VALU_PEAK_TFLOPS, 4),
+                     "traffic": _traffic(shape.name, kernel_files),
+                     "kernel": "scan_kernel (serial scan)", "flops_per_launch": fl,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "config": {"workload": shape.name, "num_seqs": n, "total_tokens": T, "seqlens": inp.seqlens,
+                   "h_qk": shape.h_qk, "h_v": shape.h_v, "d_k": shape.d_k, "d_v": shape.d_v,
+                   "io_dtype": "bf16" if shape.io_dtype == torch.bfloat16 else "f32", "state_dtype": "f32",
+                   "gates": shape.gate_mode},
+    }
+    if want_cpu:
+        line["cpu_baseline"] = cpu_baseline_prefill(shape, inp)
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_b64", choices=sorted(synth.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the gated delta-rule path here runs on a single MI355X "
+              f"(--gpus {args.gpus} is not supported; per-GPU sharding is by heads or sequences, "
+              f"with no exchange inside the op)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    shape = synth.BY_NAME[args.workload]
+    decode = shape.kind == "decode"
+    steps = args.steps if args.steps is not None else (1000 if decode else 10)
+    warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
+    want_cpu = not args.no_cpu_baseline
+    line = (bench_decode if decode else bench_prefill)(shape, steps, warmup, want_cpu)
+    head = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"), "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
+    head.update(line)
+    print(json.dumps(head), flush=True)
+
+
+if __name__ == "__main__":
+    main()

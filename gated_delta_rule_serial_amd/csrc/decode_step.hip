@@ -1,0 +1,200 @@
+// decode_step.hip -- one gated delta-rule token per sequence, state in HBM
+// updated in place (gfx950).
+//
+// Per (sequence b, value head h), with alpha = exp(g), the state S (d_k x d_v
+// float32) is read once and written once:
+//     a = S^T k,  c = S^T q,  kq = k . q          (one pass over S)
+//     delta = beta (v - alpha a)                  (retrieval on the decayed S)
+//     o     = scale (alpha c + delta kq)          (= scale S'^T q)
+//     S'    = alpha S + k delta^T                 (written back)
+// This is the order of [P4] onnx-runtime-ep-cuda, src/kernels/
+// linear_attention.rs, `linear_attention_core` steps 1-4 (readout of the
+// updated state) with the readout expanded algebraically so that it needs no
+// second pass over S: S'^T q = alpha S^T q + delta (k . q).
+//
+// Mapping: a 256-thread workgroup owns 64 state columns of one (b, h).
+// Thread (rg, tc), rg in [0, 16), tc in [0, 16), holds rows
+// rg*RPT .. rg*RPT + RPT - 1 of columns 4 tc .. 4 tc + 3 in VGPRs, RPT =
+// DK / 16.  A wave's load instruction covers 4 rows x 256 contiguous bytes.
+// The column sums over the 16 row groups go through LDS; one wave finishes
+// them, writes o and broadcasts delta through LDS; every thread then writes
+// its tile.  The state traffic (read + write once) is the kernel's HBM cost.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowGroups = 16;
+constexpr int kColThreads = 16;
+constexpr int kColsPerThread = 4;
+constexpr int kBlockCols = kColThreads * kColsPerThread;  // 64
+
+template <typename IO, int DK, bool RAW>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+  constexpr int RPT = DK / kRowGroups;
+  __shared__ float red_a[kRowGroups][kBlockCols];
+  __shared__ float red_c[kRowGroups][kBlockCols];
+  __shared__ float red_kq[kRowGroups];
+  __shared__ float sh_delta[kBlockCols];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int tc = tid % kColThreads;
+  const int rg = tid / kColThreads;
+  int unit = static_cast<int>(blockIdx.x);
+  const int cb = unit % p.col_blocks;
+  unit /= p.col_blocks;
+  const int h = unit % p.h_v;
+  const int b = unit / p.h_v;
+  const int hq = h / p.ratio;
+  const int d_k = p.d_k, d_v = p.d_v;
+  const int j0 = cb * kBlockCols + tc * kColsPerThread;  // first column of this thread
+  const int row0 = rg * RPT;
+  const bool vec_cols = (d_v % 4 == 0) && (j0 + kColsPerThread <= d_v);
+
+  float* __restrict__ Sg = p.state + (static_cast<size_t>(b) * p.h_v + h) * static_cast<size_t>(d_k) * d_v;
+
+  // ---- state tile (issued first: it is the long-latency traffic)
+  float S[RPT][kColsPerThread];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = row0 + m;
+    if (i < d_k && vec_cols) {
+      const float4 x = *reinterpret_cast<const float4*>(Sg + static_cast<size_t>(i) * d_v + j0);
+      S[m][0] = x.x;
+      S[m][1] = x.y;
+      S[m][2] = x.z;
+      S[m][3] = x.w;
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < kColsPerThread; ++cc)
+        S[m][cc] = (i < d_k && j0 + cc < d_v) ? Sg[static_cast<size_t>(i) * d_v + j0 + cc] : 0.0f;
+    }
+  }
+
+  // ---- k, q rows of this thread
+  const IO* kq_base_k = static_cast<const IO*>(p.k) + (static_cast<size_t>(b) * p.h_qk + hq) * d_k + row0;
+  const IO* kq_base_q = static_cast<const IO*>(p.q) + (static_cast<size_t>(b) * p.h_qk + hq) * d_k + row0;
+  RawSlice<IO, RPT> rk, rq;
+  if (d_k == DK) {
+    rk.load(kq_base_k);
+    rq.load(kq_base_q);
+  } else {
+    rk.load_masked(kq_base_k, d_k - row0);
+    rq.load_masked(kq_base_q, d_k - row0);
+  }
+
+  // ---- gates (one value per (b, h))
+  const size_t gidx = static_cast<size_t>(b) * p.h_v + h;
+  float alpha, beta;
+  if constexpr (RAW) {
+    const float a = widen(static_cast<const IO*>(p.gates.a)[gidx]);
+    const float bb = widen(static_cast<const IO*>(p.gates.b)[gidx]);
+    alpha = expf(gate_log_decay(a, p.gates.A_log[h], p.gates.dt_bias[h]));
+    beta = gate_sigmoid(bb);
+  } else {
+    alpha = expf(widen(static_cast<const IO*>(p.gates.g)[gidx]));
+    beta = widen(static_cast<const IO*>(p.gates.beta)[gidx]);
+  }
+
+  float kf[RPT], qf[RPT];
+  rk.widen_to(kf);
+  rq.widen_to(qf);
+
+  // ---- partial column sums over this thread's rows
+  float pa[kColsPerThread], pc[kColsPerThread];
+  float pkq = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < kColsPerThread; ++cc) {
+    pa[cc] = 0.0f;
+    pc[cc] = 0.0f;
+  }
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+#pragma unroll
+    for (int cc = 0; cc < kColsPerThread; ++cc) {
+      pa[cc] = fmaf(S[m][cc], kf[m], pa[cc]);
+      pc[cc] = fmaf(S[m][cc], qf[m], pc[cc]);
+    }
+    pkq = fmaf(kf[m], qf[m], pkq);
+  }
+#pragma unroll
+  for (int cc = 0; cc < kColsPerThread; ++cc) {
+    red_a[rg][tc * kColsPerThread + cc] = pa[cc];
+    red_c[rg][tc * kColsPerThread + cc] = pc[cc];
+  }
+  if (tc == 0) red_kq[rg] = pkq;
+  __syncthreads();
+
+  // ---- one wave finishes the column sums, writes o, publishes delta
+  if (tid < kBlockCols) {
+    float a = 0.0f, cs = 0.0f, kq = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kRowGroups; ++g) {
+      a += red_a[g][tid];
+      cs += red_c[g][tid];
+      kq += red_kq[g];
+    }
+    const int j = cb * kBlockCols + tid;
+    float vv = 0.0f;
+    if (j < d_v) vv = widen(static_cast<const IO*>(p.v)[(static_cast<size_t>(b) * p.h_v + h) * d_v + j]);
+    const float delta = beta * (vv - alpha * a);
+    sh_delta[tid] = delta;
+    if (j < d_v) {
+      const float o = p.scale * fmaf(alpha, cs, delta * kq);
+      narrow_store(static_cast<IO*>(p.out) + (static_cast<size_t>(b) * p.h_v + h) * d_v + j, o);
+    }
+  }
+  __syncthreads();
+
+  // ---- S' = alpha S + k delta^T, written back in place
+  float dl[kColsPerThread];
+#pragma unroll
+  for (int cc = 0; cc < kColsPerThread; ++cc) dl[cc] = sh_delta[tc * kColsPerThread + cc];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = row0 + m;
+    float o4[kColsPerThread];
+#pragma unroll
+    for (int cc = 0; cc < kColsPerThread; ++cc) o4[cc] = fmaf(S[m][cc], alpha, kf[m] * dl[cc]);
+    if (i < d_k && vec_cols) {
+      *reinterpret_cast<float4*>(Sg + static_cast<size_t>(i) * d_v + j0) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    } else if (i < d_k) {
+#pragma unroll
+      for (int cc = 0; cc < kColsPerThread; ++cc)
+        if (j0 + cc < d_v) Sg[static_cast<size_t>(i) * d_v + j0 + cc] = o4[cc];
+    }
+  }
+}
+
+template <typename IO, int DK>
+hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
+  const unsigned blocks = static_cast<unsigned>(p.batch) * p.h_v * p.col_blocks;
+  if (blocks == 0) return hipSuccess;
+  if (p.gates.raw)
+    hipLaunchKernelGGL((decode_kernel<IO, DK, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<IO, DK, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_io(const DecodeParams& p, hipStream_t stream) {
+  if (p.d_k <= 16) return launch_dk<IO, 16>(p, stream);
+  if (p.d_k <= 32) return launch_dk<IO, 32>(p, stream);
+  if (p.d_k <= 64) return launch_dk<IO, 64>(p, stream);
+  if (p.d_k <= 128) return launch_dk<IO, 128>(p, stream);
+  return launch_dk<IO, 256>(p, stream);
+}
+
+}  // namespace
+
+int decode_columns_per_block() { return kBlockCols; }
+
+hipError_t launch_decode_step(DecodeParams p, int io_bf16, hipStream_t stream) {
+  return io_bf16 ? launch_io<bf16_t>(p, stream) : launch_io<float>(p, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,270 @@
+// gdn_api.cpp -- the C ABI of libgdn (include/gdn.h): host-side validation,
+// error reporting and dispatch to the HIP kernels.
+//
+// Validation mirrors what the pages' execute paths check before a launch
+// ([P4] onnx-runtime-ep-cuda, src/kernels/linear_attention.rs,
+// `LinearAttentionKernel::execute`: head divisibility, d_k range, gate
+// presence and shape, contiguous uniform-dtype tensors; [P1]
+// onnxruntime-ep-mlx, src/ops/ssm.rs, `linear_attention_op` geometry checks),
+// restated for this ABI's packed layout.  Nothing is enqueued unless every
+// check passes.
+#include "gdn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <vector>
+
+#include "gdn_launch.hpp"
+
+#define GDN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdn_status fail(gdn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+gdn_status ok() {
+  g_last_error[0] = '\0';
+  return GDN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool aligned_to(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t io_size(int32_t dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+// Shared checks of the geometry and the gate inputs.  The per-token gate
+// tensors are required only when there are tokens to read them for.
+gdn_status check_problem(const gdn_problem* p, const char* fn, bool has_tokens) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: problem is NULL", fn);
+  if (p->h_qk <= 0 || p->h_v <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: head counts must be positive (h_qk=%d, h_v=%d)", fn,
+                p->h_qk, p->h_v);
+  if (p->h_v % p->h_qk != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: h_v=%d is not a multiple of h_qk=%d", fn, p->h_v, p->h_qk);
+  if (p->d_k <= 0 || p->d_v <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: head sizes must be positive (d_k=%d, d_v=%d)", fn, p->d_k,
+                p->d_v);
+  if (p->d_k > GDN_MAX_HEAD_DIM || p->d_v > GDN_MAX_HEAD_DIM)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: head sizes above %d are not supported (d_k=%d, d_v=%d)", fn,
+                GDN_MAX_HEAD_DIM, p->d_k, p->d_v);
+  if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: io_dtype %d is not supported (GDN_F32, GDN_BF16)", fn, p->io_dtype);
+  if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  const size_t es = io_size(p->io_dtype);
+  if (p->gate_mode == GDN_GATES_PRECOMPUTED) {
+    if (has_tokens && (!p->g || !p->beta))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: precomputed gates need g and beta", fn);
+    if (!aligned_to(p->g, es) || !aligned_to(p->beta, es))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: g / beta are not aligned to their element size", fn);
+  } else if (p->gate_mode == GDN_GATES_RAW) {
+    if (has_tokens && (!p->a || !p->b || !p->A_log || !p->dt_bias))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: raw gates need a, b, A_log and dt_bias", fn);
+    if (!aligned_to(p->a, es) || !aligned_to(p->b, es) || !aligned_to(p->A_log, 4) ||
+        !aligned_to(p->dt_bias, 4))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: gate inputs are not aligned to their element size", fn);
+  } else {
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: unknown gate_mode %d", fn, p->gate_mode);
+  }
+  return GDN_OK;
+}
+
+gdn::GateArgs gate_args(const gdn_problem* p) {
+  gdn::GateArgs g{};
+  g.raw = p->gate_mode == GDN_GATES_RAW ? 1 : 0;
+  g.g = p->g;
+  g.beta = p->beta;
+  g.a = p->a;
+  g.b = p->b;
+  g.A_log = p->A_log;
+  g.dt_bias = p->dt_bias;
+  return g;
+}
+
+float resolved_scale(const gdn_problem* p) {
+  return p->scale != 0.0f ? p->scale : 1.0f / std::sqrt(static_cast<float>(p->d_k));
+}
+
+}  // namespace
+
+GDN_EXPORT gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int32_t total_tokens, const void* q,
+                                  const void* k, const void* v, const float* initial_state, void* out,
+                                  float* final_state, hipStream_t stream) {
+  const char* fn = "gdn_prefill";
+  gdn_status st = check_problem(problem, fn, total_tokens > 0);
+  if (st != GDN_OK) return st;
+  if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: num_seqs=%d is negative", fn, num_seqs);
+  if (total_tokens < 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: total_tokens=%d is negative", fn, total_tokens);
+  if (num_seqs == 0 && total_tokens != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: %d tokens but no sequences", fn, total_tokens);
+  if (num_seqs > 0 && !cu_seqlens) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL", fn);
+  if (total_tokens > 0 && (!q || !k || !v))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k and v are required when total_tokens > 0", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(initial_state) ||
+      !aligned16(final_state))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, out and the states must be 16-byte aligned", fn);
+  if (!aligned_to(cu_seqlens, 4)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is misaligned", fn);
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens[0]=%d, expected 0", fn, cu_seqlens_host[0]);
+    for (int32_t n = 0; n < num_seqs; ++n)
+      if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+        return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens decreases at %d (%d -> %d)", fn, n,
+                    cu_seqlens_host[n], cu_seqlens_host[n + 1]);
+    if (cu_seqlens_host[num_seqs] != total_tokens)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens[%d]=%d but total_tokens=%d", fn, num_seqs,
+                  cu_seqlens_host[num_seqs], total_tokens);
+  }
+  const gdn_problem& p = *problem;
+  const size_t es = io_size(p.io_dtype);
+  const size_t state_bytes = static_cast<size_t>(num_seqs) * p.h_v * p.d_k * p.d_v * sizeof(float);
+  const size_t out_bytes = static_cast<size_t>(total_tokens) * p.h_v * p.d_v * es;
+  if (final_state && initial_state && final_state != initial_state &&
+      overlaps(final_state, state_bytes, initial_state, state_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: final_state partially overlaps initial_state", fn);
+  const size_t qk_bytes = static_cast<size_t>(total_tokens) * p.h_qk * p.d_k * es;
+  const size_t v_bytes = static_cast<size_t>(total_tokens) * p.h_v * p.d_v * es;
+  if (overlaps(out, out_bytes, q, qk_bytes) || overlaps(out, out_bytes, k, qk_bytes) ||
+      overlaps(out, out_bytes, v, v_bytes) || overlaps(out, out_bytes, final_state, state_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: out overlaps an input or the final state", fn);
+
+  if (num_seqs == 0 || (total_tokens == 0 && !final_state)) return ok();  // nothing to write
+
+  gdn::ScanParams sp{};
+  sp.q = q;
+  sp.k = k;
+  sp.v = v;
+  sp.gates = gate_args(problem);
+  sp.s0 = initial_state;
+  sp.out = out;
+  sp.sN = final_state;
+  sp.cu = cu_seqlens;
+  sp.num_seqs = num_seqs;
+  sp.h_qk = p.h_qk;
+  sp.h_v = p.h_v;
+  sp.d_k = p.d_k;
+  sp.d_v = p.d_v;
+  sp.ratio = p.h_v / p.h_qk;
+  const int cpw = gdn::scan_columns_per_wave(p.d_k);
+  sp.col_blocks = (p.d_v + cpw - 1) / cpw;
+  sp.scale = resolved_scale(problem);
+  const uint64_t blocks = static_cast<uint64_t>(num_seqs) * p.h_v * sp.col_blocks;
+  if (blocks > 0x7fffffffull)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", fn,
+                static_cast<unsigned long long>(blocks));
+  const hipError_t e = gdn::launch_prefill_scan(sp, p.io_dtype == GDN_BF16, stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+GDN_EXPORT gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch, const void* q, const void* k,
+                                      const void* v, float* state, void* out, hipStream_t stream) {
+  const char* fn = "gdn_decode_step";
+  gdn_status st = check_problem(problem, fn, batch > 0);
+  if (st != GDN_OK) return st;
+  if (batch < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: batch=%d is negative", fn, batch);
+  if (batch == 0) return ok();
+  if (!q || !k || !v || !state || !out)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, state and out are required", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(out))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, state and out must be 16-byte aligned", fn);
+  const gdn_problem& p = *problem;
+  const size_t es = io_size(p.io_dtype);
+  const size_t state_bytes = static_cast<size_t>(batch) * p.h_v * p.d_k * p.d_v * sizeof(float);
+  const size_t out_bytes = static_cast<size_t>(batch) * p.h_v * p.d_v * es;
+  const size_t qk_bytes = static_cast<size_t>(batch) * p.h_qk * p.d_k * es;
+  const size_t v_bytes = static_cast<size_t>(batch) * p.h_v * p.d_v * es;
+  if (overlaps(out, out_bytes, state, state_bytes) || overlaps(out, out_bytes, q, qk_bytes) ||
+      overlaps(out, out_bytes, k, qk_bytes) || overlaps(out, out_bytes, v, v_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: out overlaps the state or an input", fn);
+  if (overlaps(state, state_bytes, q, qk_bytes) || overlaps(state, state_bytes, k, qk_bytes) ||
+      overlaps(state, state_bytes, v, v_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state overlaps an input", fn);
+
+  gdn::DecodeParams dp{};
+  dp.q = q;
+  dp.k = k;
+  dp.v = v;
+  dp.gates = gate_args(problem);
+  dp.state = state;
+  dp.out = out;
+  dp.batch = batch;
+  dp.h_qk = p.h_qk;
+  dp.h_v = p.h_v;
+  dp.d_k = p.d_k;
+  dp.d_v = p.d_v;
+  dp.ratio = p.h_v / p.h_qk;
+  const int cpb = gdn::decode_columns_per_block();
+  dp.col_blocks = (p.d_v + cpb - 1) / cpb;
+  dp.scale = resolved_scale(problem);
+  const uint64_t blocks = static_cast<uint64_t>(batch) * p.h_v * dp.col_blocks;
+  if (blocks > 0x7fffffffull)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", fn,
+                static_cast<unsigned long long>(blocks));
+  const hipError_t e = gdn::launch_decode_step(dp, p.io_dtype == GDN_BF16, stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+GDN_EXPORT gdn_status gdn_gate_prologue(int32_t tokens, int32_t h_v, int32_t io_dtype, const void* a,
+                                        const void* b, const float* A_log, const float* dt_bias, void* g,
+                                        void* beta, hipStream_t stream) {
+  const char* fn = "gdn_gate_prologue";
+  if (tokens < 0 || h_v <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: tokens=%d must be >= 0 and h_v=%d > 0", fn, tokens, h_v);
+  if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: io_dtype %d is not supported", fn, io_dtype);
+  if (tokens == 0 || (!g && !beta)) return ok();
+  if (g && (!a || !A_log || !dt_bias))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: g needs a, A_log and dt_bias", fn);
+  if (beta && !b) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: beta needs b", fn);
+  const size_t es = io_size(io_dtype);
+  if (!aligned_to(a, es) || !aligned_to(b, es) || !aligned_to(g, es) || !aligned_to(beta, es) ||
+      !aligned_to(A_log, 4) || !aligned_to(dt_bias, 4))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: pointers are not aligned to their element size", fn);
+  gdn::GatePrologueParams gp{};
+  gp.a = a;
+  gp.b = b;
+  gp.A_log = A_log;
+  gp.dt_bias = dt_bias;
+  gp.g = g;
+  gp.beta = beta;
+  gp.rows = tokens;
+  gp.h_v = h_v;
+  const hipError_t e = gdn::launch_gate_prologue(gp, io_dtype == GDN_BF16, stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+GDN_EXPORT const char* gdn_last_error(void) { return g_last_error; }
+
+GDN_EXPORT const char* gdn_status_string(gdn_status status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARGUMENT: return "GDN_ERR_INVALID_ARGUMENT";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+  }
+  return "GDN_STATUS_UNKNOWN";
+}
+
+GDN_EXPORT int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }

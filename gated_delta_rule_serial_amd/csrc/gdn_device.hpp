@@ -1,0 +1,213 @@
+// gdn_device.hpp -- device helpers shared by the libgdn kernels (gfx950).
+//
+// I/O element types, widening loads of short row slices, 64-lane wavefront
+// reductions built from DPP row operations, and the gate prologue math.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+using bf16_t = uint16_t;  // bfloat16 storage
+
+// ---------------------------------------------------------------- scalars
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(bf16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+
+// Narrowing rounds to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ void narrow_store(float* p, float x) { *p = x; }
+__device__ __forceinline__ void narrow_store(bf16_t* p, float x) {
+  *p = __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
+}
+
+template <typename IO>
+__device__ __forceinline__ float load1(const IO* p) { return widen(*p); }
+
+// ---------------------------------------------------------------- row slices
+// Load N consecutive I/O elements starting at p (aligned to N elements) and
+// widen them to float.  N is a power of two, 1 .. 16.
+template <int N>
+__device__ __forceinline__ void load_slice(const float* p, float* dst) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c) {
+      const float4 x = reinterpret_cast<const float4*>(p)[c];
+      dst[4 * c + 0] = x.x;
+      dst[4 * c + 1] = x.y;
+      dst[4 * c + 2] = x.z;
+      dst[4 * c + 3] = x.w;
+    }
+  } else if constexpr (N == 2) {
+    const float2 x = *reinterpret_cast<const float2*>(p);
+    dst[0] = x.x;
+    dst[1] = x.y;
+  } else {
+    dst[0] = *p;
+  }
+}
+
+__device__ __forceinline__ void unpack2(uint32_t w, float* dst) {
+  dst[0] = __uint_as_float(w << 16);
+  dst[1] = __uint_as_float(w & 0xffff0000u);
+}
+
+template <int N>
+__device__ __forceinline__ void load_slice(const bf16_t* p, float* dst) {
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int c = 0; c < N / 8; ++c) {
+      const uint4 x = reinterpret_cast<const uint4*>(p)[c];
+      unpack2(x.x, dst + 8 * c + 0);
+      unpack2(x.y, dst + 8 * c + 2);
+      unpack2(x.z, dst + 8 * c + 4);
+      unpack2(x.w, dst + 8 * c + 6);
+    }
+  } else if constexpr (N == 4) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    unpack2(x.x, dst + 0);
+    unpack2(x.y, dst + 2);
+  } else if constexpr (N == 2) {
+    unpack2(*reinterpret_cast<const uint32_t*>(p), dst);
+  } else {
+    dst[0] = widen(*p);
+  }
+}
+
+// Bounds-checked variant: element e is read only when e < limit (else 0).
+template <int N, typename IO>
+__device__ __forceinline__ void load_slice_masked(const IO* p, int limit, float* dst) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) dst[e] = (e < limit) ? widen(p[e]) : 0.0f;
+}
+
+// A row slice of N I/O elements held in its packed (loaded, not yet widened)
+// form.  Keeping the packed words lets a load be issued many steps before its
+// value is consumed: the wait for the data lands at widen(), not at load().
+template <typename IO, int N>
+struct RawSlice {
+  static constexpr int kBytes = N * static_cast<int>(sizeof(IO));
+  static constexpr int kWords = kBytes >= 4 ? kBytes / 4 : 1;
+  uint32_t w[kWords];
+
+  // p must be aligned to min(kBytes, 16) bytes.
+  __device__ __forceinline__ void load(const IO* p) {
+    if constexpr (kBytes >= 16) {
+#pragma unroll
+      for (int c = 0; c < kBytes / 16; ++c) {
+        const uint4 x = reinterpret_cast<const uint4*>(p)[c];
+        w[4 * c + 0] = x.x;
+        w[4 * c + 1] = x.y;
+        w[4 * c + 2] = x.z;
+        w[4 * c + 3] = x.w;
+      }
+    } else if constexpr (kBytes == 8) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0] = x.x;
+      w[1] = x.y;
+    } else if constexpr (kBytes == 4) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      w[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+  }
+
+  // Element e is read only when e < limit; the rest read as zero.
+  __device__ __forceinline__ void load_masked(const IO* p, int limit) {
+#pragma unroll
+    for (int c = 0; c < kWords; ++c) w[c] = 0u;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      if (e < limit) {
+        if constexpr (sizeof(IO) == 4) {
+          w[e] = reinterpret_cast<const uint32_t*>(p)[e];
+        } else {
+          const uint32_t h = reinterpret_cast<const uint16_t*>(p)[e];
+          w[e / 2] |= (e & 1) ? (h << 16) : h;
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void widen_to(float* dst) const {
+    if constexpr (sizeof(IO) == 4) {
+#pragma unroll
+      for (int e = 0; e < N; ++e) dst[e] = __uint_as_float(w[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const uint32_t word = w[e / 2];
+        dst[e] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+      }
+    }
+  }
+};
+
+// One I/O scalar in packed form (see RawSlice).
+template <typename IO>
+struct RawScalar {
+  uint32_t w;
+  __device__ __forceinline__ void load(const IO* p) {
+    if constexpr (sizeof(IO) == 4) w = *reinterpret_cast<const uint32_t*>(p);
+    else w = *reinterpret_cast<const uint16_t*>(p);
+  }
+  __device__ __forceinline__ float value() const {
+    if constexpr (sizeof(IO) == 4) return __uint_as_float(w);
+    else return __uint_as_float(w << 16);
+  }
+};
+
+__device__ __forceinline__ float readlane(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// ---------------------------------------------------------------- DPP
+// dpp_ctrl encodings (GCN/CDNA DPP): quad_perm selectors and row mirrors.
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G consecutive lanes (G = 1, 2, 4, 8, 16, 32);
+// every lane of a group receives the group's sum.  Every lane of the wave
+// must be active.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G >= 2) x += dpp<kQuadSwap1>(x);
+  if constexpr (G >= 4) x += dpp<kQuadSwap2>(x);
+  if constexpr (G >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (G >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (G >= 32) {
+    // lane i <- lane i ^ 16 within each 32 (ds_swizzle bit-mask mode:
+    // and_mask 0x1f, or_mask 0, xor_mask 0x10).
+    x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+  }
+  static_assert(G <= 32, "group_sum supports groups of at most 32 lanes");
+  return x;
+}
+
+// ---------------------------------------------------------------- gates
+// Logistic function with exp evaluated only at non-positive arguments.
+__device__ __forceinline__ float gate_sigmoid(float x) {
+  if (x >= 0.0f) return 1.0f / (1.0f + expf(-x));
+  const float e = expf(x);
+  return e / (1.0f + e);
+}
+
+// softplus(x) = max(x, 0) + log1p(exp(-|x|)), overflow-free.
+__device__ __forceinline__ float gate_softplus(float x) {
+  return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+}
+
+// Log-decay of the raw gate: -exp(A_log) * softplus(a + dt_bias).
+__device__ __forceinline__ float gate_log_decay(float a, float A_log, float dt_bias) {
+  return -expf(A_log) * gate_softplus(a + dt_bias);
+}
+
+}  // namespace gdn

@@ -1,0 +1,75 @@
+// gdn_launch.hpp -- parameter blocks and launchers of the libgdn kernels
+// (internal to the library; the public C ABI is include/gdn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Gate inputs as the kernels see them (one of the two pairs is used).
+struct GateArgs {
+  int32_t raw;          // 0: g / beta given; 1: a / b / A_log / dt_bias given
+  const void* g;        // [tokens, h_v] io dtype
+  const void* beta;     // [tokens, h_v] io dtype
+  const void* a;        // [tokens, h_v] io dtype
+  const void* b;        // [tokens, h_v] io dtype
+  const float* A_log;   // [h_v]
+  const float* dt_bias; // [h_v]
+};
+
+// Serial scan over packed sequences.
+struct ScanParams {
+  const void* q;          // [T, h_qk, d_k]
+  const void* k;          // [T, h_qk, d_k]
+  const void* v;          // [T, h_v, d_v]
+  GateArgs gates;
+  const float* s0;        // [N, h_v, d_k, d_v] or null
+  void* out;              // [T, h_v, d_v] or null
+  float* sN;              // [N, h_v, d_k, d_v] or null
+  const int32_t* cu;      // [N + 1]
+  int32_t num_seqs;
+  int32_t h_qk, h_v, d_k, d_v;
+  int32_t ratio;          // h_v / h_qk
+  int32_t col_blocks;     // column blocks per (sequence, head)
+  float scale;
+};
+
+// One decode token per sequence, state updated in place.
+struct DecodeParams {
+  const void* q;          // [B, h_qk, d_k]
+  const void* k;          // [B, h_qk, d_k]
+  const void* v;          // [B, h_v, d_v]
+  GateArgs gates;
+  float* state;           // [B, h_v, d_k, d_v]
+  void* out;              // [B, h_v, d_v]
+  int32_t batch;
+  int32_t h_qk, h_v, d_k, d_v;
+  int32_t ratio;
+  int32_t col_blocks;
+  float scale;
+};
+
+struct GatePrologueParams {
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  void* g;
+  void* beta;
+  int64_t rows;
+  int32_t h_v;
+};
+
+// io_bf16: 1 for bfloat16 I/O, 0 for float32.  Each launcher enqueues on
+// `stream` and returns the launch status.
+hipError_t launch_prefill_scan(ScanParams p, int io_bf16, hipStream_t stream);
+hipError_t launch_decode_step(DecodeParams p, int io_bf16, hipStream_t stream);
+hipError_t launch_gate_prologue(GatePrologueParams p, int io_bf16, hipStream_t stream);
+
+// Columns one scan wave owns for a given d_k (used to size the grid).
+int scan_columns_per_wave(int d_k);
+// Columns one decode workgroup owns.
+int decode_columns_per_block();
+
+}  // namespace gdn

@@ -1,0 +1,224 @@
+// prefill_scan.hip -- serial-scan prefill of the gated delta rule on gfx950.
+//
+// What is computed (per sequence n, value head h, token t; state S is d_k x d_v
+// float32):  S <- exp(g_t) S;  r = S^T k_t;  S <- S + k_t (beta_t (v_t - r))^T;
+// o_t = scale S^T q_t on the updated S.  Pages: [P4] onnx-runtime-ep-cuda,
+// src/kernels/linear_attention.rs, `linear_attention_core` steps 1-4 and the
+// module doc "Parallelization" (each state column evolves on its own);
+// [P1] onnxruntime-ep-mlx, src/ops/ssm.rs, the wide scan (float32 working
+// state, only I/O stores rounded).
+//
+// Mapping on a CDNA4 wavefront (64 lanes):
+//   * one wave owns CPW = 64 / R state columns of one (sequence, value head);
+//   * the R consecutive lanes of a column each hold RPL = DK / R rows of it
+//     in VGPRs for the whole scan (no scratch, no LDS);
+//   * the two d_k dot products per token (retrieval before the update,
+//     readout after it) are partial sums over a lane's rows followed by a
+//     DPP row-op reduction over the R lanes (plus one ds_swizzle for R = 32);
+//   * q_t, k_t, v_t are loaded as packed words PF tokens ahead of use
+//     through a register ring, so global latency overlaps the serial chain;
+//   * the gates of 64 tokens are computed once, lane-parallel (lane l takes
+//     token t0 + l), and read per token with v_readlane.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kPrefetch = 4;  // tokens of q/k/v in flight ahead of use
+
+// Lanes per column for each padded key size (rows per lane = DK / R).
+template <int DK>
+struct ScanShape;
+template <> struct ScanShape<16> { static constexpr int R = 4; };
+template <> struct ScanShape<32> { static constexpr int R = 8; };
+template <> struct ScanShape<64> { static constexpr int R = 8; };
+template <> struct ScanShape<128> { static constexpr int R = 16; };
+template <> struct ScanShape<256> { static constexpr int R = 32; };
+
+template <typename IO, int DK, bool RAW>
+__global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
+  constexpr int R = ScanShape<DK>::R;
+  constexpr int CPW = kWave / R;
+  constexpr int RPL = DK / R;
+
+  const int lane = static_cast<int>(threadIdx.x);
+  const int c = lane / R;        // column within the wave
+  const int r = lane % R;        // row slice within the column
+  int unit = static_cast<int>(blockIdx.x);
+  const int cb = unit % p.col_blocks;
+  unit /= p.col_blocks;
+  const int h = unit % p.h_v;
+  const int n = unit / p.h_v;
+  const int hq = h / p.ratio;
+  const int j = cb * CPW + c;
+  const bool col_ok = j < p.d_v;
+  const int row0 = r * RPL;
+  const bool full_rows = (p.d_k == DK);
+  const int row_limit = p.d_k - row0;  // rows of this lane's slice that exist
+
+  const int t_begin = p.cu[n];
+  const int t_end = p.cu[n + 1];
+
+  // ---- initial state (column j, rows row0 .. row0 + RPL - 1)
+  float S[RPL];
+  const size_t sbase = (static_cast<size_t>(n) * p.h_v + h) * static_cast<size_t>(p.d_k) * p.d_v;
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) {
+    const int i = row0 + m;
+    S[m] = (p.s0 != nullptr && col_ok && i < p.d_k) ? p.s0[sbase + static_cast<size_t>(i) * p.d_v + j] : 0.0f;
+  }
+
+  const IO* __restrict__ qg = static_cast<const IO*>(p.q);
+  const IO* __restrict__ kg = static_cast<const IO*>(p.k);
+  const IO* __restrict__ vg = static_cast<const IO*>(p.v);
+  IO* __restrict__ og = static_cast<IO*>(p.out);
+  const size_t qk_stride = static_cast<size_t>(p.h_qk) * p.d_k;
+  const size_t qk_off = static_cast<size_t>(hq) * p.d_k + row0;
+  const size_t v_stride = static_cast<size_t>(p.h_v) * p.d_v;
+  const size_t v_off = static_cast<size_t>(h) * p.d_v + (col_ok ? j : 0);
+
+  // ---- gates: lane l holds (alpha, beta) of token blk + l
+  const IO* __restrict__ ga = static_cast<const IO*>(RAW ? p.gates.a : p.gates.g);
+  const IO* __restrict__ gb = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
+  float A_log = 0.0f, dt_bias = 0.0f;
+  if constexpr (RAW) {
+    if (t_begin < t_end) {  // the per-head parameters may be absent when no token needs them
+      A_log = p.gates.A_log[h];
+      dt_bias = p.gates.dt_bias[h];
+    }
+  }
+  RawScalar<IO> next_ga, next_gb;  // raw gate inputs of the next 64-token block
+  auto fetch_gate_block = [&](int blk) {
+    const int t = blk + lane;
+    if (t < t_end) {
+      next_ga.load(ga + static_cast<size_t>(t) * p.h_v + h);
+      next_gb.load(gb + static_cast<size_t>(t) * p.h_v + h);
+    } else {
+      next_ga.w = 0u;
+      next_gb.w = 0u;
+    }
+  };
+  float blk_alpha = 1.0f, blk_beta = 0.0f;
+  fetch_gate_block(t_begin);
+
+  // ---- q/k/v ring
+  RawSlice<IO, RPL> ring_k[kPrefetch], ring_q[kPrefetch];
+  RawScalar<IO> ring_v[kPrefetch];
+  auto fetch_token = [&](int slot, int t) {
+    const size_t qk = static_cast<size_t>(t) * qk_stride + qk_off;
+    if (full_rows) {
+      ring_k[slot].load(kg + qk);
+      ring_q[slot].load(qg + qk);
+    } else {
+      ring_k[slot].load_masked(kg + qk, row_limit);
+      ring_q[slot].load_masked(qg + qk, row_limit);
+    }
+    ring_v[slot].load(vg + static_cast<size_t>(t) * v_stride + v_off);
+  };
+#pragma unroll
+  for (int s = 0; s < kPrefetch; ++s)
+    if (t_begin + s < t_end) fetch_token(s, t_begin + s);
+
+  const float scale = p.scale;
+  for (int tb = t_begin; tb < t_end; tb += kPrefetch) {
+#pragma unroll
+    for (int s = 0; s < kPrefetch; ++s) {
+      const int t = tb + s;
+      if (t >= t_end) break;
+      const int rel = (t - t_begin) & (kWave - 1);
+      if (rel == 0) {
+        // gates of tokens t .. t + 63, one per lane, then prefetch the next block
+        if constexpr (RAW) {
+          const float gl = gate_log_decay(next_ga.value(), A_log, dt_bias);
+          blk_alpha = expf(gl);
+          blk_beta = gate_sigmoid(next_gb.value());
+        } else {
+          blk_alpha = expf(next_ga.value());
+          blk_beta = next_gb.value();
+        }
+        fetch_gate_block(t + kWave);
+      }
+      const float alpha = readlane(blk_alpha, rel);
+      const float beta = readlane(blk_beta, rel);
+
+      float kf[RPL], qf[RPL];
+      ring_k[s].widen_to(kf);
+      ring_q[s].widen_to(qf);
+      const float vv = ring_v[s].value();
+      if (t + kPrefetch < t_end) fetch_token(s, t + kPrefetch);
+
+      // retrieval against the decayed state: r = alpha * (S^T k)
+      float pr0 = 0.0f, pr1 = 0.0f;
+#pragma unroll
+      for (int m = 0; m < RPL; m += 2) {
+        pr0 = fmaf(S[m], kf[m], pr0);
+        if (m + 1 < RPL) pr1 = fmaf(S[m + 1], kf[m + 1], pr1);
+      }
+      const float rsum = group_sum<R>(pr0 + pr1);
+      const float delta = beta * (vv - alpha * rsum);
+
+      // decay + rank-1 update, and the readout partial of the updated state
+      float po0 = 0.0f, po1 = 0.0f;
+#pragma unroll
+      for (int m = 0; m < RPL; m += 2) {
+        S[m] = fmaf(S[m], alpha, kf[m] * delta);
+        po0 = fmaf(S[m], qf[m], po0);
+        if (m + 1 < RPL) {
+          S[m + 1] = fmaf(S[m + 1], alpha, kf[m + 1] * delta);
+          po1 = fmaf(S[m + 1], qf[m + 1], po1);
+        }
+      }
+      const float o = group_sum<R>(po0 + po1) * scale;
+      if (og != nullptr && r == 0 && col_ok)
+        narrow_store(og + static_cast<size_t>(t) * v_stride + v_off, o);
+    }
+  }
+
+  // ---- final state
+  if (p.sN != nullptr && col_ok) {
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      const int i = row0 + m;
+      if (i < p.d_k) p.sN[sbase + static_cast<size_t>(i) * p.d_v + j] = S[m];
+    }
+  }
+}
+
+template <typename IO, int DK>
+hipError_t launch_dk(const ScanParams& p, hipStream_t stream) {
+  const unsigned blocks = static_cast<unsigned>(p.num_seqs) * p.h_v * p.col_blocks;
+  if (blocks == 0) return hipSuccess;
+  if (p.gates.raw)
+    hipLaunchKernelGGL((scan_kernel<IO, DK, true>), dim3(blocks), dim3(kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL((scan_kernel<IO, DK, false>), dim3(blocks), dim3(kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
+  if (p.d_k <= 16) return launch_dk<IO, 16>(p, stream);
+  if (p.d_k <= 32) return launch_dk<IO, 32>(p, stream);
+  if (p.d_k <= 64) return launch_dk<IO, 64>(p, stream);
+  if (p.d_k <= 128) return launch_dk<IO, 128>(p, stream);
+  return launch_dk<IO, 256>(p, stream);
+}
+
+}  // namespace
+
+int scan_columns_per_wave(int d_k) {
+  if (d_k <= 16) return kWave / ScanShape<16>::R;
+  if (d_k <= 32) return kWave / ScanShape<32>::R;
+  if (d_k <= 64) return kWave / ScanShape<64>::R;
+  if (d_k <= 128) return kWave / ScanShape<128>::R;
+  return kWave / ScanShape<256>::R;
+}
+
+hipError_t launch_prefill_scan(ScanParams p, int io_bf16, hipStream_t stream) {
+  return io_bf16 ? launch_io<bf16_t>(p, stream) : launch_io<float>(p, stream);
+}
+
+}  // namespace gdn

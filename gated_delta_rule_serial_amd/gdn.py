@@ -1,0 +1,195 @@
+"""ctypes binding of libgdn (include/gdn.h).
+
+Argument marshalling only: tensors are turned into device pointers, shapes
+into the ``gdn_problem`` struct, and the C entry points of the same names are
+called on the current HIP stream.  Every step of the recurrence runs in the
+library's HIP kernels; there is no other code path.  If ``libgdn.so`` is not
+built, or no GPU is present, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "gdn.h")
+
+GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_F32, GDN_BF16 = 0, 1
+GDN_GATES_PRECOMPUTED, GDN_GATES_RAW = 0, 1
+
+_DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+
+class gdn_problem(ctypes.Structure):
+    _fields_ = [
+        ("h_qk", ctypes.c_int32), ("h_v", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("gate_mode", ctypes.c_int32),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgdn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_rule_serial_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    pp = ctypes.POINTER(gdn_problem)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.gdn_prefill.argtypes = [pp, i32, vp, ip, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_prefill.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_gate_prologue.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_gate_prologue.restype = ctypes.c_int
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def header_symbols(path: str = HEADER) -> list:
+    """Names of the functions include/gdn.h declares."""
+    with open(path) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(gdn_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def status_string(status: int) -> str:
+    return load().gdn_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().gdn_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(load().gdn_abi_version())
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libgdn takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr()) if t.data_ptr() else None
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def make_problem(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype, *, scale: float = 0.0,
+                 g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None) -> gdn_problem:
+    """Fill the ``gdn_problem`` struct.  Raw gates are used when ``a`` is given."""
+    if io_dtype not in _DTYPES:
+        raise ValueError(f"io dtype {io_dtype} is not supported")
+    raw = a is not None
+    return gdn_problem(h_qk, h_v, d_k, d_v, _DTYPES[io_dtype], float(scale),
+                       GDN_GATES_RAW if raw else GDN_GATES_PRECOMPUTED,
+                       _ptr(g), _ptr(beta), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias))
+
+
+def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                out: Optional[torch.Tensor], final_state: Optional[torch.Tensor],
+                initial_state: Optional[torch.Tensor] = None, g=None, beta=None, a=None, b=None,
+                A_log=None, dt_bias=None, scale: float = 0.0,
+                cu_seqlens_host: Optional[Sequence[int]] = None, stream=None) -> None:
+    """gdn_prefill of include/gdn.h: q, k [T, h_qk, d_k]; v, out [T, h_v, d_v];
+    cu_seqlens int32 [N+1] on the device; states float32 [N, h_v, d_k, d_v]."""
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
+                        A_log=A_log, dt_bias=dt_bias)
+    n = cu_seqlens.numel() - 1
+    host = None
+    if cu_seqlens_host is not None:
+        vals = [int(x) for x in cu_seqlens_host]
+        host = (ctypes.c_int32 * len(vals))(*vals)
+    _check(load().gdn_prefill(ctypes.byref(prob), n, _ptr(cu_seqlens), host, T, _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(initial_state), _ptr(out), _ptr(final_state), _stream(stream, q.device)))
+
+
+def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor,
+                    out: torch.Tensor, *, g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None,
+                    scale: float = 0.0, stream=None) -> None:
+    """gdn_decode_step of include/gdn.h: q, k [B, h_qk, d_k]; v, out [B, h_v, d_v];
+    state float32 [B, h_v, d_k, d_v], updated in place."""
+    B, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
+                        A_log=A_log, dt_bias=dt_bias)
+    _check(load().gdn_decode_step(ctypes.byref(prob), B, _ptr(q), _ptr(k), _ptr(v), _ptr(state), _ptr(out),
+                                  _stream(stream, q.device)))
+
+
+def gdn_gate_prologue(a: torch.Tensor, b: Optional[torch.Tensor], A_log: torch.Tensor, dt_bias: torch.Tensor,
+                      *, g: Optional[torch.Tensor], beta: Optional[torch.Tensor], stream=None) -> None:
+    """gdn_gate_prologue of include/gdn.h: a, b, g, beta [tokens, h_v]; A_log, dt_bias float32 [h_v]."""
+    tokens, h_v = a.shape
+    _check(load().gdn_gate_prologue(tokens, h_v, _DTYPES[a.dtype], _ptr(a), _ptr(b), _ptr(A_log),
+                                    _ptr(dt_bias), _ptr(g), _ptr(beta), _stream(stream, a.device)))
+
+
+# ----------------------------------------------------------------- helpers
+def prefill(q, k, v, cu_seqlens, *, initial_state=None, want_state=True, scale=0.0,
+            cu_seqlens_host=None, stream=None, **gates):
+    """Allocate ``out`` (and the final state) with torch and call gdn_prefill."""
+    T, _, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    n = cu_seqlens.numel() - 1
+    out = torch.empty(T, h_v, d_v, dtype=q.dtype, device=q.device)
+    fin = torch.empty(n, h_v, d_k, d_v, dtype=torch.float32, device=q.device) if want_state else None
+    gdn_prefill(q, k, v, cu_seqlens, out=out, final_state=fin, initial_state=initial_state, scale=scale,
+                cu_seqlens_host=cu_seqlens_host, stream=stream, **gates)
+    return out, fin
+
+
+def decode_step(q, k, v, state, *, scale=0.0, stream=None, **gates):
+    """Allocate ``out`` with torch and call gdn_decode_step (state updated in place)."""
+    out = torch.empty(q.shape[0], v.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
+    gdn_decode_step(q, k, v, state, out, scale=scale, stream=stream, **gates)
+    return out
+
+
+def gate_prologue(a, b, A_log, dt_bias, *, stream=None):
+    """Allocate g and beta with torch and call gdn_gate_prologue."""
+    g = torch.empty_like(a)
+    beta = torch.empty_like(b)
+    gdn_gate_prologue(a, b, A_log, dt_bias, g=g, beta=beta, stream=stream)
+    return g, beta

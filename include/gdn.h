@@ -1,0 +1,161 @@
+/*
+ * gdn.h -- C ABI of libgdn, the gated delta-rule (Gated DeltaNet) recurrence
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per value head h, per token t of a sequence, state S of
+ * d_k x d_v held in float32 whatever the I/O dtype):
+ *     S   <- exp(g_t) S                         decay
+ *     r    = S^T k_t                            retrieval
+ *     S   <- S + k_t (beta_t (v_t - r))^T       delta update
+ *     o_t  = scale S^T q_t                      readout of the UPDATED state
+ * as defined on the pages
+ *   [P4] onnx-runtime-ep-cuda 0.1.0-dev.6, src/kernels/linear_attention.rs:
+ *        module doc "Parallelization" and `linear_attention_core` steps 1-4;
+ *   [P1] onnxruntime-ep-mlx 0.31.1, src/ops/ssm.rs: `linear_attention_op`;
+ *   [P3] nuvec-core 0.6.1, fast/imp.rs: `gated_delta` / `gated_delta_graph`.
+ * The float32 working state follows [P4]'s module doc (widen on read, narrow
+ * on write) and [P1]'s wide scan; narrowing to bfloat16 rounds to nearest
+ * even, once per stored element.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     keeps no pointer after a call returns and allocates no device memory.
+ *   - Tensors are dense row-major with the layouts given below, and every
+ *     tensor pointer is 16-byte aligned (GDN_ERR_INVALID_ARGUMENT otherwise).
+ *   - Work is enqueued on `stream` and the call returns without waiting;
+ *     nothing in the library synchronises the device, so calls may be
+ *     captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     non-OK status nothing was enqueued and gdn_last_error() describes why.
+ *   - Value head h reads query/key head h / (h_v / h_qk): each q/k head
+ *     serves a run of consecutive value heads ([P4] inverse-GQA branch of
+ *     `linear_attention_core`; [P3] `gated_delta_graph`).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+/* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
+#define GDN_MAX_HEAD_DIM 256
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARGUMENT = 1, /* shape, pointer, alignment or value error  */
+  GDN_ERR_UNSUPPORTED = 2,      /* well-formed but outside what is built     */
+  GDN_ERR_HIP = 3               /* a HIP runtime call failed (launch, attrs) */
+} gdn_status;
+
+typedef enum gdn_dtype {
+  GDN_F32 = 0,
+  GDN_BF16 = 1
+} gdn_dtype;
+
+/* How the per-token gates reach the recurrence. */
+typedef enum gdn_gate_mode {
+  /* g (log-decay, alpha = exp(g)) and beta are given per token and value head. */
+  GDN_GATES_PRECOMPUTED = 0,
+  /* The gate prologue runs inside the kernel, in float32 with no intermediate
+   * rounding ([P4] fused sigmoid / softplus branch of `linear_attention_core`;
+   * [P1] `linear_attention_gate_op`):
+   *     beta = sigmoid(b),   g = -exp(A_log) * softplus(a + dt_bias)        */
+  GDN_GATES_RAW = 1
+} gdn_gate_mode;
+
+/* Geometry and gate inputs of one call. */
+typedef struct gdn_problem {
+  int32_t h_qk;     /* query/key heads, >= 1                                  */
+  int32_t h_v;      /* value (state, output) heads, a multiple of h_qk       */
+  int32_t d_k;      /* key/query head size, 1 .. GDN_MAX_HEAD_DIM            */
+  int32_t d_v;      /* value head size, 1 .. GDN_MAX_HEAD_DIM                */
+  int32_t io_dtype; /* gdn_dtype of q, k, v, out, g, beta, a, b              */
+  float scale;      /* readout scale; 0 selects 1/sqrt(d_k) ([P4] factory)   */
+  int32_t gate_mode;    /* gdn_gate_mode                                     */
+  const void* g;        /* PRECOMPUTED: [tokens, h_v] io_dtype, log-decay    */
+  const void* beta;     /* PRECOMPUTED: [tokens, h_v] io_dtype               */
+  const void* a;        /* RAW: [tokens, h_v] io_dtype                       */
+  const void* b;        /* RAW: [tokens, h_v] io_dtype                       */
+  const float* A_log;   /* RAW: [h_v] float32                                */
+  const float* dt_bias; /* RAW: [h_v] float32                                */
+} gdn_problem;
+
+/*
+ * gdn_prefill -- the recurrence over packed variable-length sequences.
+ *
+ *   cu_seqlens      device int32 [num_seqs + 1]: sequence n owns tokens
+ *                   cu_seqlens[n] .. cu_seqlens[n+1]-1.  Required:
+ *                   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[num_seqs]
+ *                   = total_tokens.  The device copy is not read back, so
+ *                   these are checked only through cu_seqlens_host.
+ *   cu_seqlens_host optional host copy of the same values (NULL allowed).
+ *                   When given it is validated and used to start the longest
+ *                   sequences first.
+ *   q, k            [total_tokens, h_qk, d_k] io_dtype
+ *   v               [total_tokens, h_v, d_v] io_dtype
+ *   initial_state   [num_seqs, h_v, d_k, d_v] float32, or NULL for zeros
+ *   out             [total_tokens, h_v, d_v] io_dtype, or NULL (not written)
+ *   final_state     [num_seqs, h_v, d_k, d_v] float32, or NULL (not
+ *                   returned).  It may be the same pointer as initial_state
+ *                   (each state slice is read before it is written) but must
+ *                   not overlap it otherwise.
+ * A sequence with no tokens returns its initial state (zeros without one)
+ * ([P1] zero-length time axis).  total_tokens == 0 is valid.
+ */
+gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs,
+                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                       int32_t total_tokens, const void* q, const void* k,
+                       const void* v, const float* initial_state, void* out,
+                       float* final_state, hipStream_t stream);
+
+/*
+ * gdn_decode_step -- one token for each of `batch` sequences, with the state
+ * resident in device memory and updated in place.
+ *
+ *   q, k   [batch, h_qk, d_k] io_dtype
+ *   v      [batch, h_v, d_v] io_dtype
+ *   state  [batch, h_v, d_k, d_v] float32, read and overwritten
+ *   out    [batch, h_v, d_v] io_dtype
+ * Gate tensors of `problem` are [batch, h_v].
+ * Same result as gdn_prefill with cu_seqlens = {0, 1, ..., batch} and
+ * final_state == initial_state == state.
+ */
+gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch,
+                           const void* q, const void* k, const void* v,
+                           float* state, void* out, hipStream_t stream);
+
+/*
+ * gdn_gate_prologue -- the gate prologue alone ([P1] `linear_attention_gate_op`,
+ * [P4] fused gate branch), for callers that feed precomputed gates:
+ *     g[t,h] = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])
+ *     beta[t,h] = sigmoid(b[t,h])
+ * computed in float32 and narrowed once to io_dtype.
+ *   a, b        [tokens, h_v] io_dtype (b may be NULL when beta is NULL)
+ *   A_log, dt_bias [h_v] float32
+ *   g, beta     [tokens, h_v] io_dtype outputs; either may be NULL.
+ */
+gdn_status gdn_gate_prologue(int32_t tokens, int32_t h_v, int32_t io_dtype,
+                             const void* a, const void* b, const float* A_log,
+                             const float* dt_bias, void* g, void* beta,
+                             hipStream_t stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* gdn_last_error(void);
+
+/* Fixed name of a status code. */
+const char* gdn_status_string(gdn_status status);
+
+/* GDN_ABI_VERSION of the built library. */
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,103 @@
+"""Shared plumbing of the GPU parity tests: run the same seeded inputs through
+the HIP library (via its C ABI binding) and through the oracle, and compare
+element by element.
+
+Gates for workloads with precomputed gates come from the oracle's gate
+prologue (double) rounded once to the I/O dtype; both sides then read the same
+rounded values.  Workloads with raw gates hand (a, b, A_log, dt_bias) to the
+library, and the oracle's gate prologue of the same values to the oracle.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from gated_delta_rule_serial_amd import gdn, synth
+
+# Tolerances: |gpu - ref| <= tol (1 + |ref|) elementwise.
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gates_for(inp: synth.Inputs):
+    """(g, beta) in the I/O dtype for precomputed-gate workloads, from the oracle."""
+    g, beta = oracle.default().gates(inp.a, inp.b, inp.A_log, inp.dt_bias)
+    dt = inp.shape.io_dtype
+    return torch.from_numpy(g).to(dt), torch.from_numpy(beta).to(dt)
+
+
+def to_dev(t, dev="cuda"):
+    return None if t is None else t.contiguous().to(dev)
+
+
+def gpu_prefill(inp: synth.Inputs, g=None, beta=None, *, raw=False, scale=0.0, want_out=True,
+                want_state=True, in_place=False, use_host_cu=True):
+    """Run gdn_prefill on cuda:0; returns (out, final) as CPU float64 tensors (or None)."""
+    dev = "cuda"
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    cu = to_dev(inp.cu_seqlens)
+    n = len(inp.seqlens)
+    T = inp.total_tokens
+    h_v, d_k, d_v = inp.shape.h_v, inp.shape.d_k, inp.shape.d_v
+    s0 = to_dev(inp.initial_state)
+    out = torch.full((T, h_v, d_v), float("nan"), dtype=inp.shape.io_dtype, device=dev) if want_out else None
+    if in_place:
+        assert s0 is not None
+        fin = s0
+    else:
+        fin = torch.full((n, h_v, d_k, d_v), float("nan"), dtype=torch.float32, device=dev) if want_state else None
+    gates = (dict(a=to_dev(inp.a), b=to_dev(inp.b), A_log=to_dev(inp.A_log), dt_bias=to_dev(inp.dt_bias))
+             if raw else dict(g=to_dev(g), beta=to_dev(beta)))
+    gdn.gdn_prefill(q, k, v, cu, out=out, final_state=fin, initial_state=s0, scale=scale,
+                    cu_seqlens_host=inp.cu_seqlens.tolist() if use_host_cu else None, **gates)
+    torch.cuda.synchronize()
+    return (None if out is None else out.double().cpu(), None if fin is None else fin.double().cpu())
+
+
+def oracle_prefill(inp: synth.Inputs, g=None, beta=None, *, raw=False, scale=0.0, heads=None):
+    """Oracle on all heads, or on the q/k head groups listed in ``heads``
+    (each group = one q/k head and its consecutive value heads)."""
+    orc = oracle.default()
+    if raw:
+        g, beta = orc.gates(inp.a, inp.b, inp.A_log, inp.dt_bias)
+    else:
+        g, beta = g.double().numpy(), beta.double().numpy()
+    q, k, v = inp.q.double().numpy(), inp.k.double().numpy(), inp.v.double().numpy()
+    s0 = None if inp.initial_state is None else inp.initial_state.double().numpy()
+    cu = inp.cu_seqlens.numpy()
+    if heads is None:
+        o, f = orc.prefill(q, k, v, g, beta, cu, s0, scale=scale)
+        return torch.from_numpy(o), torch.from_numpy(f)
+    ratio = inp.shape.h_v // inp.shape.h_qk
+    res = {}
+    for hq in heads:
+        hv = slice(hq * ratio, (hq + 1) * ratio)
+        o, f = orc.prefill(q[:, hq:hq + 1], k[:, hq:hq + 1], v[:, hv], g[:, hv], beta[:, hv], cu,
+                           None if s0 is None else s0[:, hv], scale=scale)
+        res[hq] = (torch.from_numpy(o), torch.from_numpy(f))
+    return res
+
+
+def max_err(gpu: torch.Tensor, ref: torch.Tensor) -> float:
+    gpu = gpu.double()
+    ref = ref.double()
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    if gpu.numel() == 0:
+        return 0.0
+    assert torch.isfinite(gpu).all(), "non-finite values in the GPU result (an element was not written?)"
+    return float(((gpu - ref).abs() / (1.0 + ref.abs())).max())
+
+
+def check(gpu, ref, tol, what):
+    e = max_err(gpu, ref)
+    rel = float((gpu.double() - ref.double()).norm() / max(ref.double().norm(), 1e-300)) if ref.numel() else 0.0
+    say(f"    {what}: max |d|/(1+|ref|) = {e:.3e}  (tol {tol:.0e}), ||d||/||ref|| = {rel:.3e}")
+    assert e <= tol, f"{what}: {e:.3e} > {tol:.0e}"
+    return e

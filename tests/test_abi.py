@@ -1,0 +1,145 @@
+"""The C ABI on the CPU: the library loads, exports what include/gdn.h
+declares, and rejects malformed calls on the host with the documented status
+before anything reaches a GPU.  Every call here fails validation, so no
+device work is ever attempted."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from gated_delta_rule_serial_amd import gdn
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gdn.LIB_PATH), reason="libgdn.so not built")
+
+FAKE = 0x100000  # 16-byte aligned non-null address; never dereferenced by validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = gdn.header_symbols()
+    assert set(declared) >= {"gdn_prefill", "gdn_decode_step", "gdn_gate_prologue", "gdn_last_error",
+                             "gdn_status_string", "gdn_abi_version"}
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in include/gdn.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == set(declared), f"exported functions {sorted(exported)} != declared {declared}"
+
+
+def test_version_and_status_strings(lib):
+    assert gdn.abi_version() == 1
+    assert gdn.status_string(0) == "GDN_OK"
+    assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
+    assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
+    assert gdn.status_string(3) == "GDN_ERR_HIP"
+    assert gdn.status_string(99) == "GDN_STATUS_UNKNOWN"
+
+
+def _prob(**kw):
+    base = dict(h_qk=2, h_v=4, d_k=16, d_v=16, io_dtype=gdn.GDN_F32, scale=0.0,
+                gate_mode=gdn.GDN_GATES_PRECOMPUTED, g=FAKE, beta=FAKE + 0x1000, a=None, b=None,
+                A_log=None, dt_bias=None)
+    base.update(kw)
+    return gdn.gdn_problem(**base)
+
+
+def _prefill(lib, prob, *, n=1, cu=FAKE + 0x2000, cu_host=None, T=8, q=FAKE + 0x10000, k=FAKE + 0x20000,
+             v=FAKE + 0x30000, s0=None, out=FAKE + 0x40000, sN=FAKE + 0x50000):
+    host = None
+    if cu_host is not None:
+        host = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    vp = ctypes.c_void_p
+    return lib.gdn_prefill(ctypes.byref(prob) if prob is not None else None, n, vp(cu) if cu else None, host, T,
+                           vp(q) if q else None, vp(k) if k else None, vp(v) if v else None,
+                           vp(s0) if s0 else None, vp(out) if out else None, vp(sN) if sN else None, None)
+
+
+INVALID, UNSUPPORTED = gdn.GDN_ERR_INVALID_ARGUMENT, gdn.GDN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("label,prob_kw,call_kw,status,needle", [
+    ("null problem", None, {}, INVALID, "problem is NULL"),
+    ("zero heads", dict(h_qk=0), {}, INVALID, "head counts"),
+    ("head ratio", dict(h_qk=3, h_v=4), {}, INVALID, "not a multiple"),
+    ("zero d_k", dict(d_k=0), {}, INVALID, "head sizes must be positive"),
+    ("d_k too large", dict(d_k=257), {}, UNSUPPORTED, "above 256"),
+    ("d_v too large", dict(d_v=512), {}, UNSUPPORTED, "above 256"),
+    ("dtype", dict(io_dtype=7), {}, UNSUPPORTED, "io_dtype"),
+    ("nan scale", dict(scale=float("nan")), {}, INVALID, "scale"),
+    ("missing g", dict(g=None), {}, INVALID, "precomputed gates"),
+    ("missing raw", dict(gate_mode=gdn.GDN_GATES_RAW, a=FAKE), {}, INVALID, "raw gates"),
+    ("bad gate mode", dict(gate_mode=5), {}, INVALID, "gate_mode"),
+    ("misaligned g", dict(g=FAKE + 2), {}, INVALID, "aligned"),
+    ("negative seqs", {}, dict(n=-1), INVALID, "negative"),
+    ("negative tokens", {}, dict(T=-1), INVALID, "negative"),
+    ("tokens without seqs", {}, dict(n=0, T=4), INVALID, "no sequences"),
+    ("null cu", {}, dict(cu=0), INVALID, "cu_seqlens is NULL"),
+    ("null q", {}, dict(q=0), INVALID, "required"),
+    ("misaligned q", {}, dict(q=FAKE + 0x10004), INVALID, "16-byte"),
+    ("misaligned state", {}, dict(s0=FAKE + 0x60008), INVALID, "16-byte"),
+    ("cu not from 0", {}, dict(cu_host=[1, 8]), INVALID, "expected 0"),
+    ("cu decreasing", {}, dict(n=2, cu_host=[0, 5, 4]), INVALID, "decreases"),
+    ("cu total", {}, dict(cu_host=[0, 7]), INVALID, "total_tokens"),
+    ("state partial overlap", {}, dict(s0=FAKE + 0x50000, sN=FAKE + 0x50010), INVALID, "partially overlaps"),
+    ("out overlaps q", {}, dict(out=FAKE + 0x10000), INVALID, "out overlaps"),
+])
+def test_prefill_validation(lib, label, prob_kw, call_kw, status, needle):
+    prob = None if prob_kw is None else _prob(**prob_kw)
+    st = _prefill(lib, prob, **call_kw)
+    assert st == status, f"{label}: status {st}, message {gdn.last_error()!r}"
+    assert needle in gdn.last_error(), f"{label}: message {gdn.last_error()!r}"
+
+
+def test_prefill_nothing_to_do_is_ok(lib):
+    # no sequences at all: OK without any launch
+    assert _prefill(lib, _prob(), n=0, T=0, cu=0, q=0, k=0, v=0, out=0, sN=0) == gdn.GDN_OK
+    assert gdn.last_error() == ""
+
+
+@pytest.mark.parametrize("label,prob_kw,args,status,needle", [
+    ("negative batch", {}, dict(B=-1), INVALID, "negative"),
+    ("null state", {}, dict(state=0), INVALID, "required"),
+    ("misaligned out", {}, dict(out=FAKE + 0x40002), INVALID, "16-byte"),
+    ("out overlaps state", {}, dict(out=FAKE + 0x50000), INVALID, "overlaps"),
+    ("state overlaps q", {}, dict(state=FAKE + 0x10000), INVALID, "overlaps"),
+    ("ratio", dict(h_qk=3), {}, INVALID, "not a multiple"),
+])
+def test_decode_validation(lib, label, prob_kw, args, status, needle):
+    a = dict(B=4, q=FAKE + 0x10000, k=FAKE + 0x20000, v=FAKE + 0x30000, state=FAKE + 0x50000,
+             out=FAKE + 0x40000)
+    a.update(args)
+    vp = ctypes.c_void_p
+    st = lib.gdn_decode_step(ctypes.byref(_prob(**prob_kw)), a["B"], vp(a["q"]), vp(a["k"]), vp(a["v"]),
+                             vp(a["state"]) if a["state"] else None, vp(a["out"]), None)
+    assert st == status, f"{label}: status {st}, message {gdn.last_error()!r}"
+    assert needle in gdn.last_error()
+
+
+def test_decode_empty_batch_is_ok(lib):
+    assert lib.gdn_decode_step(ctypes.byref(_prob()), 0, None, None, None, None, None, None) == gdn.GDN_OK
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(tokens=-1), INVALID, "tokens"),
+    (dict(h_v=0), INVALID, "h_v"),
+    (dict(dtype=3), UNSUPPORTED, "io_dtype"),
+    (dict(a=0), INVALID, "g needs"),
+    (dict(b=0), INVALID, "beta needs"),
+    (dict(g=FAKE + 0x40001), INVALID, "aligned"),
+])
+def test_gate_prologue_validation(lib, args, status, needle):
+    a = dict(tokens=8, h_v=4, dtype=gdn.GDN_BF16, a=FAKE, b=FAKE + 0x1000, A_log=FAKE + 0x2000,
+             dt_bias=FAKE + 0x3000, g=FAKE + 0x4000, beta=FAKE + 0x5000)
+    a.update(args)
+    vp = ctypes.c_void_p
+    st = lib.gdn_gate_prologue(a["tokens"], a["h_v"], a["dtype"], *(vp(a[x]) if a[x] else None for x in
+                                                                      ("a", "b", "A_log", "dt_bias", "g", "beta")),
+                               None)
+    assert st == status, gdn.last_error()
+    assert needle in gdn.last_error()

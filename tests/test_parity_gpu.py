@@ -1,0 +1,265 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle, element
+by element, on seeded synthetic inputs.
+
+Reduced sizes cover every workload's geometry with ragged tails (token counts
+that are not multiples of the 4-token prefetch ring or the 64-token gate
+block, column counts that are not multiples of a wave's column block).  The
+full-size cases run the library exactly as the benchmark launches it and
+compare sampled (q/k head group) slices that the oracle computes alone.
+
+Tolerance: |gpu - ref| <= tol (1 + |ref|) elementwise, tol = 1e-4 for float32
+I/O and 1e-2 for bfloat16 I/O.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_serial_amd import gdn, synth
+from gpu_harness import TOL, check, gates_for, gpu_prefill, oracle_prefill, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = synth.BY_NAME
+
+
+def _shape(base="tiny_prefill", **kw):
+    return dataclasses.replace(W[base], **kw)
+
+
+# ------------------------------------------------------------------ prefill, reduced sizes
+PREFILL_CASES = [
+    ("tiny_prefill", {}),
+    ("prefill_t4096_fused_gates", dict(seqlen=200)),
+    ("varlen_prefill_8seq", dict(seqlens=[37, 0, 129, 64, 1, 250, 3])),
+    ("wide_prefill_t32768_d256", dict(seqlen=97)),
+]
+
+
+@pytest.mark.parametrize("name,over", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_workload_geometry(name, over):
+    shape = W[name]
+    say(f"[prefill] {name} {over}")
+    inp = synth.generate(shape, **over)
+    raw = shape.gate_mode == "raw"
+    g, beta = (None, None) if raw else gates_for(inp)
+    out, fin = gpu_prefill(inp, g, beta, raw=raw)
+    ro, rf = oracle_prefill(inp, g, beta, raw=raw)
+    tol = TOL[shape.io_dtype]
+    check(out, ro, tol, "out")
+    check(fin, rf, tol, "final state")
+
+
+GEOMETRIES = [
+    # (h_qk, h_v, d_k, d_v, dtype, seqlens)
+    (1, 1, 1, 1, torch.float32, [5, 9]),
+    (1, 4, 48, 40, torch.bfloat16, [70, 0, 13]),
+    (2, 2, 100, 130, torch.float32, [66]),
+    (3, 6, 256, 256, torch.bfloat16, [21, 2]),
+    (1, 1, 16, 3, torch.float32, [130]),
+    (4, 8, 64, 64, torch.bfloat16, [65, 64, 63]),
+    (1, 2, 32, 200, torch.float32, [9, 17]),
+    (2, 4, 128, 128, torch.float32, [1, 2, 3, 4, 5, 6, 7, 8, 9, 10]),
+]
+
+
+@pytest.mark.parametrize("geom", GEOMETRIES, ids=lambda g: f"hq{g[0]}_hv{g[1]}_dk{g[2]}_dv{g[3]}_{str(g[4])[6:]}")
+@pytest.mark.parametrize("raw", [False, True], ids=["gates", "rawgates"])
+def test_prefill_geometry(geom, raw):
+    h_qk, h_v, d_k, d_v, dt, lens = geom
+    shape = _shape(h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v, io_dtype=dt, init_state=True,
+                   gate_mode="raw" if raw else "precomputed")
+    say(f"[prefill-geom] {geom} raw={raw}")
+    inp = synth.generate(shape, seqlens=lens, seed=77)
+    g, beta = (None, None) if raw else gates_for(inp)
+    out, fin = gpu_prefill(inp, g, beta, raw=raw)
+    ro, rf = oracle_prefill(inp, g, beta, raw=raw)
+    check(out, ro, TOL[dt], "out")
+    check(fin, rf, TOL[dt], "final state")
+
+
+def test_prefill_options():
+    """Explicit scale, in-place state, out or state omitted, no host cu_seqlens."""
+    shape = _shape("varlen_prefill_8seq", init_state=True)
+    inp = synth.generate(shape, seqlens=[40, 3, 0, 77])
+    g, beta = gates_for(inp)
+    ro, rf = oracle_prefill(inp, g, beta, scale=0.3)
+    tol = TOL[shape.io_dtype]
+    say("[prefill-options] scale 0.3 + in place")
+    out, fin = gpu_prefill(inp, g, beta, scale=0.3, in_place=True)
+    check(out, ro, tol, "out (in place)")
+    check(fin, rf, tol, "state (in place)")
+    say("[prefill-options] state only, no host cu")
+    out, fin = gpu_prefill(inp, g, beta, scale=0.3, want_out=False, use_host_cu=False)
+    assert out is None
+    check(fin, rf, tol, "state only")
+    say("[prefill-options] out only")
+    out, fin = gpu_prefill(inp, g, beta, scale=0.3, want_state=False)
+    assert fin is None
+    check(out, ro, tol, "out only")
+
+
+def test_prefill_no_tokens_returns_initial_state():
+    shape = _shape(init_state=True)
+    inp = synth.generate(shape, seqlens=[0, 0, 0])
+    g, beta = gates_for(inp)
+    say("[prefill-empty] three empty sequences")
+    out, fin = gpu_prefill(inp, g, beta)
+    assert out.shape[0] == 0
+    assert torch.equal(fin, inp.initial_state.double())
+    shape0 = _shape(init_state=False)
+    inp0 = synth.generate(shape0, seqlens=[0, 4, 0])
+    g0, b0 = gates_for(inp0)
+    out0, fin0 = gpu_prefill(inp0, g0, b0)
+    assert torch.equal(fin0[0], torch.zeros_like(fin0[0])) and torch.equal(fin0[2], torch.zeros_like(fin0[2]))
+
+
+def test_rounding_tie_to_even():
+    """q = k = e0, g = 0, beta = 1/2, S0 = e0 e0^T, v = 1.0078125, scale 1, bf16 I/O:
+    the exact outputs 1.00390625 (a bf16 tie) and 1.005859375 round to 1.0 and
+    1.0078125.  Prefill and two decode steps."""
+    d = 16
+    q = torch.zeros(2, 1, d)
+    q[:, 0, 0] = 1.0
+    v = torch.zeros(2, 1, d)
+    v[:, 0, 0] = 1.0078125
+    s0 = torch.zeros(1, 1, d, d)
+    s0[0, 0, 0, 0] = 1.0
+    bf = torch.bfloat16
+    dev = "cuda"
+    g = torch.zeros(2, 1, dtype=bf, device=dev)
+    beta = torch.full((2, 1), 0.5, dtype=bf, device=dev)
+    qd = q.to(bf).to(dev)
+    say("[rounding] prefill")
+    out, fin = gdn.prefill(qd, qd, v.to(bf).to(dev), torch.tensor([0, 2], dtype=torch.int32, device=dev),
+                           initial_state=s0.to(dev), g=g, beta=beta, scale=1.0)
+    torch.cuda.synchronize()
+    assert out[:, 0, 0].float().tolist() == [1.0, 1.0078125]
+    assert fin[0, 0, 0, 0].item() == 1.005859375
+    say("[rounding] decode")
+    st = s0.to(dev).clone()
+    outs = [gdn.decode_step(qd[t:t + 1], qd[t:t + 1], v[t:t + 1].to(bf).to(dev), st, g=g[t:t + 1],
+                            beta=beta[t:t + 1], scale=1.0) for t in range(2)]
+    torch.cuda.synchronize()
+    assert [o[0, 0, 0].item() for o in outs] == [1.0, 1.0078125]
+    assert st[0, 0, 0, 0].item() == 1.005859375
+
+
+# ------------------------------------------------------------------ decode
+def _decode_inputs(shape, seed):
+    inp = synth.generate(shape, seed=seed)
+    g, beta = gates_for(inp)
+    return inp, g, beta
+
+
+@pytest.mark.parametrize("raw", [False, True], ids=["gates", "rawgates"])
+def test_decode_b64_full(raw):
+    """The decode workload at its full size (B = 64), three chained steps."""
+    shape = W["decode_b64"]
+    say(f"[decode] B=64 full, raw={raw}")
+    inp0 = synth.generate(shape)
+    st_gpu = to_dev(inp0.initial_state).clone()
+    st_ref = inp0.initial_state.double().numpy().copy()
+    orc = oracle.default()
+    tol = TOL[shape.io_dtype]
+    for step in range(3):
+        inp = synth.generate(shape, seed=5000 + step)
+        if raw:
+            gates = dict(a=to_dev(inp.a), b=to_dev(inp.b), A_log=to_dev(inp.A_log), dt_bias=to_dev(inp.dt_bias))
+            gr, br = orc.gates(inp.a, inp.b, inp.A_log, inp.dt_bias)
+        else:
+            g, beta = gates_for(inp)
+            gates = dict(g=to_dev(g), beta=to_dev(beta))
+            gr, br = g.double().numpy(), beta.double().numpy()
+        out = gdn.decode_step(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), st_gpu, **gates)
+        torch.cuda.synchronize()
+        ro = orc.decode_step(inp.q.double().numpy(), inp.k.double().numpy(), inp.v.double().numpy(), gr, br, st_ref)
+        check(out.double().cpu(), torch.from_numpy(ro), tol, f"out step {step}")
+        check(st_gpu.double().cpu(), torch.from_numpy(st_ref), tol, f"state step {step}")
+
+
+DECODE_GEOMS = [
+    (1, 1, 16, 16, torch.float32, 3),
+    (2, 4, 48, 40, torch.bfloat16, 5),
+    (1, 1, 256, 256, torch.float32, 2),
+    (3, 6, 100, 130, torch.bfloat16, 4),
+    (1, 2, 1, 1, torch.float32, 7),
+    (2, 2, 128, 66, torch.float32, 3),
+]
+
+
+@pytest.mark.parametrize("geom", DECODE_GEOMS, ids=lambda g: f"hq{g[0]}_hv{g[1]}_dk{g[2]}_dv{g[3]}_B{g[5]}")
+def test_decode_geometry(geom):
+    h_qk, h_v, d_k, d_v, dt, B = geom
+    shape = _shape("decode_b64", h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v, io_dtype=dt, num_seqs=B)
+    say(f"[decode-geom] {geom}")
+    inp, g, beta = _decode_inputs(shape, 91)
+    st = to_dev(inp.initial_state).clone()
+    out = gdn.decode_step(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), st, g=to_dev(g), beta=to_dev(beta))
+    torch.cuda.synchronize()
+    ref_state = inp.initial_state.double().numpy().copy()
+    ro = oracle.default().decode_step(inp.q.double().numpy(), inp.k.double().numpy(), inp.v.double().numpy(),
+                                      g.double().numpy(), beta.double().numpy(), ref_state)
+    check(out.double().cpu(), torch.from_numpy(ro), TOL[dt], "out")
+    check(st.double().cpu(), torch.from_numpy(ref_state), TOL[dt], "state")
+
+
+def test_decode_steps_equal_prefill():
+    """T decode steps of one sequence reproduce a T-token prefill."""
+    shape = _shape("varlen_prefill_8seq", init_state=True)
+    inp = synth.generate(shape, seqlens=[6])
+    g, beta = gates_for(inp)
+    say("[decode-vs-prefill] 6 steps")
+    out_p, fin_p = gpu_prefill(inp, g, beta)
+    st = to_dev(inp.initial_state).clone()
+    outs = []
+    for t in range(6):
+        outs.append(gdn.decode_step(to_dev(inp.q[t:t + 1]), to_dev(inp.k[t:t + 1]), to_dev(inp.v[t:t + 1]), st,
+                                    g=to_dev(g[t:t + 1]), beta=to_dev(beta[t:t + 1])))
+    torch.cuda.synchronize()
+    tol = TOL[shape.io_dtype]
+    check(torch.cat(outs).double().cpu(), out_p, tol, "decode vs prefill out")
+    check(st.double().cpu(), fin_p, tol, "decode vs prefill state")
+
+
+# ------------------------------------------------------------------ gate prologue
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_gate_prologue(dt):
+    shape = _shape("prefill_t4096_fused_gates", io_dtype=dt)
+    inp = synth.generate(shape, seqlen=333)
+    say(f"[gates] {dt}")
+    g, beta = gdn.gate_prologue(to_dev(inp.a), to_dev(inp.b), to_dev(inp.A_log), to_dev(inp.dt_bias))
+    torch.cuda.synchronize()
+    rg, rb = oracle.default().gates(inp.a, inp.b, inp.A_log, inp.dt_bias)
+    check(g.double().cpu(), torch.from_numpy(rg), TOL[dt], "g")
+    check(beta.double().cpu(), torch.from_numpy(rb), TOL[dt], "beta")
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+FULL = [
+    ("prefill_t4096_fused_gates", [0, 15]),
+    ("varlen_prefill_8seq", [0, 7, 15]),
+    ("wide_prefill_t32768_d256", [0, 5]),
+]
+
+
+@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
+def test_prefill_full_size_sampled(name, heads):
+    """The full workload as the benchmark runs it; the oracle recomputes the
+    listed q/k head groups (all their value heads, every token) on their own."""
+    shape = W[name]
+    inp = synth.generate(shape)
+    say(f"[full] {name}: {len(inp.seqlens)} seqs, {inp.total_tokens} tokens; oracle on head groups {heads}")
+    raw = shape.gate_mode == "raw"
+    g, beta = (None, None) if raw else gates_for(inp)
+    out, fin = gpu_prefill(inp, g, beta, raw=raw)
+    ref = oracle_prefill(inp, g, beta, raw=raw, heads=heads)
+    ratio = shape.h_v // shape.h_qk
+    tol = TOL[shape.io_dtype]
+    for hq, (ro, rf) in ref.items():
+        hv = slice(hq * ratio, (hq + 1) * ratio)
+        check(out[:, hv], ro, tol, f"out head group {hq}")
+        check(fin[:, hv], rf, tol, f"state head group {hq}")
+    assert torch.isfinite(out).all() and torch.isfinite(fin).all()
