@@ -256,6 +256,26 @@ def bench_prefill(shape, steps, warmup, want_cpu):
     return line
 
 
+def bench_copy(mib, steps, warmup):
+    """A plain device copy of known size (dst.copy_(src), mib MiB each way): the
+    reference kernel that scales the rocprofv3 HBM byte counters."""
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"metric": "device copy", "value": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 6), "bytes_read": n * 4, "bytes_written": n * 4}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +283,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_b64", choices=sorted(synth.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="time a plain device copy of this many MiB instead (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the gated delta-rule path here runs on a single MI355X "
@@ -272,6 +294,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib:
+        print(json.dumps(bench_copy(args.copy_mib, args.steps or 50, args.warmup or 5)), flush=True)
+        return
     shape = synth.BY_NAME[args.workload]
     decode = shape.kind == "decode"
     steps = args.steps if args.steps is not None else (1000 if decode else 10)

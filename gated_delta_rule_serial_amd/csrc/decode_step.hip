@@ -18,7 +18,8 @@
 // DK / 16.  A wave's load instruction covers 4 rows x 256 contiguous bytes.
 // The column sums over the 16 row groups go through LDS; one wave finishes
 // them, writes o and broadcasts delta through LDS; every thread then writes
-// its tile.  The state traffic (read + write once) is the kernel's HBM cost.
+// its tile.  The state traffic (read + write once) is the kernel's HBM cost;
+// it uses non-temporal 16-byte accesses, since no state byte is reused.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   for (int m = 0; m < RPT; ++m) {
     const int i = row0 + m;
     if (i < d_k && vec_cols) {
-      const float4 x = *reinterpret_cast<const float4*>(Sg + static_cast<size_t>(i) * d_v + j0);
+      const float4 x = load_stream4(Sg + static_cast<size_t>(i) * d_v + j0);
       S[m][0] = x.x;
       S[m][1] = x.y;
       S[m][2] = x.z;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int cc = 0; cc < kColsPerThread; ++cc) o4[cc] = fmaf(S[m][cc], alpha, kf[m] * dl[cc]);
     if (i < d_k && vec_cols) {
-      *reinterpret_cast<float4*>(Sg + static_cast<size_t>(i) * d_v + j0) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+      store_stream4(Sg + static_cast<size_t>(i) * d_v + j0, make_float4(o4[0], o4[1], o4[2], o4[3]));
     } else if (i < d_k) {
 #pragma unroll
       for (int cc = 0; cc < kColsPerThread; ++cc)

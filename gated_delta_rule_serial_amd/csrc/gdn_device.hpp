@@ -157,6 +157,18 @@ struct RawScalar {
   }
 };
 
+// Streaming (non-temporal) 16-byte accesses: data touched once per kernel,
+// e.g. the decode state, bypasses cache retention.
+typedef float vfloat4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+  const vfloat4 x = __builtin_nontemporal_load(reinterpret_cast<const vfloat4*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store_stream4(float* p, float4 x) {
+  const vfloat4 y = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(y, reinterpret_cast<vfloat4*>(p));
+}
+
 __device__ __forceinline__ float readlane(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
