@@ -83,6 +83,8 @@ gdn_status check_problem(const gdn_problem* p, const char* fn, bool has_tokens) 
   } else {
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: unknown gate_mode %d", fn, p->gate_mode);
   }
+  if (p->algorithm != GDN_ALGO_AUTO && p->algorithm != GDN_ALGO_SERIAL && p->algorithm != GDN_ALGO_CHUNKED)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: unknown algorithm %d", fn, p->algorithm);
   return GDN_OK;
 }
 
@@ -164,14 +166,24 @@ GDN_EXPORT gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs, 
   sp.d_k = p.d_k;
   sp.d_v = p.d_v;
   sp.ratio = p.h_v / p.h_qk;
-  const int cpw = gdn::scan_columns_per_wave(p.d_k);
-  sp.col_blocks = (p.d_v + cpw - 1) / cpw;
   sp.scale = resolved_scale(problem);
+  const int io_bf16 = p.io_dtype == GDN_BF16;
+  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v);
+  if (p.algorithm == GDN_ALGO_CHUNKED && !can_chunk)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "%s: the chunked algorithm needs bfloat16 I/O, d_k 64 or 128 and d_v a multiple of 8 "
+                "(got %s, d_k=%d, d_v=%d)", fn, io_bf16 ? "bf16" : "f32", p.d_k, p.d_v);
+  const bool chunked = p.algorithm == GDN_ALGO_CHUNKED ||
+                       (p.algorithm == GDN_ALGO_AUTO && can_chunk &&
+                        static_cast<int64_t>(total_tokens) >= 64 * static_cast<int64_t>(num_seqs));
+  const int cols = chunked ? gdn::chunked_columns_per_block(p.d_k, p.d_v) : gdn::scan_columns_per_wave(p.d_k);
+  sp.col_blocks = (p.d_v + cols - 1) / cols;
   const uint64_t blocks = static_cast<uint64_t>(num_seqs) * p.h_v * sp.col_blocks;
   if (blocks > 0x7fffffffull)
     return fail(GDN_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", fn,
                 static_cast<unsigned long long>(blocks));
-  const hipError_t e = gdn::launch_prefill_scan(sp, p.io_dtype == GDN_BF16, stream);
+  const hipError_t e = chunked ? gdn::launch_prefill_chunked(sp, io_bf16, stream)
+                               : gdn::launch_prefill_scan(sp, io_bf16, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }

@@ -67,6 +67,12 @@ hipError_t launch_prefill_scan(ScanParams p, int io_bf16, hipStream_t stream);
 hipError_t launch_decode_step(DecodeParams p, int io_bf16, hipStream_t stream);
 hipError_t launch_gate_prologue(GatePrologueParams p, int io_bf16, hipStream_t stream);
 
+// Chunked (matrix-core) prefill: whether a geometry is built, the state
+// columns one workgroup owns, and the launcher.
+bool chunked_supported(int io_bf16, int d_k, int d_v);
+int chunked_columns_per_block(int d_k, int d_v);
+hipError_t launch_prefill_chunked(ScanParams p, int io_bf16, hipStream_t stream);
+
 // Columns one scan wave owns for a given d_k (used to size the grid).
 int scan_columns_per_wave(int d_k);
 // Columns one decode workgroup owns.

@@ -22,6 +22,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "gdn.h")
 GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_PRECOMPUTED, GDN_GATES_RAW = 0, 1
+GDN_ALGO_AUTO, GDN_ALGO_SERIAL, GDN_ALGO_CHUNKED = 0, 1, 2
+ALGORITHMS = {"auto": GDN_ALGO_AUTO, "serial": GDN_ALGO_SERIAL, "chunked": GDN_ALGO_CHUNKED}
 
 _DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
 
@@ -35,6 +37,7 @@ class gdn_problem(ctypes.Structure):
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
         ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
         ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("algorithm", ctypes.c_int32),
     ]
 
 
@@ -115,27 +118,31 @@ def _stream(stream, device) -> ctypes.c_void_p:
 
 
 def make_problem(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype, *, scale: float = 0.0,
-                 g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None) -> gdn_problem:
+                 g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None,
+                 algorithm: str = "auto") -> gdn_problem:
     """Fill the ``gdn_problem`` struct.  Raw gates are used when ``a`` is given."""
     if io_dtype not in _DTYPES:
         raise ValueError(f"io dtype {io_dtype} is not supported")
     raw = a is not None
     return gdn_problem(h_qk, h_v, d_k, d_v, _DTYPES[io_dtype], float(scale),
                        GDN_GATES_RAW if raw else GDN_GATES_PRECOMPUTED,
-                       _ptr(g), _ptr(beta), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias))
+                       _ptr(g), _ptr(beta), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                       ALGORITHMS[algorithm])
 
 
 def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
                 out: Optional[torch.Tensor], final_state: Optional[torch.Tensor],
                 initial_state: Optional[torch.Tensor] = None, g=None, beta=None, a=None, b=None,
                 A_log=None, dt_bias=None, scale: float = 0.0,
-                cu_seqlens_host: Optional[Sequence[int]] = None, stream=None) -> None:
+                cu_seqlens_host: Optional[Sequence[int]] = None, algorithm: str = "auto",
+                stream=None) -> None:
     """gdn_prefill of include/gdn.h: q, k [T, h_qk, d_k]; v, out [T, h_v, d_v];
-    cu_seqlens int32 [N+1] on the device; states float32 [N, h_v, d_k, d_v]."""
+    cu_seqlens int32 [N+1] on the device; states float32 [N, h_v, d_k, d_v];
+    algorithm "auto", "serial" or "chunked"."""
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
-                        A_log=A_log, dt_bias=dt_bias)
+                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm)
     n = cu_seqlens.numel() - 1
     host = None
     if cu_seqlens_host is not None:
@@ -168,7 +175,7 @@ def gdn_gate_prologue(a: torch.Tensor, b: Optional[torch.Tensor], A_log: torch.T
 
 # ----------------------------------------------------------------- helpers
 def prefill(q, k, v, cu_seqlens, *, initial_state=None, want_state=True, scale=0.0,
-            cu_seqlens_host=None, stream=None, **gates):
+            cu_seqlens_host=None, algorithm="auto", stream=None, **gates):
     """Allocate ``out`` (and the final state) with torch and call gdn_prefill."""
     T, _, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
@@ -176,7 +183,7 @@ def prefill(q, k, v, cu_seqlens, *, initial_state=None, want_state=True, scale=0
     out = torch.empty(T, h_v, d_v, dtype=q.dtype, device=q.device)
     fin = torch.empty(n, h_v, d_k, d_v, dtype=torch.float32, device=q.device) if want_state else None
     gdn_prefill(q, k, v, cu_seqlens, out=out, final_state=fin, initial_state=initial_state, scale=scale,
-                cu_seqlens_host=cu_seqlens_host, stream=stream, **gates)
+                cu_seqlens_host=cu_seqlens_host, algorithm=algorithm, stream=stream, **gates)
     return out, fin
 
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -69,6 +69,23 @@ typedef enum gdn_gate_mode {
   GDN_GATES_RAW = 1
 } gdn_gate_mode;
 
+/* Which prefill formulation gdn_prefill runs.  Both compute the recurrence
+ * above; they differ only in rounding. */
+typedef enum gdn_algorithm {
+  /* CHUNKED where it is supported and sequences average at least 64 tokens,
+   * SERIAL otherwise. */
+  GDN_ALGO_AUTO = 0,
+  /* Token-by-token scan in float32 on the vector ALUs ([P4]'s order of
+   * operations); any gates, any head size 1..256, float32 or bfloat16 I/O. */
+  GDN_ALGO_SERIAL = 1,
+  /* The same recurrence in chunks of 64 tokens on the matrix cores (bf16
+   * operands, f32 accumulation, f32 state carried between chunks).  Needs
+   * bfloat16 I/O, d_k of 64 or 128 and d_v a multiple of 8, and a true decay
+   * (g <= 0, as the raw-gate prologue always gives); otherwise
+   * GDN_ERR_UNSUPPORTED when requested explicitly. */
+  GDN_ALGO_CHUNKED = 2
+} gdn_algorithm;
+
 /* Geometry and gate inputs of one call. */
 typedef struct gdn_problem {
   int32_t h_qk;     /* query/key heads, >= 1                                  */
@@ -84,6 +101,7 @@ typedef struct gdn_problem {
   const void* b;        /* RAW: [tokens, h_v] io_dtype                       */
   const float* A_log;   /* RAW: [h_v] float32                                */
   const float* dt_bias; /* RAW: [h_v] float32                                */
+  int32_t algorithm;    /* gdn_algorithm; gdn_prefill only (decode ignores it) */
 } gdn_problem;
 
 /*

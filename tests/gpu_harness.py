@@ -38,7 +38,7 @@ def to_dev(t, dev="cuda"):
 
 
 def gpu_prefill(inp: synth.Inputs, g=None, beta=None, *, raw=False, scale=0.0, want_out=True,
-                want_state=True, in_place=False, use_host_cu=True):
+                want_state=True, in_place=False, use_host_cu=True, algorithm="auto"):
     """Run gdn_prefill on cuda:0; returns (out, final) as CPU float64 tensors (or None)."""
     dev = "cuda"
     q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
@@ -56,7 +56,8 @@ def gpu_prefill(inp: synth.Inputs, g=None, beta=None, *, raw=False, scale=0.0, w
     gates = (dict(a=to_dev(inp.a), b=to_dev(inp.b), A_log=to_dev(inp.A_log), dt_bias=to_dev(inp.dt_bias))
              if raw else dict(g=to_dev(g), beta=to_dev(beta)))
     gdn.gdn_prefill(q, k, v, cu, out=out, final_state=fin, initial_state=s0, scale=scale,
-                    cu_seqlens_host=inp.cu_seqlens.tolist() if use_host_cu else None, **gates)
+                    cu_seqlens_host=inp.cu_seqlens.tolist() if use_host_cu else None, algorithm=algorithm,
+                    **gates)
     torch.cuda.synchronize()
     return (None if out is None else out.double().cpu(), None if fin is None else fin.double().cpu())
 

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 1
+    assert gdn.abi_version() == 2
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -44,7 +44,7 @@ def test_version_and_status_strings(lib):
 def _prob(**kw):
     base = dict(h_qk=2, h_v=4, d_k=16, d_v=16, io_dtype=gdn.GDN_F32, scale=0.0,
                 gate_mode=gdn.GDN_GATES_PRECOMPUTED, g=FAKE, beta=FAKE + 0x1000, a=None, b=None,
-                A_log=None, dt_bias=None)
+                A_log=None, dt_bias=None, algorithm=gdn.GDN_ALGO_AUTO)
     base.update(kw)
     return gdn.gdn_problem(**base)
 
@@ -75,6 +75,10 @@ INVALID, UNSUPPORTED = gdn.GDN_ERR_INVALID_ARGUMENT, gdn.GDN_ERR_UNSUPPORTED
     ("missing g", dict(g=None), {}, INVALID, "precomputed gates"),
     ("missing raw", dict(gate_mode=gdn.GDN_GATES_RAW, a=FAKE), {}, INVALID, "raw gates"),
     ("bad gate mode", dict(gate_mode=5), {}, INVALID, "gate_mode"),
+    ("bad algorithm", dict(algorithm=7), {}, INVALID, "algorithm"),
+    ("chunked on f32", dict(algorithm=gdn.GDN_ALGO_CHUNKED), {}, UNSUPPORTED, "chunked algorithm needs"),
+    ("chunked on d_k 48", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_BF16, d_k=48), {}, UNSUPPORTED,
+     "chunked algorithm needs"),
     ("misaligned g", dict(g=FAKE + 2), {}, INVALID, "aligned"),
     ("negative seqs", {}, dict(n=-1), INVALID, "negative"),
     ("negative tokens", {}, dict(T=-1), INVALID, "negative"),

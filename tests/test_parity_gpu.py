@@ -38,14 +38,15 @@ PREFILL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("algorithm", ["serial", "auto"])
 @pytest.mark.parametrize("name,over", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
-def test_prefill_workload_geometry(name, over):
+def test_prefill_workload_geometry(name, over, algorithm):
     shape = W[name]
-    say(f"[prefill] {name} {over}")
+    say(f"[prefill] {name} {over} {algorithm}")
     inp = synth.generate(shape, **over)
     raw = shape.gate_mode == "raw"
     g, beta = (None, None) if raw else gates_for(inp)
-    out, fin = gpu_prefill(inp, g, beta, raw=raw)
+    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm=algorithm)
     ro, rf = oracle_prefill(inp, g, beta, raw=raw)
     tol = TOL[shape.io_dtype]
     check(out, ro, tol, "out")
@@ -74,7 +75,7 @@ def test_prefill_geometry(geom, raw):
     say(f"[prefill-geom] {geom} raw={raw}")
     inp = synth.generate(shape, seqlens=lens, seed=77)
     g, beta = (None, None) if raw else gates_for(inp)
-    out, fin = gpu_prefill(inp, g, beta, raw=raw)
+    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm="serial")
     ro, rf = oracle_prefill(inp, g, beta, raw=raw)
     check(out, ro, TOL[dt], "out")
     check(fin, rf, TOL[dt], "final state")
@@ -237,24 +238,80 @@ def test_gate_prologue(dt):
     check(beta.double().cpu(), torch.from_numpy(rb), TOL[dt], "beta")
 
 
-# ------------------------------------------------------------------ full sizes, sampled
-FULL = [
-    ("prefill_t4096_fused_gates", [0, 15]),
-    ("varlen_prefill_8seq", [0, 7, 15]),
-    ("wide_prefill_t32768_d256", [0, 5]),
+# ------------------------------------------------------------------ chunked (matrix-core) prefill
+CHUNKED = [
+    # (h_qk, h_v, d_k, d_v, seqlens, raw gates, initial state)
+    (16, 32, 128, 128, [200], True, False),
+    (16, 32, 128, 128, [37, 0, 129, 64, 1, 250, 3], False, True),
+    (2, 4, 64, 40, [70, 0, 13, 64], False, True),
+    (1, 2, 128, 200, [130], True, True),
+    (4, 4, 64, 64, [1, 2, 65, 128], True, False),
+    (1, 1, 128, 8, [300], False, True),
 ]
 
 
-@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
-def test_prefill_full_size_sampled(name, heads):
+@pytest.mark.parametrize("case", CHUNKED, ids=lambda c: f"hq{c[0]}_hv{c[1]}_dk{c[2]}_dv{c[3]}_T{sum(c[4])}")
+def test_chunked_prefill(case):
+    h_qk, h_v, d_k, d_v, lens, raw, init = case
+    shape = _shape("varlen_prefill_8seq", h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v, init_state=init,
+                   gate_mode="raw" if raw else "precomputed")
+    say(f"[chunked] {case}")
+    inp = synth.generate(shape, seqlens=lens, seed=99)
+    g, beta = (None, None) if raw else gates_for(inp)
+    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm="chunked")
+    ro, rf = oracle_prefill(inp, g, beta, raw=raw)
+    check(out, ro, TOL[shape.io_dtype], "out")
+    check(fin, rf, TOL[shape.io_dtype], "final state")
+
+
+def test_chunked_prefill_resets_and_weak_decay():
+    """Log-decays of -inf (a reset), of 0 (no decay) and tiny beta in one sequence."""
+    shape = _shape("varlen_prefill_8seq", init_state=True)
+    inp = synth.generate(shape, seqlens=[150, 70])
+    g, beta = gates_for(inp)
+    g = g.float()
+    g[5::37] = float("-inf")
+    g[100:140] = 0.0
+    g = g.to(torch.bfloat16)
+    beta = beta.float()
+    beta[60:70] = 1e-3
+    beta = beta.to(torch.bfloat16)
+    say("[chunked] resets / no decay / tiny beta")
+    out, fin = gpu_prefill(inp, g, beta, algorithm="chunked")
+    ro, rf = oracle_prefill(inp, g, beta)
+    check(out, ro, TOL[torch.bfloat16], "out")
+    check(fin, rf, TOL[torch.bfloat16], "final state")
+
+
+def test_chunked_unsupported_is_reported():
+    shape = _shape(init_state=False)  # float32 I/O, d_k 16
+    inp = synth.generate(shape, seqlens=[64])
+    g, beta = gates_for(inp)
+    with pytest.raises(gdn.GdnError, match="chunked algorithm needs"):
+        gpu_prefill(inp, g, beta, algorithm="chunked")
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+FULL = [
+    ("prefill_t4096_fused_gates", [0, 15], "auto"),
+    ("prefill_t4096_fused_gates", [3], "serial"),
+    ("varlen_prefill_8seq", [0, 7, 15], "auto"),
+    ("varlen_prefill_8seq", [4], "serial"),
+    ("wide_prefill_t32768_d256", [0, 5], "auto"),
+]
+
+
+@pytest.mark.parametrize("name,heads,algorithm", FULL, ids=[f"{f[0]}-{f[2]}" for f in FULL])
+def test_prefill_full_size_sampled(name, heads, algorithm):
     """The full workload as the benchmark runs it; the oracle recomputes the
     listed q/k head groups (all their value heads, every token) on their own."""
     shape = W[name]
     inp = synth.generate(shape)
-    say(f"[full] {name}: {len(inp.seqlens)} seqs, {inp.total_tokens} tokens; oracle on head groups {heads}")
+    say(f"[full] {name} ({algorithm}): {len(inp.seqlens)} seqs, {inp.total_tokens} tokens; "
+        f"oracle on head groups {heads}")
     raw = shape.gate_mode == "raw"
     g, beta = (None, None) if raw else gates_for(inp)
-    out, fin = gpu_prefill(inp, g, beta, raw=raw)
+    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm=algorithm)
     ref = oracle_prefill(inp, g, beta, raw=raw, heads=heads)
     ratio = shape.h_v // shape.h_qk
     tol = TOL[shape.io_dtype]
