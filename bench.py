@@ -37,6 +37,7 @@ from gated_delta_rule_serial_amd import gdn, synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 # FP32 vector FMA without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
 FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12  # 78.64
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 DECODE_STATE_BUFFERS = 4
 METRIC = "GDN prefill tokens/s + decode-step \u00b5s (B=64), % of HBM peak on 1 MI355X"
 
@@ -107,34 +108,42 @@ def cpu_baseline_decode(shape, inp, budget_s=10.0):
 
 
 def cpu_baseline_prefill(shape, inp, budget_s=10.0):
-    """The oracle on a bounded sample of a prefill workload: one q/k head group
-    (its value heads) over the leading tokens of every sequence, sized to ~budget_s."""
+    """The oracle on a bounded sample of a prefill workload: the first m tokens of
+    every sequence for the first k q/k head groups (all their value heads), with
+    (k, m) sized from a short probe so that the run takes about budget_s.  The
+    rate is scaled to all heads: tokens x (sampled value heads / h_v) / seconds."""
     import oracle
     orc = oracle.default()
     ratio = shape.h_v // shape.h_qk
-    hv = slice(0, ratio)
-    # probe speed on a short prefix, then size the sample
-    def run(ntok):
+
+    def run(groups, ntok):
         lens = [min(l, ntok) for l in inp.seqlens]
         idx = torch.cat([torch.arange(int(inp.cu_seqlens[i]), int(inp.cu_seqlens[i]) + lens[i])
-                         for i in range(len(lens))]) if lens else torch.zeros(0, dtype=torch.long)
+                         for i in range(len(lens))])
         cu = [0]
         for l in lens:
             cu.append(cu[-1] + l)
+        hv = slice(0, groups * ratio)
         gg, bb = orc.gates(inp.a[idx][:, hv], inp.b[idx][:, hv], inp.A_log[hv], inp.dt_bias[hv])
         s0 = None if inp.initial_state is None else inp.initial_state[:, hv].double().numpy()
+        args = (inp.q[idx][:, :groups].double().numpy(), inp.k[idx][:, :groups].double().numpy(),
+                inp.v[idx][:, hv].double().numpy(), gg, bb, cu, s0)
         t0 = time.perf_counter()
-        orc.prefill(inp.q[idx][:, 0:1].double().numpy(), inp.k[idx][:, 0:1].double().numpy(),
-                    inp.v[idx][:, hv].double().numpy(), gg, bb, cu, s0)
+        orc.prefill(*args)
         return time.perf_counter() - t0, cu[-1]
-    el, tok = run(64)
-    ntok = max(64, int(64 * budget_s / max(el, 1e-6)))
-    el, tok = run(ntok)
-    heads_frac = ratio / shape.h_v
-    return dict(value=round(tok * heads_frac / el, 3), unit="tokens/s", cores=orc.max_threads(),
+
+    max_len = max(inp.seqlens)
+    el, tok = run(1, min(128, max_len))
+    per_unit = el / max(tok, 1)                     # seconds per token per head group (one thread's share)
+    budget_units = budget_s / max(per_unit, 1e-9)   # token x group units that fit the budget
+    groups = max(1, min(shape.h_qk, int(budget_units // max(inp.total_tokens, 1))))
+    ntok = max_len if groups > 1 else max(128, min(max_len, int(budget_units / max(len(inp.seqlens), 1))))
+    el, tok = run(groups, ntok)
+    heads = groups * ratio
+    return dict(value=round(tok * heads / shape.h_v / el, 3), unit="tokens/s", cores=orc.max_threads(),
                 kind="oracle",
-                sample=f"q/k head group 0 ({ratio} of {shape.h_v} value heads), first {ntok} tokens of each "
-                       f"sequence ({tok} tokens) in {el:.1f} s; scaled to all heads")
+                sample=f"value heads 0-{heads - 1} of {shape.h_v} ({groups} q/k head groups), first {min(ntok, max_len)} "
+                       f"tokens of each sequence ({tok} tokens) in {el:.1f} s; rate scaled to all heads")
 
 
 def bench_decode(shape, steps, warmup, want_cpu):
@@ -187,7 +196,15 @@ def _flush(buf):
     buf.fill_(1.0)
 
 
-def bench_prefill(shape, steps, warmup, want_cpu):
+def chunked_flops(shape, T, chunk=64):
+    """MFMA flops of the chunked form per launch: per token and value head,
+    K K^T and Q K^T over the lower triangle (2 C d_k), W = T' K (C d_k),
+    U = T'' V (C d_v), X = W S, Y = Q S and the state update (6 d_k d_v), M D (C d_v)."""
+    dk, dv = shape.d_k, shape.d_v
+    return T * shape.h_v * (3 * chunk * dk + 2 * chunk * dv + 6 * dk * dv)
+
+
+def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto"):
     dev = "cuda"
     inp = synth.generate(shape)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -210,7 +227,7 @@ def bench_prefill(shape, steps, warmup, want_cpu):
 
     def one():
         gdn.gdn_prefill(q, k, v, cu, out=out, final_state=fin, initial_state=s0, cu_seqlens_host=cu_host,
-                        **gates)
+                        algorithm=algorithm, **gates)
 
     for _ in range(warmup):
         one()
@@ -230,9 +247,29 @@ def bench_prefill(shape, steps, warmup, want_cpu):
     ms = sum(ms_list) / len(ms_list)
     assert torch.isfinite(out.float()).all()
     nbytes = algorithmic_bytes(shape, inp)
-    fl = flops_serial(shape, T)
-    achieved_tf = fl / (ms * 1e-3) / 1e12
-    kernel_files = ["prefill_scan.hip", "gdn_device.hpp"]
+    hbm_gbs = nbytes / (ms * 1e-3) / 1e9
+    chunked = algorithm == "chunked" or (
+        algorithm == "auto" and shape.io_dtype == torch.bfloat16 and shape.d_k in (64, 128)
+        and shape.d_v % 8 == 0 and T >= 64 * n)
+    if chunked:
+        # the chunked form's intensity (~180 flop/B at d = 128) is below the bf16 MFMA
+        # ridge (2.5 PFLOP/s / 8 TB/s ~ 312 flop/B): HBM bounds it
+        fl = chunked_flops(shape, T)
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+                "traffic": _traffic(shape.name + "_chunked", ["prefill_chunked.hip", "gdn_device.hpp"]),
+                "kernel": "chunk_kernel (chunked, bf16 MFMA)", "algorithmic_bytes_per_launch": nbytes,
+                "mfma_tflops": round(fl / (ms * 1e-3) / 1e12, 2), "mfma_frac_of_bf16_peak":
+                    round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        # the serial form does 7 d_k d_v flops per token and head on the vector ALUs
+        fl = flops_serial(shape, T)
+        tf = fl / (ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(tf, 2), "peak": round(FP32_VALU_PEAK_TFLOPS, 2),
+                "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
+                "traffic": _traffic(shape.name + "_serial", ["prefill_scan.hip", "gdn_device.hpp"]),
+                "kernel": "scan_kernel (serial scan)", "flops_per_launch": fl,
+                "algorithmic_bytes_per_launch": nbytes}
     line = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -240,14 +277,11 @@ def bench_prefill(shape, steps, warmup, want_cpu):
         "ms_per_step": round(ms, 6),
         "ms_median": round(ms_list[len(ms_list) // 2], 6),
         "wall_s": round(wall, 3),
-        "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(FP32_VALU_PEAK_TFLOPS, 2),
-                     "unit": "TFLOP/s", "frac": round(achieved_tf / FP32_VALU_PEAK_TFLOPS, 4),
-                     "traffic": _traffic(shape.name, kernel_files),
-                     "kernel": "scan_kernel (serial scan)", "flops_per_launch": fl,
-                     "algorithmic_bytes_per_launch": nbytes},
-        "config": {"workload": shape.name, "num_seqs": n, "total_tokens": T, "seqlens": inp.seqlens,
-                   "h_qk": shape.h_qk, "h_v": shape.h_v, "d_k": shape.d_k, "d_v": shape.d_v,
+        "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+        "config": {"workload": shape.name, "algorithm": "chunked" if chunked else "serial", "num_seqs": n,
+                   "total_tokens": T, "seqlens": inp.seqlens, "h_qk": shape.h_qk, "h_v": shape.h_v,
+                   "d_k": shape.d_k, "d_v": shape.d_v,
                    "io_dtype": "bf16" if shape.io_dtype == torch.bfloat16 else "f32", "state_dtype": "f32",
                    "gates": shape.gate_mode},
     }
@@ -283,6 +317,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_b64", choices=sorted(synth.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--algorithm", default="auto", choices=["auto", "serial", "chunked"],
+                    help="prefill formulation (prefill workloads only)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="time a plain device copy of this many MiB instead (counter calibration)")
     args = ap.parse_args()
@@ -302,7 +338,10 @@ def main():
     steps = args.steps if args.steps is not None else (1000 if decode else 10)
     warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
     want_cpu = not args.no_cpu_baseline
-    line = (bench_decode if decode else bench_prefill)(shape, steps, warmup, want_cpu)
+    if decode:
+        line = bench_decode(shape, steps, warmup, want_cpu)
+    else:
+        line = bench_prefill(shape, steps, warmup, want_cpu, args.algorithm)
     head = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"), "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}

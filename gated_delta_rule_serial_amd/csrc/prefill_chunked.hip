@@ -25,14 +25,16 @@
 // every factor lies in [0, 1].  g is clamped below at -1e4 (exp of it is 0 in
 // float) so that a g of -infinity (a reset) never forms inf - inf.
 //
-// Mapping.  One workgroup (4 waves) owns NC columns of the state of one
+// Mapping.  One workgroup (8 waves, two per SIMD) owns NC columns of the state of one
 // (sequence, value head) and walks the sequence chunk by chunk; the state
 // slice S (DK x NC, f32) stays in MFMA accumulator registers across chunks.
 // Per chunk, all operands are staged in LDS with k contiguous so that every
 // MFMA operand fragment is one 16-byte LDS read:
-//   1. load K, Q (rows), K^T, V^T (columns of this block), gates; prefix-sum
-//      G in double;
-//   2. P = K K^T and R = Q K^T (MFMA) -> A (f32) and M (bf16);
+//   1. store K, Q (rows), K^T, V^T (columns of this block) and the gates of
+//      the chunk, which were loaded into registers during the previous chunk,
+//      then start loading the next chunk; prefix-sum G (log2 units) in double;
+//   2. P = K K^T and R = Q K^T (MFMA), tile by tile, with one exp2 per
+//      (t, s) shared by both -> A (f32) and M (bf16);
 //   3. T = (I + A)^-1: 16x16 diagonal blocks by forward substitution in f32,
 //      off-diagonal blocks by block substitution with f32 MFMA;
 //   4. W = T diag(beta gam) K and U = T diag(beta) V (MFMA);
@@ -51,11 +53,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;          // chunk length (tokens)
-constexpr int kThreads = 256;   // 4 waves
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kSC = kC + 8;     // bf16 row stride of C-long rows
 constexpr int kSA = kC + 8;     // f32 row stride of A (its buffer later holds T' and T'' in bf16)
 constexpr int kST = kC + 4;     // f32 row stride of T
 constexpr float kMinLogDecay = -1.0e4f;
+constexpr double kLog2e = 1.4426950408889634;
+
+// 2^x in one v_exp_f32; used with log-decays pre-scaled by log2(e).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16_t to_bf16(float x) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(x)); }
 
@@ -111,7 +118,7 @@ struct Lds {
   static constexpr int kSt = kMs + kC * kSC * 2;             // S^T      [NC][SK] bf16
   static constexpr int kDt = kSt + NC * SK * 2;              // D^T      [NC][SC] bf16
   static constexpr int kDtt = kDt + NC * kSC * 2;            // (exp(G_C - G) D)^T [NC][SC] bf16
-  static constexpr int kXs = kDtt + NC * kSC * 2;            // solve scratch [4][16][20] f32
+  static constexpr int kXs = kDtt + NC * kSC * 2;            // solve scratch [4 waves][16][20] f32
   static constexpr int kGd = kXs + 4 * 16 * 20 * 4;          // G        [C] f64
   static constexpr int kGam = kGd + kC * 8;                  // gam      [C] f32
   static constexpr int kBet = kGam + kC * 4;                 // beta     [C] f32
@@ -124,11 +131,14 @@ template <typename IO, int DK, int NC, bool RAW>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
   using L = Lds<DK, NC>;
   constexpr int SK = L::SK;
-  constexpr int RT = DK / 16 / 4;  // state row tiles per wave
-  constexpr int CT = NC / 16;      // column tiles
+  constexpr int CT = NC / 16;                  // column tiles of the block
+  constexpr int CTW = CT / 2;                  // column tiles per wave in the (token, column) products
+  constexpr int KTW = DK / 32;                 // key tiles per wave in W = T' K
+  constexpr int STW = (DK / 16) * CT / kWaves; // state tiles per wave
+  static_assert(CT % 2 == 0 && STW >= 1, "block shape");
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* Ks = reinterpret_cast<bf16_t*>(smem + L::kKs);
-  bf16_t* Ws = Ks;  // W overwrites K once P and R are formed
+  bf16_t* Ws = Ks;  // W overwrites K once P, R and K^T are formed
   bf16_t* Qs = reinterpret_cast<bf16_t*>(smem + L::kQs);
   bf16_t* KT = reinterpret_cast<bf16_t*>(smem + L::kKT);
   bf16_t* Vt = reinterpret_cast<bf16_t*>(smem + L::kVt);
@@ -148,6 +158,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
   const int tid = static_cast<int>(threadIdx.x);
   const int w = tid >> 6;
   const int lane = tid & 63;
+  // this wave's row block (16 tokens) and column half in the (token, column) products
+  const int rb = w & 3;
+  const int chalf = w >> 2;
   int unit = static_cast<int>(blockIdx.x);
   const int cb = unit % p.col_blocks;
   unit /= p.col_blocks;
@@ -160,30 +173,30 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
   const int d_v = p.d_v;
   const size_t sbase = (static_cast<size_t>(n) * p.h_v + h) * static_cast<size_t>(DK) * d_v;
 
-  // ---- state slice in accumulators: wave w owns row tiles w*RT .. w*RT+RT-1
-  f32x4 S[RT][CT];
+  // ---- state slice in accumulators: wave w owns state tiles w*STW .. w*STW+STW-1
+  //      (tile index = row tile * CT + column tile)
+  f32x4 S[STW];
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+  for (int e = 0; e < STW; ++e) {
+    const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * (w * RT + r) + acc_row(lane, i);
-        const int col = J0 + 16 * c + acc_col(lane);
-        S[r][c][i] = (p.s0 != nullptr && col < d_v) ? p.s0[sbase + static_cast<size_t>(row) * d_v + col] : 0.0f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * ri + acc_row(lane, i);
+      const int col = J0 + 16 * cj + acc_col(lane);
+      S[e][i] = (p.s0 != nullptr && col < d_v) ? p.s0[sbase + static_cast<size_t>(row) * d_v + col] : 0.0f;
+    }
+  }
   auto publish_state = [&]() {  // S^T (bf16) for the next chunk's X = W S and Y = Q S
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const int row = 16 * (w * RT + r) + acc_row(lane, 0);
-        const int col = 16 * c + acc_col(lane);
-        uint2 pk;
-        pk.x = static_cast<uint32_t>(to_bf16(S[r][c][0])) | (static_cast<uint32_t>(to_bf16(S[r][c][1])) << 16);
-        pk.y = static_cast<uint32_t>(to_bf16(S[r][c][2])) | (static_cast<uint32_t>(to_bf16(S[r][c][3])) << 16);
-        *reinterpret_cast<uint2*>(St + col * SK + row) = pk;
-      }
+    for (int e = 0; e < STW; ++e) {
+      const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;
+      const int row = 16 * ri + acc_row(lane, 0);
+      const int col = 16 * cj + acc_col(lane);
+      uint2 pk;
+      pk.x = static_cast<uint32_t>(to_bf16(S[e][0])) | (static_cast<uint32_t>(to_bf16(S[e][1])) << 16);
+      pk.y = static_cast<uint32_t>(to_bf16(S[e][2])) | (static_cast<uint32_t>(to_bf16(S[e][3])) << 16);
+      *reinterpret_cast<uint2*>(St + col * SK + row) = pk;
+    }
   };
   publish_state();
 
@@ -201,110 +214,156 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
     }
   }
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kC) {
-    const int L = (t_end - t0) < kC ? (t_end - t0) : kC;
+  // the upper tiles of M are never written per chunk: zero them once (M is an
+  // MFMA operand over its full k range)
+  for (int e = tid; e < 6 * 256; e += kThreads) {
+    const int tile = e >> 8;
+    const int tb = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+    const int cs = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+    const int t = 16 * tb + ((e & 255) >> 4), s = 16 * cs + (e & 15);
+    Ms[t * kSC + s] = 0;
+  }
 
-    // ================= 1. loads
-    // K, Q rows (16-byte vectors) and K^T; rows t >= L are zero.
-    constexpr int VPR = DK / 8;  // 8-element vectors per row
+  // ---- register staging of one chunk's inputs (loaded one chunk ahead)
+  constexpr int VPR = DK / 8;                              // 8-element vectors per K/Q row
+  constexpr int KQ_IT = kC * VPR / kThreads;               // vectors per thread
+  constexpr int VPV = NC / 8;                              // 8-element vectors per V row
+  constexpr int V_IT = (kC * VPV + kThreads - 1) / kThreads;
+  static_assert(KQ_IT >= 1, "block shape");
+  uint4 rk[KQ_IT], rq[KQ_IT], rv[V_IT];
+  float rg = 0.0f, rb_ = 0.0f;  // wave 0: raw gate inputs of token (chunk start + lane)
+  auto fetch = [&](int c0) {
+    const int Ln = (t_end - c0) < kC ? (t_end - c0) : kC;
 #pragma unroll
-    for (int it = 0; it < kC * VPR / kThreads; ++it) {
+    for (int it = 0; it < KQ_IT; ++it) {
       const int v = tid + it * kThreads;
       const int t = v / VPR;
       const int c8 = (v % VPR) * 8;
-      uint4 kx = make_uint4(0, 0, 0, 0), qx = make_uint4(0, 0, 0, 0);
-      if (t < L) {
-        const size_t off = static_cast<size_t>(t0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
-        kx = *reinterpret_cast<const uint4*>(kg + off);
-        qx = *reinterpret_cast<const uint4*>(qg + off);
+      rk[it] = make_uint4(0, 0, 0, 0);
+      rq[it] = make_uint4(0, 0, 0, 0);
+      if (t < Ln) {
+        const size_t off = static_cast<size_t>(c0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
+        rk[it] = *reinterpret_cast<const uint4*>(kg + off);
+        rq[it] = *reinterpret_cast<const uint4*>(qg + off);
       }
-      *reinterpret_cast<uint4*>(Ks + t * SK + c8) = kx;
-      *reinterpret_cast<uint4*>(Qs + t * SK + c8) = qx;
-      const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        KT[(c8 + e) * kSC + t] = static_cast<bf16_t>((e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu));
     }
-    // V^T of this column block; columns >= d_v and rows t >= L are zero.
-    constexpr int VPV = NC / 8;
 #pragma unroll
-    for (int it = 0; it < (kC * VPV + kThreads - 1) / kThreads; ++it) {
+    for (int it = 0; it < V_IT; ++it) {
+      const int v = tid + it * kThreads;
+      const int t = v / VPV;
+      const int c8 = (v % VPV) * 8;
+      rv[it] = make_uint4(0, 0, 0, 0);
+      if (v < kC * VPV && t < Ln && J0 + c8 < d_v)
+        rv[it] = *reinterpret_cast<const uint4*>(vg + static_cast<size_t>(c0 + t) * v_stride +
+                                                 static_cast<size_t>(h) * d_v + J0 + c8);
+    }
+    if (w == 0) {
+      rg = 0.0f;
+      rb_ = 0.0f;
+      if (lane < Ln) {
+        const size_t gi = static_cast<size_t>(c0 + lane) * p.h_v + h;
+        if constexpr (RAW) {
+          rg = widen(static_cast<const IO*>(p.gates.a)[gi]);
+          rb_ = widen(static_cast<const IO*>(p.gates.b)[gi]);
+        } else {
+          rg = widen(static_cast<const IO*>(p.gates.g)[gi]);
+          rb_ = widen(static_cast<const IO*>(p.gates.beta)[gi]);
+        }
+      }
+    }
+  };
+  if (t_begin < t_end) fetch(t_begin);
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kC) {
+    const int L = (t_end - t0) < kC ? (t_end - t0) : kC;
+
+    // ================= 1. stage the chunk in LDS, start loading the next one
+#pragma unroll
+    for (int it = 0; it < KQ_IT; ++it) {
+      const int v = tid + it * kThreads;
+      const int t = v / VPR;
+      const int c8 = (v % VPR) * 8;
+      *reinterpret_cast<uint4*>(Ks + t * SK + c8) = rk[it];
+      *reinterpret_cast<uint4*>(Qs + t * SK + c8) = rq[it];
+    }
+#pragma unroll
+    for (int it = 0; it < V_IT; ++it) {
       const int v = tid + it * kThreads;
       if (v < kC * VPV) {
         const int t = v / VPV;
         const int c8 = (v % VPV) * 8;
-        uint4 vx = make_uint4(0, 0, 0, 0);
-        if (t < L && J0 + c8 < d_v)
-          vx = *reinterpret_cast<const uint4*>(vg + static_cast<size_t>(t0 + t) * v_stride +
-                                               static_cast<size_t>(h) * d_v + J0 + c8);
-        const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
+        const uint32_t vw[4] = {rv[it].x, rv[it].y, rv[it].z, rv[it].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           Vt[(c8 + e) * kSC + t] = static_cast<bf16_t>((e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu));
       }
     }
-    // gates and the in-chunk prefix sum of the log-decay (wave 0, lane = token)
+    // gates and the in-chunk prefix sum of the log-decay, in log2 units (wave 0, lane = token)
     if (w == 0) {
       float g = 0.0f, b = 0.0f;
-      const int t = t0 + lane;
       if (lane < L) {
-        const size_t gi = static_cast<size_t>(t) * p.h_v + h;
         if constexpr (RAW) {
-          g = gate_log_decay(widen(static_cast<const IO*>(p.gates.a)[gi]), A_log, dt_bias);
-          b = gate_sigmoid(widen(static_cast<const IO*>(p.gates.b)[gi]));
+          g = gate_log_decay(rg, A_log, dt_bias);
+          b = gate_sigmoid(rb_);
         } else {
-          g = widen(static_cast<const IO*>(p.gates.g)[gi]);
-          b = widen(static_cast<const IO*>(p.gates.beta)[gi]);
+          g = rg;
+          b = rb_;
         }
         g = fmaxf(g, kMinLogDecay);
       }
-      double G = static_cast<double>(g);
+      double G = static_cast<double>(g) * kLog2e;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const double y = __shfl_up(G, off, 64);
         if (lane >= off) G += y;
       }
       Gd[lane] = G;
-      Gam[lane] = expf(static_cast<float>(G));
+      Gam[lane] = fast_exp2(static_cast<float>(G));
       Bet[lane] = b;
     }
+    if (t0 + kC < t_end) fetch(t0 + kC);  // in flight while this chunk computes
     __syncthreads();
 
-    // ================= 2. P = K K^T, R = Q K^T -> A (f32) and M (bf16)
-    // the 10 lower tiles (tb >= cs) of each, dealt round-robin to the waves
-    for (int job = w; job < 20; job += 4) {
-      const int tj = job % 10;
+    // ================= 2. P = K K^T, R = Q K^T -> A (f32) and M (bf16); K^T
+    // K^T from the staged rows (needed from step 4 on): item (i, 8 tokens) reads
+    // a column segment of K (consecutive i across lanes: no bank conflicts) and
+    // writes it as one 16-byte row segment of K^T
+#pragma unroll
+    for (int it = 0; it < DK * (kC / 8) / kThreads; ++it) {
+      const int item = tid + it * kThreads;
+      const int i = item % DK;
+      const int t8 = (item / DK) * 8;
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        wv[e] = static_cast<uint32_t>(Ks[(t8 + 2 * e) * SK + i]) |
+                (static_cast<uint32_t>(Ks[(t8 + 2 * e + 1) * SK + i]) << 16);
+      *reinterpret_cast<uint4*>(KT + i * kSC + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    // the 10 lower tiles (tb >= cs), dealt round-robin to the waves; P and R of a
+    // tile share the decay factor exp(G_t - G_s)
+    for (int tj = w; tj < 10; tj += kWaves) {
       int tb = 0;
       while ((tb + 1) * (tb + 2) / 2 <= tj) ++tb;
       const int cs = tj - tb * (tb + 1) / 2;
-      const bool isP = job < 10;
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = mma<DK>(acc, (isP ? Ks : Qs) + 16 * tb * SK, SK, Ks + 16 * cs * SK, SK, lane);
+      f32x4 pacc = {0.0f, 0.0f, 0.0f, 0.0f}, racc = {0.0f, 0.0f, 0.0f, 0.0f};
+      pacc = mma<DK>(pacc, Ks + 16 * tb * SK, SK, Ks + 16 * cs * SK, SK, lane);
+      racc = mma<DK>(racc, Qs + 16 * tb * SK, SK, Ks + 16 * cs * SK, SK, lane);
+      const int s_ = 16 * cs + acc_col(lane);
+      const double Gs = Gd[s_];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * tb + acc_row(lane, i);
-        const int s = 16 * cs + acc_col(lane);
-        const float dec = (s <= t) ? expf(static_cast<float>(Gd[t] - Gd[s])) : 0.0f;
-        if (isP) {
-          Af[t * kSA + s] = (s < t) ? Bet[t] * dec * acc[i] : 0.0f;
-        } else {
-          Ms[t * kSC + s] = to_bf16(dec * acc[i]);
-        }
+        const float dec = (s_ <= t) ? fast_exp2(static_cast<float>(Gd[t] - Gs)) : 0.0f;
+        Af[t * kSA + s_] = (s_ < t) ? Bet[t] * dec * pacc[i] : 0.0f;
+        Ms[t * kSC + s_] = to_bf16(dec * racc[i]);
       }
-    }
-    // zero the upper tiles of M (it is an MFMA operand over the full k range)
-    for (int e = tid; e < 6 * 256; e += kThreads) {
-      const int tile = e >> 8;
-      const int tb = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
-      const int cs = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
-      const int t = 16 * tb + ((e & 255) >> 4), s = 16 * cs + (e & 15);
-      Ms[t * kSC + s] = 0;
     }
     __syncthreads();
 
     // ================= 3. T = (I + A)^-1
-    // 3a. diagonal block w by forward substitution (lane c < 16 owns column c)
-    {
+    // 3a. diagonal block w (waves 0-3) by forward substitution (lane c < 16 owns column c)
+    if (w < 4) {
       const int c = lane & 15;
       const float* Ab = Af + (16 * w) * kSA + 16 * w;
       float d[16];
@@ -312,9 +371,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       for (int r = 0; r < 16; ++r) {
         float x0 = (r == c) ? 1.0f : 0.0f, x1 = 0.0f;
 #pragma unroll
-        for (int s = 0; s < r; s += 2) {
-          x0 = fmaf(-Ab[r * kSA + s], d[s], x0);
-          if (s + 1 < r) x1 = fmaf(-Ab[r * kSA + s + 1], d[s + 1], x1);
+        for (int s2 = 0; s2 < r; s2 += 2) {
+          x0 = fmaf(-Ab[r * kSA + s2], d[s2], x0);
+          if (s2 + 1 < r) x1 = fmaf(-Ab[r * kSA + s2 + 1], d[s2 + 1], x1);
         }
         d[r] = x0 + x1;
       }
@@ -347,47 +406,50 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
     }
     // 3c. T' = T diag(beta gam) and T'' = T diag(beta) in bf16, zero above the diagonal
     for (int e = tid; e < kC * kC; e += kThreads) {
-      const int t = e >> 6, s = e & 63;
-      const float tv = (s <= t) ? Tf[t * kST + s] : 0.0f;
-      const float bs = Bet[s];
-      Tp[t * kSC + s] = to_bf16(tv * bs * Gam[s]);
-      Tpp[t * kSC + s] = to_bf16(tv * bs);
+      const int t = e >> 6, s2 = e & 63;
+      const float tv = (s2 <= t) ? Tf[t * kST + s2] : 0.0f;
+      const float bs = Bet[s2];
+      Tp[t * kSC + s2] = to_bf16(tv * bs * Gam[s2]);
+      Tpp[t * kSC + s2] = to_bf16(tv * bs);
     }
     __syncthreads();
 
     // ================= 4. W = T' K (-> LDS), U = T'' V (registers)
-    const int kmax = (w < 2) ? 32 : 64;  // T' rows of block w vanish for s >= 16 (w + 1)
+    const int kmax = (rb < 2) ? 32 : 64;  // rows of block rb vanish for s >= 16 (rb + 1)
 #pragma unroll
-    for (int ci = 0; ci < DK / 16; ++ci) {
+    for (int e = 0; e < KTW; ++e) {
+      const int ci = chalf * KTW + e;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = mma_range(acc, Tp + (16 * w) * kSC, kSC, KT + (16 * ci) * kSC, kSC, 0, kmax, lane);
+      acc = mma_range(acc, Tp + (16 * rb) * kSC, kSC, KT + (16 * ci) * kSC, kSC, 0, kmax, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ws[(16 * w + acc_row(lane, i)) * SK + 16 * ci + acc_col(lane)] = to_bf16(acc[i]);
+      for (int i = 0; i < 4; ++i) Ws[(16 * rb + acc_row(lane, i)) * SK + 16 * ci + acc_col(lane)] = to_bf16(acc[i]);
     }
-    f32x4 U[CT];
+    f32x4 U[CTW];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      U[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      U[c] = mma_range(U[c], Tpp + (16 * w) * kSC, kSC, Vt + (16 * c) * kSC, kSC, 0, kmax, lane);
+    for (int e = 0; e < CTW; ++e) {
+      const int cj = chalf * CTW + e;
+      U[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      U[e] = mma_range(U[e], Tpp + (16 * rb) * kSC, kSC, Vt + (16 * cj) * kSC, kSC, 0, kmax, lane);
     }
     __syncthreads();
 
     // ================= 5. D = U - W S, Y = gam Q S
-    f32x4 Y[CT];
+    f32x4 Y[CTW];
     const double GC = Gd[kC - 1];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
+    for (int e = 0; e < CTW; ++e) {
+      const int cj = chalf * CTW + e;
       f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f}, y = {0.0f, 0.0f, 0.0f, 0.0f};
-      x = mma<DK>(x, Ws + (16 * w) * SK, SK, St + (16 * c) * SK, SK, lane);
-      y = mma<DK>(y, Qs + (16 * w) * SK, SK, St + (16 * c) * SK, SK, lane);
-      const int t = 16 * w + acc_row(lane, 0);
-      const int col = 16 * c + acc_col(lane);
+      x = mma<DK>(x, Ws + (16 * rb) * SK, SK, St + (16 * cj) * SK, SK, lane);
+      y = mma<DK>(y, Qs + (16 * rb) * SK, SK, St + (16 * cj) * SK, SK, lane);
+      const int t = 16 * rb + acc_row(lane, 0);
+      const int col = 16 * cj + acc_col(lane);
       float dl[4], dd[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dl[i] = U[c][i] - x[i];
-        dd[i] = dl[i] * expf(static_cast<float>(GC - Gd[t + i]));
-        Y[c][i] = Gam[t + i] * y[i];
+        dl[i] = U[e][i] - x[i];
+        dd[i] = dl[i] * fast_exp2(static_cast<float>(GC - Gd[t + i]));
+        Y[e][i] = Gam[t + i] * y[i];
       }
       uint2 pk;
       pk.x = static_cast<uint32_t>(to_bf16(dl[0])) | (static_cast<uint32_t>(to_bf16(dl[1])) << 16);
@@ -401,14 +463,15 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
 
     // ================= 6. O = scale (Y + M D);  S <- gam_C S + K^T Dtt
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      f32x4 o = Y[c];
-      o = mma_range(o, Ms + (16 * w) * kSC, kSC, Dt + (16 * c) * kSC, kSC, 0, kmax, lane);
+    for (int e = 0; e < CTW; ++e) {
+      const int cj = chalf * CTW + e;
+      f32x4 o = Y[e];
+      o = mma_range(o, Ms + (16 * rb) * kSC, kSC, Dt + (16 * cj) * kSC, kSC, 0, kmax, lane);
       if (og != nullptr) {
-        const int col = J0 + 16 * c + acc_col(lane);
+        const int col = J0 + 16 * cj + acc_col(lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = 16 * w + acc_row(lane, i);
+          const int t = 16 * rb + acc_row(lane, i);
           if (t < L && col < d_v)
             narrow_store(og + static_cast<size_t>(t0 + t) * v_stride + static_cast<size_t>(h) * d_v + col,
                          p.scale * o[i]);
@@ -417,13 +480,12 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
     }
     const float gamC = Gam[kC - 1];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        f32x4 acc = S[r][c] * gamC;
-        acc = mma<kC>(acc, KT + (16 * (w * RT + r)) * kSC, kSC, Dtt + (16 * c) * kSC, kSC, lane);
-        S[r][c] = acc;
-      }
+    for (int e = 0; e < STW; ++e) {
+      const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;
+      f32x4 acc = S[e] * gamC;
+      acc = mma<kC>(acc, KT + (16 * ri) * kSC, kSC, Dtt + (16 * cj) * kSC, kSC, lane);
+      S[e] = acc;
+    }
     publish_state();
     __syncthreads();
   }
@@ -431,15 +493,15 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
   // ---- final state
   if (p.sN != nullptr) {
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int e = 0; e < STW; ++e) {
+      const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * (w * RT + r) + acc_row(lane, i);
-          const int col = J0 + 16 * c + acc_col(lane);
-          if (col < d_v) p.sN[sbase + static_cast<size_t>(row) * d_v + col] = S[r][c][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * ri + acc_row(lane, i);
+        const int col = J0 + 16 * cj + acc_col(lane);
+        if (col < d_v) p.sN[sbase + static_cast<size_t>(row) * d_v + col] = S[e][i];
+      }
+    }
   }
 }
 
