@@ -12,7 +12,9 @@ from .gdn import (  # noqa: F401
     decode_step,
     gate_prologue,
     gdn_decode_step,
+    gdn_decode_step_slots,
     gdn_gate_prologue,
     gdn_prefill,
+    gdn_prefill_slots,
     prefill,
 )

@@ -55,14 +55,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int row0 = rg * RPT;
   const bool vec_cols = (d_v % 4 == 0) && (j0 + kColsPerThread <= d_v);
 
-  float* __restrict__ Sg = p.state + (static_cast<size_t>(b) * p.h_v + h) * static_cast<size_t>(d_k) * d_v;
+  bool has_state;
+  const int sidx = state_slot(p.slots, p.num_slots, b, &has_state);
+  float* __restrict__ Sg = p.state + (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(d_k) * d_v;
 
   // ---- state tile (issued first: it is the long-latency traffic)
   float S[RPT][kColsPerThread];
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = row0 + m;
-    if (i < d_k && vec_cols) {
+    if (!has_state) {
+#pragma unroll
+      for (int cc = 0; cc < kColsPerThread; ++cc) S[m][cc] = 0.0f;
+    } else if (i < d_k && vec_cols) {
       const float4 x = load_stream4(Sg + static_cast<size_t>(i) * d_v + j0);
       S[m][0] = x.x;
       S[m][1] = x.y;
@@ -160,7 +165,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     float o4[kColsPerThread];
 #pragma unroll
     for (int cc = 0; cc < kColsPerThread; ++cc) o4[cc] = fmaf(S[m][cc], alpha, kf[m] * dl[cc]);
-    if (i < d_k && vec_cols) {
+    if (!has_state) {
+      // padding slot: the updated state is discarded
+    } else if (i < d_k && vec_cols) {
       store_stream4(Sg + static_cast<size_t>(i) * d_v + j0, make_float4(o4[0], o4[1], o4[2], o4[3]));
     } else if (i < d_k) {
 #pragma unroll

@@ -104,13 +104,37 @@ float resolved_scale(const gdn_problem* p) {
   return p->scale != 0.0f ? p->scale : 1.0f / std::sqrt(static_cast<float>(p->d_k));
 }
 
-}  // namespace
+// Slot-pool arguments shared by the *_slots entry points.
+struct SlotArgs {
+  const int32_t* slots = nullptr;       // device [n] or null (no pool)
+  const int32_t* slots_host = nullptr;  // optional host copy
+  int32_t num_slots = 0;
+};
 
-GDN_EXPORT gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
-                                  const int32_t* cu_seqlens_host, int32_t total_tokens, const void* q,
-                                  const void* k, const void* v, const float* initial_state, void* out,
-                                  float* final_state, hipStream_t stream) {
-  const char* fn = "gdn_prefill";
+// Slots in [0, num_slots) must be distinct (each names one sequence's state);
+// anything else marks a padding sequence.  Checked through the host copy.
+gdn_status check_slots(const SlotArgs& sl, int32_t n, const char* fn) {
+  if (sl.num_slots < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: num_slots=%d is negative", fn, sl.num_slots);
+  if (n > 0 && !sl.slots) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: slots is NULL", fn);
+  if (!aligned_to(sl.slots, 4)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: slots is misaligned", fn);
+  if (sl.slots_host && sl.num_slots > 0) {
+    std::vector<int32_t> owner(static_cast<size_t>(sl.num_slots), -1);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t sidx = sl.slots_host[i];
+      if (sidx < 0 || sidx >= sl.num_slots) continue;  // padding
+      if (owner[static_cast<size_t>(sidx)] >= 0)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "%s: slot %d is used by sequences %d and %d", fn, sidx,
+                    owner[static_cast<size_t>(sidx)], i);
+      owner[static_cast<size_t>(sidx)] = i;
+    }
+  }
+  return GDN_OK;
+}
+
+gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
+                        const int32_t* cu_seqlens_host, int32_t total_tokens, const void* q, const void* k,
+                        const void* v, const float* initial_state, void* out, float* final_state,
+                        const SlotArgs* pool, hipStream_t stream) {
   gdn_status st = check_problem(problem, fn, total_tokens > 0);
   if (st != GDN_OK) return st;
   if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: num_seqs=%d is negative", fn, num_seqs);
@@ -137,8 +161,13 @@ GDN_EXPORT gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs, 
                   cu_seqlens_host[num_seqs], total_tokens);
   }
   const gdn_problem& p = *problem;
+  if (pool) {
+    st = check_slots(*pool, num_seqs, fn);
+    if (st != GDN_OK) return st;
+  }
   const size_t es = io_size(p.io_dtype);
-  const size_t state_bytes = static_cast<size_t>(num_seqs) * p.h_v * p.d_k * p.d_v * sizeof(float);
+  const int64_t state_count = pool ? pool->num_slots : num_seqs;
+  const size_t state_bytes = static_cast<size_t>(state_count) * p.h_v * p.d_k * p.d_v * sizeof(float);
   const size_t out_bytes = static_cast<size_t>(total_tokens) * p.h_v * p.d_v * es;
   if (final_state && initial_state && final_state != initial_state &&
       overlaps(final_state, state_bytes, initial_state, state_bytes))
@@ -160,6 +189,8 @@ GDN_EXPORT gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs, 
   sp.out = out;
   sp.sN = final_state;
   sp.cu = cu_seqlens;
+  sp.slots = pool ? pool->slots : nullptr;
+  sp.num_slots = pool ? pool->num_slots : 0;
   sp.num_seqs = num_seqs;
   sp.h_qk = p.h_qk;
   sp.h_v = p.h_v;
@@ -188,20 +219,53 @@ GDN_EXPORT gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs, 
   return ok();
 }
 
-GDN_EXPORT gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch, const void* q, const void* k,
-                                      const void* v, float* state, void* out, hipStream_t stream) {
-  const char* fn = "gdn_decode_step";
+}  // namespace
+
+GDN_EXPORT gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int32_t total_tokens, const void* q,
+                                  const void* k, const void* v, const float* initial_state, void* out,
+                                  float* final_state, hipStream_t stream) {
+  return prefill_impl("gdn_prefill", problem, num_seqs, cu_seqlens, cu_seqlens_host, total_tokens, q, k, v,
+                      initial_state, out, final_state, nullptr, stream);
+}
+
+GDN_EXPORT gdn_status gdn_prefill_slots(const gdn_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
+                                        const int32_t* cu_seqlens_host, int32_t total_tokens, const void* q,
+                                        const void* k, const void* v, float* state_pool, int32_t num_slots,
+                                        const int32_t* slots, const int32_t* slots_host, void* out,
+                                        hipStream_t stream) {
+  const char* fn = "gdn_prefill_slots";
+  if (num_slots > 0 && !state_pool) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_pool is NULL", fn);
+  SlotArgs sl;
+  sl.slots = slots;
+  sl.slots_host = slots_host;
+  sl.num_slots = num_slots;
+  return prefill_impl(fn, problem, num_seqs, cu_seqlens, cu_seqlens_host, total_tokens, q, k, v, state_pool, out,
+                      state_pool, &sl, stream);
+}
+
+namespace {
+
+gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch, const void* q, const void* k,
+                       const void* v, float* state, void* out, const SlotArgs* pool, hipStream_t stream) {
   gdn_status st = check_problem(problem, fn, batch > 0);
   if (st != GDN_OK) return st;
   if (batch < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: batch=%d is negative", fn, batch);
   if (batch == 0) return ok();
-  if (!q || !k || !v || !state || !out)
+  if (pool) {
+    st = check_slots(*pool, batch, fn);
+    if (st != GDN_OK) return st;
+  }
+  // an empty pool (every sequence padding) needs no state buffer
+  const bool needs_state = !(pool && pool->num_slots == 0);
+  if (!q || !k || !v || !out || (needs_state && !state))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, state and out are required", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(out))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, state and out must be 16-byte aligned", fn);
   const gdn_problem& p = *problem;
   const size_t es = io_size(p.io_dtype);
-  const size_t state_bytes = static_cast<size_t>(batch) * p.h_v * p.d_k * p.d_v * sizeof(float);
+  const int64_t state_count = pool ? pool->num_slots : batch;
+  const size_t state_bytes = static_cast<size_t>(state_count) * p.h_v * p.d_k * p.d_v * sizeof(float);
   const size_t out_bytes = static_cast<size_t>(batch) * p.h_v * p.d_v * es;
   const size_t qk_bytes = static_cast<size_t>(batch) * p.h_qk * p.d_k * es;
   const size_t v_bytes = static_cast<size_t>(batch) * p.h_v * p.d_v * es;
@@ -219,6 +283,8 @@ GDN_EXPORT gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch,
   dp.gates = gate_args(problem);
   dp.state = state;
   dp.out = out;
+  dp.slots = pool ? pool->slots : nullptr;
+  dp.num_slots = pool ? pool->num_slots : 0;
   dp.batch = batch;
   dp.h_qk = p.h_qk;
   dp.h_v = p.h_v;
@@ -235,6 +301,26 @@ GDN_EXPORT gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch,
   const hipError_t e = gdn::launch_decode_step(dp, p.io_dtype == GDN_BF16, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+GDN_EXPORT gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch, const void* q, const void* k,
+                                      const void* v, float* state, void* out, hipStream_t stream) {
+  return decode_impl("gdn_decode_step", problem, batch, q, k, v, state, out, nullptr, stream);
+}
+
+GDN_EXPORT gdn_status gdn_decode_step_slots(const gdn_problem* problem, int32_t batch, const void* q,
+                                            const void* k, const void* v, float* state_pool, int32_t num_slots,
+                                            const int32_t* slots, const int32_t* slots_host, void* out,
+                                            hipStream_t stream) {
+  const char* fn = "gdn_decode_step_slots";
+  if (num_slots > 0 && !state_pool) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_pool is NULL", fn);
+  SlotArgs sl;
+  sl.slots = slots;
+  sl.slots_host = slots_host;
+  sl.num_slots = num_slots;
+  return decode_impl(fn, problem, batch, q, k, v, num_slots > 0 ? state_pool : nullptr, out, &sl, stream);
 }
 
 GDN_EXPORT gdn_status gdn_gate_prologue(int32_t tokens, int32_t h_v, int32_t io_dtype, const void* a,

@@ -28,6 +28,11 @@ struct ScanParams {
   void* out;              // [T, h_v, d_v] or null
   float* sN;              // [N, h_v, d_k, d_v] or null
   const int32_t* cu;      // [N + 1]
+  // State pool indirection: when slots != null, sequence n's state is
+  // s0/sN[slots[n]] (both point at the pool); a slot outside [0, num_slots)
+  // starts from zeros and is not written back.
+  const int32_t* slots;   // [N] or null (state n belongs to sequence n)
+  int32_t num_slots;
   int32_t num_seqs;
   int32_t h_qk, h_v, d_k, d_v;
   int32_t ratio;          // h_v / h_qk
@@ -41,8 +46,10 @@ struct DecodeParams {
   const void* k;          // [B, h_qk, d_k]
   const void* v;          // [B, h_v, d_v]
   GateArgs gates;
-  float* state;           // [B, h_v, d_k, d_v]
+  float* state;           // [B, h_v, d_k, d_v], or the pool [num_slots, ...] when slots != null
   void* out;              // [B, h_v, d_v]
+  const int32_t* slots;   // [B] or null; see ScanParams
+  int32_t num_slots;
   int32_t batch;
   int32_t h_qk, h_v, d_k, d_v;
   int32_t ratio;
@@ -72,6 +79,17 @@ hipError_t launch_gate_prologue(GatePrologueParams p, int io_bf16, hipStream_t s
 bool chunked_supported(int io_bf16, int d_k, int d_v);
 int chunked_columns_per_block(int d_k, int d_v);
 hipError_t launch_prefill_chunked(ScanParams p, int io_bf16, hipStream_t stream);
+
+// Index of sequence n's state and whether it exists (slot-pool indirection).
+__device__ __forceinline__ int state_slot(const int32_t* slots, int32_t num_slots, int n, bool* valid) {
+  if (slots == nullptr) {
+    *valid = true;
+    return n;
+  }
+  const int s = slots[n];
+  *valid = s >= 0 && s < num_slots;
+  return *valid ? s : 0;
+}
 
 // Columns one scan wave owns for a given d_k (used to size the grid).
 int scan_columns_per_wave(int d_k);

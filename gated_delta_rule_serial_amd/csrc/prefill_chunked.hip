@@ -171,7 +171,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
   const int t_begin = p.cu[n];
   const int t_end = p.cu[n + 1];
   const int d_v = p.d_v;
-  const size_t sbase = (static_cast<size_t>(n) * p.h_v + h) * static_cast<size_t>(DK) * d_v;
+  bool has_state;
+  const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
+  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(DK) * d_v;
 
   // ---- state slice in accumulators: wave w owns state tiles w*STW .. w*STW+STW-1
   //      (tile index = row tile * CT + column tile)
@@ -183,7 +185,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * ri + acc_row(lane, i);
       const int col = J0 + 16 * cj + acc_col(lane);
-      S[e][i] = (p.s0 != nullptr && col < d_v) ? p.s0[sbase + static_cast<size_t>(row) * d_v + col] : 0.0f;
+      S[e][i] = (p.s0 != nullptr && has_state && col < d_v) ? p.s0[sbase + static_cast<size_t>(row) * d_v + col]
+                                                             : 0.0f;
     }
   }
   auto publish_state = [&]() {  // S^T (bf16) for the next chunk's X = W S and Y = Q S
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
   }
 
   // ---- final state
-  if (p.sN != nullptr) {
+  if (p.sN != nullptr && has_state) {
 #pragma unroll
     for (int e = 0; e < STW; ++e) {
       const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;

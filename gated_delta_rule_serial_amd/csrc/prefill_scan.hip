@@ -63,12 +63,15 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   const int t_end = p.cu[n + 1];
 
   // ---- initial state (column j, rows row0 .. row0 + RPL - 1)
+  bool has_state;
+  const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
   float S[RPL];
-  const size_t sbase = (static_cast<size_t>(n) * p.h_v + h) * static_cast<size_t>(p.d_k) * p.d_v;
+  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(p.d_k) * p.d_v;
 #pragma unroll
   for (int m = 0; m < RPL; ++m) {
     const int i = row0 + m;
-    S[m] = (p.s0 != nullptr && col_ok && i < p.d_k) ? p.s0[sbase + static_cast<size_t>(i) * p.d_v + j] : 0.0f;
+    S[m] = (p.s0 != nullptr && has_state && col_ok && i < p.d_k) ? p.s0[sbase + static_cast<size_t>(i) * p.d_v + j]
+                                                                  : 0.0f;
   }
 
   const IO* __restrict__ qg = static_cast<const IO*>(p.q);
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   }
 
   // ---- final state
-  if (p.sN != nullptr && col_ok) {
+  if (p.sN != nullptr && has_state && col_ok) {
 #pragma unroll
     for (int m = 0; m < RPL; ++m) {
       const int i = row0 + m;

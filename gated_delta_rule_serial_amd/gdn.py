@@ -65,6 +65,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_prefill.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_prefill_slots.argtypes = [pp, i32, vp, ip, i32, vp, vp, vp, vp, i32, vp, ip, vp, vp]
+    lib.gdn_prefill_slots.restype = ctypes.c_int
+    lib.gdn_decode_step_slots.argtypes = [pp, i32, vp, vp, vp, vp, i32, vp, ip, vp, vp]
+    lib.gdn_decode_step_slots.restype = ctypes.c_int
     lib.gdn_gate_prologue.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_gate_prologue.restype = ctypes.c_int
     lib.gdn_last_error.argtypes = []
@@ -163,6 +167,44 @@ def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: to
                         A_log=A_log, dt_bias=dt_bias)
     _check(load().gdn_decode_step(ctypes.byref(prob), B, _ptr(q), _ptr(k), _ptr(v), _ptr(state), _ptr(out),
                                   _stream(stream, q.device)))
+
+
+def _host_i32(vals):
+    if vals is None:
+        return None
+    vals = [int(x) for x in vals]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def gdn_prefill_slots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                      state_pool: torch.Tensor, slots: torch.Tensor, *, out: Optional[torch.Tensor], g=None,
+                      beta=None, a=None, b=None, A_log=None, dt_bias=None, scale: float = 0.0,
+                      cu_seqlens_host: Optional[Sequence[int]] = None, slots_host: Optional[Sequence[int]] = None,
+                      algorithm: str = "auto", stream=None) -> None:
+    """gdn_prefill_slots of include/gdn.h: sequence i runs from and writes back
+    state_pool[slots[i]] (float32 [num_slots, h_v, d_k, d_v])."""
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
+                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm)
+    n = cu_seqlens.numel() - 1
+    _check(load().gdn_prefill_slots(ctypes.byref(prob), n, _ptr(cu_seqlens), _host_i32(cu_seqlens_host), T,
+                                    _ptr(q), _ptr(k), _ptr(v), _ptr(state_pool), state_pool.shape[0], _ptr(slots),
+                                    _host_i32(slots_host), _ptr(out), _stream(stream, q.device)))
+
+
+def gdn_decode_step_slots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state_pool: torch.Tensor,
+                          slots: torch.Tensor, out: torch.Tensor, *, g=None, beta=None, a=None, b=None,
+                          A_log=None, dt_bias=None, scale: float = 0.0,
+                          slots_host: Optional[Sequence[int]] = None, stream=None) -> None:
+    """gdn_decode_step_slots of include/gdn.h: sequence i updates state_pool[slots[i]] in place."""
+    B, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
+                        A_log=A_log, dt_bias=dt_bias)
+    _check(load().gdn_decode_step_slots(ctypes.byref(prob), B, _ptr(q), _ptr(k), _ptr(v), _ptr(state_pool),
+                                        state_pool.shape[0], _ptr(slots), _host_i32(slots_host), _ptr(out),
+                                        _stream(stream, q.device)))
 
 
 def gdn_gate_prologue(a: torch.Tensor, b: Optional[torch.Tensor], A_log: torch.Tensor, dt_bias: torch.Tensor,

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -147,6 +147,35 @@ gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs,
 gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch,
                            const void* q, const void* k, const void* v,
                            float* state, void* out, hipStream_t stream);
+
+/*
+ * Slot-indexed state pool ([P3] nuvec-core, fast/imp.rs, `gated_delta_slots`:
+ * recurrent states live in a pool and each sequence of a batch names its
+ * state by an int32 slot; the state is gathered, run and scattered back).
+ *
+ *   state_pool  [num_slots, h_v, d_k, d_v] float32, read and updated in place
+ *   slots       device int32 [n] (n = num_seqs or batch): sequence i uses
+ *               state_pool[slots[i]].  A slot outside [0, num_slots) marks a
+ *               padding sequence: it runs from a zero state and nothing is
+ *               written back for it (its outputs are still written).  Slots
+ *               inside the range must be distinct.
+ *   slots_host  optional host copy of slots; when given, distinctness is
+ *               checked (GDN_ERR_INVALID_ARGUMENT on a repeated slot).  The
+ *               kernels bounds-check every slot they read.
+ * Everything else is as in gdn_prefill / gdn_decode_step.
+ */
+gdn_status gdn_prefill_slots(const gdn_problem* problem, int32_t num_seqs,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             int32_t total_tokens, const void* q, const void* k,
+                             const void* v, float* state_pool, int32_t num_slots,
+                             const int32_t* slots, const int32_t* slots_host,
+                             void* out, hipStream_t stream);
+
+gdn_status gdn_decode_step_slots(const gdn_problem* problem, int32_t batch,
+                                 const void* q, const void* k, const void* v,
+                                 float* state_pool, int32_t num_slots,
+                                 const int32_t* slots, const int32_t* slots_host,
+                                 void* out, hipStream_t stream);
 
 /*
  * gdn_gate_prologue -- the gate prologue alone ([P1] `linear_attention_gate_op`,

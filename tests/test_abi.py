@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 2
+    assert gdn.abi_version() == 3
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -147,3 +147,25 @@ def test_gate_prologue_validation(lib, args, status, needle):
                                None)
     assert st == status, gdn.last_error()
     assert needle in gdn.last_error()
+
+
+def test_slot_validation(lib):
+    vp = ctypes.c_void_p
+    prob = _prob()
+    host = (ctypes.c_int32 * 3)(2, 5, 2)
+    cu_host = (ctypes.c_int32 * 4)(0, 2, 4, 8)
+    st = lib.gdn_prefill_slots(ctypes.byref(prob), 3, vp(FAKE + 0x2000), cu_host, 8, vp(FAKE + 0x10000),
+                               vp(FAKE + 0x20000), vp(FAKE + 0x30000), vp(FAKE + 0x80000), 6, vp(FAKE + 0x3000),
+                               host, vp(FAKE + 0x40000), None)
+    assert st == INVALID and "slot 2 is used by sequences 0 and 2" in gdn.last_error()
+    st = lib.gdn_prefill_slots(ctypes.byref(prob), 3, vp(FAKE + 0x2000), cu_host, 8, vp(FAKE + 0x10000),
+                               vp(FAKE + 0x20000), vp(FAKE + 0x30000), None, 6, vp(FAKE + 0x3000), None,
+                               vp(FAKE + 0x40000), None)
+    assert st == INVALID and "state_pool is NULL" in gdn.last_error()
+    st = lib.gdn_decode_step_slots(ctypes.byref(prob), 4, vp(FAKE + 0x10000), vp(FAKE + 0x20000),
+                                   vp(FAKE + 0x30000), vp(FAKE + 0x80000), 6, None, None, vp(FAKE + 0x40000), None)
+    assert st == INVALID and "slots is NULL" in gdn.last_error()
+    st = lib.gdn_decode_step_slots(ctypes.byref(prob), 4, vp(FAKE + 0x10000), vp(FAKE + 0x20000),
+                                   vp(FAKE + 0x30000), vp(FAKE + 0x80000), -1, vp(FAKE + 0x3000), None,
+                                   vp(FAKE + 0x40000), None)
+    assert st == INVALID and "num_slots" in gdn.last_error()

@@ -320,3 +320,89 @@ def test_prefill_full_size_sampled(name, heads, algorithm):
         check(out[:, hv], ro, tol, f"out head group {hq}")
         check(fin[:, hv], rf, tol, f"state head group {hq}")
     assert torch.isfinite(out).all() and torch.isfinite(fin).all()
+
+
+# ------------------------------------------------------------------ slot-indexed state pool
+def _pool(num_slots, shape, seed):
+    gen = torch.Generator().manual_seed(seed)
+    return torch.randn(num_slots, shape.h_v, shape.d_k, shape.d_v, generator=gen) * 0.05
+
+
+@pytest.mark.parametrize("raw", [False, True], ids=["gates", "rawgates"])
+def test_decode_slots(raw):
+    """Decode over a pool: sequence i updates pool[slots[i]]; slot -1 and 99 are
+    padding (zero state, nothing written); untouched slots stay bit-identical."""
+    shape = _shape("decode_b64", num_seqs=6)
+    inp, g, beta = _decode_inputs(shape, 123)
+    slots = [3, 7, 0, -1, 9, 99]
+    pool = _pool(10, shape, 5)
+    say(f"[decode-slots] raw={raw} slots={slots}")
+    pool_gpu = pool.cuda()
+    slots_d = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    out = torch.empty(6, shape.h_v, shape.d_v, dtype=shape.io_dtype, device="cuda")
+    orc = oracle.default()
+    if raw:
+        gates = dict(a=to_dev(inp.a), b=to_dev(inp.b), A_log=to_dev(inp.A_log), dt_bias=to_dev(inp.dt_bias))
+        gr, br = orc.gates(inp.a, inp.b, inp.A_log, inp.dt_bias)
+    else:
+        gates = dict(g=to_dev(g), beta=to_dev(beta))
+        gr, br = g.double().numpy(), beta.double().numpy()
+    gdn.gdn_decode_step_slots(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), pool_gpu, slots_d, out,
+                              slots_host=slots, **gates)
+    torch.cuda.synchronize()
+    # oracle: gather (padding -> zeros), step, scatter back
+    st = np.stack([pool[s].double().numpy() if 0 <= s < 10 else np.zeros(pool.shape[1:]) for s in slots])
+    ro = orc.decode_step(inp.q.double().numpy(), inp.k.double().numpy(), inp.v.double().numpy(), gr, br, st)
+    ref_pool = pool.double().clone()
+    for i, s in enumerate(slots):
+        if 0 <= s < 10:
+            ref_pool[s] = torch.from_numpy(st[i])
+    check(out.double().cpu(), torch.from_numpy(ro), TOL[shape.io_dtype], "out")
+    check(pool_gpu.double().cpu(), ref_pool, TOL[shape.io_dtype], "pool")
+    for s in (1, 2, 4, 5, 6, 8):
+        assert torch.equal(pool_gpu[s].cpu(), pool[s]), f"untouched slot {s} changed"
+
+
+@pytest.mark.parametrize("algorithm", ["serial", "chunked"])
+def test_prefill_slots(algorithm):
+    shape = _shape("varlen_prefill_8seq", init_state=False)
+    inp = synth.generate(shape, seqlens=[70, 0, 33, 129])
+    g, beta = gates_for(inp)
+    slots = [5, -1, 2, 0]
+    pool = _pool(6, shape, 9)
+    say(f"[prefill-slots] {algorithm} slots={slots}")
+    pool_gpu = pool.cuda()
+    out = torch.full((inp.total_tokens, shape.h_v, shape.d_v), float("nan"), dtype=shape.io_dtype, device="cuda")
+    gdn.gdn_prefill_slots(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.cu_seqlens), pool_gpu,
+                          torch.tensor(slots, dtype=torch.int32, device="cuda"), out=out, g=to_dev(g),
+                          beta=to_dev(beta), cu_seqlens_host=inp.cu_seqlens.tolist(), slots_host=slots,
+                          algorithm=algorithm)
+    torch.cuda.synchronize()
+    s0 = torch.stack([pool[s] if 0 <= s < 6 else torch.zeros(pool.shape[1:]) for s in slots])
+    ref_inp = dataclasses.replace(inp, initial_state=s0)
+    ro, rf = oracle_prefill(ref_inp, g, beta)
+    ref_pool = pool.double().clone()
+    for i, s in enumerate(slots):
+        if 0 <= s < 6:
+            ref_pool[s] = rf[i]
+    check(out.double().cpu(), ro, TOL[shape.io_dtype], "out")
+    check(pool_gpu.double().cpu(), ref_pool, TOL[shape.io_dtype], "pool")
+    for s in (1, 3, 4):
+        assert torch.equal(pool_gpu[s].cpu(), pool[s]), f"untouched slot {s} changed"
+
+
+def test_slots_identity_equals_plain():
+    """slots = 0..N-1 over a pool is the plain call with the pool as in/out state (bitwise)."""
+    shape = _shape("varlen_prefill_8seq", init_state=True)
+    inp = synth.generate(shape, seqlens=[40, 90, 7])
+    g, beta = gates_for(inp)
+    say("[slots-identity]")
+    out_a, fin_a = gpu_prefill(inp, g, beta, algorithm="serial")
+    pool = to_dev(inp.initial_state).clone()
+    out_b = torch.empty(inp.total_tokens, shape.h_v, shape.d_v, dtype=shape.io_dtype, device="cuda")
+    gdn.gdn_prefill_slots(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.cu_seqlens), pool,
+                          torch.arange(3, dtype=torch.int32, device="cuda"), out=out_b, g=to_dev(g),
+                          beta=to_dev(beta), algorithm="serial")
+    torch.cuda.synchronize()
+    assert torch.equal(out_b.double().cpu(), out_a)
+    assert torch.equal(pool.double().cpu(), fin_a)
