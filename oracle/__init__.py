@@ -73,6 +73,9 @@ class Oracle:
         lib.gdnref_prefill.argtypes = [i32, i32, i32, i32, i32, f64, i32, ip,
                                        dp, dp, dp, dp, dp, dp, dp, dp]
         lib.gdnref_prefill.restype = ctypes.c_int
+        lib.gdnref_prefill_ex.argtypes = [i32, i32, i32, i32, i32, f64, i32, ip,
+                                          dp, dp, dp, dp, dp, i32, i32, dp, dp, dp, i32, dp]
+        lib.gdnref_prefill_ex.restype = ctypes.c_int
         lib.gdnref_decode_step.argtypes = [i32, i32, i32, i32, i32, f64, i32,
                                            dp, dp, dp, dp, dp, dp, dp]
         lib.gdnref_decode_step.restype = ctypes.c_int
@@ -102,13 +105,16 @@ class Oracle:
         return g, beta
 
     def prefill(self, q, k, v, g, beta, cu_seqlens, initial_state=None, *,
-                rule="gated_delta", scale=0.0, want_out=True):
+                rule="gated_delta", scale=0.0, want_out=True, decay_per_key=False,
+                beta_shared=False, window=0):
         """Serial scan over packed sequences.
 
-        q, k: [T, h_qk, d_k]; v: [T, h_v, d_v]; g, beta: [T, h_v] (None when the
-        rule does not use them); cu_seqlens: ints [N+1]; initial_state:
+        q, k: [T, h_qk, d_k]; v: [T, h_v, d_v]; g: [T, h_v] ([T, h_v, d_k] with
+        decay_per_key); beta: [T, h_v] ([T] with beta_shared) -- None when the
+        rule does not use them; cu_seqlens: ints [N+1]; initial_state:
         [N, h_v, d_k, d_v] or None.  Returns (out [T, h_v, d_v], final
-        [N, h_v, d_k, d_v]) as float64 arrays.
+        [N, h_v, d_k, d_v]) as float64 arrays, plus the state history
+        [N, window, h_v, d_k, d_v] when window > 0.
         """
         q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
         s0 = _f64(initial_state)
@@ -118,12 +124,14 @@ class Oracle:
         n = cu.size - 1
         out = np.empty((T, h_v, d_v), np.float64) if want_out else None
         fin = np.empty((n, h_v, d_k, d_v), np.float64)
-        rc = self.lib.gdnref_prefill(RULES[rule], h_qk, h_v, d_k, d_v, float(scale), n,
-                                     _ptr(cu, ctypes.c_int32), _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(g), _ptr(beta), _ptr(s0), _ptr(out), _ptr(fin))
+        hist = np.empty((n, window, h_v, d_k, d_v), np.float64) if window > 0 else None
+        rc = self.lib.gdnref_prefill_ex(RULES[rule], h_qk, h_v, d_k, d_v, float(scale), n,
+                                        _ptr(cu, ctypes.c_int32), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(g), _ptr(beta), int(decay_per_key), int(beta_shared),
+                                        _ptr(s0), _ptr(out), _ptr(fin), int(window), _ptr(hist))
         if rc != 0:
-            raise ValueError("gdnref_prefill rejected its arguments")
-        return out, fin
+            raise ValueError("gdnref_prefill_ex rejected its arguments")
+        return (out, fin, hist) if window > 0 else (out, fin)
 
     def decode_step(self, q, k, v, g, beta, state, *, rule="gated_delta", scale=0.0):
         """One token per sequence; ``state`` (float64 [B, h_v, d_k, d_v]) is updated in place."""

@@ -63,23 +63,36 @@ static void scan_unit(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
                       int32_t d_v, double scale, int64_t t0, int64_t t1,
                       int32_t h, const double* q, const double* k,
                       const double* v, const double* g, const double* beta,
-                      double* S, double* r, double* d, double* out) {
+                      int32_t decay_per_key, int32_t beta_shared, int32_t window,
+                      double* history, double* S, double* r, double* d, double* out) {
   const int32_t hq = h / (h_v / h_qk); /* consecutive value heads share q/k */
+  const int64_t state_elems = (int64_t)d_k * d_v;
+  /* history slots before the first token stay zero ([P1] state_window) */
+  for (int64_t w = 0; window > 0 && w < window - (t1 - t0); ++w)
+    memset(history + (w * h_v + h) * state_elems, 0, sizeof(double) * (size_t)state_elems);
   for (int64_t t = t0; t < t1; ++t) {
     const double* kt = k + (t * h_qk + hq) * d_k;
     const double* qt = q + (t * h_qk + hq) * d_k;
     const double* vt = v + (t * h_v + h) * d_v;
 
-    /* decay: S <- exp(g) S */
+    /* decay: S <- exp(g) S; per-key-dim decay scales row i by exp(g_i) */
     if (rule_decays(rule)) {
-      const double alpha = exp(g[t * h_v + h]);
-      for (int32_t i = 0; i < d_k; ++i)
-        for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] *= alpha;
+      if (decay_per_key) {
+        const double* gt = g + (t * h_v + h) * d_k;
+        for (int32_t i = 0; i < d_k; ++i) {
+          const double alpha_i = exp(gt[i]);
+          for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] *= alpha_i;
+        }
+      } else {
+        const double alpha = exp(g[t * h_v + h]);
+        for (int32_t i = 0; i < d_k; ++i)
+          for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] *= alpha;
+      }
     }
 
     /* retrieval r = S^T k and delta d = beta (v - r); plain rules use d = v */
     if (rule_deltas(rule)) {
-      const double bt = beta[t * h_v + h];
+      const double bt = beta_shared ? beta[t] : beta[t * h_v + h];
       for (int32_t j = 0; j < d_v; ++j) {
         double acc = 0.0;
         for (int32_t i = 0; i < d_k; ++i) acc += S[i * d_v + j] * kt[i];
@@ -103,6 +116,11 @@ static void scan_unit(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
         ot[j] = scale * acc;
       }
     }
+
+    /* state after this token, for the last `window` tokens */
+    const int64_t w = (t - t0) - ((t1 - t0) - window);
+    if (window > 0 && w >= 0)
+      memcpy(history + (w * h_v + h) * state_elems, S, sizeof(double) * (size_t)state_elems);
   }
 }
 
@@ -114,16 +132,19 @@ static int valid_geometry(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
   return 1;
 }
 
-int gdnref_prefill(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
-                   int32_t d_v, double scale, int32_t num_seqs,
-                   const int32_t* cu_seqlens, const double* q,
-                   const double* k, const double* v, const double* g,
-                   const double* beta, const double* initial_state,
-                   double* out, double* final_state) {
+int gdnref_prefill_ex(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                      int32_t d_v, double scale, int32_t num_seqs,
+                      const int32_t* cu_seqlens, const double* q,
+                      const double* k, const double* v, const double* g,
+                      const double* beta, int32_t decay_per_key,
+                      int32_t beta_shared, const double* initial_state,
+                      double* out, double* final_state, int32_t window,
+                      double* history) {
   if (!valid_geometry(rule, h_qk, h_v, d_k, d_v) || num_seqs < 0) return -1;
   if (num_seqs > 0 && !cu_seqlens) return -1;
   if (rule_decays(rule) && !g && num_seqs > 0) return -1;
   if (rule_deltas(rule) && !beta && num_seqs > 0) return -1;
+  if (window < 0 || (window > 0 && !history)) return -1;
   if (num_seqs > 0 && cu_seqlens[0] != 0) return -1;
   for (int32_t n = 0; n < num_seqs; ++n)
     if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
@@ -150,12 +171,23 @@ int gdnref_prefill(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
     else
       memset(S, 0, sizeof(double) * (size_t)state_elems);
     scan_unit(rule, h_qk, h_v, d_k, d_v, scale, cu_seqlens[n], cu_seqlens[n + 1], h,
-              q, k, v, g, beta, S, r, d, out);
+              q, k, v, g, beta, decay_per_key, beta_shared, window,
+              window > 0 ? history + (int64_t)n * window * h_v * state_elems : NULL, S, r, d, out);
     if (final_state)
       memcpy(final_state + u * state_elems, S, sizeof(double) * (size_t)state_elems);
     free(S);
   }
   return failed ? -1 : 0;
+}
+
+int gdnref_prefill(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                   int32_t d_v, double scale, int32_t num_seqs,
+                   const int32_t* cu_seqlens, const double* q,
+                   const double* k, const double* v, const double* g,
+                   const double* beta, const double* initial_state,
+                   double* out, double* final_state) {
+  return gdnref_prefill_ex(rule, h_qk, h_v, d_k, d_v, scale, num_seqs, cu_seqlens, q, k, v, g,
+                           beta, 0, 0, initial_state, out, final_state, 0, NULL);
 }
 
 int gdnref_decode_step(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,

@@ -89,6 +89,26 @@ int gdnref_prefill(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
                    const double* beta, const double* initial_state,
                    double* out, double* final_state);
 
+/* gdnref_prefill with the variants the pages define:
+ *   decay_per_key  g is [T_total, h_v, d_k]: row i of the state decays by
+ *                  exp(g[t,h,i]) ([P4] `linear_attention_core` per-key-dim
+ *                  decay; [P1] per-head-per-key-dim decay form)
+ *   beta_shared    beta is [T_total]: one write strength per token, shared by
+ *                  all value heads ([P4] beta layout [B, T, 1])
+ *   window > 0     history [num_seqs, window, h_v, d_k, d_v] receives the
+ *                  state after each of the last `window` tokens of every
+ *                  sequence, oldest first; slots before the first token are
+ *                  zero ([P1] `state_window`; window = T gives [P3]
+ *                  `gated_delta_steps`). */
+int gdnref_prefill_ex(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
+                      int32_t d_v, double scale, int32_t num_seqs,
+                      const int32_t* cu_seqlens, const double* q,
+                      const double* k, const double* v, const double* g,
+                      const double* beta, int32_t decay_per_key,
+                      int32_t beta_shared, const double* initial_state,
+                      double* out, double* final_state, int32_t window,
+                      double* history);
+
 /* One token per sequence, state read and written in place:
  * identical to gdnref_prefill with cu_seqlens = {0, 1, ..., batch}. */
 int gdnref_decode_step(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,

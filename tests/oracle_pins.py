@@ -48,13 +48,15 @@ def random_case(seed, *, T_list=(5, 0, 7), h_qk=2, h_v=4, d_k=5, d_v=3, init=Tru
     return dict(q=q, k=k, v=v, g=g, beta=beta, cu=cu, s0=s0)
 
 
-def brute_force(q, k, v, g, beta, cu, s0, *, rule="gated_delta", scale=0.0):
+def brute_force(q, k, v, g, beta, cu, s0, *, rule="gated_delta", scale=0.0, decay_per_key=False,
+                beta_shared=False):
     """Unrolled matrix form, long double.
 
     Token t of a sequence maps the state by S -> A_t S + B_t with
-      A_t = alpha_t (I - beta_t k_t k_t^T),  B_t = beta_t k_t v_t^T   (delta rules)
-      A_t = alpha_t I,                       B_t = k_t v_t^T          (plain rules)
-    and alpha_t = exp(g_t) for gated rules, 1 otherwise.  The state after
+      A_t = (I - beta_t k_t k_t^T) D_t,  B_t = beta_t k_t v_t^T   (delta rules)
+      A_t = D_t,                         B_t = k_t v_t^T          (plain rules)
+    with the decay D_t = exp(g_t) I (diag(exp(g_t)) for per-key-dim decay) for
+    gated rules and D_t = I otherwise.  The state after
     token t is formed from scratch as
       S_t = (A_t ... A_1) S_0 + sum_s (A_t ... A_{s+1}) B_s
     and read out as out_t = scale S_t^T q_t.  Query/key heads are widened to
@@ -80,13 +82,18 @@ def brute_force(q, k, v, g, beta, cu, s0, *, rule="gated_delta", scale=0.0):
             A, B = [], []
             for t in toks:
                 kt = kr[t, h][:, None]
-                alpha = np.exp(LD(g[t, h])) if decays else LD(1)
+                if not decays:
+                    Dg = eye
+                elif decay_per_key:
+                    Dg = np.diag(np.exp(np.asarray(g[t, h], LD)))   # row i scaled by exp(g_i)
+                else:
+                    Dg = np.exp(LD(g[t, h])) * eye
                 if deltas:
-                    bt = LD(beta[t, h])
-                    A.append(alpha * (eye - bt * (kt @ kt.T)))
+                    bt = LD(beta[t] if beta_shared else beta[t, h])
+                    A.append((eye - bt * (kt @ kt.T)) @ Dg)
                     B.append(bt * (kt @ vv[t, h][None, :]))
                 else:
-                    A.append(alpha * eye)
+                    A.append(Dg)
                     B.append(kt @ vv[t, h][None, :])
             St = S0
             for idx, t in enumerate(toks):
@@ -353,9 +360,89 @@ def pin_rounding_tie(orc):
     assert torch.tensor(o[:, 0, 0]).to(torch.bfloat16).tolist() == [1.0, 1.0078125]
 
 
+# ---------------------------------------------------------------- variants
+def pin_variants_brute_force(orc):
+    """Per-key-dim decay, shared beta and every rule against the unrolled form."""
+    rng = np.random.default_rng(31)
+    for seed, rule, per_key, shared in [(32, "gated_delta", True, False), (33, "gated_delta", False, True),
+                                        (34, "gated", True, False), (35, "delta", False, True),
+                                        (36, "gated_delta", True, True)]:
+        x = random_case(seed, T_list=(6, 0, 5), h_qk=1, h_v=3, d_k=4, d_v=3)
+        T = x["q"].shape[0]
+        g = -np.abs(rng.standard_normal((T, 3, 4))) if per_key else x["g"]
+        beta = rng.uniform(0.05, 0.95, T) if shared else x["beta"]
+        uses_g = rule in ("gated", "gated_delta")
+        uses_b = rule in ("delta", "gated_delta")
+        o, f = orc.prefill(x["q"], x["k"], x["v"], g if uses_g else None, beta if uses_b else None, x["cu"],
+                           x["s0"], rule=rule, decay_per_key=per_key, beta_shared=shared)
+        bo, bf = brute_force(x["q"], x["k"], x["v"], g, beta, x["cu"], x["s0"], rule=rule,
+                             decay_per_key=per_key, beta_shared=shared)
+        _close(o, bo, 1e-12, f"variant out ({rule}, per_key={per_key}, shared={shared})")
+        _close(f, bf, 1e-12, f"variant state ({rule}, per_key={per_key}, shared={shared})")
+
+
+def pin_variant_reductions(orc):
+    """Per-key-dim decay with equal rows is the per-head decay; a shared beta is a
+    per-head beta broadcast over the heads (both bitwise)."""
+    x = random_case(37, T_list=(7, 3), h_qk=2, h_v=4, d_k=5, d_v=3)
+    g_rows = np.repeat(x["g"][:, :, None], 5, axis=2)
+    o1, f1 = orc.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], x["s0"])
+    o2, f2 = orc.prefill(x["q"], x["k"], x["v"], g_rows, x["beta"], x["cu"], x["s0"], decay_per_key=True)
+    _bitwise(o1, o2, "per-key decay with equal rows")
+    _bitwise(f1, f2, "per-key decay with equal rows (state)")
+    b1 = x["beta"][:, 0].copy()
+    o3, f3 = orc.prefill(x["q"], x["k"], x["v"], x["g"], b1, x["cu"], x["s0"], beta_shared=True)
+    o4, f4 = orc.prefill(x["q"], x["k"], x["v"], x["g"], np.repeat(b1[:, None], 4, axis=1), x["cu"], x["s0"])
+    _bitwise(o3, o4, "shared beta")
+    _bitwise(f3, f4, "shared beta (state)")
+
+
+def pin_state_history(orc):
+    """History slot w holds the state after token L - W + w (the final state of
+    the prefix that ends there); slots before the first token are zero."""
+    x = random_case(38, T_list=(5, 2, 0), h_qk=1, h_v=2, d_k=3, d_v=4)
+    W = 4
+    _, fin, hist = orc.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], x["s0"], window=W)
+    cu = x["cu"]
+    nonempty = [s for s in range(3) if cu[s + 1] > cu[s]]
+    _bitwise(hist[nonempty, W - 1], fin[nonempty], "last history slot = final state")
+    for s in range(3):
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        for w in range(W):
+            end = L - W + w + 1  # tokens in the prefix
+            if end <= 0:
+                assert np.all(hist[s, w] == 0.0), f"seq {s} slot {w} should be zero"
+                continue
+            _, fp = orc.prefill(x["q"][a:a + end], x["k"][a:a + end], x["v"][a:a + end], x["g"][a:a + end],
+                                x["beta"][a:a + end], [0, end], x["s0"][s:s + 1])
+            _bitwise(hist[s, w], fp[0], f"seq {s} slot {w}")
+
+
+def pin_page_worked_example_window(orc):
+    """The worked example with a state window of 4: slots before the first
+    step are zero, then the bf16 states 1.0, 1.0078125, 1.015625 in order
+    (tests/golden/p1_wide_bf16_linear_state.json)."""
+    with open(os.path.join(GOLDEN, "p1_wide_bf16_linear_state.json")) as fh:
+        fx = json.load(fh)
+    W = fx["window"]
+    for d_k in fx["d_k_cases"]:
+        for T in fx["T_cases"]:
+            q = np.zeros((T, 1, d_k))
+            q[:, 0, 0] = 1.0
+            s0 = np.zeros((1, 1, d_k, 1))
+            s0[0, 0, 0, 0] = fx["initial_state_row0"]
+            _, _, hist = orc.prefill(q, q, np.full((T, 1, 1), fx["value"]), None, None, [0, T], s0,
+                                     rule="linear", scale=fx["scale"], window=W)
+            st = torch.from_numpy(hist[0, :, 0, :, 0]).to(torch.bfloat16).double().numpy()
+            expect = [0.0] * (W - T) + fx["expected_state_bf16_after_T_steps"][:T]
+            assert st[:, 0].tolist() == expect, f"window slots d_k={d_k} T={T}: {st[:, 0].tolist()} != {expect}"
+            assert np.all(st[:, 1:] == 0.0)
+
+
 ALL_PINS = [
     pin_brute_force, pin_delta_rule_memorises, pin_frozen_state, pin_reset,
     pin_power_of_two_scaling, pin_packing_invariance, pin_continuation, pin_gqa_repeat,
     pin_empty, pin_scalar_closed_form, pin_orthonormal_keys, pin_gates_library,
-    pin_default_scale, pin_page_worked_example, pin_rounding_tie,
+    pin_default_scale, pin_page_worked_example, pin_rounding_tie, pin_variants_brute_force,
+    pin_variant_reductions, pin_state_history, pin_page_worked_example_window,
 ]

@@ -28,6 +28,10 @@ MUTANTS = [
     ("sigmoid negative branch", "return e / (1.0 + e);", "return 1.0 / (1.0 + e);"),
     ("decay sign", "g[idx] = -exp(A_log[h])", "g[idx] = exp(A_log[h])"),
     ("dt_bias dropped", "gdnref_softplus(a[idx] + dt_bias[h])", "gdnref_softplus(a[idx])"),
+    ("per-key decay row ignored", "const double alpha_i = exp(gt[i]);", "const double alpha_i = exp(gt[0]);"),
+    ("shared beta not per token", "beta_shared ? beta[t] :", "beta_shared ? beta[0] :"),
+    ("history slot off by one", "const int64_t w = (t - t0) - ((t1 - t0) - window);",
+     "const int64_t w = (t - t0) - ((t1 - t0) - window) - 1;"),
 ]
 
 
