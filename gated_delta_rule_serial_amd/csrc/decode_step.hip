@@ -1,18 +1,21 @@
 // decode_step.hip -- one gated delta-rule token per sequence, state in HBM
 // updated in place (gfx950).
 //
-// Per (sequence b, value head h), with alpha = exp(g), the state S (d_k x d_v
-// float32) is read once and written once:
-//     a = S^T k,  c = S^T q,  kq = k . q          (one pass over S)
-//     delta = beta (v - alpha a)                  (retrieval on the decayed S)
-//     o     = scale (alpha c + delta kq)          (= scale S'^T q)
-//     S'    = alpha S + k delta^T                 (written back)
+// Per (sequence b, value head h), with the decay D = diag(alpha) (alpha_i =
+// exp(g) for a per-head decay, exp(g_i) per key dimension, 1 without decay),
+// the state S (d_k x d_v float32) is read once and written once:
+//     a = S^T (alpha k),  c = S^T (alpha q),  kq = k . q   (one pass over S)
+//     delta = beta (v - a)       (retrieval on the decayed state; v for the
+//                                 rules without the delta correction)
+//     o     = scale (c + delta kq)                (= scale S'^T q)
+//     S'    = D S + k delta^T                     (written back)
 // This is the order of [P4] onnx-runtime-ep-cuda, src/kernels/
 // linear_attention.rs, `linear_attention_core` steps 1-4 (readout of the
 // updated state) with the readout expanded algebraically so that it needs no
 // second pass over S: S'^T q = alpha S^T q + delta (k . q).
 //
-// Mapping: a 256-thread workgroup owns 64 state columns of one (b, h).
+// Mapping: a 256-thread workgroup owns 64 state columns of one (b, h); the
+// grid is (column block, h, b), so no index needs an integer division.
 // Thread (rg, tc), rg in [0, 16), tc in [0, 16), holds rows
 // rg*RPT .. rg*RPT + RPT - 1 of columns 4 tc .. 4 tc + 3 in VGPRs, RPT =
 // DK / 16.  A wave's load instruction covers 4 rows x 256 contiguous bytes.
@@ -33,7 +36,9 @@ constexpr int kColThreads = 16;
 constexpr int kColsPerThread = 4;
 constexpr int kBlockCols = kColThreads * kColsPerThread;  // 64
 
-template <typename IO, int DK, bool RAW>
+// FULL: d_k == DK and d_v a multiple of the block's 64 columns, so every
+// thread's tile lies inside the state and the accesses need no masks.
+template <typename IO, int DK, bool PERKEY, bool FULL>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   constexpr int RPT = DK / kRowGroups;
   __shared__ float red_a[kRowGroups][kBlockCols];
@@ -44,39 +49,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int tid = static_cast<int>(threadIdx.x);
   const int tc = tid % kColThreads;
   const int rg = tid / kColThreads;
-  int unit = static_cast<int>(blockIdx.x);
-  const int cb = unit % p.col_blocks;
-  unit /= p.col_blocks;
-  const int h = unit % p.h_v;
-  const int b = unit / p.h_v;
+  const int cb = static_cast<int>(blockIdx.x);
+  const int h = static_cast<int>(blockIdx.y);
+  const int b = p.b_offset + static_cast<int>(blockIdx.z);
   const int hq = h / p.ratio;
-  const int d_k = p.d_k, d_v = p.d_v;
+  const int d_k = FULL ? DK : p.d_k, d_v = p.d_v;
   const int j0 = cb * kBlockCols + tc * kColsPerThread;  // first column of this thread
   const int row0 = rg * RPT;
-  const bool vec_cols = (d_v % 4 == 0) && (j0 + kColsPerThread <= d_v);
+  const bool vec_cols = FULL || ((d_v % 4 == 0) && (j0 + kColsPerThread <= d_v));
 
   bool has_state;
   const int sidx = state_slot(p.slots, p.num_slots, b, &has_state);
   float* __restrict__ Sg = p.state + (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(d_k) * d_v;
 
-  // ---- state tile (issued first: it is the long-latency traffic)
+  // ---- state tile (issued first: it is the long-latency traffic); a padding
+  //      slot starts from zeros
   float S[RPT][kColsPerThread];
+  if (!has_state) {
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = row0 + m;
-    if (!has_state) {
+    for (int m = 0; m < RPT; ++m)
 #pragma unroll
       for (int cc = 0; cc < kColsPerThread; ++cc) S[m][cc] = 0.0f;
-    } else if (i < d_k && vec_cols) {
-      const float4 x = load_stream4(Sg + static_cast<size_t>(i) * d_v + j0);
-      S[m][0] = x.x;
-      S[m][1] = x.y;
-      S[m][2] = x.z;
-      S[m][3] = x.w;
-    } else {
+  } else {
 #pragma unroll
-      for (int cc = 0; cc < kColsPerThread; ++cc)
-        S[m][cc] = (i < d_k && j0 + cc < d_v) ? Sg[static_cast<size_t>(i) * d_v + j0 + cc] : 0.0f;
+    for (int m = 0; m < RPT; ++m) {
+      const int i = row0 + m;
+      if (FULL || (i < d_k && vec_cols)) {
+        const float4 x = load_stream4(Sg + static_cast<size_t>(i) * d_v + j0);
+        S[m][0] = x.x;
+        S[m][1] = x.y;
+        S[m][2] = x.z;
+        S[m][3] = x.w;
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < kColsPerThread; ++cc)
+          S[m][cc] = (i < d_k && j0 + cc < d_v) ? Sg[static_cast<size_t>(i) * d_v + j0 + cc] : 0.0f;
+      }
     }
   }
 
@@ -84,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const IO* kq_base_k = static_cast<const IO*>(p.k) + (static_cast<size_t>(b) * p.h_qk + hq) * d_k + row0;
   const IO* kq_base_q = static_cast<const IO*>(p.q) + (static_cast<size_t>(b) * p.h_qk + hq) * d_k + row0;
   RawSlice<IO, RPT> rk, rq;
-  if (d_k == DK) {
+  if (FULL || d_k == DK) {
     rk.load(kq_base_k);
     rq.load(kq_base_q);
   } else {
@@ -92,22 +100,56 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     rq.load_masked(kq_base_q, d_k - row0);
   }
 
-  // ---- gates (one value per (b, h))
+  // ---- gates: beta per (b, h) (or per b); the decay per (b, h) or, per key
+  //      dimension, per row of this thread (alpha_r).
   const size_t gidx = static_cast<size_t>(b) * p.h_v + h;
-  float alpha, beta;
-  if constexpr (RAW) {
-    const float a = widen(static_cast<const IO*>(p.gates.a)[gidx]);
-    const float bb = widen(static_cast<const IO*>(p.gates.b)[gidx]);
-    alpha = expf(gate_log_decay(a, p.gates.A_log[h], p.gates.dt_bias[h]));
-    beta = gate_sigmoid(bb);
-  } else {
-    alpha = expf(widen(static_cast<const IO*>(p.gates.g)[gidx]));
-    beta = widen(static_cast<const IO*>(p.gates.beta)[gidx]);
+  const bool decays = p.gates.decays != 0, deltas = p.gates.deltas != 0;
+  float beta = 0.0f;
+  if (deltas) {
+    const size_t bi = p.gates.beta_shared ? static_cast<size_t>(b) : gidx;
+    if (p.gates.raw) beta = gate_sigmoid(widen(static_cast<const IO*>(p.gates.b)[bi]));
+    else beta = widen(static_cast<const IO*>(p.gates.beta)[bi]);
+  }
+  // per-head decay: one alpha, applied to the column sums; per key dimension:
+  // alpha_r for this thread's rows, folded into k and q
+  float alpha = 1.0f;
+  float alpha_r[PERKEY ? RPT : 1];
+  if constexpr (PERKEY) {
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int i = row0 + m;
+      float lg = 0.0f;
+      if (decays && i < d_k) {
+        const size_t gi = gidx * d_k + i;
+        const size_t pi = static_cast<size_t>(h) * d_k + i;
+        if (p.gates.raw)
+          lg = gate_log_decay(widen(static_cast<const IO*>(p.gates.a)[gi]), p.gates.A_log[pi], p.gates.dt_bias[pi]);
+        else
+          lg = widen(static_cast<const IO*>(p.gates.g)[gi]);
+      }
+      alpha_r[m] = expf(lg);
+    }
+  } else if (decays) {
+    float lg;
+    if (p.gates.raw)
+      lg = gate_log_decay(widen(static_cast<const IO*>(p.gates.a)[gidx]), p.gates.A_log[h], p.gates.dt_bias[h]);
+    else
+      lg = widen(static_cast<const IO*>(p.gates.g)[gidx]);
+    alpha = expf(lg);
   }
 
   float kf[RPT], qf[RPT];
   rk.widen_to(kf);
   rq.widen_to(qf);
+  // the decayed state's retrieval and readout sums: (diag(alpha) S)^T x = S^T (alpha x)
+  float ka[PERKEY ? RPT : 1], qa[PERKEY ? RPT : 1];
+  if constexpr (PERKEY) {
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      ka[m] = alpha_r[m] * kf[m];
+      qa[m] = alpha_r[m] * qf[m];
+    }
+  }
 
   // ---- partial column sums over this thread's rows
   float pa[kColsPerThread], pc[kColsPerThread];
@@ -121,15 +163,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   for (int m = 0; m < RPT; ++m) {
 #pragma unroll
     for (int cc = 0; cc < kColsPerThread; ++cc) {
-      pa[cc] = fmaf(S[m][cc], kf[m], pa[cc]);
-      pc[cc] = fmaf(S[m][cc], qf[m], pc[cc]);
+      pa[cc] = fmaf(S[m][cc], PERKEY ? ka[PERKEY ? m : 0] : kf[m], pa[cc]);
+      pc[cc] = fmaf(S[m][cc], PERKEY ? qa[PERKEY ? m : 0] : qf[m], pc[cc]);
     }
     pkq = fmaf(kf[m], qf[m], pkq);
   }
 #pragma unroll
   for (int cc = 0; cc < kColsPerThread; ++cc) {
-    red_a[rg][tc * kColsPerThread + cc] = pa[cc];
-    red_c[rg][tc * kColsPerThread + cc] = pc[cc];
+    red_a[rg][tc * kColsPerThread + cc] = PERKEY ? pa[cc] : alpha * pa[cc];
+    red_c[rg][tc * kColsPerThread + cc] = PERKEY ? pc[cc] : alpha * pc[cc];
   }
   if (tc == 0) red_kq[rg] = pkq;
   __syncthreads();
@@ -145,11 +187,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     const int j = cb * kBlockCols + tid;
     float vv = 0.0f;
-    if (j < d_v) vv = widen(static_cast<const IO*>(p.v)[(static_cast<size_t>(b) * p.h_v + h) * d_v + j]);
-    const float delta = beta * (vv - alpha * a);
+    if (FULL || j < d_v) vv = widen(static_cast<const IO*>(p.v)[(static_cast<size_t>(b) * p.h_v + h) * d_v + j]);
+    const float delta = deltas ? beta * (vv - a) : vv;
     sh_delta[tid] = delta;
-    if (j < d_v) {
-      const float o = p.scale * fmaf(alpha, cs, delta * kq);
+    if (FULL || j < d_v) {
+      const float o = p.scale * fmaf(delta, kq, cs);
       narrow_store(static_cast<IO*>(p.out) + (static_cast<size_t>(b) * p.h_v + h) * d_v + j, o);
     }
   }
@@ -164,10 +206,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int i = row0 + m;
     float o4[kColsPerThread];
 #pragma unroll
-    for (int cc = 0; cc < kColsPerThread; ++cc) o4[cc] = fmaf(S[m][cc], alpha, kf[m] * dl[cc]);
+    for (int cc = 0; cc < kColsPerThread; ++cc)
+      o4[cc] = fmaf(S[m][cc], PERKEY ? alpha_r[PERKEY ? m : 0] : alpha, kf[m] * dl[cc]);
     if (!has_state) {
       // padding slot: the updated state is discarded
-    } else if (i < d_k && vec_cols) {
+    } else if (FULL || (i < d_k && vec_cols)) {
       store_stream4(Sg + static_cast<size_t>(i) * d_v + j0, make_float4(o4[0], o4[1], o4[2], o4[3]));
     } else if (i < d_k) {
 #pragma unroll
@@ -177,15 +220,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 }
 
+template <typename IO, int DK, bool PERKEY, bool FULL>
+hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
+  // grid: (column block, value head, sequence); the sequence axis is split
+  // into launches of at most 65535
+  constexpr int kMaxZ = 65535;
+  for (int off = 0; off < p.batch; off += kMaxZ) {
+    p.b_offset = off;
+    const unsigned nz = static_cast<unsigned>(p.batch - off < kMaxZ ? p.batch - off : kMaxZ);
+    hipLaunchKernelGGL((decode_kernel<IO, DK, PERKEY, FULL>),
+                       dim3(static_cast<unsigned>(p.col_blocks), static_cast<unsigned>(p.h_v), nz),
+                       dim3(kThreads), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <typename IO, int DK>
 hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
-  const unsigned blocks = static_cast<unsigned>(p.batch) * p.h_v * p.col_blocks;
-  if (blocks == 0) return hipSuccess;
-  if (p.gates.raw)
-    hipLaunchKernelGGL((decode_kernel<IO, DK, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_kernel<IO, DK, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  if (p.batch == 0 || p.h_v == 0 || p.col_blocks == 0) return hipSuccess;
+  const bool per_key = p.gates.per_key && p.gates.decays;
+  const bool full = p.d_k == DK && p.d_v % kBlockCols == 0;
+  if (per_key) return full ? launch_grid<IO, DK, true, true>(p, stream) : launch_grid<IO, DK, true, false>(p, stream);
+  return full ? launch_grid<IO, DK, false, true>(p, stream) : launch_grid<IO, DK, false, false>(p, stream);
 }
 
 template <typename IO>

@@ -50,6 +50,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 size_t io_size(int32_t dtype) { return dtype == GDN_BF16 ? 2 : 4; }
 
+bool rule_decays(int32_t rule) { return rule == GDN_RULE_GATED_DELTA || rule == GDN_RULE_GATED; }
+bool rule_deltas(int32_t rule) { return rule == GDN_RULE_GATED_DELTA || rule == GDN_RULE_DELTA; }
+
 // Shared checks of the geometry and the gate inputs.  The per-token gate
 // tensors are required only when there are tokens to read them for.
 gdn_status check_problem(const gdn_problem* p, const char* fn, bool has_tokens) {
@@ -69,13 +72,18 @@ gdn_status check_problem(const gdn_problem* p, const char* fn, bool has_tokens) 
     return fail(GDN_ERR_UNSUPPORTED, "%s: io_dtype %d is not supported (GDN_F32, GDN_BF16)", fn, p->io_dtype);
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
   const size_t es = io_size(p->io_dtype);
+  if (p->rule < GDN_RULE_GATED_DELTA || p->rule > GDN_RULE_LINEAR)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: unknown rule %d", fn, p->rule);
+  if ((p->decay_per_key != 0 && p->decay_per_key != 1) || (p->beta_shared != 0 && p->beta_shared != 1))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: decay_per_key and beta_shared must be 0 or 1", fn);
+  const bool decays = rule_decays(p->rule), deltas = rule_deltas(p->rule);
   if (p->gate_mode == GDN_GATES_PRECOMPUTED) {
-    if (has_tokens && (!p->g || !p->beta))
+    if (has_tokens && ((decays && !p->g) || (deltas && !p->beta)))
       return fail(GDN_ERR_INVALID_ARGUMENT, "%s: precomputed gates need g and beta", fn);
     if (!aligned_to(p->g, es) || !aligned_to(p->beta, es))
       return fail(GDN_ERR_INVALID_ARGUMENT, "%s: g / beta are not aligned to their element size", fn);
   } else if (p->gate_mode == GDN_GATES_RAW) {
-    if (has_tokens && (!p->a || !p->b || !p->A_log || !p->dt_bias))
+    if (has_tokens && ((decays && (!p->a || !p->A_log || !p->dt_bias)) || (deltas && !p->b)))
       return fail(GDN_ERR_INVALID_ARGUMENT, "%s: raw gates need a, b, A_log and dt_bias", fn);
     if (!aligned_to(p->a, es) || !aligned_to(p->b, es) || !aligned_to(p->A_log, 4) ||
         !aligned_to(p->dt_bias, 4))
@@ -83,6 +91,9 @@ gdn_status check_problem(const gdn_problem* p, const char* fn, bool has_tokens) 
   } else {
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: unknown gate_mode %d", fn, p->gate_mode);
   }
+  // a per-key-dim decay is read in row slices like k: 16-byte alignment
+  if (p->decay_per_key && !aligned16(p->gate_mode == GDN_GATES_RAW ? p->a : p->g))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a per-key-dim decay tensor must be 16-byte aligned", fn);
   if (p->algorithm != GDN_ALGO_AUTO && p->algorithm != GDN_ALGO_SERIAL && p->algorithm != GDN_ALGO_CHUNKED)
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: unknown algorithm %d", fn, p->algorithm);
   return GDN_OK;
@@ -91,6 +102,10 @@ gdn_status check_problem(const gdn_problem* p, const char* fn, bool has_tokens) 
 gdn::GateArgs gate_args(const gdn_problem* p) {
   gdn::GateArgs g{};
   g.raw = p->gate_mode == GDN_GATES_RAW ? 1 : 0;
+  g.decays = rule_decays(p->rule) ? 1 : 0;
+  g.deltas = rule_deltas(p->rule) ? 1 : 0;
+  g.per_key = p->decay_per_key;
+  g.beta_shared = p->beta_shared;
   g.g = p->g;
   g.beta = p->beta;
   g.a = p->a;
@@ -149,6 +164,12 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
       !aligned16(final_state))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, out and the states must be 16-byte aligned", fn);
   if (!aligned_to(cu_seqlens, 4)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is misaligned", fn);
+  if (problem->state_window < 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_window=%d is negative", fn, problem->state_window);
+  if (problem->state_window > 0 && num_seqs > 0 && !problem->state_history)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_window > 0 needs state_history", fn);
+  if (!aligned16(problem->state_history))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_history must be 16-byte aligned", fn);
   if (cu_seqlens_host) {
     if (cu_seqlens_host[0] != 0)
       return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens[0]=%d, expected 0", fn, cu_seqlens_host[0]);
@@ -177,8 +198,14 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   if (overlaps(out, out_bytes, q, qk_bytes) || overlaps(out, out_bytes, k, qk_bytes) ||
       overlaps(out, out_bytes, v, v_bytes) || overlaps(out, out_bytes, final_state, state_bytes))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: out overlaps an input or the final state", fn);
+  const int32_t window = problem->state_window;
+  const size_t hist_bytes = static_cast<size_t>(num_seqs) * window * p.h_v * p.d_k * p.d_v * sizeof(float);
+  if (window > 0 && (overlaps(problem->state_history, hist_bytes, out, out_bytes) ||
+                     overlaps(problem->state_history, hist_bytes, final_state, state_bytes) ||
+                     overlaps(problem->state_history, hist_bytes, initial_state, state_bytes)))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_history overlaps out or a state", fn);
 
-  if (num_seqs == 0 || (total_tokens == 0 && !final_state)) return ok();  // nothing to write
+  if (num_seqs == 0 || (total_tokens == 0 && !final_state && window == 0)) return ok();  // nothing to write
 
   gdn::ScanParams sp{};
   sp.q = q;
@@ -199,11 +226,15 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   sp.ratio = p.h_v / p.h_qk;
   sp.scale = resolved_scale(problem);
   const int io_bf16 = p.io_dtype == GDN_BF16;
-  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v);
+  sp.window = window;
+  sp.history = window > 0 ? problem->state_history : nullptr;
+  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v, sp.gates, window);
   if (p.algorithm == GDN_ALGO_CHUNKED && !can_chunk)
     return fail(GDN_ERR_UNSUPPORTED,
-                "%s: the chunked algorithm needs bfloat16 I/O, d_k 64 or 128 and d_v a multiple of 8 "
-                "(got %s, d_k=%d, d_v=%d)", fn, io_bf16 ? "bf16" : "f32", p.d_k, p.d_v);
+                "%s: the chunked algorithm needs bfloat16 I/O, d_k 64 or 128, d_v a multiple of 8, the "
+                "gated-delta or delta rule with a per-head decay and no state history (got %s, d_k=%d, "
+                "d_v=%d, rule=%d, decay_per_key=%d, state_window=%d)",
+                fn, io_bf16 ? "bf16" : "f32", p.d_k, p.d_v, p.rule, p.decay_per_key, window);
   const bool chunked = p.algorithm == GDN_ALGO_CHUNKED ||
                        (p.algorithm == GDN_ALGO_AUTO && can_chunk &&
                         static_cast<int64_t>(total_tokens) >= 64 * static_cast<int64_t>(num_seqs));

@@ -10,6 +10,10 @@ namespace gdn {
 // Gate inputs as the kernels see them (one of the two pairs is used).
 struct GateArgs {
   int32_t raw;          // 0: g / beta given; 1: a / b / A_log / dt_bias given
+  int32_t decays;       // the rule decays the state (g / a read)
+  int32_t deltas;       // the rule applies the delta correction (beta / b read)
+  int32_t per_key;      // g / a are [tokens, h_v, d_k]; A_log / dt_bias [h_v, d_k]
+  int32_t beta_shared;  // beta / b are [tokens]
   const void* g;        // [tokens, h_v] io dtype
   const void* beta;     // [tokens, h_v] io dtype
   const void* a;        // [tokens, h_v] io dtype
@@ -38,6 +42,8 @@ struct ScanParams {
   int32_t ratio;          // h_v / h_qk
   int32_t col_blocks;     // column blocks per (sequence, head)
   float scale;
+  int32_t window;         // > 0: history of the last `window` states per sequence
+  float* history;         // [N, window, h_v, d_k, d_v]
 };
 
 // One decode token per sequence, state updated in place.
@@ -51,6 +57,7 @@ struct DecodeParams {
   const int32_t* slots;   // [B] or null; see ScanParams
   int32_t num_slots;
   int32_t batch;
+  int32_t b_offset;       // first sequence of this launch (set by the launcher)
   int32_t h_qk, h_v, d_k, d_v;
   int32_t ratio;
   int32_t col_blocks;
@@ -76,7 +83,7 @@ hipError_t launch_gate_prologue(GatePrologueParams p, int io_bf16, hipStream_t s
 
 // Chunked (matrix-core) prefill: whether a geometry is built, the state
 // columns one workgroup owns, and the launcher.
-bool chunked_supported(int io_bf16, int d_k, int d_v);
+bool chunked_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window);
 int chunked_columns_per_block(int d_k, int d_v);
 hipError_t launch_prefill_chunked(ScanParams p, int io_bf16, hipStream_t stream);
 

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
   const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
   float A_log = 0.0f, dt_bias = 0.0f;
   if constexpr (RAW) {
-    if (t_begin < t_end) {
+    if (t_begin < t_end && p.gates.decays) {
       A_log = p.gates.A_log[h];
       dt_bias = p.gates.dt_bias[h];
     }
@@ -265,12 +265,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       rb_ = 0.0f;
       if (lane < Ln) {
         const size_t gi = static_cast<size_t>(c0 + lane) * p.h_v + h;
+        const size_t bi = p.gates.beta_shared ? static_cast<size_t>(c0 + lane) : gi;
         if constexpr (RAW) {
-          rg = widen(static_cast<const IO*>(p.gates.a)[gi]);
-          rb_ = widen(static_cast<const IO*>(p.gates.b)[gi]);
+          if (p.gates.decays) rg = widen(static_cast<const IO*>(p.gates.a)[gi]);
+          rb_ = widen(static_cast<const IO*>(p.gates.b)[bi]);
         } else {
-          rg = widen(static_cast<const IO*>(p.gates.g)[gi]);
-          rb_ = widen(static_cast<const IO*>(p.gates.beta)[gi]);
+          if (p.gates.decays) rg = widen(static_cast<const IO*>(p.gates.g)[gi]);
+          rb_ = widen(static_cast<const IO*>(p.gates.beta)[bi]);
         }
       }
     }
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       float g = 0.0f, b = 0.0f;
       if (lane < L) {
         if constexpr (RAW) {
-          g = gate_log_decay(rg, A_log, dt_bias);
+          g = p.gates.decays ? gate_log_decay(rg, A_log, dt_bias) : 0.0f;
           b = gate_sigmoid(rb_);
         } else {
           g = rg;
@@ -532,8 +533,8 @@ hipError_t launch_nc(const ScanParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool chunked_supported(int io_bf16, int d_k, int d_v) {
-  return io_bf16 && (d_k == 64 || d_k == 128) && d_v % 8 == 0;
+bool chunked_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window) {
+  return io_bf16 && (d_k == 64 || d_k == 128) && d_v % 8 == 0 && gates.deltas && !gates.per_key && window == 0;
 }
 
 int chunked_columns_per_block(int d_k, int d_v) {
@@ -542,7 +543,7 @@ int chunked_columns_per_block(int d_k, int d_v) {
 }
 
 hipError_t launch_prefill_chunked(ScanParams p, int io_bf16, hipStream_t stream) {
-  if (!chunked_supported(io_bf16, p.d_k, p.d_v)) return hipErrorInvalidValue;
+  if (!chunked_supported(io_bf16, p.d_k, p.d_v, p.gates, p.window)) return hipErrorInvalidValue;
   const int nc = chunked_columns_per_block(p.d_k, p.d_v);
   if (p.d_k == 128) return nc == 64 ? launch_nc<bf16_t, 128, 64>(p, stream) : launch_nc<bf16_t, 128, 32>(p, stream);
   return nc == 64 ? launch_nc<bf16_t, 64, 64>(p, stream) : launch_nc<bf16_t, 64, 32>(p, stream);

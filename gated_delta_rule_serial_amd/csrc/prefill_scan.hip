@@ -18,7 +18,11 @@
 //   * q_t, k_t, v_t are loaded as packed words PF tokens ahead of use
 //     through a register ring, so global latency overlaps the serial chain;
 //   * the gates of 64 tokens are computed once, lane-parallel (lane l takes
-//     token t0 + l), and read per token with v_readlane.
+//     token t0 + l), and read per token with v_readlane; a per-key-dim decay
+//     instead travels with q/k through the ring (the lane's RPL rows);
+//   * the update rule ([P4] `UpdateRule`) switches the decay and the delta
+//     correction off uniformly per launch; the optional state history stores
+//     the lane's rows after each of the last W tokens.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -38,7 +42,7 @@ template <> struct ScanShape<64> { static constexpr int R = 8; };
 template <> struct ScanShape<128> { static constexpr int R = 16; };
 template <> struct ScanShape<256> { static constexpr int R = 32; };
 
-template <typename IO, int DK, bool RAW>
+template <typename IO, int DK, bool RAW, bool PERKEY>
 __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   constexpr int R = ScanShape<DK>::R;
   constexpr int CPW = kWave / R;
@@ -58,6 +62,8 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   const int row0 = r * RPL;
   const bool full_rows = (p.d_k == DK);
   const int row_limit = p.d_k - row0;  // rows of this lane's slice that exist
+  const bool decays = p.gates.decays != 0;
+  const bool deltas = p.gates.deltas != 0;
 
   const int t_begin = p.cu[n];
   const int t_end = p.cu[n + 1];
@@ -66,12 +72,27 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   bool has_state;
   const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
   float S[RPL];
-  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(p.d_k) * p.d_v;
+  const size_t state_elems = static_cast<size_t>(p.d_k) * p.d_v;
+  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * state_elems;
 #pragma unroll
   for (int m = 0; m < RPL; ++m) {
     const int i = row0 + m;
     S[m] = (p.s0 != nullptr && has_state && col_ok && i < p.d_k) ? p.s0[sbase + static_cast<size_t>(i) * p.d_v + j]
                                                                   : 0.0f;
+  }
+
+  // ---- state history: slot w of sequence n holds the state after token
+  //      t_end - W + w; slots before the first token are zero
+  const int W = p.window;
+  auto history_slot = [&](int w) {
+    return p.history + ((static_cast<size_t>(n) * W + w) * p.h_v + h) * state_elems;
+  };
+  if (W > 0 && col_ok) {
+    for (int w = 0; w < W - (t_end - t_begin); ++w) {
+#pragma unroll
+      for (int m = 0; m < RPL; ++m)
+        if (row0 + m < p.d_k) history_slot(w)[static_cast<size_t>(row0 + m) * p.d_v + j] = 0.0f;
+    }
   }
 
   const IO* __restrict__ qg = static_cast<const IO*>(p.q);
@@ -83,32 +104,45 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   const size_t v_stride = static_cast<size_t>(p.h_v) * p.d_v;
   const size_t v_off = static_cast<size_t>(h) * p.d_v + (col_ok ? j : 0);
 
-  // ---- gates: lane l holds (alpha, beta) of token blk + l
+  // ---- gates.  Per-head gates: lane l holds (alpha, beta) of token blk + l.
+  //      Per-key-dim decay: the decay of this lane's rows travels with q/k.
   const IO* __restrict__ ga = static_cast<const IO*>(RAW ? p.gates.a : p.gates.g);
   const IO* __restrict__ gb = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
-  float A_log = 0.0f, dt_bias = 0.0f;
+  float A_log = 0.0f, dt_bias = 0.0f;           // per-head raw decay parameters
+  float A_log_r[RPL], dt_bias_r[RPL];           // per-key-dim raw decay parameters
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) A_log_r[m] = dt_bias_r[m] = 0.0f;
   if constexpr (RAW) {
-    if (t_begin < t_end) {  // the per-head parameters may be absent when no token needs them
-      A_log = p.gates.A_log[h];
-      dt_bias = p.gates.dt_bias[h];
+    if (t_begin < t_end && decays) {  // the parameters may be absent when nothing reads them
+      if constexpr (PERKEY) {
+#pragma unroll
+        for (int m = 0; m < RPL; ++m)
+          if (row0 + m < p.d_k) {
+            A_log_r[m] = p.gates.A_log[static_cast<size_t>(h) * p.d_k + row0 + m];
+            dt_bias_r[m] = p.gates.dt_bias[static_cast<size_t>(h) * p.d_k + row0 + m];
+          }
+      } else {
+        A_log = p.gates.A_log[h];
+        dt_bias = p.gates.dt_bias[h];
+      }
     }
   }
-  RawScalar<IO> next_ga, next_gb;  // raw gate inputs of the next 64-token block
+  RawScalar<IO> next_ga, next_gb;  // raw per-head gate inputs of the next 64-token block
   auto fetch_gate_block = [&](int blk) {
     const int t = blk + lane;
+    next_ga.w = 0u;
+    next_gb.w = 0u;
     if (t < t_end) {
-      next_ga.load(ga + static_cast<size_t>(t) * p.h_v + h);
-      next_gb.load(gb + static_cast<size_t>(t) * p.h_v + h);
-    } else {
-      next_ga.w = 0u;
-      next_gb.w = 0u;
+      if (decays && !PERKEY) next_ga.load(ga + static_cast<size_t>(t) * p.h_v + h);
+      if (deltas) next_gb.load(gb + (p.gates.beta_shared ? static_cast<size_t>(t) : static_cast<size_t>(t) * p.h_v + h));
     }
   };
   float blk_alpha = 1.0f, blk_beta = 0.0f;
   fetch_gate_block(t_begin);
 
-  // ---- q/k/v ring
+  // ---- q/k/v (and per-key-dim decay) ring
   RawSlice<IO, RPL> ring_k[kPrefetch], ring_q[kPrefetch];
+  RawSlice<IO, PERKEY ? RPL : 1> ring_g[kPrefetch];
   RawScalar<IO> ring_v[kPrefetch];
   auto fetch_token = [&](int slot, int t) {
     const size_t qk = static_cast<size_t>(t) * qk_stride + qk_off;
@@ -119,6 +153,13 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
       ring_k[slot].load_masked(kg + qk, row_limit);
       ring_q[slot].load_masked(qg + qk, row_limit);
     }
+    if constexpr (PERKEY) {
+      if (decays) {
+        const IO* gp = ga + (static_cast<size_t>(t) * p.h_v + h) * p.d_k + row0;
+        if (full_rows) ring_g[slot].load(gp);
+        else ring_g[slot].load_masked(gp, row_limit);
+      }
+    }
     ring_v[slot].load(vg + static_cast<size_t>(t) * v_stride + v_off);
   };
 #pragma unroll
@@ -126,6 +167,7 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
     if (t_begin + s < t_end) fetch_token(s, t_begin + s);
 
   const float scale = p.scale;
+  const int hist_from = (t_end - t_begin) - W;  // first token (relative) whose state is kept
   for (int tb = t_begin; tb < t_end; tb += kPrefetch) {
 #pragma unroll
     for (int s = 0; s < kPrefetch; ++s) {
@@ -134,49 +176,89 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
       const int rel = (t - t_begin) & (kWave - 1);
       if (rel == 0) {
         // gates of tokens t .. t + 63, one per lane, then prefetch the next block
-        if constexpr (RAW) {
-          const float gl = gate_log_decay(next_ga.value(), A_log, dt_bias);
-          blk_alpha = expf(gl);
-          blk_beta = gate_sigmoid(next_gb.value());
-        } else {
-          blk_alpha = expf(next_ga.value());
-          blk_beta = next_gb.value();
+        if (decays && !PERKEY) {
+          if constexpr (RAW) blk_alpha = expf(gate_log_decay(next_ga.value(), A_log, dt_bias));
+          else blk_alpha = expf(next_ga.value());
+        }
+        if (deltas) {
+          if constexpr (RAW) blk_beta = gate_sigmoid(next_gb.value());
+          else blk_beta = next_gb.value();
         }
         fetch_gate_block(t + kWave);
       }
-      const float alpha = readlane(blk_alpha, rel);
       const float beta = readlane(blk_beta, rel);
 
       float kf[RPL], qf[RPL];
       ring_k[s].widen_to(kf);
       ring_q[s].widen_to(qf);
       const float vv = ring_v[s].value();
+      float gr[PERKEY ? RPL : 1];
+      if constexpr (PERKEY) ring_g[s].widen_to(gr);
       if (t + kPrefetch < t_end) fetch_token(s, t + kPrefetch);
 
-      // retrieval against the decayed state: r = alpha * (S^T k)
-      float pr0 = 0.0f, pr1 = 0.0f;
-#pragma unroll
-      for (int m = 0; m < RPL; m += 2) {
-        pr0 = fmaf(S[m], kf[m], pr0);
-        if (m + 1 < RPL) pr1 = fmaf(S[m + 1], kf[m + 1], pr1);
-      }
-      const float rsum = group_sum<R>(pr0 + pr1);
-      const float delta = beta * (vv - alpha * rsum);
-
-      // decay + rank-1 update, and the readout partial of the updated state
       float po0 = 0.0f, po1 = 0.0f;
+      if constexpr (PERKEY) {
+        // decay row by row, then retrieval, delta update and readout
+        if (decays) {
 #pragma unroll
-      for (int m = 0; m < RPL; m += 2) {
-        S[m] = fmaf(S[m], alpha, kf[m] * delta);
-        po0 = fmaf(S[m], qf[m], po0);
-        if (m + 1 < RPL) {
-          S[m + 1] = fmaf(S[m + 1], alpha, kf[m + 1] * delta);
-          po1 = fmaf(S[m + 1], qf[m + 1], po1);
+          for (int m = 0; m < RPL; ++m) {
+            const float lg = RAW ? gate_log_decay(gr[m], A_log_r[m], dt_bias_r[m]) : gr[m];
+            S[m] *= expf(lg);
+          }
+        }
+        float delta = vv;
+        if (deltas) {
+          float pr0 = 0.0f, pr1 = 0.0f;
+#pragma unroll
+          for (int m = 0; m < RPL; m += 2) {
+            pr0 = fmaf(S[m], kf[m], pr0);
+            if (m + 1 < RPL) pr1 = fmaf(S[m + 1], kf[m + 1], pr1);
+          }
+          delta = beta * (vv - group_sum<R>(pr0 + pr1));
+        }
+#pragma unroll
+        for (int m = 0; m < RPL; m += 2) {
+          S[m] = fmaf(kf[m], delta, S[m]);
+          po0 = fmaf(S[m], qf[m], po0);
+          if (m + 1 < RPL) {
+            S[m + 1] = fmaf(kf[m + 1], delta, S[m + 1]);
+            po1 = fmaf(S[m + 1], qf[m + 1], po1);
+          }
+        }
+      } else {
+        const float alpha = decays ? readlane(blk_alpha, rel) : 1.0f;
+        // retrieval against the decayed state: r = alpha * (S^T k)
+        float delta = vv;
+        if (deltas) {
+          float pr0 = 0.0f, pr1 = 0.0f;
+#pragma unroll
+          for (int m = 0; m < RPL; m += 2) {
+            pr0 = fmaf(S[m], kf[m], pr0);
+            if (m + 1 < RPL) pr1 = fmaf(S[m + 1], kf[m + 1], pr1);
+          }
+          const float rsum = group_sum<R>(pr0 + pr1);
+          delta = beta * (vv - alpha * rsum);
+        }
+        // decay + rank-1 update, and the readout partial of the updated state
+#pragma unroll
+        for (int m = 0; m < RPL; m += 2) {
+          S[m] = fmaf(S[m], alpha, kf[m] * delta);
+          po0 = fmaf(S[m], qf[m], po0);
+          if (m + 1 < RPL) {
+            S[m + 1] = fmaf(S[m + 1], alpha, kf[m + 1] * delta);
+            po1 = fmaf(S[m + 1], qf[m + 1], po1);
+          }
         }
       }
       const float o = group_sum<R>(po0 + po1) * scale;
       if (og != nullptr && r == 0 && col_ok)
         narrow_store(og + static_cast<size_t>(t) * v_stride + v_off, o);
+      const int w = (t - t_begin) - hist_from;
+      if (W > 0 && w >= 0 && col_ok) {
+#pragma unroll
+        for (int m = 0; m < RPL; ++m)
+          if (row0 + m < p.d_k) history_slot(w)[static_cast<size_t>(row0 + m) * p.d_v + j] = S[m];
+      }
     }
   }
 
@@ -194,10 +276,14 @@ template <typename IO, int DK>
 hipError_t launch_dk(const ScanParams& p, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>(p.num_seqs) * p.h_v * p.col_blocks;
   if (blocks == 0) return hipSuccess;
-  if (p.gates.raw)
-    hipLaunchKernelGGL((scan_kernel<IO, DK, true>), dim3(blocks), dim3(kWave), 0, stream, p);
-  else
-    hipLaunchKernelGGL((scan_kernel<IO, DK, false>), dim3(blocks), dim3(kWave), 0, stream, p);
+  const bool per_key = p.gates.per_key && p.gates.decays;
+  if (p.gates.raw) {
+    if (per_key) hipLaunchKernelGGL((scan_kernel<IO, DK, true, true>), dim3(blocks), dim3(kWave), 0, stream, p);
+    else hipLaunchKernelGGL((scan_kernel<IO, DK, true, false>), dim3(blocks), dim3(kWave), 0, stream, p);
+  } else {
+    if (per_key) hipLaunchKernelGGL((scan_kernel<IO, DK, false, true>), dim3(blocks), dim3(kWave), 0, stream, p);
+    else hipLaunchKernelGGL((scan_kernel<IO, DK, false, false>), dim3(blocks), dim3(kWave), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_PRECOMPUTED, GDN_GATES_RAW = 0, 1
 GDN_ALGO_AUTO, GDN_ALGO_SERIAL, GDN_ALGO_CHUNKED = 0, 1, 2
 ALGORITHMS = {"auto": GDN_ALGO_AUTO, "serial": GDN_ALGO_SERIAL, "chunked": GDN_ALGO_CHUNKED}
+RULES = {"gated_delta": 0, "delta": 1, "gated": 2, "linear": 3}
 
 _DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
 
@@ -38,6 +39,11 @@ class gdn_problem(ctypes.Structure):
         ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
         ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
         ("algorithm", ctypes.c_int32),
+        ("rule", ctypes.c_int32),
+        ("decay_per_key", ctypes.c_int32),
+        ("beta_shared", ctypes.c_int32),
+        ("state_window", ctypes.c_int32),
+        ("state_history", ctypes.c_void_p),
     ]
 
 
@@ -123,15 +129,20 @@ def _stream(stream, device) -> ctypes.c_void_p:
 
 def make_problem(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype, *, scale: float = 0.0,
                  g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None,
-                 algorithm: str = "auto") -> gdn_problem:
-    """Fill the ``gdn_problem`` struct.  Raw gates are used when ``a`` is given."""
+                 algorithm: str = "auto", rule: str = "gated_delta", decay_per_key: bool = False,
+                 beta_shared: bool = False, state_history: Optional[torch.Tensor] = None) -> gdn_problem:
+    """Fill the ``gdn_problem`` struct.  Raw gates are used when ``a`` (or, for
+    rules without decay, ``b``) is given.  ``state_history`` [N, W, h_v, d_k, d_v]
+    sets the state window W."""
     if io_dtype not in _DTYPES:
         raise ValueError(f"io dtype {io_dtype} is not supported")
-    raw = a is not None
+    raw = a is not None or (g is None and b is not None)
+    window = 0 if state_history is None else int(state_history.shape[1])
     return gdn_problem(h_qk, h_v, d_k, d_v, _DTYPES[io_dtype], float(scale),
                        GDN_GATES_RAW if raw else GDN_GATES_PRECOMPUTED,
                        _ptr(g), _ptr(beta), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
-                       ALGORITHMS[algorithm])
+                       ALGORITHMS[algorithm], RULES[rule], int(decay_per_key), int(beta_shared),
+                       window, _ptr(state_history))
 
 
 def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
@@ -139,14 +150,15 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
                 initial_state: Optional[torch.Tensor] = None, g=None, beta=None, a=None, b=None,
                 A_log=None, dt_bias=None, scale: float = 0.0,
                 cu_seqlens_host: Optional[Sequence[int]] = None, algorithm: str = "auto",
-                stream=None) -> None:
+                stream=None, **variant) -> None:
     """gdn_prefill of include/gdn.h: q, k [T, h_qk, d_k]; v, out [T, h_v, d_v];
     cu_seqlens int32 [N+1] on the device; states float32 [N, h_v, d_k, d_v];
-    algorithm "auto", "serial" or "chunked"."""
+    algorithm "auto", "serial" or "chunked"; ``variant``: rule, decay_per_key,
+    beta_shared, state_history (see make_problem)."""
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
-                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm)
+                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm, **variant)
     n = cu_seqlens.numel() - 1
     host = None
     if cu_seqlens_host is not None:
@@ -158,13 +170,14 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
 
 def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor,
                     out: torch.Tensor, *, g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None,
-                    scale: float = 0.0, stream=None) -> None:
+                    scale: float = 0.0, stream=None, **variant) -> None:
     """gdn_decode_step of include/gdn.h: q, k [B, h_qk, d_k]; v, out [B, h_v, d_v];
-    state float32 [B, h_v, d_k, d_v], updated in place."""
+    state float32 [B, h_v, d_k, d_v], updated in place; ``variant``: rule,
+    decay_per_key, beta_shared."""
     B, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
-                        A_log=A_log, dt_bias=dt_bias)
+                        A_log=A_log, dt_bias=dt_bias, **variant)
     _check(load().gdn_decode_step(ctypes.byref(prob), B, _ptr(q), _ptr(k), _ptr(v), _ptr(state), _ptr(out),
                                   _stream(stream, q.device)))
 
@@ -217,7 +230,7 @@ def gdn_gate_prologue(a: torch.Tensor, b: Optional[torch.Tensor], A_log: torch.T
 
 # ----------------------------------------------------------------- helpers
 def prefill(q, k, v, cu_seqlens, *, initial_state=None, want_state=True, scale=0.0,
-            cu_seqlens_host=None, algorithm="auto", stream=None, **gates):
+            cu_seqlens_host=None, algorithm="auto", stream=None, **kw):
     """Allocate ``out`` (and the final state) with torch and call gdn_prefill."""
     T, _, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
@@ -225,14 +238,14 @@ def prefill(q, k, v, cu_seqlens, *, initial_state=None, want_state=True, scale=0
     out = torch.empty(T, h_v, d_v, dtype=q.dtype, device=q.device)
     fin = torch.empty(n, h_v, d_k, d_v, dtype=torch.float32, device=q.device) if want_state else None
     gdn_prefill(q, k, v, cu_seqlens, out=out, final_state=fin, initial_state=initial_state, scale=scale,
-                cu_seqlens_host=cu_seqlens_host, algorithm=algorithm, stream=stream, **gates)
+                cu_seqlens_host=cu_seqlens_host, algorithm=algorithm, stream=stream, **kw)
     return out, fin
 
 
-def decode_step(q, k, v, state, *, scale=0.0, stream=None, **gates):
+def decode_step(q, k, v, state, *, scale=0.0, stream=None, **kw):
     """Allocate ``out`` with torch and call gdn_decode_step (state updated in place)."""
     out = torch.empty(q.shape[0], v.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
-    gdn_decode_step(q, k, v, state, out, scale=scale, stream=stream, **gates)
+    gdn_decode_step(q, k, v, state, out, scale=scale, stream=stream, **kw)
     return out
 
 

@@ -123,3 +123,24 @@ def generate(shape: Shape, *, seqlen: Optional[int] = None, num_seqs: Optional[i
     dt = shape.io_dtype
     return Inputs(shape, lens, cu, q.to(dt), k.to(dt), v.to(dt), a.to(dt), b.to(dt),
                   A_log, dt_bias, s0)
+
+
+@dataclasses.dataclass
+class VariantGates:
+    a_key: torch.Tensor        # [T, h_v, d_k] raw per-key-dim decay input
+    A_log_key: torch.Tensor    # [h_v, d_k] float32
+    dt_bias_key: torch.Tensor  # [h_v, d_k] float32
+    b_shared: torch.Tensor     # [T] raw write-strength input shared by the heads
+
+
+def variant_gates(T: int, h_v: int, d_k: int, *, seed: int, io_dtype: torch.dtype) -> VariantGates:
+    """Raw gate inputs for the per-key-dim decay and shared-beta layouts, drawn
+    like the per-head ones: a, b ~ N(0, 1), A_log ~ U(0, 1), dt_bias ~ U(-1, 1)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    f32 = torch.float32
+    a = torch.randn(T, h_v, d_k, generator=gen, dtype=f32)
+    A_log = torch.rand(h_v, d_k, generator=gen, dtype=f32)
+    dt_bias = torch.rand(h_v, d_k, generator=gen, dtype=f32) * 2.0 - 1.0
+    b = torch.randn(T, generator=gen, dtype=f32)
+    return VariantGates(a.to(io_dtype), A_log, dt_bias, b.to(io_dtype))

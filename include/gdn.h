@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -80,11 +80,26 @@ typedef enum gdn_algorithm {
   GDN_ALGO_SERIAL = 1,
   /* The same recurrence in chunks of 64 tokens on the matrix cores (bf16
    * operands, f32 accumulation, f32 state carried between chunks).  Needs
-   * bfloat16 I/O, d_k of 64 or 128 and d_v a multiple of 8, and a true decay
+   * bfloat16 I/O, d_k of 64 or 128 and d_v a multiple of 8, the gated-delta
+   * or delta rule with a per-head decay, no state history, and a true decay
    * (g <= 0, as the raw-gate prologue always gives); otherwise
    * GDN_ERR_UNSUPPORTED when requested explicitly. */
   GDN_ALGO_CHUNKED = 2
 } gdn_algorithm;
+
+/* Update rule ([P4] `UpdateRule`; [P1] `is_known_rule`).  The default (0) is
+ * the gated delta rule; the others drop the decay, the delta correction, or
+ * both:
+ *   GATED_DELTA  S <- exp(g) S;  S <- S + k (beta (v - S^T k))^T
+ *   DELTA        S <- S + k (beta (v - S^T k))^T          (g not read)
+ *   GATED        S <- exp(g) S + k v^T                     (beta not read)
+ *   LINEAR       S <- S + k v^T                            (neither read)  */
+typedef enum gdn_rule {
+  GDN_RULE_GATED_DELTA = 0,
+  GDN_RULE_DELTA = 1,
+  GDN_RULE_GATED = 2,
+  GDN_RULE_LINEAR = 3
+} gdn_rule;
 
 /* Geometry and gate inputs of one call. */
 typedef struct gdn_problem {
@@ -102,6 +117,21 @@ typedef struct gdn_problem {
   const float* A_log;   /* RAW: [h_v] float32                                */
   const float* dt_bias; /* RAW: [h_v] float32                                */
   int32_t algorithm;    /* gdn_algorithm; gdn_prefill only (decode ignores it) */
+  int32_t rule;         /* gdn_rule                                          */
+  /* 1: the decay is per key dimension ([P4] decay layout [B, T, H_kv d_k]):
+   * g (or a) is [tokens, h_v, d_k] and row i of the state decays by
+   * exp(g[t,h,i]); with raw gates A_log and dt_bias are [h_v, d_k].       */
+  int32_t decay_per_key;
+  /* 1: one beta per token shared by all value heads ([P4] beta layout
+   * [B, T, 1]): beta (or b) is [tokens].                                  */
+  int32_t beta_shared;
+  /* gdn_prefill / gdn_prefill_slots only: W > 0 writes the state after each
+   * of the last W tokens of every sequence, oldest first, to state_history
+   * [num_seqs, W, h_v, d_k, d_v] float32; slots before a sequence's first
+   * token are zero ([P1] `state_window`; W = T gives every step, as [P3]
+   * `gated_delta_steps`).  Decode ignores both fields.                    */
+  int32_t state_window;
+  float* state_history;
 } gdn_problem;
 
 /*

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 3
+    assert gdn.abi_version() == 4
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -44,7 +44,8 @@ def test_version_and_status_strings(lib):
 def _prob(**kw):
     base = dict(h_qk=2, h_v=4, d_k=16, d_v=16, io_dtype=gdn.GDN_F32, scale=0.0,
                 gate_mode=gdn.GDN_GATES_PRECOMPUTED, g=FAKE, beta=FAKE + 0x1000, a=None, b=None,
-                A_log=None, dt_bias=None, algorithm=gdn.GDN_ALGO_AUTO)
+                A_log=None, dt_bias=None, algorithm=gdn.GDN_ALGO_AUTO, rule=0, decay_per_key=0, beta_shared=0,
+                state_window=0, state_history=None)
     base.update(kw)
     return gdn.gdn_problem(**base)
 
@@ -80,6 +81,16 @@ INVALID, UNSUPPORTED = gdn.GDN_ERR_INVALID_ARGUMENT, gdn.GDN_ERR_UNSUPPORTED
     ("chunked on d_k 48", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_BF16, d_k=48), {}, UNSUPPORTED,
      "chunked algorithm needs"),
     ("misaligned g", dict(g=FAKE + 2), {}, INVALID, "aligned"),
+    ("bad rule", dict(rule=4), {}, INVALID, "unknown rule"),
+    ("bad flag", dict(beta_shared=2), {}, INVALID, "must be 0 or 1"),
+    ("per-key g misaligned", dict(decay_per_key=1, g=FAKE + 8), {}, INVALID, "16-byte"),
+    ("delta rule needs beta", dict(rule=1, beta=None), {}, INVALID, "need g and beta"),
+    ("window without history", dict(state_window=3), {}, INVALID, "needs state_history"),
+    ("negative window", dict(state_window=-1), {}, INVALID, "negative"),
+    ("chunked per-key", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_BF16, d_k=64, d_v=64,
+                             decay_per_key=1), {}, UNSUPPORTED, "chunked algorithm needs"),
+    ("chunked gated rule", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_BF16, d_k=64, d_v=64, rule=2),
+     {}, UNSUPPORTED, "chunked algorithm needs"),
     ("negative seqs", {}, dict(n=-1), INVALID, "negative"),
     ("negative tokens", {}, dict(T=-1), INVALID, "negative"),
     ("tokens without seqs", {}, dict(n=0, T=4), INVALID, "no sequences"),

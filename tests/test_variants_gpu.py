@@ -1,0 +1,161 @@
+"""GPU parity of the variants the pages define, against the oracle: the update
+rules (linear / gated / delta / gated delta), per-key-dim decay, one beta per
+token shared by the heads, and the per-step state history -- through the
+serial scan, the decode step and (where it applies) the chunked prefill."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_serial_amd import gdn, synth
+from gpu_harness import TOL, check, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RULES = ["gated_delta", "delta", "gated", "linear"]
+
+
+def _setup(h_qk, h_v, d_k, d_v, dt, lens, *, seed, per_key=False, shared=False, init=True):
+    shape = dataclasses.replace(synth.BY_NAME["tiny_prefill"], h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v,
+                                io_dtype=dt, init_state=init)
+    inp = synth.generate(shape, seqlens=lens, seed=seed)
+    vg = synth.variant_gates(inp.total_tokens, h_v, d_k, seed=seed + 1, io_dtype=dt)
+    orc = oracle.default()
+    T = inp.total_tokens
+    # raw inputs of each layout, and the oracle's gates from exactly those values
+    a = vg.a_key if per_key else inp.a
+    A_log = vg.A_log_key if per_key else inp.A_log
+    dt_bias = vg.dt_bias_key if per_key else inp.dt_bias
+    b = vg.b_shared if shared else inp.b
+    if per_key:
+        g64, _ = orc.gates(a.reshape(T, h_v * d_k), a.reshape(T, h_v * d_k), A_log.reshape(-1),
+                           dt_bias.reshape(-1))
+        g64 = g64.reshape(T, h_v, d_k)
+    else:
+        g64, _ = orc.gates(a, a, A_log, dt_bias)
+    _, b64 = orc.gates(b.reshape(-1, 1), b.reshape(-1, 1), torch.zeros(1), torch.zeros(1))
+    b64 = b64.reshape(b.shape)
+    return inp, dict(a=a, b=b, A_log=A_log, dt_bias=dt_bias), g64, b64
+
+
+def _oracle(inp, g, beta, *, rule, per_key, shared, window=0):
+    orc = oracle.default()
+    uses_g = rule in ("gated", "gated_delta")
+    uses_b = rule in ("delta", "gated_delta")
+    return orc.prefill(inp.q, inp.k, inp.v, g if uses_g else None, beta if uses_b else None,
+                       inp.cu_seqlens.numpy(), inp.initial_state, rule=rule, decay_per_key=per_key,
+                       beta_shared=shared, window=window)
+
+
+def _gpu_prefill(inp, gates, *, raw, rule, per_key, shared, window=0, algorithm="serial"):
+    dev = "cuda"
+    T, n = inp.total_tokens, len(inp.seqlens)
+    h_v, d_k, d_v = inp.shape.h_v, inp.shape.d_k, inp.shape.d_v
+    out = torch.full((T, h_v, d_v), float("nan"), dtype=inp.shape.io_dtype, device=dev)
+    fin = torch.full((n, h_v, d_k, d_v), float("nan"), device=dev)
+    hist = torch.full((n, window, h_v, d_k, d_v), float("nan"), device=dev) if window else None
+    kw = {k: to_dev(v) for k, v in gates.items()}
+    gdn.gdn_prefill(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.cu_seqlens), out=out, final_state=fin,
+                    initial_state=to_dev(inp.initial_state), cu_seqlens_host=inp.cu_seqlens.tolist(),
+                    algorithm=algorithm, rule=rule, decay_per_key=per_key, beta_shared=shared,
+                    state_history=hist, **kw)
+    torch.cuda.synchronize()
+    return out.double().cpu(), fin.double().cpu(), (None if hist is None else hist.double().cpu())
+
+
+def _gate_kwargs(raw, raw_in, g64, b64, dt):
+    if raw:
+        return dict(raw_in)
+    return dict(g=torch.from_numpy(g64).to(dt), beta=torch.from_numpy(b64).to(dt))
+
+
+CASES = [
+    # (h_qk, h_v, d_k, d_v, dtype, seqlens)
+    (2, 4, 48, 40, torch.float32, [70, 0, 13]),
+    (16, 32, 128, 128, torch.bfloat16, [150, 66]),
+    (1, 2, 256, 64, torch.float32, [33]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"dk{c[2]}_dv{c[3]}_{str(c[4])[6:]}")
+@pytest.mark.parametrize("rule", RULES)
+@pytest.mark.parametrize("raw", [False, True], ids=["gates", "rawgates"])
+def test_rules_serial(case, rule, raw):
+    h_qk, h_v, d_k, d_v, dt, lens = case
+    say(f"[rule] {rule} raw={raw} {case}")
+    inp, raw_in, g64, b64 = _setup(h_qk, h_v, d_k, d_v, dt, lens, seed=200)
+    gates = _gate_kwargs(raw, raw_in, g64, b64, dt)
+    # the oracle sees the gates the kernel reads: rounded to the I/O dtype when precomputed
+    if not raw:
+        g64, b64 = gates["g"].double().numpy(), gates["beta"].double().numpy()
+    out, fin, _ = _gpu_prefill(inp, gates, raw=raw, rule=rule, per_key=False, shared=False)
+    ro, rf = _oracle(inp, g64, b64, rule=rule, per_key=False, shared=False)
+    check(out, torch.from_numpy(ro), TOL[dt], "out")
+    check(fin, torch.from_numpy(rf), TOL[dt], "final state")
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"dk{c[2]}_dv{c[3]}_{str(c[4])[6:]}")
+@pytest.mark.parametrize("per_key,shared", [(True, False), (False, True), (True, True)],
+                         ids=["perkey", "sharedbeta", "both"])
+@pytest.mark.parametrize("raw", [False, True], ids=["gates", "rawgates"])
+def test_layouts_serial(case, per_key, shared, raw):
+    h_qk, h_v, d_k, d_v, dt, lens = case
+    say(f"[layout] per_key={per_key} shared={shared} raw={raw} {case}")
+    inp, raw_in, g64, b64 = _setup(h_qk, h_v, d_k, d_v, dt, lens, seed=300, per_key=per_key, shared=shared)
+    gates = _gate_kwargs(raw, raw_in, g64, b64, dt)
+    if not raw:
+        g64, b64 = gates["g"].double().numpy(), gates["beta"].double().numpy()
+    out, fin, _ = _gpu_prefill(inp, gates, raw=raw, rule="gated_delta", per_key=per_key, shared=shared)
+    ro, rf = _oracle(inp, g64, b64, rule="gated_delta", per_key=per_key, shared=shared)
+    check(out, torch.from_numpy(ro), TOL[dt], "out")
+    check(fin, torch.from_numpy(rf), TOL[dt], "final state")
+
+
+@pytest.mark.parametrize("window", [1, 4, 80])
+def test_state_history(window):
+    dt = torch.float32
+    say(f"[history] W={window}")
+    inp, raw_in, g64, b64 = _setup(2, 4, 32, 24, dt, [70, 0, 3, 9], seed=400)
+    gates = _gate_kwargs(False, raw_in, g64, b64, dt)
+    g64, b64 = gates["g"].double().numpy(), gates["beta"].double().numpy()
+    out, fin, hist = _gpu_prefill(inp, gates, raw=False, rule="gated_delta", per_key=False, shared=False,
+                                  window=window)
+    ro, rf, rh = _oracle(inp, g64, b64, rule="gated_delta", per_key=False, shared=False, window=window)
+    check(out, torch.from_numpy(ro), TOL[dt], "out")
+    check(fin, torch.from_numpy(rf), TOL[dt], "final state")
+    check(hist, torch.from_numpy(rh), TOL[dt], "history")
+
+
+@pytest.mark.parametrize("shared", [False, True], ids=["perhead", "sharedbeta"])
+@pytest.mark.parametrize("rule", ["gated_delta", "delta"])
+def test_chunked_rules_and_shared_beta(rule, shared):
+    dt = torch.bfloat16
+    say(f"[chunked-variant] {rule} shared={shared}")
+    inp, raw_in, g64, b64 = _setup(16, 32, 128, 128, dt, [150, 70, 1], seed=500, shared=shared)
+    gates = _gate_kwargs(True, raw_in, g64, b64, dt)
+    out, fin, _ = _gpu_prefill(inp, gates, raw=True, rule=rule, per_key=False, shared=shared, algorithm="chunked")
+    ro, rf = _oracle(inp, g64, b64, rule=rule, per_key=False, shared=shared)
+    check(out, torch.from_numpy(ro), TOL[dt], "out")
+    check(fin, torch.from_numpy(rf), TOL[dt], "final state")
+
+
+@pytest.mark.parametrize("rule", RULES)
+@pytest.mark.parametrize("per_key,shared", [(False, False), (True, False), (False, True), (True, True)],
+                         ids=["plain", "perkey", "sharedbeta", "both"])
+@pytest.mark.parametrize("raw", [False, True], ids=["gates", "rawgates"])
+def test_decode_variants(rule, per_key, shared, raw):
+    dt = torch.bfloat16
+    say(f"[decode-variant] {rule} per_key={per_key} shared={shared} raw={raw}")
+    inp, raw_in, g64, b64 = _setup(2, 4, 64, 80, dt, [1] * 5, seed=600, per_key=per_key, shared=shared)
+    gates = _gate_kwargs(raw, raw_in, g64, b64, dt)
+    if not raw:
+        g64, b64 = gates["g"].double().numpy(), gates["beta"].double().numpy()
+    st = to_dev(inp.initial_state).clone()
+    out = gdn.decode_step(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), st, rule=rule, decay_per_key=per_key,
+                          beta_shared=shared, **{k: to_dev(v) for k, v in gates.items()})
+    torch.cuda.synchronize()
+    ro, rf = _oracle(inp, g64, b64, rule=rule, per_key=per_key, shared=shared)
+    check(out.double().cpu(), torch.from_numpy(ro), TOL[dt], "out")
+    check(st.double().cpu(), torch.from_numpy(rf), TOL[dt], "state")
