@@ -181,7 +181,7 @@ def bench_decode(shape, steps, warmup, want_cpu):
         "wall_s": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_kernel<bf16, 128, precomputed gates>",
+                     "kernel": "decode_kernel<bf16, d_k 128, 128 columns per workgroup, precomputed gates>",
                      "algorithmic_bytes_per_launch": nbytes},
         "config": {"workload": shape.name, "batch": shape.num_seqs, "h_qk": shape.h_qk, "h_v": shape.h_v,
                    "d_k": shape.d_k, "d_v": shape.d_v, "io_dtype": "bf16", "state_dtype": "f32",

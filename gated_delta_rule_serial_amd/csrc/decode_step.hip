@@ -14,15 +14,17 @@
 // updated state) with the readout expanded algebraically so that it needs no
 // second pass over S: S'^T q = alpha S^T q + delta (k . q).
 //
-// Mapping: a 256-thread workgroup owns 64 state columns of one (b, h); the
-// grid is (column block, h, b), so no index needs an integer division.
-// Thread (rg, tc), rg in [0, 16), tc in [0, 16), holds rows
+// Mapping: a 256-thread workgroup owns BC state columns of one (b, h), BC =
+// 128 (d_k <= 128) or 64; the grid is (column block, h, b), so no index needs
+// an integer division.  Thread (rg, tc), tc in [0, BC/4), holds rows
 // rg*RPT .. rg*RPT + RPT - 1 of columns 4 tc .. 4 tc + 3 in VGPRs, RPT =
-// DK / 16.  A wave's load instruction covers 4 rows x 256 contiguous bytes.
-// The column sums over the 16 row groups go through LDS; one wave finishes
-// them, writes o and broadcasts delta through LDS; every thread then writes
-// its tile.  The state traffic (read + write once) is the kernel's HBM cost;
-// it uses non-temporal 16-byte accesses, since no state byte is reused.
+// d_k BC / 1024; a wave's load instruction covers 256 / BC rows of BC
+// contiguous floats.  The column sums are first reduced across the row groups
+// of each wave with lane exchanges, then across the four waves through LDS;
+// the first BC threads write o and broadcast delta through LDS; every thread
+// then writes its tile.  The state traffic (read + write once) is the
+// kernel's HBM cost; it uses non-temporal 16-byte accesses, since no state
+// byte is reused.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -31,19 +33,22 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowGroups = 16;
-constexpr int kColThreads = 16;
+constexpr int kWaves = kThreads / 64;
 constexpr int kColsPerThread = 4;
-constexpr int kBlockCols = kColThreads * kColsPerThread;  // 64
 
-// FULL: d_k == DK and d_v a multiple of the block's 64 columns, so every
-// thread's tile lies inside the state and the accesses need no masks.
-template <typename IO, int DK, bool PERKEY, bool FULL>
+// BC: state columns per workgroup (64 or 128).  FULL: d_k == DK and d_v a
+// multiple of BC, so every thread's tile lies inside the state and the
+// accesses need no masks.
+template <typename IO, int DK, int BC, bool PERKEY, bool FULL>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+  constexpr int kColThreads = BC / kColsPerThread;
+  constexpr int kRowGroups = kThreads / kColThreads;
+  constexpr int kBlockCols = BC;
   constexpr int RPT = DK / kRowGroups;
-  __shared__ float red_a[kRowGroups][kBlockCols];
-  __shared__ float red_c[kRowGroups][kBlockCols];
-  __shared__ float red_kq[kRowGroups];
+  static_assert(RPT >= 1 && RPT * kRowGroups == DK, "row groups must tile d_k");
+  __shared__ float red_a[kWaves][kBlockCols];
+  __shared__ float red_c[kWaves][kBlockCols];
+  __shared__ float red_kq[kWaves];
   __shared__ float sh_delta[kBlockCols];
 
   const int tid = static_cast<int>(threadIdx.x);
@@ -168,22 +173,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     pkq = fmaf(kf[m], qf[m], pkq);
   }
+  // the row groups inside one wave (lanes tc, tc + kColThreads, ...) are
+  // summed with lane exchanges; LDS then holds one partial per wave
 #pragma unroll
-  for (int cc = 0; cc < kColsPerThread; ++cc) {
-    red_a[rg][tc * kColsPerThread + cc] = PERKEY ? pa[cc] : alpha * pa[cc];
-    red_c[rg][tc * kColsPerThread + cc] = PERKEY ? pc[cc] : alpha * pc[cc];
+  for (int off = kColThreads; off < 64; off *= 2) {
+#pragma unroll
+    for (int cc = 0; cc < kColsPerThread; ++cc) {
+      pa[cc] += __shfl_xor(pa[cc], off);
+      pc[cc] += __shfl_xor(pc[cc], off);
+    }
+    pkq += __shfl_xor(pkq, off);
   }
-  if (tc == 0) red_kq[rg] = pkq;
+  const int wave = tid / 64;
+  if (tid % 64 < kColThreads) {
+#pragma unroll
+    for (int cc = 0; cc < kColsPerThread; ++cc) {
+      red_a[wave][tc * kColsPerThread + cc] = PERKEY ? pa[cc] : alpha * pa[cc];
+      red_c[wave][tc * kColsPerThread + cc] = PERKEY ? pc[cc] : alpha * pc[cc];
+    }
+    if (tc == 0) red_kq[wave] = pkq;
+  }
   __syncthreads();
 
-  // ---- one wave finishes the column sums, writes o, publishes delta
+  // ---- the first BC threads finish the column sums, write o, publish delta
   if (tid < kBlockCols) {
     float a = 0.0f, cs = 0.0f, kq = 0.0f;
 #pragma unroll
-    for (int g = 0; g < kRowGroups; ++g) {
-      a += red_a[g][tid];
-      cs += red_c[g][tid];
-      kq += red_kq[g];
+    for (int w = 0; w < kWaves; ++w) {
+      a += red_a[w][tid];
+      cs += red_c[w][tid];
+      kq += red_kq[w];
     }
     const int j = cb * kBlockCols + tid;
     float vv = 0.0f;
@@ -220,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <typename IO, int DK, bool PERKEY, bool FULL>
+template <typename IO, int DK, int BC, bool PERKEY, bool FULL>
 hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
   // grid: (column block, value head, sequence); the sequence axis is split
   // into launches of at most 65535
@@ -228,7 +247,7 @@ hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
   for (int off = 0; off < p.batch; off += kMaxZ) {
     p.b_offset = off;
     const unsigned nz = static_cast<unsigned>(p.batch - off < kMaxZ ? p.batch - off : kMaxZ);
-    hipLaunchKernelGGL((decode_kernel<IO, DK, PERKEY, FULL>),
+    hipLaunchKernelGGL((decode_kernel<IO, DK, BC, PERKEY, FULL>),
                        dim3(static_cast<unsigned>(p.col_blocks), static_cast<unsigned>(p.h_v), nz),
                        dim3(kThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
@@ -237,13 +256,24 @@ hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
   return hipSuccess;
 }
 
+template <typename IO, int DK, int BC>
+hipError_t launch_bc(const DecodeParams& p, hipStream_t stream) {
+  const bool full = p.d_k == DK && p.d_v % BC == 0;
+  if constexpr (BC == 64) {
+    if (p.gates.per_key && p.gates.decays)
+      return full ? launch_grid<IO, DK, BC, true, true>(p, stream) : launch_grid<IO, DK, BC, true, false>(p, stream);
+  }
+  return full ? launch_grid<IO, DK, BC, false, true>(p, stream) : launch_grid<IO, DK, BC, false, false>(p, stream);
+}
+
 template <typename IO, int DK>
 hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
   if (p.batch == 0 || p.h_v == 0 || p.col_blocks == 0) return hipSuccess;
-  const bool per_key = p.gates.per_key && p.gates.decays;
-  const bool full = p.d_k == DK && p.d_v % kBlockCols == 0;
-  if (per_key) return full ? launch_grid<IO, DK, true, true>(p, stream) : launch_grid<IO, DK, true, false>(p, stream);
-  return full ? launch_grid<IO, DK, false, true>(p, stream) : launch_grid<IO, DK, false, false>(p, stream);
+  if constexpr (DK <= 128) {
+    if (decode_columns_per_block(p.d_k, p.d_v, p.gates.per_key && p.gates.decays) == 128)
+      return launch_bc<IO, DK, 128>(p, stream);
+  }
+  return launch_bc<IO, DK, 64>(p, stream);
 }
 
 template <typename IO>
@@ -257,7 +287,12 @@ hipError_t launch_io(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int decode_columns_per_block() { return kBlockCols; }
+// A workgroup takes a whole 128-column row block when d_k <= 128 (its 16 x 4
+// register tile per thread still fits), d_v is wider than 64 and the decay is
+// per head (a per-key decay keeps a second per-row array live); otherwise 64.
+int decode_columns_per_block(int d_k, int d_v, bool per_key) {
+  return (d_k <= 128 && d_v > 64 && !per_key) ? 128 : 64;
+}
 
 hipError_t launch_decode_step(DecodeParams p, int io_bf16, hipStream_t stream) {
   return io_bf16 ? launch_io<bf16_t>(p, stream) : launch_io<float>(p, stream);

@@ -322,13 +322,11 @@ gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch
   dp.d_k = p.d_k;
   dp.d_v = p.d_v;
   dp.ratio = p.h_v / p.h_qk;
-  const int cpb = gdn::decode_columns_per_block();
+  const int cpb = gdn::decode_columns_per_block(p.d_k, p.d_v, dp.gates.per_key && dp.gates.decays);
   dp.col_blocks = (p.d_v + cpb - 1) / cpb;
   dp.scale = resolved_scale(problem);
-  const uint64_t blocks = static_cast<uint64_t>(batch) * p.h_v * dp.col_blocks;
-  if (blocks > 0x7fffffffull)
-    return fail(GDN_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", fn,
-                static_cast<unsigned long long>(blocks));
+  if (p.h_v > 65535)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: h_v = %d exceeds the grid's head axis (65535)", fn, p.h_v);
   const hipError_t e = gdn::launch_decode_step(dp, p.io_dtype == GDN_BF16, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
