@@ -42,7 +42,10 @@ template <> struct ScanShape<64> { static constexpr int R = 8; };
 template <> struct ScanShape<128> { static constexpr int R = 16; };
 template <> struct ScanShape<256> { static constexpr int R = 32; };
 
-template <typename IO, int DK, bool RAW, bool PERKEY>
+// GENERAL = false compiles the plain gated delta rule with no state history
+// (the rule flags and the window are constants); GENERAL = true reads them
+// at run time and serves every other variant.
+template <typename IO, int DK, bool RAW, bool PERKEY, bool GENERAL>
 __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   constexpr int R = ScanShape<DK>::R;
   constexpr int CPW = kWave / R;
@@ -62,8 +65,8 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   const int row0 = r * RPL;
   const bool full_rows = (p.d_k == DK);
   const int row_limit = p.d_k - row0;  // rows of this lane's slice that exist
-  const bool decays = p.gates.decays != 0;
-  const bool deltas = p.gates.deltas != 0;
+  const bool decays = GENERAL ? p.gates.decays != 0 : true;
+  const bool deltas = GENERAL ? p.gates.deltas != 0 : true;
 
   const int t_begin = p.cu[n];
   const int t_end = p.cu[n + 1];
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
 
   // ---- state history: slot w of sequence n holds the state after token
   //      t_end - W + w; slots before the first token are zero
-  const int W = p.window;
+  const int W = GENERAL ? p.window : 0;
   auto history_slot = [&](int w) {
     return p.history + ((static_cast<size_t>(n) * W + w) * p.h_v + h) * state_elems;
   };
@@ -272,19 +275,24 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   }
 }
 
+template <typename IO, int DK, bool RAW>
+hipError_t launch_gates(const ScanParams& p, unsigned blocks, hipStream_t stream) {
+  const bool per_key = p.gates.per_key && p.gates.decays;
+  const bool plain = p.gates.decays && p.gates.deltas && p.window == 0;
+  if (per_key)
+    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, true, true>), dim3(blocks), dim3(kWave), 0, stream, p);
+  else if (plain)
+    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, false>), dim3(blocks), dim3(kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, true>), dim3(blocks), dim3(kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename IO, int DK>
 hipError_t launch_dk(const ScanParams& p, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>(p.num_seqs) * p.h_v * p.col_blocks;
   if (blocks == 0) return hipSuccess;
-  const bool per_key = p.gates.per_key && p.gates.decays;
-  if (p.gates.raw) {
-    if (per_key) hipLaunchKernelGGL((scan_kernel<IO, DK, true, true>), dim3(blocks), dim3(kWave), 0, stream, p);
-    else hipLaunchKernelGGL((scan_kernel<IO, DK, true, false>), dim3(blocks), dim3(kWave), 0, stream, p);
-  } else {
-    if (per_key) hipLaunchKernelGGL((scan_kernel<IO, DK, false, true>), dim3(blocks), dim3(kWave), 0, stream, p);
-    else hipLaunchKernelGGL((scan_kernel<IO, DK, false, false>), dim3(blocks), dim3(kWave), 0, stream, p);
-  }
-  return hipGetLastError();
+  return p.gates.raw ? launch_gates<IO, DK, true>(p, blocks, stream) : launch_gates<IO, DK, false>(p, blocks, stream);
 }
 
 template <typename IO>
