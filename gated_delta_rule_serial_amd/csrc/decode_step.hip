@@ -294,8 +294,10 @@ int decode_columns_per_block(int d_k, int d_v, bool per_key) {
   return (d_k <= 128 && d_v > 64 && !per_key) ? 128 : 64;
 }
 
-hipError_t launch_decode_step(DecodeParams p, int io_bf16, hipStream_t stream) {
-  return io_bf16 ? launch_io<bf16_t>(p, stream) : launch_io<float>(p, stream);
+hipError_t launch_decode_step(DecodeParams p, int io_dtype, hipStream_t stream) {
+  if (io_dtype == 1) return launch_io<bf16_t>(p, stream);
+  if (io_dtype == 2) return launch_io<f16_t>(p, stream);
+  return launch_io<float>(p, stream);
 }
 
 }  // namespace gdn

@@ -30,13 +30,15 @@ __global__ __launch_bounds__(256) void gate_kernel(GatePrologueParams p) {
 
 }  // namespace
 
-hipError_t launch_gate_prologue(GatePrologueParams p, int io_bf16, hipStream_t stream) {
+hipError_t launch_gate_prologue(GatePrologueParams p, int io_dtype, hipStream_t stream) {
   const int64_t total = p.rows * p.h_v;
   if (total == 0) return hipSuccess;
   const int64_t want = (total + 255) / 256;
   const unsigned blocks = static_cast<unsigned>(want < 4096 ? want : 4096);
-  if (io_bf16)
+  if (io_dtype == 1)
     hipLaunchKernelGGL((gate_kernel<bf16_t>), dim3(blocks), dim3(256), 0, stream, p);
+  else if (io_dtype == 2)
+    hipLaunchKernelGGL((gate_kernel<f16_t>), dim3(blocks), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((gate_kernel<float>), dim3(blocks), dim3(256), 0, stream, p);
   return hipGetLastError();

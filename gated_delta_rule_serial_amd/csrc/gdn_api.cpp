@@ -48,7 +48,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-size_t io_size(int32_t dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+size_t io_size(int32_t dtype) { return dtype == GDN_F32 ? 4 : 2; }
+bool io_known(int32_t dtype) { return dtype == GDN_F32 || dtype == GDN_BF16 || dtype == GDN_F16; }
+const char* io_name(int32_t dtype) { return dtype == GDN_F32 ? "f32" : dtype == GDN_BF16 ? "bf16" : "f16"; }
 
 bool rule_decays(int32_t rule) { return rule == GDN_RULE_GATED_DELTA || rule == GDN_RULE_GATED; }
 bool rule_deltas(int32_t rule) { return rule == GDN_RULE_GATED_DELTA || rule == GDN_RULE_DELTA; }
@@ -68,8 +70,9 @@ gdn_status check_problem(const gdn_problem* p, const char* fn, bool has_tokens) 
   if (p->d_k > GDN_MAX_HEAD_DIM || p->d_v > GDN_MAX_HEAD_DIM)
     return fail(GDN_ERR_UNSUPPORTED, "%s: head sizes above %d are not supported (d_k=%d, d_v=%d)", fn,
                 GDN_MAX_HEAD_DIM, p->d_k, p->d_v);
-  if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16)
-    return fail(GDN_ERR_UNSUPPORTED, "%s: io_dtype %d is not supported (GDN_F32, GDN_BF16)", fn, p->io_dtype);
+  if (!io_known(p->io_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: io_dtype %d is not supported (GDN_F32, GDN_BF16, GDN_F16)", fn,
+                p->io_dtype);
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
   const size_t es = io_size(p->io_dtype);
   if (p->rule < GDN_RULE_GATED_DELTA || p->rule > GDN_RULE_LINEAR)
@@ -234,7 +237,7 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
                 "%s: the chunked algorithm needs bfloat16 I/O, d_k 64 or 128, d_v a multiple of 8, the "
                 "gated-delta or delta rule with a per-head decay and no state history (got %s, d_k=%d, "
                 "d_v=%d, rule=%d, decay_per_key=%d, state_window=%d)",
-                fn, io_bf16 ? "bf16" : "f32", p.d_k, p.d_v, p.rule, p.decay_per_key, window);
+                fn, io_name(p.io_dtype), p.d_k, p.d_v, p.rule, p.decay_per_key, window);
   const bool chunked = p.algorithm == GDN_ALGO_CHUNKED ||
                        (p.algorithm == GDN_ALGO_AUTO && can_chunk &&
                         static_cast<int64_t>(total_tokens) >= 64 * static_cast<int64_t>(num_seqs));
@@ -245,7 +248,7 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
     return fail(GDN_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", fn,
                 static_cast<unsigned long long>(blocks));
   const hipError_t e = chunked ? gdn::launch_prefill_chunked(sp, io_bf16, stream)
-                               : gdn::launch_prefill_scan(sp, io_bf16, stream);
+                               : gdn::launch_prefill_scan(sp, p.io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -327,7 +330,7 @@ gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch
   dp.scale = resolved_scale(problem);
   if (p.h_v > 65535)
     return fail(GDN_ERR_UNSUPPORTED, "%s: h_v = %d exceeds the grid's head axis (65535)", fn, p.h_v);
-  const hipError_t e = gdn::launch_decode_step(dp, p.io_dtype == GDN_BF16, stream);
+  const hipError_t e = gdn::launch_decode_step(dp, p.io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -358,7 +361,7 @@ GDN_EXPORT gdn_status gdn_gate_prologue(int32_t tokens, int32_t h_v, int32_t io_
   const char* fn = "gdn_gate_prologue";
   if (tokens < 0 || h_v <= 0)
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: tokens=%d must be >= 0 and h_v=%d > 0", fn, tokens, h_v);
-  if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
+  if (!io_known(io_dtype))
     return fail(GDN_ERR_UNSUPPORTED, "%s: io_dtype %d is not supported", fn, io_dtype);
   if (tokens == 0 || (!g && !beta)) return ok();
   if (g && (!a || !A_log || !dt_bias))
@@ -377,7 +380,7 @@ GDN_EXPORT gdn_status gdn_gate_prologue(int32_t tokens, int32_t h_v, int32_t io_
   gp.beta = beta;
   gp.rows = tokens;
   gp.h_v = h_v;
-  const hipError_t e = gdn::launch_gate_prologue(gp, io_dtype == GDN_BF16, stream);
+  const hipError_t e = gdn::launch_gate_prologue(gp, io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }

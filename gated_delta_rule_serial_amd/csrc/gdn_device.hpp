@@ -10,16 +10,27 @@
 namespace gdn {
 
 using bf16_t = uint16_t;  // bfloat16 storage
+using f16_t = _Float16;   // IEEE binary16 storage
 
 // ---------------------------------------------------------------- scalars
 __device__ __forceinline__ float widen(float x) { return x; }
 __device__ __forceinline__ float widen(bf16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+__device__ __forceinline__ float widen(f16_t x) { return static_cast<float>(x); }
 
-// Narrowing rounds to nearest even (gfx950 v_cvt_pk_bf16_f32).
+// Widen the 16-bit pattern in the low half of `bits` as an element of IO.
+template <typename IO>
+__device__ __forceinline__ float widen_bits16(uint32_t bits) {
+  if constexpr (__is_same(IO, f16_t)) return static_cast<float>(__builtin_bit_cast(f16_t, static_cast<uint16_t>(bits)));
+  else return __uint_as_float(bits << 16);
+}
+
+// Narrowing rounds to nearest even (gfx950 v_cvt_pk_bf16_f32, v_cvt_f16_f32
+// in the default rounding mode).
 __device__ __forceinline__ void narrow_store(float* p, float x) { *p = x; }
 __device__ __forceinline__ void narrow_store(bf16_t* p, float x) {
   *p = __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
 }
+__device__ __forceinline__ void narrow_store(f16_t* p, float x) { *p = static_cast<f16_t>(x); }
 
 template <typename IO>
 __device__ __forceinline__ float load1(const IO* p) { return widen(*p); }
@@ -137,7 +148,7 @@ struct RawSlice {
 #pragma unroll
       for (int e = 0; e < N; ++e) {
         const uint32_t word = w[e / 2];
-        dst[e] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+        dst[e] = widen_bits16<IO>((e & 1) ? (word >> 16) : (word & 0xffffu));
       }
     }
   }
@@ -153,7 +164,7 @@ struct RawScalar {
   }
   __device__ __forceinline__ float value() const {
     if constexpr (sizeof(IO) == 4) return __uint_as_float(w);
-    else return __uint_as_float(w << 16);
+    else return widen_bits16<IO>(w);
   }
 };
 

@@ -75,11 +75,12 @@ struct GatePrologueParams {
   int32_t h_v;
 };
 
-// io_bf16: 1 for bfloat16 I/O, 0 for float32.  Each launcher enqueues on
-// `stream` and returns the launch status.
-hipError_t launch_prefill_scan(ScanParams p, int io_bf16, hipStream_t stream);
-hipError_t launch_decode_step(DecodeParams p, int io_bf16, hipStream_t stream);
-hipError_t launch_gate_prologue(GatePrologueParams p, int io_bf16, hipStream_t stream);
+// io_dtype: the gdn_dtype of the I/O tensors (0 float32, 1 bfloat16,
+// 2 float16).  Each launcher enqueues on `stream` and returns the launch
+// status.
+hipError_t launch_prefill_scan(ScanParams p, int io_dtype, hipStream_t stream);
+hipError_t launch_decode_step(DecodeParams p, int io_dtype, hipStream_t stream);
+hipError_t launch_gate_prologue(GatePrologueParams p, int io_dtype, hipStream_t stream);
 
 // Chunked (matrix-core) prefill: whether a geometry is built, the state
 // columns one workgroup owns, and the launcher.

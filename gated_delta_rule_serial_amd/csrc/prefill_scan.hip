@@ -314,8 +314,10 @@ int scan_columns_per_wave(int d_k) {
   return kWave / ScanShape<256>::R;
 }
 
-hipError_t launch_prefill_scan(ScanParams p, int io_bf16, hipStream_t stream) {
-  return io_bf16 ? launch_io<bf16_t>(p, stream) : launch_io<float>(p, stream);
+hipError_t launch_prefill_scan(ScanParams p, int io_dtype, hipStream_t stream) {
+  if (io_dtype == 1) return launch_io<bf16_t>(p, stream);
+  if (io_dtype == 2) return launch_io<f16_t>(p, stream);
+  return launch_io<float>(p, stream);
 }
 
 }  // namespace gdn

@@ -20,13 +20,13 @@ LIB_PATH = os.path.join(PKG, "libgdn.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "gdn.h")
 
 GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
-GDN_F32, GDN_BF16 = 0, 1
+GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 GDN_GATES_PRECOMPUTED, GDN_GATES_RAW = 0, 1
 GDN_ALGO_AUTO, GDN_ALGO_SERIAL, GDN_ALGO_CHUNKED = 0, 1, 2
 ALGORITHMS = {"auto": GDN_ALGO_AUTO, "serial": GDN_ALGO_SERIAL, "chunked": GDN_ALGO_CHUNKED}
 RULES = {"gated_delta": 0, "delta": 1, "gated": 2, "linear": 3}
 
-_DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+_DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
 
 
 class gdn_problem(ctypes.Structure):

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -53,9 +53,13 @@ typedef enum gdn_status {
   GDN_ERR_HIP = 3               /* a HIP runtime call failed (launch, attrs) */
 } gdn_status;
 
+/* I/O element types ([P4] module doc: half-precision inputs are widened to
+ * float32 on read and narrowed on write; its `linear_attention_f16` and
+ * `linear_attention_bf16` entry kernels).  Narrowing rounds to nearest even. */
 typedef enum gdn_dtype {
   GDN_F32 = 0,
-  GDN_BF16 = 1
+  GDN_BF16 = 1,
+  GDN_F16 = 2
 } gdn_dtype;
 
 /* How the per-token gates reach the recurrence. */
@@ -76,7 +80,8 @@ typedef enum gdn_algorithm {
    * SERIAL otherwise. */
   GDN_ALGO_AUTO = 0,
   /* Token-by-token scan in float32 on the vector ALUs ([P4]'s order of
-   * operations); any gates, any head size 1..256, float32 or bfloat16 I/O. */
+   * operations); any gates, any head size 1..256, float32, bfloat16 or
+   * float16 I/O. */
   GDN_ALGO_SERIAL = 1,
   /* The same recurrence in chunks of 64 tokens on the matrix cores (bf16
    * operands, f32 accumulation, f32 state carried between chunks).  Needs

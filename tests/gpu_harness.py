@@ -17,8 +17,11 @@ import torch
 import oracle
 from gated_delta_rule_serial_amd import gdn, synth
 
-# Tolerances: |gpu - ref| <= tol (1 + |ref|) elementwise.
-TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+# Tolerances: |gpu - ref| <= tol (1 + |ref|) elementwise.  float32 and
+# bfloat16 are the stated bars; float16 takes twice its unit roundoff
+# (2^-11): the output is narrowed once, the inputs are the same float16
+# values on both sides, and float32 accumulation adds ~1e-6.
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2, torch.float16: 1e-3}
 
 
 def say(msg: str):

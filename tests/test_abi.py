@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 4
+    assert gdn.abi_version() == 5
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -78,6 +78,8 @@ INVALID, UNSUPPORTED = gdn.GDN_ERR_INVALID_ARGUMENT, gdn.GDN_ERR_UNSUPPORTED
     ("bad gate mode", dict(gate_mode=5), {}, INVALID, "gate_mode"),
     ("bad algorithm", dict(algorithm=7), {}, INVALID, "algorithm"),
     ("chunked on f32", dict(algorithm=gdn.GDN_ALGO_CHUNKED), {}, UNSUPPORTED, "chunked algorithm needs"),
+    ("chunked on f16", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_F16, d_k=64, d_v=64), {}, UNSUPPORTED,
+     "got f16"),
     ("chunked on d_k 48", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_BF16, d_k=48), {}, UNSUPPORTED,
      "chunked algorithm needs"),
     ("misaligned g", dict(g=FAKE + 2), {}, INVALID, "aligned"),
@@ -144,6 +146,7 @@ def test_decode_empty_batch_is_ok(lib):
     (dict(tokens=-1), INVALID, "tokens"),
     (dict(h_v=0), INVALID, "h_v"),
     (dict(dtype=3), UNSUPPORTED, "io_dtype"),
+    (dict(dtype=-1), UNSUPPORTED, "io_dtype"),
     (dict(a=0), INVALID, "g needs"),
     (dict(b=0), INVALID, "beta needs"),
     (dict(g=FAKE + 0x40001), INVALID, "aligned"),

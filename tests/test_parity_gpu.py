@@ -8,7 +8,7 @@ full-size cases run the library exactly as the benchmark launches it and
 compare sampled (q/k head group) slices that the oracle computes alone.
 
 Tolerance: |gpu - ref| <= tol (1 + |ref|) elementwise, tol = 1e-4 for float32
-I/O and 1e-2 for bfloat16 I/O.
+I/O, 1e-2 for bfloat16 I/O and 1e-3 for float16 I/O.
 """
 import dataclasses
 
@@ -63,6 +63,9 @@ GEOMETRIES = [
     (4, 8, 64, 64, torch.bfloat16, [65, 64, 63]),
     (1, 2, 32, 200, torch.float32, [9, 17]),
     (2, 4, 128, 128, torch.float32, [1, 2, 3, 4, 5, 6, 7, 8, 9, 10]),
+    (2, 4, 128, 128, torch.float16, [70, 0, 13]),
+    (1, 1, 16, 3, torch.float16, [130]),
+    (3, 6, 256, 256, torch.float16, [21, 2]),
 ]
 
 
@@ -148,6 +151,36 @@ def test_rounding_tie_to_even():
     assert st[0, 0, 0, 0].item() == 1.005859375
 
 
+def test_rounding_tie_to_even_f16():
+    """The float16 form of the same question: v = 1 + 2^-10 gives the exact
+    outputs 1 + 2^-11 (a float16 tie, to 1.0) and 1 + 3 2^-12 (to 1 + 2^-10)."""
+    d = 16
+    q = torch.zeros(2, 1, d)
+    q[:, 0, 0] = 1.0
+    v = torch.zeros(2, 1, d)
+    v[:, 0, 0] = 1.0 + 2.0 ** -10
+    s0 = torch.zeros(1, 1, d, d)
+    s0[0, 0, 0, 0] = 1.0
+    hf = torch.float16
+    dev = "cuda"
+    g = torch.zeros(2, 1, dtype=hf, device=dev)
+    beta = torch.full((2, 1), 0.5, dtype=hf, device=dev)
+    qd = q.to(hf).to(dev)
+    say("[rounding-f16] prefill")
+    out, fin = gdn.prefill(qd, qd, v.to(hf).to(dev), torch.tensor([0, 2], dtype=torch.int32, device=dev),
+                           initial_state=s0.to(dev), g=g, beta=beta, scale=1.0)
+    torch.cuda.synchronize()
+    assert out[:, 0, 0].float().tolist() == [1.0, 1.0 + 2.0 ** -10]
+    assert fin[0, 0, 0, 0].item() == 1.0 + 3 * 2.0 ** -12
+    say("[rounding-f16] decode")
+    st = s0.to(dev).clone()
+    outs = [gdn.decode_step(qd[t:t + 1], qd[t:t + 1], v[t:t + 1].to(hf).to(dev), st, g=g[t:t + 1],
+                            beta=beta[t:t + 1], scale=1.0) for t in range(2)]
+    torch.cuda.synchronize()
+    assert [o[0, 0, 0].item() for o in outs] == [1.0, 1.0 + 2.0 ** -10]
+    assert st[0, 0, 0, 0].item() == 1.0 + 3 * 2.0 ** -12
+
+
 # ------------------------------------------------------------------ decode
 def _decode_inputs(shape, seed):
     inp = synth.generate(shape, seed=seed)
@@ -188,6 +221,8 @@ DECODE_GEOMS = [
     (3, 6, 100, 130, torch.bfloat16, 4),
     (1, 2, 1, 1, torch.float32, 7),
     (2, 2, 128, 66, torch.float32, 3),
+    (16, 32, 128, 128, torch.float16, 8),
+    (1, 1, 48, 40, torch.float16, 3),
 ]
 
 
@@ -226,7 +261,7 @@ def test_decode_steps_equal_prefill():
 
 
 # ------------------------------------------------------------------ gate prologue
-@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16, torch.float16], ids=["f32", "bf16", "f16"])
 def test_gate_prologue(dt):
     shape = _shape("prefill_t4096_fused_gates", io_dtype=dt)
     inp = synth.generate(shape, seqlen=333)
