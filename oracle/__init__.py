@@ -79,6 +79,10 @@ class Oracle:
         lib.gdnref_decode_step.argtypes = [i32, i32, i32, i32, i32, f64, i32,
                                            dp, dp, dp, dp, dp, dp, dp]
         lib.gdnref_decode_step.restype = ctypes.c_int
+        lib.gdnref_causal_conv.argtypes = [i32, i32, i32, i32, i32, ip, dp, dp, dp, dp, dp, dp]
+        lib.gdnref_causal_conv.restype = ctypes.c_int
+        lib.gdnref_gated_rmsnorm.argtypes = [i64, i32, i32, dp, dp, dp, f64, i32, dp]
+        lib.gdnref_gated_rmsnorm.restype = ctypes.c_int
         lib.gdnref_max_threads.argtypes = []
         lib.gdnref_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -148,6 +152,37 @@ class Oracle:
         if rc != 0:
             raise ValueError("gdnref_decode_step rejected its arguments")
         return out
+
+
+    def causal_conv(self, x, weight, cu_seqlens, bias=None, initial_state=None, *, dilation=1, silu=False):
+        """Causal depthwise conv with carried state.  x: [T, C]; weight: [C, K];
+        bias: [C] or None; cu_seqlens: ints [N+1]; initial_state: [N, carry, C]
+        or None (zeros).  Returns (y [T, C], final_state [N, carry, C]) float64."""
+        x, w, b, s0 = _f64(x), _f64(weight), _f64(bias), _f64(initial_state)
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        T, C = x.shape
+        K = w.shape[1]
+        carry = (K - 1) * dilation
+        n = cu.size - 1
+        y = np.empty((T, C), np.float64)
+        fin = np.empty((n, carry, C), np.float64)
+        rc = self.lib.gdnref_causal_conv(C, K, int(dilation), int(bool(silu)), n, _ptr(cu, ctypes.c_int32),
+                                         _ptr(x), _ptr(w), _ptr(b), _ptr(s0), _ptr(y), _ptr(fin))
+        if rc != 0:
+            raise ValueError("gdnref_causal_conv rejected its arguments")
+        return y, fin
+
+    def gated_rmsnorm(self, x, gate, scale, *, eps=1e-5, activation="silu"):
+        """Gated RMSNorm over groups of len(scale) elements of the last axis of x."""
+        x, g, s = _f64(x), _f64(gate), _f64(scale)
+        width = x.shape[-1]
+        rows = x.size // width if width else 0
+        y = np.empty(x.shape, np.float64)
+        act = {"silu": 1, "swish": 1, "sigmoid": 2}[activation]
+        rc = self.lib.gdnref_gated_rmsnorm(rows, width, s.size, _ptr(x), _ptr(g), _ptr(s), float(eps), act, _ptr(y))
+        if rc != 0:
+            raise ValueError("gdnref_gated_rmsnorm rejected its arguments")
+        return y
 
 
 _default = None

@@ -207,6 +207,67 @@ int gdnref_decode_step(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
   return rc;
 }
 
+/* [P1] `causal_conv_op`: the past state is concatenated in front of the
+ * input along time, a depthwise conv1d (a cross-correlation: tap j meets
+ * input position t - carry + j * dilation) runs over it, the bias is added
+ * and silu applied; the present state is the last `carry` positions of the
+ * padded input.  [P3]'s fallback graph does the same with a pool. */
+int gdnref_causal_conv(int32_t channels, int32_t ksize, int32_t dilation, int32_t silu,
+                       int32_t num_seqs, const int32_t* cu_seqlens, const double* x,
+                       const double* weight, const double* bias,
+                       const double* initial_state, double* y, double* final_state) {
+  if (channels <= 0 || ksize <= 0 || dilation <= 0 || num_seqs < 0) return -1;
+  if (num_seqs > 0 && (!cu_seqlens || cu_seqlens[0] != 0)) return -1;
+  for (int32_t n = 0; n < num_seqs; ++n)
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+  const int64_t carry = (int64_t)(ksize - 1) * dilation;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t t0 = cu_seqlens[n];
+    const int64_t L = cu_seqlens[n + 1] - t0;
+    const double* s0 = initial_state ? initial_state + (int64_t)n * carry * channels : NULL;
+    for (int32_t c = 0; c < channels; ++c) {
+      /* padded input at position p, -carry <= p < L */
+#define XP(p) ((p) < 0 ? (s0 ? s0[(carry + (p)) * channels + c] : 0.0) : x[(t0 + (p)) * channels + c])
+      for (int64_t t = 0; t < L && y; ++t) {
+        double z = bias ? bias[c] : 0.0;
+        for (int32_t j = 0; j < ksize; ++j)
+          z += weight[(int64_t)c * ksize + j] * XP(t - carry + (int64_t)j * dilation);
+        y[(t0 + t) * channels + c] = silu ? z * gdnref_sigmoid(z) : z;
+      }
+      if (final_state) {
+        double* fs = final_state + (int64_t)n * carry * channels;
+        for (int64_t i = 0; i < carry; ++i) fs[i * channels + c] = XP(L - carry + i);
+      }
+#undef XP
+    }
+  }
+  return 0;
+}
+
+/* [P1] `gated_rms_norm_op`: rows of `group` elements in float, mean of the
+ * squares plus epsilon, reciprocal square root, times the scale, times the
+ * gate's activation (silu by default, or sigmoid). */
+int gdnref_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, const double* x,
+                         const double* gate, const double* scale, double eps,
+                         int32_t activation, double* y) {
+  if (rows < 0 || width <= 0 || group <= 0 || width % group != 0) return -1;
+  if (activation != 1 && activation != 2) return -1;
+  const int64_t groups = rows * (width / group);
+  for (int64_t r = 0; r < groups; ++r) {
+    const double* xr = x + r * group;
+    const double* gr = gate + r * group;
+    double ss = 0.0;
+    for (int32_t i = 0; i < group; ++i) ss += xr[i] * xr[i];
+    const double inv = 1.0 / sqrt(ss / group + eps);
+    for (int32_t i = 0; i < group; ++i) {
+      const double s = gdnref_sigmoid(gr[i]);
+      const double act = activation == 1 ? gr[i] * s : s;
+      y[r * group + i] = xr[i] * inv * scale[i] * act;
+    }
+  }
+  return 0;
+}
+
 int gdnref_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

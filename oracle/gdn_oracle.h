@@ -10,8 +10,10 @@
  * Sources (web pages; cited by page and section, no line numbers):
  *   [P1] onnxruntime-ep-mlx 0.31.1, src/ops/ssm.rs
  *        -- `linear_attention_op` (stable unroll, T = 0 handling),
- *           `linear_attention_gate_op`, the wide-BF16 working-state test.
- *   [P3] nuvec-core 0.6.1, fast/imp.rs -- `gated_delta_graph`.
+ *           `linear_attention_gate_op`, the wide-BF16 working-state test,
+ *           `causal_conv_op` (CausalConvWithState), `gated_rms_norm_op`.
+ *   [P3] nuvec-core 0.6.1, fast/imp.rs -- `gated_delta_graph`, the
+ *        `causal_conv1d_slots` fallback graph.
  *   [P4] onnx-runtime-ep-cuda 0.1.0-dev.6, src/kernels/linear_attention.rs
  *        -- module doc "Parallelization", `linear_attention_core` steps
  *           1-4, the gate helpers `la_sigmoid` / `la_softplus`,
@@ -116,6 +118,32 @@ int gdnref_decode_step(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
                        const double* q, const double* k, const double* v,
                        const double* g, const double* beta, double* state,
                        double* out);
+
+/* Causal depthwise conv1d with a carried state ([P1] `causal_conv_op`,
+ * channels-last layout; [P3] `causal_conv1d_slots` fallback graph).  With
+ * carry = (ksize - 1) * dilation and, for sequence n of length L, the padded
+ * input xp(p) = initial_state[n, carry + p, c] for -carry <= p < 0 (zeros
+ * without an initial state) and x[cu[n] + p, c] for 0 <= p < L:
+ *     z = bias[c] + sum_j weight[c, j] * xp(t - carry + j * dilation)
+ *     y[cu[n] + t, c] = silu ? z * sigmoid(z) : z
+ *     final_state[n, i, c] = xp(L - carry + i),  0 <= i < carry.
+ * Layouts: x, y [T_total, channels]; weight [channels, ksize]; bias
+ * [channels] or NULL; states [num_seqs, carry, channels] (either may be
+ * NULL).  Returns 0, or -1 on an invalid argument. */
+int gdnref_causal_conv(int32_t channels, int32_t ksize, int32_t dilation, int32_t silu,
+                       int32_t num_seqs, const int32_t* cu_seqlens, const double* x,
+                       const double* weight, const double* bias,
+                       const double* initial_state, double* y, double* final_state);
+
+/* Gated RMSNorm ([P1] `gated_rms_norm_op`): each row of `width` elements is
+ * split into width / group groups of `group` consecutive elements; per group
+ *     y = x / sqrt(mean(x^2) + eps) * scale * act(gate)
+ * with scale [group] and act = silu (activation 1: gate * sigmoid(gate)) or
+ * sigmoid (activation 2).  x, gate, y are [rows, width].  Returns 0, or -1 on
+ * an invalid argument. */
+int gdnref_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, const double* x,
+                         const double* gate, const double* scale, double eps,
+                         int32_t activation, double* y);
 
 /* Threads the parallel loop over independent (sequence, head) units uses. */
 int gdnref_max_threads(void);

@@ -5,7 +5,8 @@ Every function here takes an ``oracle.Oracle`` instance and raises
   * a brute-force unrolled matrix form in long double (shares no code with the
     scan: it multiplies the per-token transition matrices out explicitly),
   * invariants the delta rule fixes, closed forms and special cases,
-  * library routines (numpy / scipy) for the gate functions,
+  * library routines (numpy / scipy / torch) for the gate functions, the
+    depthwise convolution and the RMS normalisation,
   * the values printed in the pages' one worked example (tests/golden/).
 
 ``test_oracle_pins.py`` runs them on the real oracle;
@@ -439,10 +440,139 @@ def pin_page_worked_example_window(orc):
             assert np.all(st[:, 1:] == 0.0)
 
 
+# ---------------------------------------------------------------- causal conv with state
+def _conv_case(seed, lens, C=5, K=4, init=True):
+    rng = np.random.default_rng(seed)
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, K))
+    b = rng.standard_normal(C)
+    return rng, cu, x, w, b
+
+
+def pin_conv_library(orc):
+    """Each sequence against torch's depthwise conv1d (groups = channels, a
+    cross-correlation) over [initial state ; x], plus torch's silu."""
+    import torch.nn.functional as F
+    for dil, silu, bias_on in [(1, False, True), (1, True, True), (2, True, False), (3, False, True)]:
+        rng, cu, x, w, b = _conv_case(11 + dil, [9, 0, 3, 1])
+        K, C = w.shape[1], w.shape[0]
+        carry = (K - 1) * dil
+        s0 = rng.standard_normal((len(cu) - 1, carry, C))
+        y, fin = orc.causal_conv(x, w, cu, b if bias_on else None, s0, dilation=dil, silu=silu)
+        for n in range(len(cu) - 1):
+            xp = np.concatenate([s0[n], x[cu[n]:cu[n + 1]]], 0)           # [carry + L, C]
+            assert np.array_equal(fin[n], xp[xp.shape[0] - carry:]), (dil, n)
+            if cu[n + 1] == cu[n]:
+                continue
+            ref = F.conv1d(torch.from_numpy(xp.T[None].copy()), torch.from_numpy(w[:, None, :].copy()),
+                           torch.from_numpy(b) if bias_on else None, dilation=dil, groups=C)[0].T
+            if silu:
+                ref = F.silu(ref)
+            assert np.allclose(y[cu[n]:cu[n + 1]], ref.numpy(), rtol=1e-13, atol=1e-13), (dil, silu, n)
+
+
+def pin_conv_continuation(orc):
+    """conv(x1) then conv(x2) from its final state = conv(x1 x2), bitwise, for
+    pieces shorter and longer than the carried window; token-by-token steps
+    equal the whole sequence."""
+    for dil in (1, 2):
+        rng, _, x, w, b = _conv_case(21 + dil, [13])
+        K, C = w.shape[1], w.shape[0]
+        s0 = rng.standard_normal((1, (K - 1) * dil, C))
+        y_all, f_all = orc.causal_conv(x, w, [0, 13], b, s0, dilation=dil, silu=True)
+        for cut in (1, 2, 5, 12):
+            y1, f1 = orc.causal_conv(x[:cut], w, [0, cut], b, s0, dilation=dil, silu=True)
+            y2, f2 = orc.causal_conv(x[cut:], w, [0, 13 - cut], b, f1, dilation=dil, silu=True)
+            assert np.array_equal(np.concatenate([y1, y2]), y_all) and np.array_equal(f2, f_all), (dil, cut)
+        st, ys = s0, []
+        for t in range(13):
+            yt, st = orc.causal_conv(x[t:t + 1], w, [0, 1], b, st, dilation=dil, silu=True)
+            ys.append(yt)
+        assert np.array_equal(np.concatenate(ys), y_all) and np.array_equal(st, f_all), dil
+
+
+def pin_conv_special_kernels(orc):
+    """A kernel with only its last tap set passes x through; only its first
+    tap delays x by the carried window; an empty sequence keeps its state;
+    packed = each sequence alone."""
+    rng, cu, x, w, b = _conv_case(31, [6, 0, 4])
+    C, K = w.shape
+    s0 = rng.standard_normal((3, K - 1, C))
+    last = np.zeros((C, K)); last[:, K - 1] = 1.0
+    y, fin = orc.causal_conv(x, last, cu, None, s0)
+    assert np.array_equal(y, x)
+    assert np.array_equal(fin[1], s0[1])                      # empty sequence
+    first = np.zeros((C, K)); first[:, 0] = 1.0
+    y, _ = orc.causal_conv(x, first, cu, None, s0)
+    for n in range(3):
+        xp = np.concatenate([s0[n], x[cu[n]:cu[n + 1]]], 0)
+        assert np.array_equal(y[cu[n]:cu[n + 1]], xp[:cu[n + 1] - cu[n]])
+    y_all, f_all = orc.causal_conv(x, w, cu, b, s0, silu=True)
+    for n in range(3):
+        yn, fn = orc.causal_conv(x[cu[n]:cu[n + 1]], w, [0, cu[n + 1] - cu[n]], b, s0[n:n + 1], silu=True)
+        assert np.array_equal(yn, y_all[cu[n]:cu[n + 1]]) and np.array_equal(fn[0], f_all[n])
+    y0, f0 = orc.causal_conv(x, w, cu, b, None)              # no initial state = zeros
+    yz, fz = orc.causal_conv(x, w, cu, b, np.zeros_like(s0))
+    assert np.array_equal(y0, yz) and np.array_equal(f0, fz)
+
+
+# ---------------------------------------------------------------- gated RMSNorm
+def pin_rmsnorm_library(orc):
+    """Against torch's rms_norm (with the scale as its weight) times torch's
+    silu / sigmoid of the gate; a saturated sigmoid gate leaves rms_norm alone."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(41)
+    C = 12
+    x = rng.standard_normal((7, 3 * C))
+    gate = rng.standard_normal((7, 3 * C)) * 3
+    scale = rng.standard_normal(C)
+    eps = 1e-5
+    xt = torch.from_numpy(x.reshape(-1, C))
+    norm = F.rms_norm(xt, (C,), weight=torch.from_numpy(scale), eps=eps)
+    gt = torch.from_numpy(gate.reshape(-1, C))
+    for act, f in (("silu", F.silu), ("sigmoid", torch.sigmoid)):
+        y = orc.gated_rmsnorm(x, gate, scale, eps=eps, activation=act)
+        ref = (norm * f(gt)).reshape(x.shape).numpy()
+        assert np.allclose(y, ref, rtol=1e-13, atol=1e-15), act
+    y = orc.gated_rmsnorm(x, np.full_like(x, 50.0), scale, eps=eps, activation="sigmoid")
+    assert np.allclose(y, norm.reshape(x.shape).numpy(), rtol=1e-14, atol=1e-15)
+
+
+def pin_rmsnorm_invariants(orc):
+    """eps = 0: scaling x by a power of two changes nothing (bitwise); the
+    normalised rows have unit mean square; a constant row normalises to its
+    sign; a zero gate gives 0 (silu) or half the normalised row (sigmoid);
+    groups are independent rows."""
+    rng = np.random.default_rng(43)
+    C = 8
+    x = rng.standard_normal((5, 2 * C))
+    gate = rng.standard_normal((5, 2 * C))
+    scale = rng.standard_normal(C)
+    y = orc.gated_rmsnorm(x, gate, scale, eps=0.0)
+    assert np.array_equal(orc.gated_rmsnorm(x * 2.0 ** 7, gate, scale, eps=0.0), y)
+    sat = np.full_like(x, 60.0)
+    u = orc.gated_rmsnorm(x, sat, np.ones(C), eps=0.0, activation="sigmoid")
+    assert np.allclose((u.reshape(-1, C) ** 2).mean(1), 1.0, rtol=0, atol=1e-14)
+    const = np.full((2, C), -3.25)
+    assert np.array_equal(orc.gated_rmsnorm(const, np.full((2, C), 60.0), scale, eps=0.0, activation="sigmoid"),
+                          np.broadcast_to(-scale, (2, C)))
+    z = np.zeros_like(x)
+    assert np.array_equal(orc.gated_rmsnorm(x, z, scale, eps=0.0, activation="silu"), z)
+    half = orc.gated_rmsnorm(x, z, scale, eps=0.0, activation="sigmoid")
+    assert np.allclose(half, 0.5 * orc.gated_rmsnorm(x, sat, scale, eps=0.0, activation="sigmoid"), rtol=1e-15)
+    rows = orc.gated_rmsnorm(x.reshape(-1, C), gate.reshape(-1, C), scale)
+    assert np.array_equal(rows.reshape(x.shape), orc.gated_rmsnorm(x, gate, scale))
+    assert np.array_equal(orc.gated_rmsnorm(np.zeros((1, C)), gate[:1, :C], scale), np.zeros((1, C)))
+
+
 ALL_PINS = [
     pin_brute_force, pin_delta_rule_memorises, pin_frozen_state, pin_reset,
     pin_power_of_two_scaling, pin_packing_invariance, pin_continuation, pin_gqa_repeat,
     pin_empty, pin_scalar_closed_form, pin_orthonormal_keys, pin_gates_library,
     pin_default_scale, pin_page_worked_example, pin_rounding_tie, pin_variants_brute_force,
     pin_variant_reductions, pin_state_history, pin_page_worked_example_window,
+    pin_conv_library, pin_conv_continuation, pin_conv_special_kernels,
+    pin_rmsnorm_library, pin_rmsnorm_invariants,
 ]

@@ -32,6 +32,17 @@ MUTANTS = [
     ("shared beta not per token", "beta_shared ? beta[t] :", "beta_shared ? beta[0] :"),
     ("history slot off by one", "const int64_t w = (t - t0) - ((t1 - t0) - window);",
      "const int64_t w = (t - t0) - ((t1 - t0) - window) - 1;"),
+    ("conv taps reversed", "z += weight[(int64_t)c * ksize + j]", "z += weight[(int64_t)c * ksize + (ksize - 1 - j)]"),
+    ("conv dilation ignored", "XP(t - carry + (int64_t)j * dilation)", "XP(t - carry + (int64_t)j)"),
+    ("conv silu dropped", "y[(t0 + t) * channels + c] = silu ? z * gdnref_sigmoid(z) : z;",
+     "y[(t0 + t) * channels + c] = z;"),
+    ("conv bias dropped", "double z = bias ? bias[c] : 0.0;", "double z = 0.0;"),
+    ("conv state off by one", "fs[i * channels + c] = XP(L - carry + i);", "fs[i * channels + c] = XP(L - carry + i - 1);"),
+    ("conv initial state ignored", "(s0 ? s0[(carry + (p)) * channels + c] : 0.0)", "0.0"),
+    ("rmsnorm mean over the row", "sqrt(ss / group + eps)", "sqrt(ss / width + eps)"),
+    ("rmsnorm eps outside the root", "sqrt(ss / group + eps)", "(sqrt(ss / group) + eps)"),
+    ("rmsnorm activations swapped", "activation == 1 ? gr[i] * s : s", "activation == 2 ? gr[i] * s : s"),
+    ("rmsnorm scale not per element", "scale[i] * act", "scale[0] * act"),
 ]
 
 
