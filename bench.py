@@ -13,7 +13,9 @@ events on the stream the kernel runs on.  Prints ONE JSON line.
 Other workloads (--workload prefill_t4096_fused_gates, varlen_prefill_8seq,
 wide_prefill_t32768_d256, tiny_prefill) time one gdn_prefill per step, each
 between its own events, with a 1 GiB write in between that flushes the L2 and
-the Infinity Cache.
+the Infinity Cache.  The block's neighbouring operations are timed the same
+way: conv_step_b64 (gdn_causal_conv_step), conv_varlen_8seq (gdn_causal_conv)
+and gated_rmsnorm_t33173 (gdn_gated_rmsnorm).
 
 Inputs are synthetic and seeded (gated_delta_rule_serial_amd.synth); they are
 resident in device memory before the timed region starts.
@@ -290,6 +292,115 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto"):
     return line
 
 
+def _timed(one, steps, warmup, flush=None):
+    """Mean and median ms of `one` over `steps` launches, each between its own
+    events on the current stream (after a cache flush when given)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    times = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if flush is not None:
+            _flush(flush)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        one()
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_list = sorted(a.elapsed_time(b) for a, b in times)
+    return sum(ms_list) / len(ms_list), ms_list[len(ms_list) // 2], wall
+
+
+def bench_conv(shape, steps, warmup, want_cpu):
+    """gdn_causal_conv over packed sequences, or gdn_causal_conv_step for the
+    one-token workload.  HBM-bound: x and y once, the states in and out once,
+    the weights and bias once."""
+    dev = "cuda"
+    inp = synth.generate_conv(shape)
+    es = inp.x.element_size()
+    C, K = inp.weight.shape
+    carry = (K - 1) * shape.dilation
+    x, w, b = inp.x.to(dev), inp.weight.to(dev), inp.bias.to(dev)
+    n = len(inp.seqlens)
+    T = sum(inp.seqlens)
+    y = torch.empty_like(x)
+    step = shape.seqlen == 1
+    s0 = inp.initial_state.to(dev)
+    fin = s0 if step else torch.empty_like(s0)
+    cu = inp.cu_seqlens.to(dev)
+    cu_host = inp.cu_seqlens.tolist()
+    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+
+    def one():
+        if step:
+            gdn.gdn_causal_conv_step(x, w, fin, y=y, bias=b, dilation=shape.dilation)
+        else:
+            gdn.gdn_causal_conv(x, w, cu, y=y, bias=b, initial_state=s0, final_state=fin,
+                                dilation=shape.dilation, cu_seqlens_host=cu_host)
+
+    ms, med, wall = _timed(one, steps, warmup, flush)
+    nbytes = 2 * T * C * es + 2 * n * carry * C * es + C * K * es + C * es + (0 if step else (n + 1) * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    line = {"metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 6),
+            "ms_median": round(med, 6), "wall_s": round(wall, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": _traffic(shape.name, ["causal_conv.hip", "gdn_device.hpp"]),
+                         "kernel": "conv_step_kernel" if step else "conv_window_kernel + conv_state_kernel",
+                         "algorithmic_bytes_per_launch": nbytes},
+            "config": {"workload": shape.name, "num_seqs": n, "total_tokens": T, "channels": C, "kernel_size": K,
+                       "dilation": shape.dilation, "io_dtype": "bf16", "activation": "silu"}}
+    if want_cpu:
+        import oracle
+        orc = oracle.default()
+        cols = min(C, 64)
+        t0 = time.perf_counter()
+        orc.causal_conv(inp.x[:, :cols], inp.weight[:cols], cu_host, inp.bias[:cols], inp.initial_state[:, :, :cols],
+                        dilation=shape.dilation, silu=True)
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(T * cols / C / el, 3), "unit": "tokens/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"channels 0-{cols - 1} of {C}, every token ({T}), in {el:.2f} s on one "
+                                          f"thread; rate scaled to all channels"}
+    return line
+
+
+def bench_norm(shape, steps, warmup, want_cpu):
+    """gdn_gated_rmsnorm over [rows, width]: x and gate read once, y written once."""
+    dev = "cuda"
+    inp = synth.generate_norm(shape)
+    es = inp.x.element_size()
+    x, g, sc = inp.x.to(dev), inp.gate.to(dev), inp.scale.to(dev)
+    y = torch.empty_like(x)
+    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    ms, med, wall = _timed(lambda: gdn.gdn_gated_rmsnorm(x, g, sc, y=y), steps, warmup, flush)
+    nbytes = 3 * x.numel() * es + sc.numel() * es
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    line = {"metric": METRIC, "value": round(shape.rows / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 6), "ms_median": round(med, 6), "wall_s": round(wall, 3),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": _traffic(shape.name, ["gated_rmsnorm.hip", "gdn_device.hpp"]),
+                         "kernel": "rmsnorm_kernel", "algorithmic_bytes_per_launch": nbytes},
+            "config": {"workload": shape.name, "rows": shape.rows, "width": shape.width, "group": shape.group,
+                       "io_dtype": "bf16", "activation": "silu", "eps": 1e-5}}
+    if want_cpu:
+        import oracle
+        orc = oracle.default()
+        rows = min(shape.rows, 2048)
+        t0 = time.perf_counter()
+        orc.gated_rmsnorm(inp.x[:rows], inp.gate[:rows], inp.scale)
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(rows / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                "sample": f"rows 0-{rows - 1} of {shape.rows} in {el:.2f} s on one thread"}
+    return line
+
+
 def bench_copy(mib, steps, warmup):
     """A plain device copy of known size (dst.copy_(src), mib MiB each way): the
     reference kernel that scales the rocprofv3 HBM byte counters."""
@@ -315,7 +426,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_b64", choices=sorted(synth.BY_NAME))
+    ap.add_argument("--workload", default="decode_b64",
+                    choices=sorted(synth.BY_NAME) + sorted(synth.CONV_BY_NAME) + sorted(synth.NORM_BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algorithm", default="auto", choices=["auto", "serial", "chunked"],
                     help="prefill formulation (prefill workloads only)")
@@ -333,15 +445,23 @@ def main():
     if args.copy_mib:
         print(json.dumps(bench_copy(args.copy_mib, args.steps or 50, args.warmup or 5)), flush=True)
         return
-    shape = synth.BY_NAME[args.workload]
-    decode = shape.kind == "decode"
-    steps = args.steps if args.steps is not None else (1000 if decode else 10)
-    warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
     want_cpu = not args.no_cpu_baseline
-    if decode:
-        line = bench_decode(shape, steps, warmup, want_cpu)
+    if args.workload in synth.CONV_BY_NAME or args.workload in synth.NORM_BY_NAME:
+        steps = args.steps if args.steps is not None else 20
+        warmup = args.warmup if args.warmup is not None else 3
+        if args.workload in synth.CONV_BY_NAME:
+            line = bench_conv(synth.CONV_BY_NAME[args.workload], steps, warmup, want_cpu)
+        else:
+            line = bench_norm(synth.NORM_BY_NAME[args.workload], steps, warmup, want_cpu)
     else:
-        line = bench_prefill(shape, steps, warmup, want_cpu, args.algorithm)
+        shape = synth.BY_NAME[args.workload]
+        decode = shape.kind == "decode"
+        steps = args.steps if args.steps is not None else (1000 if decode else 10)
+        warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
+        if decode:
+            line = bench_decode(shape, steps, warmup, want_cpu)
+        else:
+            line = bench_prefill(shape, steps, warmup, want_cpu, args.algorithm)
     head = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"), "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}

@@ -1,0 +1,318 @@
+// causal_conv.hip -- causal depthwise conv1d with a carried state (gfx950),
+// the operation in front of the gated delta-rule recurrence in its block.
+//
+// Definition ([P1] onnxruntime-ep-mlx, src/ops/ssm.rs, `causal_conv_op`
+// (CausalConvWithState); [P3] nuvec-core, fast/imp.rs, the
+// `causal_conv1d_slots` fallback graph): the carried state (the last
+// carry = (K - 1) * dilation inputs of the sequence so far) is put in front
+// of the new inputs along time, and per channel c
+//     z_t = bias_c + sum_j w[c, j] * xp(t - carry + j * dilation)
+//     y_t = z_t (or z_t * sigmoid(z_t) with silu)
+// where xp(p) is the state for p < 0 and the input for p >= 0; the new
+// state is the last `carry` positions of the padded input.  Layouts are
+// channels-last: x, y [T, C], states [N, carry, C], w [C, K].
+//
+// HBM-bound elementwise work (K multiply-adds per element).  Kernels:
+//   conv_window_kernel  dilation 1, K <= 4, C a multiple of one 16-byte
+//       vector: a thread owns one channel vector (16 bytes) of kSeg = 8
+//       consecutive tokens of the packed axis, loads their rows at once and
+//       slides the K - 1 previous inputs through registers; a wave reads
+//       1 KiB contiguous per token and writes it with 16-byte stores.  A
+//       segment may cross sequence boundaries; the window is then refilled
+//       from the next state.  Consecutive segments run on one L2 domain, so
+//       the rows in front of a segment tend to come from L2.  The silu uses
+//       the hardware exp2 / reciprocal: with the precise forms the kernel
+//       was bound by the vector ALUs, not by HBM.
+//   conv_generic_kernel any K and dilation: one thread per (token, channel).
+//   conv_state_kernel   the new state, one thread per (sequence, channel),
+//       after the outputs (stream order), so the state may be updated in place.
+//   conv_step_kernel    one token per sequence, state read and shifted in place.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 8;                // token rows loaded at once
+constexpr int kSeg = kChunk;             // tokens per thread in the window kernel
+constexpr int kXcds = 8;                 // L2 domains; workgroups go to them round-robin
+
+// Sequence holding packed token t: the n with cu[n] <= t < cu[n + 1].
+__device__ __forceinline__ int find_seq(const int32_t* cu, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Bounds of sequence n clamped into [0, T], so that a malformed cu_seqlens
+// (which is not read back to the host) can never send an access out of x.
+__device__ __forceinline__ int seq_begin(const int32_t* cu, int n, int T) { return min(max(cu[n], 0), T); }
+__device__ __forceinline__ int seq_end(const int32_t* cu, int n, int T) {
+  return min(max(cu[n + 1], seq_begin(cu, n, T)), T);
+}
+
+template <typename IO>
+__device__ __forceinline__ float silu_if(float z, int silu) {
+  return silu ? z * fast_sigmoid(z) : z;
+}
+
+// Padded input of sequence n (first token t0, state row base s0n) at
+// position p relative to the sequence start, channel c.
+template <typename IO>
+__device__ __forceinline__ float xp_at(const IO* __restrict__ x, const IO* __restrict__ s0, int C, int carry,
+                                       int n, int t0, int p, int c) {
+  if (p >= 0) return widen(x[static_cast<size_t>(t0 + p) * C + c]);
+  if (s0 == nullptr || p < -carry) return 0.0f;
+  return widen(s0[(static_cast<size_t>(n) * carry + carry + p) * C + c]);
+}
+
+// Grid: kXcds * segs_per_xcd * channel_blocks workgroups.  Workgroup L runs
+// on L2 domain L % kXcds; it takes channel block (L / kXcds) % channel_blocks
+// and segment (L % kXcds) * segs_per_xcd + (L / kXcds) / channel_blocks, so a
+// domain walks consecutive segments of the packed axis in order and the
+// K - 1 rows in front of a segment are still in its L2.
+template <typename IO, int K, bool SILU>
+__global__ __launch_bounds__(kThreads) void conv_window_kernel(ConvParams p, int channel_blocks, int segs_per_xcd) {
+  constexpr int V = 16 / static_cast<int>(sizeof(IO));
+  const int C = p.channels;
+  const int L = static_cast<int>(blockIdx.x);
+  const int slot = L / kXcds;
+  const int seg = (L % kXcds) * segs_per_xcd + slot / channel_blocks;
+  const int cv = (slot % channel_blocks) * kThreads + static_cast<int>(threadIdx.x);
+  const int t_first = seg * kSeg;
+  if (cv * V >= C || t_first >= p.total_tokens) return;
+  const int c0 = cv * V;
+  const int t_stop = min(t_first + kSeg, p.total_tokens);
+  const IO* __restrict__ x = static_cast<const IO*>(p.x);
+  const IO* __restrict__ s0 = static_cast<const IO*>(p.s0);
+  IO* __restrict__ y = static_cast<IO*>(p.y);
+
+  // weights [C, K]: the V channels' K taps are V * K consecutive elements
+  float w[K][V], bias[V];
+  {
+    RawSlice<IO, V * K> rw;
+    rw.load(static_cast<const IO*>(p.weight) + static_cast<size_t>(c0) * K);
+    float wf[V * K];
+    rw.widen_to(wf);
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+#pragma unroll
+      for (int j = 0; j < K; ++j) w[j][e] = wf[e * K + j];
+  }
+  if (p.bias != nullptr) {
+    RawSlice<IO, V> rb;
+    rb.load(static_cast<const IO*>(p.bias) + c0);
+    rb.widen_to(bias);
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) bias[e] = 0.0f;
+  }
+
+  // window: win[m - 1][e] = xp(t - m), m = 1 .. K - 1
+  float win[K > 1 ? K - 1 : 1][V];
+  int n = find_seq(p.cu, p.num_seqs, t_first);
+  int t0 = seq_begin(p.cu, n, p.total_tokens), t_end = seq_end(p.cu, n, p.total_tokens);
+  auto fill_window = [&](int t) {
+#pragma unroll
+    for (int m = 1; m < K; ++m) {
+      const int pos = t - t0 - m;
+      if (pos >= 0) {
+        RawSlice<IO, V> r;
+        r.load(x + static_cast<size_t>(t - m) * C + c0);
+        r.widen_to(win[m - 1]);
+      } else if (s0 != nullptr && pos >= -p.carry) {
+        RawSlice<IO, V> r;
+        r.load(s0 + (static_cast<size_t>(n) * p.carry + p.carry + pos) * C + c0);
+        r.widen_to(win[m - 1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) win[m - 1][e] = 0.0f;
+      }
+    }
+  };
+  fill_window(t_first);
+
+  for (int tc = t_first; tc < t_stop; tc += kChunk) {
+    // the chunk's input rows, issued before any is used
+    RawSlice<IO, V> raw[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      if (tc + i < t_stop) raw[i].load(x + static_cast<size_t>(tc + i) * C + c0);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int t = tc + i;
+      if (t >= t_stop) break;
+      if (t >= t_end) {  // next (non-empty) sequence: refill the window from its state
+        while (n + 1 < p.num_seqs && seq_end(p.cu, n, p.total_tokens) <= t) ++n;
+        t0 = seq_begin(p.cu, n, p.total_tokens);
+        t_end = seq_end(p.cu, n, p.total_tokens);
+        fill_window(t);
+      }
+      float cur[V], out[V];
+      raw[i].widen_to(cur);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        float z = fmaf(w[K - 1][e], cur[e], bias[e]);
+#pragma unroll
+        for (int m = 1; m < K; ++m) z = fmaf(w[K - 1 - m][e], win[m - 1][e], z);
+        out[e] = SILU ? z * fast_sigmoid(z) : z;
+      }
+      store_slice<IO, V>(y + static_cast<size_t>(t) * C + c0, out);
+#pragma unroll
+      for (int m = K - 1; m >= 2; --m)
+#pragma unroll
+        for (int e = 0; e < V; ++e) win[m - 1][e] = win[m - 2][e];
+      if constexpr (K > 1) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) win[0][e] = cur[e];
+      }
+    }
+  }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(kThreads) void conv_generic_kernel(ConvParams p) {
+  const int C = p.channels, K = p.ksize;
+  const IO* __restrict__ x = static_cast<const IO*>(p.x);
+  const IO* __restrict__ s0 = static_cast<const IO*>(p.s0);
+  const IO* __restrict__ wt = static_cast<const IO*>(p.weight);
+  const IO* __restrict__ bs = static_cast<const IO*>(p.bias);
+  IO* __restrict__ y = static_cast<IO*>(p.y);
+  const int64_t total = static_cast<int64_t>(p.total_tokens) * C;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int t = static_cast<int>(e / C);
+    const int c = static_cast<int>(e % C);
+    const int n = find_seq(p.cu, p.num_seqs, t);
+    const int t0 = seq_begin(p.cu, n, p.total_tokens);
+    float z = bs != nullptr ? widen(bs[c]) : 0.0f;
+    for (int j = 0; j < K; ++j)
+      z = fmaf(widen(wt[static_cast<size_t>(c) * K + j]), xp_at(x, s0, C, p.carry, n, t0, t - t0 - p.carry + j * p.dilation, c), z);
+    narrow_store(y + e, silu_if<IO>(z, p.silu));
+  }
+}
+
+// New state of sequence n: sN[n, i] = xp(L - carry + i).  In ascending i the
+// source position L + i (state) or an input row never precedes an already
+// written destination, so sN may be s0.
+template <typename IO>
+__global__ __launch_bounds__(kThreads) void conv_state_kernel(ConvParams p) {
+  const int C = p.channels;
+  const IO* __restrict__ x = static_cast<const IO*>(p.x);
+  const IO* s0 = static_cast<const IO*>(p.s0);
+  IO* sN = static_cast<IO*>(p.sN);
+  const int64_t total = static_cast<int64_t>(p.num_seqs) * C;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int n = static_cast<int>(e / C);
+    const int c = static_cast<int>(e % C);
+    const int t0 = seq_begin(p.cu, n, p.total_tokens);
+    const int L = seq_end(p.cu, n, p.total_tokens) - t0;
+    if (L == 0 && s0 == sN) continue;  // the state is unchanged
+    for (int i = 0; i < p.carry; ++i) {
+      const float v = xp_at(x, s0, C, p.carry, n, t0, L - p.carry + i, c);
+      narrow_store(sN + (static_cast<size_t>(n) * p.carry + i) * C + c, v);
+    }
+  }
+}
+
+// One token per sequence: y from the state and x, then the state shifts by
+// one position in place (ascending order reads s[i + 1] before writing it).
+template <typename IO>
+__global__ __launch_bounds__(kThreads) void conv_step_kernel(ConvParams p) {
+  const int C = p.channels, K = p.ksize;
+  const IO* __restrict__ x = static_cast<const IO*>(p.x);
+  const IO* __restrict__ wt = static_cast<const IO*>(p.weight);
+  const IO* __restrict__ bs = static_cast<const IO*>(p.bias);
+  IO* __restrict__ y = static_cast<IO*>(p.y);
+  IO* st = static_cast<IO*>(p.sN);
+  const int64_t total = static_cast<int64_t>(p.num_seqs) * C;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int b = static_cast<int>(e / C);
+    const int c = static_cast<int>(e % C);
+    IO* sb = st + static_cast<size_t>(b) * p.carry * C + c;
+    const IO xv = x[e];
+    float z = bs != nullptr ? widen(bs[c]) : 0.0f;
+    for (int j = 0; j < K; ++j) {
+      const int pos = j * p.dilation - p.carry;  // <= 0
+      const float xin = pos == 0 ? widen(xv) : widen(sb[static_cast<size_t>(p.carry + pos) * C]);
+      z = fmaf(widen(wt[static_cast<size_t>(c) * K + j]), xin, z);
+    }
+    narrow_store(y + e, silu_if<IO>(z, p.silu));
+    for (int i = 0; i + 1 < p.carry; ++i) sb[static_cast<size_t>(i) * C] = sb[static_cast<size_t>(i + 1) * C];
+    if (p.carry > 0) sb[static_cast<size_t>(p.carry - 1) * C] = xv;
+  }
+}
+
+unsigned grid_for(int64_t elems) {
+  const int64_t want = (elems + kThreads - 1) / kThreads;
+  return static_cast<unsigned>(want < 8192 ? (want > 0 ? want : 1) : 8192);
+}
+
+template <typename IO, bool SILU>
+void launch_window(const ConvParams& p, int cb, int per_xcd, dim3 grid, hipStream_t stream) {
+  switch (p.ksize) {
+    case 1: hipLaunchKernelGGL((conv_window_kernel<IO, 1, SILU>), grid, dim3(kThreads), 0, stream, p, cb, per_xcd); break;
+    case 2: hipLaunchKernelGGL((conv_window_kernel<IO, 2, SILU>), grid, dim3(kThreads), 0, stream, p, cb, per_xcd); break;
+    case 3: hipLaunchKernelGGL((conv_window_kernel<IO, 3, SILU>), grid, dim3(kThreads), 0, stream, p, cb, per_xcd); break;
+    default: hipLaunchKernelGGL((conv_window_kernel<IO, 4, SILU>), grid, dim3(kThreads), 0, stream, p, cb, per_xcd); break;
+  }
+}
+
+template <typename IO>
+hipError_t launch_conv_io(const ConvParams& p, hipStream_t stream) {
+  constexpr int V = 16 / static_cast<int>(sizeof(IO));
+  if (p.total_tokens > 0 && p.y != nullptr) {
+    const bool window = p.dilation == 1 && p.ksize <= 4 && p.channels % V == 0;
+    if (window) {
+      const int cb = (p.channels / V + kThreads - 1) / kThreads;
+      const int segs = (p.total_tokens + kSeg - 1) / kSeg;
+      const int per_xcd = (segs + kXcds - 1) / kXcds;
+      const dim3 grid(static_cast<unsigned>(kXcds * per_xcd * cb));
+      if (p.silu) launch_window<IO, true>(p, cb, per_xcd, grid, stream);
+      else launch_window<IO, false>(p, cb, per_xcd, grid, stream);
+    } else {
+      hipLaunchKernelGGL((conv_generic_kernel<IO>), dim3(grid_for(static_cast<int64_t>(p.total_tokens) * p.channels)),
+                         dim3(kThreads), 0, stream, p);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.sN != nullptr && p.carry > 0 && p.num_seqs > 0) {
+    hipLaunchKernelGGL((conv_state_kernel<IO>), dim3(grid_for(static_cast<int64_t>(p.num_seqs) * p.channels)),
+                       dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <typename IO>
+hipError_t launch_step_io(const ConvParams& p, hipStream_t stream) {
+  if (p.num_seqs == 0) return hipSuccess;
+  hipLaunchKernelGGL((conv_step_kernel<IO>), dim3(grid_for(static_cast<int64_t>(p.num_seqs) * p.channels)),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_causal_conv(ConvParams p, int io_dtype, hipStream_t stream) {
+  if (io_dtype == 1) return launch_conv_io<bf16_t>(p, stream);
+  if (io_dtype == 2) return launch_conv_io<f16_t>(p, stream);
+  return launch_conv_io<float>(p, stream);
+}
+
+hipError_t launch_causal_conv_step(ConvParams p, int io_dtype, hipStream_t stream) {
+  if (io_dtype == 1) return launch_step_io<bf16_t>(p, stream);
+  if (io_dtype == 2) return launch_step_io<f16_t>(p, stream);
+  return launch_step_io<float>(p, stream);
+}
+
+}  // namespace gdn

@@ -385,6 +385,167 @@ GDN_EXPORT gdn_status gdn_gate_prologue(int32_t tokens, int32_t h_v, int32_t io_
   return ok();
 }
 
+namespace {
+
+constexpr int32_t kMaxConvCarry = 4096;
+
+gdn_status check_conv(const gdn_conv_problem* c, const char* fn) {
+  if (!c) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: problem is NULL", fn);
+  if (c->channels <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: channels=%d must be positive", fn, c->channels);
+  if (c->kernel_size <= 0 || c->dilation <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: kernel_size=%d and dilation=%d must be positive", fn,
+                c->kernel_size, c->dilation);
+  if (c->kernel_size > GDN_MAX_CONV_KERNEL)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: kernel_size=%d is above %d", fn, c->kernel_size, GDN_MAX_CONV_KERNEL);
+  if (static_cast<int64_t>(c->kernel_size - 1) * c->dilation > kMaxConvCarry)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: (kernel_size - 1) * dilation is above %d", fn, kMaxConvCarry);
+  if (!io_known(c->io_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: io_dtype %d is not supported (GDN_F32, GDN_BF16, GDN_F16)", fn,
+                c->io_dtype);
+  if (c->activation != GDN_ACT_NONE && c->activation != GDN_ACT_SILU)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: activation %d is not GDN_ACT_NONE or GDN_ACT_SILU", fn,
+                c->activation);
+  if (!aligned16(c->weight) || !aligned16(c->bias))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: weight and bias must be 16-byte aligned", fn);
+  return GDN_OK;
+}
+
+gdn::ConvParams conv_params(const gdn_conv_problem& c) {
+  gdn::ConvParams cp{};
+  cp.weight = c.weight;
+  cp.bias = c.bias;
+  cp.channels = c.channels;
+  cp.ksize = c.kernel_size;
+  cp.dilation = c.dilation;
+  cp.carry = (c.kernel_size - 1) * c.dilation;
+  cp.silu = c.activation == GDN_ACT_SILU;
+  return cp;
+}
+
+}  // namespace
+
+GDN_EXPORT gdn_status gdn_causal_conv(const gdn_conv_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
+                                      const int32_t* cu_seqlens_host, int32_t total_tokens, const void* x,
+                                      const void* initial_state, void* y, void* final_state, hipStream_t stream) {
+  const char* fn = "gdn_causal_conv";
+  gdn_status st = check_conv(problem, fn);
+  if (st != GDN_OK) return st;
+  const gdn_conv_problem& c = *problem;
+  if (num_seqs < 0 || total_tokens < 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: num_seqs=%d and total_tokens=%d must be >= 0", fn, num_seqs,
+                total_tokens);
+  if (num_seqs == 0 && total_tokens != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: %d tokens but no sequences", fn, total_tokens);
+  if (num_seqs > 0 && !cu_seqlens) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL", fn);
+  if (total_tokens > 0 && (!x || !y || !c.weight))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, y and weight are required when total_tokens > 0", fn);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(initial_state) || !aligned16(final_state))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, y and the states must be 16-byte aligned", fn);
+  if (!aligned_to(cu_seqlens, 4)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is misaligned", fn);
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens[0]=%d, expected 0", fn, cu_seqlens_host[0]);
+    for (int32_t n = 0; n < num_seqs; ++n)
+      if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+        return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens decreases at %d (%d -> %d)", fn, n,
+                    cu_seqlens_host[n], cu_seqlens_host[n + 1]);
+    if (cu_seqlens_host[num_seqs] != total_tokens)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens[%d]=%d but total_tokens=%d", fn, num_seqs,
+                  cu_seqlens_host[num_seqs], total_tokens);
+  }
+  const size_t es = io_size(c.io_dtype);
+  const int32_t carry = (c.kernel_size - 1) * c.dilation;
+  const size_t xy_bytes = static_cast<size_t>(total_tokens) * c.channels * es;
+  const size_t st_bytes = static_cast<size_t>(num_seqs) * carry * c.channels * es;
+  if (overlaps(y, xy_bytes, x, xy_bytes)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: y overlaps x", fn);
+  if (overlaps(y, xy_bytes, initial_state, st_bytes) || overlaps(y, xy_bytes, final_state, st_bytes) ||
+      overlaps(x, xy_bytes, final_state, st_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a state overlaps x or y", fn);
+  if (final_state && initial_state && final_state != initial_state &&
+      overlaps(final_state, st_bytes, initial_state, st_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: final_state partially overlaps initial_state", fn);
+  gdn::ConvParams cp = conv_params(c);
+  cp.x = x;
+  cp.s0 = carry > 0 ? initial_state : nullptr;
+  cp.y = y;
+  cp.sN = carry > 0 ? final_state : nullptr;
+  cp.cu = cu_seqlens;
+  cp.num_seqs = num_seqs;
+  cp.total_tokens = total_tokens;
+  const hipError_t e = gdn::launch_causal_conv(cp, c.io_dtype, stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+GDN_EXPORT gdn_status gdn_causal_conv_step(const gdn_conv_problem* problem, int32_t batch, const void* x, void* state,
+                                           void* y, hipStream_t stream) {
+  const char* fn = "gdn_causal_conv_step";
+  gdn_status st = check_conv(problem, fn);
+  if (st != GDN_OK) return st;
+  const gdn_conv_problem& c = *problem;
+  if (batch < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: batch=%d is negative", fn, batch);
+  if (batch == 0) return ok();
+  const int32_t carry = (c.kernel_size - 1) * c.dilation;
+  if (!x || !y || !c.weight || (carry > 0 && !state))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, y, weight and the state are required", fn);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(state))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, y and the state must be 16-byte aligned", fn);
+  const size_t es = io_size(c.io_dtype);
+  const size_t xy_bytes = static_cast<size_t>(batch) * c.channels * es;
+  const size_t st_bytes = static_cast<size_t>(batch) * carry * c.channels * es;
+  if (overlaps(y, xy_bytes, x, xy_bytes) || overlaps(y, xy_bytes, state, st_bytes) ||
+      overlaps(x, xy_bytes, state, st_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, y and the state must not overlap", fn);
+  gdn::ConvParams cp = conv_params(c);
+  cp.x = x;
+  cp.s0 = state;
+  cp.sN = state;
+  cp.y = y;
+  cp.num_seqs = batch;
+  cp.total_tokens = batch;
+  const hipError_t e = gdn::launch_causal_conv_step(cp, c.io_dtype, stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+GDN_EXPORT gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, int32_t io_dtype, const void* x,
+                                        const void* gate, const void* scale, float eps, int32_t activation, void* y,
+                                        hipStream_t stream) {
+  const char* fn = "gdn_gated_rmsnorm";
+  if (rows < 0 || width <= 0 || group <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: rows=%lld must be >= 0, width=%d and group=%d positive", fn,
+                static_cast<long long>(rows), width, group);
+  if (width % group != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: width=%d is not a multiple of group=%d", fn, width, group);
+  if (!io_known(io_dtype)) return fail(GDN_ERR_UNSUPPORTED, "%s: io_dtype %d is not supported", fn, io_dtype);
+  if (activation != GDN_ACT_SILU && activation != GDN_ACT_SIGMOID)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: activation %d is not GDN_ACT_SILU or GDN_ACT_SIGMOID", fn,
+                activation);
+  if (!(eps >= 0.0f) || !std::isfinite(eps))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+  if (!gdn::gated_rmsnorm_supported(io_dtype, group))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: group=%d is larger than the kernel serves", fn, group);
+  if (rows == 0) return ok();
+  if (!x || !gate || !scale || !y) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, gate, scale and y are required", fn);
+  if (!aligned16(x) || !aligned16(gate) || !aligned16(scale) || !aligned16(y))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, gate, scale and y must be 16-byte aligned", fn);
+  const size_t bytes = static_cast<size_t>(rows) * width * io_size(io_dtype);
+  if ((y != x && overlaps(y, bytes, x, bytes)) || overlaps(y, bytes, gate, bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: y overlaps gate, or x other than exactly", fn);
+  gdn::NormParams np{};
+  np.x = x;
+  np.gate = gate;
+  np.scale = scale;
+  np.y = y;
+  np.groups = rows * (width / group);
+  np.group = group;
+  np.eps = eps;
+  np.activation = activation;
+  const hipError_t e = gdn::launch_gated_rmsnorm(np, io_dtype, stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 GDN_EXPORT const char* gdn_last_error(void) { return g_last_error; }
 
 GDN_EXPORT const char* gdn_status_string(gdn_status status) {

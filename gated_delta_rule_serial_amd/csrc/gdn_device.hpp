@@ -35,6 +35,41 @@ __device__ __forceinline__ void narrow_store(f16_t* p, float x) { *p = static_ca
 template <typename IO>
 __device__ __forceinline__ float load1(const IO* p) { return widen(*p); }
 
+// Two floats narrowed (round to nearest even) into one 32-bit word, the first
+// in the low half.
+template <typename IO>
+__device__ __forceinline__ uint32_t narrow_pair(float a, float b) {
+  if constexpr (__is_same(IO, f16_t)) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<f16_t>(a))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<f16_t>(b))) << 16);
+  } else {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+  }
+}
+
+// Narrow N floats and store them with 16-byte stores; p is 16-byte aligned
+// and N * sizeof(IO) a multiple of 16.
+template <typename IO, int N>
+__device__ __forceinline__ void store_slice(IO* p, const float* v) {
+  static_assert((N * static_cast<int>(sizeof(IO))) % 16 == 0, "whole 16-byte stores only");
+  if constexpr (sizeof(IO) == 4) {
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c)
+      reinterpret_cast<float4*>(p)[c] = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < N / 8; ++c) {
+      uint4 w;
+      w.x = narrow_pair<IO>(v[8 * c + 0], v[8 * c + 1]);
+      w.y = narrow_pair<IO>(v[8 * c + 2], v[8 * c + 3]);
+      w.z = narrow_pair<IO>(v[8 * c + 4], v[8 * c + 5]);
+      w.w = narrow_pair<IO>(v[8 * c + 6], v[8 * c + 7]);
+      reinterpret_cast<uint4*>(p)[c] = w;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- row slices
 // Load N consecutive I/O elements starting at p (aligned to N elements) and
 // widen them to float.  N is a power of two, 1 .. 16.
@@ -197,9 +232,9 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of G consecutive lanes (G = 1, 2, 4, 8, 16, 32);
-// every lane of a group receives the group's sum.  Every lane of the wave
-// must be active.
+// Sum over aligned groups of G consecutive lanes (G = 1, 2, 4, 8, 16, 32,
+// 64); every lane of a group receives the group's sum.  Every lane of the
+// wave must be active.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
   if constexpr (G >= 2) x += dpp<kQuadSwap1>(x);
@@ -211,7 +246,8 @@ __device__ __forceinline__ float group_sum(float x) {
     // and_mask 0x1f, or_mask 0, xor_mask 0x10).
     x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
   }
-  static_assert(G <= 32, "group_sum supports groups of at most 32 lanes");
+  if constexpr (G >= 64) x += __shfl_xor(x, 32);
+  static_assert(G <= 64, "group_sum supports groups of at most 64 lanes");
   return x;
 }
 
@@ -221,6 +257,15 @@ __device__ __forceinline__ float gate_sigmoid(float x) {
   if (x >= 0.0f) return 1.0f / (1.0f + expf(-x));
   const float e = expf(x);
   return e / (1.0f + e);
+}
+
+// Logistic function from the hardware exp2 and reciprocal (v_exp_f32,
+// v_rcp_f32; about one ulp each): 1 / (1 + 2^(-x log2(e))).  Saturates
+// cleanly: 2^(+large) = inf gives 0, 2^(-large) = 0 gives 1.  For the
+// elementwise epilogues, where the precise division would cost as much time
+// as the memory traffic.
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
 // softplus(x) = max(x, 0) + log1p(exp(-|x|)), overflow-free.

@@ -75,12 +75,49 @@ struct GatePrologueParams {
   int32_t h_v;
 };
 
+// Causal depthwise conv1d with a carried state, over packed sequences (or
+// one token per sequence for the step form).
+struct ConvParams {
+  const void* x;          // [T, C]
+  const void* weight;     // [C, K]
+  const void* bias;       // [C] or null
+  const void* s0;         // [N, carry, C] or null (zeros)
+  void* y;                // [T, C]
+  void* sN;               // [N, carry, C] or null; may equal s0
+  const int32_t* cu;      // [N + 1]; null for the step form (sequence n = token n)
+  int32_t num_seqs;
+  int32_t total_tokens;
+  int32_t channels;
+  int32_t ksize;
+  int32_t dilation;
+  int32_t carry;          // (ksize - 1) * dilation
+  int32_t silu;
+};
+
+// Gated RMSNorm over groups of `group` elements.
+struct NormParams {
+  const void* x;          // [rows, width]
+  const void* gate;       // [rows, width]
+  const void* scale;      // [group]
+  void* y;                // [rows, width]
+  int64_t groups;         // rows * width / group
+  int32_t group;
+  float eps;
+  int32_t activation;     // 1 silu, 2 sigmoid
+};
+
 // io_dtype: the gdn_dtype of the I/O tensors (0 float32, 1 bfloat16,
 // 2 float16).  Each launcher enqueues on `stream` and returns the launch
 // status.
 hipError_t launch_prefill_scan(ScanParams p, int io_dtype, hipStream_t stream);
 hipError_t launch_decode_step(DecodeParams p, int io_dtype, hipStream_t stream);
 hipError_t launch_gate_prologue(GatePrologueParams p, int io_dtype, hipStream_t stream);
+hipError_t launch_causal_conv(ConvParams p, int io_dtype, hipStream_t stream);
+hipError_t launch_causal_conv_step(ConvParams p, int io_dtype, hipStream_t stream);
+// Whether the norm kernel serves this group size (at most 512 vectors of
+// 16 bytes, or 512 elements when the group is not a multiple of 16 bytes).
+bool gated_rmsnorm_supported(int io_dtype, int group);
+hipError_t launch_gated_rmsnorm(NormParams p, int io_dtype, hipStream_t stream);
 
 // Chunked (matrix-core) prefill: whether a geometry is built, the state
 // columns one workgroup owns, and the launcher.

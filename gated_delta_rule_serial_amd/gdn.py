@@ -25,6 +25,8 @@ GDN_GATES_PRECOMPUTED, GDN_GATES_RAW = 0, 1
 GDN_ALGO_AUTO, GDN_ALGO_SERIAL, GDN_ALGO_CHUNKED = 0, 1, 2
 ALGORITHMS = {"auto": GDN_ALGO_AUTO, "serial": GDN_ALGO_SERIAL, "chunked": GDN_ALGO_CHUNKED}
 RULES = {"gated_delta": 0, "delta": 1, "gated": 2, "linear": 3}
+GDN_ACT_NONE, GDN_ACT_SILU, GDN_ACT_SIGMOID = 0, 1, 2
+ACTIVATIONS = {"none": GDN_ACT_NONE, "silu": GDN_ACT_SILU, "swish": GDN_ACT_SILU, "sigmoid": GDN_ACT_SIGMOID}
 
 _DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
 
@@ -44,6 +46,15 @@ class gdn_problem(ctypes.Structure):
         ("beta_shared", ctypes.c_int32),
         ("state_window", ctypes.c_int32),
         ("state_history", ctypes.c_void_p),
+    ]
+
+
+class gdn_conv_problem(ctypes.Structure):
+    _fields_ = [
+        ("channels", ctypes.c_int32), ("kernel_size", ctypes.c_int32),
+        ("dilation", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
+        ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
     ]
 
 
@@ -77,6 +88,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_decode_step_slots.restype = ctypes.c_int
     lib.gdn_gate_prologue.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_gate_prologue.restype = ctypes.c_int
+    cp = ctypes.POINTER(gdn_conv_problem)
+    lib.gdn_causal_conv.argtypes = [cp, i32, vp, ip, i32, vp, vp, vp, vp, vp]
+    lib.gdn_causal_conv.restype = ctypes.c_int
+    lib.gdn_causal_conv_step.argtypes = [cp, i32, vp, vp, vp, vp]
+    lib.gdn_causal_conv_step.restype = ctypes.c_int
+    lib.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, i32, vp, vp, vp, ctypes.c_float, i32, vp, vp]
+    lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -228,6 +246,48 @@ def gdn_gate_prologue(a: torch.Tensor, b: Optional[torch.Tensor], A_log: torch.T
                                     _ptr(dt_bias), _ptr(g), _ptr(beta), _stream(stream, a.device)))
 
 
+def make_conv_problem(weight: torch.Tensor, bias: Optional[torch.Tensor] = None, *, dilation: int = 1,
+                      activation: str = "silu") -> gdn_conv_problem:
+    """Fill the ``gdn_conv_problem`` struct from weight [C, K] (and bias [C])."""
+    if weight.dtype not in _DTYPES:
+        raise ValueError(f"io dtype {weight.dtype} is not supported")
+    C, K = weight.shape
+    return gdn_conv_problem(C, K, int(dilation), _DTYPES[weight.dtype], ACTIVATIONS[activation],
+                            _ptr(weight), _ptr(bias))
+
+
+def gdn_causal_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor, *, y: torch.Tensor,
+                    bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                    final_state: Optional[torch.Tensor] = None, dilation: int = 1, activation: str = "silu",
+                    cu_seqlens_host: Optional[Sequence[int]] = None, stream=None) -> None:
+    """gdn_causal_conv of include/gdn.h: x, y [T, C]; weight [C, K]; states
+    [N, (K - 1) dilation, C], all in the I/O dtype; cu_seqlens int32 [N+1]."""
+    prob = make_conv_problem(weight, bias, dilation=dilation, activation=activation)
+    n = cu_seqlens.numel() - 1
+    _check(load().gdn_causal_conv(ctypes.byref(prob), n, _ptr(cu_seqlens), _host_i32(cu_seqlens_host), x.shape[0],
+                                  _ptr(x), _ptr(initial_state), _ptr(y), _ptr(final_state),
+                                  _stream(stream, x.device)))
+
+
+def gdn_causal_conv_step(x: torch.Tensor, weight: torch.Tensor, state: torch.Tensor, *, y: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None, dilation: int = 1, activation: str = "silu",
+                         stream=None) -> None:
+    """gdn_causal_conv_step of include/gdn.h: x, y [B, C]; state [B, carry, C], shifted in place."""
+    prob = make_conv_problem(weight, bias, dilation=dilation, activation=activation)
+    _check(load().gdn_causal_conv_step(ctypes.byref(prob), x.shape[0], _ptr(x), _ptr(state), _ptr(y),
+                                       _stream(stream, x.device)))
+
+
+def gdn_gated_rmsnorm(x: torch.Tensor, gate: torch.Tensor, scale: torch.Tensor, *, y: torch.Tensor,
+                      eps: float = 1e-5, activation: str = "silu", stream=None) -> None:
+    """gdn_gated_rmsnorm of include/gdn.h over groups of len(scale) elements of
+    x's last axis; x, gate, y share a shape, all in the I/O dtype."""
+    width = x.shape[-1]
+    rows = x.numel() // width if width else 0
+    _check(load().gdn_gated_rmsnorm(rows, width, scale.numel(), _DTYPES[x.dtype], _ptr(x), _ptr(gate), _ptr(scale),
+                                    float(eps), ACTIVATIONS[activation], _ptr(y), _stream(stream, x.device)))
+
+
 # ----------------------------------------------------------------- helpers
 def prefill(q, k, v, cu_seqlens, *, initial_state=None, want_state=True, scale=0.0,
             cu_seqlens_host=None, algorithm="auto", stream=None, **kw):
@@ -247,6 +307,25 @@ def decode_step(q, k, v, state, *, scale=0.0, stream=None, **kw):
     out = torch.empty(q.shape[0], v.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
     gdn_decode_step(q, k, v, state, out, scale=scale, stream=stream, **kw)
     return out
+
+
+def causal_conv(x, weight, cu_seqlens, *, bias=None, initial_state=None, want_state=True, dilation=1,
+                activation="silu", cu_seqlens_host=None, stream=None):
+    """Allocate y (and the final state) with torch and call gdn_causal_conv."""
+    C, K = weight.shape
+    n = cu_seqlens.numel() - 1
+    y = torch.empty_like(x)
+    fin = torch.empty(n, (K - 1) * dilation, C, dtype=x.dtype, device=x.device) if want_state else None
+    gdn_causal_conv(x, weight, cu_seqlens, y=y, bias=bias, initial_state=initial_state, final_state=fin,
+                    dilation=dilation, activation=activation, cu_seqlens_host=cu_seqlens_host, stream=stream)
+    return y, fin
+
+
+def gated_rmsnorm(x, gate, scale, *, eps=1e-5, activation="silu", stream=None):
+    """Allocate y with torch and call gdn_gated_rmsnorm."""
+    y = torch.empty_like(x)
+    gdn_gated_rmsnorm(x, gate, scale, y=y, eps=eps, activation=activation, stream=stream)
+    return y
 
 
 def gate_prologue(a, b, A_log, dt_bias, *, stream=None):

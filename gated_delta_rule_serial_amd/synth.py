@@ -144,3 +144,110 @@ def variant_gates(T: int, h_v: int, d_k: int, *, seed: int, io_dtype: torch.dtyp
     dt_bias = torch.rand(h_v, d_k, generator=gen, dtype=f32) * 2.0 - 1.0
     b = torch.randn(T, generator=gen, dtype=f32)
     return VariantGates(a.to(io_dtype), A_log, dt_bias, b.to(io_dtype))
+
+
+# ---------------------------------------------------------------- the block's neighbouring ops
+@dataclasses.dataclass(frozen=True)
+class ConvShape:
+    """Causal depthwise conv in front of the recurrence: channels = the q, k
+    and v projections side by side (2 h_qk d_k + h_v d_v)."""
+    name: str
+    io_dtype: torch.dtype
+    channels: int
+    kernel_size: int
+    dilation: int
+    num_seqs: int
+    seqlen: Optional[int]                 # tokens per sequence, or None for drawn lengths
+    len_range: Optional[tuple] = None
+    init_state: bool = True
+    bias: bool = True
+    seed_index: int = 10
+
+
+@dataclasses.dataclass(frozen=True)
+class NormShape:
+    """Gated RMSNorm after the recurrence: rows = tokens, width = h_v d_v,
+    one group per value head."""
+    name: str
+    io_dtype: torch.dtype
+    rows: int
+    width: int
+    group: int
+    seed_index: int = 20
+
+
+# The decode and packed-prefill geometry of the recurrence (h_qk 16, h_v 32,
+# d 128), with the block's usual width-4 convolution.
+CONV_WORKLOADS: List[ConvShape] = [
+    ConvShape("conv_step_b64", torch.bfloat16, 8192, 4, 1, num_seqs=64, seqlen=1, seed_index=10),
+    # seed index 3: the lengths are the packed recurrence workload's (drawn first)
+    ConvShape("conv_varlen_8seq", torch.bfloat16, 8192, 4, 1, num_seqs=8, seqlen=None, len_range=(512, 8192),
+              seed_index=3),
+]
+NORM_WORKLOADS: List[NormShape] = [
+    NormShape("gated_rmsnorm_t33173", torch.bfloat16, 33173, 32 * 128, 128, seed_index=20),
+]
+CONV_BY_NAME = {w.name: w for w in CONV_WORKLOADS}
+NORM_BY_NAME = {w.name: w for w in NORM_WORKLOADS}
+
+
+@dataclasses.dataclass
+class ConvInputs:
+    shape: ConvShape
+    seqlens: List[int]
+    cu_seqlens: torch.Tensor               # int32 [N+1]
+    x: torch.Tensor                        # [T, C] io dtype
+    weight: torch.Tensor                   # [C, K] io dtype
+    bias: Optional[torch.Tensor]           # [C] io dtype
+    initial_state: Optional[torch.Tensor]  # [N, carry, C] io dtype
+
+
+def generate_conv(shape: ConvShape, *, seqlens: Optional[List[int]] = None, seed: Optional[int] = None) -> ConvInputs:
+    """Draw the conv inputs on the CPU (seed 1234 + index), in float32, in this
+    order: lengths (drawn workloads), x ~ N(0, 1) [T, C], weight ~ U(-1, 1) / sqrt(K)
+    [C, K], bias ~ N(0, 0.1^2) [C], initial state ~ N(0, 1) [N, carry, C]; then
+    every tensor is cast to the I/O dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(1234 + shape.seed_index if seed is None else seed)
+    if seqlens is not None:
+        lens = [int(v) for v in seqlens]
+    elif shape.seqlen is None:
+        lo, hi = shape.len_range
+        lens = torch.randint(lo, hi + 1, (shape.num_seqs,), generator=gen).tolist()
+    else:
+        lens = [shape.seqlen] * shape.num_seqs
+    n, T, C, K = len(lens), sum(lens), shape.channels, shape.kernel_size
+    cu = torch.zeros(n + 1, dtype=torch.int32)
+    if n:
+        cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    f32 = torch.float32
+    x = torch.randn(T, C, generator=gen, dtype=f32)
+    w = (torch.rand(C, K, generator=gen, dtype=f32) * 2.0 - 1.0) / K ** 0.5
+    b = torch.randn(C, generator=gen, dtype=f32) * 0.1
+    carry = (K - 1) * shape.dilation
+    s0 = torch.randn(n, carry, C, generator=gen, dtype=f32) if shape.init_state else None
+    dt = shape.io_dtype
+    return ConvInputs(shape, lens, cu, x.to(dt), w.to(dt), b.to(dt) if shape.bias else None,
+                      None if s0 is None else s0.to(dt))
+
+
+@dataclasses.dataclass
+class NormInputs:
+    shape: NormShape
+    x: torch.Tensor       # [rows, width] io dtype
+    gate: torch.Tensor    # [rows, width] io dtype
+    scale: torch.Tensor   # [group] io dtype
+
+
+def generate_norm(shape: NormShape, *, rows: Optional[int] = None, seed: Optional[int] = None) -> NormInputs:
+    """Draw the norm inputs on the CPU (seed 1234 + index), in float32: x ~ N(0, 1),
+    gate ~ N(0, 2^2) [rows, width], scale ~ N(1, 0.1^2) [group]; cast to the I/O dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(1234 + shape.seed_index if seed is None else seed)
+    r = shape.rows if rows is None else rows
+    f32 = torch.float32
+    x = torch.randn(r, shape.width, generator=gen, dtype=f32)
+    gate = torch.randn(r, shape.width, generator=gen, dtype=f32) * 2.0
+    scale = 1.0 + 0.1 * torch.randn(shape.group, generator=gen, dtype=f32)
+    dt = shape.io_dtype
+    return NormInputs(shape, x.to(dt), gate.to(dt), scale.to(dt))

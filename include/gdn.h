@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -226,6 +226,82 @@ gdn_status gdn_gate_prologue(int32_t tokens, int32_t h_v, int32_t io_dtype,
                              const void* a, const void* b, const float* A_log,
                              const float* dt_bias, void* g, void* beta,
                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The block's neighbouring operations: the causal depthwise convolution in
+ * front of the recurrence and the gated RMSNorm after it.
+ * ---------------------------------------------------------------------- */
+
+/* Activation applied by the convolution and the norm. */
+typedef enum gdn_activation {
+  GDN_ACT_NONE = 0,    /* convolution only                        */
+  GDN_ACT_SILU = 1,    /* x * sigmoid(x)                          */
+  GDN_ACT_SIGMOID = 2  /* gated RMSNorm only: sigmoid(gate)       */
+} gdn_activation;
+
+/* Largest convolution kernel (taps per channel). */
+#define GDN_MAX_CONV_KERNEL 64
+
+/* Causal depthwise conv1d with a carried state ([P1] `causal_conv_op`,
+ * CausalConvWithState, channels-last; [P3] `causal_conv1d_slots` fallback
+ * graph).  With carry = (kernel_size - 1) * dilation, sequence n's padded
+ * input is its state (the last `carry` inputs seen so far, oldest first)
+ * followed by its new inputs, and per channel c
+ *     z_t = bias[c] + sum_j weight[c, j] * xp(t - carry + j * dilation)
+ *     y_t = z_t, or z_t * sigmoid(z_t) with GDN_ACT_SILU
+ * (a cross-correlation: the last tap meets the current input).  The new
+ * state is the last `carry` positions of the padded input; a sequence with
+ * no tokens keeps its state.  Accumulation is float32; y is narrowed once. */
+typedef struct gdn_conv_problem {
+  int32_t channels;     /* C >= 1                                          */
+  int32_t kernel_size;  /* K, 1 .. GDN_MAX_CONV_KERNEL                      */
+  int32_t dilation;     /* >= 1, (K - 1) * dilation <= 4096                */
+  int32_t io_dtype;     /* gdn_dtype of x, y, weight, bias and the states  */
+  int32_t activation;   /* GDN_ACT_NONE or GDN_ACT_SILU                    */
+  const void* weight;   /* [C, K] io_dtype                                 */
+  const void* bias;     /* [C] io_dtype, or NULL                           */
+} gdn_conv_problem;
+
+/*
+ * gdn_causal_conv -- the convolution over packed variable-length sequences.
+ *   cu_seqlens, cu_seqlens_host, total_tokens  as in gdn_prefill
+ *   x, y            [total_tokens, C] io_dtype (y may not overlap x)
+ *   initial_state   [num_seqs, carry, C] io_dtype, or NULL for zeros
+ *   final_state     [num_seqs, carry, C] io_dtype, or NULL; it may be the
+ *                   same pointer as initial_state (updated in place) but
+ *                   must not overlap it otherwise.
+ */
+gdn_status gdn_causal_conv(const gdn_conv_problem* problem, int32_t num_seqs,
+                           const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                           int32_t total_tokens, const void* x, const void* initial_state,
+                           void* y, void* final_state, hipStream_t stream);
+
+/*
+ * gdn_causal_conv_step -- one token for each of `batch` sequences, the
+ * state resident in device memory and shifted in place:
+ *   x, y    [batch, C] io_dtype
+ *   state   [batch, carry, C] io_dtype, read and overwritten
+ * Same result as gdn_causal_conv with cu_seqlens = {0, 1, ..., batch} and
+ * final_state == initial_state == state.
+ */
+gdn_status gdn_causal_conv_step(const gdn_conv_problem* problem, int32_t batch, const void* x,
+                                void* state, void* y, hipStream_t stream);
+
+/*
+ * gdn_gated_rmsnorm -- gated RMSNorm ([P1] `gated_rms_norm_op`): each row of
+ * `width` elements is split into width / group groups of `group` consecutive
+ * elements, and per group, in float32,
+ *     y = x / sqrt(mean(x^2) + eps) * scale * act(gate)
+ * with act = silu (GDN_ACT_SILU) or sigmoid (GDN_ACT_SIGMOID).
+ *   x, gate, y  [rows, width] io_dtype (y may be x)
+ *   scale       [group] io_dtype
+ * width must be a multiple of group; groups of up to 512 16-byte vectors
+ * (4096 bf16/f16 or 2048 f32 elements; 512 elements when the group is not a
+ * multiple of 16 bytes) are served, larger ones give GDN_ERR_UNSUPPORTED.
+ */
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, int32_t io_dtype,
+                             const void* x, const void* gate, const void* scale, float eps,
+                             int32_t activation, void* y, hipStream_t stream);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char* gdn_last_error(void);

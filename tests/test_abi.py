@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 5
+    assert gdn.abi_version() == 6
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -183,3 +183,91 @@ def test_slot_validation(lib):
                                    vp(FAKE + 0x30000), vp(FAKE + 0x80000), -1, vp(FAKE + 0x3000), None,
                                    vp(FAKE + 0x40000), None)
     assert st == INVALID and "num_slots" in gdn.last_error()
+
+
+# ------------------------------------------------------------------ conv and norm
+def _conv_prob(**kw):
+    base = dict(channels=64, kernel_size=4, dilation=1, io_dtype=gdn.GDN_BF16, activation=gdn.GDN_ACT_SILU,
+                weight=FAKE + 0x6000, bias=None)
+    base.update(kw)
+    return gdn.gdn_conv_problem(**base)
+
+
+def _conv(lib, prob, *, n=2, cu=FAKE + 0x2000, cu_host=(0, 3, 8), T=8, x=FAKE + 0x10000, s0=None,
+          y=FAKE + 0x40000, sN=None):
+    vp = ctypes.c_void_p
+    host = None if cu_host is None else (ctypes.c_int32 * len(cu_host))(*cu_host)
+    return lib.gdn_causal_conv(ctypes.byref(prob) if prob is not None else None, n, vp(cu) if cu else None, host,
+                               T, vp(x) if x else None, vp(s0) if s0 else None, vp(y) if y else None,
+                               vp(sN) if sN else None, None)
+
+
+@pytest.mark.parametrize("label,prob_kw,call_kw,status,needle", [
+    ("null problem", None, {}, INVALID, "problem is NULL"),
+    ("channels", dict(channels=0), {}, INVALID, "channels"),
+    ("kernel size", dict(kernel_size=0), {}, INVALID, "kernel_size"),
+    ("dilation", dict(dilation=0), {}, INVALID, "dilation"),
+    ("kernel too large", dict(kernel_size=65), {}, UNSUPPORTED, "above 64"),
+    ("receptive field", dict(kernel_size=64, dilation=100), {}, UNSUPPORTED, "4096"),
+    ("dtype", dict(io_dtype=5), {}, UNSUPPORTED, "io_dtype"),
+    ("activation", dict(activation=gdn.GDN_ACT_SIGMOID), {}, INVALID, "activation"),
+    ("weight misaligned", dict(weight=FAKE + 0x6002), {}, INVALID, "16-byte"),
+    ("negative tokens", {}, dict(T=-1), INVALID, "must be >= 0"),
+    ("tokens without sequences", {}, dict(n=0, cu_host=None), INVALID, "no sequences"),
+    ("no cu", {}, dict(cu=None), INVALID, "cu_seqlens is NULL"),
+    ("no x", {}, dict(x=None), INVALID, "required"),
+    ("no weight", dict(weight=None), {}, INVALID, "required"),
+    ("x misaligned", {}, dict(x=FAKE + 0x10008), INVALID, "16-byte"),
+    ("cu start", {}, dict(cu_host=(1, 3, 8)), INVALID, "expected 0"),
+    ("cu decreasing", {}, dict(cu_host=(0, 5, 3)), INVALID, "decreases"),
+    ("cu total", {}, dict(cu_host=(0, 3, 7)), INVALID, "total_tokens"),
+    ("y overlaps x", {}, dict(y=FAKE + 0x10000 + 0x100), INVALID, "y overlaps x"),
+    ("state overlaps y", {}, dict(sN=FAKE + 0x40000 + 0x40), INVALID, "overlaps"),
+    ("states partly overlap", {}, dict(s0=FAKE + 0x80000, sN=FAKE + 0x80000 + 0x40), INVALID, "partially"),
+])
+def test_conv_validation(lib, label, prob_kw, call_kw, status, needle):
+    prob = None if prob_kw is None else _conv_prob(**prob_kw)
+    st = _conv(lib, prob, **call_kw)
+    assert st == status, (label, gdn.last_error())
+    assert needle in gdn.last_error(), (label, gdn.last_error())
+
+
+def test_conv_nothing_to_do_is_ok(lib):
+    vp = ctypes.c_void_p
+    assert _conv(lib, _conv_prob(), n=0, cu=None, cu_host=None, T=0, x=None, y=None) == gdn.GDN_OK
+    assert lib.gdn_causal_conv_step(ctypes.byref(_conv_prob()), 0, None, None, None, None) == gdn.GDN_OK
+    st = lib.gdn_causal_conv_step(ctypes.byref(_conv_prob()), 2, vp(FAKE), None, vp(FAKE + 0x1000), None)
+    assert st == INVALID and "required" in gdn.last_error()
+    st = lib.gdn_causal_conv_step(ctypes.byref(_conv_prob()), 2, vp(FAKE), vp(FAKE + 0x40), vp(FAKE + 0x1000), None)
+    assert st == INVALID and "overlap" in gdn.last_error()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(rows=-1), INVALID, "rows"),
+    (dict(width=0), INVALID, "width"),
+    (dict(width=100, group=64), INVALID, "multiple"),
+    (dict(dtype=9), UNSUPPORTED, "io_dtype"),
+    (dict(act=gdn.GDN_ACT_NONE), INVALID, "activation"),
+    (dict(eps=-1.0), INVALID, "eps"),
+    (dict(eps=float("inf")), INVALID, "eps"),
+    (dict(group=8192, width=8192), UNSUPPORTED, "larger"),
+    (dict(group=513, width=513), UNSUPPORTED, "larger"),
+    (dict(x=0), INVALID, "required"),
+    (dict(gate=FAKE + 0x20004), INVALID, "16-byte"),
+    (dict(y=FAKE + 0x20000), INVALID, "overlaps"),
+    (dict(y=FAKE + 0x10010), INVALID, "overlaps"),
+])
+def test_gated_rmsnorm_validation(lib, args, status, needle):
+    a = dict(rows=4, width=256, group=128, dtype=gdn.GDN_BF16, x=FAKE + 0x10000, gate=FAKE + 0x20000,
+             scale=FAKE + 0x30000, eps=1e-5, act=gdn.GDN_ACT_SILU, y=FAKE + 0x40000)
+    a.update(args)
+    vp = ctypes.c_void_p
+    st = lib.gdn_gated_rmsnorm(a["rows"], a["width"], a["group"], a["dtype"], vp(a["x"]) if a["x"] else None,
+                               vp(a["gate"]), vp(a["scale"]), a["eps"], a["act"], vp(a["y"]), None)
+    assert st == status, gdn.last_error()
+    assert needle in gdn.last_error()
+
+
+def test_gated_rmsnorm_no_rows_is_ok(lib):
+    assert lib.gdn_gated_rmsnorm(0, 128, 128, gdn.GDN_F32, None, None, None, 1e-5, gdn.GDN_ACT_SILU, None,
+                                 None) == gdn.GDN_OK
