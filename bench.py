@@ -206,7 +206,7 @@ def chunked_flops(shape, T, chunk=64):
     return T * shape.h_v * (3 * chunk * dk + 2 * chunk * dv + 6 * dk * dv)
 
 
-def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto"):
+def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=True):
     dev = "cuda"
     inp = synth.generate(shape)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -226,6 +226,11 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto"):
     fin = torch.empty(n, shape.h_v, shape.d_k, shape.d_v, dtype=torch.float32, device=dev)
     flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)  # 1 GiB
     stream = torch.cuda.current_stream()
+    # the chunked form's workspace (two passes), allocated before the timed region
+    ws_bytes = gdn.prefill_workspace_size(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, n, T,
+                                          algorithm=algorithm) if two_pass else 0
+    if ws_bytes:
+        gates["workspace"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def one():
         gdn.gdn_prefill(q, k, v, cu, out=out, final_state=fin, initial_state=s0, cu_seqlens_host=cu_host,
@@ -260,7 +265,9 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto"):
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
                 "traffic": _traffic(shape.name + "_chunked", ["prefill_chunked.hip", "gdn_device.hpp"]),
-                "kernel": "chunk_kernel (chunked, bf16 MFMA)", "algorithmic_bytes_per_launch": nbytes,
+                "kernel": ("chunk_prep_kernel + chunk_state_kernel (chunked in two passes, bf16 MFMA)" if ws_bytes
+                           else "chunk_kernel (chunked, bf16 MFMA)"),
+                "algorithmic_bytes_per_launch": nbytes, "workspace_bytes": ws_bytes,
                 "mfma_tflops": round(fl / (ms * 1e-3) / 1e12, 2), "mfma_frac_of_bf16_peak":
                     round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
     else:
@@ -281,7 +288,9 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto"):
         "wall_s": round(wall, 3),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "roofline": roof,
-        "config": {"workload": shape.name, "algorithm": "chunked" if chunked else "serial", "num_seqs": n,
+        "config": {"workload": shape.name,
+                   "algorithm": ("chunked, two passes" if ws_bytes else "chunked") if chunked else "serial",
+                   "num_seqs": n,
                    "total_tokens": T, "seqlens": inp.seqlens, "h_qk": shape.h_qk, "h_v": shape.h_v,
                    "d_k": shape.d_k, "d_v": shape.d_v,
                    "io_dtype": "bf16" if shape.io_dtype == torch.bfloat16 else "f32", "state_dtype": "f32",
@@ -431,6 +440,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algorithm", default="auto", choices=["auto", "serial", "chunked"],
                     help="prefill formulation (prefill workloads only)")
+    ap.add_argument("--one-pass", action="store_true",
+                    help="chunked prefill: no workspace, one pass per sequence")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="time a plain device copy of this many MiB instead (counter calibration)")
     args = ap.parse_args()
@@ -461,7 +472,7 @@ def main():
         if decode:
             line = bench_decode(shape, steps, warmup, want_cpu)
         else:
-            line = bench_prefill(shape, steps, warmup, want_cpu, args.algorithm)
+            line = bench_prefill(shape, steps, warmup, want_cpu, args.algorithm, not args.one_pass)
     head = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"), "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}

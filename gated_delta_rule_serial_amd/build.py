@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.cpp", "prefill_scan.hip", "prefill_chunked.hip", "decode_step.hip", "gate_prologue.hip",
-           "causal_conv.hip", "gated_rmsnorm.hip"]
+SOURCES = ["gdn_api.cpp", "prefill_scan.hip", "prefill_chunked.hip", "prefill_split.hip", "decode_step.hip",
+           "gate_prologue.hip", "causal_conv.hip", "gated_rmsnorm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -173,6 +173,8 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_window > 0 needs state_history", fn);
   if (!aligned16(problem->state_history))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_history must be 16-byte aligned", fn);
+  if (!aligned16(problem->workspace))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
   if (cu_seqlens_host) {
     if (cu_seqlens_host[0] != 0)
       return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens[0]=%d, expected 0", fn, cu_seqlens_host[0]);
@@ -222,6 +224,7 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   sp.slots = pool ? pool->slots : nullptr;
   sp.num_slots = pool ? pool->num_slots : 0;
   sp.num_seqs = num_seqs;
+  sp.total_tokens = total_tokens;
   sp.h_qk = p.h_qk;
   sp.h_v = p.h_v;
   sp.d_k = p.d_k;
@@ -241,14 +244,21 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   const bool chunked = p.algorithm == GDN_ALGO_CHUNKED ||
                        (p.algorithm == GDN_ALGO_AUTO && can_chunk &&
                         static_cast<int64_t>(total_tokens) >= 64 * static_cast<int64_t>(num_seqs));
-  const int cols = chunked ? gdn::chunked_columns_per_block(p.d_k, p.d_v) : gdn::scan_columns_per_wave(p.d_k);
+  // the two-pass chunked form when the caller's workspace holds it
+  const bool split = chunked && gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) &&
+                     p.workspace != nullptr &&
+                     p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  const int cols = split     ? gdn::split_columns_per_block(p.d_v)
+                   : chunked ? gdn::chunked_columns_per_block(p.d_k, p.d_v)
+                             : gdn::scan_columns_per_wave(p.d_k);
   sp.col_blocks = (p.d_v + cols - 1) / cols;
   const uint64_t blocks = static_cast<uint64_t>(num_seqs) * p.h_v * sp.col_blocks;
   if (blocks > 0x7fffffffull)
     return fail(GDN_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", fn,
                 static_cast<unsigned long long>(blocks));
-  const hipError_t e = chunked ? gdn::launch_prefill_chunked(sp, io_bf16, stream)
-                               : gdn::launch_prefill_scan(sp, p.io_dtype, stream);
+  const hipError_t e = split     ? gdn::launch_prefill_split(sp, p.workspace, stream)
+                       : chunked ? gdn::launch_prefill_chunked(sp, io_bf16, stream)
+                                 : gdn::launch_prefill_scan(sp, p.io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -336,6 +346,24 @@ gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch
 }
 
 }  // namespace
+
+GDN_EXPORT gdn_status gdn_prefill_workspace_size(const gdn_problem* problem, int32_t num_seqs, int32_t total_tokens,
+                                                 uint64_t* bytes) {
+  const char* fn = "gdn_prefill_workspace_size";
+  if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  *bytes = 0;
+  gdn_status st = check_problem(problem, fn, false);
+  if (st != GDN_OK) return st;
+  if (num_seqs < 0 || total_tokens < 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: num_seqs=%d and total_tokens=%d must be >= 0", fn, num_seqs,
+                total_tokens);
+  const gdn_problem& p = *problem;
+  if (p.algorithm == GDN_ALGO_SERIAL) return ok();
+  const gdn::GateArgs gates = gate_args(problem);
+  if (!gdn::split_supported(p.io_dtype == GDN_BF16, p.d_k, p.d_v, gates, p.state_window)) return ok();
+  *bytes = gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  return ok();
+}
 
 GDN_EXPORT gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch, const void* q, const void* k,
                                       const void* v, float* state, void* out, hipStream_t stream) {

@@ -38,6 +38,7 @@ struct ScanParams {
   const int32_t* slots;   // [N] or null (state n belongs to sequence n)
   int32_t num_slots;
   int32_t num_seqs;
+  int32_t total_tokens;
   int32_t h_qk, h_v, d_k, d_v;
   int32_t ratio;          // h_v / h_qk
   int32_t col_blocks;     // column blocks per (sequence, head)
@@ -124,6 +125,12 @@ hipError_t launch_gated_rmsnorm(NormParams p, int io_dtype, hipStream_t stream);
 bool chunked_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window);
 int chunked_columns_per_block(int d_k, int d_v);
 hipError_t launch_prefill_chunked(ScanParams p, int io_bf16, hipStream_t stream);
+// The chunked prefill in two passes (chunk-parallel preparation, then the
+// sequential state pass) through a caller-provided workspace.
+bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window);
+int split_columns_per_block(int d_v);
+size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v);
+hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t stream);
 
 // Index of sequence n's state and whether it exists (slot-pool indirection).
 __device__ __forceinline__ int state_slot(const int32_t* slots, int32_t num_slots, int n, bool* valid) {

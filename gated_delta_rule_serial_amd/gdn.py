@@ -46,6 +46,8 @@ class gdn_problem(ctypes.Structure):
         ("beta_shared", ctypes.c_int32),
         ("state_window", ctypes.c_int32),
         ("state_history", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_uint64),
     ]
 
 
@@ -95,6 +97,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_causal_conv_step.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, i32, vp, vp, vp, ctypes.c_float, i32, vp, vp]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_prefill_workspace_size.argtypes = [pp, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
+    lib.gdn_prefill_workspace_size.restype = ctypes.c_int
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -148,10 +152,12 @@ def _stream(stream, device) -> ctypes.c_void_p:
 def make_problem(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype, *, scale: float = 0.0,
                  g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None,
                  algorithm: str = "auto", rule: str = "gated_delta", decay_per_key: bool = False,
-                 beta_shared: bool = False, state_history: Optional[torch.Tensor] = None) -> gdn_problem:
+                 beta_shared: bool = False, state_history: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> gdn_problem:
     """Fill the ``gdn_problem`` struct.  Raw gates are used when ``a`` (or, for
     rules without decay, ``b``) is given.  ``state_history`` [N, W, h_v, d_k, d_v]
-    sets the state window W."""
+    sets the state window W; ``workspace`` (a device tensor of at least
+    prefill_workspace_size bytes) enables the two-pass chunked prefill."""
     if io_dtype not in _DTYPES:
         raise ValueError(f"io dtype {io_dtype} is not supported")
     raw = a is not None or (g is None and b is not None)
@@ -160,7 +166,8 @@ def make_problem(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype,
                        GDN_GATES_RAW if raw else GDN_GATES_PRECOMPUTED,
                        _ptr(g), _ptr(beta), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
                        ALGORITHMS[algorithm], RULES[rule], int(decay_per_key), int(beta_shared),
-                       window, _ptr(state_history))
+                       window, _ptr(state_history), _ptr(workspace),
+                       0 if workspace is None else workspace.numel() * workspace.element_size())
 
 
 def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
@@ -172,7 +179,7 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
     """gdn_prefill of include/gdn.h: q, k [T, h_qk, d_k]; v, out [T, h_v, d_v];
     cu_seqlens int32 [N+1] on the device; states float32 [N, h_v, d_k, d_v];
     algorithm "auto", "serial" or "chunked"; ``variant``: rule, decay_per_key,
-    beta_shared, state_history (see make_problem)."""
+    beta_shared, state_history, workspace (see make_problem)."""
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
@@ -200,6 +207,15 @@ def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: to
                                   _stream(stream, q.device)))
 
 
+def prefill_workspace_size(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype, num_seqs: int,
+                           total_tokens: int, *, algorithm: str = "auto", **variant) -> int:
+    """gdn_prefill_workspace_size of include/gdn.h (0 when the two-pass form does not apply)."""
+    prob = make_problem(h_qk, h_v, d_k, d_v, io_dtype, algorithm=algorithm, **variant)
+    out = ctypes.c_uint64(0)
+    _check(load().gdn_prefill_workspace_size(ctypes.byref(prob), num_seqs, total_tokens, ctypes.byref(out)))
+    return int(out.value)
+
+
 def _host_i32(vals):
     if vals is None:
         return None
@@ -211,13 +227,13 @@ def gdn_prefill_slots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seql
                       state_pool: torch.Tensor, slots: torch.Tensor, *, out: Optional[torch.Tensor], g=None,
                       beta=None, a=None, b=None, A_log=None, dt_bias=None, scale: float = 0.0,
                       cu_seqlens_host: Optional[Sequence[int]] = None, slots_host: Optional[Sequence[int]] = None,
-                      algorithm: str = "auto", stream=None) -> None:
+                      algorithm: str = "auto", workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """gdn_prefill_slots of include/gdn.h: sequence i runs from and writes back
     state_pool[slots[i]] (float32 [num_slots, h_v, d_k, d_v])."""
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
-                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm)
+                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm, workspace=workspace)
     n = cu_seqlens.numel() - 1
     _check(load().gdn_prefill_slots(ctypes.byref(prob), n, _ptr(cu_seqlens), _host_i32(cu_seqlens_host), T,
                                     _ptr(q), _ptr(k), _ptr(v), _ptr(state_pool), state_pool.shape[0], _ptr(slots),
@@ -290,15 +306,22 @@ def gdn_gated_rmsnorm(x: torch.Tensor, gate: torch.Tensor, scale: torch.Tensor, 
 
 # ----------------------------------------------------------------- helpers
 def prefill(q, k, v, cu_seqlens, *, initial_state=None, want_state=True, scale=0.0,
-            cu_seqlens_host=None, algorithm="auto", stream=None, **kw):
-    """Allocate ``out`` (and the final state) with torch and call gdn_prefill."""
-    T, _, d_k = q.shape
+            cu_seqlens_host=None, algorithm="auto", two_pass=True, stream=None, **kw):
+    """Allocate ``out`` (and the final state, and the chunked form's workspace
+    unless two_pass is False) with torch and call gdn_prefill."""
+    T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     n = cu_seqlens.numel() - 1
     out = torch.empty(T, h_v, d_v, dtype=q.dtype, device=q.device)
     fin = torch.empty(n, h_v, d_k, d_v, dtype=torch.float32, device=q.device) if want_state else None
+    ws = None
+    if two_pass and "workspace" not in kw:
+        variant = {key: kw[key] for key in ("rule", "decay_per_key", "beta_shared", "state_history") if key in kw}
+        nbytes = prefill_workspace_size(h_qk, h_v, d_k, d_v, q.dtype, n, T, algorithm=algorithm, **variant)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     gdn_prefill(q, k, v, cu_seqlens, out=out, final_state=fin, initial_state=initial_state, scale=scale,
-                cu_seqlens_host=cu_seqlens_host, algorithm=algorithm, stream=stream, **kw)
+                cu_seqlens_host=cu_seqlens_host, algorithm=algorithm, stream=stream,
+                **({"workspace": ws} if ws is not None else {}), **kw)
     return out, fin
 
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -137,6 +137,16 @@ typedef struct gdn_problem {
    * `gated_delta_steps`).  Decode ignores both fields.                    */
   int32_t state_window;
   float* state_history;
+  /* Optional device workspace for the chunked prefill (gdn_prefill and
+   * gdn_prefill_slots).  When the chunked form runs and workspace_bytes is at
+   * least gdn_prefill_workspace_size(), it runs in two passes: every chunk's
+   * factors are prepared in parallel into the workspace, then a sequential
+   * pass carries the state from chunk to chunk.  Otherwise one pass walks
+   * each sequence chunk by chunk.  Both give the same result up to rounding.
+   * The workspace is the caller's (16-byte aligned); its contents are
+   * scratch, and calls that share it must not overlap in time. */
+  void* workspace;
+  uint64_t workspace_bytes;
 } gdn_problem;
 
 /*
@@ -182,6 +192,16 @@ gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs,
 gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch,
                            const void* q, const void* k, const void* v,
                            float* state, void* out, hipStream_t stream);
+
+/*
+ * gdn_prefill_workspace_size -- bytes of workspace that let gdn_prefill (or
+ * gdn_prefill_slots) with this problem, num_seqs sequences and total_tokens
+ * tokens run the chunked form in two passes; 0 when that form does not apply
+ * (the serial algorithm, or a geometry the chunked form does not serve).  The
+ * size is a bound that holds for any split of the tokens into sequences.
+ */
+gdn_status gdn_prefill_workspace_size(const gdn_problem* problem, int32_t num_seqs,
+                                      int32_t total_tokens, uint64_t* bytes);
 
 /*
  * Slot-indexed state pool ([P3] nuvec-core, fast/imp.rs, `gated_delta_slots`:

@@ -40,9 +40,18 @@ def to_dev(t, dev="cuda"):
     return None if t is None else t.contiguous().to(dev)
 
 
+def workspace_for(inp: synth.Inputs, algorithm="auto", **variant):
+    """The two-pass chunked form's workspace for these inputs (None when it does not apply)."""
+    sh = inp.shape
+    nbytes = gdn.prefill_workspace_size(sh.h_qk, sh.h_v, sh.d_k, sh.d_v, sh.io_dtype, len(inp.seqlens),
+                                        inp.total_tokens, algorithm=algorithm, **variant)
+    return torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda") if nbytes else None
+
+
 def gpu_prefill(inp: synth.Inputs, g=None, beta=None, *, raw=False, scale=0.0, want_out=True,
-                want_state=True, in_place=False, use_host_cu=True, algorithm="auto"):
-    """Run gdn_prefill on cuda:0; returns (out, final) as CPU float64 tensors (or None)."""
+                want_state=True, in_place=False, use_host_cu=True, algorithm="auto", two_pass=False):
+    """Run gdn_prefill on cuda:0; returns (out, final) as CPU float64 tensors (or None).
+    two_pass: hand the call a workspace, so the chunked form runs in two passes."""
     dev = "cuda"
     q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
     cu = to_dev(inp.cu_seqlens)
@@ -58,6 +67,9 @@ def gpu_prefill(inp: synth.Inputs, g=None, beta=None, *, raw=False, scale=0.0, w
         fin = torch.full((n, h_v, d_k, d_v), float("nan"), dtype=torch.float32, device=dev) if want_state else None
     gates = (dict(a=to_dev(inp.a), b=to_dev(inp.b), A_log=to_dev(inp.A_log), dt_bias=to_dev(inp.dt_bias))
              if raw else dict(g=to_dev(g), beta=to_dev(beta)))
+    ws = workspace_for(inp, algorithm) if two_pass else None
+    if ws is not None:
+        gates["workspace"] = ws
     gdn.gdn_prefill(q, k, v, cu, out=out, final_state=fin, initial_state=s0, scale=scale,
                     cu_seqlens_host=inp.cu_seqlens.tolist() if use_host_cu else None, algorithm=algorithm,
                     **gates)

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 6
+    assert gdn.abi_version() == 7
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -45,7 +45,7 @@ def _prob(**kw):
     base = dict(h_qk=2, h_v=4, d_k=16, d_v=16, io_dtype=gdn.GDN_F32, scale=0.0,
                 gate_mode=gdn.GDN_GATES_PRECOMPUTED, g=FAKE, beta=FAKE + 0x1000, a=None, b=None,
                 A_log=None, dt_bias=None, algorithm=gdn.GDN_ALGO_AUTO, rule=0, decay_per_key=0, beta_shared=0,
-                state_window=0, state_history=None)
+                state_window=0, state_history=None, workspace=None, workspace_bytes=0)
     base.update(kw)
     return gdn.gdn_problem(**base)
 
@@ -271,3 +271,26 @@ def test_gated_rmsnorm_validation(lib, args, status, needle):
 def test_gated_rmsnorm_no_rows_is_ok(lib):
     assert lib.gdn_gated_rmsnorm(0, 128, 128, gdn.GDN_F32, None, None, None, 1e-5, gdn.GDN_ACT_SILU, None,
                                  None) == gdn.GDN_OK
+
+
+def test_prefill_workspace_size(lib):
+    size = ctypes.c_uint64(123)
+    chunky = dict(io_dtype=gdn.GDN_BF16, d_k=128, d_v=128, h_qk=16, h_v=32)
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), 8, 33173, ctypes.byref(size)) == gdn.GDN_OK
+    # the chunk table, then one record per (chunk, head) for ceil(T / 64) + N chunks
+    per_rec = 64 * 128 * 2 + 128 * 64 * 2 + 64 * 64 * 2 + 64 * 128 * 4 + 68 * 4
+    per_rec = (per_rec + 255) // 256 * 256
+    assert size.value == 256 + (33173 // 64 + 1 + 8) * 32 * per_rec
+    for kw in (dict(algorithm=gdn.GDN_ALGO_SERIAL), dict(io_dtype=gdn.GDN_F32), dict(d_k=96), dict(rule=2),
+               dict(decay_per_key=1), dict(state_window=2)):
+        st = lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**{**chunky, **kw})), 8, 33173, ctypes.byref(size))
+        assert st == gdn.GDN_OK and size.value == 0, kw
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), 0, 0, ctypes.byref(size)) == gdn.GDN_OK
+    assert size.value == 0
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), -1, 0, ctypes.byref(size)) == INVALID
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), 1, 1, None) == INVALID
+
+
+def test_prefill_workspace_misaligned(lib):
+    st = _prefill(lib, _prob(workspace=FAKE + 0x90008, workspace_bytes=1 << 20))
+    assert st == INVALID and "workspace" in gdn.last_error()

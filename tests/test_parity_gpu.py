@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from gated_delta_rule_serial_amd import gdn, synth
-from gpu_harness import TOL, check, gates_for, gpu_prefill, oracle_prefill, say, to_dev
+from gpu_harness import TOL, check, gates_for, gpu_prefill, oracle_prefill, say, to_dev, workspace_for
 
 pytestmark = pytest.mark.gpu
 
@@ -285,21 +285,23 @@ CHUNKED = [
 ]
 
 
+@pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "two_pass"])
 @pytest.mark.parametrize("case", CHUNKED, ids=lambda c: f"hq{c[0]}_hv{c[1]}_dk{c[2]}_dv{c[3]}_T{sum(c[4])}")
-def test_chunked_prefill(case):
+def test_chunked_prefill(case, two_pass):
     h_qk, h_v, d_k, d_v, lens, raw, init = case
     shape = _shape("varlen_prefill_8seq", h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v, init_state=init,
                    gate_mode="raw" if raw else "precomputed")
-    say(f"[chunked] {case}")
+    say(f"[chunked] {case} two_pass={two_pass}")
     inp = synth.generate(shape, seqlens=lens, seed=99)
     g, beta = (None, None) if raw else gates_for(inp)
-    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm="chunked")
+    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm="chunked", two_pass=two_pass)
     ro, rf = oracle_prefill(inp, g, beta, raw=raw)
     check(out, ro, TOL[shape.io_dtype], "out")
     check(fin, rf, TOL[shape.io_dtype], "final state")
 
 
-def test_chunked_prefill_resets_and_weak_decay():
+@pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "two_pass"])
+def test_chunked_prefill_resets_and_weak_decay(two_pass):
     """Log-decays of -inf (a reset), of 0 (no decay) and tiny beta in one sequence."""
     shape = _shape("varlen_prefill_8seq", init_state=True)
     inp = synth.generate(shape, seqlens=[150, 70])
@@ -311,8 +313,8 @@ def test_chunked_prefill_resets_and_weak_decay():
     beta = beta.float()
     beta[60:70] = 1e-3
     beta = beta.to(torch.bfloat16)
-    say("[chunked] resets / no decay / tiny beta")
-    out, fin = gpu_prefill(inp, g, beta, algorithm="chunked")
+    say(f"[chunked] resets / no decay / tiny beta, two_pass={two_pass}")
+    out, fin = gpu_prefill(inp, g, beta, algorithm="chunked", two_pass=two_pass)
     ro, rf = oracle_prefill(inp, g, beta)
     check(out, ro, TOL[torch.bfloat16], "out")
     check(fin, rf, TOL[torch.bfloat16], "final state")
@@ -329,8 +331,10 @@ def test_chunked_unsupported_is_reported():
 # ------------------------------------------------------------------ full sizes, sampled
 FULL = [
     ("prefill_t4096_fused_gates", [0, 15], "auto"),
+    ("prefill_t4096_fused_gates", [5, 9], "two_pass"),
     ("prefill_t4096_fused_gates", [3], "serial"),
     ("varlen_prefill_8seq", [0, 7, 15], "auto"),
+    ("varlen_prefill_8seq", [2, 11], "two_pass"),
     ("varlen_prefill_8seq", [4], "serial"),
     ("wide_prefill_t32768_d256", [0, 5], "auto"),
 ]
@@ -346,7 +350,8 @@ def test_prefill_full_size_sampled(name, heads, algorithm):
         f"oracle on head groups {heads}")
     raw = shape.gate_mode == "raw"
     g, beta = (None, None) if raw else gates_for(inp)
-    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm=algorithm)
+    two_pass = algorithm == "two_pass"
+    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm="auto" if two_pass else algorithm, two_pass=two_pass)
     ref = oracle_prefill(inp, g, beta, raw=raw, heads=heads)
     ratio = shape.h_v // shape.h_qk
     tol = TOL[shape.io_dtype]
@@ -398,7 +403,7 @@ def test_decode_slots(raw):
         assert torch.equal(pool_gpu[s].cpu(), pool[s]), f"untouched slot {s} changed"
 
 
-@pytest.mark.parametrize("algorithm", ["serial", "chunked"])
+@pytest.mark.parametrize("algorithm", ["serial", "chunked", "two_pass"])
 def test_prefill_slots(algorithm):
     shape = _shape("varlen_prefill_8seq", init_state=False)
     inp = synth.generate(shape, seqlens=[70, 0, 33, 129])
@@ -408,10 +413,12 @@ def test_prefill_slots(algorithm):
     say(f"[prefill-slots] {algorithm} slots={slots}")
     pool_gpu = pool.cuda()
     out = torch.full((inp.total_tokens, shape.h_v, shape.d_v), float("nan"), dtype=shape.io_dtype, device="cuda")
+    two_pass = algorithm == "two_pass"
     gdn.gdn_prefill_slots(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.cu_seqlens), pool_gpu,
                           torch.tensor(slots, dtype=torch.int32, device="cuda"), out=out, g=to_dev(g),
                           beta=to_dev(beta), cu_seqlens_host=inp.cu_seqlens.tolist(), slots_host=slots,
-                          algorithm=algorithm)
+                          algorithm="chunked" if two_pass else algorithm,
+                          workspace=workspace_for(inp, "chunked") if two_pass else None)
     torch.cuda.synchronize()
     s0 = torch.stack([pool[s] if 0 <= s < 6 else torch.zeros(pool.shape[1:]) for s in slots])
     ref_inp = dataclasses.replace(inp, initial_state=s0)

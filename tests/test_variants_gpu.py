@@ -49,7 +49,7 @@ def _oracle(inp, g, beta, *, rule, per_key, shared, window=0):
                        beta_shared=shared, window=window)
 
 
-def _gpu_prefill(inp, gates, *, raw, rule, per_key, shared, window=0, algorithm="serial"):
+def _gpu_prefill(inp, gates, *, raw, rule, per_key, shared, window=0, algorithm="serial", two_pass=False):
     dev = "cuda"
     T, n = inp.total_tokens, len(inp.seqlens)
     h_v, d_k, d_v = inp.shape.h_v, inp.shape.d_k, inp.shape.d_v
@@ -57,6 +57,12 @@ def _gpu_prefill(inp, gates, *, raw, rule, per_key, shared, window=0, algorithm=
     fin = torch.full((n, h_v, d_k, d_v), float("nan"), device=dev)
     hist = torch.full((n, window, h_v, d_k, d_v), float("nan"), device=dev) if window else None
     kw = {k: to_dev(v) for k, v in gates.items()}
+    if two_pass:
+        sh = inp.shape
+        nbytes = gdn.prefill_workspace_size(sh.h_qk, sh.h_v, sh.d_k, sh.d_v, sh.io_dtype, n, T, algorithm=algorithm,
+                                            rule=rule, decay_per_key=per_key, beta_shared=shared)
+        assert nbytes > 0
+        kw["workspace"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     gdn.gdn_prefill(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.cu_seqlens), out=out, final_state=fin,
                     initial_state=to_dev(inp.initial_state), cu_seqlens_host=inp.cu_seqlens.tolist(),
                     algorithm=algorithm, rule=rule, decay_per_key=per_key, beta_shared=shared,
@@ -130,12 +136,14 @@ def test_state_history(window):
 
 @pytest.mark.parametrize("shared", [False, True], ids=["perhead", "sharedbeta"])
 @pytest.mark.parametrize("rule", ["gated_delta", "delta"])
-def test_chunked_rules_and_shared_beta(rule, shared):
+@pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "two_pass"])
+def test_chunked_rules_and_shared_beta(rule, shared, two_pass):
     dt = torch.bfloat16
-    say(f"[chunked-variant] {rule} shared={shared}")
+    say(f"[chunked-variant] {rule} shared={shared} two_pass={two_pass}")
     inp, raw_in, g64, b64 = _setup(16, 32, 128, 128, dt, [150, 70, 1], seed=500, shared=shared)
     gates = _gate_kwargs(True, raw_in, g64, b64, dt)
-    out, fin, _ = _gpu_prefill(inp, gates, raw=True, rule=rule, per_key=False, shared=shared, algorithm="chunked")
+    out, fin, _ = _gpu_prefill(inp, gates, raw=True, rule=rule, per_key=False, shared=shared, algorithm="chunked",
+                               two_pass=two_pass)
     ro, rf = _oracle(inp, g64, b64, rule=rule, per_key=False, shared=shared)
     check(out, torch.from_numpy(ro), TOL[dt], "out")
     check(fin, torch.from_numpy(rf), TOL[dt], "final state")
