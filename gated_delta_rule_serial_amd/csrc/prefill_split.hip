@@ -63,8 +63,10 @@ __device__ __forceinline__ int seq_hi(const int32_t* cu, int n, int T) {
   return min(max(cu[n + 1], seq_lo(cu, n, T)), T);
 }
 
-// cs[n] = chunks of the sequences before n; cs[N] = all chunks.
-__global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int num_seqs, int T, int32_t* cs) {
+// cs[n] = chunks of the sequences before n; cs[N] = all chunks; info[c] =
+// (first token, tokens) of chunk c.
+__global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int num_seqs, int T, int32_t* cs,
+                                                           int2* info) {
   __shared__ int part[1024];
   const int tid = static_cast<int>(threadIdx.x);
   const int per = (num_seqs + 1023) / 1024;
@@ -83,7 +85,8 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
   int run = part[tid] - sum;
   for (int n = a; n < b; ++n) {
     cs[n] = run;
-    run += chunks(n);
+    const int lo = seq_lo(cu, n, T), hi = seq_hi(cu, n, T);
+    for (int t = lo; t < hi; t += kC) info[run++] = make_int2(t, min(kC, hi - t));
   }
   if (tid == 1023) cs[num_seqs] = part[1023];
 }
@@ -109,9 +112,12 @@ struct PrepLds {
   static_assert(kBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
+// Persistent: one workgroup per CU (the LDS holds one) walks the (chunk,
+// value head) items blockIdx.x, + gridDim.x, ...; the next item's K, Q, V rows
+// and gates are loaded into registers while the current one computes.
 template <typename IO, int DK, int DVT, bool RAW>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
-                                                              const int32_t* cs) {
+                                                              const int32_t* cs, const int2* info, int items) {
   using L_ = PrepLds<DK, DVT>;
   constexpr int SK = L_::SK;
   constexpr int DVP = L_::DVP;
@@ -132,19 +138,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   float* Bet = reinterpret_cast<float*>(smem + L_::kBet);
 
   const int T = p.total_tokens;
-  const int c = static_cast<int>(blockIdx.x);
-  const int h = static_cast<int>(blockIdx.y);
-  if (c >= cs[p.num_seqs]) return;  // the grid is sized for the worst case
-  int lo = 0, hi = p.num_seqs - 1;  // largest n with cs[n] <= c
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cs[mid] <= c) lo = mid;
-    else hi = mid - 1;
-  }
-  const int n = lo;
-  const int t0 = seq_lo(p.cu, n, T) + (c - cs[n]) * kC;
-  const int Lc = min(kC, seq_hi(p.cu, n, T) - t0);
-  const int hq = h / p.ratio;
+  const int total = cs[p.num_seqs] * p.h_v;  // live items; the grid covers a bound
+  const int n_items = items < total ? items : total;
   const int d_v = p.d_v;
   const int tid = static_cast<int>(threadIdx.x);
   const int w = tid >> 6;
@@ -152,65 +147,78 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   const int rb = w & 3;
   const int chalf = w >> 2;
   const Rec rec(DK, DVP);
-  unsigned char* base = ws + (static_cast<size_t>(c) * p.h_v + h) * rec_bytes;
-
   const IO* qg = static_cast<const IO*>(p.q);
   const IO* kg = static_cast<const IO*>(p.k);
   const IO* vg = static_cast<const IO*>(p.v);
   const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
   const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
 
-  // ================= 1. K, Q rows; V^T; gates and the prefix sum of the log-decay
+  // item i is chunk c = i / h_v (first token, tokens from the chunk table), head h = i % h_v
+  struct Where {
+    int c, h, t0, Lc;
+  };
+  auto locate = [&](int item, int2 ci) __attribute__((always_inline)) {
+    Where at;
+    at.c = item / p.h_v;
+    at.h = item % p.h_v;
+    at.t0 = ci.x;
+    at.Lc = ci.y;
+    return at;
+  };
+  auto info_of = [&](int item) __attribute__((always_inline)) {
+    return item < n_items ? info[item / p.h_v] : make_int2(0, 0);
+  };
+
+  // ---- register staging of one item (vector-typed, so that it stays in registers)
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   constexpr int VPR = DK / 8;
-  for (int v = tid; v < kC * VPR; v += kThreads) {
-    const int t = v / VPR, c8 = (v % VPR) * 8;
-    uint4 kk = make_uint4(0, 0, 0, 0), qq = make_uint4(0, 0, 0, 0);
-    if (t < Lc) {
-      const size_t off = static_cast<size_t>(t0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
-      kk = *reinterpret_cast<const uint4*>(kg + off);
-      qq = *reinterpret_cast<const uint4*>(qg + off);
-    }
-    *reinterpret_cast<uint4*>(Ks + t * SK + c8) = kk;
-    *reinterpret_cast<uint4*>(Qs + t * SK + c8) = qq;
-  }
+  constexpr int KQ_IT = kC * VPR / kThreads;
   constexpr int VPV = DVP / 8;
-  for (int v = tid; v < kC * VPV; v += kThreads) {
-    const int t = v / VPV, c8 = (v % VPV) * 8;
-    uint4 vv = make_uint4(0, 0, 0, 0);
-    if (t < Lc && c8 < d_v)
-      vv = *reinterpret_cast<const uint4*>(vg + static_cast<size_t>(t0 + t) * v_stride + static_cast<size_t>(h) * d_v + c8);
-    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+  constexpr int V_IT = kC * VPV / kThreads;
+  static_assert(KQ_IT >= 1 && V_IT >= 1, "block shape");
+  u32x4 rk[KQ_IT], rq[KQ_IT], rv[V_IT];
+  float rg = 0.0f, rbt = 0.0f;  // wave 0: gate inputs of token (chunk start + lane)
+  auto fetch = [&](const Where& at) __attribute__((always_inline)) {
+    const int hq = at.h / p.ratio;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      Vt[(c8 + e) * kSC + t] = static_cast<bf16_t>((e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu));
-  }
-  if (w == 0) {
-    float g = 0.0f, b = 0.0f;
-    if (lane < Lc) {
-      const size_t gi = static_cast<size_t>(t0 + lane) * p.h_v + h;
-      const size_t bi = p.gates.beta_shared ? static_cast<size_t>(t0 + lane) : gi;
-      if constexpr (RAW) {
-        g = p.gates.decays ? gate_log_decay(widen(static_cast<const IO*>(p.gates.a)[gi]), p.gates.A_log[h],
-                                            p.gates.dt_bias[h])
-                           : 0.0f;
-        b = gate_sigmoid(widen(static_cast<const IO*>(p.gates.b)[bi]));
-      } else {
-        g = p.gates.decays ? widen(static_cast<const IO*>(p.gates.g)[gi]) : 0.0f;
-        b = widen(static_cast<const IO*>(p.gates.beta)[bi]);
+    for (int it = 0; it < KQ_IT; ++it) {
+      const int v = tid + it * kThreads;
+      const int t = v / VPR, c8 = (v % VPR) * 8;
+      rk[it] = u32x4{0u, 0u, 0u, 0u};
+      rq[it] = u32x4{0u, 0u, 0u, 0u};
+      if (t < at.Lc) {
+        const size_t off = static_cast<size_t>(at.t0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
+        rk[it] = *reinterpret_cast<const u32x4*>(kg + off);
+        rq[it] = *reinterpret_cast<const u32x4*>(qg + off);
       }
-      g = fmaxf(g, kMinLogDecay);
     }
-    double G = static_cast<double>(g) * kLog2e;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double y = __shfl_up(G, off, 64);
-      if (lane >= off) G += y;
+    for (int it = 0; it < V_IT; ++it) {
+      const int v = tid + it * kThreads;
+      const int t = v / VPV, c8 = (v % VPV) * 8;
+      rv[it] = u32x4{0u, 0u, 0u, 0u};
+      if (t < at.Lc && c8 < d_v)
+        rv[it] = *reinterpret_cast<const u32x4*>(vg + static_cast<size_t>(at.t0 + t) * v_stride +
+                                                 static_cast<size_t>(at.h) * d_v + c8);
     }
-    Gd[lane] = G;
-    Gam[lane] = fast_exp2(static_cast<float>(G));
-    Bet[lane] = b;
-  }
-  // the upper tiles of M stay zero
+    if (w == 0) {
+      rg = 0.0f;
+      rbt = 0.0f;
+      if (lane < at.Lc) {
+        const size_t gi = static_cast<size_t>(at.t0 + lane) * p.h_v + at.h;
+        const size_t bi = p.gates.beta_shared ? static_cast<size_t>(at.t0 + lane) : gi;
+        if constexpr (RAW) {
+          if (p.gates.decays) rg = widen(static_cast<const IO*>(p.gates.a)[gi]);
+          rbt = widen(static_cast<const IO*>(p.gates.b)[bi]);
+        } else {
+          if (p.gates.decays) rg = widen(static_cast<const IO*>(p.gates.g)[gi]);
+          rbt = widen(static_cast<const IO*>(p.gates.beta)[bi]);
+        }
+      }
+    }
+  };
+
+  // the upper tiles of M stay zero for every item
   for (int e = tid; e < 6 * 256; e += kThreads) {
     const int tile = e >> 8;
     const int tb = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
@@ -218,12 +226,69 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     const int t = 16 * tb + ((e & 255) >> 4), s = 16 * cs_ + (e & 15);
     Ms[t * kSC + s] = 0;
   }
-  __syncthreads();
+
+  int item = static_cast<int>(blockIdx.x);
+  if (item >= n_items) return;
+  Where at = locate(item, info[item / p.h_v]);
+  fetch(at);
+  int2 next_info = info_of(item + static_cast<int>(gridDim.x));  // one item ahead of the fetch
+  for (; item < n_items; item += static_cast<int>(gridDim.x)) {
+    const int h = at.h;
+    const int Lc = at.Lc;
+    unsigned char* base = ws + (static_cast<size_t>(at.c) * p.h_v + h) * rec_bytes;
+
+    // ================= 1. stage K, Q rows and V^T; gates and the prefix sum of the log-decay
+#pragma unroll
+    for (int it = 0; it < KQ_IT; ++it) {
+      const int v = tid + it * kThreads;
+      const int t = v / VPR, c8 = (v % VPR) * 8;
+      *reinterpret_cast<u32x4*>(Ks + t * SK + c8) = rk[it];
+      *reinterpret_cast<u32x4*>(Qs + t * SK + c8) = rq[it];
+    }
+#pragma unroll
+    for (int it = 0; it < V_IT; ++it) {
+      const int v = tid + it * kThreads;
+      const int t = v / VPV, c8 = (v % VPV) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        Vt[(c8 + e) * kSC + t] =
+            static_cast<bf16_t>((e & 1) ? (rv[it][e >> 1] >> 16) : (rv[it][e >> 1] & 0xffffu));
+    }
+    if (w == 0) {
+      float g = 0.0f, b = 0.0f;
+      if (lane < Lc) {
+        if constexpr (RAW) {
+          g = p.gates.decays ? gate_log_decay(rg, p.gates.A_log[h], p.gates.dt_bias[h]) : 0.0f;
+          b = gate_sigmoid(rbt);
+        } else {
+          g = rg;
+          b = rbt;
+        }
+        g = fmaxf(g, kMinLogDecay);
+      }
+      double G = static_cast<double>(g) * kLog2e;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(G, off, 64);
+        if (lane >= off) G += y;
+      }
+      Gd[lane] = G;
+      Gam[lane] = fast_exp2(static_cast<float>(G));
+      Bet[lane] = b;
+    }
+    // the next item's inputs, in flight while this one computes
+    const int next = item + static_cast<int>(gridDim.x);
+    if (next < n_items) {
+      at = locate(next, next_info);
+      fetch(at);
+      next_info = info_of(next + static_cast<int>(gridDim.x));
+    }
+    __syncthreads();
 
   // ================= 2. K^T; P = K K^T, R = Q K^T -> A (f32) and M (bf16)
-  for (int item = tid; item < DK * (kC / 8); item += kThreads) {
-    const int i = item % DK;
-    const int t8 = (item / DK) * 8;
+  for (int ix = tid; ix < DK * (kC / 8); ix += kThreads) {
+    const int i = ix % DK;
+    const int t8 = (ix / DK) * 8;
     uint32_t wv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -329,9 +394,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   }
   bf16_t* ktg = reinterpret_cast<bf16_t*>(base + rec.kt);
   const double Glast = Gd[kC - 1];  // gates past the chunk's end are 0: G stays at its last value
-  for (int item = tid; item < DK * (kC / 8); item += kThreads) {
-    const int i = item / (kC / 8);
-    const int t8 = (item % (kC / 8)) * 8;
+  for (int ix = tid; ix < DK * (kC / 8); ix += kThreads) {
+    const int i = ix / (kC / 8);
+    const int t8 = (ix % (kC / 8)) * 8;
     uint32_t wv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -351,6 +416,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     gg[lane] = Gam[lane];
     if (lane == 0) gg[kC] = Gam[kC - 1];
   }
+  __syncthreads();  // the LDS is restaged for the next item
+  }
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -364,7 +431,8 @@ struct StateLds {
   static constexpr int kSt = kMs + kC * kSC * 2;         // S^T    [NC][SK] bf16
   static constexpr int kDt = kSt + NC * SK * 2;          // D^T    [NC][SC] bf16
   static constexpr int kGam = kDt + NC * kSC * 2;        // gam    [C] f32
-  static constexpr int kBytes = kGam + kC * 4;
+  static constexpr int kOs = kGam + kC * 4;              // O      [8 waves][16][NC / 2 + 8] bf16
+  static constexpr int kBytes = kOs + kWaves * 16 * (NC / 2 + 8) * 2;
   static_assert(kBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
@@ -379,6 +447,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   constexpr int CTW = CT / 2;                   // column tiles per wave in the (token, column) products
   constexpr int STW = (DK / 16) * CT / kWaves;  // state tiles per wave
   static_assert(CT % 2 == 0 && STW >= 1, "block shape");
+  static_assert(STW <= CT && CT % STW == 0, "a wave's state tiles lie in one row tile");
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* Ws = reinterpret_cast<bf16_t*>(smem + L_::kWs);
   bf16_t* Qs = reinterpret_cast<bf16_t*>(smem + L_::kQs);
@@ -387,12 +456,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   bf16_t* St = reinterpret_cast<bf16_t*>(smem + L_::kSt);
   bf16_t* Dt = reinterpret_cast<bf16_t*>(smem + L_::kDt);
   float* Gam = reinterpret_cast<float*>(smem + L_::kGam);
+  constexpr int kSO = NC / 2 + 8;  // bf16 row stride of a wave's output block
 
   const int tid = static_cast<int>(threadIdx.x);
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int rb = w & 3;
   const int chalf = w >> 2;
+  bf16_t* Os = reinterpret_cast<bf16_t*>(smem + L_::kOs) + w * 16 * kSO;
   int unit = static_cast<int>(blockIdx.x);
   const int cb = unit % p.col_blocks;
   unit /= p.col_blocks;
@@ -545,29 +616,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
     __syncthreads();
 
-    // ================= c. O = scale (gam Q S + M D)
+    // ================= c. O = scale (gam Q S + M D); the A fragment (M rows) is shared by the wave's tiles
     const int kmax = (rb < 2) ? 32 : 64;  // M vanishes above the diagonal
+    for (int kk = 0; kk < kmax; kk += 32) {
+      const bf16x8 am = frag(Ms + (16 * rb) * kSC + kk, kSC, lane);
 #pragma unroll
-    for (int e = 0; e < CTW; ++e) {
-      const int cj = chalf * CTW + e;
-      f32x4 o = mma_range(Y[e], Ms + (16 * rb) * kSC, kSC, Dt + (16 * cj) * kSC, kSC, 0, kmax, lane);
-      if (og != nullptr) {
-        const int col = J0 + 16 * cj + acc_col(lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * rb + acc_row(lane, i);
-          if (t < Lc && col < d_v)
-            narrow_store(og + static_cast<size_t>(c0 + t) * v_stride + static_cast<size_t>(h) * d_v + col, p.scale * o[i]);
-        }
+      for (int e = 0; e < CTW; ++e) {
+        const int cj = chalf * CTW + e;
+        Y[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, frag(Dt + (16 * cj) * kSC + kk, kSC, lane), Y[e], 0, 0, 0);
       }
     }
-    // ================= d. S <- gam_last S + Kt^T D
+    // the wave's 16 x NC/2 output block goes through LDS and out in 16-byte rows
+    if (og != nullptr) {
 #pragma unroll
-    for (int e = 0; e < STW; ++e) {
-      const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;
-      f32x4 acc = S[e] * gam_last;
-      acc = mma<kC>(acc, KTs + (16 * ri) * kSC, kSC, Dt + (16 * cj) * kSC, kSC, lane);
-      S[e] = acc;
+      for (int e = 0; e < CTW; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Os[acc_row(lane, i) * kSO + 16 * e + acc_col(lane)] = to_bf16(p.scale * Y[e][i]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+      constexpr int VPRO = NC / 16;  // 8-element vectors per row of the block
+#pragma unroll
+      for (int it = 0; it < 16 * VPRO / 64; ++it) {
+        const int v = lane + 64 * it;
+        const int r = v / VPRO, c8 = (v % VPRO) * 8;
+        const int t = 16 * rb + r;
+        const int col = J0 + chalf * (NC / 2) + c8;
+        if (t < Lc && col < d_v)
+          *reinterpret_cast<uint4*>(og + static_cast<size_t>(c0 + t) * v_stride + static_cast<size_t>(h) * d_v + col) =
+              *reinterpret_cast<const uint4*>(Os + r * kSO + c8);
+      }
+    }
+    // ================= d. S <- gam_last S + Kt^T D; a wave's state tiles share one row tile (its A fragment)
+#pragma unroll
+    for (int e = 0; e < STW; ++e) S[e] = S[e] * gam_last;
+#pragma unroll
+    for (int kk = 0; kk < kC; kk += 32) {
+      const bf16x8 ak = frag(KTs + (16 * ((w * STW) / CT)) * kSC + kk, kSC, lane);
+#pragma unroll
+      for (int e = 0; e < STW; ++e) {
+        const int cj = (w * STW + e) % CT;
+        S[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, frag(Dt + (16 * cj) * kSC + kk, kSC, lane), S[e], 0, 0, 0);
+      }
     }
     publish_state();
     __syncthreads();
@@ -599,23 +688,38 @@ hipError_t set_lds(K kern, int bytes, bool* configured) {
 
 int split_columns(int d_v) { return d_v > 64 ? 128 : 64; }
 
+// Persistent grid of the preparation pass: one workgroup per compute unit.
+int prep_workgroups() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 template <typename IO, int DK, int DVT>
-hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, int32_t* cs, int chunk_bound,
-                      hipStream_t stream) {
+hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, int32_t* cs, const int2* info,
+                      int chunk_bound, hipStream_t stream) {
   if (chunk_bound > 0 && p.h_v > 0) {
     constexpr int bytes = PrepLds<DK, DVT>::kBytes;
+    const int items = chunk_bound * p.h_v;
+    const unsigned grid = static_cast<unsigned>(items < prep_workgroups() ? items : prep_workgroups());
     if (p.gates.raw) {
       static bool cfg = false;
       auto kern = chunk_prep_kernel<IO, DK, DVT, true>;
       hipError_t e = set_lds(kern, bytes, &cfg);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(chunk_bound, p.h_v), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs);
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items);
     } else {
       static bool cfg = false;
       auto kern = chunk_prep_kernel<IO, DK, DVT, false>;
       hipError_t e = set_lds(kern, bytes, &cfg);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(chunk_bound, p.h_v), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs);
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -652,11 +756,16 @@ bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int w
 
 int split_columns_per_block(int d_v) { return split_columns(d_v); }
 
+// Workspace: cs [N + 1] int32, info [chunk bound] int2, then the records.
+static size_t table_bytes(int num_seqs, int total_tokens) {
+  return align256(static_cast<size_t>(num_seqs + 1) * 4) + align256(static_cast<size_t>(chunk_bound_of(num_seqs, total_tokens)) * 8);
+}
+
 size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v) {
   if (num_seqs <= 0) return 0;
   const int dvt = pad16(d_v) > 128 ? 16 : 8;
   const Rec rec(d_k, 16 * dvt);
-  return align256(static_cast<size_t>(num_seqs + 1) * 4) +
+  return table_bytes(num_seqs, total_tokens) +
          static_cast<size_t>(chunk_bound_of(num_seqs, total_tokens)) * h_v * rec.bytes;
 }
 
@@ -664,19 +773,21 @@ hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t strea
   if (p.num_seqs <= 0) return hipSuccess;
   const int dvt = pad16(p.d_v) > 128 ? 16 : 8;
   const Rec rec(p.d_k, 16 * dvt);
-  int32_t* cs = static_cast<int32_t*>(workspace);
-  unsigned char* recs = static_cast<unsigned char*>(workspace) + align256(static_cast<size_t>(p.num_seqs + 1) * 4);
   // total tokens: the caller's count (the kernels clamp the sequences to it)
   const int T = p.total_tokens;
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, stream, p.cu, p.num_seqs, T, cs);
+  int32_t* cs = static_cast<int32_t*>(workspace);
+  int2* info = reinterpret_cast<int2*>(static_cast<unsigned char*>(workspace) +
+                                       align256(static_cast<size_t>(p.num_seqs + 1) * 4));
+  unsigned char* recs = static_cast<unsigned char*>(workspace) + table_bytes(p.num_seqs, T);
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, stream, p.cu, p.num_seqs, T, cs, info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int bound = chunk_bound_of(p.num_seqs, T);
   if (p.d_k == 128)
-    return dvt == 16 ? launch_dvt<bf16_t, 128, 16>(p, recs, rec.bytes, cs, bound, stream)
-                     : launch_dvt<bf16_t, 128, 8>(p, recs, rec.bytes, cs, bound, stream);
-  return dvt == 16 ? launch_dvt<bf16_t, 64, 16>(p, recs, rec.bytes, cs, bound, stream)
-                   : launch_dvt<bf16_t, 64, 8>(p, recs, rec.bytes, cs, bound, stream);
+    return dvt == 16 ? launch_dvt<bf16_t, 128, 16>(p, recs, rec.bytes, cs, info, bound, stream)
+                     : launch_dvt<bf16_t, 128, 8>(p, recs, rec.bytes, cs, info, bound, stream);
+  return dvt == 16 ? launch_dvt<bf16_t, 64, 16>(p, recs, rec.bytes, cs, info, bound, stream)
+                   : launch_dvt<bf16_t, 64, 8>(p, recs, rec.bytes, cs, info, bound, stream);
 }
 
 }  // namespace gdn

@@ -280,7 +280,8 @@ def test_prefill_workspace_size(lib):
     # the chunk table, then one record per (chunk, head) for ceil(T / 64) + N chunks
     per_rec = 64 * 128 * 2 + 128 * 64 * 2 + 64 * 64 * 2 + 64 * 128 * 4 + 68 * 4
     per_rec = (per_rec + 255) // 256 * 256
-    assert size.value == 256 + (33173 // 64 + 1 + 8) * 32 * per_rec
+    bound = 33173 // 64 + 1 + 8
+    assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * per_rec
     for kw in (dict(algorithm=gdn.GDN_ALGO_SERIAL), dict(io_dtype=gdn.GDN_F32), dict(d_k=96), dict(rule=2),
                dict(decay_per_key=1), dict(state_window=2)):
         st = lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**{**chunky, **kw})), 8, 33173, ctypes.byref(size))
