@@ -14,7 +14,8 @@
 //     in VGPRs for the whole scan (no scratch, no LDS);
 //   * the two d_k dot products per token (retrieval before the update,
 //     readout after it) are partial sums over a lane's rows followed by a
-//     DPP row-op reduction over the R lanes (plus one ds_swizzle for R = 32);
+//     DPP row-op reduction over the R lanes (plus a ds_swizzle and a lane
+//     exchange across the wave halves for R = 64);
 //   * q_t, k_t, v_t are loaded as packed words PF tokens ahead of use
 //     through a register ring, so global latency overlaps the serial chain;
 //   * the gates of 64 tokens are computed once, lane-parallel (lane l takes
@@ -31,7 +32,12 @@ namespace gdn {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kPrefetch = 4;  // tokens of q/k/v in flight ahead of use
+// Tokens of q/k/v in flight ahead of use.  Four suffice when several waves
+// share a SIMD; the widest head (d_k = 256, a whole wave per column) runs
+// few waves per SIMD, and there the serial chain of one token is far shorter
+// than a load's latency, so it keeps eight in flight.
+template <int DK>
+constexpr int prefetch_depth() { return DK >= 256 ? 8 : 4; }
 
 // Lanes per column for each padded key size (rows per lane = DK / R).
 template <int DK>
@@ -40,7 +46,7 @@ template <> struct ScanShape<16> { static constexpr int R = 4; };
 template <> struct ScanShape<32> { static constexpr int R = 8; };
 template <> struct ScanShape<64> { static constexpr int R = 8; };
 template <> struct ScanShape<128> { static constexpr int R = 16; };
-template <> struct ScanShape<256> { static constexpr int R = 32; };
+template <> struct ScanShape<256> { static constexpr int R = 64; };  // one column per wave
 
 // GENERAL = false compiles the plain gated delta rule with no state history
 // (the rule flags and the window are constants); GENERAL = true reads them
@@ -50,6 +56,7 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   constexpr int R = ScanShape<DK>::R;
   constexpr int CPW = kWave / R;
   constexpr int RPL = DK / R;
+  constexpr int kPrefetch = prefetch_depth<DK>();
 
   const int lane = static_cast<int>(threadIdx.x);
   const int c = lane / R;        // column within the wave
