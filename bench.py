@@ -264,7 +264,9 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=Tru
         fl = chunked_flops(shape, T)
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-                "traffic": _traffic(shape.name + "_chunked", ["prefill_chunked.hip", "gdn_device.hpp"]),
+                "traffic": (_traffic(shape.name + "_two_pass", ["prefill_split.hip", "chunk_mfma.hpp", "gdn_device.hpp"])
+                            if ws_bytes else
+                            _traffic(shape.name + "_chunked", ["prefill_chunked.hip", "chunk_mfma.hpp", "gdn_device.hpp"])),
                 "kernel": ("chunk_prep_kernel + chunk_state_kernel (chunked in two passes, bf16 MFMA)" if ws_bytes
                            else "chunk_kernel (chunked, bf16 MFMA)"),
                 "algorithmic_bytes_per_launch": nbytes, "workspace_bytes": ws_bytes,
