@@ -179,10 +179,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   for (int off = kColThreads; off < 64; off *= 2) {
 #pragma unroll
     for (int cc = 0; cc < kColsPerThread; ++cc) {
-      pa[cc] += __shfl_xor(pa[cc], off);
-      pc[cc] += __shfl_xor(pc[cc], off);
+      pa[cc] = off == 16 ? xor16_sum(pa[cc]) : xor32_sum(pa[cc]);
+      pc[cc] = off == 16 ? xor16_sum(pc[cc]) : xor32_sum(pc[cc]);
     }
-    pkq += __shfl_xor(pkq, off);
+    pkq = off == 16 ? xor16_sum(pkq) : xor32_sum(pkq);
   }
   const int wave = tid / 64;
   if (tid % 64 < kColThreads) {

@@ -232,6 +232,25 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// x + (x of lane i ^ 16) and x + (x of lane i ^ 32) with the gfx950 lane
+// swaps (VALU, no LDS): v_permlane16_swap exchanges the odd 16-lane rows of
+// its first operand with the even rows of its second, v_permlane32_swap the
+// upper half of the first with the lower half of the second; with both
+// operands holding x, their sum is the pairwise sum in every lane.  The
+// instructions are written out because the compiler's builtins return one
+// operand for both results.  The s_nop pairs cover the hazards around a
+// lane swap that reads a just-written register.
+__device__ __forceinline__ float xor16_sum(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+
 // Sum over aligned groups of G consecutive lanes (G = 1, 2, 4, 8, 16, 32,
 // 64); every lane of a group receives the group's sum.  Every lane of the
 // wave must be active.
@@ -241,12 +260,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (G >= 4) x += dpp<kQuadSwap2>(x);
   if constexpr (G >= 8) x += dpp<kRowHalfMirror>(x);
   if constexpr (G >= 16) x += dpp<kRowMirror>(x);
-  if constexpr (G >= 32) {
-    // lane i <- lane i ^ 16 within each 32 (ds_swizzle bit-mask mode:
-    // and_mask 0x1f, or_mask 0, xor_mask 0x10).
-    x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
-  }
-  if constexpr (G >= 64) x += __shfl_xor(x, 32);
+  if constexpr (G >= 32) x = xor16_sum(x);
+  if constexpr (G >= 64) x = xor32_sum(x);
   static_assert(G <= 64, "group_sum supports groups of at most 64 lanes");
   return x;
 }

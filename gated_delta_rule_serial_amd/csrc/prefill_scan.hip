@@ -14,8 +14,8 @@
 //     in VGPRs for the whole scan (no scratch, no LDS);
 //   * the two d_k dot products per token (retrieval before the update,
 //     readout after it) are partial sums over a lane's rows followed by a
-//     DPP row-op reduction over the R lanes (plus a ds_swizzle and a lane
-//     exchange across the wave halves for R = 64);
+//     DPP row-op reduction over the R lanes (plus the gfx950 lane swaps
+//     across 16-lane rows and wave halves for R = 32 and 64);
 //   * q_t, k_t, v_t are loaded as packed words PF tokens ahead of use
 //     through a register ring, so global latency overlaps the serial chain;
 //   * the gates of 64 tokens are computed once, lane-parallel (lane l takes
@@ -51,12 +51,18 @@ template <> struct ScanShape<256> { static constexpr int R = 64; };  // one colu
 // GENERAL = false compiles the plain gated delta rule with no state history
 // (the rule flags and the window are constants); GENERAL = true reads them
 // at run time and serves every other variant.
-template <typename IO, int DK, bool RAW, bool PERKEY, bool GENERAL>
+// FULL: d_k == DK, so every lane's rows exist and the q/k loads need no masks.
+template <typename IO, int DK, bool RAW, bool PERKEY, bool GENERAL, bool FULL>
 __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   constexpr int R = ScanShape<DK>::R;
   constexpr int CPW = kWave / R;
   constexpr int RPL = DK / R;
   constexpr int kPrefetch = prefetch_depth<DK>();
+  // Tokens per loop iteration.  Ring registers that cross the loop's back
+  // edge with loads in flight make the compiler wait for those loads at the
+  // loop head; d_k = 256 (few waves per SIMD to hide that) unrolls a whole
+  // 64-token gate block, so the wait comes once per 64 tokens.
+  constexpr int kGroup = (DK >= 256 && !GENERAL) ? kWave : kPrefetch;
 
   const int lane = static_cast<int>(threadIdx.x);
   const int c = lane / R;        // column within the wave
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   const int j = cb * CPW + c;
   const bool col_ok = j < p.d_v;
   const int row0 = r * RPL;
-  const bool full_rows = (p.d_k == DK);
+  const bool full_rows = FULL || (p.d_k == DK);
   const int row_limit = p.d_k - row0;  // rows of this lane's slice that exist
   const bool decays = GENERAL ? p.gates.decays != 0 : true;
   const bool deltas = GENERAL ? p.gates.deltas != 0 : true;
@@ -172,17 +178,24 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
     }
     ring_v[slot].load(vg + static_cast<size_t>(t) * v_stride + v_off);
   };
+  // every slot holds a real token (clamped to the last one), so padded tokens
+  // at the end compute on finite values
+  if (t_begin < t_end) {
 #pragma unroll
-  for (int s = 0; s < kPrefetch; ++s)
-    if (t_begin + s < t_end) fetch_token(s, t_begin + s);
+    for (int s = 0; s < kPrefetch; ++s) fetch_token(s, min(t_begin + s, t_end - 1));
+  }
 
   const float scale = p.scale;
   const int hist_from = (t_end - t_begin) - W;  // first token (relative) whose state is kept
-  for (int tb = t_begin; tb < t_end; tb += kPrefetch) {
+  // The last group runs whole: tokens past the end take alpha = 1 and a zero
+  // update (the state stays as it is) and store nothing, so the unrolled
+  // group has one exit.
+  for (int tb = t_begin; tb < t_end; tb += kGroup) {
 #pragma unroll
-    for (int s = 0; s < kPrefetch; ++s) {
-      const int t = tb + s;
-      if (t >= t_end) break;
+    for (int u = 0; u < kGroup; ++u) {
+      const int s = u % kPrefetch;  // ring slot
+      const int t = tb + u;
+      const bool live = t < t_end;
       const int rel = (t - t_begin) & (kWave - 1);
       if (rel == 0) {
         // gates of tokens t .. t + 63, one per lane, then prefetch the next block
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
         }
         fetch_gate_block(t + kWave);
       }
-      const float beta = readlane(blk_beta, rel);
+      const float beta = live ? readlane(blk_beta, rel) : 0.0f;
 
       float kf[RPL], qf[RPL];
       ring_k[s].widen_to(kf);
@@ -204,19 +217,22 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
       const float vv = ring_v[s].value();
       float gr[PERKEY ? RPL : 1];
       if constexpr (PERKEY) ring_g[s].widen_to(gr);
-      if (t + kPrefetch < t_end) fetch_token(s, t + kPrefetch);
+      // unconditional (clamped to the last token): a conditional load would
+      // make the slot a choice between old and new values, which the compiler
+      // resolves with a copy that waits for the load
+      fetch_token(s, min(t + kPrefetch, t_end - 1));
 
       float po0 = 0.0f, po1 = 0.0f;
       if constexpr (PERKEY) {
         // decay row by row, then retrieval, delta update and readout
-        if (decays) {
+        if (decays && live) {
 #pragma unroll
           for (int m = 0; m < RPL; ++m) {
             const float lg = RAW ? gate_log_decay(gr[m], A_log_r[m], dt_bias_r[m]) : gr[m];
             S[m] *= expf(lg);
           }
         }
-        float delta = vv;
+        float delta = live ? vv : 0.0f;  // a padded token leaves the state as it is
         if (deltas) {
           float pr0 = 0.0f, pr1 = 0.0f;
 #pragma unroll
@@ -236,9 +252,9 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
           }
         }
       } else {
-        const float alpha = decays ? readlane(blk_alpha, rel) : 1.0f;
+        const float alpha = (decays && live) ? readlane(blk_alpha, rel) : 1.0f;
         // retrieval against the decayed state: r = alpha * (S^T k)
-        float delta = vv;
+        float delta = live ? vv : 0.0f;  // a padded token leaves the state as it is
         if (deltas) {
           float pr0 = 0.0f, pr1 = 0.0f;
 #pragma unroll
@@ -261,10 +277,10 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
         }
       }
       const float o = group_sum<R>(po0 + po1) * scale;
-      if (og != nullptr && r == 0 && col_ok)
+      if (og != nullptr && r == 0 && col_ok && live)
         narrow_store(og + static_cast<size_t>(t) * v_stride + v_off, o);
       const int w = (t - t_begin) - hist_from;
-      if (W > 0 && w >= 0 && col_ok) {
+      if (W > 0 && w >= 0 && col_ok && live) {
 #pragma unroll
         for (int m = 0; m < RPL; ++m)
           if (row0 + m < p.d_k) history_slot(w)[static_cast<size_t>(row0 + m) * p.d_v + j] = S[m];
@@ -287,11 +303,13 @@ hipError_t launch_gates(const ScanParams& p, unsigned blocks, hipStream_t stream
   const bool per_key = p.gates.per_key && p.gates.decays;
   const bool plain = p.gates.decays && p.gates.deltas && p.window == 0;
   if (per_key)
-    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, true, true>), dim3(blocks), dim3(kWave), 0, stream, p);
+    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, true, true, false>), dim3(blocks), dim3(kWave), 0, stream, p);
+  else if (plain && p.d_k == DK)
+    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, false, true>), dim3(blocks), dim3(kWave), 0, stream, p);
   else if (plain)
-    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, false>), dim3(blocks), dim3(kWave), 0, stream, p);
+    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, false, false>), dim3(blocks), dim3(kWave), 0, stream, p);
   else
-    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, true>), dim3(blocks), dim3(kWave), 0, stream, p);
+    hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, true, false>), dim3(blocks), dim3(kWave), 0, stream, p);
   return hipGetLastError();
 }
 
