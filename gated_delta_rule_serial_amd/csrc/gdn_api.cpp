@@ -248,7 +248,7 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   const bool split = chunked && gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) &&
                      p.workspace != nullptr &&
                      p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
-  const int cols = split     ? gdn::split_columns_per_block(p.d_v)
+  const int cols = split     ? gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v)
                    : chunked ? gdn::chunked_columns_per_block(p.d_k, p.d_v)
                              : gdn::scan_columns_per_wave(p.d_k);
   sp.col_blocks = (p.d_v + cols - 1) / cols;

@@ -128,7 +128,7 @@ hipError_t launch_prefill_chunked(ScanParams p, int io_bf16, hipStream_t stream)
 // The chunked prefill in two passes (chunk-parallel preparation, then the
 // sequential state pass) through a caller-provided workspace.
 bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window);
-int split_columns_per_block(int d_v);
+int split_columns_per_block(int d_v, int units);
 size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v);
 hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t stream);
 

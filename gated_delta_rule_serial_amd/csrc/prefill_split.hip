@@ -43,16 +43,27 @@ constexpr double kLog2e = 1.4426950408889634;
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Shared operand fragments of the state pass, per (chunk, value head): W and
+// diag(gam) Q as 16 x 32 blocks (4 token tiles x DK / 32 key blocks), Kt^T
+// (DK / 16 key tiles x 2 token blocks) and the six lower blocks of M.  Each is
+// stored as the 64 lanes x 16 bytes one wave loads for a 16x16x32 MFMA, with
+// the contraction index of a block permuted so that lane group g holds
+// k = 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3: the order in which two
+// stacked accumulator tiles already hold the other operand (state rows, or
+// the tokens of D), so that operand never leaves the registers.
+__host__ __device__ constexpr int frags_w(int dk) { return 4 * (dk / 32); }
+__host__ __device__ constexpr int frags_total(int dk) { return 2 * frags_w(dk) + 2 * (dk / 16) + 6; }
+// M block (token tile tt, token block kb), kb <= tt / 2
+__host__ __device__ constexpr int m_frag(int tt, int kb) { return tt < 2 ? tt : 2 + 2 * (tt - 2) + kb; }
+
 // One (chunk, value head) record of the workspace.
 struct Rec {
-  size_t w, kt, m, u, g, bytes;
+  size_t frag, u, g, bytes;
   __host__ __device__ Rec(int dk, int dvp) {
-    w = 0;                                                  // W      [C][dk] bf16
-    kt = w + static_cast<size_t>(kC) * dk * 2;              // Kt^T   [dk][C] bf16
-    m = kt + static_cast<size_t>(dk) * kC * 2;              // M      [C][C] bf16
-    u = m + static_cast<size_t>(kC) * kC * 2;               // U      [4][dvp / 16][64 lanes][4] f32
-    g = u + static_cast<size_t>(kC) * dvp * 4;              // gam    [C] f32, then gam_last
-    bytes = align256(g + (kC + 4) * 4);
+    frag = 0;                                               // fragments [frags_total][64 lanes] x 16 B
+    u = frag + static_cast<size_t>(frags_total(dk)) * 1024;  // U      [4][dvp / 16][64 lanes][4] f32
+    g = u + static_cast<size_t>(kC) * dvp * 4;              // gam_last f32 (a 256-byte slot)
+    bytes = align256(g + 256);
   }
 };
 
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   constexpr int VPR = DK / 8;
   constexpr int KQ_IT = kC * VPR / kThreads;
   constexpr int VPV = DVP / 8;
-  constexpr int V_IT = kC * VPV / kThreads;
+  constexpr int V_IT = kC * VPV / kThreads;  // V rows are staged in token pairs: V_IT / 2 (pair, 8 columns) per thread
   static_assert(KQ_IT >= 1 && V_IT >= 1, "block shape");
   u32x4 rk[KQ_IT], rq[KQ_IT], rv[V_IT];
   float rg = 0.0f, rbt = 0.0f;  // wave 0: gate inputs of token (chunk start + lane)
@@ -194,8 +205,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     }
 #pragma unroll
     for (int it = 0; it < V_IT; ++it) {
-      const int v = tid + it * kThreads;
-      const int t = v / VPV, c8 = (v % VPV) * 8;
+      const int v = tid + (it >> 1) * kThreads;
+      const int t = 2 * (v % (kC / 2)) + (it & 1), c8 = (v / (kC / 2)) * 8;
       rv[it] = u32x4{0u, 0u, 0u, 0u};
       if (t < at.Lc && c8 < d_v)
         rv[it] = *reinterpret_cast<const u32x4*>(vg + static_cast<size_t>(at.t0 + t) * v_stride +
@@ -245,14 +256,19 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       *reinterpret_cast<u32x4*>(Ks + t * SK + c8) = rk[it];
       *reinterpret_cast<u32x4*>(Qs + t * SK + c8) = rq[it];
     }
+    // V^T from token pairs: one 4-byte word (tokens t, t + 1) per column; the
+    // 32 pairs of a wave fill 32 consecutive words and its two 8-column
+    // groups sit 32 banks apart, so the writes are free of bank conflicts
 #pragma unroll
-    for (int it = 0; it < V_IT; ++it) {
-      const int v = tid + it * kThreads;
-      const int t = v / VPV, c8 = (v % VPV) * 8;
+    for (int it = 0; it < V_IT; it += 2) {
+      const int v = tid + (it >> 1) * kThreads;
+      const int t = 2 * (v % (kC / 2)), c8 = (v / (kC / 2)) * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Vt[(c8 + e) * kSC + t] =
-            static_cast<bf16_t>((e & 1) ? (rv[it][e >> 1] >> 16) : (rv[it][e >> 1] & 0xffffu));
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = (e & 1) ? (rv[it][e >> 1] >> 16) : (rv[it][e >> 1] & 0xffffu);
+        const uint32_t b = (e & 1) ? (rv[it + 1][e >> 1] >> 16) : (rv[it + 1][e >> 1] & 0xffffu);
+        *reinterpret_cast<uint32_t*>(Vt + (c8 + e) * kSC + t) = a | (b << 16);
+      }
     }
     if (w == 0) {
       float g = 0.0f, b = 0.0f;
@@ -386,294 +402,323 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   }
   __syncthreads();
 
-  // ================= 5. W, Kt^T = (exp(G_last - G_t) K)^T, M and gam to the workspace
-  bf16_t* wg = reinterpret_cast<bf16_t*>(base + rec.w);
-  for (int v = tid; v < kC * VPR; v += kThreads) {
-    const int t = v / VPR, c8 = (v % VPR) * 8;
-    *reinterpret_cast<uint4*>(wg + t * DK + c8) = *reinterpret_cast<const uint4*>(Ws + t * SK + c8);
-  }
-  bf16_t* ktg = reinterpret_cast<bf16_t*>(base + rec.kt);
-  const double Glast = Gd[kC - 1];  // gates past the chunk's end are 0: G stays at its last value
-  for (int ix = tid; ix < DK * (kC / 8); ix += kThreads) {
-    const int i = ix / (kC / 8);
-    const int t8 = (ix % (kC / 8)) * 8;
-    uint32_t wv[4];
+  // ================= 5. operand fragments (W, diag(gam) Q, Kt^T, M) and gam_last to the workspace
+  {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int KB = DK / 32;
+    constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16), NF = frags_total(DK);
+    u32x4_t* fr = reinterpret_cast<u32x4_t*>(base + rec.frag);
+    const int g = lane >> 4, r = lane & 15;
+    const double Glast = Gd[kC - 1];  // gates past the chunk's end are 0: G stays at its last value
+    // k values of this lane's slots, relative to the block: 4 g + e (e < 4), 16 + 4 g + (e - 4)
+    auto slot_k = [&](int e) __attribute__((always_inline)) { return 4 * g + (e & 3) + 16 * (e >> 2); };
+    auto pick = [&](const bf16_t* row, int kb) __attribute__((always_inline)) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * g);
+      const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * g);
+      return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    };
+    auto scaled = [&](u32x4_t x, auto factor) __attribute__((always_inline)) {
+      u32x4_t y;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a0 = widen(KT[i * kSC + t8 + 2 * e]) * fast_exp2(static_cast<float>(Glast - Gd[t8 + 2 * e]));
-      const float a1 = widen(KT[i * kSC + t8 + 2 * e + 1]) * fast_exp2(static_cast<float>(Glast - Gd[t8 + 2 * e + 1]));
-      wv[e] = static_cast<uint32_t>(to_bf16(a0)) | (static_cast<uint32_t>(to_bf16(a1)) << 16);
+      for (int q = 0; q < 4; ++q) {
+        const float a0 = widen(static_cast<bf16_t>(x[q] & 0xffffu)) * factor(2 * q);
+        const float a1 = widen(static_cast<bf16_t>(x[q] >> 16)) * factor(2 * q + 1);
+        y[q] = static_cast<uint32_t>(to_bf16(a0)) | (static_cast<uint32_t>(to_bf16(a1)) << 16);
+      }
+      return y;
+    };
+    for (int f = w; f < NF; f += kWaves) {
+      u32x4_t piece;
+      if (f < FQ) {
+        piece = pick(Ws + (16 * (f / KB) + r) * SK, f % KB);
+      } else if (f < FK) {
+        const int t = 16 * ((f - FQ) / KB) + r;
+        const float gm = Gam[t];
+        piece = scaled(pick(Qs + t * SK, (f - FQ) % KB), [&](int) { return gm; });
+      } else if (f < FM) {
+        const int kb = (f - FK) & 1;
+        piece = scaled(pick(KT + (16 * ((f - FK) >> 1) + r) * kSC, kb), [&](int e) {
+          return fast_exp2(static_cast<float>(Glast - Gd[32 * kb + slot_k(e)]));
+        });
+      } else {
+        const int mf = f - FM;
+        const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
+        const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
+        piece = pick(Ms + (16 * tt + r) * kSC, kb);
+      }
+      fr[f * 64 + lane] = piece;
     }
-    *reinterpret_cast<uint4*>(ktg + i * kC + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-  }
-  bf16_t* mg = reinterpret_cast<bf16_t*>(base + rec.m);
-  for (int v = tid; v < kC * (kC / 8); v += kThreads) {
-    const int t = v / (kC / 8), s8 = (v % (kC / 8)) * 8;
-    *reinterpret_cast<uint4*>(mg + t * kC + s8) = *reinterpret_cast<const uint4*>(Ms + t * kSC + s8);
-  }
-  if (w == 0) {
-    float* gg = reinterpret_cast<float*>(base + rec.g);
-    gg[lane] = Gam[lane];
-    if (lane == 0) gg[kC] = Gam[kC - 1];
+    if (tid == 0) *reinterpret_cast<float*>(base + rec.g) = Gam[kC - 1];
   }
   __syncthreads();  // the LDS is restaged for the next item
   }
 }
 
 // ---------------------------------------------------------------- pass 2
-template <int DK, int NC>
-struct StateLds {
-  static constexpr int SK = DK + 8;
-  static constexpr int kWs = 0;                          // W      [C][SK] bf16
-  static constexpr int kQs = kWs + kC * SK * 2;          // Q      [C][SK] bf16
-  static constexpr int kKT = kQs + kC * SK * 2;          // Kt^T   [DK][SC] bf16
-  static constexpr int kMs = kKT + DK * kSC * 2;         // M      [C][SC] bf16
-  static constexpr int kSt = kMs + kC * kSC * 2;         // S^T    [NC][SK] bf16
-  static constexpr int kDt = kSt + NC * SK * 2;          // D^T    [NC][SC] bf16
-  static constexpr int kGam = kDt + NC * kSC * 2;        // gam    [C] f32
-  static constexpr int kOs = kGam + kC * 4;              // O      [8 waves][16][NC / 2 + 8] bf16
-  static constexpr int kBytes = kOs + kWaves * 16 * (NC / 2 + 8) * 2;
-  static_assert(kBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-};
+constexpr int kStateWaves = 4;
 
-// One workgroup of 8 waves per CU (the LDS holds one): two waves per SIMD may
-// use 256 registers each, which keeps the staging arrays in registers.
-template <typename IO, int DK, int NC, int DVT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void chunk_state_kernel(ScanParams p, const unsigned char* ws, size_t rec_bytes,
-                                                               const int32_t* cs) {
-  using L_ = StateLds<DK, NC>;
-  constexpr int SK = L_::SK;
-  constexpr int CT = NC / 16;                   // column tiles of the block
-  constexpr int CTW = CT / 2;                   // column tiles per wave in the (token, column) products
-  constexpr int STW = (DK / 16) * CT / kWaves;  // state tiles per wave
-  static_assert(CT % 2 == 0 && STW >= 1, "block shape");
-  static_assert(STW <= CT && CT % STW == 0, "a wave's state tiles lie in one row tile");
-  extern __shared__ __align__(16) unsigned char smem[];
-  bf16_t* Ws = reinterpret_cast<bf16_t*>(smem + L_::kWs);
-  bf16_t* Qs = reinterpret_cast<bf16_t*>(smem + L_::kQs);
-  bf16_t* KTs = reinterpret_cast<bf16_t*>(smem + L_::kKT);
-  bf16_t* Ms = reinterpret_cast<bf16_t*>(smem + L_::kMs);
-  bf16_t* St = reinterpret_cast<bf16_t*>(smem + L_::kSt);
-  bf16_t* Dt = reinterpret_cast<bf16_t*>(smem + L_::kDt);
-  float* Gam = reinterpret_cast<float*>(smem + L_::kGam);
-  constexpr int kSO = NC / 2 + 8;  // bf16 row stride of a wave's output block
+// Global and LDS address spaces, as the direct global-to-LDS load takes them.
+#define GDN_GLOBAL(ptr) ((const __attribute__((address_space(1))) void*)(ptr))
+#define GDN_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
+
+// One workgroup of four waves (one per SIMD) per (sequence, value head, block
+// of 64 SL columns).  Wave w owns state columns 16 SL w .. +16 SL - 1 for all
+// DK rows, as MFMA accumulators that never leave its registers: two stacked
+// accumulator tiles, packed to bf16, are directly the B operand of the next
+// products, because the prepared fragments carry the matching permutation of
+// the contraction index.  The fragments of chunk j + 1 travel straight from
+// the workspace into the second LDS buffer (global-to-LDS loads, no
+// registers) while chunk j computes, so a chunk costs one barrier.
+template <typename IO, int DK, int SL, int DVT>
+__global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_state_kernel(
+    ScanParams p, const unsigned char* ws, size_t rec_bytes, const int32_t* cs) {
+  constexpr int KB = DK / 32;   // key blocks of 32
+  constexpr int RT = DK / 16;   // state row tiles
+  constexpr int NC = kStateWaves * 16 * SL;
+  constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * RT, NF = frags_total(DK);
+  constexpr int STG = (NF + kStateWaves - 1) / kStateWaves;  // fragments loaded per wave
+  constexpr int kSO = 16 * SL;                                 // bf16 row stride of a wave's output block
+  constexpr int kUT = 4 * SL;                                  // U tiles of a wave
+  // two fragment buffers as distinct objects, so that loads into one are not
+  // mistaken for writes to the other
+  __shared__ __align__(16) bf16x8 frag0[NF * 64];
+  __shared__ __align__(16) bf16x8 frag1[NF * 64];
+  __shared__ __align__(16) f32x4 u_blk[kStateWaves * kUT * 64];   // each wave's U tiles of the current chunk
+  __shared__ __align__(16) float gl_blk[kStateWaves * 64];        // each wave's copy of gam_last
+  __shared__ __align__(16) bf16_t out_blk[kStateWaves * kC * kSO];  // each wave's output block
+  static_assert(sizeof(frag0) + sizeof(frag1) + sizeof(u_blk) + sizeof(gl_blk) + sizeof(out_blk) <= 160 * 1024,
+                "LDS budget of one gfx950 workgroup");
 
   const int tid = static_cast<int>(threadIdx.x);
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int rb = w & 3;
-  const int chalf = w >> 2;
-  bf16_t* Os = reinterpret_cast<bf16_t*>(smem + L_::kOs) + w * 16 * kSO;
-  int unit = static_cast<int>(blockIdx.x);
-  const int cb = unit % p.col_blocks;
-  unit /= p.col_blocks;
+  bf16_t* Os = out_blk + w * kC * kSO;
+  // blocks go round-robin over the 8 XCDs: the column blocks of one (sequence,
+  // head) unit are placed 8 apart, on one XCD, so they share its L2
+  const int xcd = static_cast<int>(blockIdx.x) % 8, r = static_cast<int>(blockIdx.x) / 8;
+  const int unit = (r / p.col_blocks) * 8 + xcd;
+  const int cb = r % p.col_blocks;
+  if (unit >= p.num_seqs * p.h_v) return;  // the grid is padded to whole rounds of 8 units
   const int h = unit % p.h_v;
   const int n = unit / p.h_v;
-  const int hq = h / p.ratio;
-  const int J0 = cb * NC;
   const int d_v = p.d_v;
   const int T = p.total_tokens;
   const int t_begin = seq_lo(p.cu, n, T);
   const int t_end = seq_hi(p.cu, n, T);
   const int c_first = cs[n];
   const int nchunks = (t_end - t_begin + kC - 1) / kC;
+  const int Jw = cb * NC + 16 * SL * w;  // first column of the wave
   bool has_state;
   const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
   const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(DK) * d_v;
   const Rec rec(DK, 16 * DVT);
 
-  // ---- state slice in accumulators: wave w owns tiles w*STW .. (row tile * CT + column tile)
-  f32x4 S[STW];
+  // ---- the wave's state slice: row tile ri, column tile sl
+  f32x4 S[RT][SL];
 #pragma unroll
-  for (int e = 0; e < STW; ++e) {
-    const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;
+  for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) {
+      const int col = Jw + 16 * sl + acc_col(lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * ri + acc_row(lane, i);
+        S[ri][sl][i] = (p.s0 != nullptr && has_state && col < d_v) ? p.s0[sbase + static_cast<size_t>(row) * d_v + col] : 0.0f;
+      }
+    }
+
+  IO* og = static_cast<IO*>(p.out);
+  const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
+  auto record = [&](int j) __attribute__((always_inline)) {
+    return ws + (static_cast<size_t>(c_first + j) * p.h_v + h) * rec_bytes;
+  };
+  // the shared fragments of chunk j into an LDS buffer, a quarter per wave;
+  // load_frag(e) issues the wave's e-th one
+  auto load_frag = [&](int j, bf16x8* dst, int e) __attribute__((always_inline)) {
+    const int f = w + kStateWaves * e;
+    if (f < NF)
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(record(j) + rec.frag + (static_cast<size_t>(f) * 64 + lane) * 16),
+                                       GDN_LDS(dst + f * 64), 16, 0, 0);
+  };
+  auto load_frags = [&](int j, bf16x8* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < STG; ++e) load_frag(j, dst, e);
+  };
+  // this wave's U tiles and gam_last of chunk j into its LDS blocks; load_u1(e)
+  // issues the e-th of the 4 SL + 1 loads
+  f32x4* Uw = u_blk + w * kUT * 64;
+  float* Gw = gl_blk + w * 64;
+  auto load_u1 = [&](int j, int e) __attribute__((always_inline)) {
+    if (e < kUT) {
+      const int tt = e / SL, sl = e % SL;
+      const int cj = min(Jw / 16 + sl, DVT - 1);  // column tile of the whole head (past d_v: U is 0 there anyway)
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(record(j) + rec.u + ((static_cast<size_t>(tt) * DVT + cj) * 64 + lane) * 16),
+                                       GDN_LDS(Uw + e * 64), 16, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(record(j) + rec.g + lane * 4), GDN_LDS(Gw), 4, 0, 0);
+    }
+  };
+  auto load_u = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e <= kUT; ++e) load_u1(j, e);
+  };
+  // swizzled output block: the 8-column piece pc of row t sits at piece pc ^ ((t / 4) % (2 SL))
+  auto out_at = [](int t, int c) __attribute__((always_inline)) {
+    return t * kSO + ((((c >> 3) ^ (t >> 2)) & (2 * SL - 1)) << 3) + (c & 7);
+  };
+  // the output block of chunk j (its scaled Y, kept in registers until no
+  // global-to-LDS load is in flight) through the wave's LDS block, in 16-byte rows
+  f32x4 Yp[4][SL];
+  auto store_out = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Os[out_at(16 * tt + acc_row(lane, i), 16 * sl + acc_col(lane))] = to_bf16(Yp[tt][sl][i]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    const int c0 = t_begin + j * kC;
+    const int Lc = min(kC, t_end - c0);
+    constexpr int VPRO = 2 * SL;  // 8-column pieces per row
+#pragma unroll
+    for (int it = 0; it < kC * VPRO / 64; ++it) {
+      const int v = lane + 64 * it;
+      const int t = v / VPRO, c8 = (v % VPRO) * 8;
+      if (t < Lc && Jw + c8 < d_v)
+        *reinterpret_cast<uint4*>(og + static_cast<size_t>(c0 + t) * v_stride + static_cast<size_t>(h) * d_v + Jw + c8) =
+            *reinterpret_cast<const uint4*>(Os + out_at(t, c8));
+    }
+  };
+  auto pack = [](f32x4 a, f32x4 b) __attribute__((always_inline)) {
+    bf16x8 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 16 * ri + acc_row(lane, i);
-      const int col = J0 + 16 * cj + acc_col(lane);
-      S[e][i] = (p.s0 != nullptr && has_state && col < d_v) ? p.s0[sbase + static_cast<size_t>(row) * d_v + col] : 0.0f;
+      r[i] = static_cast<__bf16>(a[i]);
+      r[4 + i] = static_cast<__bf16>(b[i]);
     }
-  }
-  auto publish_state = [&]() __attribute__((always_inline)) {  // S^T (bf16) for the next chunk's W S and Q S
-#pragma unroll
-    for (int e = 0; e < STW; ++e) {
-      const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;
-      const int row = 16 * ri + acc_row(lane, 0);
-      const int col = 16 * cj + acc_col(lane);
-      uint2 pk;
-      pk.x = static_cast<uint32_t>(to_bf16(S[e][0])) | (static_cast<uint32_t>(to_bf16(S[e][1])) << 16);
-      pk.y = static_cast<uint32_t>(to_bf16(S[e][2])) | (static_cast<uint32_t>(to_bf16(S[e][3])) << 16);
-      *reinterpret_cast<uint2*>(St + col * SK + row) = pk;
-    }
+    return r;
   };
-  publish_state();
-
-  const IO* qg = static_cast<const IO*>(p.q);
-  IO* og = static_cast<IO*>(p.out);
-  const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
-  const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
-
-  // ---- register staging of one chunk (loaded one chunk ahead)
-  constexpr int VPR = DK / 8;
-  constexpr int R_IT = kC * VPR / kThreads;      // W and Q rows, Kt^T
-  constexpr int M_IT = kC * (kC / 8) / kThreads;
-  static_assert(R_IT >= 1 && M_IT >= 1, "block shape");
-  // vector-typed staging arrays stay in registers (arrays of uint4 structs
-  // were left in scratch memory by the compiler)
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 rw[R_IT], rk[R_IT];
-  uint4 rq[R_IT], rm[M_IT];
-  f32x4 ru[CTW];
-  float rgam = 0.0f, rgl = 0.0f;
-  auto fetch = [&](int j) __attribute__((always_inline)) {
-    const unsigned char* base = ws + (static_cast<size_t>(c_first + j) * p.h_v + h) * rec_bytes;
-    const int c0 = t_begin + j * kC;
-    const int Lc = min(kC, t_end - c0);
-    const bf16_t* wg = reinterpret_cast<const bf16_t*>(base + rec.w);
-    const bf16_t* ktg = reinterpret_cast<const bf16_t*>(base + rec.kt);
-#pragma unroll
-    for (int it = 0; it < R_IT; ++it) {
-      const int v = tid + it * kThreads;
-      const int t = v / VPR, c8 = (v % VPR) * 8;
-      rw[it] = *reinterpret_cast<const u32x4*>(wg + t * DK + c8);
-      rk[it] = reinterpret_cast<const u32x4*>(ktg)[v];  // Kt^T is [DK][C]: 8 consecutive per item
-      rq[it] = make_uint4(0, 0, 0, 0);
-      if (t < Lc)
-        rq[it] = *reinterpret_cast<const uint4*>(qg + static_cast<size_t>(c0 + t) * qk_stride +
-                                                 static_cast<size_t>(hq) * DK + c8);
-    }
-    const bf16_t* mg = reinterpret_cast<const bf16_t*>(base + rec.m);
-#pragma unroll
-    for (int it = 0; it < M_IT; ++it) rm[it] = *reinterpret_cast<const uint4*>(mg + (tid + it * kThreads) * 8);
-    const float* ug = reinterpret_cast<const float*>(base + rec.u);
-#pragma unroll
-    for (int e = 0; e < CTW; ++e) {
-      const int cj = cb * CT + chalf * CTW + e;  // column tile of the whole head
-      ru[e] = cj < DVT ? *reinterpret_cast<const f32x4*>(ug + ((static_cast<size_t>(rb) * DVT + cj) * 64 + lane) * 4)
-                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    const float* gg = reinterpret_cast<const float*>(base + rec.g);
-    rgam = gg[lane];  // gam_t of token lane (used by wave 0)
-    rgl = gg[kC];     // gam_last
+  // fragments in the order a chunk consumes them: W and diag(gam) Q per
+  // (token tile, key block), then M, then Kt^T per (key tile, token block)
+  auto frag_at = [](int q) constexpr {
+    return q < 8 * KB ? ((q & 1) ? FQ : 0) + (q >> 1) : (q < 8 * KB + 6 ? FM + (q - 8 * KB) : FK + (q - 8 * KB - 6));
   };
-  if (nchunks > 0) fetch(0);
+  constexpr int P = 6;  // fragment reads in flight
 
-  for (int j = 0; j < nchunks; ++j) {
-    const int c0 = t_begin + j * kC;
-    const int Lc = min(kC, t_end - c0);
+  auto chunk = [&](int j, const bf16x8* cur, bf16x8* nxt) __attribute__((always_inline)) {
+    // the next chunk's loads are spread over this chunk's products (a burst
+    // would stall the wave on the memory pipeline while its MFMAs wait)
+    const bool more = j + 1 < nchunks;
+    if (og != nullptr && j > 0) store_out(j - 1);
 
-    // ================= a. stage W, Q, Kt^T, M, gam; U to registers; fetch the next chunk
+    const bf16x8* fb = cur + lane;
+    bf16x8 ring[P];
 #pragma unroll
-    for (int it = 0; it < R_IT; ++it) {
-      const int v = tid + it * kThreads;
-      const int t = v / VPR, c8 = (v % VPR) * 8;
-      *reinterpret_cast<u32x4*>(Ws + t * SK + c8) = rw[it];
-      *reinterpret_cast<uint4*>(Qs + t * SK + c8) = rq[it];
-      const int i = (v * 8) / kC, t8 = (v * 8) % kC;
-      *reinterpret_cast<u32x4*>(KTs + i * kSC + t8) = rk[it];
-    }
-#pragma unroll
-    for (int it = 0; it < M_IT; ++it) {
-      const int v = tid + it * kThreads;
-      const int t = (v * 8) / kC, s8 = (v * 8) % kC;
-      *reinterpret_cast<uint4*>(Ms + t * kSC + s8) = rm[it];
-    }
-    if (w == 0) Gam[lane] = rgam;
-    f32x4 U[CTW];
-#pragma unroll
-    for (int e = 0; e < CTW; ++e) U[e] = ru[e];
-    const float gam_last = rgl;
-    __syncthreads();
-    if (j + 1 < nchunks) fetch(j + 1);  // in flight while this chunk computes
+    for (int q = 0; q < P; ++q) ring[q] = fb[frag_at(q) * 64];
+    auto take = [&](int q) __attribute__((always_inline)) {
+      const bf16x8 v = ring[q % P];
+      if (q + P < NF) ring[q % P] = fb[frag_at(q + P) * 64];
+      return v;
+    };
 
-    // ================= b. X = W S, Y = Q S (shared B fragments); D = U - X
-    f32x4 X[CTW], Y[CTW];
+    // ================= a. X = W S and Y = diag(gam) Q S, the state (bf16) as B operand from registers
+    bf16x8 SB[KB][SL];
 #pragma unroll
-    for (int e = 0; e < CTW; ++e) X[e] = Y[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int kk = 0; kk < DK; kk += 32) {
-      const bf16x8 aw = frag(Ws + (16 * rb) * SK + kk, SK, lane);
-      const bf16x8 aq = frag(Qs + (16 * rb) * SK + kk, SK, lane);
+      for (int sl = 0; sl < SL; ++sl) SB[kb][sl] = pack(S[2 * kb][sl], S[2 * kb + 1][sl]);
+    f32x4 X[4][SL], Y[4][SL];
 #pragma unroll
-      for (int e = 0; e < CTW; ++e) {
-        const int cj = chalf * CTW + e;
-        const bf16x8 bs = frag(St + (16 * cj) * SK + kk, SK, lane);
-        X[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bs, X[e], 0, 0, 0);
-        Y[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bs, Y[e], 0, 0, 0);
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) X[tt][sl] = Y[tt][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int step = tt * KB + kb;  // 4 KB steps; the STG fragment loads are spread over them
+#pragma unroll
+        for (int e = (step * STG) / (4 * KB); e < ((step + 1) * STG) / (4 * KB); ++e)
+          if (more) load_frag(j + 1, nxt, e);
+        const bf16x8 aw = take(2 * step);
+        const bf16x8 aq = take(2 * step + 1);
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) {
+          X[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, SB[kb][sl], X[tt][sl], 0, 0, 0);
+          Y[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, SB[kb][sl], Y[tt][sl], 0, 0, 0);
+        }
       }
     }
+    // ================= b. D = U - X, packed as the B operand over tokens
+    bf16x8 DB[2][SL];
 #pragma unroll
-    for (int e = 0; e < CTW; ++e) {
-      const int cj = chalf * CTW + e;
-      const int t = 16 * rb + acc_row(lane, 0);
-      const int col = 16 * cj + acc_col(lane);
-      uint2 pk;
-      pk.x = static_cast<uint32_t>(to_bf16(U[e][0] - X[e][0])) | (static_cast<uint32_t>(to_bf16(U[e][1] - X[e][1])) << 16);
-      pk.y = static_cast<uint32_t>(to_bf16(U[e][2] - X[e][2])) | (static_cast<uint32_t>(to_bf16(U[e][3] - X[e][3])) << 16);
-      *reinterpret_cast<uint2*>(Dt + col * kSC + t) = pk;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Y[e][i] *= Gam[t + i];
-    }
-    __syncthreads();
+      for (int sl = 0; sl < SL; ++sl)
+        DB[kb][sl] = pack(Uw[((2 * kb) * SL + sl) * 64 + lane] - X[2 * kb][sl], Uw[((2 * kb + 1) * SL + sl) * 64 + lane] - X[2 * kb + 1][sl]);
+    const float gl = Gw[0];
 
-    // ================= c. O = scale (gam Q S + M D); the A fragment (M rows) is shared by the wave's tiles
-    const int kmax = (rb < 2) ? 32 : 64;  // M vanishes above the diagonal
-    for (int kk = 0; kk < kmax; kk += 32) {
-      const bf16x8 am = frag(Ms + (16 * rb) * kSC + kk, kSC, lane);
+    // ================= c. O = scale (Y + M D), stored at the start of the next chunk
 #pragma unroll
-      for (int e = 0; e < CTW; ++e) {
-        const int cj = chalf * CTW + e;
-        Y[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, frag(Dt + (16 * cj) * kSC + kk, kSC, lane), Y[e], 0, 0, 0);
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int kb = 0; kb <= tt / 2; ++kb) {
+        const bf16x8 am = take(8 * KB + m_frag(tt, kb));
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) Y[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, DB[kb][sl], Y[tt][sl], 0, 0, 0);
+      }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) Yp[tt][sl] = p.scale * Y[tt][sl];
+    // the wave's U and gam_last blocks are free again (their reads have
+    // returned): the next chunk's go in during the state update
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ================= d. S <- gam_last S + Kt^T D
+#pragma unroll
+    for (int ri = 0; ri < RT; ++ri) {
+#pragma unroll
+      for (int e = (ri * (kUT + 1)) / RT; e < ((ri + 1) * (kUT + 1)) / RT; ++e)
+        if (more) load_u1(j + 1, e);
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) S[ri][sl] = S[ri][sl] * gl;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ak = take(8 * KB + 6 + 2 * ri + kb);
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) S[ri][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, DB[kb][sl], S[ri][sl], 0, 0, 0);
       }
     }
-    // the wave's 16 x NC/2 output block goes through LDS and out in 16-byte rows
-    if (og != nullptr) {
-#pragma unroll
-      for (int e = 0; e < CTW; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Os[acc_row(lane, i) * kSO + 16 * e + acc_col(lane)] = to_bf16(p.scale * Y[e][i]);
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-      constexpr int VPRO = NC / 16;  // 8-element vectors per row of the block
-#pragma unroll
-      for (int it = 0; it < 16 * VPRO / 64; ++it) {
-        const int v = lane + 64 * it;
-        const int r = v / VPRO, c8 = (v % VPRO) * 8;
-        const int t = 16 * rb + r;
-        const int col = J0 + chalf * (NC / 2) + c8;
-        if (t < Lc && col < d_v)
-          *reinterpret_cast<uint4*>(og + static_cast<size_t>(c0 + t) * v_stride + static_cast<size_t>(h) * d_v + col) =
-              *reinterpret_cast<const uint4*>(Os + r * kSO + c8);
-      }
-    }
-    // ================= d. S <- gam_last S + Kt^T D; a wave's state tiles share one row tile (its A fragment)
-#pragma unroll
-    for (int e = 0; e < STW; ++e) S[e] = S[e] * gam_last;
-#pragma unroll
-    for (int kk = 0; kk < kC; kk += 32) {
-      const bf16x8 ak = frag(KTs + (16 * ((w * STW) / CT)) * kSC + kk, kSC, lane);
-#pragma unroll
-      for (int e = 0; e < STW; ++e) {
-        const int cj = (w * STW + e) % CT;
-        S[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, frag(Dt + (16 * cj) * kSC + kk, kSC, lane), S[e], 0, 0, 0);
-      }
-    }
-    publish_state();
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's share of the next buffer has landed
+    __syncthreads();                     // the next buffer is complete; this one may be refilled
+  };
+
+  if (nchunks > 0) {
+    load_frags(0, frag0);
+    load_u(0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
   }
+  __syncthreads();
+  for (int j = 0; j < nchunks; j += 2) {
+    chunk(j, frag0, frag1);
+    if (j + 1 < nchunks) chunk(j + 1, frag1, frag0);
+  }
+  if (og != nullptr && nchunks > 0) store_out(nchunks - 1);
 
   // ---- final state
   if (p.sN != nullptr && has_state) {
 #pragma unroll
-    for (int e = 0; e < STW; ++e) {
-      const int ri = (w * STW + e) / CT, cj = (w * STW + e) % CT;
+    for (int ri = 0; ri < RT; ++ri)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * ri + acc_row(lane, i);
-        const int col = J0 + 16 * cj + acc_col(lane);
-        if (col < d_v) p.sN[sbase + static_cast<size_t>(row) * d_v + col] = S[e][i];
+      for (int sl = 0; sl < SL; ++sl) {
+        const int col = Jw + 16 * sl + acc_col(lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * ri + acc_row(lane, i);
+          if (col < d_v) p.sN[sbase + static_cast<size_t>(row) * d_v + col] = S[ri][sl][i];
+        }
       }
-    }
   }
 }
 
@@ -686,9 +731,16 @@ hipError_t set_lds(K kern, int bytes, bool* configured) {
   return e;
 }
 
-int split_columns(int d_v) { return d_v > 64 ? 128 : 64; }
 
 // Persistent grid of the preparation pass: one workgroup per compute unit.
+int prep_workgroups();
+
+// Columns per state-pass workgroup: 128 (two per wave), or 64 when the
+// (sequence, head) units leave compute units idle and splitting fills them.
+int split_columns(int d_v, int units) {
+  return d_v > 64 && static_cast<int64_t>(units) * ((d_v + 63) / 64) > prep_workgroups() ? 128 : 64;
+}
+
 int prep_workgroups() {
   static int cus = 0;
   if (cus == 0) {
@@ -724,23 +776,13 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const unsigned blocks = static_cast<unsigned>(p.num_seqs) * p.h_v * p.col_blocks;
-  if (blocks == 0) return hipSuccess;
-  if (split_columns(p.d_v) == 128) {
-    static bool cfg = false;
-    constexpr int bytes = StateLds<DK, 128>::kBytes;
-    auto kern = chunk_state_kernel<IO, DK, 128, DVT>;
-    hipError_t e = set_lds(kern, bytes, &cfg);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs);
-  } else {
-    static bool cfg = false;
-    constexpr int bytes = StateLds<DK, 64>::kBytes;
-    auto kern = chunk_state_kernel<IO, DK, 64, DVT>;
-    hipError_t e = set_lds(kern, bytes, &cfg);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs);
-  }
+  const int units = p.num_seqs * p.h_v;
+  const unsigned blocks = static_cast<unsigned>((units + 7) / 8) * 8u * static_cast<unsigned>(p.col_blocks);
+  if (units == 0) return hipSuccess;
+  if (split_columns(p.d_v, units) == 128)
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, DVT>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
+  else
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 1, DVT>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
   return hipGetLastError();
 }
 
@@ -754,7 +796,7 @@ bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int w
   return chunked_supported(io_bf16, d_k, d_v, gates, window) && d_v <= 256;
 }
 
-int split_columns_per_block(int d_v) { return split_columns(d_v); }
+int split_columns_per_block(int d_v, int units) { return split_columns(d_v, units); }
 
 // Workspace: cs [N + 1] int32, info [chunk bound] int2, then the records.
 static size_t table_bytes(int num_seqs, int total_tokens) {

@@ -278,7 +278,8 @@ def test_prefill_workspace_size(lib):
     chunky = dict(io_dtype=gdn.GDN_BF16, d_k=128, d_v=128, h_qk=16, h_v=32)
     assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), 8, 33173, ctypes.byref(size)) == gdn.GDN_OK
     # the chunk table, then one record per (chunk, head) for ceil(T / 64) + N chunks
-    per_rec = 64 * 128 * 2 + 128 * 64 * 2 + 64 * 64 * 2 + 64 * 128 * 4 + 68 * 4
+    # operand fragments (W, diag(gam) Q: 16 each; Kt^T: 16; M: 6) of 1 KiB, U in f32, gam_last
+    per_rec = (16 + 16 + 16 + 6) * 1024 + 64 * 128 * 4 + 16
     per_rec = (per_rec + 255) // 256 * 256
     bound = 33173 // 64 + 1 + 8
     assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * per_rec
