@@ -232,6 +232,37 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// Inclusive prefix sum of a double over the 64 lanes of a wave, without LDS:
+// Hillis-Steele steps inside each 16-lane row (DPP row_shr 1, 2, 4, 8 on both
+// halves; lanes shifted in from outside the row read 0), then each row adds
+// the totals of the rows before it (read from lanes 15, 31, 47).
+template <int N>
+__device__ __forceinline__ double dpp_row_shr(double x) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0x110 + N, 0xF, 0xF, false));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), 0x110 + N, 0xF, 0xF, false));
+  return __builtin_bit_cast(double, static_cast<unsigned long long>(lo) | (static_cast<unsigned long long>(hi) << 32));
+}
+__device__ __forceinline__ double readlane(double x, int lane) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b), lane));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane));
+  return __builtin_bit_cast(double, static_cast<unsigned long long>(lo) | (static_cast<unsigned long long>(hi) << 32));
+}
+__device__ __forceinline__ double wave_prefix_sum(double x, int lane) {
+  x += dpp_row_shr<1>(x);
+  x += dpp_row_shr<2>(x);
+  x += dpp_row_shr<4>(x);
+  x += dpp_row_shr<8>(x);
+  const double r0 = readlane(x, 15), r1 = readlane(x, 31), r2 = readlane(x, 47);
+  const int row = lane >> 4;
+  double before = 0.0;
+  if (row >= 1) before += r0;
+  if (row >= 2) before += r1;
+  if (row >= 3) before += r2;
+  return x + before;
+}
+
 // x + (x of lane i ^ 16) and x + (x of lane i ^ 32) with the gfx950 lane
 // swaps (VALU, no LDS): v_permlane16_swap exchanges the odd 16-lane rows of
 // its first operand with the even rows of its second, v_permlane32_swap the

@@ -272,12 +272,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
         }
         g = fmaxf(g, kMinLogDecay);
       }
-      double G = static_cast<double>(g) * kLog2e;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(G, off, 64);
-        if (lane >= off) G += y;
-      }
+      const double G = wave_prefix_sum(static_cast<double>(g) * kLog2e, lane);
       Gd[lane] = G;
       Gam[lane] = fast_exp2(static_cast<float>(G));
       Bet[lane] = b;

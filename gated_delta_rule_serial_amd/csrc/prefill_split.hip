@@ -128,7 +128,7 @@ struct PrepLds {
 // and gates are loaded into registers while the current one computes.
 template <typename IO, int DK, int DVT, bool RAW>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
-                                                              const int32_t* cs, const int2* info, int items) {
+                                                              const int32_t* cs, const int2* __restrict__ info, int items) {
   using L_ = PrepLds<DK, DVT>;
   constexpr int SK = L_::SK;
   constexpr int DVP = L_::DVP;
@@ -176,9 +176,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     at.Lc = ci.y;
     return at;
   };
-  auto info_of = [&](int item) __attribute__((always_inline)) {
-    return item < n_items ? info[item / p.h_v] : make_int2(0, 0);
-  };
+  // unconditional (clamped) loads: a load under a condition becomes a choice
+  // between old and new values that the compiler settles with a copy waiting
+  // for the load, which would stall the wave right after the load is issued
+  auto info_of = [&](int item) __attribute__((always_inline)) { return info[min(item, n_items - 1) / p.h_v]; };
 
   // ---- register staging of one item (vector-typed, so that it stays in registers)
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -188,43 +189,42 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   constexpr int V_IT = kC * VPV / kThreads;  // V rows are staged in token pairs: V_IT / 2 (pair, 8 columns) per thread
   static_assert(KQ_IT >= 1 && V_IT >= 1, "block shape");
   u32x4 rk[KQ_IT], rq[KQ_IT], rv[V_IT];
-  float rg = 0.0f, rbt = 0.0f;  // wave 0: gate inputs of token (chunk start + lane)
+  // gate inputs of token (chunk start + lane) as raw 16-bit patterns, and the
+  // head's A_log, dt_bias: converted where they are used, so that no
+  // conversion waits for the loads right after they are issued
+  uint32_t rg = 0u, rbt = 0u;
+  float rAl = 0.0f, rdt = 0.0f;
   auto fetch = [&](const Where& at) __attribute__((always_inline)) {
     const int hq = at.h / p.ratio;
 #pragma unroll
     for (int it = 0; it < KQ_IT; ++it) {
       const int v = tid + it * kThreads;
-      const int t = v / VPR, c8 = (v % VPR) * 8;
-      rk[it] = u32x4{0u, 0u, 0u, 0u};
-      rq[it] = u32x4{0u, 0u, 0u, 0u};
-      if (t < at.Lc) {
-        const size_t off = static_cast<size_t>(at.t0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
-        rk[it] = *reinterpret_cast<const u32x4*>(kg + off);
-        rq[it] = *reinterpret_cast<const u32x4*>(qg + off);
-      }
+      const int t = min(v / VPR, at.Lc - 1), c8 = (v % VPR) * 8;  // rows past the chunk: zeroed when staged
+      const size_t off = static_cast<size_t>(at.t0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
+      rk[it] = *reinterpret_cast<const u32x4*>(kg + off);
+      rq[it] = *reinterpret_cast<const u32x4*>(qg + off);
     }
 #pragma unroll
     for (int it = 0; it < V_IT; ++it) {
       const int v = tid + (it >> 1) * kThreads;
-      const int t = 2 * (v % (kC / 2)) + (it & 1), c8 = (v / (kC / 2)) * 8;
-      rv[it] = u32x4{0u, 0u, 0u, 0u};
-      if (t < at.Lc && c8 < d_v)
-        rv[it] = *reinterpret_cast<const u32x4*>(vg + static_cast<size_t>(at.t0 + t) * v_stride +
-                                                 static_cast<size_t>(at.h) * d_v + c8);
+      // rows past the chunk and columns past d_v: clamped here, zeroed when staged
+      const int t = min(2 * (v % (kC / 2)) + (it & 1), at.Lc - 1), c8 = min((v / (kC / 2)) * 8, d_v - 8);
+      rv[it] = *reinterpret_cast<const u32x4*>(vg + static_cast<size_t>(at.t0 + t) * v_stride +
+                                               static_cast<size_t>(at.h) * d_v + c8);
     }
-    if (w == 0) {
-      rg = 0.0f;
-      rbt = 0.0f;
-      if (lane < at.Lc) {
-        const size_t gi = static_cast<size_t>(at.t0 + lane) * p.h_v + at.h;
-        const size_t bi = p.gates.beta_shared ? static_cast<size_t>(at.t0 + lane) : gi;
-        if constexpr (RAW) {
-          if (p.gates.decays) rg = widen(static_cast<const IO*>(p.gates.a)[gi]);
-          rbt = widen(static_cast<const IO*>(p.gates.b)[bi]);
-        } else {
-          if (p.gates.decays) rg = widen(static_cast<const IO*>(p.gates.g)[gi]);
-          rbt = widen(static_cast<const IO*>(p.gates.beta)[bi]);
-        }
+    {
+      // gate inputs of token (chunk start + lane), clamped into the chunk (wave 0
+      // uses them; every wave loads, so no wave keeps an old value)
+      const int tl = at.t0 + min(lane, max(at.Lc - 1, 0));
+      const size_t gi = static_cast<size_t>(tl) * p.h_v + at.h;
+      const size_t bi = p.gates.beta_shared ? static_cast<size_t>(tl) : gi;
+      const IO* bsrc = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
+      const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : bsrc;
+      rg = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : bi];
+      rbt = reinterpret_cast<const uint16_t*>(bsrc)[bi];
+      if constexpr (RAW) {
+        rAl = p.gates.A_log[at.h];
+        rdt = p.gates.dt_bias[at.h];
       }
     }
   };
@@ -253,8 +253,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     for (int it = 0; it < KQ_IT; ++it) {
       const int v = tid + it * kThreads;
       const int t = v / VPR, c8 = (v % VPR) * 8;
-      *reinterpret_cast<u32x4*>(Ks + t * SK + c8) = rk[it];
-      *reinterpret_cast<u32x4*>(Qs + t * SK + c8) = rq[it];
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(Ks + t * SK + c8) = t < Lc ? rk[it] : zero;
+      *reinterpret_cast<u32x4*>(Qs + t * SK + c8) = t < Lc ? rq[it] : zero;
     }
     // V^T from token pairs: one 4-byte word (tokens t, t + 1) per column; the
     // 32 pairs of a wave fill 32 consecutive words and its two 8-column
@@ -263,10 +264,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     for (int it = 0; it < V_IT; it += 2) {
       const int v = tid + (it >> 1) * kThreads;
       const int t = 2 * (v % (kC / 2)), c8 = (v / (kC / 2)) * 8;
+      const bool col_ok = c8 < d_v;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (e & 1) ? (rv[it][e >> 1] >> 16) : (rv[it][e >> 1] & 0xffffu);
-        const uint32_t b = (e & 1) ? (rv[it + 1][e >> 1] >> 16) : (rv[it + 1][e >> 1] & 0xffffu);
+        const uint32_t a = (col_ok && t < Lc) ? ((e & 1) ? (rv[it][e >> 1] >> 16) : (rv[it][e >> 1] & 0xffffu)) : 0u;
+        const uint32_t b = (col_ok && t + 1 < Lc) ? ((e & 1) ? (rv[it + 1][e >> 1] >> 16) : (rv[it + 1][e >> 1] & 0xffffu)) : 0u;
         *reinterpret_cast<uint32_t*>(Vt + (c8 + e) * kSC + t) = a | (b << 16);
       }
     }
@@ -274,30 +276,18 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       float g = 0.0f, b = 0.0f;
       if (lane < Lc) {
         if constexpr (RAW) {
-          g = p.gates.decays ? gate_log_decay(rg, p.gates.A_log[h], p.gates.dt_bias[h]) : 0.0f;
-          b = gate_sigmoid(rbt);
+          g = p.gates.decays ? gate_log_decay(widen_bits16<IO>(rg), rAl, rdt) : 0.0f;
+          b = gate_sigmoid(widen_bits16<IO>(rbt));
         } else {
-          g = rg;
-          b = rbt;
+          g = p.gates.decays ? widen_bits16<IO>(rg) : 0.0f;
+          b = widen_bits16<IO>(rbt);
         }
         g = fmaxf(g, kMinLogDecay);
       }
-      double G = static_cast<double>(g) * kLog2e;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(G, off, 64);
-        if (lane >= off) G += y;
-      }
+      const double G = wave_prefix_sum(static_cast<double>(g) * kLog2e, lane);
       Gd[lane] = G;
       Gam[lane] = fast_exp2(static_cast<float>(G));
       Bet[lane] = b;
-    }
-    // the next item's inputs, in flight while this one computes
-    const int next = item + static_cast<int>(gridDim.x);
-    if (next < n_items) {
-      at = locate(next, next_info);
-      fetch(at);
-      next_info = info_of(next + static_cast<int>(gridDim.x));
     }
     __syncthreads();
 
@@ -377,6 +367,17 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     Tpp[t * kSC + s2] = to_bf16(tv * bs);
   }
   __syncthreads();
+
+  // the next item's inputs, in flight while this one finishes: issued here,
+  // where the memory pipeline is idle, ahead of this item's workspace stores
+  {
+    const int next = item + static_cast<int>(gridDim.x);
+    if (next < n_items) {
+      at = locate(next, next_info);
+      fetch(at);
+      next_info = info_of(next + static_cast<int>(gridDim.x));
+    }
+  }
 
   // ================= 4. W = T' K (-> LDS, over K), U = T'' V (-> workspace, tile order)
   const int kmax = (rb < 2) ? 32 : 64;  // T' and T'' vanish above the diagonal
