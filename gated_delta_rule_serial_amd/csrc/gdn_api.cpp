@@ -250,7 +250,7 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
                      p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
   const int cols = split     ? gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v)
                    : chunked ? gdn::chunked_columns_per_block(p.d_k, p.d_v)
-                             : gdn::scan_columns_per_wave(p.d_k);
+                             : gdn::scan_columns_per_wave(sp);
   sp.col_blocks = (p.d_v + cols - 1) / cols;
   const uint64_t blocks = static_cast<uint64_t>(num_seqs) * p.h_v * sp.col_blocks;
   if (blocks > 0x7fffffffull)

@@ -282,6 +282,57 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return a + b;
 }
 
+// Two independent sums over all 64 lanes, interleaved step by step so that
+// each chain's dependent DPP and lane-swap steps fill the other's hazard
+// slots; every lane receives both sums.
+__device__ __forceinline__ void wave_sum2(float& x, float& y) {
+  x += dpp<kQuadSwap1>(x);
+  y += dpp<kQuadSwap1>(y);
+  x += dpp<kQuadSwap2>(x);
+  y += dpp<kQuadSwap2>(y);
+  x += dpp<kRowHalfMirror>(x);
+  y += dpp<kRowHalfMirror>(y);
+  x += dpp<kRowMirror>(x);
+  y += dpp<kRowMirror>(y);
+  float x1 = x, x2 = x, y1 = y, y2 = y;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\ts_nop 1"
+               : "+v"(x1), "+v"(x2), "+v"(y1), "+v"(y2));
+  x = x1 + x2;
+  y = y1 + y2;
+  x1 = x2 = x;
+  y1 = y2 = y;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\ts_nop 1"
+               : "+v"(x1), "+v"(x2), "+v"(y1), "+v"(y2));
+  x = x1 + x2;
+  y = y1 + y2;
+}
+
+// Two independent sums over aligned groups of G = 16, 32 or 64 lanes,
+// interleaved as in wave_sum2.
+template <int G>
+__device__ __forceinline__ void group_sum2(float& x, float& y) {
+  static_assert(G == 16 || G == 32 || G == 64, "group_sum2 takes groups of 16, 32 or 64 lanes");
+  if constexpr (G == 64) {
+    wave_sum2(x, y);
+  } else {
+    x += dpp<kQuadSwap1>(x);
+    y += dpp<kQuadSwap1>(y);
+    x += dpp<kQuadSwap2>(x);
+    y += dpp<kQuadSwap2>(y);
+    x += dpp<kRowHalfMirror>(x);
+    y += dpp<kRowHalfMirror>(y);
+    x += dpp<kRowMirror>(x);
+    y += dpp<kRowMirror>(y);
+    if constexpr (G == 32) {
+      float x1 = x, x2 = x, y1 = y, y2 = y;
+      asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\ts_nop 1"
+                   : "+v"(x1), "+v"(x2), "+v"(y1), "+v"(y2));
+      x = x1 + x2;
+      y = y1 + y2;
+    }
+  }
+}
+
 // Sum over aligned groups of G consecutive lanes (G = 1, 2, 4, 8, 16, 32,
 // 64); every lane of a group receives the group's sum.  Every lane of the
 // wave must be active.

@@ -298,11 +298,221 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   }
 }
 
+// The plain gated delta rule at d_k = 256 (the widest head): CPW state
+// columns per wave, R = 64 / CPW lanes per column, RPL = 256 / R rows per
+// lane.  Against scan_kernel:
+//   * the readout reduction of token t and the retrieval reduction of token
+//     t + 1 (both read the state after token t) run interleaved, so the
+//     dependent steps of one fill the other's hazard slots;
+//   * q/k/v addresses are wave-uniform bases advanced token by token plus a
+//     fixed lane offset, with no per-token 64-bit products;
+//   * whole 64-token blocks run without bounds checks; the last block or two
+//     run a guarded copy, eight tokens at a time;
+//   * a block's 64 outputs of a column leave in one store, lane u holding
+//     token u's.
+template <int CPW>
+struct WideShape {
+  static constexpr int R = kWave / CPW;   // lanes per column
+  static constexpr int RPL = 256 / R;     // rows per lane
+};
+constexpr int kWideColumns = 2;  // columns per wave of the wide scan
+
+template <typename IO, bool RAW, int CPW>
+__global__ __launch_bounds__(kWave) void scan_wide_kernel(ScanParams p) {
+  constexpr int R = WideShape<CPW>::R;
+  constexpr int RPL = WideShape<CPW>::RPL;
+  constexpr int P = 16;  // tokens of q/k/v in flight (ring slots)
+  const int lane = static_cast<int>(threadIdx.x);
+  const int c = lane / R;  // column within the wave
+  // blocks go round-robin over the 8 XCDs: the column blocks of one (sequence,
+  // head) unit are placed 8 apart, on one XCD, so its q/k rows come from that
+  // XCD's L2 for all of them
+  const int xcd = static_cast<int>(blockIdx.x) % 8, rr = static_cast<int>(blockIdx.x) / 8;
+  const int unit = (rr / p.col_blocks) * 8 + xcd;
+  const int cb = rr % p.col_blocks;
+  if (unit >= p.num_seqs * p.h_v) return;  // the grid is padded to whole rounds of 8 units
+  const int h = unit % p.h_v;
+  const int n = unit / p.h_v;
+  const int hq = h / p.ratio;
+  const int j = cb * CPW + c;
+  const bool col_ok = j < p.d_v;
+  const int row0 = (lane % R) * RPL;
+  const int t_begin = p.cu[n];
+  const int t_end = p.cu[n + 1];
+
+  bool has_state;
+  const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
+  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(256) * p.d_v;
+  float S[RPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m)
+    S[m] = (p.s0 != nullptr && has_state && col_ok) ? p.s0[sbase + static_cast<size_t>(row0 + m) * p.d_v + j] : 0.0f;
+
+  if (t_end > t_begin) {
+    const IO* __restrict__ qg = static_cast<const IO*>(p.q);
+    const IO* __restrict__ kg = static_cast<const IO*>(p.k);
+    const IO* __restrict__ vg = static_cast<const IO*>(p.v);
+    IO* __restrict__ og = static_cast<IO*>(p.out);
+    const size_t qk_stride = static_cast<size_t>(p.h_qk) * 256;
+    const size_t v_stride = static_cast<size_t>(p.h_v) * p.d_v;
+    const IO* kbase = kg + static_cast<size_t>(hq) * 256;
+    const IO* qbase = qg + static_cast<size_t>(hq) * 256;
+    const IO* vbase = vg + static_cast<size_t>(h) * p.d_v + cb * CPW;  // + the lane's column
+    const int vcol = col_ok ? c : 0;
+    const float scale = p.scale;
+
+    // gates: lane l of a block holds token blk + l (loaded clamped one block ahead)
+    const IO* __restrict__ ga = static_cast<const IO*>(RAW ? p.gates.a : p.gates.g);
+    const IO* __restrict__ gb = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
+    const float A_log = RAW ? p.gates.A_log[h] : 0.0f;
+    const float dt_bias = RAW ? p.gates.dt_bias[h] : 0.0f;
+    RawScalar<IO> next_ga, next_gb;
+    auto fetch_gate_block = [&](int blk) __attribute__((always_inline)) {
+      const int t = min(blk + lane, t_end - 1);
+      next_ga.load(ga + static_cast<size_t>(t) * p.h_v + h);
+      next_gb.load(gb + (p.gates.beta_shared ? static_cast<size_t>(t) : static_cast<size_t>(t) * p.h_v + h));
+    };
+    float blk_alpha = 1.0f, blk_beta = 0.0f;
+    auto open_block = [&](int blk) __attribute__((always_inline)) {
+      if constexpr (RAW) {
+        blk_alpha = expf(gate_log_decay(next_ga.value(), A_log, dt_bias));
+        blk_beta = gate_sigmoid(next_gb.value());
+      } else {
+        blk_alpha = expf(next_ga.value());
+        blk_beta = next_gb.value();
+      }
+      fetch_gate_block(blk + kWave);
+    };
+
+    // q/k/v ring: slot (t - t_begin) % P holds token t
+    RawSlice<IO, RPL> ring_k[P], ring_q[P];
+    RawScalar<IO> ring_v[P];
+    auto load_token = [&](int s, int t) __attribute__((always_inline)) {
+      ring_k[s].load(kbase + static_cast<size_t>(t) * qk_stride + row0);
+      ring_q[s].load(qbase + static_cast<size_t>(t) * qk_stride + row0);
+      ring_v[s].load(vbase + static_cast<size_t>(t) * v_stride + vcol);
+    };
+    fetch_gate_block(t_begin);
+#pragma unroll
+    for (int s = 0; s < P; ++s) load_token(s, min(t_begin + s, t_end - 1));
+
+    // two-chain partial dot product of the lane's rows
+    auto dot = [&](const float* x) __attribute__((always_inline)) {
+      float a = S[0] * x[0], b = S[1] * x[1];
+#pragma unroll
+      for (int m = 2; m < RPL; m += 2) {
+        a = fmaf(S[m], x[m], a);
+        b = fmaf(S[m + 1], x[m + 1], b);
+      }
+      return a + b;
+    };
+    // retrieval of the first token
+    float rcur;
+    {
+      float kf[RPL];
+      ring_k[0].widen_to(kf);
+      rcur = group_sum<R>(dot(kf));
+    }
+    float o_acc[CPW];  // column c, lane u: output of token blk + u
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) o_acc[cc] = 0.0f;
+
+    // one token: update with rcur, then the readout of t and the retrieval of t + 1
+    auto token = [&](int s, int rel, bool live) __attribute__((always_inline)) {
+      const float beta = live ? readlane(blk_beta, rel) : 0.0f;
+      const float alpha = live ? readlane(blk_alpha, rel) : 1.0f;
+      float kf[RPL], qf[RPL], kn[RPL];
+      ring_k[s].widen_to(kf);
+      ring_q[s].widen_to(qf);
+      const float vv = ring_v[s].value();
+      const float delta = live ? beta * (vv - alpha * rcur) : 0.0f;
+#pragma unroll
+      for (int m = 0; m < RPL; ++m) S[m] = fmaf(S[m], alpha, kf[m] * delta);
+      ring_k[(s + 1) % P].widen_to(kn);
+      float po = dot(qf), pn = dot(kn);
+      group_sum2<R>(po, pn);
+      // the column sums into lane rel of the output registers (read first:
+      // a lane read inside the select would make it a branch)
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) {
+        const float val = readlane(po, cc * R) * scale;
+        o_acc[cc] = (lane == rel) ? val : o_acc[cc];
+      }
+      rcur = pn;
+    };
+    auto store_block = [&](int blk) __attribute__((always_inline)) {
+      if (og != nullptr && blk + lane < t_end) {
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc)
+          if (cb * CPW + cc < p.d_v)
+            narrow_store(og + static_cast<size_t>(blk + lane) * v_stride + static_cast<size_t>(h) * p.d_v + cb * CPW + cc,
+                         o_acc[cc]);
+      }
+    };
+
+    int blk = t_begin;
+    // ---- whole blocks: every token and every prefetch (t + P) lies inside the sequence
+    {
+      // wave-uniform token bases; the lane's rows and column are fixed offsets from them
+      const IO* pk = kbase + static_cast<size_t>(t_begin + P) * qk_stride;
+      const IO* pq = qbase + static_cast<size_t>(t_begin + P) * qk_stride;
+      const IO* pv = vbase + static_cast<size_t>(t_begin + P) * v_stride;
+      for (; blk + kWave + P <= t_end; blk += kWave) {
+        open_block(blk);
+        // eight tokens per iteration (one turn of the ring): a short loop body
+        // stays in the instruction cache
+        for (int g8 = 0; g8 < kWave; g8 += P) {
+#pragma unroll
+          for (int u = 0; u < P; ++u) {
+            token(u, g8 + u, true);
+            // the slot just consumed takes token t + P
+            ring_k[u].load(pk + row0);
+            ring_q[u].load(pq + row0);
+            ring_v[u].load(pv + vcol);
+            pk += qk_stride;
+            pq += qk_stride;
+            pv += v_stride;
+          }
+        }
+        store_block(blk);
+      }
+    }
+    // ---- the rest, eight tokens at a time: padded tokens leave the state
+    //      as it is, prefetches are clamped to the last token
+    for (; blk < t_end; blk += kWave) {
+      open_block(blk);
+      for (int g8 = 0; g8 < kWave && blk + g8 < t_end; g8 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+          const int t = blk + g8 + u;
+          token(u, g8 + u, t < t_end);
+          load_token(u, min(t + P, t_end - 1));
+        }
+      }
+      store_block(blk);
+    }
+  }
+
+  if (p.sN != nullptr && has_state && col_ok) {
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) p.sN[sbase + static_cast<size_t>(row0 + m) * p.d_v + j] = S[m];
+  }
+}
+
+// Whether a launch takes the wide scan (the plain rule at d_k = 256).
+bool wide_scan(const ScanParams& p) {
+  const bool per_key = p.gates.per_key && p.gates.decays;
+  const bool plain = p.gates.decays && p.gates.deltas && p.window == 0;
+  return p.d_k == 256 && plain && !per_key;
+}
+
 template <typename IO, int DK, bool RAW>
 hipError_t launch_gates(const ScanParams& p, unsigned blocks, hipStream_t stream) {
   const bool per_key = p.gates.per_key && p.gates.decays;
   const bool plain = p.gates.decays && p.gates.deltas && p.window == 0;
-  if (per_key)
+  if (DK == 256 && wide_scan(p))
+    hipLaunchKernelGGL((scan_wide_kernel<IO, RAW, kWideColumns>), dim3(blocks), dim3(kWave), 0, stream, p);
+  else if (per_key)
     hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, true, true, false>), dim3(blocks), dim3(kWave), 0, stream, p);
   else if (plain && p.d_k == DK)
     hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, false, true>), dim3(blocks), dim3(kWave), 0, stream, p);
@@ -315,7 +525,10 @@ hipError_t launch_gates(const ScanParams& p, unsigned blocks, hipStream_t stream
 
 template <typename IO, int DK>
 hipError_t launch_dk(const ScanParams& p, hipStream_t stream) {
-  const unsigned blocks = static_cast<unsigned>(p.num_seqs) * p.h_v * p.col_blocks;
+  const int units = p.num_seqs * p.h_v;
+  if (units == 0) return hipSuccess;
+  const unsigned blocks = (DK == 256 && wide_scan(p)) ? static_cast<unsigned>((units + 7) / 8) * 8u * p.col_blocks
+                                                       : static_cast<unsigned>(units) * p.col_blocks;
   if (blocks == 0) return hipSuccess;
   return p.gates.raw ? launch_gates<IO, DK, true>(p, blocks, stream) : launch_gates<IO, DK, false>(p, blocks, stream);
 }
@@ -331,7 +544,9 @@ hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int scan_columns_per_wave(int d_k) {
+int scan_columns_per_wave(const ScanParams& p) {
+  const int d_k = p.d_k;
+  if (wide_scan(p)) return kWideColumns;
   if (d_k <= 16) return kWave / ScanShape<16>::R;
   if (d_k <= 32) return kWave / ScanShape<32>::R;
   if (d_k <= 64) return kWave / ScanShape<64>::R;
