@@ -188,49 +188,48 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
   constexpr int VPR = DK / 8;                              // 8-element vectors per K/Q row
   constexpr int KQ_IT = kC * VPR / kThreads;               // vectors per thread
   constexpr int VPV = NC / 8;                              // 8-element vectors per V row
-  constexpr int V_IT = (kC * VPV + kThreads - 1) / kThreads;
+  // V rows are staged in token pairs: (pair, 8 columns) items, two rows each
+  constexpr int V_PAIRS = (kC / 2) * VPV;
+  constexpr int V_IT = (V_PAIRS + kThreads - 1) / kThreads;
   static_assert(KQ_IT >= 1, "block shape");
-  uint4 rk[KQ_IT], rq[KQ_IT], rv[V_IT];
-  float rg = 0.0f, rb_ = 0.0f;  // wave 0: raw gate inputs of token (chunk start + lane)
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 rk[KQ_IT], rq[KQ_IT], rv[2 * V_IT];
+  // gate inputs of token (chunk start + lane) as raw 16-bit patterns, widened
+  // where they are used
+  uint32_t rg = 0u, rb_ = 0u;
+  // Unconditional (clamped) loads: a load under a condition becomes a choice
+  // between old and new values that the compiler settles with a copy waiting
+  // for the load right after it is issued.  Rows past the chunk and columns
+  // past d_v are zeroed when staged.
   auto fetch = [&](int c0) {
     const int Ln = (t_end - c0) < kC ? (t_end - c0) : kC;
 #pragma unroll
     for (int it = 0; it < KQ_IT; ++it) {
       const int v = tid + it * kThreads;
-      const int t = v / VPR;
+      const int t = min(v / VPR, Ln - 1);
       const int c8 = (v % VPR) * 8;
-      rk[it] = make_uint4(0, 0, 0, 0);
-      rq[it] = make_uint4(0, 0, 0, 0);
-      if (t < Ln) {
-        const size_t off = static_cast<size_t>(c0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
-        rk[it] = *reinterpret_cast<const uint4*>(kg + off);
-        rq[it] = *reinterpret_cast<const uint4*>(qg + off);
-      }
+      const size_t off = static_cast<size_t>(c0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
+      rk[it] = *reinterpret_cast<const u32x4*>(kg + off);
+      rq[it] = *reinterpret_cast<const u32x4*>(qg + off);
     }
 #pragma unroll
     for (int it = 0; it < V_IT; ++it) {
-      const int v = tid + it * kThreads;
-      const int t = v / VPV;
-      const int c8 = (v % VPV) * 8;
-      rv[it] = make_uint4(0, 0, 0, 0);
-      if (v < kC * VPV && t < Ln && J0 + c8 < d_v)
-        rv[it] = *reinterpret_cast<const uint4*>(vg + static_cast<size_t>(c0 + t) * v_stride +
-                                                 static_cast<size_t>(h) * d_v + J0 + c8);
+      const int v = min(tid + it * kThreads, V_PAIRS - 1);
+      const int t = 2 * (v % (kC / 2));
+      const int col = min(J0 + (v / (kC / 2)) * 8, d_v - 8);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        rv[2 * it + hh] = *reinterpret_cast<const u32x4*>(vg + static_cast<size_t>(c0 + min(t + hh, Ln - 1)) * v_stride +
+                                                         static_cast<size_t>(h) * d_v + col);
     }
-    if (w == 0) {
-      rg = 0.0f;
-      rb_ = 0.0f;
-      if (lane < Ln) {
-        const size_t gi = static_cast<size_t>(c0 + lane) * p.h_v + h;
-        const size_t bi = p.gates.beta_shared ? static_cast<size_t>(c0 + lane) : gi;
-        if constexpr (RAW) {
-          if (p.gates.decays) rg = widen(static_cast<const IO*>(p.gates.a)[gi]);
-          rb_ = widen(static_cast<const IO*>(p.gates.b)[bi]);
-        } else {
-          if (p.gates.decays) rg = widen(static_cast<const IO*>(p.gates.g)[gi]);
-          rb_ = widen(static_cast<const IO*>(p.gates.beta)[bi]);
-        }
-      }
+    {
+      const int tl = c0 + min(lane, Ln - 1);
+      const size_t gi = static_cast<size_t>(tl) * p.h_v + h;
+      const size_t bi = p.gates.beta_shared ? static_cast<size_t>(tl) : gi;
+      const IO* bsrc = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
+      const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : bsrc;
+      rg = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : bi];
+      rb_ = reinterpret_cast<const uint16_t*>(bsrc)[bi];
     }
   };
   if (t_begin < t_end) fetch(t_begin);
@@ -244,19 +243,25 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       const int v = tid + it * kThreads;
       const int t = v / VPR;
       const int c8 = (v % VPR) * 8;
-      *reinterpret_cast<uint4*>(Ks + t * SK + c8) = rk[it];
-      *reinterpret_cast<uint4*>(Qs + t * SK + c8) = rq[it];
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(Ks + t * SK + c8) = t < L ? rk[it] : zero;
+      *reinterpret_cast<u32x4*>(Qs + t * SK + c8) = t < L ? rq[it] : zero;
     }
+    // V^T from token pairs: one 4-byte word (tokens t, t + 1) per column; the
+    // 32 pairs of a wave fill 32 consecutive words and its two 8-column groups
+    // sit 32 banks apart, so the writes are free of bank conflicts
 #pragma unroll
     for (int it = 0; it < V_IT; ++it) {
       const int v = tid + it * kThreads;
-      if (v < kC * VPV) {
-        const int t = v / VPV;
-        const int c8 = (v % VPV) * 8;
-        const uint32_t vw[4] = {rv[it].x, rv[it].y, rv[it].z, rv[it].w};
+      if (v < V_PAIRS) {
+        const int t = 2 * (v % (kC / 2)), c8 = (v / (kC / 2)) * 8;
+        const bool col_ok = J0 + c8 < d_v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          Vt[(c8 + e) * kSC + t] = static_cast<bf16_t>((e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu));
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t a = (col_ok && t < L) ? ((e & 1) ? (rv[2 * it][e >> 1] >> 16) : (rv[2 * it][e >> 1] & 0xffffu)) : 0u;
+          const uint32_t b = (col_ok && t + 1 < L) ? ((e & 1) ? (rv[2 * it + 1][e >> 1] >> 16) : (rv[2 * it + 1][e >> 1] & 0xffffu)) : 0u;
+          *reinterpret_cast<uint32_t*>(Vt + (c8 + e) * kSC + t) = a | (b << 16);
+        }
       }
     }
     // gates and the in-chunk prefix sum of the log-decay, in log2 units (wave 0, lane = token)
@@ -264,11 +269,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       float g = 0.0f, b = 0.0f;
       if (lane < L) {
         if constexpr (RAW) {
-          g = p.gates.decays ? gate_log_decay(rg, A_log, dt_bias) : 0.0f;
-          b = gate_sigmoid(rb_);
+          g = p.gates.decays ? gate_log_decay(widen_bits16<IO>(rg), A_log, dt_bias) : 0.0f;
+          b = gate_sigmoid(widen_bits16<IO>(rb_));
         } else {
-          g = rg;
-          b = rb_;
+          g = p.gates.decays ? widen_bits16<IO>(rg) : 0.0f;
+          b = widen_bits16<IO>(rb_);
         }
         g = fmaxf(g, kMinLogDecay);
       }

@@ -84,6 +84,34 @@ def test_prefill_geometry(geom, raw):
     check(fin, rf, TOL[dt], "final state")
 
 
+# ------------------------------------------------------------------ the d_k = 256 wide scan
+# The plain rule at d_k = 256 runs its own kernel: two columns per wave, whole
+# 64-token blocks unguarded while the 16-token ring stays inside the sequence
+# (from 64 + 16 = 80 tokens on), a guarded tail in groups of 16.  Lengths
+# around those edges, an odd d_v (the second column of the last wave is
+# padding), every I/O dtype, precomputed and raw gates.
+WIDE_CASES = [
+    (torch.float32, 255, [1, 15, 16, 79, 80, 81, 200]),
+    (torch.bfloat16, 256, [81, 145, 0, 17]),
+    (torch.float16, 33, [96, 97, 5]),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"dv{c[1]}_{str(c[0])[6:]}")
+@pytest.mark.parametrize("raw", [False, True], ids=["gates", "rawgates"])
+def test_wide_scan_blocks_and_tails(case, raw):
+    dt, d_v, lens = case
+    shape = _shape("wide_prefill_t32768_d256", h_qk=2, h_v=4, d_v=d_v, io_dtype=dt, init_state=True,
+                   gate_mode="raw" if raw else "precomputed")
+    say(f"[wide] d_v={d_v} {dt} lens={lens} raw={raw}")
+    inp = synth.generate(shape, seqlens=lens, seed=11)
+    g, beta = (None, None) if raw else gates_for(inp)
+    out, fin = gpu_prefill(inp, g, beta, raw=raw, algorithm="serial")
+    ro, rf = oracle_prefill(inp, g, beta, raw=raw)
+    check(out, ro, TOL[dt], "out")
+    check(fin, rf, TOL[dt], "final state")
+
+
 def test_prefill_options():
     """Explicit scale, in-place state, out or state omitted, no host cu_seqlens."""
     shape = _shape("varlen_prefill_8seq", init_state=True)
