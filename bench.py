@@ -279,8 +279,8 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=Tru
         roof = {"bound": "alu", "achieved": round(tf, 2), "peak": round(FP32_VALU_PEAK_TFLOPS, 2),
                 "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
                 "traffic": _traffic(shape.name + "_serial", ["prefill_scan.hip", "gdn_device.hpp"]),
-                "kernel": ("scan_wide_kernel (serial scan, d_k 256, two columns per wave)" if shape.d_k == 256
-                           else "scan_kernel (serial scan)"), "flops_per_launch": fl,
+                "kernel": ("scan_plain_kernel (serial scan, d_k 256, two columns per wave)" if shape.d_k == 256
+                           else "scan_plain_kernel or scan_kernel (serial scan)"), "flops_per_launch": fl,
                 "algorithmic_bytes_per_launch": nbytes}
     line = {
         "metric": METRIC,

@@ -145,6 +145,9 @@ __device__ __forceinline__ int state_slot(const int32_t* slots, int32_t num_slot
 
 // Columns one scan wave owns for a given d_k (used to size the grid).
 int scan_columns_per_wave(const ScanParams& p);
+
+// Compute units of the current device (queried once; 256 if the query fails).
+int device_compute_units();
 // Columns one decode workgroup owns.
 int decode_columns_per_block(int d_k, int d_v, bool per_key);
 

@@ -298,8 +298,8 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   }
 }
 
-// The plain gated delta rule at d_k = 256 (the widest head): CPW state
-// columns per wave, R = 64 / CPW lanes per column, RPL = 256 / R rows per
+// The plain gated delta rule with every row present (d_k = 128 or 256): CPW
+// state columns per wave, R = 64 / CPW lanes per column, RPL = DK / R rows per
 // lane.  Against scan_kernel:
 //   * the readout reduction of token t and the retrieval reduction of token
 //     t + 1 (both read the state after token t) run interleaved, so the
@@ -307,21 +307,29 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
 //   * q/k/v addresses are wave-uniform bases advanced token by token plus a
 //     fixed lane offset, with no per-token 64-bit products;
 //   * whole 64-token blocks run without bounds checks; the last block or two
-//     run a guarded copy, eight tokens at a time;
+//     run a guarded copy, P tokens at a time;
 //   * a block's 64 outputs of a column leave in one store, lane u holding
-//     token u's.
-template <int CPW>
-struct WideShape {
-  static constexpr int R = kWave / CPW;   // lanes per column
-  static constexpr int RPL = 256 / R;     // rows per lane
+//     token u's;
+//   * the column blocks of a (sequence, head) are placed on one XCD.
+// d_k = 256 takes two columns per wave (32 lanes, 8 rows each) and 16 tokens
+// in flight: with one wave per SIMD, load latency would otherwise set the
+// pace.  d_k = 128 keeps scan_kernel's four columns per wave (16 lanes, 8
+// rows each, no lane swaps) and 8 tokens in flight.
+template <int DK>
+struct PlainShape {
+  static constexpr int CPW = DK >= 256 ? 2 : 4;  // columns per wave
+  static constexpr int P = DK >= 256 ? 16 : 8;   // tokens of q/k/v in flight (ring slots)
+  static constexpr int R = kWave / CPW;          // lanes per column
+  static constexpr int RPL = DK / R;             // rows per lane
 };
-constexpr int kWideColumns = 2;  // columns per wave of the wide scan
 
-template <typename IO, bool RAW, int CPW>
-__global__ __launch_bounds__(kWave) void scan_wide_kernel(ScanParams p) {
-  constexpr int R = WideShape<CPW>::R;
-  constexpr int RPL = WideShape<CPW>::RPL;
-  constexpr int P = 16;  // tokens of q/k/v in flight (ring slots)
+template <typename IO, bool RAW, int DK>
+__global__ __launch_bounds__(kWave) void scan_plain_kernel(ScanParams p) {
+  static_assert(DK == 128 || DK == 256, "the plain scan covers d_k = 128 and 256");
+  constexpr int CPW = PlainShape<DK>::CPW;
+  constexpr int R = PlainShape<DK>::R;
+  constexpr int RPL = PlainShape<DK>::RPL;
+  constexpr int P = PlainShape<DK>::P;
   const int lane = static_cast<int>(threadIdx.x);
   const int c = lane / R;  // column within the wave
   // blocks go round-robin over the 8 XCDs: the column blocks of one (sequence,
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(kWave) void scan_wide_kernel(ScanParams p) {
 
   bool has_state;
   const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
-  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(256) * p.d_v;
+  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(DK) * p.d_v;
   float S[RPL];
 #pragma unroll
   for (int m = 0; m < RPL; ++m)
@@ -353,10 +361,10 @@ __global__ __launch_bounds__(kWave) void scan_wide_kernel(ScanParams p) {
     const IO* __restrict__ kg = static_cast<const IO*>(p.k);
     const IO* __restrict__ vg = static_cast<const IO*>(p.v);
     IO* __restrict__ og = static_cast<IO*>(p.out);
-    const size_t qk_stride = static_cast<size_t>(p.h_qk) * 256;
+    const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
     const size_t v_stride = static_cast<size_t>(p.h_v) * p.d_v;
-    const IO* kbase = kg + static_cast<size_t>(hq) * 256;
-    const IO* qbase = qg + static_cast<size_t>(hq) * 256;
+    const IO* kbase = kg + static_cast<size_t>(hq) * DK;
+    const IO* qbase = qg + static_cast<size_t>(hq) * DK;
     const IO* vbase = vg + static_cast<size_t>(h) * p.d_v + cb * CPW;  // + the lane's column
     const int vcol = col_ok ? c : 0;
     const float scale = p.scale;
@@ -499,20 +507,31 @@ __global__ __launch_bounds__(kWave) void scan_wide_kernel(ScanParams p) {
   }
 }
 
-// Whether a launch takes the wide scan (the plain rule at d_k = 256).
-bool wide_scan(const ScanParams& p) {
+// Whether a launch takes scan_plain_kernel (the plain rule, d_k = 128 or 256).
+// At d_k = 128 only small grids take it (at most two waves per SIMD): larger
+// ones hide latency with scan_kernel's higher occupancy instead (measured on
+// the 8-sequence, 33k-token workload).
+bool plain_scan(const ScanParams& p) {
   const bool per_key = p.gates.per_key && p.gates.decays;
   const bool plain = p.gates.decays && p.gates.deltas && p.window == 0;
-  return p.d_k == 256 && plain && !per_key;
+  if (!plain || per_key) return false;
+  if (p.d_k == 256) return true;
+  if (p.d_k != 128) return false;
+  const int64_t waves = static_cast<int64_t>(p.num_seqs) * p.h_v * ((p.d_v + PlainShape<128>::CPW - 1) / PlainShape<128>::CPW);
+  return waves <= 2 * 4 * static_cast<int64_t>(device_compute_units());
 }
 
 template <typename IO, int DK, bool RAW>
 hipError_t launch_gates(const ScanParams& p, unsigned blocks, hipStream_t stream) {
   const bool per_key = p.gates.per_key && p.gates.decays;
   const bool plain = p.gates.decays && p.gates.deltas && p.window == 0;
-  if (DK == 256 && wide_scan(p))
-    hipLaunchKernelGGL((scan_wide_kernel<IO, RAW, kWideColumns>), dim3(blocks), dim3(kWave), 0, stream, p);
-  else if (per_key)
+  if constexpr (DK == 256 || DK == 128) {
+    if (plain_scan(p)) {
+      hipLaunchKernelGGL((scan_plain_kernel<IO, RAW, DK>), dim3(blocks), dim3(kWave), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  if (per_key)
     hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, true, true, false>), dim3(blocks), dim3(kWave), 0, stream, p);
   else if (plain && p.d_k == DK)
     hipLaunchKernelGGL((scan_kernel<IO, DK, RAW, false, false, true>), dim3(blocks), dim3(kWave), 0, stream, p);
@@ -527,8 +546,9 @@ template <typename IO, int DK>
 hipError_t launch_dk(const ScanParams& p, hipStream_t stream) {
   const int units = p.num_seqs * p.h_v;
   if (units == 0) return hipSuccess;
-  const unsigned blocks = (DK == 256 && wide_scan(p)) ? static_cast<unsigned>((units + 7) / 8) * 8u * p.col_blocks
-                                                       : static_cast<unsigned>(units) * p.col_blocks;
+  const unsigned blocks = ((DK == 256 || DK == 128) && plain_scan(p))
+                              ? static_cast<unsigned>((units + 7) / 8) * 8u * p.col_blocks
+                              : static_cast<unsigned>(units) * p.col_blocks;
   if (blocks == 0) return hipSuccess;
   return p.gates.raw ? launch_gates<IO, DK, true>(p, blocks, stream) : launch_gates<IO, DK, false>(p, blocks, stream);
 }
@@ -546,7 +566,7 @@ hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
 
 int scan_columns_per_wave(const ScanParams& p) {
   const int d_k = p.d_k;
-  if (wide_scan(p)) return kWideColumns;
+  if (plain_scan(p)) return d_k == 256 ? PlainShape<256>::CPW : PlainShape<128>::CPW;
   if (d_k <= 16) return kWave / ScanShape<16>::R;
   if (d_k <= 32) return kWave / ScanShape<32>::R;
   if (d_k <= 64) return kWave / ScanShape<64>::R;

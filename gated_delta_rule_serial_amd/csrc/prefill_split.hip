@@ -734,7 +734,7 @@ hipError_t set_lds(K kern, int bytes, bool* configured) {
 
 
 // Persistent grid of the preparation pass: one workgroup per compute unit.
-int prep_workgroups();
+int prep_workgroups() { return device_compute_units(); }
 
 // Columns per state-pass workgroup: 128 (two per wave), or 64 when the
 // (sequence, head) units leave compute units idle and splitting fills them.
@@ -742,17 +742,6 @@ int split_columns(int d_v, int units) {
   return d_v > 64 && static_cast<int64_t>(units) * ((d_v + 63) / 64) > prep_workgroups() ? 128 : 64;
 }
 
-int prep_workgroups() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 template <typename IO, int DK, int DVT>
 hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, int32_t* cs, const int2* info,
@@ -792,6 +781,18 @@ int chunk_bound_of(int num_seqs, int total_tokens) {
 }
 
 }  // namespace
+
+int device_compute_units() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
 
 bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window) {
   return chunked_supported(io_bf16, d_k, d_v, gates, window) && d_v <= 256;
