@@ -291,6 +291,18 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     }
     __syncthreads();
 
+  // the next item's inputs, in flight while this one computes: issued once
+  // the staging registers are free, so they drain during the products and
+  // the solve, ahead of this item's workspace stores
+  {
+    const int next = item + static_cast<int>(gridDim.x);
+    if (next < n_items) {
+      at = locate(next, next_info);
+      fetch(at);
+      next_info = info_of(next + static_cast<int>(gridDim.x));
+    }
+  }
+
   // ================= 2. K^T; P = K K^T, R = Q K^T -> A (f32) and M (bf16)
   for (int ix = tid; ix < DK * (kC / 8); ix += kThreads) {
     const int i = ix % DK;
@@ -367,17 +379,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     Tpp[t * kSC + s2] = to_bf16(tv * bs);
   }
   __syncthreads();
-
-  // the next item's inputs, in flight while this one finishes: issued here,
-  // where the memory pipeline is idle, ahead of this item's workspace stores
-  {
-    const int next = item + static_cast<int>(gridDim.x);
-    if (next < n_items) {
-      at = locate(next, next_info);
-      fetch(at);
-      next_info = info_of(next + static_cast<int>(gridDim.x));
-    }
-  }
 
   // ================= 4. W = T' K (-> LDS, over K), U = T'' V (-> workspace, tile order)
   const int kmax = (rb < 2) ? 32 : 64;  // T' and T'' vanish above the diagonal
