@@ -12,8 +12,9 @@ events on the stream the kernel runs on.  Prints ONE JSON line.
 
 Other workloads (--workload prefill_t4096_fused_gates, varlen_prefill_8seq,
 wide_prefill_t32768_d256, tiny_prefill) time one gdn_prefill per step, each
-between its own events, with a 1 GiB write in between that flushes the L2 and
-the Infinity Cache.  The block's neighbouring operations are timed the same
+between its own events, with a 1 GiB read in between that flushes the L2 and
+the Infinity Cache (clean lines only, so no write-back lands in the timed
+launch).  The block's neighbouring operations are timed the same
 way: conv_step_b64 (gdn_causal_conv_step), conv_varlen_8seq (gdn_causal_conv)
 and gated_rmsnorm_t33173 (gdn_gated_rmsnorm).
 
@@ -195,7 +196,11 @@ def bench_decode(shape, steps, warmup, want_cpu):
 
 
 def _flush(buf):
-    buf.fill_(1.0)
+    """Evict L2 and the 256 MB Infinity Cache before a timed launch by reading a
+    1 GiB buffer.  A read leaves clean lines behind; a write-based flush leaves
+    dirty ones, and their write-back to HBM then runs inside the timed launch
+    (about 40 us on a 272 MB x 3 elementwise kernel)."""
+    buf.sum()
 
 
 def chunked_flops(shape, T, chunk=64):
@@ -224,7 +229,7 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=Tru
     n = len(inp.seqlens)
     out = torch.empty(T, shape.h_v, shape.d_v, dtype=shape.io_dtype, device=dev)
     fin = torch.empty(n, shape.h_v, shape.d_k, shape.d_v, dtype=torch.float32, device=dev)
-    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)  # 1 GiB
+    flush = torch.zeros(256 * 1024 * 1024, dtype=torch.float32, device=dev)  # 1 GiB
     stream = torch.cuda.current_stream()
     # the chunked form's workspace (two passes), allocated before the timed region
     ws_bytes = gdn.prefill_workspace_size(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, n, T,
@@ -345,7 +350,7 @@ def bench_conv(shape, steps, warmup, want_cpu):
     fin = s0 if step else torch.empty_like(s0)
     cu = inp.cu_seqlens.to(dev)
     cu_host = inp.cu_seqlens.tolist()
-    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    flush = torch.zeros(256 * 1024 * 1024, dtype=torch.float32, device=dev)
 
     def one():
         if step:
@@ -388,7 +393,7 @@ def bench_norm(shape, steps, warmup, want_cpu):
     es = inp.x.element_size()
     x, g, sc = inp.x.to(dev), inp.gate.to(dev), inp.scale.to(dev)
     y = torch.empty_like(x)
-    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    flush = torch.zeros(256 * 1024 * 1024, dtype=torch.float32, device=dev)
     ms, med, wall = _timed(lambda: gdn.gdn_gated_rmsnorm(x, g, sc, y=y), steps, warmup, flush)
     nbytes = 3 * x.numel() * es + sc.numel() * es
     gbs = nbytes / (ms * 1e-3) / 1e9

@@ -15,12 +15,12 @@
 // HBM-bound elementwise work (K multiply-adds per element).  Kernels:
 //   conv_window_kernel  dilation 1, K <= 4, C a multiple of one 16-byte
 //       vector: a thread owns one channel vector (16 bytes) of kSeg = 8
-//       consecutive tokens of the packed axis, loads their rows at once and
-//       slides the K - 1 previous inputs through registers; a wave reads
-//       1 KiB contiguous per token and writes it with 16-byte stores.  A
-//       segment may cross sequence boundaries; the window is then refilled
-//       from the next state.  Consecutive segments run on one L2 domain, so
-//       the rows in front of a segment tend to come from L2.  The silu uses
+//       consecutive tokens of the packed axis and issues all its loads at
+//       once (weights, bias, the K - 1 rows in front and the kSeg rows); a
+//       wave reads 1 KiB contiguous per row and writes it with 16-byte
+//       stores.  A segment that touches a sequence start reads the carried
+//       state for positions before it.  Consecutive segments run on one L2
+//       domain, so the rows in front of a segment tend to come from L2.  The silu uses
 //       the hardware exp2 / reciprocal: with the precise forms the kernel
 //       was bound by the vector ALUs, not by HBM.
 //   conv_generic_kernel any K and dilation: one thread per (token, channel).
@@ -80,6 +80,8 @@ __device__ __forceinline__ float xp_at(const IO* __restrict__ x, const IO* __res
 template <typename IO, int K, bool SILU>
 __global__ __launch_bounds__(kThreads) void conv_window_kernel(ConvParams p, int channel_blocks, int segs_per_xcd) {
   constexpr int V = 16 / static_cast<int>(sizeof(IO));
+  constexpr int W = K - 1;     // rows in front of a token that its output reads
+  constexpr int R = W + kSeg;  // rows held: tokens t_first - W .. t_first + kSeg - 1
   const int C = p.channels;
   const int L = static_cast<int>(blockIdx.x);
   const int slot = L / kXcds;
@@ -91,88 +93,97 @@ __global__ __launch_bounds__(kThreads) void conv_window_kernel(ConvParams p, int
   const int t_stop = min(t_first + kSeg, p.total_tokens);
   const IO* __restrict__ x = static_cast<const IO*>(p.x);
   const IO* __restrict__ s0 = static_cast<const IO*>(p.s0);
+  const IO* __restrict__ wt = static_cast<const IO*>(p.weight) + static_cast<size_t>(c0) * K;
   IO* __restrict__ y = static_cast<IO*>(p.y);
 
-  // weights [C, K]: the V channels' K taps are V * K consecutive elements
+  // Every load is issued first and unconditionally (a load under a condition
+  // is waited for on its own): the weights [C, K] (the V channels' K taps are
+  // V * K consecutive elements), the bias (the weights stand in when there is
+  // none) and the R rows, clamped into [0, t_stop - 1].  A row before the
+  // token's sequence or past the segment's end is loaded and not used.
+  RawSlice<IO, V * K> rw;
+  rw.load(wt);
+  RawSlice<IO, V> rb;
+  rb.load(p.bias != nullptr ? static_cast<const IO*>(p.bias) + c0 : wt);
+  RawSlice<IO, V> raw[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    raw[r].load(x + static_cast<size_t>(min(max(t_first - W + r, 0), t_stop - 1)) * C + c0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  int n = find_seq(p.cu, p.num_seqs, t_first);
+  int ts = seq_begin(p.cu, n, p.total_tokens), te = seq_end(p.cu, n, p.total_tokens);
   float w[K][V], bias[V];
   {
-    RawSlice<IO, V * K> rw;
-    rw.load(static_cast<const IO*>(p.weight) + static_cast<size_t>(c0) * K);
     float wf[V * K];
     rw.widen_to(wf);
 #pragma unroll
     for (int e = 0; e < V; ++e)
 #pragma unroll
       for (int j = 0; j < K; ++j) w[j][e] = wf[e * K + j];
-  }
-  if (p.bias != nullptr) {
-    RawSlice<IO, V> rb;
-    rb.load(static_cast<const IO*>(p.bias) + c0);
     rb.widen_to(bias);
-  } else {
 #pragma unroll
-    for (int e = 0; e < V; ++e) bias[e] = 0.0f;
+    for (int e = 0; e < V; ++e) bias[e] = p.bias != nullptr ? bias[e] : 0.0f;
   }
 
-  // window: win[m - 1][e] = xp(t - m), m = 1 .. K - 1
-  float win[K > 1 ? K - 1 : 1][V];
-  int n = find_seq(p.cu, p.num_seqs, t_first);
-  int t0 = seq_begin(p.cu, n, p.total_tokens), t_end = seq_end(p.cu, n, p.total_tokens);
-  auto fill_window = [&](int t) {
+  if (t_first + kSeg <= p.total_tokens && t_first - W >= ts && t_first + kSeg <= te) {
+    // the segment and the rows in front of it lie in one sequence: output
+    // i reads rows i .. i + W
+    float rows[R][V];
 #pragma unroll
-    for (int m = 1; m < K; ++m) {
-      const int pos = t - t0 - m;
+    for (int r = 0; r < R; ++r) raw[r].widen_to(rows[r]);
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      float out[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        float z = bias[e];
+#pragma unroll
+        for (int j = 0; j < K; ++j) z = fmaf(w[j][e], rows[i + j][e], z);
+        out[e] = SILU ? z * fast_sigmoid(z) : z;
+      }
+      store_slice<IO, V>(y + static_cast<size_t>(t_first + i) * C + c0, out);
+    }
+    return;
+  }
+
+  // General case: a sequence starts in front of or inside the segment, or
+  // the segment is the last, partial one.  Token t reads input t - m from
+  // the held rows when it belongs to t's sequence, from the sequence's
+  // carried state when it lies up to carry positions before it, else zero.
+#pragma unroll
+  for (int i = 0; i < kSeg; ++i) {
+    const int t = t_first + i;
+    if (t >= t_stop) break;
+    if (t >= te) {  // t opens a later (non-empty) sequence
+      while (n + 1 < p.num_seqs && seq_end(p.cu, n, p.total_tokens) <= t) ++n;
+      ts = seq_begin(p.cu, n, p.total_tokens);
+      te = seq_end(p.cu, n, p.total_tokens);
+    }
+    float z[V], in[V];
+    raw[W + i].widen_to(in);
+#pragma unroll
+    for (int e = 0; e < V; ++e) z[e] = fmaf(w[W][e], in[e], bias[e]);
+#pragma unroll
+    for (int m = 1; m <= W; ++m) {
+      const int pos = t - m - ts;  // position in the sequence; < 0 is the state
       if (pos >= 0) {
-        RawSlice<IO, V> r;
-        r.load(x + static_cast<size_t>(t - m) * C + c0);
-        r.widen_to(win[m - 1]);
+        raw[W + i - m].widen_to(in);
       } else if (s0 != nullptr && pos >= -p.carry) {
         RawSlice<IO, V> r;
         r.load(s0 + (static_cast<size_t>(n) * p.carry + p.carry + pos) * C + c0);
-        r.widen_to(win[m - 1]);
+        r.widen_to(in);
       } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) win[m - 1][e] = 0.0f;
+        for (int e = 0; e < V; ++e) in[e] = 0.0f;
       }
+#pragma unroll
+      for (int e = 0; e < V; ++e) z[e] = fmaf(w[W - m][e], in[e], z[e]);
     }
-  };
-  fill_window(t_first);
-
-  for (int tc = t_first; tc < t_stop; tc += kChunk) {
-    // the chunk's input rows, issued before any is used
-    RawSlice<IO, V> raw[kChunk];
+    float out[V];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i)
-      if (tc + i < t_stop) raw[i].load(x + static_cast<size_t>(tc + i) * C + c0);
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      const int t = tc + i;
-      if (t >= t_stop) break;
-      if (t >= t_end) {  // next (non-empty) sequence: refill the window from its state
-        while (n + 1 < p.num_seqs && seq_end(p.cu, n, p.total_tokens) <= t) ++n;
-        t0 = seq_begin(p.cu, n, p.total_tokens);
-        t_end = seq_end(p.cu, n, p.total_tokens);
-        fill_window(t);
-      }
-      float cur[V], out[V];
-      raw[i].widen_to(cur);
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        float z = fmaf(w[K - 1][e], cur[e], bias[e]);
-#pragma unroll
-        for (int m = 1; m < K; ++m) z = fmaf(w[K - 1 - m][e], win[m - 1][e], z);
-        out[e] = SILU ? z * fast_sigmoid(z) : z;
-      }
-      store_slice<IO, V>(y + static_cast<size_t>(t) * C + c0, out);
-#pragma unroll
-      for (int m = K - 1; m >= 2; --m)
-#pragma unroll
-        for (int e = 0; e < V; ++e) win[m - 1][e] = win[m - 2][e];
-      if constexpr (K > 1) {
-#pragma unroll
-        for (int e = 0; e < V; ++e) win[0][e] = cur[e];
-      }
-    }
+    for (int e = 0; e < V; ++e) out[e] = SILU ? z[e] * fast_sigmoid(z[e]) : z[e];
+    store_slice<IO, V>(y + static_cast<size_t>(t) * C + c0, out);
   }
 }
 

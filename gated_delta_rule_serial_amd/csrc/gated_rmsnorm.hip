@@ -40,65 +40,68 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(NormParams p) {
   IO* __restrict__ yg = static_cast<IO*>(p.y);
   const float inv_n = 1.0f / static_cast<float>(p.group);
 
-  // this lane's scale elements (the same for every group)
-  float sc[NV][V];
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const int vi = k * TL + tl;
-    if (vi < nvec) {
-      RawSlice<IO, V> r;
-      r.load(sg + static_cast<size_t>(vi) * V);
-      r.widen_to(sc[k]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < V; ++e) sc[k][e] = 0.0f;
-    }
-  }
-
   // a wave takes U * kTeams consecutive groups per iteration (team u * kTeams +
   // team), so each load instruction covers kTeams consecutive groups; every
   // lane runs the same number of iterations (the DPP reduction needs the whole
-  // wave) and teams past the end compute on zeros and store nothing
+  // wave), and a team past the end repeats the last group
   const int64_t per_wave = static_cast<int64_t>(U) * kTeams;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * (kThreads / 64) * per_wave;
   const int64_t first = (static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave) * per_wave;
   for (int64_t base = first; base < p.groups; base += stride) {
-    RawSlice<IO, V> rx[U][NV], rg[U][NV];
+    // Loads are unconditional, from clamped (existing) groups and vectors:
+    // under a condition, the compiler could no longer count the loads issued
+    // after a given one and would wait for every memory operation, stores
+    // included, before each use.  Vectors past the group read as zero below.
+    // This lane's scale elements (the same for every group) are loaded first
+    // in every iteration: most waves run one iteration, and a load before the
+    // loop would cost them a second full memory latency.  They come from
+    // cache after the first; the empty asm keeps the load in the loop.
+    int opaque_zero = 0;
+    asm volatile("" : "+s"(opaque_zero));
+    const IO* sgi = sg + opaque_zero;
+    RawSlice<IO, V> rs[NV], rx[U][NV], rg[U][NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) rs[k].load(sgi + static_cast<size_t>(min(k * TL + tl, nvec - 1)) * V);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t grp = base + u * kTeams + team;
-      const size_t off = static_cast<size_t>(grp < p.groups ? grp : 0) * p.group;
+      const size_t off = static_cast<size_t>(grp < p.groups ? grp : p.groups - 1) * p.group;
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const int vi = k * TL + tl;
-        if (grp < p.groups && vi < nvec) {
-          rx[u][k].load(xg + off + static_cast<size_t>(vi) * V);
-          rg[u][k].load(gg + off + static_cast<size_t>(vi) * V);
-        } else {
-#pragma unroll
-          for (int c = 0; c < RawSlice<IO, V>::kWords; ++c) rx[u][k].w[c] = rg[u][k].w[c] = 0u;
-        }
+        const int vi = min(k * TL + tl, nvec - 1);
+        rx[u][k].load(xg + off + static_cast<size_t>(vi) * V);
+        rg[u][k].load(gg + off + static_cast<size_t>(vi) * V);
       }
     }
+    // every load of the iteration is issued before the first use waits
+    __builtin_amdgcn_sched_barrier(0);
+    float sc[NV][V];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) rs[k].widen_to(sc[k]);
+    // Stores are unconditional too (a load used only under a condition is
+    // sunk into it and waited for there): a lane past the end computes and
+    // stores the clamped vector it loaded, with that group's norm, which
+    // repeats its owner's store bit for bit.
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t grp = base + u * kTeams + team;
-      const size_t off = static_cast<size_t>(grp < p.groups ? grp : 0) * p.group;
+      const size_t off = static_cast<size_t>(grp < p.groups ? grp : p.groups - 1) * p.group;
       float xv[NV][V];
       float ss = 0.0f;
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         rx[u][k].widen_to(xv[k]);
+        float part = 0.0f;
 #pragma unroll
-        for (int e = 0; e < V; ++e) ss = fmaf(xv[k][e], xv[k][e], ss);
+        for (int e = 0; e < V; ++e) part = fmaf(xv[k][e], xv[k][e], part);
+        ss += k * TL + tl < nvec ? part : 0.0f;
       }
       ss = group_sum<TL>(ss);
-      const float inv = 1.0f / sqrtf(fmaf(ss, inv_n, p.eps));
-      if (grp >= p.groups) continue;
+      // v_rsq_f32 (about 1 ulp); the argument is at least eps
+      const float inv = __builtin_amdgcn_rsqf(fmaf(ss, inv_n, p.eps));
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const int vi = k * TL + tl;
-        if (vi >= nvec) continue;
+        const int vi = min(k * TL + tl, nvec - 1);
         float gv[V], out[V];
         rg[u][k].widen_to(gv);
 #pragma unroll

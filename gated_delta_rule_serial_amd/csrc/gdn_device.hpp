@@ -43,8 +43,11 @@ __device__ __forceinline__ uint32_t narrow_pair(float a, float b) {
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<f16_t>(a))) |
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<f16_t>(b))) << 16);
   } else {
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+    // one v_cvt_pk_bf16_f32 for the pair
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 ab = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(ab, bf16x2));
   }
 }
 
