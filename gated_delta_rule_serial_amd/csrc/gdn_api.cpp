@@ -234,21 +234,29 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   const int io_bf16 = p.io_dtype == GDN_BF16;
   sp.window = window;
   sp.history = window > 0 ? problem->state_history : nullptr;
-  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v, sp.gates, window);
+  // float32 I/O: the chunked form exists in two passes only, through a workspace
+  const bool wide_ok = gdn::wide_supported(p.io_dtype, p.d_k, p.d_v, sp.gates, window);
+  const bool wide_ws = wide_ok && p.workspace != nullptr &&
+                       p.workspace_bytes >= gdn::wide_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) || wide_ws;
   if (p.algorithm == GDN_ALGO_CHUNKED && !can_chunk)
     return fail(GDN_ERR_UNSUPPORTED,
-                "%s: the chunked algorithm needs bfloat16 I/O, d_k 64 or 128, d_v a multiple of 8, the "
-                "gated-delta or delta rule with a per-head decay and no state history (got %s, d_k=%d, "
-                "d_v=%d, rule=%d, decay_per_key=%d, state_window=%d)",
-                fn, io_name(p.io_dtype), p.d_k, p.d_v, p.rule, p.decay_per_key, window);
+                "%s: the chunked algorithm needs bfloat16 I/O with d_k 64 or 128 and d_v a multiple of 8, or "
+                "float32 I/O with d_k 128 or 256, d_v a multiple of 16 up to 256 and a workspace of "
+                "gdn_prefill_workspace_size bytes; and the gated-delta or delta rule with a per-head decay "
+                "and no state history (got %s, d_k=%d, d_v=%d, rule=%d, decay_per_key=%d, state_window=%d%s)",
+                fn, io_name(p.io_dtype), p.d_k, p.d_v, p.rule, p.decay_per_key, window,
+                wide_ok && !wide_ws ? ", no or too small a workspace" : "");
   const bool chunked = p.algorithm == GDN_ALGO_CHUNKED ||
-                       (p.algorithm == GDN_ALGO_AUTO && can_chunk &&
+                       (p.algorithm == GDN_ALGO_AUTO && can_chunk && (!wide_ws || gdn::wide_auto(p.d_k)) &&
                         static_cast<int64_t>(total_tokens) >= 64 * static_cast<int64_t>(num_seqs));
+  const bool wide = chunked && wide_ws;
   // the two-pass chunked form when the caller's workspace holds it
-  const bool split = chunked && gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) &&
+  const bool split = chunked && !wide && gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) &&
                      p.workspace != nullptr &&
                      p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
-  const int cols = split     ? gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v)
+  const int cols = wide      ? 16
+                   : split   ? gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v)
                    : chunked ? gdn::chunked_columns_per_block(p.d_k, p.d_v)
                              : gdn::scan_columns_per_wave(sp);
   sp.col_blocks = (p.d_v + cols - 1) / cols;
@@ -256,7 +264,8 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   if (blocks > 0x7fffffffull)
     return fail(GDN_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", fn,
                 static_cast<unsigned long long>(blocks));
-  const hipError_t e = split     ? gdn::launch_prefill_split(sp, p.workspace, stream)
+  const hipError_t e = wide      ? gdn::launch_prefill_wide(sp, p.workspace, stream)
+                       : split   ? gdn::launch_prefill_split(sp, p.workspace, stream)
                        : chunked ? gdn::launch_prefill_chunked(sp, io_bf16, stream)
                                  : gdn::launch_prefill_scan(sp, p.io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -360,6 +369,11 @@ GDN_EXPORT gdn_status gdn_prefill_workspace_size(const gdn_problem* problem, int
   const gdn_problem& p = *problem;
   if (p.algorithm == GDN_ALGO_SERIAL) return ok();
   const gdn::GateArgs gates = gate_args(problem);
+  if (gdn::wide_supported(p.io_dtype, p.d_k, p.d_v, gates, p.state_window)) {
+    if (p.algorithm == GDN_ALGO_CHUNKED || gdn::wide_auto(p.d_k))
+      *bytes = gdn::wide_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+    return ok();
+  }
   if (!gdn::split_supported(p.io_dtype == GDN_BF16, p.d_k, p.d_v, gates, p.state_window)) return ok();
   *bytes = gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
   return ok();

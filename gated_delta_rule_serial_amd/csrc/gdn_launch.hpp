@@ -131,6 +131,19 @@ bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int w
 int split_columns_per_block(int d_v, int units);
 size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v);
 hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t stream);
+// The chunk table at the head of a two-pass workspace: cs [N + 1] int32 (the
+// chunks before each sequence), then info [bound] int2 (first token, tokens of
+// every chunk), each in a 256-byte aligned slot.
+int chunk_table_bound(int num_seqs, int total_tokens);
+size_t chunk_table_bytes(int num_seqs, int total_tokens);
+hipError_t launch_chunk_table(const int32_t* cu, int num_seqs, int total_tokens, void* workspace, hipStream_t stream);
+// The two-pass chunked prefill for float32 I/O (d_k 128 or 256): matrix-core
+// products on operands split into two bfloat16 parts.
+bool wide_supported(int io_dtype, int d_k, int d_v, const GateArgs& gates, int window);
+size_t wide_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v);
+hipError_t launch_prefill_wide(ScanParams p, void* workspace, hipStream_t stream);
+// Whether GDN_ALGO_AUTO takes the float32 two-pass form at this d_k (when a workspace is given).
+bool wide_auto(int d_k);
 
 // Index of sequence n's state and whether it exists (slot-pool indirection).
 __device__ __forceinline__ int state_slot(const int32_t* slots, int32_t num_slots, int n, bool* valid) {

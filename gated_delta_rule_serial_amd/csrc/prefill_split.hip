@@ -806,6 +806,17 @@ static size_t table_bytes(int num_seqs, int total_tokens) {
   return align256(static_cast<size_t>(num_seqs + 1) * 4) + align256(static_cast<size_t>(chunk_bound_of(num_seqs, total_tokens)) * 8);
 }
 
+int chunk_table_bound(int num_seqs, int total_tokens) { return chunk_bound_of(num_seqs, total_tokens); }
+size_t chunk_table_bytes(int num_seqs, int total_tokens) { return num_seqs > 0 ? table_bytes(num_seqs, total_tokens) : 0; }
+
+hipError_t launch_chunk_table(const int32_t* cu, int num_seqs, int total_tokens, void* workspace, hipStream_t stream) {
+  int32_t* cs = static_cast<int32_t*>(workspace);
+  int2* info = reinterpret_cast<int2*>(static_cast<unsigned char*>(workspace) +
+                                       align256(static_cast<size_t>(num_seqs + 1) * 4));
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, num_seqs, total_tokens, cs, info);
+  return hipGetLastError();
+}
+
 size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v) {
   if (num_seqs <= 0) return 0;
   const int dvt = pad16(d_v) > 128 ? 16 : 8;

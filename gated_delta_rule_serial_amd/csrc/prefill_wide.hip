@@ -1,0 +1,684 @@
+// prefill_wide.hip -- the two-pass chunked prefill for float32 I/O (gfx950
+// MFMA, d_k 128 or 256).
+//
+// The chunked form is the one the bfloat16 two-pass prefill uses, derived
+// from [P4] onnx-runtime-ep-cuda, src/kernels/linear_attention.rs,
+// `linear_attention_core` steps 1-4.  Per chunk of C = 64 tokens (G_t the
+// in-chunk prefix of the log-decay, gam_t = exp(G_t), T = (I + A)^-1 with the
+// strictly lower A_ts = beta_t exp(G_t - G_s) k_t.k_s):
+//     W  = T diag(beta gam) K          U = T diag(beta) V
+//     M_ts = scale exp(G_t - G_s) q_t.k_s (s <= t)
+//     Kt = diag(exp(G_last - G)) K
+// depend on the chunk alone, while
+//     D = U - W S,   O = scale diag(gam) Q S + M D,   S <- gam_last S + Kt^T D
+// carry the state from chunk to chunk.
+//
+// Float32 I/O asks for float32-class products, which the bfloat16 matrix
+// cores give when each operand x is split into hi = bf16(x) and
+// lo = bf16(x - hi) and a product is formed from the three terms
+// hi.hi + hi.lo + lo.hi (the dropped lo.lo is below 2^-16 of the product).
+// Accumulation is float32 throughout, and the state is carried in float32
+// MFMA accumulators.
+//
+// Pass 1 (wide_prep_kernel): one workgroup per (chunk, value head) computes
+// W, Kt^T and M as split operand fragments, U in float32 and the decay
+// factors into a caller-provided workspace.  Pass 2 (wide_state_kernel): one
+// workgroup of four waves per (sequence, value head, block of 16 state
+// columns); wave w owns rows [w d_k / 4, (w + 1) d_k / 4) of the state block
+// and the partial products W S and Q S over its rows meet in LDS once per
+// chunk.
+#include "chunk_mfma.hpp"
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kC = 64;            // chunk length (tokens)
+constexpr int kThreads = 256;     // four waves
+constexpr int kSF = kC + 4;       // f32 row stride of the 64 x 64 matrices in LDS
+constexpr int kSH = kC + 8;       // bf16 row stride of the split T diag(beta) and T diag(beta gam)
+constexpr float kMinLogDecay = -1.0e4f;
+constexpr double kLog2e = 1.4426950408889634;
+
+__host__ __device__ constexpr size_t align256w(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// One (chunk, value head) record.  Fragments are 1 KiB: the 64 lanes x 16
+// bytes one wave loads as an operand of v_mfma_f32_16x16x32_bf16, hi part then
+// lo part.  The contraction index inside each 32-wide block is permuted so
+// that lane group g holds k = 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, the
+// order in which two stacked accumulator tiles hold the other operand (state
+// rows for W, the tokens of D for Kt^T and M).
+//   w   [DK / 32 key blocks][4 token tiles][hi, lo]      rows: tokens, k: keys
+//   kt  [DK / 16 key tiles][2 token blocks][hi, lo]      rows: keys, k: tokens
+//   ms  [6 lower blocks][hi, lo]                          rows: tokens, k: tokens
+//   u   [d_v / 16 column tiles][4 token tiles][64 lanes][4] f32, accumulator order
+//   gam [64] f32 gam_t, then gam_last
+struct WideRec {
+  size_t w, kt, ms, u, gam, bytes;
+  __host__ __device__ WideRec(int dk, int dv) {
+    w = 0;
+    kt = w + static_cast<size_t>(dk / 32) * 8 * 1024;
+    ms = kt + static_cast<size_t>(dk / 16) * 4 * 1024;
+    u = ms + 12 * 1024;
+    gam = u + static_cast<size_t>(dv / 16) * 4 * 1024;
+    bytes = align256w(gam + 512);
+  }
+};
+
+// M block (token tile tt, token block kb), kb <= tt / 2
+__device__ __forceinline__ int m_block(int tt, int kb) { return tt < 2 ? tt : 2 + 2 * (tt - 2) + kb; }
+
+__device__ __forceinline__ int wseq_lo(const int32_t* cu, int n, int T) { return min(max(cu[n], 0), T); }
+__device__ __forceinline__ int wseq_hi(const int32_t* cu, int n, int T) {
+  return min(max(cu[n + 1], wseq_lo(cu, n, T)), T);
+}
+
+struct Split8 {
+  bf16x8 hi, lo;
+};
+
+// x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi), |r| <= 2^-17 |x|
+// (both roundings to nearest even).
+__device__ __forceinline__ Split8 split8(const float (&x)[8]) {
+  Split8 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(x[e]);
+    s.hi[e] = h;
+    s.lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
+  }
+  return s;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+// acc += A B from split operands: the two small cross terms first.
+__device__ __forceinline__ f32x4 mma3(f32x4 acc, const Split8& a, const Split8& b) {
+  acc = mfma_bf16(a.lo, b.hi, acc);
+  acc = mfma_bf16(a.hi, b.lo, acc);
+  return mfma_bf16(a.hi, b.hi, acc);
+}
+
+// k (inside a 32-wide block) of slot e of lane group g
+__device__ __forceinline__ int slot_k(int g, int e) { return 4 * g + (e & 3) + 16 * (e >> 2); }
+
+typedef unsigned u32x4w __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_frag(unsigned char* dst, const bf16x8& f, int lane) {
+  *reinterpret_cast<bf16x8*>(dst + 16 * lane) = f;
+}
+__device__ __forceinline__ bf16x8 load_frag(const unsigned char* src, int lane) {
+  return *reinterpret_cast<const bf16x8*>(src + 16 * lane);
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+// slots 0-3 from p[0..3], slots 4-7 from p[16..19]
+__device__ __forceinline__ void load8_perm(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 16);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// ---------------------------------------------------------------- pass 1
+struct WidePrepLds {
+  static constexpr int kAf = 0;                          // A      [C][SF] f32
+  static constexpr int kTf = kAf + kC * kSF * 4;         // T      [C][SF] f32
+  static constexpr int kMf = kTf + kC * kSF * 4;         // M      [C][SF] f32
+  static constexpr int kTb = kMf + kC * kSF * 4;         // T diag(beta)      [hi, lo][C][SH] bf16
+  static constexpr int kTg = kTb + 2 * kC * kSH * 2;     // T diag(beta gam)  [hi, lo][C][SH] bf16
+  static constexpr int kXs = kTg + 2 * kC * kSH * 2;     // solve scratch [4][16][20] f32
+  static constexpr int kGd = kXs + 4 * 16 * 20 * 4;      // G   [C] f64 (log2 units)
+  static constexpr int kGam = kGd + kC * 8;              // gam [C] f32
+  static constexpr int kEps = kGam + kC * 4;             // exp(G_last - G) [C] f32
+  static constexpr int kBet = kEps + kC * 4;             // beta [C] f32
+  static constexpr int kBytes = kBet + kC * 4;
+  static_assert(kBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+};
+
+template <int DK, bool RAW>
+__global__ __launch_bounds__(kThreads) void wide_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
+                                                             const int32_t* cs, const int2* __restrict__ info) {
+  using L_ = WidePrepLds;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* Af = reinterpret_cast<float*>(smem + L_::kAf);
+  float* Tf = reinterpret_cast<float*>(smem + L_::kTf);
+  float* Mf = reinterpret_cast<float*>(smem + L_::kMf);
+  __bf16* Tb = reinterpret_cast<__bf16*>(smem + L_::kTb);
+  __bf16* Tg = reinterpret_cast<__bf16*>(smem + L_::kTg);
+  float* Xs = reinterpret_cast<float*>(smem + L_::kXs);
+  double* Gd = reinterpret_cast<double*>(smem + L_::kGd);
+  float* Gam = reinterpret_cast<float*>(smem + L_::kGam);
+  float* Eps = reinterpret_cast<float*>(smem + L_::kEps);
+  float* Bet = reinterpret_cast<float*>(smem + L_::kBet);
+
+  const int items = cs[p.num_seqs] * p.h_v;
+  const int item = static_cast<int>(blockIdx.x);
+  if (item >= items) return;
+  const int c = item / p.h_v, h = item % p.h_v;
+  const int2 ci = info[c];
+  const int t0 = ci.x, Lc = ci.y;
+  const int hq = h / p.ratio;
+  const int d_v = p.d_v;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const float* kg = static_cast<const float*>(p.k);
+  const float* qg = static_cast<const float*>(p.q);
+  const float* vg = static_cast<const float*>(p.v);
+  const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
+  const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
+  const WideRec rec(DK, d_v);
+  unsigned char* base = ws + static_cast<size_t>(item) * rec_bytes;
+  // row of token t of this chunk (clamped into the chunk: rows past its end
+  // are finite and meet zero factors, beta = 0 for them)
+  auto krow = [&](int t) __attribute__((always_inline)) {
+    return kg + static_cast<size_t>(t0 + min(t, Lc - 1)) * qk_stride + static_cast<size_t>(hq) * DK;
+  };
+  auto qrow = [&](int t) __attribute__((always_inline)) {
+    return qg + static_cast<size_t>(t0 + min(t, Lc - 1)) * qk_stride + static_cast<size_t>(hq) * DK;
+  };
+
+  // ================= 1. gates, the prefix sum of the log-decay, decay factors
+  if (w == 0) {
+    float gv = 0.0f, b = 0.0f;
+    if (lane < Lc) {
+      const size_t gi = static_cast<size_t>(t0 + lane) * p.h_v + h;
+      const size_t bi = p.gates.beta_shared ? static_cast<size_t>(t0 + lane) : gi;
+      if constexpr (RAW) {
+        gv = p.gates.decays ? gate_log_decay(static_cast<const float*>(p.gates.a)[gi], p.gates.A_log[h], p.gates.dt_bias[h]) : 0.0f;
+        b = gate_sigmoid(static_cast<const float*>(p.gates.b)[bi]);
+      } else {
+        gv = p.gates.decays ? static_cast<const float*>(p.gates.g)[gi] : 0.0f;
+        b = static_cast<const float*>(p.gates.beta)[bi];
+      }
+      gv = fmaxf(gv, kMinLogDecay);
+    }
+    const double G = wave_prefix_sum(static_cast<double>(gv) * kLog2e, lane);
+    const double Glast = readlane(G, 63);
+    Gd[lane] = G;
+    const float gam = fast_exp2(static_cast<float>(G));
+    Gam[lane] = gam;
+    Eps[lane] = fast_exp2(static_cast<float>(Glast - G));
+    Bet[lane] = b;
+    float* gr = reinterpret_cast<float*>(base + rec.gam);
+    gr[lane] = gam;
+    if (lane == 63) gr[64] = gam;
+  }
+  __syncthreads();
+
+  // ================= 2. P = K K^T, R = Q K^T (row tile w, lower tiles) -> A, M
+  {
+    const int tt = w;
+    f32x4 pacc[4], racc[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      pacc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      racc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const float* ka_row = krow(16 * tt + r16) + 8 * g;
+    const float* qa_row = qrow(16 * tt + r16) + 8 * g;
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      float x[8];
+      load8(ka_row + 32 * kb, x);
+      const Split8 KA = split8(x);
+      load8(qa_row + 32 * kb, x);
+      const Split8 QA = split8(x);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (st <= tt) {
+          load8(krow(16 * st + r16) + 8 * g + 32 * kb, x);
+          const Split8 KB = split8(x);
+          pacc[st] = mma3(pacc[st], KA, KB);
+          racc[st] = mma3(racc[st], QA, KB);
+        }
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int s = 16 * st + acc_col(lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tt + acc_row(lane, i);
+        float a = 0.0f, m = 0.0f;
+        if (st <= tt && s <= t) {
+          const float dec = fast_exp2(static_cast<float>(Gd[t] - Gd[s]));
+          m = p.scale * dec * racc[st][i];
+          if (s < t) a = Bet[t] * dec * pacc[st][i];
+        }
+        Af[t * kSF + s] = a;
+        Mf[t * kSF + s] = m;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ================= 3. M fragments; T = (I + A)^-1 (diagonal blocks by
+  // substitution, the rest by block substitution on the f32 MFMA)
+  {
+    const int g4 = 4 * g;
+    for (int blk = w; blk < 6; blk += 4) {
+      const int tt = blk < 2 ? blk : 2 + (blk - 2) / 2;
+      const int kb = blk < 2 ? 0 : (blk - 2) % 2;
+      float x[8];
+      load8_perm(Mf + (16 * tt + r16) * kSF + 32 * kb + g4, x);
+      const Split8 s = split8(x);
+      store_frag(base + rec.ms + (2 * blk) * 1024, s.hi, lane);
+      store_frag(base + rec.ms + (2 * blk + 1) * 1024, s.lo, lane);
+    }
+  }
+  {
+    const int cc = lane & 15;
+    const float* Ab = Af + (16 * w) * kSF + 16 * w;
+    float d[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x0 = (r == cc) ? 1.0f : 0.0f, x1 = 0.0f;
+#pragma unroll
+      for (int s2 = 0; s2 < r; s2 += 2) {
+        x0 = fmaf(-Ab[r * kSF + s2], d[s2], x0);
+        if (s2 + 1 < r) x1 = fmaf(-Ab[r * kSF + s2 + 1], d[s2 + 1], x1);
+      }
+      d[r] = x0 + x1;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tf[(16 * w + r) * kSF + 16 * w + cc] = d[r];
+    }
+  }
+  __syncthreads();
+  for (int dist = 1; dist < 4; ++dist) {
+    const int i = w + dist, j = w;
+    if (i < 4) {
+      f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k = j; k < i; ++k)
+        x = mma_f32(x, Af + (16 * i) * kSF + 16 * k, kSF, Tf + (16 * k) * kSF + 16 * j, kSF, lane);
+      float* xs = Xs + w * 16 * 20;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[acc_row(lane, e) * 20 + acc_col(lane)] = x[e];
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+      f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+      y = mma_f32(y, Tf + (16 * i) * kSF + 16 * i, kSF, xs, 20, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Tf[(16 * i + acc_row(lane, e)) * kSF + 16 * j + acc_col(lane)] = -y[e];
+    }
+    __syncthreads();
+  }
+  // T diag(beta) and T diag(beta gam), split
+  for (int e = tid; e < kC * kC; e += kThreads) {
+    const int t = e >> 6, s = e & 63;
+    const float tv = (s <= t) ? Tf[t * kSF + s] : 0.0f;
+    const float xb = tv * Bet[s];
+    const float xg = xb * Gam[s];
+    const __bf16 hb = static_cast<__bf16>(xb), hg = static_cast<__bf16>(xg);
+    Tb[t * kSH + s] = hb;
+    Tb[kC * kSH + t * kSH + s] = static_cast<__bf16>(xb - static_cast<float>(hb));
+    Tg[t * kSH + s] = hg;
+    Tg[kC * kSH + t * kSH + s] = static_cast<__bf16>(xg - static_cast<float>(hg));
+  }
+  __syncthreads();
+
+  // ================= 4. Kt^T fragments and W (as W^T tiles, which are W's
+  // operand fragments in the permuted key order)
+  {
+    // B operand of W^T = K^T (T diag(beta gam))^T: lane supplies
+    // Tg[token 16 tt + r16][token' 32 kb + slot_k(g, e)], token' <= token
+    Split8 TG[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (kb == 1 && tt < 2) continue;
+        const int off = (16 * tt + r16) * kSH + 32 * kb + 4 * g;
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) {
+          const __bf16* src = Tg + hl * kC * kSH + off;
+          const uint2 lo4 = *reinterpret_cast<const uint2*>(src);
+          const uint2 hi4 = *reinterpret_cast<const uint2*>(src + 16);
+          const u32x4w v = {lo4.x, lo4.y, hi4.x, hi4.y};
+          (hl == 0 ? TG[kb][tt].hi : TG[kb][tt].lo) = __builtin_bit_cast(bf16x8, v);
+        }
+      }
+    constexpr int PAIRS = DK / 128;  // key-block pairs (two key tiles each) per wave
+#pragma unroll
+    for (int pr = 0; pr < PAIRS; ++pr) {
+      const int kbk = w * PAIRS + pr;  // key block of 32
+      f32x4 acc[2][4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int r = 2 * kbk + half;  // key tile
+        const int key = 16 * r + r16;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[half][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float x[8], xe[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tok = 32 * kb + slot_k(g, e);
+            x[e] = krow(tok)[key];
+            xe[e] = x[e] * Eps[tok];
+          }
+          const Split8 KE = split8(xe);
+          store_frag(base + rec.kt + ((r * 2 + kb) * 2) * 1024, KE.hi, lane);
+          store_frag(base + rec.kt + ((r * 2 + kb) * 2 + 1) * 1024, KE.lo, lane);
+          const Split8 KW = split8(x);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            if (kb == 1 && tt < 2) continue;
+            acc[half][tt] = mma3(acc[half][tt], KW, TG[kb][tt]);
+          }
+        }
+      }
+      // acc[half][tt] element i of lane l: W[token 16 tt + r16][key 16 (2 kbk + half) + 4 g + i]
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = acc[0][tt][i];
+          x[4 + i] = acc[1][tt][i];
+        }
+        const Split8 s = split8(x);
+        store_frag(base + rec.w + ((kbk * 4 + tt) * 2) * 1024, s.hi, lane);
+        store_frag(base + rec.w + ((kbk * 4 + tt) * 2 + 1) * 1024, s.lo, lane);
+      }
+    }
+  }
+
+  // ================= 5. U = T diag(beta) V, in accumulator order
+  {
+    Split8 TA[4][2];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 1 && tt < 2) continue;
+        const int off = (16 * tt + r16) * kSH + 32 * kb + 8 * g;
+        TA[tt][kb].hi = *reinterpret_cast<const bf16x8*>(Tb + off);
+        TA[tt][kb].lo = *reinterpret_cast<const bf16x8*>(Tb + kC * kSH + off);
+      }
+    const int nct = d_v / 16;
+    for (int ct = w; ct < nct; ct += 4) {
+      const int col = 16 * ct + r16;
+      Split8 VB[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = min(32 * kb + 8 * g + e, Lc - 1);
+          x[e] = vg[static_cast<size_t>(t0 + tok) * v_stride + static_cast<size_t>(h) * d_v + col];
+        }
+        VB[kb] = split8(x);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mma3(acc, TA[tt][0], VB[0]);
+        if (tt >= 2) acc = mma3(acc, TA[tt][1], VB[1]);
+        *reinterpret_cast<f32x4*>(base + rec.u + ((static_cast<size_t>(ct) * 4 + tt) * 64 + lane) * 16) = acc;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pass 2
+// One workgroup per (sequence, value head, 16-column tile); wave w owns state
+// rows [w DK / 4, (w + 1) DK / 4) of the tile as KT accumulator tiles.
+template <int DK>
+__global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, const unsigned char* ws, size_t rec_bytes,
+                                                              const int32_t* cs, int units8) {
+  constexpr int KT = DK / 64;   // key tiles per wave
+  constexpr int KB = DK / 128;  // key blocks of 32 per wave
+  __shared__ __align__(16) f32x4 part[2][2][4][4][64];  // [buffer][X, Y][wave][token tile][lane]
+
+  const int unit = static_cast<int>(blockIdx.x) % units8;
+  const int ct = static_cast<int>(blockIdx.x) / units8;
+  const int units = p.num_seqs * p.h_v;
+  if (unit >= units) return;
+  const int n = unit / p.h_v, h = unit % p.h_v;
+  const int hq = h / p.ratio;
+  const int d_v = p.d_v;
+  const int T = p.total_tokens;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int col = 16 * ct + r16;
+  const int key0 = w * (DK / 4);
+  const WideRec rec(DK, d_v);
+  const float* qg = static_cast<const float*>(p.q);
+  float* og = static_cast<float*>(p.out);
+  const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
+  const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
+
+  bool has_state = true;
+  const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
+  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * DK * d_v;
+
+  f32x4 S[KT];
+#pragma unroll
+  for (int r = 0; r < KT; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[r][i] = (p.s0 != nullptr && has_state)
+                    ? p.s0[sbase + static_cast<size_t>(key0 + 16 * r + acc_row(lane, i)) * d_v + col]
+                    : 0.0f;
+
+  const int lo = wseq_lo(p.cu, n, T), hi = wseq_hi(p.cu, n, T);
+  const int nchunks = (hi - lo + kC - 1) / kC;
+  const int c0 = cs[n];
+  for (int j = 0; j < nchunks; ++j) {
+    const int t0 = lo + kC * j;
+    const int Lc = min(kC, hi - t0);
+    const unsigned char* rb = ws + (static_cast<size_t>(c0 + j) * p.h_v + h) * rec_bytes;
+    const int buf = j & 1;
+
+    // ---- loads of this chunk
+    Split8 WA[KB][4];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const unsigned char* f = rb + rec.w + (((w * KB + kb) * 4 + tt) * 2) * 1024;
+        WA[kb][tt].hi = load_frag(f, lane);
+        WA[kb][tt].lo = load_frag(f + 1024, lane);
+      }
+    float qx[4][KB][8];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const float* qr = qg + static_cast<size_t>(t0 + min(16 * tt + r16, Lc - 1)) * qk_stride +
+                        static_cast<size_t>(hq) * DK + key0 + 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) load8_perm(qr + 32 * kb, qx[tt][kb]);
+    }
+    Split8 KtA[KT][2];
+#pragma unroll
+    for (int r = 0; r < KT; ++r)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const unsigned char* f = rb + rec.kt + (((w * KT + r) * 2 + kb) * 2) * 1024;
+        KtA[r][kb].hi = load_frag(f, lane);
+        KtA[r][kb].lo = load_frag(f + 1024, lane);
+      }
+    Split8 MA[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int blk = m_block(w, kb < (w >> 1) + 1 ? kb : 0);
+      const unsigned char* f = rb + rec.ms + (2 * blk) * 1024;
+      MA[kb].hi = load_frag(f, lane);
+      MA[kb].lo = load_frag(f + 1024, lane);
+    }
+    f32x4 U[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      U[tt] = *reinterpret_cast<const f32x4*>(rb + rec.u + ((static_cast<size_t>(ct) * 4 + tt) * 64 + lane) * 16);
+    const float* gr = reinterpret_cast<const float*>(rb + rec.gam);
+    const f32x4 gam4 = *reinterpret_cast<const f32x4*>(gr + 16 * w + 4 * g);
+    const float gam_last = gr[64];
+
+    // ---- partial W S and Q S over this wave's rows
+    Split8 SB[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = S[2 * kb][i];
+        x[4 + i] = S[2 * kb + 1][i];
+      }
+      SB[kb] = split8(x);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 xa = {0.0f, 0.0f, 0.0f, 0.0f}, ya = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        xa = mma3(xa, WA[kb][tt], SB[kb]);
+        ya = mma3(ya, split8(qx[tt][kb]), SB[kb]);
+      }
+      part[buf][0][w][tt][lane] = xa;
+      part[buf][1][w][tt][lane] = ya;
+    }
+    __syncthreads();
+
+    // ---- D = U - W S (every wave, all tokens), O for token tile w
+    f32x4 D[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 x = part[buf][0][0][tt][lane];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) x += part[buf][0][ww][tt][lane];
+      D[tt] = U[tt] - x;
+    }
+    f32x4 y = part[buf][1][0][w][lane];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) y += part[buf][1][ww][w][lane];
+    Split8 DB[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = D[2 * kb][i];
+        x[4 + i] = D[2 * kb + 1][i];
+      }
+      DB[kb] = split8(x);
+    }
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    o = mma3(o, MA[0], DB[0]);
+    if (w >= 2) o = mma3(o, MA[1], DB[1]);
+    if (og != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * w + acc_row(lane, i);
+        if (t < Lc)
+          og[static_cast<size_t>(t0 + t) * v_stride + static_cast<size_t>(h) * d_v + col] =
+              fmaf(p.scale * gam4[i], y[i], o[i]);
+      }
+    }
+
+    // ---- S <- gam_last S + Kt^T D over this wave's rows
+#pragma unroll
+    for (int r = 0; r < KT; ++r) {
+      f32x4 s = S[r] * gam_last;
+      s = mma3(s, KtA[r][0], DB[0]);
+      s = mma3(s, KtA[r][1], DB[1]);
+      S[r] = s;
+    }
+  }
+
+  if (p.sN != nullptr && has_state) {
+#pragma unroll
+    for (int r = 0; r < KT; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.sN[sbase + static_cast<size_t>(key0 + 16 * r + acc_row(lane, i)) * d_v + col] = S[r][i];
+  }
+}
+
+template <typename K>
+hipError_t set_lds_once(K kern, int bytes, bool* configured) {
+  if (*configured) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) *configured = true;
+  return e;
+}
+
+template <int DK>
+hipError_t launch_dk(const ScanParams& p, unsigned char* recs, size_t rec_bytes, const int32_t* cs, const int2* info,
+                     int bound, hipStream_t stream) {
+  if (bound > 0 && p.h_v > 0) {
+    constexpr int bytes = WidePrepLds::kBytes;
+    const unsigned grid = static_cast<unsigned>(bound) * static_cast<unsigned>(p.h_v);
+    if (p.gates.raw) {
+      static bool cfg = false;
+      auto kern = wide_prep_kernel<DK, true>;
+      hipError_t e = set_lds_once(kern, bytes, &cfg);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, recs, rec_bytes, cs, info);
+    } else {
+      static bool cfg = false;
+      auto kern = wide_prep_kernel<DK, false>;
+      hipError_t e = set_lds_once(kern, bytes, &cfg);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, recs, rec_bytes, cs, info);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int units = p.num_seqs * p.h_v;
+  if (units == 0) return hipSuccess;
+  // the column tiles of a unit sit units8 blocks apart: on one XCD (blocks
+  // are dealt to the eight XCDs in turn), sharing its L2
+  const int units8 = (units + 7) / 8 * 8;
+  const unsigned blocks = static_cast<unsigned>(units8) * static_cast<unsigned>(p.d_v / 16);
+  hipLaunchKernelGGL((wide_state_kernel<DK>), dim3(blocks), dim3(kThreads), 0, stream, p, recs, rec_bytes, cs, units8);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool wide_supported(int io_dtype, int d_k, int d_v, const GateArgs& gates, int window) {
+  return io_dtype == 0 && (d_k == 128 || d_k == 256) && d_v >= 16 && d_v <= 256 && d_v % 16 == 0 && gates.deltas &&
+         !gates.per_key && window == 0;
+}
+
+bool wide_auto(int d_k) {
+  (void)d_k;
+  return false;
+}
+
+size_t wide_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v) {
+  if (num_seqs <= 0) return 0;
+  const WideRec rec(d_k, d_v);
+  return chunk_table_bytes(num_seqs, total_tokens) +
+         static_cast<size_t>(chunk_table_bound(num_seqs, total_tokens)) * h_v * rec.bytes;
+}
+
+hipError_t launch_prefill_wide(ScanParams p, void* workspace, hipStream_t stream) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  if (!wide_supported(0, p.d_k, p.d_v, p.gates, p.window)) return hipErrorInvalidValue;
+  const WideRec rec(p.d_k, p.d_v);
+  const int T = p.total_tokens;
+  hipError_t e = launch_chunk_table(p.cu, p.num_seqs, T, workspace, stream);
+  if (e != hipSuccess) return e;
+  const int32_t* cs = static_cast<const int32_t*>(workspace);
+  const int2* info = reinterpret_cast<const int2*>(static_cast<unsigned char*>(workspace) +
+                                                   align256w(static_cast<size_t>(p.num_seqs + 1) * 4));
+  unsigned char* recs = static_cast<unsigned char*>(workspace) + chunk_table_bytes(p.num_seqs, T);
+  const int bound = chunk_table_bound(p.num_seqs, T);
+  return p.d_k == 256 ? launch_dk<256>(p, recs, rec.bytes, cs, info, bound, stream)
+                      : launch_dk<128>(p, recs, rec.bytes, cs, info, bound, stream);
+}
+
+}  // namespace gdn
