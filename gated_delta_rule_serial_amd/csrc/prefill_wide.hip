@@ -21,8 +21,8 @@
 // MFMA accumulators.
 //
 // Pass 1 (wide_prep_kernel): one workgroup per (chunk, value head) computes
-// W, Kt^T and M as split operand fragments, U in float32 and the decay
-// factors into a caller-provided workspace.  Pass 2 (wide_state_kernel): one
+// W, scale diag(gam) Q, Kt^T and M as split operand fragments, U in float32
+// and gam_last into a caller-provided workspace.  Pass 2 (wide_state_kernel): one
 // workgroup of four waves per (sequence, value head, block of 16 state
 // columns); wave w owns rows [w d_k / 4, (w + 1) d_k / 4) of the state block
 // and the partial products W S and Q S over its rows meet in LDS once per
@@ -51,19 +51,21 @@ __host__ __device__ constexpr size_t align256w(size_t x) { return (x + 255) & ~s
 // order in which two stacked accumulator tiles hold the other operand (state
 // rows for W, the tokens of D for Kt^T and M).
 //   w   [DK / 32 key blocks][4 token tiles][hi, lo]      rows: tokens, k: keys
+//   qf  [DK / 32 key blocks][4 token tiles][hi, lo]      scale diag(gam) Q, as w
 //   kt  [DK / 16 key tiles][2 token blocks][hi, lo]      rows: keys, k: tokens
 //   ms  [6 lower blocks][hi, lo]                          rows: tokens, k: tokens
 //   u   [d_v / 16 column tiles][4 token tiles][64 lanes][4] f32, accumulator order
-//   gam [64] f32 gam_t, then gam_last
+//   gam gam_last (f32, in a 256-byte slot)
 struct WideRec {
-  size_t w, kt, ms, u, gam, bytes;
+  size_t w, qf, kt, ms, u, gam, bytes;
   __host__ __device__ WideRec(int dk, int dv) {
     w = 0;
-    kt = w + static_cast<size_t>(dk / 32) * 8 * 1024;
+    qf = w + static_cast<size_t>(dk / 32) * 8 * 1024;
+    kt = qf + static_cast<size_t>(dk / 32) * 8 * 1024;
     ms = kt + static_cast<size_t>(dk / 16) * 4 * 1024;
     u = ms + 12 * 1024;
     gam = u + static_cast<size_t>(dv / 16) * 4 * 1024;
-    bytes = align256w(gam + 512);
+    bytes = align256w(gam + 256);
   }
 };
 
@@ -135,18 +137,17 @@ struct WidePrepLds {
   static constexpr int kTf = kAf + kC * kSF * 4;         // T      [C][SF] f32
   static constexpr int kMf = kTf + kC * kSF * 4;         // M      [C][SF] f32
   static constexpr int kTb = kMf + kC * kSF * 4;         // T diag(beta)      [hi, lo][C][SH] bf16
-  static constexpr int kTg = kTb + 2 * kC * kSH * 2;     // T diag(beta gam)  [hi, lo][C][SH] bf16
-  static constexpr int kXs = kTg + 2 * kC * kSH * 2;     // solve scratch [4][16][20] f32
+  static constexpr int kXs = kTb + 2 * kC * kSH * 2;     // solve scratch [4][16][20] f32
   static constexpr int kGd = kXs + 4 * 16 * 20 * 4;      // G   [C] f64 (log2 units)
   static constexpr int kGam = kGd + kC * 8;              // gam [C] f32
   static constexpr int kEps = kGam + kC * 4;             // exp(G_last - G) [C] f32
   static constexpr int kBet = kEps + kC * 4;             // beta [C] f32
   static constexpr int kBytes = kBet + kC * 4;
-  static_assert(kBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+  static_assert(2 * kBytes <= 160 * 1024, "two workgroups per gfx950 compute unit");
 };
 
 template <int DK, bool RAW>
-__global__ __launch_bounds__(kThreads) void wide_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void wide_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
                                                              const int32_t* cs, const int2* __restrict__ info) {
   using L_ = WidePrepLds;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -154,7 +155,6 @@ __global__ __launch_bounds__(kThreads) void wide_prep_kernel(ScanParams p, unsig
   float* Tf = reinterpret_cast<float*>(smem + L_::kTf);
   float* Mf = reinterpret_cast<float*>(smem + L_::kMf);
   __bf16* Tb = reinterpret_cast<__bf16*>(smem + L_::kTb);
-  __bf16* Tg = reinterpret_cast<__bf16*>(smem + L_::kTg);
   float* Xs = reinterpret_cast<float*>(smem + L_::kXs);
   double* Gd = reinterpret_cast<double*>(smem + L_::kGd);
   float* Gam = reinterpret_cast<float*>(smem + L_::kGam);
@@ -209,9 +209,7 @@ __global__ __launch_bounds__(kThreads) void wide_prep_kernel(ScanParams p, unsig
     Gam[lane] = gam;
     Eps[lane] = fast_exp2(static_cast<float>(Glast - G));
     Bet[lane] = b;
-    float* gr = reinterpret_cast<float*>(base + rec.gam);
-    gr[lane] = gam;
-    if (lane == 63) gr[64] = gam;
+    if (lane == 63) *reinterpret_cast<float*>(base + rec.gam) = gam;
   }
   __syncthreads();
 
@@ -313,26 +311,23 @@ __global__ __launch_bounds__(kThreads) void wide_prep_kernel(ScanParams p, unsig
     }
     __syncthreads();
   }
-  // T diag(beta) and T diag(beta gam), split
+  // T diag(beta), split
   for (int e = tid; e < kC * kC; e += kThreads) {
     const int t = e >> 6, s = e & 63;
     const float tv = (s <= t) ? Tf[t * kSF + s] : 0.0f;
     const float xb = tv * Bet[s];
-    const float xg = xb * Gam[s];
-    const __bf16 hb = static_cast<__bf16>(xb), hg = static_cast<__bf16>(xg);
+    const __bf16 hb = static_cast<__bf16>(xb);
     Tb[t * kSH + s] = hb;
     Tb[kC * kSH + t * kSH + s] = static_cast<__bf16>(xb - static_cast<float>(hb));
-    Tg[t * kSH + s] = hg;
-    Tg[kC * kSH + t * kSH + s] = static_cast<__bf16>(xg - static_cast<float>(hg));
   }
   __syncthreads();
 
-  // ================= 4. Kt^T fragments and W (as W^T tiles, which are W's
-  // operand fragments in the permuted key order)
+  // ================= 4. Kt^T, W and scale diag(gam) Q fragments.  W^T =
+  // (diag(gam) K)^T (T diag(beta))^T is formed in accumulator tiles, which are
+  // W's operand fragments in the permuted key order.
   {
-    // B operand of W^T = K^T (T diag(beta gam))^T: lane supplies
-    // Tg[token 16 tt + r16][token' 32 kb + slot_k(g, e)], token' <= token
-    Split8 TG[2][4];
+    // B operand: lane supplies Tb[token 16 tt + r16][token' 32 kb + slot_k(g, e)], token' <= token
+    Split8 TB[2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -341,56 +336,78 @@ __global__ __launch_bounds__(kThreads) void wide_prep_kernel(ScanParams p, unsig
         const int off = (16 * tt + r16) * kSH + 32 * kb + 4 * g;
 #pragma unroll
         for (int hl = 0; hl < 2; ++hl) {
-          const __bf16* src = Tg + hl * kC * kSH + off;
+          const __bf16* src = Tb + hl * kC * kSH + off;
           const uint2 lo4 = *reinterpret_cast<const uint2*>(src);
           const uint2 hi4 = *reinterpret_cast<const uint2*>(src + 16);
           const u32x4w v = {lo4.x, lo4.y, hi4.x, hi4.y};
-          (hl == 0 ? TG[kb][tt].hi : TG[kb][tt].lo) = __builtin_bit_cast(bf16x8, v);
+          (hl == 0 ? TB[kb][tt].hi : TB[kb][tt].lo) = __builtin_bit_cast(bf16x8, v);
         }
       }
-    constexpr int PAIRS = DK / 128;  // key-block pairs (two key tiles each) per wave
+    constexpr int PAIRS = DK / 128;  // key blocks of 32 (two key tiles each) per wave
+    float gq[4];                     // scale gam of this lane's Q rows
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) gq[tt] = p.scale * Gam[16 * tt + r16];
 #pragma unroll
     for (int pr = 0; pr < PAIRS; ++pr) {
       const int kbk = w * PAIRS + pr;  // key block of 32
+      // every load of the block first: K^T slots (two key tiles x two token
+      // blocks), Q rows (four token tiles)
+      float x[2][2][8], qv[4][8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[half][kb][e] = krow(32 * kb + slot_k(g, e))[32 * kbk + 16 * half + r16];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) load8_perm(qrow(16 * tt + r16) + 32 * kbk + 4 * g, qv[tt]);
+
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[tt][e] *= gq[tt];
+        const Split8 qs = split8(qv[tt]);
+        store_frag(base + rec.qf + ((kbk * 4 + tt) * 2) * 1024, qs.hi, lane);
+        store_frag(base + rec.qf + ((kbk * 4 + tt) * 2 + 1) * 1024, qs.lo, lane);
+      }
       f32x4 acc[2][4];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int r = 2 * kbk + half;  // key tile
-        const int key = 16 * r + r16;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) acc[half][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          float x[8], xe[8];
+          float xe[8], xg[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int tok = 32 * kb + slot_k(g, e);
-            x[e] = krow(tok)[key];
-            xe[e] = x[e] * Eps[tok];
+            xe[e] = x[half][kb][e] * Eps[tok];
+            xg[e] = x[half][kb][e] * Gam[tok];
           }
           const Split8 KE = split8(xe);
           store_frag(base + rec.kt + ((r * 2 + kb) * 2) * 1024, KE.hi, lane);
           store_frag(base + rec.kt + ((r * 2 + kb) * 2 + 1) * 1024, KE.lo, lane);
-          const Split8 KW = split8(x);
+          const Split8 KW = split8(xg);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             if (kb == 1 && tt < 2) continue;
-            acc[half][tt] = mma3(acc[half][tt], KW, TG[kb][tt]);
+            acc[half][tt] = mma3(acc[half][tt], KW, TB[kb][tt]);
           }
         }
       }
       // acc[half][tt] element i of lane l: W[token 16 tt + r16][key 16 (2 kbk + half) + 4 g + i]
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        float x[8];
+        float xw[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[i] = acc[0][tt][i];
-          x[4 + i] = acc[1][tt][i];
+          xw[i] = acc[0][tt][i];
+          xw[4 + i] = acc[1][tt][i];
         }
-        const Split8 s = split8(x);
-        store_frag(base + rec.w + ((kbk * 4 + tt) * 2) * 1024, s.hi, lane);
-        store_frag(base + rec.w + ((kbk * 4 + tt) * 2 + 1) * 1024, s.lo, lane);
+        const Split8 sw = split8(xw);
+        store_frag(base + rec.w + ((kbk * 4 + tt) * 2) * 1024, sw.hi, lane);
+        store_frag(base + rec.w + ((kbk * 4 + tt) * 2 + 1) * 1024, sw.lo, lane);
       }
     }
   }
@@ -447,17 +464,14 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
   const int units = p.num_seqs * p.h_v;
   if (unit >= units) return;
   const int n = unit / p.h_v, h = unit % p.h_v;
-  const int hq = h / p.ratio;
   const int d_v = p.d_v;
   const int T = p.total_tokens;
   const int tid = static_cast<int>(threadIdx.x);
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = tid >> 6, lane = tid & 63, r16 = lane & 15;
   const int col = 16 * ct + r16;
   const int key0 = w * (DK / 4);
   const WideRec rec(DK, d_v);
-  const float* qg = static_cast<const float*>(p.q);
   float* og = static_cast<float*>(p.out);
-  const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
   const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
 
   bool has_state = true;
@@ -476,30 +490,39 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
   const int lo = wseq_lo(p.cu, n, T), hi = wseq_hi(p.cu, n, T);
   const int nchunks = (hi - lo + kC - 1) / kC;
   const int c0 = cs[n];
-  for (int j = 0; j < nchunks; ++j) {
-    const int t0 = lo + kC * j;
-    const int Lc = min(kC, hi - t0);
-    const unsigned char* rb = ws + (static_cast<size_t>(c0 + j) * p.h_v + h) * rec_bytes;
-    const int buf = j & 1;
-
-    // ---- loads of this chunk
-    Split8 WA[KB][4];
+  // Operands of the partial products W S and Q S (set A) are loaded one chunk
+  // ahead, into the second of two register sets, as soon as the current
+  // chunk's products have read them; the operands used after the barrier
+  // (set B: Kt^T, M, U, the decay factors) are issued at the top of their
+  // own chunk.  Loads of a chunk past the last are clamped to the last one.
+  struct SetA {
+    Split8 W[KB][4];
+    Split8 Q[KB][4];
+  };
+  auto rec_of = [&](int j) __attribute__((always_inline)) {
+    return ws + (static_cast<size_t>(c0 + min(j, nchunks - 1)) * p.h_v + h) * rec_bytes;
+  };
+  auto load_a = [&](int j, SetA& a) __attribute__((always_inline)) {
+    const unsigned char* rb = rec_of(j);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const unsigned char* f = rb + rec.w + (((w * KB + kb) * 4 + tt) * 2) * 1024;
-        WA[kb][tt].hi = load_frag(f, lane);
-        WA[kb][tt].lo = load_frag(f + 1024, lane);
+        const size_t f = (((w * KB + kb) * 4 + tt) * 2) * 1024;
+        a.W[kb][tt].hi = load_frag(rb + rec.w + f, lane);
+        a.W[kb][tt].lo = load_frag(rb + rec.w + f + 1024, lane);
+        a.Q[kb][tt].hi = load_frag(rb + rec.qf + f, lane);
+        a.Q[kb][tt].lo = load_frag(rb + rec.qf + f + 1024, lane);
       }
-    float qx[4][KB][8];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const float* qr = qg + static_cast<size_t>(t0 + min(16 * tt + r16, Lc - 1)) * qk_stride +
-                        static_cast<size_t>(hq) * DK + key0 + 4 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) load8_perm(qr + 32 * kb, qx[tt][kb]);
-    }
+  };
+
+  auto chunk = [&](int j, SetA& cur, SetA& nxt) __attribute__((always_inline)) {
+    const int t0 = lo + kC * j;
+    const int Lc = min(kC, hi - t0);
+    const unsigned char* rb = rec_of(j);
+    const int buf = j & 1;
+
+    // ---- set B of this chunk
     Split8 KtA[KT][2];
 #pragma unroll
     for (int r = 0; r < KT; ++r)
@@ -521,9 +544,7 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
       U[tt] = *reinterpret_cast<const f32x4*>(rb + rec.u + ((static_cast<size_t>(ct) * 4 + tt) * 64 + lane) * 16);
-    const float* gr = reinterpret_cast<const float*>(rb + rec.gam);
-    const f32x4 gam4 = *reinterpret_cast<const f32x4*>(gr + 16 * w + 4 * g);
-    const float gam_last = gr[64];
+    const float gam_last = *reinterpret_cast<const float*>(rb + rec.gam);
 
     // ---- partial W S and Q S over this wave's rows
     Split8 SB[KB];
@@ -542,12 +563,13 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
       f32x4 xa = {0.0f, 0.0f, 0.0f, 0.0f}, ya = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        xa = mma3(xa, WA[kb][tt], SB[kb]);
-        ya = mma3(ya, split8(qx[tt][kb]), SB[kb]);
+        xa = mma3(xa, cur.W[kb][tt], SB[kb]);
+        ya = mma3(ya, cur.Q[kb][tt], SB[kb]);
       }
       part[buf][0][w][tt][lane] = xa;
       part[buf][1][w][tt][lane] = ya;
     }
+    load_a(j + 1, nxt);
     __syncthreads();
 
     // ---- D = U - W S (every wave, all tokens), O for token tile w
@@ -582,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
         const int t = 16 * w + acc_row(lane, i);
         if (t < Lc)
           og[static_cast<size_t>(t0 + t) * v_stride + static_cast<size_t>(h) * d_v + col] =
-              fmaf(p.scale * gam4[i], y[i], o[i]);
+              y[i] + o[i];
       }
     }
 
@@ -593,6 +615,15 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
       s = mma3(s, KtA[r][0], DB[0]);
       s = mma3(s, KtA[r][1], DB[1]);
       S[r] = s;
+    }
+  };
+
+  if (nchunks > 0) {
+    SetA a0, a1;
+    load_a(0, a0);
+    for (int j = 0; j < nchunks; j += 2) {
+      chunk(j, a0, a1);
+      if (j + 1 < nchunks) chunk(j + 1, a1, a0);
     }
   }
 
