@@ -260,10 +260,24 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=Tru
     assert torch.isfinite(out.float()).all()
     nbytes = algorithmic_bytes(shape, inp)
     hbm_gbs = nbytes / (ms * 1e-3) / 1e9
-    chunked = algorithm == "chunked" or (
+    # the float32 chunked form (two passes, products on split bf16 operands) runs
+    # whenever the workspace is given for float32 I/O
+    wide = shape.io_dtype == torch.float32 and ws_bytes > 0
+    chunked = wide or algorithm == "chunked" or (
         algorithm == "auto" and shape.io_dtype == torch.bfloat16 and shape.d_k in (64, 128)
         and shape.d_v % 8 == 0 and T >= 64 * n)
-    if chunked:
+    if wide:
+        # three bf16 MFMA products (hi.hi + hi.lo + lo.hi) per float32-class product
+        fl = 3 * chunked_flops(shape, T)
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+                "traffic": _traffic(shape.name + "_chunked_f32",
+                                    ["prefill_wide.hip", "prefill_split.hip", "chunk_mfma.hpp", "gdn_device.hpp"]),
+                "kernel": "wide_prep_kernel + wide_state_kernel (float32 I/O, chunked in two passes, split-bf16 MFMA)",
+                "algorithmic_bytes_per_launch": nbytes, "workspace_bytes": ws_bytes,
+                "mfma_tflops": round(fl / (ms * 1e-3) / 1e12, 2), "mfma_frac_of_bf16_peak":
+                    round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+    elif chunked:
         # the chunked form's intensity (~180 flop/B at d = 128) is below the bf16 MFMA
         # ridge (2.5 PFLOP/s / 8 TB/s ~ 312 flop/B): HBM bounds it
         fl = chunked_flops(shape, T)
@@ -297,7 +311,8 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=Tru
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "roofline": roof,
         "config": {"workload": shape.name,
-                   "algorithm": ("chunked, two passes" if ws_bytes else "chunked") if chunked else "serial",
+                   "algorithm": (("chunked, two passes, split-bf16 products" if wide else "chunked, two passes")
+                                 if ws_bytes else "chunked") if chunked else "serial",
                    "num_seqs": n,
                    "total_tokens": T, "seqlens": inp.seqlens, "h_qk": shape.h_qk, "h_v": shape.h_v,
                    "d_k": shape.d_k, "d_v": shape.d_v,

@@ -75,11 +75,18 @@ __device__ __forceinline__ int seq_hi(const int32_t* cu, int n, int T) {
 }
 
 // cs[n] = chunks of the sequences before n; cs[N] = all chunks; info[c] =
-// (first token, tokens) of chunk c.
+// (first token, tokens) of chunk c.  A thread writes the entries of its own
+// short sequences; those of long ones (up to 256 of them) are written by the
+// whole block, so that one long sequence does not leave a single thread
+// writing hundreds of entries.
 __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int num_seqs, int T, int32_t* cs,
                                                            int2* info) {
+  constexpr int kLongChunks = 16, kMaxLong = 256;
   __shared__ int part[1024];
+  __shared__ int nlong;
+  __shared__ int2 longs[kMaxLong];  // (sequence, its first chunk)
   const int tid = static_cast<int>(threadIdx.x);
+  if (tid == 0) nlong = 0;
   const int per = (num_seqs + 1023) / 1024;
   const int a = min(tid * per, num_seqs), b = min(a + per, num_seqs);
   auto chunks = [&](int n) { return (seq_hi(cu, n, T) - seq_lo(cu, n, T) + kC - 1) / kC; };
@@ -97,7 +104,21 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
   for (int n = a; n < b; ++n) {
     cs[n] = run;
     const int lo = seq_lo(cu, n, T), hi = seq_hi(cu, n, T);
-    for (int t = lo; t < hi; t += kC) info[run++] = make_int2(t, min(kC, hi - t));
+    const int cnt = (hi - lo + kC - 1) / kC;
+    const int slot = cnt > kLongChunks ? atomicAdd(&nlong, 1) : kMaxLong;
+    if (slot < kMaxLong) {
+      longs[slot] = make_int2(n, run);
+      run += cnt;
+    } else {
+      for (int t = lo; t < hi; t += kC) info[run++] = make_int2(t, min(kC, hi - t));
+    }
+  }
+  __syncthreads();
+  const int m = min(nlong, kMaxLong);
+  for (int i = 0; i < m; ++i) {
+    const int n = longs[i].x, c0 = longs[i].y;
+    const int lo = seq_lo(cu, n, T), hi = seq_hi(cu, n, T);
+    for (int t = lo + kC * tid; t < hi; t += kC * 1024) info[c0 + (t - lo) / kC] = make_int2(t, min(kC, hi - t));
   }
   if (tid == 1023) cs[num_seqs] = part[1023];
 }

@@ -684,10 +684,7 @@ bool wide_supported(int io_dtype, int d_k, int d_v, const GateArgs& gates, int w
          !gates.per_key && window == 0;
 }
 
-bool wide_auto(int d_k) {
-  (void)d_k;
-  return false;
-}
+bool wide_auto(int d_k) { return d_k == 256; }
 
 size_t wide_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v) {
   if (num_seqs <= 0) return 0;

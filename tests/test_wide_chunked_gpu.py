@@ -84,6 +84,20 @@ def test_wide_chunked_delta_rule_and_state_only():
     check(fin2, rf2, F32, "final state only")
 
 
+def test_wide_chunked_auto_with_workspace():
+    """GDN_ALGO_AUTO takes the float32 two-pass form at d_k = 256 when handed a workspace."""
+    shape = _shape(h_qk=2, h_v=4, d_k=256, d_v=32, init_state=True)
+    inp = synth.generate(shape, seqlens=[129, 70], seed=8)
+    g, beta = gates_for(inp)
+    nbytes = gdn.prefill_workspace_size(2, 4, 256, 32, torch.float32, 2, inp.total_tokens)
+    assert nbytes > 0
+    say("[wide-chunked] auto with a workspace")
+    out, fin = gpu_prefill(inp, g, beta, algorithm="auto", two_pass=True)
+    ro, rf = oracle_prefill(inp, g, beta)
+    check(out, ro, F32, "out")
+    check(fin, rf, F32, "final state")
+
+
 def test_wide_chunked_needs_workspace():
     shape = _shape(h_qk=1, h_v=1, d_k=256, d_v=16, init_state=False)
     inp = synth.generate(shape, seqlens=[64])
