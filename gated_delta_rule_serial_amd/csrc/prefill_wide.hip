@@ -40,6 +40,10 @@ constexpr int kThreads = 256;     // four waves
 constexpr int kSF = kC + 4;       // f32 row stride of the 64 x 64 matrices in LDS
 constexpr int kSH = kC + 8;       // bf16 row stride of the split T diag(beta) and T diag(beta gam)
 constexpr float kMinLogDecay = -1.0e4f;
+#ifndef WIDE_TOUCH_AHEAD
+#define WIDE_TOUCH_AHEAD 3
+#endif
+constexpr int kTouchAhead = WIDE_TOUCH_AHEAD;  // chunks between a record's touch and its use
 constexpr double kLog2e = 1.4426950408889634;
 
 __host__ __device__ constexpr size_t align256w(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -589,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
       part[buf][1][w][tt][lane] = ya;
     }
     load_a(j + 1, nxt);
-    if (touching) touch(j + 2);
+    if (touching) touch(j + kTouchAhead);
     __syncthreads();
 
     // ---- D = U - W S (every wave, all tokens), O for token tile w
