@@ -77,18 +77,22 @@ typedef enum gdn_gate_mode {
  * above; they differ only in rounding. */
 typedef enum gdn_algorithm {
   /* CHUNKED where it is supported and sequences average at least 64 tokens,
-   * SERIAL otherwise. */
+   * SERIAL otherwise.  For float32 I/O, CHUNKED is taken only at d_k = 256
+   * and only with a workspace (below). */
   GDN_ALGO_AUTO = 0,
   /* Token-by-token scan in float32 on the vector ALUs ([P4]'s order of
    * operations); any gates, any head size 1..256, float32, bfloat16 or
    * float16 I/O. */
   GDN_ALGO_SERIAL = 1,
-  /* The same recurrence in chunks of 64 tokens on the matrix cores (bf16
-   * operands, f32 accumulation, f32 state carried between chunks).  Needs
-   * bfloat16 I/O, d_k of 64 or 128 and d_v a multiple of 8, the gated-delta
-   * or delta rule with a per-head decay, no state history, and a true decay
-   * (g <= 0, as the raw-gate prologue always gives); otherwise
-   * GDN_ERR_UNSUPPORTED when requested explicitly. */
+  /* The same recurrence in chunks of 64 tokens on the matrix cores (f32
+   * accumulation, f32 state carried between chunks).  bfloat16 I/O: bf16
+   * operands, d_k of 64 or 128 and d_v a multiple of 8.  float32 I/O: every
+   * operand split into two bf16 parts and each product formed as
+   * hi.hi + hi.lo + lo.hi (float32-class accuracy), d_k of 128 or 256, d_v a
+   * multiple of 16 up to 256, and a workspace (the two-pass form only).
+   * Both need the gated-delta or delta rule with a per-head decay, no state
+   * history, and a true decay (g <= 0, as the raw-gate prologue always
+   * gives); otherwise GDN_ERR_UNSUPPORTED when requested explicitly. */
   GDN_ALGO_CHUNKED = 2
 } gdn_algorithm;
 
@@ -141,8 +145,10 @@ typedef struct gdn_problem {
    * gdn_prefill_slots).  When the chunked form runs and workspace_bytes is at
    * least gdn_prefill_workspace_size(), it runs in two passes: every chunk's
    * factors are prepared in parallel into the workspace, then a sequential
-   * pass carries the state from chunk to chunk.  Otherwise one pass walks
-   * each sequence chunk by chunk.  Both give the same result up to rounding.
+   * pass carries the state from chunk to chunk.  Otherwise (bfloat16 I/O
+   * only) one pass walks each sequence chunk by chunk.  Both give the same
+   * result up to rounding.  The float32 form needs about 270 KiB per chunk
+   * of 64 tokens and value head at d_k = d_v = 256.
    * The workspace is the caller's (16-byte aligned); its contents are
    * scratch, and calls that share it must not overlap in time. */
   void* workspace;
