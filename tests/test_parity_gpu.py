@@ -348,6 +348,23 @@ def test_chunked_prefill_resets_and_weak_decay(two_pass):
     check(fin, rf, TOL[torch.bfloat16], "final state")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_two_pass_chunk_table_many_long_sequences(dtype):
+    """The two-pass workspace's chunk table: a block-wide pass writes the
+    entries of sequences longer than 16 chunks, up to 256 of them; the rest
+    (here 14 more long ones) and the short ones are written per thread."""
+    lens = [1100 if i % 10 else 70 for i in range(300)]  # 270 long, 30 short, interleaved
+    d_k = 64 if dtype == torch.bfloat16 else 128
+    shape = _shape("varlen_prefill_8seq", h_qk=1, h_v=1, d_k=d_k, d_v=16, io_dtype=dtype, init_state=True)
+    inp = synth.generate(shape, seqlens=lens, seed=21)
+    g, beta = gates_for(inp)
+    say(f"[chunk table] {len(lens)} sequences, {inp.total_tokens} tokens, {dtype}")
+    out, fin = gpu_prefill(inp, g, beta, algorithm="chunked", two_pass=True)
+    ro, rf = oracle_prefill(inp, g, beta)
+    check(out, ro, TOL[dtype], "out")
+    check(fin, rf, TOL[dtype], "final state")
+
+
 def test_chunked_unsupported_is_reported():
     shape = _shape(init_state=False)  # float32 I/O, d_k 16
     inp = synth.generate(shape, seqlens=[64])
