@@ -448,9 +448,13 @@ def test_decode_slots(raw):
         assert torch.equal(pool_gpu[s].cpu(), pool[s]), f"untouched slot {s} changed"
 
 
-@pytest.mark.parametrize("algorithm", ["serial", "chunked", "two_pass"])
+@pytest.mark.parametrize("algorithm", ["serial", "chunked", "two_pass", "two_pass_f32"])
 def test_prefill_slots(algorithm):
-    shape = _shape("varlen_prefill_8seq", init_state=False)
+    if algorithm == "two_pass_f32":  # the float32 chunked form (d_k 256)
+        shape = _shape("wide_prefill_t32768_d256", h_qk=2, h_v=2, d_v=32, init_state=False)
+        algorithm = "two_pass"
+    else:
+        shape = _shape("varlen_prefill_8seq", init_state=False)
     inp = synth.generate(shape, seqlens=[70, 0, 33, 129])
     g, beta = gates_for(inp)
     slots = [5, -1, 2, 0]
