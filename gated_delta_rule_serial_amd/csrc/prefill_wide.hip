@@ -228,17 +228,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     const float* ka_row = krow(16 * tt + r16) + 8 * g;
     const float* qa_row = qrow(16 * tt + r16) + 8 * g;
+    // the rows of key block kb + 1 are loaded while block kb is multiplied
+    float xa[2][8], xq[2][8], xb[2][4][8];
+    auto fetch = [&](int kb, int buf) __attribute__((always_inline)) {
+      load8(ka_row + 32 * kb, xa[buf]);
+      load8(qa_row + 32 * kb, xq[buf]);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        if (st <= tt) load8(krow(16 * st + r16) + 8 * g + 32 * kb, xb[buf][st]);
+    };
+    fetch(0, 0);
+#pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb) {
-      float x[8];
-      load8(ka_row + 32 * kb, x);
-      const Split8 KA = split8(x);
-      load8(qa_row + 32 * kb, x);
-      const Split8 QA = split8(x);
+      const int buf = kb & 1;
+      if (kb + 1 < DK / 32) fetch(kb + 1, buf ^ 1);
+      const Split8 KA = split8(xa[buf]);
+      const Split8 QA = split8(xq[buf]);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         if (st <= tt) {
-          load8(krow(16 * st + r16) + 8 * g + 32 * kb, x);
-          const Split8 KB = split8(x);
+          const Split8 KB = split8(xb[buf][st]);
           pacc[st] = mma3(pacc[st], KA, KB);
           racc[st] = mma3(racc[st], QA, KB);
         }
@@ -351,20 +360,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     float gq[4];                     // scale gam of this lane's Q rows
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) gq[tt] = p.scale * Gam[16 * tt + r16];
+    // every load of the wave's key blocks first: K^T slots (two key tiles x
+    // two token blocks each), Q rows (four token tiles each)
+    float xk[PAIRS][2][2][8], xqv[PAIRS][4][8];
 #pragma unroll
     for (int pr = 0; pr < PAIRS; ++pr) {
-      const int kbk = w * PAIRS + pr;  // key block of 32
-      // every load of the block first: K^T slots (two key tiles x two token
-      // blocks), Q rows (four token tiles)
-      float x[2][2][8], qv[4][8];
+      const int kbk = w * PAIRS + pr;
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[half][kb][e] = krow(32 * kb + slot_k(g, e))[32 * kbk + 16 * half + r16];
+          for (int e = 0; e < 8; ++e) xk[pr][half][kb][e] = krow(32 * kb + slot_k(g, e))[32 * kbk + 16 * half + r16];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) load8_perm(qrow(16 * tt + r16) + 32 * kbk + 4 * g, qv[tt]);
+      for (int tt = 0; tt < 4; ++tt) load8_perm(qrow(16 * tt + r16) + 32 * kbk + 4 * g, xqv[pr][tt]);
+    }
+#pragma unroll
+    for (int pr = 0; pr < PAIRS; ++pr) {
+      const int kbk = w * PAIRS + pr;  // key block of 32
+      auto& x = xk[pr];
+      auto& qv = xqv[pr];
 
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
@@ -428,20 +443,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         TA[tt][kb].hi = *reinterpret_cast<const bf16x8*>(Tb + off);
         TA[tt][kb].lo = *reinterpret_cast<const bf16x8*>(Tb + kC * kSH + off);
       }
+    // the V columns of all this wave's column tiles are loaded first
+    // (d_v <= 256: at most four tiles per wave; past d_v the loads are clamped
+    // and unused)
     const int nct = d_v / 16;
-    for (int ct = w; ct < nct; ct += 4) {
-      const int col = 16 * ct + r16;
-      Split8 VB[2];
+    float xv[4][2][8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float x[8];
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int col = min(16 * (w + 4 * c4) + r16, d_v - 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tok = min(32 * kb + 8 * g + e, Lc - 1);
-          x[e] = vg[static_cast<size_t>(t0 + tok) * v_stride + static_cast<size_t>(h) * d_v + col];
+          xv[c4][kb][e] = vg[static_cast<size_t>(t0 + tok) * v_stride + static_cast<size_t>(h) * d_v + col];
         }
-        VB[kb] = split8(x);
-      }
+    }
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int ct = w + 4 * c4;
+      if (ct >= nct) break;
+      Split8 VB[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) VB[kb] = split8(xv[c4][kb]);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
