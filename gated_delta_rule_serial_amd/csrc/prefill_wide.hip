@@ -579,18 +579,24 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
         KtA[r][kb].hi = load_frag(f, lane);
         KtA[r][kb].lo = load_frag(f + 1024, lane);
       }
+    // M blocks of token tile w (one block for tiles 0 and 1, two for 2 and 3)
     Split8 MA[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int blk = m_block(w, kb < (w >> 1) + 1 ? kb : 0);
-      const unsigned char* f = rb + rec.ms + (2 * blk) * 1024;
-      MA[kb].hi = load_frag(f, lane);
-      MA[kb].lo = load_frag(f + 1024, lane);
+    {
+      const unsigned char* f = rb + rec.ms + (2 * m_block(w, 0)) * 1024;
+      MA[0].hi = load_frag(f, lane);
+      MA[0].lo = load_frag(f + 1024, lane);
+      if (w >= 2) {
+        f = rb + rec.ms + (2 * m_block(w, 1)) * 1024;
+        MA[1].hi = load_frag(f, lane);
+        MA[1].lo = load_frag(f + 1024, lane);
+      } else {
+        MA[1] = MA[0];
+      }
     }
-    f32x4 U[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      U[tt] = *reinterpret_cast<const f32x4*>(rb + rec.u + ((static_cast<size_t>(ct) * 4 + tt) * 64 + lane) * 16);
+    // U of token tile w: folded into this wave's partial of that tile, so
+    // that the sum of the partials is W S - U = -D
+    const f32x4 Uw =
+        *reinterpret_cast<const f32x4*>(rb + rec.u + ((static_cast<size_t>(ct) * 4 + w) * 64 + lane) * 16);
     const float gam_last = *reinterpret_cast<const float*>(rb + rec.gam);
 
     // ---- partial W S and Q S over this wave's rows
@@ -613,21 +619,21 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
         xa = mma3(xa, cur.W[kb][tt], SB[kb]);
         ya = mma3(ya, cur.Q[kb][tt], SB[kb]);
       }
-      part[buf][0][w][tt][lane] = xa;
+      part[buf][0][w][tt][lane] = tt == w ? xa - Uw : xa;
       part[buf][1][w][tt][lane] = ya;
     }
     load_a(j + 1, nxt);
     if (touching) touch(j + kTouchAhead);
     __syncthreads();
 
-    // ---- D = U - W S (every wave, all tokens), O for token tile w
+    // ---- D = U - W S = -(sum of the partials) (every wave, all tokens), O for token tile w
     f32x4 D[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       f32x4 x = part[buf][0][0][tt][lane];
 #pragma unroll
       for (int ww = 1; ww < 4; ++ww) x += part[buf][0][ww][tt][lane];
-      D[tt] = U[tt] - x;
+      D[tt] = -x;
     }
     f32x4 y = part[buf][1][0][w][lane];
 #pragma unroll
