@@ -293,6 +293,45 @@ def test_prefill_workspace_size(lib):
     assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), 1, 1, None) == INVALID
 
 
+def test_prefill_workspace_size_f32(lib):
+    """The float32 chunked form (two passes only): a record of split W, scale diag(gam) Q and
+    Kt^T fragments, M's six lower blocks (hi and lo, 1 KiB each), U in f32 and gam_last."""
+    size = ctypes.c_uint64(123)
+
+    def rec_bytes(d_k, d_v):
+        b = (d_k // 32) * 8 * 1024 * 2 + (d_k // 16) * 4 * 1024 + 12 * 1024 + (d_v // 16) * 4 * 1024 + 256
+        return (b + 255) // 256 * 256
+
+    wide = dict(io_dtype=gdn.GDN_F32, d_k=256, d_v=256, h_qk=8, h_v=8)
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**wide)), 1, 32768, ctypes.byref(size)) == gdn.GDN_OK
+    bound = (32768 + 63) // 64 + 1
+    assert rec_bytes(256, 256) == 268 * 1024 + 256
+    assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 8 * rec_bytes(256, 256)
+    # AUTO takes it at d_k = 256 only; CHUNKED at d_k 128 too
+    d128 = dict(wide, d_k=128, d_v=48)
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**d128)), 3, 1000, ctypes.byref(size)) == gdn.GDN_OK
+    assert size.value == 0
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**d128, algorithm=gdn.GDN_ALGO_CHUNKED)), 3, 1000,
+                                          ctypes.byref(size)) == gdn.GDN_OK
+    bound = (1000 + 63) // 64 + 3
+    assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 8 * rec_bytes(128, 48)
+    # geometries the float32 form does not serve
+    for kw in (dict(d_k=64), dict(d_v=24), dict(rule=2), dict(decay_per_key=1), dict(state_window=1),
+               dict(algorithm=gdn.GDN_ALGO_SERIAL)):
+        st = lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**{**wide, **kw})), 1, 32768, ctypes.byref(size))
+        assert st == gdn.GDN_OK and size.value == 0, kw
+
+
+def test_prefill_chunked_f32_without_workspace(lib):
+    prob = _prob(io_dtype=gdn.GDN_F32, d_k=256, d_v=32, h_qk=1, h_v=1, algorithm=gdn.GDN_ALGO_CHUNKED)
+    st = _prefill(lib, prob, n=1, cu_host=[0, 8], T=8)
+    assert st == gdn.GDN_ERR_UNSUPPORTED and "workspace" in gdn.last_error()
+    prob = _prob(io_dtype=gdn.GDN_F32, d_k=256, d_v=32, h_qk=1, h_v=1, algorithm=gdn.GDN_ALGO_CHUNKED,
+                 workspace=FAKE + 0x900000, workspace_bytes=1024)
+    st = _prefill(lib, prob, n=1, cu_host=[0, 8], T=8)
+    assert st == gdn.GDN_ERR_UNSUPPORTED and "too small a workspace" in gdn.last_error()
+
+
 def test_prefill_workspace_misaligned(lib):
     st = _prefill(lib, _prob(workspace=FAKE + 0x90008, workspace_bytes=1 << 20))
     assert st == INVALID and "workspace" in gdn.last_error()
