@@ -98,6 +98,21 @@ def test_wide_chunked_auto_with_workspace():
     check(fin, rf, F32, "final state")
 
 
+@pytest.mark.parametrize("in_place", [False, True], ids=["out_of_place", "in_place"])
+def test_wide_chunked_long_varlen(in_place):
+    """Long packed sequences of 313, 3, 0 and 141 chunks, the initial state
+    updated in place or written to a separate final state."""
+    lens = [20000, 130, 0, 9000]
+    shape = _shape(h_qk=1, h_v=2, d_k=128, d_v=16, init_state=True)
+    inp = synth.generate(shape, seqlens=lens, seed=13)
+    g, beta = gates_for(inp)
+    say(f"[wide-chunked long varlen] lens={lens} in_place={in_place}")
+    out, fin = gpu_prefill(inp, g, beta, algorithm="chunked", two_pass=True, in_place=in_place)
+    ro, rf = oracle_prefill(inp, g, beta)
+    check(out, ro, F32, "out")
+    check(fin, rf, F32, "final state")
+
+
 def test_wide_chunked_needs_workspace():
     shape = _shape(h_qk=1, h_v=1, d_k=256, d_v=16, init_state=False)
     inp = synth.generate(shape, seqlens=[64])
