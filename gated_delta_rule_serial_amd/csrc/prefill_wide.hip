@@ -545,8 +545,8 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
   };
 
   // The column tiles of a unit share each chunk's record through one L2.
-  // Each tile touches its share of the record two chunks ahead (one 4-byte
-  // load per 128-byte line), so the record comes in from HBM while earlier
+  // Each tile touches its share of the record kTouchAhead chunks ahead (one
+  // 4-byte load per 128-byte line), so the record comes in from HBM while earlier
   // chunks compute and the fragment loads meet L2 hits.  The touch is issued
   // after the chunk's other loads and its value is consumed a chunk later,
   // so no wait ever falls on it early (loads complete in issue order).
