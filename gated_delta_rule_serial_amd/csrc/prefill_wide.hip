@@ -740,7 +740,10 @@ bool wide_supported(int io_dtype, int d_k, int d_v, const GateArgs& gates, int w
          !gates.per_key && window == 0;
 }
 
-bool wide_auto(int d_k) { return d_k == 256; }
+// Measured against the serial scan (8 or 32 heads, 1 or 8 sequences of 128 to
+// 4096 tokens), the float32 chunked form is as fast at 128 tokens and faster
+// from 256 on, at d_k 128 and 256 alike.
+bool wide_auto(int d_k) { return d_k == 128 || d_k == 256; }
 
 size_t wide_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v) {
   if (num_seqs <= 0) return 0;

@@ -77,8 +77,8 @@ typedef enum gdn_gate_mode {
  * above; they differ only in rounding. */
 typedef enum gdn_algorithm {
   /* CHUNKED where it is supported and sequences average at least 64 tokens,
-   * SERIAL otherwise.  For float32 I/O, CHUNKED is taken only at d_k = 256
-   * and only with a workspace (below). */
+   * SERIAL otherwise.  For float32 I/O, CHUNKED is taken only with a
+   * workspace (below). */
   GDN_ALGO_AUTO = 0,
   /* Token-by-token scan in float32 on the vector ALUs ([P4]'s order of
    * operations); any gates, any head size 1..256, float32, bfloat16 or

@@ -283,7 +283,7 @@ def test_prefill_workspace_size(lib):
     per_rec = (per_rec + 255) // 256 * 256
     bound = 33173 // 64 + 1 + 8
     assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * per_rec
-    for kw in (dict(algorithm=gdn.GDN_ALGO_SERIAL), dict(io_dtype=gdn.GDN_F32), dict(d_k=96), dict(rule=2),
+    for kw in (dict(algorithm=gdn.GDN_ALGO_SERIAL), dict(io_dtype=gdn.GDN_F16), dict(d_k=96), dict(rule=2),
                dict(decay_per_key=1), dict(state_window=2)):
         st = lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**{**chunky, **kw})), 8, 33173, ctypes.byref(size))
         assert st == gdn.GDN_OK and size.value == 0, kw
@@ -307,14 +307,13 @@ def test_prefill_workspace_size_f32(lib):
     bound = (32768 + 63) // 64 + 1
     assert rec_bytes(256, 256) == 268 * 1024 + 256
     assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 8 * rec_bytes(256, 256)
-    # AUTO takes it at d_k = 256 only; CHUNKED at d_k 128 too
+    # d_k = 128: AUTO and CHUNKED alike
     d128 = dict(wide, d_k=128, d_v=48)
-    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**d128)), 3, 1000, ctypes.byref(size)) == gdn.GDN_OK
-    assert size.value == 0
-    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**d128, algorithm=gdn.GDN_ALGO_CHUNKED)), 3, 1000,
-                                          ctypes.byref(size)) == gdn.GDN_OK
     bound = (1000 + 63) // 64 + 3
-    assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 8 * rec_bytes(128, 48)
+    for algo in (gdn.GDN_ALGO_AUTO, gdn.GDN_ALGO_CHUNKED):
+        assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**d128, algorithm=algo)), 3, 1000,
+                                              ctypes.byref(size)) == gdn.GDN_OK
+        assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 8 * rec_bytes(128, 48)
     # geometries the float32 form does not serve
     for kw in (dict(d_k=64), dict(d_v=24), dict(rule=2), dict(decay_per_key=1), dict(state_window=1),
                dict(algorithm=gdn.GDN_ALGO_SERIAL)):
