@@ -23,10 +23,9 @@
 // Pass 1 (wide_prep_kernel): one workgroup per (chunk, value head) computes
 // W, scale diag(gam) Q, Kt^T and M as split operand fragments, U in float32
 // and gam_last into a caller-provided workspace.  Pass 2 (wide_state_kernel): one
-// workgroup of four waves per (sequence, value head, block of 16 state
-// columns); wave w owns rows [w d_k / 4, (w + 1) d_k / 4) of the state block
-// and the partial products W S and Q S over its rows meet in LDS once per
-// chunk.
+// workgroup of d_k / 32 waves per (sequence, value head, block of 16 state
+// columns); wave w owns rows [32 w, 32 w + 32) of the state block and the
+// partial products W S and Q S over its rows meet in LDS once per chunk.
 #include "chunk_mfma.hpp"
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
@@ -36,7 +35,7 @@ namespace gdn {
 namespace {
 
 constexpr int kC = 64;            // chunk length (tokens)
-constexpr int kThreads = 256;     // four waves
+constexpr int kThreads = 256;     // four waves (pass 1)
 constexpr int kSF = kC + 4;       // f32 row stride of the 64 x 64 matrices in LDS
 constexpr int kSH = kC + 8;       // bf16 row stride of the split T diag(beta) and T diag(beta gam)
 constexpr float kMinLogDecay = -1.0e4f;
@@ -478,14 +477,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // ---------------------------------------------------------------- pass 2
-// One workgroup per (sequence, value head, 16-column tile); wave w owns state
-// rows [w DK / 4, (w + 1) DK / 4) of the tile as KT accumulator tiles.
+// One workgroup per (sequence, value head, 16-column tile) with one wave per
+// 32 state rows (d_k / 32 waves: two per SIMD at d_k = 256, so that each
+// compute unit keeps twice the fragment loads of four waves in flight).  Wave
+// w holds rows [32 w, 32 w + 32) of the tile as two accumulator tiles.  Per
+// chunk, with two barriers:
+//  1. every wave forms its partial W S over its rows -> LDS; after the first
+//     barrier, its partial Q S -> LDS (both double-buffered by chunk parity);
+//  2. waves 0-3 sum the partials of token tile w: D = U - W S -> LDS;
+//  3. after the second barrier every wave reads D and updates its rows,
+//     S <- gam_C S + Kt^T D, and waves 0-3 write the output of token tile w,
+//     O = (sum of the Q S partials) + M D.
 template <int DK>
-__global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, const unsigned char* ws, size_t rec_bytes,
-                                                              const int32_t* cs, int units8) {
-  constexpr int KT = DK / 64;   // key tiles per wave
-  constexpr int KB = DK / 128;  // key blocks of 32 per wave
-  __shared__ __align__(16) f32x4 part[2][2][4][4][64];  // [buffer][X, Y][wave][token tile][lane]
+struct WideStateLds {
+  static constexpr int NW = DK / 32;
+  static constexpr int kX = 0;                              // X partials [2][NW][4 tt][64] f32x4
+  static constexpr int kY = kX + 2 * NW * 4 * 64 * 16;      // Y partials [2][NW][4 tt][64] f32x4
+  static constexpr int kD = kY + 2 * NW * 4 * 64 * 16;      // D          [4 tt][64] f32x4
+  static constexpr int kBytes = kD + 4 * 64 * 16;
+  static_assert(kBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+};
+
+template <int DK>
+__global__ __launch_bounds__(64 * (DK / 32)) void wide_state_kernel(ScanParams p, const unsigned char* ws,
+                                                                    size_t rec_bytes, const int32_t* cs, int units8) {
+  using L_ = WideStateLds<DK>;
+  constexpr int NW = L_::NW;
+  constexpr int kThr = 64 * NW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  f32x4* Xp = reinterpret_cast<f32x4*>(smem + L_::kX);
+  f32x4* Yp = reinterpret_cast<f32x4*>(smem + L_::kY);
+  f32x4* Dt = reinterpret_cast<f32x4*>(smem + L_::kD);
 
   const int unit = static_cast<int>(blockIdx.x) % units8;
   const int ct = static_cast<int>(blockIdx.x) / units8;
@@ -496,8 +518,9 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
   const int T = p.total_tokens;
   const int tid = static_cast<int>(threadIdx.x);
   const int w = tid >> 6, lane = tid & 63, r16 = lane & 15;
+  const int wt = w & 3;  // token tile of the second phase (waves 0-3)
   const int col = 16 * ct + r16;
-  const int key0 = w * (DK / 4);
+  const int key0 = 32 * w;
   const WideRec rec(DK, d_v);
   float* og = static_cast<float*>(p.out);
   const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
@@ -506,9 +529,9 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
   const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
   const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * DK * d_v;
 
-  f32x4 S[KT];
+  f32x4 S[2];
 #pragma unroll
-  for (int r = 0; r < KT; ++r)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       S[r][i] = (p.s0 != nullptr && has_state)
@@ -518,32 +541,36 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
   const int lo = wseq_lo(p.cu, n, T), hi = wseq_hi(p.cu, n, T);
   const int nchunks = (hi - lo + kC - 1) / kC;
   const int c0 = cs[n];
-  // Operands of the partial products W S and Q S (set A) are loaded one chunk
-  // ahead, into the second of two register sets, as soon as the current
-  // chunk's products have read them; the operands used after the barrier
-  // (set B: Kt^T, M, U, the decay factors) are issued at the top of their
-  // own chunk.  Loads of a chunk past the last are clamped to the last one.
   struct SetA {
-    Split8 W[KB][4];
-    Split8 Q[KB][4];
+    Split8 W[4];
+    Split8 Q[4];
   };
   auto rec_of = [&](int j) __attribute__((always_inline)) {
     return ws + (static_cast<size_t>(c0 + min(j, nchunks - 1)) * p.h_v + h) * rec_bytes;
   };
-  auto load_a = [&](int j, SetA& a) __attribute__((always_inline)) {
+  // The W fragments of the next chunk are loaded as soon as this chunk's W S
+  // products have read theirs, the Q fragments after the Q S products: one
+  // register set, refilled in two halves.  The operands used after the second
+  // barrier (set B: Kt^T, M, U, the decay factor) are issued at the top of
+  // their own chunk.  Loads of a chunk past the last are clamped to the last.
+  auto load_w = [&](int j, SetA& a) __attribute__((always_inline)) {
     const unsigned char* rb = rec_of(j);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const size_t f = (((w * KB + kb) * 4 + tt) * 2) * 1024;
-        a.W[kb][tt].hi = load_frag(rb + rec.w + f, lane);
-        a.W[kb][tt].lo = load_frag(rb + rec.w + f + 1024, lane);
-        a.Q[kb][tt].hi = load_frag(rb + rec.qf + f, lane);
-        a.Q[kb][tt].lo = load_frag(rb + rec.qf + f + 1024, lane);
-      }
+    for (int tt = 0; tt < 4; ++tt) {
+      const size_t f = ((w * 4 + tt) * 2) * 1024;  // key block w of 32, token tile tt
+      a.W[tt].hi = load_frag(rb + rec.w + f, lane);
+      a.W[tt].lo = load_frag(rb + rec.w + f + 1024, lane);
+    }
   };
-
+  auto load_q = [&](int j, SetA& a) __attribute__((always_inline)) {
+    const unsigned char* rb = rec_of(j);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const size_t f = ((w * 4 + tt) * 2) * 1024;
+      a.Q[tt].hi = load_frag(rb + rec.qf + f, lane);
+      a.Q[tt].lo = load_frag(rb + rec.qf + f + 1024, lane);
+    }
+  };
   // The column tiles of a unit share each chunk's record through one L2.
   // Each tile touches its share of the record kTouchAhead chunks ahead (one
   // 4-byte load per 128-byte line), so the record comes in from HBM while earlier
@@ -554,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
   const int nct = d_v / 16;
   const int lines = static_cast<int>(rec_bytes / 128);
   const int per_tile = (lines + nct - 1) / nct;
-  const bool touching = per_tile <= kThreads;
+  const bool touching = per_tile <= kThr;
   int touched = 0, tv = 0;
   auto touch = [&](int j) __attribute__((always_inline)) {
     touched += tv;
@@ -563,129 +590,126 @@ __global__ __launch_bounds__(kThreads) void wide_state_kernel(ScanParams p, cons
                                        static_cast<size_t>(line) * 128);
   };
 
-  auto chunk = [&](int j, SetA& cur, SetA& nxt) __attribute__((always_inline)) {
+  SetA a;
+  auto chunk = [&](int j) __attribute__((always_inline)) {
     const int t0 = lo + kC * j;
     const int Lc = min(kC, hi - t0);
     const unsigned char* rb = rec_of(j);
     const int buf = j & 1;
+    f32x4* Xb = Xp + buf * NW * 4 * 64;
+    f32x4* Yb = Yp + buf * NW * 4 * 64;
 
-    // ---- set B of this chunk
-    Split8 KtA[KT][2];
+    // ---- set B of this chunk: Kt^T over this wave's 32 rows; M blocks and
+    //      the U tile of token tile wt (used by waves 0-3)
+    Split8 KtA[2][2];
 #pragma unroll
-    for (int r = 0; r < KT; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const unsigned char* f = rb + rec.kt + (((w * KT + r) * 2 + kb) * 2) * 1024;
+        const unsigned char* f = rb + rec.kt + (((w * 2 + r) * 2 + kb) * 2) * 1024;
         KtA[r][kb].hi = load_frag(f, lane);
         KtA[r][kb].lo = load_frag(f + 1024, lane);
       }
-    // M blocks of token tile w (one block for tiles 0 and 1, two for 2 and 3)
     Split8 MA[2];
-    {
-      const unsigned char* f = rb + rec.ms + (2 * m_block(w, 0)) * 1024;
+    f32x4 Uw = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (w < 4) {
+      const unsigned char* f = rb + rec.ms + (2 * m_block(wt, 0)) * 1024;
       MA[0].hi = load_frag(f, lane);
       MA[0].lo = load_frag(f + 1024, lane);
-      if (w >= 2) {
-        f = rb + rec.ms + (2 * m_block(w, 1)) * 1024;
+      if (wt >= 2) {
+        f = rb + rec.ms + (2 * m_block(wt, 1)) * 1024;
         MA[1].hi = load_frag(f, lane);
         MA[1].lo = load_frag(f + 1024, lane);
       } else {
         MA[1] = MA[0];
       }
+      Uw = *reinterpret_cast<const f32x4*>(rb + rec.u + ((static_cast<size_t>(ct) * 4 + wt) * 64 + lane) * 16);
     }
-    // U of token tile w: folded into this wave's partial of that tile, so
-    // that the sum of the partials is W S - U = -D
-    const f32x4 Uw =
-        *reinterpret_cast<const f32x4*>(rb + rec.u + ((static_cast<size_t>(ct) * 4 + w) * 64 + lane) * 16);
     const float gam_last = *reinterpret_cast<const float*>(rb + rec.gam);
 
-    // ---- partial W S and Q S over this wave's rows
-    Split8 SB[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    // ---- 1. partial W S and Q S over this wave's rows (U of token tile w
+    //      folded into wave w's W S partial of that tile: the partials sum to -D)
+    Split8 SB;
+    {
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = S[2 * kb][i];
-        x[4 + i] = S[2 * kb + 1][i];
+        x[i] = S[0][i];
+        x[4 + i] = S[1][i];
       }
-      SB[kb] = split8(x);
+      SB = split8(x);
     }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      f32x4 xa = {0.0f, 0.0f, 0.0f, 0.0f}, ya = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        xa = mma3(xa, cur.W[kb][tt], SB[kb]);
-        ya = mma3(ya, cur.Q[kb][tt], SB[kb]);
-      }
-      part[buf][0][w][tt][lane] = tt == w ? xa - Uw : xa;
-      part[buf][1][w][tt][lane] = ya;
+      f32x4 xa = {0.0f, 0.0f, 0.0f, 0.0f};
+      xa = mma3(xa, a.W[tt], SB);
+      Xb[(w * 4 + tt) * 64 + lane] = tt == w ? xa - Uw : xa;
     }
-    load_a(j + 1, nxt);
+    load_w(j + 1, a);
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 ya = {0.0f, 0.0f, 0.0f, 0.0f};
+      ya = mma3(ya, a.Q[tt], SB);
+      Yb[(w * 4 + tt) * 64 + lane] = ya;
+    }
+    load_q(j + 1, a);
     if (touching) touch(j + kTouchAhead);
+
+    // ---- 2. waves 0-3: D of token tile w
+    if (w < 4) {
+      f32x4 x = Xb[w * 64 + lane];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) x += Xb[(ww * 4 + w) * 64 + lane];
+      Dt[w * 64 + lane] = -x;
+    }
     __syncthreads();
 
-    // ---- D = U - W S = -(sum of the partials) (every wave, all tokens), O for token tile w
-    f32x4 D[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      f32x4 x = part[buf][0][0][tt][lane];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) x += part[buf][0][ww][tt][lane];
-      D[tt] = -x;
-    }
-    f32x4 y = part[buf][1][0][w][lane];
-#pragma unroll
-    for (int ww = 1; ww < 4; ++ww) y += part[buf][1][ww][w][lane];
+    // ---- 3. D fragments; the output of tile w (waves 0-3); the state update
     Split8 DB[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      const f32x4 d0 = Dt[(2 * kb) * 64 + lane], d1 = Dt[(2 * kb + 1) * 64 + lane];
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = D[2 * kb][i];
-        x[4 + i] = D[2 * kb + 1][i];
+        x[i] = d0[i];
+        x[4 + i] = d1[i];
       }
       DB[kb] = split8(x);
     }
-    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-    o = mma3(o, MA[0], DB[0]);
-    if (w >= 2) o = mma3(o, MA[1], DB[1]);
-    if (og != nullptr) {
+    if (w < 4 && og != nullptr) {
+      f32x4 y = Yb[w * 64 + lane];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) y += Yb[(ww * 4 + w) * 64 + lane];
+      f32x4 o = mma3(y, MA[0], DB[0]);
+      if (w >= 2) o = mma3(o, MA[1], DB[1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * w + acc_row(lane, i);
-        if (t < Lc)
-          og[static_cast<size_t>(t0 + t) * v_stride + static_cast<size_t>(h) * d_v + col] =
-              y[i] + o[i];
+        if (t < Lc) og[static_cast<size_t>(t0 + t) * v_stride + static_cast<size_t>(h) * d_v + col] = o[i];
       }
     }
-
-    // ---- S <- gam_last S + Kt^T D over this wave's rows
 #pragma unroll
-    for (int r = 0; r < KT; ++r) {
-      f32x4 s = S[r] * gam_last;
-      s = mma3(s, KtA[r][0], DB[0]);
-      s = mma3(s, KtA[r][1], DB[1]);
-      S[r] = s;
+    for (int r = 0; r < 2; ++r) {
+      f32x4 sacc = S[r] * gam_last;
+      sacc = mma3(sacc, KtA[r][0], DB[0]);
+      sacc = mma3(sacc, KtA[r][1], DB[1]);
+      S[r] = sacc;
     }
   };
 
   if (nchunks > 0) {
-    SetA a0, a1;
-    load_a(0, a0);
-    for (int j = 0; j < nchunks; j += 2) {
-      chunk(j, a0, a1);
-      if (j + 1 < nchunks) chunk(j + 1, a1, a0);
-    }
+    load_w(0, a);
+    load_q(0, a);
+    for (int j = 0; j < nchunks; ++j) chunk(j);
   }
 
   // keeps the touches alive (never true: the host rejects negative token counts)
   if (p.total_tokens < 0 && touched + tv == 1) og[0] = 0.0f;
   if (p.sN != nullptr && has_state) {
 #pragma unroll
-    for (int r = 0; r < KT; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         p.sN[sbase + static_cast<size_t>(key0 + 16 * r + acc_row(lane, i)) * d_v + col] = S[r][i];
@@ -729,7 +753,14 @@ hipError_t launch_dk(const ScanParams& p, unsigned char* recs, size_t rec_bytes,
   // are dealt to the eight XCDs in turn), sharing its L2
   const int units8 = (units + 7) / 8 * 8;
   const unsigned blocks = static_cast<unsigned>(units8) * static_cast<unsigned>(p.d_v / 16);
-  hipLaunchKernelGGL((wide_state_kernel<DK>), dim3(blocks), dim3(kThreads), 0, stream, p, recs, rec_bytes, cs, units8);
+  {
+    static bool cfg = false;
+    constexpr int bytes = WideStateLds<DK>::kBytes;
+    auto kern = wide_state_kernel<DK>;
+    const hipError_t e = set_lds_once(kern, bytes, &cfg);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (DK / 32)), bytes, stream, p, recs, rec_bytes, cs, units8);
+  }
   return hipGetLastError();
 }
 
