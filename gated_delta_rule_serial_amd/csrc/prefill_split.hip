@@ -20,7 +20,9 @@
 // W, Kt^T, M, U and gam into a caller-provided workspace; all chunks of all
 // sequences run at once.  Pass 2 (chunk_state_kernel): one workgroup per
 // (sequence, value head, column block) walks its sequence's chunks, doing only
-// the four products above with the state in MFMA accumulators.  The serial
+// the four products above with the state in MFMA accumulators; for few units
+// at d_k = 128, chunk_rows_kernel splits each 16-column tile's state rows over
+// four waves instead.  The serial
 // chain per chunk shrinks from the whole chunked step to those four products,
 // and pass 1 fills the whole chip however few sequences and heads there are.
 // A chunk table (chunk_table_kernel) maps the packed sequences to chunks.
@@ -745,6 +747,195 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
   }
 }
 
+// The state pass for few (sequence, head) units, at d_k = 128: one workgroup
+// of four waves per (sequence, value head, 16-column tile), wave w owning
+// state rows [32 w, 32 w + 32) of the tile as two accumulator tiles.  Where
+// the column-block form above would leave most compute units idle (32 heads
+// of one sequence fill 64 of them), this form puts a head's 16-column tiles on
+// as many compute units, and each wave loads only the fragments of its own
+// key block, straight into registers.  Per chunk, with two barriers:
+//  1. every wave forms its partial W S over its rows -> LDS; after the first
+//     barrier, its partial diag(gam) Q S -> LDS (double-buffered by chunk parity);
+//  2. wave w sums the partials of token tile w: D = U - W S -> LDS;
+//  3. after the second barrier every wave packs D and updates its rows,
+//     S <- gam_last S + Kt^T D, and wave w writes the output of token tile w,
+//     O = scale ((sum of the Q S partials) + M D).
+constexpr int kRowWaves = 4;
+constexpr int kRowTouchAhead = 3;  // chunks between a record's touch and its use
+
+template <int DVT>
+__global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p, const unsigned char* ws,
+                                                                   size_t rec_bytes, const int32_t* cs, int units8) {
+  constexpr int DK = 128;
+  constexpr int KB = DK / 32;
+  constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16);
+  __shared__ __align__(16) f32x4 xpart[2][kRowWaves][4][64];  // [buffer][wave][token tile][lane]
+  __shared__ __align__(16) f32x4 ypart[2][kRowWaves][4][64];
+  __shared__ __align__(16) f32x4 dt[4][64];                    // D per token tile
+
+  const int unit = static_cast<int>(blockIdx.x) % units8;
+  const int ct = static_cast<int>(blockIdx.x) / units8;
+  if (unit >= p.num_seqs * p.h_v) return;  // the grid is padded to whole rounds of 8 units
+  const int n = unit / p.h_v, h = unit % p.h_v;
+  const int d_v = p.d_v;
+  const int T = p.total_tokens;
+  const int tid = static_cast<int>(threadIdx.x);
+  // w is wave-uniform, and the compiler is told so: a branch on it must skip
+  // its MFMAs, which run whatever the execution mask
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int col = 16 * ct + acc_col(lane);
+  const bool col_ok = col < d_v;
+  const Rec rec(DK, 16 * DVT);
+  bf16_t* og = static_cast<bf16_t*>(p.out);
+  const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
+
+  bool has_state = true;
+  const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
+  const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * DK * d_v;
+  f32x4 S[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[r][i] = (p.s0 != nullptr && has_state && col_ok)
+                    ? p.s0[sbase + static_cast<size_t>(32 * w + 16 * r + acc_row(lane, i)) * d_v + col]
+                    : 0.0f;
+
+  const int t_begin = seq_lo(p.cu, n, T), t_end = seq_hi(p.cu, n, T);
+  const int nchunks = (t_end - t_begin + kC - 1) / kC;
+  const int c_first = cs[n];
+  // loads of a chunk past the last are clamped to the last
+  auto record = [&](int j) __attribute__((always_inline)) {
+    return ws + (static_cast<size_t>(c_first + min(j, nchunks - 1)) * p.h_v + h) * rec_bytes;
+  };
+  auto frag = [&](const unsigned char* rb, int f) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(rb + rec.frag + (static_cast<size_t>(f) * 64 + lane) * 16);
+  };
+  auto pack = [](f32x4 a, f32x4 b) __attribute__((always_inline)) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = static_cast<__bf16>(a[i]);
+      r[4 + i] = static_cast<__bf16>(b[i]);
+    }
+    return r;
+  };
+  // W and diag(gam) Q of this wave's key block: the next chunk's are loaded
+  // as soon as this chunk's products have read them; the operands used after
+  // the second barrier (Kt^T, M, U, gam_last) at the top of their own chunk
+  bf16x8 Wf[4], Qf[4];
+  auto load_w = [&](int j) __attribute__((always_inline)) {
+    const unsigned char* rb = record(j);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) Wf[tt] = frag(rb, tt * KB + w);
+  };
+  auto load_q = [&](int j) __attribute__((always_inline)) {
+    const unsigned char* rb = record(j);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) Qf[tt] = frag(rb, FQ + tt * KB + w);
+  };
+  // The column tiles of a unit share each chunk's record through one L2 (they
+  // sit units8 blocks apart: on one XCD).  Each tile touches its share of the
+  // record kRowTouchAhead chunks ahead, one 4-byte load per 128-byte line, so
+  // the record comes in from HBM while earlier chunks compute; the touch is
+  // issued after the chunk's other loads and its value consumed a chunk
+  // later, so no wait falls on it early (loads complete in issue order).
+  const int ntiles = (d_v + 15) / 16;
+  const int lines = static_cast<int>(rec_bytes / 128);
+  const int per_tile = (lines + ntiles - 1) / ntiles;
+  const bool touching = per_tile <= 64 * kRowWaves;
+  int touched = 0, tv = 0;
+  auto touch = [&](int j) __attribute__((always_inline)) {
+    touched += tv;
+    const int line = min(ct * per_tile + tid, lines - 1);
+    tv = *reinterpret_cast<const int*>(record(j) + static_cast<size_t>(line) * 128);
+  };
+
+  auto chunk = [&](int j) __attribute__((always_inline)) {
+    const int t0 = t_begin + kC * j;
+    const int Lc = min(kC, t_end - t0);
+    const unsigned char* rb = record(j);
+    const int buf = j & 1;
+
+    bf16x8 KtA[2][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) KtA[r][kb] = frag(rb, FK + 2 * (2 * w + r) + kb);
+    bf16x8 MA[2];
+    MA[0] = frag(rb, FM + m_frag(w, 0));
+    MA[1] = w >= 2 ? frag(rb, FM + m_frag(w, 1)) : MA[0];
+    const f32x4 Uw = *reinterpret_cast<const f32x4*>(rb + rec.u + ((static_cast<size_t>(w) * DVT + ct) * 64 + lane) * 16);
+    const float gam_last = *reinterpret_cast<const float*>(rb + rec.g);
+
+    // ---- 1. partials over this wave's rows (U of token tile w folded into
+    //      wave w's W S partial of that tile: the partials sum to -D)
+    const bf16x8 SB = pack(S[0], S[1]);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const f32x4 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[tt], SB, (f32x4{0.0f, 0.0f, 0.0f, 0.0f}), 0, 0, 0);
+      xpart[buf][w][tt][lane] = tt == w ? x - Uw : x;
+    }
+    load_w(j + 1);
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      ypart[buf][w][tt][lane] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Qf[tt], SB, (f32x4{0.0f, 0.0f, 0.0f, 0.0f}), 0, 0, 0);
+    load_q(j + 1);
+    if (touching) touch(j + kRowTouchAhead);
+
+    // ---- 2. D of token tile w
+    {
+      f32x4 x = xpart[buf][0][w][lane];
+#pragma unroll
+      for (int ww = 1; ww < kRowWaves; ++ww) x += xpart[buf][ww][w][lane];
+      dt[w][lane] = -x;
+    }
+    __syncthreads();
+
+    // ---- 3. D as the B operand over tokens; the output of tile w; the state update
+    bf16x8 DB[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) DB[kb] = pack(dt[2 * kb][lane], dt[2 * kb + 1][lane]);
+    if (og != nullptr) {
+      f32x4 y = ypart[buf][0][w][lane];
+#pragma unroll
+      for (int ww = 1; ww < kRowWaves; ++ww) y += ypart[buf][ww][w][lane];
+      y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(MA[0], DB[0], y, 0, 0, 0);
+      if (w >= 2) y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(MA[1], DB[1], y, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * w + acc_row(lane, i);
+        if (t < Lc && col_ok)
+          og[static_cast<size_t>(t0 + t) * v_stride + static_cast<size_t>(h) * d_v + col] = to_bf16(p.scale * y[i]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      f32x4 sacc = S[r] * gam_last;
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KtA[r][0], DB[0], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KtA[r][1], DB[1], sacc, 0, 0, 0);
+      S[r] = sacc;
+    }
+  };
+
+  if (nchunks > 0) {
+    load_w(0);
+    load_q(0);
+    for (int j = 0; j < nchunks; ++j) chunk(j);
+  }
+
+  // keeps the touches alive (never true: the host rejects negative token counts)
+  if (p.total_tokens < 0 && touched + tv == 1) og[0] = 0;
+  if (p.sN != nullptr && has_state && col_ok) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.sN[sbase + static_cast<size_t>(32 * w + 16 * r + acc_row(lane, i)) * d_v + col] = S[r][i];
+  }
+}
+
 template <typename K>
 hipError_t set_lds(K kern, int bytes, bool* configured) {
   if (*configured) return hipSuccess;
@@ -763,6 +954,15 @@ int prep_workgroups() { return device_compute_units(); }
 // unit): the smaller blocks fill units left idle, and in a second round they
 // take the places freed by short sequences (the 8-sequence packed workload:
 // 1.07 against 1.10 ms).
+// The row-split state pass (16-column tiles) at d_k = 128 while its
+// workgroups take at most one round of the compute units: 32 heads of one
+// 4096-token sequence 0.196 against 0.244 ms, 8 heads 0.124 against 0.173 ms;
+// at two rounds (2 sequences x 32 heads) the column blocks are faster
+// (0.52 against 0.60 ms).
+bool split_rows(int d_k, int d_v, int units) {
+  return d_k == 128 && static_cast<int64_t>(units) * ((d_v + 15) / 16) <= device_compute_units();
+}
+
 int split_columns(int d_v, int units) {
   return d_v > 64 && static_cast<int64_t>(units) * ((d_v + 63) / 64) > 2 * static_cast<int64_t>(prep_workgroups()) ? 128 : 64;
 }
@@ -794,6 +994,14 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
   const int units = p.num_seqs * p.h_v;
   const unsigned blocks = static_cast<unsigned>((units + 7) / 8) * 8u * static_cast<unsigned>(p.col_blocks);
   if (units == 0) return hipSuccess;
+  if constexpr (DK == 128) {
+    if (split_rows(p.d_k, p.d_v, units)) {
+      const int units8 = (units + 7) / 8 * 8;
+      const unsigned rblocks = static_cast<unsigned>(units8) * static_cast<unsigned>((p.d_v + 15) / 16);
+      hipLaunchKernelGGL((chunk_rows_kernel<DVT>), dim3(rblocks), dim3(64 * kRowWaves), 0, stream, p, ws, rec_bytes, cs, units8);
+      return hipGetLastError();
+    }
+  }
   if (split_columns(p.d_v, units) == 128)
     hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, DVT>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
   else

@@ -517,7 +517,9 @@ __global__ __launch_bounds__(64 * (DK / 32)) void wide_state_kernel(ScanParams p
   const int d_v = p.d_v;
   const int T = p.total_tokens;
   const int tid = static_cast<int>(threadIdx.x);
-  const int w = tid >> 6, lane = tid & 63, r16 = lane & 15;
+  // w is wave-uniform, and the compiler is told so: a branch on it must skip
+  // its MFMAs, which run whatever the execution mask
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r16 = lane & 15;
   const int wt = w & 3;  // token tile of the second phase (waves 0-3)
   const int col = 16 * ct + r16;
   const int key0 = 32 * w;

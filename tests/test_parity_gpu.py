@@ -328,6 +328,31 @@ def test_chunked_prefill(case, two_pass):
     check(fin, rf, TOL[shape.io_dtype], "final state")
 
 
+# The bf16 two-pass state pass at d_k = 128 runs 16-column tiles with the
+# state rows split over four waves while those tiles take one round of the
+# compute units or less (256 on an MI355X), and blocks of 64 or 128 columns
+# otherwise.  Both forms against the oracle, on either side of that rule.
+TWO_PASS_FORMS = [
+    # (h_qk, h_v, d_v, seqlens, initial state updated in place)
+    (16, 32, 128, [300], False),         # 32 units x 8 tiles: row-split
+    (16, 32, 128, [300, 5], False),      # 64 units x 8 tiles: column blocks
+    (2, 4, 40, [2000, 1, 64], True),     # row-split, a ragged last tile, the state in place
+]
+
+
+@pytest.mark.parametrize("case", TWO_PASS_FORMS, ids=["rows_one_round", "columns_two_rounds", "rows_ragged_in_place"])
+def test_two_pass_state_forms(case):
+    h_qk, h_v, d_v, lens, in_place = case
+    shape = _shape("varlen_prefill_8seq", h_qk=h_qk, h_v=h_v, d_v=d_v, init_state=True)
+    say(f"[two-pass forms] {case}")
+    inp = synth.generate(shape, seqlens=lens, seed=21)
+    g, beta = gates_for(inp)
+    out, fin = gpu_prefill(inp, g, beta, algorithm="chunked", two_pass=True, in_place=in_place)
+    ro, rf = oracle_prefill(inp, g, beta)
+    check(out, ro, TOL[shape.io_dtype], "out")
+    check(fin, rf, TOL[shape.io_dtype], "final state")
+
+
 @pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "two_pass"])
 def test_chunked_prefill_resets_and_weak_decay(two_pass):
     """Log-decays of -inf (a reset), of 0 (no decay) and tiny beta in one sequence."""
