@@ -113,8 +113,11 @@ __device__ __forceinline__ int slot_k(int g, int e) { return 4 * g + (e & 3) + 1
 
 typedef unsigned u32x4w __attribute__((ext_vector_type(4)));
 
+// Record stores are nontemporal: the records (about 1 GiB at 32 K tokens and
+// d = 256) stream through, and the q and k rows that the preparation reads
+// again keep their place in L2.
 __device__ __forceinline__ void store_frag(unsigned char* dst, const bf16x8& f, int lane) {
-  *reinterpret_cast<bf16x8*>(dst + 16 * lane) = f;
+  __builtin_nontemporal_store(f, reinterpret_cast<bf16x8*>(dst + 16 * lane));
 }
 __device__ __forceinline__ bf16x8 load_frag(const unsigned char* src, int lane) {
   return *reinterpret_cast<const bf16x8*>(src + 16 * lane);
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         acc = mma3(acc, TA[tt][0], VB[0]);
         if (tt >= 2) acc = mma3(acc, TA[tt][1], VB[1]);
-        *reinterpret_cast<f32x4*>(base + rec.u + ((static_cast<size_t>(ct) * 4 + tt) * 64 + lane) * 16) = acc;
+        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(base + rec.u + ((static_cast<size_t>(ct) * 4 + tt) * 64 + lane) * 16));
       }
     }
   }
