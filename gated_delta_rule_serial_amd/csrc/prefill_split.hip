@@ -151,7 +151,8 @@ struct PrepLds {
 // and gates are loaded into registers while the current one computes.
 template <typename IO, int DK, int DVT, bool RAW>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
-                                                              const int32_t* cs, const int2* __restrict__ info, int items) {
+                                                              const int32_t* cs, const int2* __restrict__ info, int items,
+                                                              int nt_stores) {
   using L_ = PrepLds<DK, DVT>;
   constexpr int SK = L_::SK;
   constexpr int DVP = L_::DVP;
@@ -422,7 +423,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       const int cj = chalf * UTW + e;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       acc = mma_range(acc, Tpp + (16 * rb) * kSC, kSC, Vt + (16 * cj) * kSC, kSC, 0, kmax, lane);
-      *reinterpret_cast<f32x4*>(ug + ((static_cast<size_t>(rb) * DVT + cj) * 64 + lane) * 4) = acc;
+      f32x4* dst = reinterpret_cast<f32x4*>(ug + ((static_cast<size_t>(rb) * DVT + cj) * 64 + lane) * 4);
+      if (nt_stores)
+        __builtin_nontemporal_store(acc, dst);
+      else
+        *dst = acc;
     }
   }
   __syncthreads();
@@ -471,7 +476,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
         const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
         piece = pick(Ms + (16 * tt + r) * kSC, kb);
       }
-      fr[f * 64 + lane] = piece;
+      if (nt_stores)
+        __builtin_nontemporal_store(piece, fr + f * 64 + lane);
+      else
+        fr[f * 64 + lane] = piece;
     }
     if (tid == 0) *reinterpret_cast<float*>(base + rec.g) = Gam[kC - 1];
   }
@@ -975,18 +983,22 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
     constexpr int bytes = PrepLds<DK, DVT>::kBytes;
     const int items = chunk_bound * p.h_v;
     const unsigned grid = static_cast<unsigned>(items < prep_workgroups() ? items : prep_workgroups());
+    // Nontemporal record stores ahead of the column-block state pass (the
+    // 8-sequence packed workload 1.07-1.08 against 1.09-1.10 ms); ahead of
+    // the row-split pass they cost about 1 % (one 4096-token sequence).
+    const int nt = DK == 128 && split_rows(p.d_k, p.d_v, p.num_seqs * p.h_v) ? 0 : 1;
     if (p.gates.raw) {
       static bool cfg = false;
       auto kern = chunk_prep_kernel<IO, DK, DVT, true>;
       hipError_t e = set_lds(kern, bytes, &cfg);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items);
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
     } else {
       static bool cfg = false;
       auto kern = chunk_prep_kernel<IO, DK, DVT, false>;
       hipError_t e = set_lds(kern, bytes, &cfg);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items);
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
