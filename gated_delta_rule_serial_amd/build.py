@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.cpp", "prefill_scan.hip", "prefill_chunked.hip", "prefill_split.hip", "prefill_wide.hip", "decode_step.hip",
+SOURCES = ["gdn_api.cpp", "gdn_runtime.cpp", "prefill_scan.hip", "prefill_chunked.hip", "prefill_split.hip", "prefill_wide.hip", "decode_step.hip",
            "gate_prologue.hip", "causal_conv.hip", "gated_rmsnorm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -149,6 +149,71 @@ gdn_status check_slots(const SlotArgs& sl, int32_t n, const char* fn) {
   return GDN_OK;
 }
 
+// The prefill formulation a call takes, and the state columns one workgroup
+// (serial: one wave) of its sequential kernel owns.  The single place where
+// GDN_ALGO_AUTO is resolved: gdn_prefill and gdn_prefill_query_plan both ask it.
+struct Plan {
+  int form = GDN_FORM_SERIAL;
+  int cols = 1;
+};
+
+gdn::ScanParams plan_params(const gdn_problem& p, int32_t num_seqs, int32_t total_tokens) {
+  gdn::ScanParams sp{};
+  sp.gates = gate_args(&p);
+  sp.num_seqs = num_seqs;
+  sp.total_tokens = total_tokens;
+  sp.h_qk = p.h_qk;
+  sp.h_v = p.h_v;
+  sp.d_k = p.d_k;
+  sp.d_v = p.d_v;
+  sp.ratio = p.h_v / p.h_qk;
+  sp.window = p.state_window;
+  return sp;
+}
+
+gdn_status plan_prefill(const gdn_problem& p, int32_t num_seqs, int32_t total_tokens, const char* fn, Plan* plan) {
+  const gdn::ScanParams sp = plan_params(p, num_seqs, total_tokens);
+  const int window = p.state_window;
+  const int io_bf16 = p.io_dtype == GDN_BF16;
+  // float32 I/O: the chunked form exists in two passes only, through a workspace
+  const bool wide_ok = gdn::wide_supported(p.io_dtype, p.d_k, p.d_v, sp.gates, window);
+  const bool wide_ws = wide_ok && p.workspace != nullptr &&
+                       p.workspace_bytes >= gdn::wide_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) || wide_ws;
+  if (p.algorithm == GDN_ALGO_CHUNKED && !can_chunk)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "%s: the chunked algorithm needs bfloat16 I/O with d_k 64 or 128 and d_v a multiple of 8, or "
+                "float32 I/O with d_k 128 or 256, d_v a multiple of 16 up to 256 and a workspace of "
+                "gdn_prefill_workspace_size bytes; and the gated-delta or delta rule with a per-head decay "
+                "and no state history (got %s, d_k=%d, d_v=%d, rule=%d, decay_per_key=%d, state_window=%d%s)",
+                fn, io_name(p.io_dtype), p.d_k, p.d_v, p.rule, p.decay_per_key, window,
+                wide_ok && !wide_ws ? ", no or too small a workspace" : "");
+  const bool chunked = p.algorithm == GDN_ALGO_CHUNKED ||
+                       (p.algorithm == GDN_ALGO_AUTO && can_chunk && (!wide_ws || gdn::wide_auto(p.d_k)) &&
+                        static_cast<int64_t>(total_tokens) >= 64 * static_cast<int64_t>(num_seqs));
+  const bool wide = chunked && wide_ws;
+  // the two-pass chunked form when the caller's workspace holds it
+  const bool split = chunked && !wide && gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) &&
+                     p.workspace != nullptr &&
+                     p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  if (wide) {
+    plan->form = GDN_FORM_CHUNKED_F32;
+    plan->cols = 16;
+  } else if (split) {
+    plan->form = GDN_FORM_CHUNKED_TWO_PASS;
+    plan->cols = gdn::split_takes_rows_kernel(p.d_k, p.d_v, num_seqs * p.h_v)
+                     ? 16
+                     : gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v);
+  } else if (chunked) {
+    plan->form = GDN_FORM_CHUNKED_ONE_PASS;
+    plan->cols = gdn::chunked_columns_per_block(p.d_k, p.d_v);
+  } else {
+    plan->form = GDN_FORM_SERIAL;
+    plan->cols = gdn::scan_columns_per_wave(sp);
+  }
+  return GDN_OK;
+}
+
 gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
                         const int32_t* cu_seqlens_host, int32_t total_tokens, const void* q, const void* k,
                         const void* v, const float* initial_state, void* out, float* final_state,
@@ -234,36 +299,16 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   const int io_bf16 = p.io_dtype == GDN_BF16;
   sp.window = window;
   sp.history = window > 0 ? problem->state_history : nullptr;
-  // float32 I/O: the chunked form exists in two passes only, through a workspace
-  const bool wide_ok = gdn::wide_supported(p.io_dtype, p.d_k, p.d_v, sp.gates, window);
-  const bool wide_ws = wide_ok && p.workspace != nullptr &&
-                       p.workspace_bytes >= gdn::wide_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
-  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) || wide_ws;
-  if (p.algorithm == GDN_ALGO_CHUNKED && !can_chunk)
-    return fail(GDN_ERR_UNSUPPORTED,
-                "%s: the chunked algorithm needs bfloat16 I/O with d_k 64 or 128 and d_v a multiple of 8, or "
-                "float32 I/O with d_k 128 or 256, d_v a multiple of 16 up to 256 and a workspace of "
-                "gdn_prefill_workspace_size bytes; and the gated-delta or delta rule with a per-head decay "
-                "and no state history (got %s, d_k=%d, d_v=%d, rule=%d, decay_per_key=%d, state_window=%d%s)",
-                fn, io_name(p.io_dtype), p.d_k, p.d_v, p.rule, p.decay_per_key, window,
-                wide_ok && !wide_ws ? ", no or too small a workspace" : "");
-  const bool chunked = p.algorithm == GDN_ALGO_CHUNKED ||
-                       (p.algorithm == GDN_ALGO_AUTO && can_chunk && (!wide_ws || gdn::wide_auto(p.d_k)) &&
-                        static_cast<int64_t>(total_tokens) >= 64 * static_cast<int64_t>(num_seqs));
-  const bool wide = chunked && wide_ws;
-  // the two-pass chunked form when the caller's workspace holds it
-  const bool split = chunked && !wide && gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) &&
-                     p.workspace != nullptr &&
-                     p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
-  const int cols = wide      ? 16
-                   : split   ? gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v)
-                   : chunked ? gdn::chunked_columns_per_block(p.d_k, p.d_v)
-                             : gdn::scan_columns_per_wave(sp);
-  sp.col_blocks = (p.d_v + cols - 1) / cols;
+  Plan plan;
+  st = plan_prefill(p, num_seqs, total_tokens, fn, &plan);
+  if (st != GDN_OK) return st;
+  sp.col_blocks = (p.d_v + plan.cols - 1) / plan.cols;
   const uint64_t blocks = static_cast<uint64_t>(num_seqs) * p.h_v * sp.col_blocks;
   if (blocks > 0x7fffffffull)
     return fail(GDN_ERR_UNSUPPORTED, "%s: %llu workgroups exceed the grid limit", fn,
                 static_cast<unsigned long long>(blocks));
+  const bool wide = plan.form == GDN_FORM_CHUNKED_F32, split = plan.form == GDN_FORM_CHUNKED_TWO_PASS,
+             chunked = plan.form == GDN_FORM_CHUNKED_ONE_PASS;
   const hipError_t e = wide      ? gdn::launch_prefill_wide(sp, p.workspace, stream)
                        : split   ? gdn::launch_prefill_split(sp, p.workspace, stream)
                        : chunked ? gdn::launch_prefill_chunked(sp, io_bf16, stream)
@@ -376,6 +421,62 @@ GDN_EXPORT gdn_status gdn_prefill_workspace_size(const gdn_problem* problem, int
   }
   if (!gdn::split_supported(p.io_dtype == GDN_BF16, p.d_k, p.d_v, gates, p.state_window)) return ok();
   *bytes = gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  return ok();
+}
+
+GDN_EXPORT gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t num_seqs, int32_t total_tokens,
+                                             gdn_prefill_plan* plan) {
+  const char* fn = "gdn_prefill_query_plan";
+  if (!plan) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: plan is NULL", fn);
+  *plan = gdn_prefill_plan{};
+  gdn_status st = check_problem(problem, fn, false);
+  if (st != GDN_OK) return st;
+  if (num_seqs < 0 || total_tokens < 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: num_seqs=%d and total_tokens=%d must be >= 0", fn, num_seqs,
+                total_tokens);
+  const gdn_problem& p = *problem;
+  if (num_seqs == 0) {
+    plan->form = GDN_FORM_NONE;
+    return ok();
+  }
+  Plan pl;
+  st = plan_prefill(p, num_seqs, total_tokens, fn, &pl);
+  if (st != GDN_OK) return st;
+  plan->form = pl.form;
+  plan->columns_per_block = pl.cols;
+  const int units = num_seqs * p.h_v;
+  const int units8 = (units + 7) / 8 * 8;
+  char* k = plan->kernels;
+  const size_t kn = sizeof(plan->kernels);
+  switch (pl.form) {
+    case GDN_FORM_SERIAL: {
+      const gdn::ScanParams sp = plan_params(p, num_seqs, total_tokens);
+      const bool lean = gdn::scan_takes_plain_kernel(sp);
+      const int blocks = (p.d_v + pl.cols - 1) / pl.cols;
+      plan->state_workgroups = (lean ? units8 : units) * blocks;
+      std::snprintf(k, kn, "%s", lean ? "scan_plain_kernel" : "scan_kernel");
+      break;
+    }
+    case GDN_FORM_CHUNKED_ONE_PASS:
+      plan->state_workgroups = units * ((p.d_v + pl.cols - 1) / pl.cols);
+      std::snprintf(k, kn, "chunk_kernel");
+      break;
+    case GDN_FORM_CHUNKED_TWO_PASS:
+      if (gdn::split_takes_rows_kernel(p.d_k, p.d_v, units)) {
+        plan->state_workgroups = units8 * ((p.d_v + 15) / 16);
+        std::snprintf(k, kn, "chunk_table_kernel + chunk_prep_kernel + chunk_rows_kernel");
+      } else {
+        plan->state_workgroups = units8 * ((p.d_v + pl.cols - 1) / pl.cols);
+        std::snprintf(k, kn, "chunk_table_kernel + chunk_prep_kernel + chunk_state_kernel");
+      }
+      break;
+    case GDN_FORM_CHUNKED_F32:
+      plan->state_workgroups = units8 * (p.d_v / 16);
+      std::snprintf(k, kn, "chunk_table_kernel + wide_prep_kernel + wide_state_kernel");
+      break;
+    default:
+      break;
+  }
   return ok();
 }
 

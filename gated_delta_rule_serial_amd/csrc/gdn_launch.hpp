@@ -158,9 +158,18 @@ __device__ __forceinline__ int state_slot(const int32_t* slots, int32_t num_slot
 
 // Columns one scan wave owns for a given d_k (used to size the grid).
 int scan_columns_per_wave(const ScanParams& p);
+// Whether the serial scan of `p` runs scan_plain_kernel (else scan_kernel).
+bool scan_takes_plain_kernel(const ScanParams& p);
+// Whether the bf16 two-pass state pass runs the row-split chunk_rows_kernel
+// (else chunk_state_kernel with split_columns_per_block columns).
+bool split_takes_rows_kernel(int d_k, int d_v, int units);
 
-// Compute units of the current device (queried once; 256 if the query fails).
+// Compute units of the current device (queried once per device; 256 when
+// there is no device to ask).  Thread-safe.
 int device_compute_units();
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per (kernel, device).  Thread-safe.
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
 // Columns one decode workgroup owns.
 int decode_columns_per_block(int d_k, int d_v, bool per_key);
 

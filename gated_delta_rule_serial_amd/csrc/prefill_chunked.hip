@@ -470,13 +470,8 @@ template <typename IO, int DK, int NC, bool RAW>
 hipError_t launch_variant(const ScanParams& p, hipStream_t stream) {
   auto kern = chunk_kernel<IO, DK, NC, RAW>;
   constexpr int bytes = Lds<DK, NC>::kBytes;
-  static bool configured = false;  // one attribute call per instantiation and process
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), bytes);
+  if (e != hipSuccess) return e;
   const unsigned blocks = static_cast<unsigned>(p.num_seqs) * p.h_v * p.col_blocks;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), bytes, stream, p);

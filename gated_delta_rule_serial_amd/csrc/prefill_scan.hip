@@ -564,6 +564,8 @@ hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
 
 }  // namespace
 
+bool scan_takes_plain_kernel(const ScanParams& p) { return plain_scan(p); }
+
 int scan_columns_per_wave(const ScanParams& p) {
   const int d_k = p.d_k;
   if (plain_scan(p)) return d_k == 256 ? PlainShape<256>::CPW : PlainShape<128>::CPW;

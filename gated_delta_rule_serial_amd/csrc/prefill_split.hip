@@ -945,12 +945,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p
 }
 
 template <typename K>
-hipError_t set_lds(K kern, int bytes, bool* configured) {
-  if (*configured) return hipSuccess;
-  const hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) *configured = true;
-  return e;
+hipError_t set_lds(K kern, int bytes) {
+  return ensure_dynamic_lds(reinterpret_cast<const void*>(kern), bytes);
 }
 
 
@@ -988,15 +984,13 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
     // the row-split pass they cost about 1 % (one 4096-token sequence).
     const int nt = DK == 128 && split_rows(p.d_k, p.d_v, p.num_seqs * p.h_v) ? 0 : 1;
     if (p.gates.raw) {
-      static bool cfg = false;
       auto kern = chunk_prep_kernel<IO, DK, DVT, true>;
-      hipError_t e = set_lds(kern, bytes, &cfg);
+      hipError_t e = set_lds(kern, bytes);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
     } else {
-      static bool cfg = false;
       auto kern = chunk_prep_kernel<IO, DK, DVT, false>;
-      hipError_t e = set_lds(kern, bytes, &cfg);
+      hipError_t e = set_lds(kern, bytes);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
     }
@@ -1027,23 +1021,13 @@ int chunk_bound_of(int num_seqs, int total_tokens) {
 
 }  // namespace
 
-int device_compute_units() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
-
 bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window) {
   return chunked_supported(io_bf16, d_k, d_v, gates, window) && d_v <= 256;
 }
 
 int split_columns_per_block(int d_v, int units) { return split_columns(d_v, units); }
+
+bool split_takes_rows_kernel(int d_k, int d_v, int units) { return split_rows(d_k, d_v, units); }
 
 // Workspace: cs [N + 1] int32, info [chunk bound] int2, then the records.
 static size_t table_bytes(int num_seqs, int total_tokens) {

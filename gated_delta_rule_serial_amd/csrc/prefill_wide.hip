@@ -722,12 +722,8 @@ __global__ __launch_bounds__(64 * (DK / 32)) void wide_state_kernel(ScanParams p
 }
 
 template <typename K>
-hipError_t set_lds_once(K kern, int bytes, bool* configured) {
-  if (*configured) return hipSuccess;
-  const hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) *configured = true;
-  return e;
+hipError_t set_lds_once(K kern, int bytes) {
+  return ensure_dynamic_lds(reinterpret_cast<const void*>(kern), bytes);
 }
 
 template <int DK>
@@ -737,15 +733,13 @@ hipError_t launch_dk(const ScanParams& p, unsigned char* recs, size_t rec_bytes,
     constexpr int bytes = WidePrepLds::kBytes;
     const unsigned grid = static_cast<unsigned>(bound) * static_cast<unsigned>(p.h_v);
     if (p.gates.raw) {
-      static bool cfg = false;
       auto kern = wide_prep_kernel<DK, true>;
-      hipError_t e = set_lds_once(kern, bytes, &cfg);
+      hipError_t e = set_lds_once(kern, bytes);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, recs, rec_bytes, cs, info);
     } else {
-      static bool cfg = false;
       auto kern = wide_prep_kernel<DK, false>;
-      hipError_t e = set_lds_once(kern, bytes, &cfg);
+      hipError_t e = set_lds_once(kern, bytes);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, recs, rec_bytes, cs, info);
     }
@@ -759,10 +753,9 @@ hipError_t launch_dk(const ScanParams& p, unsigned char* recs, size_t rec_bytes,
   const int units8 = (units + 7) / 8 * 8;
   const unsigned blocks = static_cast<unsigned>(units8) * static_cast<unsigned>(p.d_v / 16);
   {
-    static bool cfg = false;
     constexpr int bytes = WideStateLds<DK>::kBytes;
     auto kern = wide_state_kernel<DK>;
-    const hipError_t e = set_lds_once(kern, bytes, &cfg);
+    const hipError_t e = set_lds_once(kern, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (DK / 32)), bytes, stream, p, recs, rec_bytes, cs, units8);
   }

@@ -51,6 +51,16 @@ class gdn_problem(ctypes.Structure):
     ]
 
 
+class gdn_prefill_plan(ctypes.Structure):
+    _fields_ = [
+        ("form", ctypes.c_int32), ("columns_per_block", ctypes.c_int32),
+        ("state_workgroups", ctypes.c_int32), ("kernels", ctypes.c_char * 188),
+    ]
+
+
+FORMS = {0: "none", 1: "serial", 2: "chunked_one_pass", 3: "chunked_two_pass", 4: "chunked_f32"}
+
+
 class gdn_conv_problem(ctypes.Structure):
     _fields_ = [
         ("channels", ctypes.c_int32), ("kernel_size", ctypes.c_int32),
@@ -99,6 +109,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_prefill_workspace_size.argtypes = [pp, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
     lib.gdn_prefill_workspace_size.restype = ctypes.c_int
+    lib.gdn_prefill_query_plan.argtypes = [pp, i32, i32, ctypes.POINTER(gdn_prefill_plan)]
+    lib.gdn_prefill_query_plan.restype = ctypes.c_int
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -214,6 +226,24 @@ def prefill_workspace_size(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: to
     out = ctypes.c_uint64(0)
     _check(load().gdn_prefill_workspace_size(ctypes.byref(prob), num_seqs, total_tokens, ctypes.byref(out)))
     return int(out.value)
+
+
+def prefill_query_plan(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype, num_seqs: int,
+                       total_tokens: int, *, algorithm: str = "auto", raw_gates: bool = False,
+                       workspace_bytes: int = 0, **variant) -> dict:
+    """gdn_prefill_query_plan of include/gdn.h: what gdn_prefill would launch.
+    ``workspace_bytes`` stands for a workspace of that size (no memory is
+    touched).  Returns {"form", "columns_per_block", "state_workgroups", "kernels"}."""
+    prob = make_problem(h_qk, h_v, d_k, d_v, io_dtype, algorithm=algorithm, **variant)
+    if raw_gates:
+        prob.gate_mode = GDN_GATES_RAW
+    if workspace_bytes:
+        prob.workspace = ctypes.c_void_p(256)  # a non-null, aligned stand-in: the query reads no memory
+        prob.workspace_bytes = int(workspace_bytes)
+    plan = gdn_prefill_plan()
+    _check(load().gdn_prefill_query_plan(ctypes.byref(prob), num_seqs, total_tokens, ctypes.byref(plan)))
+    return {"form": FORMS.get(plan.form, str(plan.form)), "columns_per_block": plan.columns_per_block,
+            "state_workgroups": plan.state_workgroups, "kernels": plan.kernels.decode()}
 
 
 def _host_i32(vals):

@@ -251,3 +251,27 @@ def generate_norm(shape: NormShape, *, rows: Optional[int] = None, seed: Optiona
     scale = 1.0 + 0.1 * torch.randn(shape.group, generator=gen, dtype=f32)
     dt = shape.io_dtype
     return NormInputs(shape, x.to(dt), gate.to(dt), scale.to(dt))
+
+
+# ---------------------------------------------------------------- inputs outside the workloads' domain
+def rescale_rows(x: torch.Tensor, lo: float, hi: float, *, seed: int) -> torch.Tensor:
+    """Multiply each last-axis row of x by its own factor ~ U(lo, hi) (one
+    seeded draw per row, in float32), then cast back to x's dtype: applied to
+    L2-normalised keys it gives keys with norms spread over [lo, hi]."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    f = lo + (hi - lo) * torch.rand(x.shape[:-1] + (1,), generator=gen, dtype=torch.float32)
+    return (x.float() * f).to(x.dtype)
+
+
+def positive_log_decays(g: torch.Tensor, every: int, hi: float, *, seed: int) -> torch.Tensor:
+    """A copy of the log-decays g [T, h_v] in which every `every`-th (token,
+    head) entry (flattened order) is replaced by a draw ~ U(0, hi]: gates that
+    grow the state instead of decaying it, which the gate prologue never gives
+    but precomputed gates may carry."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    flat = g.float().flatten().clone()
+    idx = torch.arange(0, flat.numel(), every)
+    flat[idx] = hi * (1.0 - torch.rand(idx.numel(), generator=gen, dtype=torch.float32))
+    return flat.reshape(g.shape).to(g.dtype)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -185,7 +185,11 @@ gdn_status gdn_prefill(const gdn_problem* problem, int32_t num_seqs,
 
 /*
  * gdn_decode_step -- one token for each of `batch` sequences, with the state
- * resident in device memory and updated in place.
+ * resident in device memory and updated in place: the recurrence above with a
+ * time axis of length one, the present state written over the past one ([P4]
+ * execute contract with T = 1, past_state -> present_state; [P1]
+ * `linear_attention_op` with a one-step sequence; [P3] `gated_delta_slots` is
+ * the same step over a state pool).
  *
  *   q, k   [batch, h_qk, d_k] io_dtype
  *   v      [batch, h_v, d_v] io_dtype
@@ -208,6 +212,40 @@ gdn_status gdn_decode_step(const gdn_problem* problem, int32_t batch,
  */
 gdn_status gdn_prefill_workspace_size(const gdn_problem* problem, int32_t num_seqs,
                                       int32_t total_tokens, uint64_t* bytes);
+
+/* The formulation gdn_prefill takes for a given problem ("plan"), as
+ * resolved from problem->algorithm, the geometry, the workspace and the
+ * device's compute-unit count.  Every form computes the recurrence above; they
+ * differ in rounding only. */
+typedef enum gdn_prefill_form {
+  GDN_FORM_NONE = 0,              /* no sequences: nothing is launched          */
+  GDN_FORM_SERIAL = 1,            /* token-by-token scan on the vector ALUs     */
+  GDN_FORM_CHUNKED_ONE_PASS = 2,  /* bf16 chunks of 64, one pass per sequence   */
+  GDN_FORM_CHUNKED_TWO_PASS = 3,  /* bf16 chunks, chunk-parallel preparation
+                                     into the workspace, then a state pass     */
+  GDN_FORM_CHUNKED_F32 = 4        /* float32 I/O chunks on split-bf16 products,
+                                     two passes through the workspace          */
+} gdn_prefill_form;
+
+typedef struct gdn_prefill_plan {
+  int32_t form;               /* gdn_prefill_form                              */
+  int32_t columns_per_block;  /* state columns one workgroup of the sequential
+                                 kernel owns (serial form: one wave)           */
+  int32_t state_workgroups;   /* workgroups of the sequential kernel's grid    */
+  char kernels[188];          /* the kernels launched, in order, joined by
+                                 " + ", NUL-terminated                         */
+} gdn_prefill_plan;
+
+/*
+ * gdn_prefill_query_plan -- host-only: fills `plan` with what gdn_prefill (or
+ * gdn_prefill_slots) would launch for this problem, num_seqs sequences and
+ * total_tokens tokens, with outputs requested.  Enqueues nothing and touches
+ * no device memory; the same function resolves GDN_ALGO_AUTO for gdn_prefill.
+ * Returns the status gdn_prefill would return for an explicit
+ * GDN_ALGO_CHUNKED request that the geometry does not serve.
+ */
+gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t num_seqs,
+                                  int32_t total_tokens, gdn_prefill_plan* plan);
 
 /*
  * Slot-indexed state pool ([P3] nuvec-core, fast/imp.rs, `gated_delta_slots`:
@@ -329,13 +367,19 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, int32_t
                              const void* x, const void* gate, const void* scale, float eps,
                              int32_t activation, void* y, hipStream_t stream);
 
-/* Message for the last non-OK status returned on the calling thread. */
+/* Message for the last non-OK status returned on the calling thread; the
+ * empty string after a call that returned GDN_OK.  The pages' execute paths
+ * report each failed check with a message before launching anything ([P4]
+ * `LinearAttentionKernel::execute`, its invalid-argument and not-implemented
+ * returns); this ABI keeps the message per thread instead of in an exception.
+ * The pointer stays valid until the next libgdn call on the same thread. */
 const char* gdn_last_error(void);
 
-/* Fixed name of a status code. */
+/* Fixed name of a status code ("GDN_OK", ...), a static string. */
 const char* gdn_status_string(gdn_status status);
 
-/* GDN_ABI_VERSION of the built library. */
+/* GDN_ABI_VERSION of the built library, to be compared with the header a
+ * caller was compiled against (the struct layouts above change with it). */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

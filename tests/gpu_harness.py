@@ -111,9 +111,38 @@ def max_err(gpu: torch.Tensor, ref: torch.Tensor) -> float:
     return float(((gpu - ref).abs() / (1.0 + ref.abs())).max())
 
 
-def check(gpu, ref, tol, what):
+def rel_errors(gpu: torch.Tensor, ref: torch.Tensor):
+    """(||d||_F / ||ref||_F, max |d|/|ref| over |ref| >= 1e-3) with d = gpu - ref.
+    The normwise figure falls back to ||d||_F when ref is all zero."""
+    d = gpu.double() - ref.double()
+    r = ref.double()
+    if r.numel() == 0:
+        return 0.0, 0.0
+    nref = float(r.norm())
+    fro = float(d.norm()) / nref if nref > 0 else float(d.norm())
+    big = r.abs() >= 1e-3
+    mrel = float((d.abs()[big] / r.abs()[big]).max()) if bool(big.any()) else 0.0
+    return fro, mrel
+
+
+# Half-precision I/O ("<= 1e-2 relative" for bfloat16) is held to a normwise
+# relative bound as well as the elementwise one: at these workloads the
+# outputs have an RMS near 5e-3, so tol (1 + |ref|) alone would admit errors
+# of the outputs' own size.  float32 I/O keeps the stated elementwise bound.
+
+
+def check(gpu, ref, tol, what, normwise=None):
+    """Assert |gpu - ref| <= tol (1 + |ref|) elementwise and, for half-precision
+    tolerances (tol >= 1e-3, i.e. bf16 and f16 I/O) or when ``normwise`` is
+    True, ||gpu - ref||_F <= tol ||ref||_F.  Prints both, and the largest
+    elementwise relative error over |ref| >= 1e-3."""
     e = max_err(gpu, ref)
-    rel = float((gpu.double() - ref.double()).norm() / max(ref.double().norm(), 1e-300)) if ref.numel() else 0.0
-    say(f"    {what}: max |d|/(1+|ref|) = {e:.3e}  (tol {tol:.0e}), ||d||/||ref|| = {rel:.3e}")
+    fro, mrel = rel_errors(gpu, ref)
+    if normwise is None:
+        normwise = tol >= 1e-3
+    say(f"    {what}: max |d|/(1+|ref|) = {e:.3e}  (tol {tol:.0e}), ||d||/||ref|| = {fro:.3e}"
+        f"{' (asserted)' if normwise else ''}, max |d|/|ref| over |ref|>=1e-3 = {mrel:.3e}")
     assert e <= tol, f"{what}: {e:.3e} > {tol:.0e}"
+    if normwise:
+        assert fro <= tol, f"{what}: normwise relative error {fro:.3e} > {tol:.0e}"
     return e

@@ -7,6 +7,7 @@ import os
 import subprocess
 
 import pytest
+import torch
 
 from gated_delta_rule_serial_amd import gdn
 
@@ -33,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 7
+    assert gdn.abi_version() == 8
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -334,3 +335,34 @@ def test_prefill_chunked_f32_without_workspace(lib):
 def test_prefill_workspace_misaligned(lib):
     st = _prefill(lib, _prob(workspace=FAKE + 0x90008, workspace_bytes=1 << 20))
     assert st == INVALID and "workspace" in gdn.last_error()
+
+
+def test_prefill_query_plan(lib):
+    """The host-only plan query: the form AUTO resolves to at each workload's
+    geometry (on a 256-compute-unit device, which is also the answer when no
+    device can be asked), and the refusal of an unserved explicit request."""
+    ws = 1 << 40
+    q = gdn.prefill_query_plan
+    bf16, f32 = torch.bfloat16, torch.float32
+    p = q(2, 2, 16, 16, f32, 1, 64)
+    assert p["form"] == "serial" and p["kernels"] == "scan_kernel"
+    p = q(16, 32, 128, 128, bf16, 1, 4096, raw_gates=True, workspace_bytes=ws)
+    assert p["form"] == "chunked_two_pass" and p["kernels"].endswith("chunk_rows_kernel")
+    assert p["state_workgroups"] == 32 * 8
+    p = q(16, 32, 128, 128, bf16, 8, 33173, workspace_bytes=ws)
+    assert p["form"] == "chunked_two_pass" and p["kernels"].endswith("chunk_state_kernel")
+    assert p["columns_per_block"] == 64
+    p = q(16, 32, 128, 128, bf16, 8, 33173)
+    assert p["form"] == "chunked_one_pass" and p["kernels"] == "chunk_kernel"
+    p = q(8, 8, 256, 256, f32, 1, 32768, workspace_bytes=ws)
+    assert p["form"] == "chunked_f32" and p["kernels"].split(" + ")[-1] == "wide_state_kernel"
+    p = q(8, 8, 256, 256, f32, 1, 32768)
+    assert p["form"] == "serial" and p["kernels"] == "scan_plain_kernel"
+    # sequences averaging under 64 tokens stay serial under AUTO
+    assert q(16, 32, 128, 128, bf16, 8, 8 * 63)["form"] == "serial"
+    assert q(16, 32, 128, 128, bf16, 8, 8 * 63, algorithm="chunked")["form"] == "chunked_one_pass"
+    assert q(16, 32, 128, 128, bf16, 8, 33173, algorithm="serial")["form"] == "serial"
+    assert q(16, 32, 128, 128, bf16, 0, 0)["form"] == "none"
+    with pytest.raises(gdn.GdnError, match="chunked algorithm needs"):
+        q(2, 2, 16, 16, f32, 1, 64, algorithm="chunked")
+    assert lib.gdn_prefill_query_plan(None, 1, 8, None) == INVALID
