@@ -3,20 +3,29 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Default workload: the decode step at B = 64 (H_qk 16, H_v 32, d_k = d_v = 128,
-bfloat16 q/k/v/gates, float32 state updated in place).  One step = one
-gdn_decode_step over the whole batch.  The state rotates over 4 buffers
-(4 x 128 MiB, more than the 256 MB Infinity Cache) so each step streams its
-state from HBM.  W untimed steps, then K steps timed back to back between HIP
-events on the stream the kernel runs on.  Prints ONE JSON line.
+Default: the decode step at B = 64 (H_qk 16, H_v 32, d_k = d_v = 128,
+bfloat16 q/k/v/gates, float32 state updated in place) is the headline: one
+step = one gdn_decode_step over the whole batch; the state rotates over 4
+buffers (4 x 128 MiB, more than the 256 MB Infinity Cache) so each step
+streams its state from HBM; W untimed steps, then K steps timed back to back
+between HIP events on the stream the kernel runs on.  The same line then
+carries, under "workloads", every prefill workload (tiny_prefill,
+prefill_t4096_fused_gates, varlen_prefill_8seq, wide_prefill_t32768_d256):
+min(K, 10) launches of gdn_prefill as the library's AUTO plan takes it (with a
+workspace, so the chunked forms run in two passes), each between its own
+events after a 1 GiB read that flushes the L2 and the Infinity Cache.  Each
+entry has its mean and median time, tokens/s, the plan the library reports,
+its own roofline and the oracle's CPU baseline.  Prints ONE JSON line.
 
-Other workloads (--workload prefill_t4096_fused_gates, varlen_prefill_8seq,
-wide_prefill_t32768_d256, tiny_prefill) time one gdn_prefill per step, each
-between its own events, with a 1 GiB read in between that flushes the L2 and
-the Infinity Cache (clean lines only, so no write-back lands in the timed
-launch).  The block's neighbouring operations are timed the same
-way: conv_step_b64 (gdn_causal_conv_step), conv_varlen_8seq (gdn_causal_conv)
-and gated_rmsnorm_t33173 (gdn_gated_rmsnorm).
+--workload NAME times one workload alone (any prefill workload, or the
+block's neighbouring operations: conv_step_b64, conv_varlen_8seq,
+gated_rmsnorm_t33173), for profiling.
+
+CPU baseline: the oracle's float32 build (the same C source with a float32
+working state, gcc -O3 -march=native, OpenMP over independent (sequence,
+head) units, built on the host that runs it) on a bounded sample of each
+workload: median of 3 runs on the host's threads, plus one run on a single
+thread; nproc and the CPU model are reported.
 
 Inputs are synthetic and seeded (gated_delta_rule_serial_amd.synth); they are
 resident in device memory before the timed region starts.
@@ -24,7 +33,6 @@ resident in device memory before the timed region starts.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,6 +50,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12  # 78.64
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 DECODE_STATE_BUFFERS = 4
+PREFILL_WORKLOADS = ["tiny_prefill", "prefill_t4096_fused_gates", "varlen_prefill_8seq", "wide_prefill_t32768_d256"]
 METRIC = "GDN prefill tokens/s + decode-step \u00b5s (B=64), % of HBM peak on 1 MI355X"
 
 
@@ -66,89 +75,153 @@ def flops_serial(shape: synth.Shape, T: int) -> int:
     return 7 * T * shape.h_v * shape.d_k * shape.d_v
 
 
-def _kernel_hash(files) -> str:
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "gated_delta_rule_serial_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def chunked_flops(shape, T, chunk=64):
+    """MFMA flops of the chunked form per launch: per token and value head,
+    K K^T and Q K^T over the lower triangle (2 C d_k), W = T' K (C d_k),
+    U = T'' V (C d_v), X = W S, Y = Q S and the state update (6 d_k d_v), M D (C d_v)."""
+    dk, dv = shape.d_k, shape.d_v
+    return T * shape.h_v * (3 * chunk * dk + 2 * chunk * dv + 6 * dk * dv)
 
 
-def _traffic(name: str, kernel_files) -> float | None:
-    """HBM bytes per launch measured with rocprofv3 counters (profiles/<name>_traffic.json),
-    or None when absent or taken on a different kernel source."""
+def _manifest():
+    try:
+        from gated_delta_rule_serial_amd import build as libbuild
+        return libbuild.load_manifest()
+    except (OSError, ValueError):
+        return None
+
+
+def _traffic(name: str):
+    """HBM bytes per launch measured with rocprofv3 counters
+    (profiles/<name>_traffic.json), or None when there is no record or when
+    the machine code of a kernel it measured differs from the built one (the
+    record lists each kernel's code digest, from the build's manifest)."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("kernel_source_sha256_16") != _kernel_hash(kernel_files):
+    code = rec.get("kernels_code")
+    man = _manifest()
+    if not code or man is None:
         return None
+    for kname, digest in code.items():
+        if man.get(kname, {}).get("code_sha256_16") != digest:
+            return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline_decode(shape, inp, budget_s=10.0):
-    """The oracle (as it stands) on a bounded sample of the decode workload:
-    whole B = 64 decode steps on the host cores until ~budget_s has passed."""
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+def _cpu_env(orc):
+    import oracle
+    cpu = oracle.host_cpu()
+    return {"cpu_model": cpu["model"], "nproc": cpu["logical_cpus"], "threads_available": orc.max_threads(),
+            "build": "oracle float32 working state, gcc -O3 -march=native, OpenMP over (sequence, head) units"}
+
+
+def _median_runs(fn, runs=3):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2], ts
+
+
+def cpu_baseline_decode(shape, inp, budget_s=1.5):
+    """The oracle's float32 build on a bounded sample of the decode workload:
+    k whole B = 64 decode steps (all heads), k sized from a probe so that one
+    run takes about budget_s; median of 3 runs, then a single-thread run."""
     import numpy as np
 
     import oracle
-    orc = oracle.default()
+    orc = oracle.float32_baseline()
     q, k, v = inp.q.double().numpy(), inp.k.double().numpy(), inp.v.double().numpy()
-    gg, bb = orc.gates(inp.a, inp.b, inp.A_log, inp.dt_bias)
-    st = inp.initial_state.double().numpy().copy()
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.decode_step(q, k, v, gg, bb, st)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s and steps >= 2:
-            break
-    assert np.isfinite(st).all()
-    return dict(value=round(shape.num_seqs * steps / el, 3), unit="tokens/s", cores=orc.max_threads(),
-                kind="oracle", sample=f"{steps} full decode steps (B={shape.num_seqs}, all heads) in {el:.1f} s")
+    gg, bb = oracle.default().gates(inp.a, inp.b, inp.A_log, inp.dt_bias)
+    st0 = inp.initial_state.double().numpy()
+    threads = orc.max_threads()
+
+    def steps_fn(nsteps):
+        def run():
+            st = st0.copy()
+            for _ in range(nsteps):
+                orc.decode_step(q, k, v, gg, bb, st)
+            assert np.isfinite(st).all()
+        return run
+
+    _median_runs(steps_fn(1), runs=1)  # first touch of the inputs
+    t1, _ = _median_runs(steps_fn(1), runs=1)
+    nsteps = max(1, int(budget_s / max(t1, 1e-6)))
+    med, ts = _median_runs(steps_fn(nsteps))
+    orc.set_threads(1)
+    try:
+        n1 = max(1, int(budget_s / max(t1 * threads, 1e-6)))
+        one, _ = _median_runs(steps_fn(n1), runs=1)
+    finally:
+        orc.set_threads(threads)
+    B = shape.num_seqs
+    res = {"value": round(B * nsteps / med, 3), "unit": "tokens/s", "cores": min(threads, B * shape.h_v),
+           "kind": "oracle",
+           "sample": f"{nsteps} whole decode steps (B={B}, all {shape.h_v} heads) per run, median of 3 runs "
+                     f"({', '.join(f'{t:.2f}' for t in ts)} s)",
+           "one_thread_value": round(B * n1 / one, 3),
+           "one_thread_sample": f"{n1} decode steps in {one:.2f} s on 1 thread"}
+    res.update(_cpu_env(orc))
+    return res
 
 
-def cpu_baseline_prefill(shape, inp, budget_s=10.0):
-    """The oracle on a bounded sample of a prefill workload: the first m tokens of
-    every sequence for the first k q/k head groups (all their value heads), with
-    (k, m) sized from a short probe so that the run takes about budget_s.  The
-    rate is scaled to all heads: tokens x (sampled value heads / h_v) / seconds."""
+def cpu_baseline_prefill(shape, inp, budget_s=1.5):
+    """The oracle's float32 build on a bounded sample of a prefill workload:
+    the first m tokens of every sequence, all heads, m sized from a probe so
+    that one run takes about budget_s (the whole workload when it fits);
+    median of 3 runs, then a single-thread run on its own sample."""
     import oracle
-    orc = oracle.default()
-    ratio = shape.h_v // shape.h_qk
+    orc = oracle.float32_baseline()
+    threads = orc.max_threads()
+    max_len = max(inp.seqlens)
 
-    def run(groups, ntok):
-        lens = [min(l, ntok) for l in inp.seqlens]
+    def sample(m):
+        lens = [min(l, m) for l in inp.seqlens]
         idx = torch.cat([torch.arange(int(inp.cu_seqlens[i]), int(inp.cu_seqlens[i]) + lens[i])
                          for i in range(len(lens))])
         cu = [0]
         for l in lens:
             cu.append(cu[-1] + l)
-        hv = slice(0, groups * ratio)
-        gg, bb = orc.gates(inp.a[idx][:, hv], inp.b[idx][:, hv], inp.A_log[hv], inp.dt_bias[hv])
-        s0 = None if inp.initial_state is None else inp.initial_state[:, hv].double().numpy()
-        args = (inp.q[idx][:, :groups].double().numpy(), inp.k[idx][:, :groups].double().numpy(),
-                inp.v[idx][:, hv].double().numpy(), gg, bb, cu, s0)
-        t0 = time.perf_counter()
-        orc.prefill(*args)
-        return time.perf_counter() - t0, cu[-1]
+        gg, bb = oracle.default().gates(inp.a[idx], inp.b[idx], inp.A_log, inp.dt_bias)
+        s0 = None if inp.initial_state is None else inp.initial_state.double().numpy()
+        args = (inp.q[idx].double().numpy(), inp.k[idx].double().numpy(), inp.v[idx].double().numpy(), gg, bb,
+                cu, s0)
+        return (lambda: orc.prefill(*args)), cu[-1]
 
-    max_len = max(inp.seqlens)
-    el, tok = run(1, min(128, max_len))
-    per_unit = el / max(tok, 1)                     # seconds per token per head group (one thread's share)
-    budget_units = budget_s / max(per_unit, 1e-9)   # token x group units that fit the budget
-    groups = max(1, min(shape.h_qk, int(budget_units // max(inp.total_tokens, 1))))
-    ntok = max_len if groups > 1 else max(128, min(max_len, int(budget_units / max(len(inp.seqlens), 1))))
-    el, tok = run(groups, ntok)
-    heads = groups * ratio
-    return dict(value=round(tok * heads / shape.h_v / el, 3), unit="tokens/s", cores=orc.max_threads(),
-                kind="oracle",
-                sample=f"value heads 0-{heads - 1} of {shape.h_v} ({groups} q/k head groups), first {min(ntok, max_len)} "
-                       f"tokens of each sequence ({tok} tokens) in {el:.1f} s; rate scaled to all heads")
+    m0 = min(64, max_len)
+    fn, tok0 = sample(m0)
+    _median_runs(fn, runs=1)  # first touch of the inputs
+    t0, _ = _median_runs(fn, runs=1)
+    per_tok = t0 / max(tok0, 1)
+    m = max(m0, min(max_len, int(m0 * budget_s / max(t0, 1e-6))))
+    fn, tok = sample(m)
+    med, ts = _median_runs(fn)
+    units = len(inp.seqlens) * shape.h_v
+    used = min(threads, units)
+    orc.set_threads(1)
+    try:
+        m1 = max(1, min(max_len, int(budget_s / max(per_tok * used, 1e-9) / max(len(inp.seqlens), 1))))
+        fn1, tok1 = sample(m1)
+        one, _ = _median_runs(fn1, runs=1)
+    finally:
+        orc.set_threads(threads)
+    whole = m >= max_len
+    res = {"value": round(tok / med, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": (("the whole workload" if whole else f"the first {m} tokens of each sequence") +
+                      f" ({tok} tokens, all {shape.h_v} value heads) per run, median of 3 runs "
+                      f"({', '.join(f'{t:.2f}' for t in ts)} s)"),
+           "one_thread_value": round(tok1 / one, 3),
+           "one_thread_sample": f"{tok1} tokens (all heads) in {one:.2f} s on 1 thread"}
+    res.update(_cpu_env(orc))
+    return res
 
 
+# ---------------------------------------------------------------- GPU
 def bench_decode(shape, steps, warmup, want_cpu):
     dev = "cuda"
     inp = synth.generate(shape)
@@ -173,8 +246,6 @@ def bench_decode(shape, steps, warmup, want_cpu):
     assert torch.isfinite(out.float()).all()
     nbytes = algorithmic_bytes(shape, inp)
     achieved = nbytes / (ms * 1e-3) / 1e9
-    kernel_files = ["decode_step.hip", "gdn_device.hpp"]
-    traffic = _traffic(shape.name, kernel_files)
     line = {
         "metric": METRIC,
         "value": round(shape.num_seqs / (ms * 1e-3), 1),
@@ -183,7 +254,7 @@ def bench_decode(shape, steps, warmup, want_cpu):
         "ms_per_step": round(ms, 6),
         "wall_s": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(shape.name),
                      "kernel": "decode_kernel<bf16, d_k 128, 128 columns per workgroup, precomputed gates>",
                      "algorithmic_bytes_per_launch": nbytes},
         "config": {"workload": shape.name, "batch": shape.num_seqs, "h_qk": shape.h_qk, "h_v": shape.h_v,
@@ -203,15 +274,32 @@ def _flush(buf):
     buf.sum()
 
 
-def chunked_flops(shape, T, chunk=64):
-    """MFMA flops of the chunked form per launch: per token and value head,
-    K K^T and Q K^T over the lower triangle (2 C d_k), W = T' K (C d_k),
-    U = T'' V (C d_v), X = W S, Y = Q S and the state update (6 d_k d_v), M D (C d_v)."""
-    dk, dv = shape.d_k, shape.d_v
-    return T * shape.h_v * (3 * chunk * dk + 2 * chunk * dv + 6 * dk * dv)
+def prefill_roofline(shape, T, ms, nbytes, plan, ws_bytes):
+    """The roofline of the form the library took: HBM for the chunked forms
+    (their ~180 flop/B at d = 128 sit below the bf16 MFMA ridge of
+    2.5 PFLOP/s / 8 TB/s ~ 312 flop/B), with the MFMA rate beside it; the
+    vector ALUs for the serial scan (7 d_k d_v flops per token and head), with
+    the HBM fraction beside it."""
+    hbm_gbs = nbytes / (ms * 1e-3) / 1e9
+    form = plan["form"]
+    traffic = _traffic(f"{shape.name}_{form}")
+    if form.startswith("chunked"):
+        # float32 I/O: three bf16 MFMA products (hi.hi + hi.lo + lo.hi) per product
+        fl = chunked_flops(shape, T) * (3 if form == "chunked_f32" else 1)
+        tf = fl / (ms * 1e-3) / 1e12
+        return {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": plan["kernels"],
+                "algorithmic_bytes_per_launch": nbytes, "workspace_bytes": ws_bytes,
+                "mfma_tflops": round(tf, 2), "mfma_frac_of_bf16_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+    fl = flops_serial(shape, T)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": round(tf, 2), "peak": round(FP32_VALU_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+            "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": plan["kernels"],
+            "flops_per_launch": fl, "algorithmic_bytes_per_launch": nbytes,
+            "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
 
 
-def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=True):
+def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=True, flush=None):
     dev = "cuda"
     inp = synth.generate(shape)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -220,7 +308,6 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=Tru
     raw = shape.gate_mode == "raw"
     if raw:
         gates = dict(a=inp.a.to(dev), b=inp.b.to(dev), A_log=inp.A_log.to(dev), dt_bias=inp.dt_bias.to(dev))
-        g = beta = None
     else:
         g, beta = gdn.gate_prologue(inp.a.to(dev), inp.b.to(dev), inp.A_log.to(dev), inp.dt_bias.to(dev))
         gates = dict(g=g, beta=beta)
@@ -229,99 +316,41 @@ def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=Tru
     n = len(inp.seqlens)
     out = torch.empty(T, shape.h_v, shape.d_v, dtype=shape.io_dtype, device=dev)
     fin = torch.empty(n, shape.h_v, shape.d_k, shape.d_v, dtype=torch.float32, device=dev)
-    flush = torch.zeros(256 * 1024 * 1024, dtype=torch.float32, device=dev)  # 1 GiB
-    stream = torch.cuda.current_stream()
+    if flush is None:
+        flush = torch.zeros(256 * 1024 * 1024, dtype=torch.float32, device=dev)  # 1 GiB
     # the chunked form's workspace (two passes), allocated before the timed region
     ws_bytes = gdn.prefill_workspace_size(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, n, T,
                                           algorithm=algorithm) if two_pass else 0
     if ws_bytes:
         gates["workspace"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    plan = gdn.prefill_query_plan(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, n, T,
+                                  algorithm=algorithm, raw_gates=raw, workspace_bytes=ws_bytes)
 
     def one():
         gdn.gdn_prefill(q, k, v, cu, out=out, final_state=fin, initial_state=s0, cu_seqlens_host=cu_host,
                         algorithm=algorithm, **gates)
 
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    times = []
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        _flush(flush)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        one()
-        e1.record(stream)
-        times.append((e0, e1))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_list = sorted(a.elapsed_time(b) for a, b in times)
-    ms = sum(ms_list) / len(ms_list)
+    ms, med, wall = _timed(one, steps, warmup, flush)
     assert torch.isfinite(out.float()).all()
     nbytes = algorithmic_bytes(shape, inp)
-    hbm_gbs = nbytes / (ms * 1e-3) / 1e9
-    # the float32 chunked form (two passes, products on split bf16 operands) runs
-    # whenever the workspace is given for float32 I/O
-    wide = shape.io_dtype == torch.float32 and ws_bytes > 0
-    chunked = wide or algorithm == "chunked" or (
-        algorithm == "auto" and shape.io_dtype == torch.bfloat16 and shape.d_k in (64, 128)
-        and shape.d_v % 8 == 0 and T >= 64 * n)
-    if wide:
-        # three bf16 MFMA products (hi.hi + hi.lo + lo.hi) per float32-class product
-        fl = 3 * chunked_flops(shape, T)
-        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-                "traffic": _traffic(shape.name + "_chunked_f32",
-                                    ["prefill_wide.hip", "prefill_split.hip", "chunk_mfma.hpp", "gdn_device.hpp"]),
-                "kernel": "wide_prep_kernel + wide_state_kernel (float32 I/O, chunked in two passes, split-bf16 MFMA)",
-                "algorithmic_bytes_per_launch": nbytes, "workspace_bytes": ws_bytes,
-                "mfma_tflops": round(fl / (ms * 1e-3) / 1e12, 2), "mfma_frac_of_bf16_peak":
-                    round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
-    elif chunked:
-        # the chunked form's intensity (~180 flop/B at d = 128) is below the bf16 MFMA
-        # ridge (2.5 PFLOP/s / 8 TB/s ~ 312 flop/B): HBM bounds it
-        fl = chunked_flops(shape, T)
-        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-                "traffic": (_traffic(shape.name + "_two_pass", ["prefill_split.hip", "chunk_mfma.hpp", "gdn_device.hpp"])
-                            if ws_bytes else
-                            _traffic(shape.name + "_chunked", ["prefill_chunked.hip", "chunk_mfma.hpp", "gdn_device.hpp"])),
-                "kernel": ("chunk_prep_kernel + chunk_state_kernel (chunked in two passes, bf16 MFMA)" if ws_bytes
-                           else "chunk_kernel (chunked, bf16 MFMA)"),
-                "algorithmic_bytes_per_launch": nbytes, "workspace_bytes": ws_bytes,
-                "mfma_tflops": round(fl / (ms * 1e-3) / 1e12, 2), "mfma_frac_of_bf16_peak":
-                    round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
-    else:
-        # the serial form does 7 d_k d_v flops per token and head on the vector ALUs
-        fl = flops_serial(shape, T)
-        tf = fl / (ms * 1e-3) / 1e12
-        roof = {"bound": "alu", "achieved": round(tf, 2), "peak": round(FP32_VALU_PEAK_TFLOPS, 2),
-                "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
-                "traffic": _traffic(shape.name + "_serial", ["prefill_scan.hip", "gdn_device.hpp"]),
-                "kernel": ("scan_plain_kernel (serial scan, d_k 256, two columns per wave)" if shape.d_k == 256
-                           else "scan_plain_kernel or scan_kernel (serial scan)"), "flops_per_launch": fl,
-                "algorithmic_bytes_per_launch": nbytes}
-    line = {
-        "metric": METRIC,
-        "value": round(T / (ms * 1e-3), 1),
-        "unit": "tokens/s",
-        "ms_per_step": round(ms, 6),
-        "ms_median": round(ms_list[len(ms_list) // 2], 6),
+    entry = {
+        "ms": round(ms, 6),
+        "ms_median": round(med, 6),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "steps": steps,
+        "warmup": warmup,
         "wall_s": round(wall, 3),
-        "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-        "roofline": roof,
-        "config": {"workload": shape.name,
-                   "algorithm": (("chunked, two passes, split-bf16 products" if wide else "chunked, two passes")
-                                 if ws_bytes else "chunked") if chunked else "serial",
-                   "num_seqs": n,
-                   "total_tokens": T, "seqlens": inp.seqlens, "h_qk": shape.h_qk, "h_v": shape.h_v,
-                   "d_k": shape.d_k, "d_v": shape.d_v,
+        "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "plan": plan,
+        "roofline": prefill_roofline(shape, T, ms, nbytes, plan, ws_bytes),
+        "config": {"workload": shape.name, "num_seqs": n, "total_tokens": T, "seqlens": inp.seqlens,
+                   "h_qk": shape.h_qk, "h_v": shape.h_v, "d_k": shape.d_k, "d_v": shape.d_v,
                    "io_dtype": "bf16" if shape.io_dtype == torch.bfloat16 else "f32", "state_dtype": "f32",
-                   "gates": shape.gate_mode},
+                   "gates": shape.gate_mode, "initial_state": inp.initial_state is not None},
     }
     if want_cpu:
-        line["cpu_baseline"] = cpu_baseline_prefill(shape, inp)
-    return line
+        entry["cpu_baseline"] = cpu_baseline_prefill(shape, inp)
+    return entry
 
 
 def _timed(one, steps, warmup, flush=None):
@@ -381,7 +410,7 @@ def bench_conv(shape, steps, warmup, want_cpu):
             "ms_median": round(med, 6), "wall_s": round(wall, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": _traffic(shape.name, ["causal_conv.hip", "gdn_device.hpp"]),
+                         "traffic": _traffic(shape.name),
                          "kernel": "conv_step_kernel" if step else "conv_window_kernel + conv_state_kernel",
                          "algorithmic_bytes_per_launch": nbytes},
             "config": {"workload": shape.name, "num_seqs": n, "total_tokens": T, "channels": C, "kernel_size": K,
@@ -417,7 +446,7 @@ def bench_norm(shape, steps, warmup, want_cpu):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": _traffic(shape.name, ["gated_rmsnorm.hip", "gdn_device.hpp"]),
+                         "traffic": _traffic(shape.name),
                          "kernel": "rmsnorm_kernel", "algorithmic_bytes_per_launch": nbytes},
             "config": {"workload": shape.name, "rows": shape.rows, "width": shape.width, "group": shape.group,
                        "io_dtype": "bf16", "activation": "silu", "eps": 1e-5}}
@@ -458,8 +487,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_b64",
-                    choices=sorted(synth.BY_NAME) + sorted(synth.CONV_BY_NAME) + sorted(synth.NORM_BY_NAME))
+    ap.add_argument("--workload", default="all",
+                    choices=["all"] + sorted(synth.BY_NAME) + sorted(synth.CONV_BY_NAME) + sorted(synth.NORM_BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algorithm", default="auto", choices=["auto", "serial", "chunked"],
                     help="prefill formulation (prefill workloads only)")
@@ -487,15 +516,28 @@ def main():
             line = bench_conv(synth.CONV_BY_NAME[args.workload], steps, warmup, want_cpu)
         else:
             line = bench_norm(synth.NORM_BY_NAME[args.workload], steps, warmup, want_cpu)
+    elif args.workload in ("all", "decode_b64"):
+        steps = args.steps if args.steps is not None else 1000
+        warmup = args.warmup if args.warmup is not None else 50
+        line = bench_decode(synth.BY_NAME["decode_b64"], steps, warmup, want_cpu)
+        print(f"decode_b64: {line['decode_step_us']} us/step", file=sys.stderr, flush=True)
+        if args.workload == "all":
+            psteps, pwarm = max(3, min(steps, 10)), max(1, min(warmup, 3))
+            flush = torch.zeros(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+            line["workloads"] = {}
+            for name in PREFILL_WORKLOADS:
+                e = bench_prefill(synth.BY_NAME[name], psteps, pwarm, want_cpu, args.algorithm, not args.one_pass,
+                                  flush=flush)
+                line["workloads"][name] = e
+                print(f"{name}: {e['ms']} ms ({e['plan']['form']}), HBM {100 * e['hbm_frac']:.1f} %",
+                      file=sys.stderr, flush=True)
     else:
         shape = synth.BY_NAME[args.workload]
-        decode = shape.kind == "decode"
-        steps = args.steps if args.steps is not None else (1000 if decode else 10)
-        warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
-        if decode:
-            line = bench_decode(shape, steps, warmup, want_cpu)
-        else:
-            line = bench_prefill(shape, steps, warmup, want_cpu, args.algorithm, not args.one_pass)
+        steps = args.steps if args.steps is not None else 10
+        warmup = args.warmup if args.warmup is not None else 3
+        e = bench_prefill(shape, steps, warmup, want_cpu, args.algorithm, not args.one_pass)
+        line = {"metric": METRIC, "value": e.pop("tokens_per_s"), "unit": "tokens/s", "ms_per_step": e.pop("ms")}
+        line.update(e)
     head = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"), "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}

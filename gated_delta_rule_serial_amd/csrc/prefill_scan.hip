@@ -61,8 +61,11 @@ __global__ __launch_bounds__(kWave) void scan_kernel(ScanParams p) {
   // Tokens per loop iteration.  Ring registers that cross the loop's back
   // edge with loads in flight make the compiler wait for those loads at the
   // loop head; d_k = 256 (few waves per SIMD to hide that) unrolls a whole
-  // 64-token gate block, so the wait comes once per 64 tokens.
-  constexpr int kGroup = (DK >= 256 && !GENERAL) ? kWave : kPrefetch;
+  // 64-token gate block, so the wait comes once per 64 tokens.  With masked
+  // rows (d_k below 256) and half-precision words that unroll left the ring
+  // partly in scratch (112 bytes of private segment), so those variants
+  // keep the ring-sized group.
+  constexpr int kGroup = (DK >= 256 && !GENERAL && (FULL || sizeof(IO) == 4)) ? kWave : kPrefetch;
 
   const int lane = static_cast<int>(threadIdx.x);
   const int c = lane / R;        // column within the wave

@@ -36,10 +36,56 @@ def compile_source(src: str, out: str) -> str:
 
 
 def build(force: bool = True) -> str:
-    """Compile ``gdn_oracle.c`` into ``oracle/libgdn_oracle.so``."""
+    """Compile ``gdn_oracle.c`` into ``oracle/libgdn_oracle.so`` (and the
+    float32 baseline build for this host, see ``build_f32``)."""
     if not force and os.path.exists(LIB_PATH) and os.path.getmtime(LIB_PATH) >= os.path.getmtime(SRC):
         return LIB_PATH
-    return compile_source(SRC, LIB_PATH)
+    out = compile_source(SRC, LIB_PATH)
+    build_f32(force=force)
+    return out
+
+
+# The timed CPU baseline: the same source with a float32 working state,
+# optimised for the host it runs on.  -march=native makes the library specific
+# to the CPU that built it, so its file name carries a digest of that CPU's
+# model and feature flags and it is rebuilt on any other host.
+CFLAGS_F32 = ["-O3", "-march=native", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-DGDNREF_ACC=float",
+              "-Wall", "-Wextra"]
+
+
+def host_cpu() -> dict:
+    """Model name and logical CPU count of this host (from /proc/cpuinfo)."""
+    model, flags, n = "unknown", "", 0
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("processor"):
+                    n += 1
+                elif line.startswith("model name") and model == "unknown":
+                    model = line.split(":", 1)[1].strip()
+                elif line.startswith("flags") and not flags:
+                    flags = line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return {"model": model, "flags": flags, "logical_cpus": n or os.cpu_count() or 1}
+
+
+def f32_lib_path() -> str:
+    import hashlib
+    cpu = host_cpu()
+    tag = hashlib.sha256((cpu["model"] + "|" + cpu["flags"]).encode()).hexdigest()[:10]
+    return os.path.join(HERE, f"libgdn_oracle_f32_{tag}.so")
+
+
+def build_f32(force: bool = False) -> str:
+    """Compile the float32 baseline build of ``gdn_oracle.c`` for this host."""
+    path = f32_lib_path()
+    if not force and os.path.exists(path) and os.path.getmtime(path) >= os.path.getmtime(SRC):
+        return path
+    tmp = path + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *CFLAGS_F32, "-I", HERE, "-o", tmp, SRC, "-lm"], check=True)
+    os.replace(tmp, path)
+    return path
 
 
 def _f64(x):
@@ -85,6 +131,10 @@ class Oracle:
         lib.gdnref_gated_rmsnorm.restype = ctypes.c_int
         lib.gdnref_max_threads.argtypes = []
         lib.gdnref_max_threads.restype = ctypes.c_int
+        lib.gdnref_set_threads.argtypes = [i32]
+        lib.gdnref_set_threads.restype = None
+        lib.gdnref_acc_bytes.argtypes = []
+        lib.gdnref_acc_bytes.restype = i32
         self.lib = lib
         self.path = lib_path
 
@@ -96,6 +146,13 @@ class Oracle:
 
     def max_threads(self) -> int:
         return int(self.lib.gdnref_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        self.lib.gdnref_set_threads(int(n))
+
+    def acc_bytes(self) -> int:
+        """8 for the reference (double) build, 4 for the float32 baseline build."""
+        return int(self.lib.gdnref_acc_bytes())
 
     def gates(self, a, b, A_log, dt_bias):
         """(g, beta) = (-exp(A_log) softplus(a + dt_bias), sigmoid(b)), shaped like ``a``."""
@@ -186,6 +243,7 @@ class Oracle:
 
 
 _default = None
+_f32 = None
 
 
 def default() -> Oracle:
@@ -196,3 +254,11 @@ def default() -> Oracle:
             build()
         _default = Oracle(LIB_PATH)
     return _default
+
+
+def float32_baseline() -> Oracle:
+    """The float32 baseline build for this host (compiled on first use)."""
+    global _f32
+    if _f32 is None:
+        _f32 = Oracle(build_f32())
+    return _f32

@@ -16,6 +16,17 @@
 #include <omp.h>
 #endif
 
+/* Working precision of the recurrence's state and accumulations.  The
+ * reference build keeps double; a second build of this same source with
+ * -DGDNREF_ACC=float is the timed CPU baseline (float32 working state, as the
+ * pages' kernels keep), and is itself held to the double build by the tests.
+ * Inputs and outputs stay double arrays either way: each input value is the
+ * widened I/O value, exact in float as well. */
+#ifndef GDNREF_ACC
+#define GDNREF_ACC double
+#endif
+typedef GDNREF_ACC acc_t;
+
 /* [P4] `la_sigmoid`: two branches so that exp only sees arguments <= 0. */
 double gdnref_sigmoid(double x) {
   if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
@@ -64,7 +75,7 @@ static void scan_unit(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
                       int32_t h, const double* q, const double* k,
                       const double* v, const double* g, const double* beta,
                       int32_t decay_per_key, int32_t beta_shared, int32_t window,
-                      double* history, double* S, double* r, double* d, double* out) {
+                      double* history, acc_t* S, acc_t* r, acc_t* d, double* out) {
   const int32_t hq = h / (h_v / h_qk); /* consecutive value heads share q/k */
   const int64_t state_elems = (int64_t)d_k * d_v;
   /* history slots before the first token stay zero ([P1] state_window) */
@@ -80,11 +91,11 @@ static void scan_unit(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
       if (decay_per_key) {
         const double* gt = g + (t * h_v + h) * d_k;
         for (int32_t i = 0; i < d_k; ++i) {
-          const double alpha_i = exp(gt[i]);
+          const acc_t alpha_i = (acc_t)exp(gt[i]);
           for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] *= alpha_i;
         }
       } else {
-        const double alpha = exp(g[t * h_v + h]);
+        const acc_t alpha = (acc_t)exp(g[t * h_v + h]);
         for (int32_t i = 0; i < d_k; ++i)
           for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] *= alpha;
       }
@@ -92,35 +103,37 @@ static void scan_unit(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
 
     /* retrieval r = S^T k and delta d = beta (v - r); plain rules use d = v */
     if (rule_deltas(rule)) {
-      const double bt = beta_shared ? beta[t] : beta[t * h_v + h];
+      const acc_t bt = (acc_t)(beta_shared ? beta[t] : beta[t * h_v + h]);
       for (int32_t j = 0; j < d_v; ++j) {
-        double acc = 0.0;
-        for (int32_t i = 0; i < d_k; ++i) acc += S[i * d_v + j] * kt[i];
+        acc_t acc = 0;
+        for (int32_t i = 0; i < d_k; ++i) acc += S[i * d_v + j] * (acc_t)kt[i];
         r[j] = acc;
       }
-      for (int32_t j = 0; j < d_v; ++j) d[j] = bt * (vt[j] - r[j]);
+      for (int32_t j = 0; j < d_v; ++j) d[j] = bt * ((acc_t)vt[j] - r[j]);
     } else {
-      for (int32_t j = 0; j < d_v; ++j) d[j] = vt[j];
+      for (int32_t j = 0; j < d_v; ++j) d[j] = (acc_t)vt[j];
     }
 
     /* rank-1 update S <- S + k d^T */
     for (int32_t i = 0; i < d_k; ++i)
-      for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] += kt[i] * d[j];
+      for (int32_t j = 0; j < d_v; ++j) S[i * d_v + j] += (acc_t)kt[i] * d[j];
 
     /* readout of the updated state: out = scale * S^T q */
     if (out) {
       double* ot = out + (t * h_v + h) * d_v;
       for (int32_t j = 0; j < d_v; ++j) {
-        double acc = 0.0;
-        for (int32_t i = 0; i < d_k; ++i) acc += S[i * d_v + j] * qt[i];
-        ot[j] = scale * acc;
+        acc_t acc = 0;
+        for (int32_t i = 0; i < d_k; ++i) acc += S[i * d_v + j] * (acc_t)qt[i];
+        ot[j] = (double)((acc_t)scale * acc);
       }
     }
 
     /* state after this token, for the last `window` tokens */
     const int64_t w = (t - t0) - ((t1 - t0) - window);
-    if (window > 0 && w >= 0)
-      memcpy(history + (w * h_v + h) * state_elems, S, sizeof(double) * (size_t)state_elems);
+    if (window > 0 && w >= 0) {
+      double* hw = history + (w * h_v + h) * state_elems;
+      for (int64_t e = 0; e < state_elems; ++e) hw[e] = (double)S[e];
+    }
   }
 }
 
@@ -158,23 +171,21 @@ int gdnref_prefill_ex(int32_t rule, int32_t h_qk, int32_t h_v, int32_t d_k,
   for (int64_t u = 0; u < units; ++u) {
     const int32_t n = (int32_t)(u / h_v);
     const int32_t h = (int32_t)(u % h_v);
-    double* S = (double*)malloc(sizeof(double) * (size_t)(state_elems + 2 * d_v));
+    acc_t* S = (acc_t*)malloc(sizeof(acc_t) * (size_t)(state_elems + 2 * d_v));
     if (!S) {
 #pragma omp atomic write
       failed = 1;
       continue;
     }
-    double* r = S + state_elems;
-    double* d = r + d_v;
-    if (initial_state)
-      memcpy(S, initial_state + u * state_elems, sizeof(double) * (size_t)state_elems);
-    else
-      memset(S, 0, sizeof(double) * (size_t)state_elems);
+    acc_t* r = S + state_elems;
+    acc_t* d = r + d_v;
+    for (int64_t e = 0; e < state_elems; ++e)
+      S[e] = initial_state ? (acc_t)initial_state[u * state_elems + e] : (acc_t)0;
     scan_unit(rule, h_qk, h_v, d_k, d_v, scale, cu_seqlens[n], cu_seqlens[n + 1], h,
               q, k, v, g, beta, decay_per_key, beta_shared, window,
               window > 0 ? history + (int64_t)n * window * h_v * state_elems : NULL, S, r, d, out);
     if (final_state)
-      memcpy(final_state + u * state_elems, S, sizeof(double) * (size_t)state_elems);
+      for (int64_t e = 0; e < state_elems; ++e) final_state[u * state_elems + e] = (double)S[e];
     free(S);
   }
   return failed ? -1 : 0;
@@ -267,6 +278,19 @@ int gdnref_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, const doubl
   }
   return 0;
 }
+
+/* Threads the OpenMP loop over (sequence, head) units uses from now on. */
+void gdnref_set_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* sizeof the working precision: 8 for the reference build, 4 for the
+ * float32 baseline build. */
+int32_t gdnref_acc_bytes(void) { return (int32_t)sizeof(acc_t); }
 
 int gdnref_max_threads(void) {
 #ifdef _OPENMP

@@ -148,6 +148,14 @@ int gdnref_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, const doubl
 /* Threads the parallel loop over independent (sequence, head) units uses. */
 int gdnref_max_threads(void);
 
+/* Sets that thread count (n > 0) for later calls. */
+void gdnref_set_threads(int32_t n);
+
+/* Bytes of the working precision of the state and its accumulations: 8 in
+ * the reference build (double), 4 in the float32 baseline build of the same
+ * source (-DGDNREF_ACC=float). */
+int32_t gdnref_acc_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

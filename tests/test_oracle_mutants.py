@@ -11,24 +11,25 @@ import oracle_pins
 # (label, text in gdn_oracle.c, replacement)
 MUTANTS = [
     ("dropped decay", "S[i * d_v + j] *= alpha;", ";"),
-    ("decay applied as g, not exp(g)", "const double alpha = exp(g[t * h_v + h]);",
-     "const double alpha = g[t * h_v + h];"),
-    ("delta sign flipped", "d[j] = bt * (vt[j] - r[j]);", "d[j] = bt * (r[j] - vt[j]);"),
-    ("beta ignored", "d[j] = bt * (vt[j] - r[j]);", "d[j] = (vt[j] - r[j]);"),
-    ("retrieval against the query", "acc += S[i * d_v + j] * kt[i];\n        r[j] = acc;",
-     "acc += S[i * d_v + j] * qt[i];\n        r[j] = acc;"),
-    ("update with the query", "S[i * d_v + j] += kt[i] * d[j];", "S[i * d_v + j] += qt[i] * d[j];"),
-    ("scale dropped", "ot[j] = scale * acc;", "ot[j] = acc;"),
+    ("decay applied as g, not exp(g)", "const acc_t alpha = (acc_t)exp(g[t * h_v + h]);",
+     "const acc_t alpha = (acc_t)g[t * h_v + h];"),
+    ("delta sign flipped", "d[j] = bt * ((acc_t)vt[j] - r[j]);", "d[j] = bt * (r[j] - (acc_t)vt[j]);"),
+    ("beta ignored", "d[j] = bt * ((acc_t)vt[j] - r[j]);", "d[j] = ((acc_t)vt[j] - r[j]);"),
+    ("retrieval against the query", "acc += S[i * d_v + j] * (acc_t)kt[i];\n        r[j] = acc;",
+     "acc += S[i * d_v + j] * (acc_t)qt[i];\n        r[j] = acc;"),
+    ("update with the query", "S[i * d_v + j] += (acc_t)kt[i] * d[j];", "S[i * d_v + j] += (acc_t)qt[i] * d[j];"),
+    ("scale dropped", "ot[j] = (double)((acc_t)scale * acc);", "ot[j] = (double)acc;"),
     ("interleaved head map", "const int32_t hq = h / (h_v / h_qk);", "const int32_t hq = h % h_qk;"),
     ("initial state ignored",
-     "memcpy(S, initial_state + u * state_elems, sizeof(double) * (size_t)state_elems);",
-     "memset(S, 0, sizeof(double) * (size_t)state_elems);"),
+     "S[e] = initial_state ? (acc_t)initial_state[u * state_elems + e] : (acc_t)0;",
+     "S[e] = (acc_t)0;"),
     ("default scale from d_v", "scale = 1.0 / sqrt((double)d_k);", "scale = 1.0 / sqrt((double)d_v);"),
     ("softplus tail sign", "log1p(exp(-fabs(x)))", "log1p(exp(fabs(x)))"),
     ("sigmoid negative branch", "return e / (1.0 + e);", "return 1.0 / (1.0 + e);"),
     ("decay sign", "g[idx] = -exp(A_log[h])", "g[idx] = exp(A_log[h])"),
     ("dt_bias dropped", "gdnref_softplus(a[idx] + dt_bias[h])", "gdnref_softplus(a[idx])"),
-    ("per-key decay row ignored", "const double alpha_i = exp(gt[i]);", "const double alpha_i = exp(gt[0]);"),
+    ("per-key decay row ignored", "const acc_t alpha_i = (acc_t)exp(gt[i]);",
+     "const acc_t alpha_i = (acc_t)exp(gt[0]);"),
     ("shared beta not per token", "beta_shared ? beta[t] :", "beta_shared ? beta[0] :"),
     ("history slot off by one", "const int64_t w = (t - t0) - ((t1 - t0) - window);",
      "const int64_t w = (t - t0) - ((t1 - t0) - window) - 1;"),
