@@ -33,7 +33,7 @@ MANIFEST = os.path.join(PKG, "kernel_manifest.json")
 LLVM = "/opt/rocm/llvm/bin"
 
 SOURCES = ["gdn_api.cpp", "gdn_runtime.cpp", "prefill_scan.hip", "prefill_chunked.hip", "prefill_split.hip", "prefill_wide.hip", "decode_step.hip",
-           "gate_prologue.hip", "causal_conv.hip", "gated_rmsnorm.hip"]
+           "gate_prologue.hip", "causal_conv.hip", "gated_rmsnorm.hip", "static_workspace.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

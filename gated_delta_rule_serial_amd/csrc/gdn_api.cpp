@@ -424,6 +424,41 @@ GDN_EXPORT gdn_status gdn_prefill_workspace_size(const gdn_problem* problem, int
   return ok();
 }
 
+GDN_EXPORT gdn_status gdn_prefill_static_workspace(const gdn_problem* problem, int32_t num_seqs,
+                                                   const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                                   int32_t total_tokens, const void* q, const void* k, const void* v,
+                                                   const float* initial_state, void* out, float* final_state,
+                                                   hipStream_t stream) {
+  const char* fn = "gdn_prefill_static_workspace";
+  gdn_status st = check_problem(problem, fn, total_tokens > 0);
+  if (st != GDN_OK) return st;
+  if (problem->workspace != nullptr || problem->workspace_bytes != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: takes no workspace (the library's own is used)", fn);
+  uint64_t need = 0;
+  st = gdn_prefill_workspace_size(problem, num_seqs, total_tokens, &need);
+  if (st != GDN_OK) return fail(st, "%s: %s", fn, g_last_error);
+  if (need > GDN_STATIC_WORKSPACE_BYTES)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "%s: %d sequences of %d tokens in all need %llu bytes of workspace, above the %llu bytes this "
+                "entry point holds; call gdn_prefill with a workspace of gdn_prefill_workspace_size bytes, or "
+                "fewer tokens per call",
+                fn, num_seqs, total_tokens, static_cast<unsigned long long>(need),
+                static_cast<unsigned long long>(GDN_STATIC_WORKSPACE_BYTES));
+  if (need == 0)  // a form without a workspace: nothing to lend
+    return prefill_impl(fn, problem, num_seqs, cu_seqlens, cu_seqlens_host, total_tokens, q, k, v, initial_state,
+                        out, final_state, nullptr, stream);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  const hipError_t e = gdn::static_workspace(&ws, &ws_bytes);
+  if (e != hipSuccess)
+    return fail(GDN_ERR_HIP, "%s: the static workspace's device address: %s", fn, hipGetErrorString(e));
+  gdn_problem p = *problem;
+  p.workspace = ws;
+  p.workspace_bytes = ws_bytes;
+  return prefill_impl(fn, &p, num_seqs, cu_seqlens, cu_seqlens_host, total_tokens, q, k, v, initial_state, out,
+                      final_state, nullptr, stream);
+}
+
 GDN_EXPORT gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t num_seqs, int32_t total_tokens,
                                              gdn_prefill_plan* plan) {
   const char* fn = "gdn_prefill_query_plan";

@@ -170,6 +170,9 @@ int device_compute_units();
 // Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
 // per (kernel, device).  Thread-safe.
 hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
+// The device address (per device, resolved once) and size of the library's
+// own two-pass workspace, a file-scope device array.
+hipError_t static_workspace(void** ptr, size_t* bytes);
 // Columns one decode workgroup owns.
 int decode_columns_per_block(int d_k, int d_v, bool per_key);
 

@@ -109,6 +109,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_prefill_workspace_size.argtypes = [pp, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
     lib.gdn_prefill_workspace_size.restype = ctypes.c_int
+    lib.gdn_prefill_static_workspace.argtypes = [pp, i32, vp, ip, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_prefill_static_workspace.restype = ctypes.c_int
     lib.gdn_prefill_query_plan.argtypes = [pp, i32, i32, ctypes.POINTER(gdn_prefill_plan)]
     lib.gdn_prefill_query_plan.restype = ctypes.c_int
     lib.gdn_last_error.argtypes = []
@@ -203,6 +205,28 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
         host = (ctypes.c_int32 * len(vals))(*vals)
     _check(load().gdn_prefill(ctypes.byref(prob), n, _ptr(cu_seqlens), host, T, _ptr(q), _ptr(k), _ptr(v),
                               _ptr(initial_state), _ptr(out), _ptr(final_state), _stream(stream, q.device)))
+
+
+STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def gdn_prefill_static_workspace(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                                 out: Optional[torch.Tensor], final_state: Optional[torch.Tensor],
+                                 initial_state: Optional[torch.Tensor] = None, g=None, beta=None, a=None, b=None,
+                                 A_log=None, dt_bias=None, scale: float = 0.0,
+                                 cu_seqlens_host: Optional[Sequence[int]] = None, algorithm: str = "auto",
+                                 stream=None, **variant) -> None:
+    """gdn_prefill_static_workspace of include/gdn.h: gdn_prefill with the
+    two-pass form's workspace taken from the library's own device array (no
+    ``workspace`` argument)."""
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
+                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm, **variant)
+    n = cu_seqlens.numel() - 1
+    _check(load().gdn_prefill_static_workspace(ctypes.byref(prob), n, _ptr(cu_seqlens), _host_i32(cu_seqlens_host),
+                                               T, _ptr(q), _ptr(k), _ptr(v), _ptr(initial_state), _ptr(out),
+                                               _ptr(final_state), _stream(stream, q.device)))
 
 
 def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor,

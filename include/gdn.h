@@ -248,6 +248,31 @@ gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t num_seqs,
                                   int32_t total_tokens, gdn_prefill_plan* plan);
 
 /*
+ * gdn_prefill_static_workspace -- gdn_prefill for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  Same arguments and result as
+ * gdn_prefill, with problem->workspace NULL and workspace_bytes 0: where the
+ * chunked form runs in two passes, its workspace is an array of
+ * GDN_STATIC_WORKSPACE_BYTES that the library holds in each device's memory
+ * from its first use there until the process ends.  The call allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.
+ *   - A problem whose two-pass workspace (gdn_prefill_workspace_size) exceeds
+ *     GDN_STATIC_WORKSPACE_BYTES is refused with GDN_ERR_UNSUPPORTED and
+ *     nothing is enqueued; forms without a workspace run as in gdn_prefill.
+ *   - Every call on one device shares that device's array: calls that overlap
+ *     in time on one device (on different streams, or from several threads
+ *     without ordering) race on it and give undefined results.  Calls in
+ *     stream order are safe; nothing in the array needs clearing between
+ *     them, as each call writes all it reads.
+ */
+#define GDN_STATIC_WORKSPACE_BYTES (64ull << 20)
+gdn_status gdn_prefill_static_workspace(const gdn_problem* problem, int32_t num_seqs,
+                                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                        int32_t total_tokens, const void* q, const void* k,
+                                        const void* v, const float* initial_state, void* out,
+                                        float* final_state, hipStream_t stream);
+
+/*
  * Slot-indexed state pool ([P3] nuvec-core, fast/imp.rs, `gated_delta_slots`:
  * recurrent states live in a pool and each sequence of a batch names its
  * state by an int32 slot; the state is gathered, run and scattered back).
