@@ -10,7 +10,11 @@
 //     y_t = z_t (or z_t * sigmoid(z_t) with silu)
 // where xp(p) is the state for p < 0 and the input for p >= 0; the new
 // state is the last `carry` positions of the padded input.  Layouts are
-// channels-last: x, y [T, C], states [N, carry, C], w [C, K].
+// channels-last: x, y [T, C], states [N, carry, C], w [C, K].  With a state
+// pool ([P3] `causal_conv1d_slots`: pool [slots, K - 1, C], int32 slots [B])
+// sequence n's state is row slots[n] of the pool, gathered and scattered back
+// in place; a slot outside the pool is a padding sequence (zero state,
+// nothing written back).
 //
 // HBM-bound elementwise work (K multiply-adds per element).  Kernels:
 //   conv_window_kernel  dilation 1, K <= 4, C a multiple of one 16-byte
@@ -62,14 +66,22 @@ __device__ __forceinline__ float silu_if(float z, int silu) {
   return silu ? z * fast_sigmoid(z) : z;
 }
 
-// Padded input of sequence n (first token t0, state row base s0n) at
+// Row of the state array that holds sequence n's state (n itself, or its
+// slot in a pool), or -1 when it has none (a padding slot).
+__device__ __forceinline__ int state_row(const ConvParams& p, int n) {
+  if (p.slots == nullptr) return n;
+  const int s = p.slots[n];
+  return (s >= 0 && s < p.num_slots) ? s : -1;
+}
+
+// Padded input of sequence n (first token t0, state row sr, -1 for none) at
 // position p relative to the sequence start, channel c.
 template <typename IO>
 __device__ __forceinline__ float xp_at(const IO* __restrict__ x, const IO* __restrict__ s0, int C, int carry,
-                                       int n, int t0, int p, int c) {
+                                       int sr, int t0, int p, int c) {
   if (p >= 0) return widen(x[static_cast<size_t>(t0 + p) * C + c]);
-  if (s0 == nullptr || p < -carry) return 0.0f;
-  return widen(s0[(static_cast<size_t>(n) * carry + carry + p) * C + c]);
+  if (s0 == nullptr || sr < 0 || p < -carry) return 0.0f;
+  return widen(s0[(static_cast<size_t>(sr) * carry + carry + p) * C + c]);
 }
 
 // Grid: kXcds * segs_per_xcd * channel_blocks workgroups.  Workgroup L runs
@@ -169,9 +181,9 @@ __global__ __launch_bounds__(kThreads) void conv_window_kernel(ConvParams p, int
       const int pos = t - m - ts;  // position in the sequence; < 0 is the state
       if (pos >= 0) {
         raw[W + i - m].widen_to(in);
-      } else if (s0 != nullptr && pos >= -p.carry) {
+      } else if (s0 != nullptr && pos >= -p.carry && state_row(p, n) >= 0) {
         RawSlice<IO, V> r;
-        r.load(s0 + (static_cast<size_t>(n) * p.carry + p.carry + pos) * C + c0);
+        r.load(s0 + (static_cast<size_t>(state_row(p, n)) * p.carry + p.carry + pos) * C + c0);
         r.widen_to(in);
       } else {
 #pragma unroll
@@ -204,7 +216,8 @@ __global__ __launch_bounds__(kThreads) void conv_generic_kernel(ConvParams p) {
     const int t0 = seq_begin(p.cu, n, p.total_tokens);
     float z = bs != nullptr ? widen(bs[c]) : 0.0f;
     for (int j = 0; j < K; ++j)
-      z = fmaf(widen(wt[static_cast<size_t>(c) * K + j]), xp_at(x, s0, C, p.carry, n, t0, t - t0 - p.carry + j * p.dilation, c), z);
+      z = fmaf(widen(wt[static_cast<size_t>(c) * K + j]),
+               xp_at(x, s0, C, p.carry, state_row(p, n), t0, t - t0 - p.carry + j * p.dilation, c), z);
     narrow_store(y + e, silu_if<IO>(z, p.silu));
   }
 }
@@ -223,12 +236,14 @@ __global__ __launch_bounds__(kThreads) void conv_state_kernel(ConvParams p) {
        e += static_cast<int64_t>(gridDim.x) * kThreads) {
     const int n = static_cast<int>(e / C);
     const int c = static_cast<int>(e % C);
+    const int sr = state_row(p, n);
+    if (sr < 0) continue;  // a padding slot keeps nothing
     const int t0 = seq_begin(p.cu, n, p.total_tokens);
     const int L = seq_end(p.cu, n, p.total_tokens) - t0;
     if (L == 0 && s0 == sN) continue;  // the state is unchanged
     for (int i = 0; i < p.carry; ++i) {
-      const float v = xp_at(x, s0, C, p.carry, n, t0, L - p.carry + i, c);
-      narrow_store(sN + (static_cast<size_t>(n) * p.carry + i) * C + c, v);
+      const float v = xp_at(x, s0, C, p.carry, sr, t0, L - p.carry + i, c);
+      narrow_store(sN + (static_cast<size_t>(sr) * p.carry + i) * C + c, v);
     }
   }
 }
@@ -248,15 +263,17 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(ConvParams p) {
        e += static_cast<int64_t>(gridDim.x) * kThreads) {
     const int b = static_cast<int>(e / C);
     const int c = static_cast<int>(e % C);
-    IO* sb = st + static_cast<size_t>(b) * p.carry * C + c;
+    const int sr = state_row(p, b);  // -1: a padding slot, zero state, nothing kept
+    IO* sb = sr >= 0 ? st + static_cast<size_t>(sr) * p.carry * C + c : nullptr;
     const IO xv = x[e];
     float z = bs != nullptr ? widen(bs[c]) : 0.0f;
     for (int j = 0; j < K; ++j) {
       const int pos = j * p.dilation - p.carry;  // <= 0
-      const float xin = pos == 0 ? widen(xv) : widen(sb[static_cast<size_t>(p.carry + pos) * C]);
+      const float xin = pos == 0 ? widen(xv) : (sb != nullptr ? widen(sb[static_cast<size_t>(p.carry + pos) * C]) : 0.0f);
       z = fmaf(widen(wt[static_cast<size_t>(c) * K + j]), xin, z);
     }
     narrow_store(y + e, silu_if<IO>(z, p.silu));
+    if (sb == nullptr) continue;
     for (int i = 0; i + 1 < p.carry; ++i) sb[static_cast<size_t>(i) * C] = sb[static_cast<size_t>(i + 1) * C];
     if (p.carry > 0) sb[static_cast<size_t>(p.carry - 1) * C] = xv;
   }

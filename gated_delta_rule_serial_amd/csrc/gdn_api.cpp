@@ -602,10 +602,11 @@ gdn::ConvParams conv_params(const gdn_conv_problem& c) {
 
 }  // namespace
 
-GDN_EXPORT gdn_status gdn_causal_conv(const gdn_conv_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
-                                      const int32_t* cu_seqlens_host, int32_t total_tokens, const void* x,
-                                      const void* initial_state, void* y, void* final_state, hipStream_t stream) {
-  const char* fn = "gdn_causal_conv";
+namespace {
+
+gdn_status conv_impl(const char* fn, const gdn_conv_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
+                     const int32_t* cu_seqlens_host, int32_t total_tokens, const void* x, const void* initial_state,
+                     void* y, void* final_state, const SlotArgs* pool, hipStream_t stream) {
   gdn_status st = check_conv(problem, fn);
   if (st != GDN_OK) return st;
   const gdn_conv_problem& c = *problem;
@@ -631,10 +632,14 @@ GDN_EXPORT gdn_status gdn_causal_conv(const gdn_conv_problem* problem, int32_t n
       return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens[%d]=%d but total_tokens=%d", fn, num_seqs,
                   cu_seqlens_host[num_seqs], total_tokens);
   }
+  if (pool) {
+    st = check_slots(*pool, num_seqs, fn);
+    if (st != GDN_OK) return st;
+  }
   const size_t es = io_size(c.io_dtype);
   const int32_t carry = (c.kernel_size - 1) * c.dilation;
   const size_t xy_bytes = static_cast<size_t>(total_tokens) * c.channels * es;
-  const size_t st_bytes = static_cast<size_t>(num_seqs) * carry * c.channels * es;
+  const size_t st_bytes = static_cast<size_t>(pool ? pool->num_slots : num_seqs) * carry * c.channels * es;
   if (overlaps(y, xy_bytes, x, xy_bytes)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: y overlaps x", fn);
   if (overlaps(y, xy_bytes, initial_state, st_bytes) || overlaps(y, xy_bytes, final_state, st_bytes) ||
       overlaps(x, xy_bytes, final_state, st_bytes))
@@ -650,27 +655,33 @@ GDN_EXPORT gdn_status gdn_causal_conv(const gdn_conv_problem* problem, int32_t n
   cp.cu = cu_seqlens;
   cp.num_seqs = num_seqs;
   cp.total_tokens = total_tokens;
+  cp.slots = pool ? pool->slots : nullptr;
+  cp.num_slots = pool ? pool->num_slots : 0;
   const hipError_t e = gdn::launch_causal_conv(cp, c.io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
 
-GDN_EXPORT gdn_status gdn_causal_conv_step(const gdn_conv_problem* problem, int32_t batch, const void* x, void* state,
-                                           void* y, hipStream_t stream) {
-  const char* fn = "gdn_causal_conv_step";
+gdn_status conv_step_impl(const char* fn, const gdn_conv_problem* problem, int32_t batch, const void* x, void* state,
+                          void* y, const SlotArgs* pool, hipStream_t stream) {
   gdn_status st = check_conv(problem, fn);
   if (st != GDN_OK) return st;
   const gdn_conv_problem& c = *problem;
   if (batch < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: batch=%d is negative", fn, batch);
   if (batch == 0) return ok();
+  if (pool) {
+    st = check_slots(*pool, batch, fn);
+    if (st != GDN_OK) return st;
+  }
   const int32_t carry = (c.kernel_size - 1) * c.dilation;
-  if (!x || !y || !c.weight || (carry > 0 && !state))
+  const bool needs_state = carry > 0 && !(pool && pool->num_slots == 0);
+  if (!x || !y || !c.weight || (needs_state && !state))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, y, weight and the state are required", fn);
   if (!aligned16(x) || !aligned16(y) || !aligned16(state))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, y and the state must be 16-byte aligned", fn);
   const size_t es = io_size(c.io_dtype);
   const size_t xy_bytes = static_cast<size_t>(batch) * c.channels * es;
-  const size_t st_bytes = static_cast<size_t>(batch) * carry * c.channels * es;
+  const size_t st_bytes = static_cast<size_t>(pool ? pool->num_slots : batch) * carry * c.channels * es;
   if (overlaps(y, xy_bytes, x, xy_bytes) || overlaps(y, xy_bytes, state, st_bytes) ||
       overlaps(x, xy_bytes, state, st_bytes))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, y and the state must not overlap", fn);
@@ -681,9 +692,51 @@ GDN_EXPORT gdn_status gdn_causal_conv_step(const gdn_conv_problem* problem, int3
   cp.y = y;
   cp.num_seqs = batch;
   cp.total_tokens = batch;
+  cp.slots = pool ? pool->slots : nullptr;
+  cp.num_slots = pool ? pool->num_slots : 0;
   const hipError_t e = gdn::launch_causal_conv_step(cp, c.io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+GDN_EXPORT gdn_status gdn_causal_conv(const gdn_conv_problem* problem, int32_t num_seqs, const int32_t* cu_seqlens,
+                                      const int32_t* cu_seqlens_host, int32_t total_tokens, const void* x,
+                                      const void* initial_state, void* y, void* final_state, hipStream_t stream) {
+  return conv_impl("gdn_causal_conv", problem, num_seqs, cu_seqlens, cu_seqlens_host, total_tokens, x,
+                   initial_state, y, final_state, nullptr, stream);
+}
+
+GDN_EXPORT gdn_status gdn_causal_conv_slots(const gdn_conv_problem* problem, int32_t num_seqs,
+                                            const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                            int32_t total_tokens, const void* x, void* state_pool, int32_t num_slots,
+                                            const int32_t* slots, const int32_t* slots_host, void* y,
+                                            hipStream_t stream) {
+  const char* fn = "gdn_causal_conv_slots";
+  if (num_slots > 0 && !state_pool && problem && problem->kernel_size > 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_pool is NULL", fn);
+  SlotArgs sl;
+  sl.slots = slots;
+  sl.slots_host = slots_host;
+  sl.num_slots = num_slots;
+  return conv_impl(fn, problem, num_seqs, cu_seqlens, cu_seqlens_host, total_tokens, x, state_pool, y, state_pool,
+                   &sl, stream);
+}
+
+GDN_EXPORT gdn_status gdn_causal_conv_step(const gdn_conv_problem* problem, int32_t batch, const void* x, void* state,
+                                           void* y, hipStream_t stream) {
+  return conv_step_impl("gdn_causal_conv_step", problem, batch, x, state, y, nullptr, stream);
+}
+
+GDN_EXPORT gdn_status gdn_causal_conv_step_slots(const gdn_conv_problem* problem, int32_t batch, const void* x,
+                                                 void* state_pool, int32_t num_slots, const int32_t* slots,
+                                                 const int32_t* slots_host, void* y, hipStream_t stream) {
+  SlotArgs sl;
+  sl.slots = slots;
+  sl.slots_host = slots_host;
+  sl.num_slots = num_slots;
+  return conv_step_impl("gdn_causal_conv_step_slots", problem, batch, x, state_pool, y, &sl, stream);
 }
 
 GDN_EXPORT gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, int32_t io_dtype, const void* x,

@@ -93,6 +93,11 @@ struct ConvParams {
   int32_t dilation;
   int32_t carry;          // (ksize - 1) * dilation
   int32_t silu;
+  // State pool indirection: when slots != null, sequence n's state is row
+  // slots[n] of s0/sN (both point at the pool [num_slots, carry, C]); a slot
+  // outside [0, num_slots) starts from zeros and is not written back.
+  const int32_t* slots;   // [N] or null
+  int32_t num_slots;
 };
 
 // Gated RMSNorm over groups of `group` elements.

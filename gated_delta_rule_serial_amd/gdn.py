@@ -105,6 +105,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_causal_conv.restype = ctypes.c_int
     lib.gdn_causal_conv_step.argtypes = [cp, i32, vp, vp, vp, vp]
     lib.gdn_causal_conv_step.restype = ctypes.c_int
+    lib.gdn_causal_conv_slots.argtypes = [cp, i32, vp, ip, i32, vp, vp, i32, vp, ip, vp, vp]
+    lib.gdn_causal_conv_slots.restype = ctypes.c_int
+    lib.gdn_causal_conv_step_slots.argtypes = [cp, i32, vp, vp, i32, vp, ip, vp, vp]
+    lib.gdn_causal_conv_step_slots.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, i32, vp, vp, vp, ctypes.c_float, i32, vp, vp]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_prefill_workspace_size.argtypes = [pp, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
@@ -346,6 +350,31 @@ def gdn_causal_conv_step(x: torch.Tensor, weight: torch.Tensor, state: torch.Ten
     prob = make_conv_problem(weight, bias, dilation=dilation, activation=activation)
     _check(load().gdn_causal_conv_step(ctypes.byref(prob), x.shape[0], _ptr(x), _ptr(state), _ptr(y),
                                        _stream(stream, x.device)))
+
+
+def gdn_causal_conv_slots(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor, state_pool: torch.Tensor,
+                          slots: torch.Tensor, *, y: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                          dilation: int = 1, activation: str = "silu", cu_seqlens_host: Optional[Sequence[int]] = None,
+                          slots_host: Optional[Sequence[int]] = None, stream=None) -> None:
+    """gdn_causal_conv_slots of include/gdn.h: sequence i runs from and writes
+    back state_pool[slots[i]] ([num_slots, carry, C], the I/O dtype)."""
+    prob = make_conv_problem(weight, bias, dilation=dilation, activation=activation)
+    n = cu_seqlens.numel() - 1
+    _check(load().gdn_causal_conv_slots(ctypes.byref(prob), n, _ptr(cu_seqlens), _host_i32(cu_seqlens_host),
+                                        x.shape[0], _ptr(x), _ptr(state_pool), state_pool.shape[0], _ptr(slots),
+                                        _host_i32(slots_host), _ptr(y), _stream(stream, x.device)))
+
+
+def gdn_causal_conv_step_slots(x: torch.Tensor, weight: torch.Tensor, state_pool: torch.Tensor, slots: torch.Tensor,
+                               *, y: torch.Tensor, bias: Optional[torch.Tensor] = None, dilation: int = 1,
+                               activation: str = "silu", slots_host: Optional[Sequence[int]] = None,
+                               stream=None) -> None:
+    """gdn_causal_conv_step_slots of include/gdn.h: one token per sequence, the
+    state of sequence i at state_pool[slots[i]] shifted in place."""
+    prob = make_conv_problem(weight, bias, dilation=dilation, activation=activation)
+    _check(load().gdn_causal_conv_step_slots(ctypes.byref(prob), x.shape[0], _ptr(x), _ptr(state_pool),
+                                             state_pool.shape[0], _ptr(slots), _host_i32(slots_host), _ptr(y),
+                                             _stream(stream, x.device)))
 
 
 def gdn_gated_rmsnorm(x: torch.Tensor, gate: torch.Tensor, scale: torch.Tensor, *, y: torch.Tensor,

@@ -377,6 +377,35 @@ gdn_status gdn_causal_conv_step(const gdn_conv_problem* problem, int32_t batch, 
                                 void* state, void* y, hipStream_t stream);
 
 /*
+ * The convolution over a slot-indexed state pool ([P3] nuvec-core, fast/imp.rs,
+ * `causal_conv1d_slots`: pool [slots, K - 1, C] and int32 slots [B]; each
+ * sequence's state pool[slots[b]] is put in front of its new inputs, the
+ * depthwise convolution (and silu) runs over them, and the last K - 1 inputs
+ * are written back to the same pool row).
+ *   state_pool  [num_slots, carry, C] io_dtype, read and updated in place
+ *   slots       device int32 [n] (n = num_seqs or batch): sequence i's state
+ *               is state_pool[slots[i]].  A slot outside [0, num_slots) is a
+ *               padding sequence: it starts from a zero state and nothing is
+ *               written back for it (its outputs are still written).  Slots
+ *               inside the range must be distinct.
+ *   slots_host  optional host copy; when given, distinctness is checked
+ *               (GDN_ERR_INVALID_ARGUMENT on a repeated slot).  The kernels
+ *               bounds-check every slot they read.
+ * Everything else is as in gdn_causal_conv / gdn_causal_conv_step (carry =
+ * (kernel_size - 1) * dilation; [P3] has dilation 1).
+ */
+gdn_status gdn_causal_conv_slots(const gdn_conv_problem* problem, int32_t num_seqs,
+                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                 int32_t total_tokens, const void* x, void* state_pool,
+                                 int32_t num_slots, const int32_t* slots,
+                                 const int32_t* slots_host, void* y, hipStream_t stream);
+
+gdn_status gdn_causal_conv_step_slots(const gdn_conv_problem* problem, int32_t batch,
+                                      const void* x, void* state_pool, int32_t num_slots,
+                                      const int32_t* slots, const int32_t* slots_host, void* y,
+                                      hipStream_t stream);
+
+/*
  * gdn_gated_rmsnorm -- gated RMSNorm ([P1] `gated_rms_norm_op`): each row of
  * `width` elements is split into width / group groups of `group` consecutive
  * elements, and per group, in float32,

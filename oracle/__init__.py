@@ -127,6 +127,8 @@ class Oracle:
         lib.gdnref_decode_step.restype = ctypes.c_int
         lib.gdnref_causal_conv.argtypes = [i32, i32, i32, i32, i32, ip, dp, dp, dp, dp, dp, dp]
         lib.gdnref_causal_conv.restype = ctypes.c_int
+        lib.gdnref_causal_conv_slots.argtypes = [i32, i32, i32, i32, i32, ip, dp, dp, dp, dp, i32, ip, dp]
+        lib.gdnref_causal_conv_slots.restype = ctypes.c_int
         lib.gdnref_gated_rmsnorm.argtypes = [i64, i32, i32, dp, dp, dp, f64, i32, dp]
         lib.gdnref_gated_rmsnorm.restype = ctypes.c_int
         lib.gdnref_max_threads.argtypes = []
@@ -228,6 +230,23 @@ class Oracle:
         if rc != 0:
             raise ValueError("gdnref_causal_conv rejected its arguments")
         return y, fin
+
+    def causal_conv_slots(self, x, weight, cu_seqlens, pool, slots, bias=None, *, dilation=1, silu=False):
+        """The convolution over a state pool.  pool: [num_slots, carry, C] (not
+        modified); slots: ints [N].  Returns (y [T, C], the updated pool) float64."""
+        x, w, b = _f64(x), _f64(weight), _f64(bias)
+        pool = _f64(pool).copy()
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+        T, C = x.shape
+        n = cu.size - 1
+        y = np.empty((T, C), np.float64)
+        rc = self.lib.gdnref_causal_conv_slots(C, w.shape[1], int(dilation), int(bool(silu)), n,
+                                               _ptr(cu, ctypes.c_int32), _ptr(x), _ptr(w), _ptr(b), _ptr(pool),
+                                               pool.shape[0], _ptr(sl, ctypes.c_int32), _ptr(y))
+        if rc != 0:
+            raise ValueError("gdnref_causal_conv_slots rejected its arguments")
+        return y, pool
 
     def gated_rmsnorm(self, x, gate, scale, *, eps=1e-5, activation="silu"):
         """Gated RMSNorm over groups of len(scale) elements of the last axis of x."""

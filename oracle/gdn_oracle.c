@@ -255,6 +255,42 @@ int gdnref_causal_conv(int32_t channels, int32_t ksize, int32_t dilation, int32_
   return 0;
 }
 
+/* [P3] `causal_conv1d_slots`: the states of the sequences are gathered from
+ * the pool at their slots (pool[slots[n]]), the convolution above runs on
+ * them, and each new state is scattered back to its slot.  A slot outside
+ * [0, num_slots) is a padding sequence: a zero state, nothing written back. */
+int gdnref_causal_conv_slots(int32_t channels, int32_t ksize, int32_t dilation, int32_t silu,
+                             int32_t num_seqs, const int32_t* cu_seqlens, const double* x,
+                             const double* weight, const double* bias, double* pool,
+                             int32_t num_slots, const int32_t* slots, double* y) {
+  if (num_seqs < 0 || num_slots < 0 || (num_seqs > 0 && !slots)) return -1;
+  const int64_t carry = (int64_t)(ksize - 1) * dilation;
+  const int64_t per = carry * channels;
+  double* states = (double*)calloc((size_t)(num_seqs * per + 1), sizeof(double));
+  double* fresh = (double*)calloc((size_t)(num_seqs * per + 1), sizeof(double));
+  if (!states || !fresh) {
+    free(states);
+    free(fresh);
+    return -1;
+  }
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int32_t s = slots[n];
+    if (s >= 0 && s < num_slots)
+      for (int64_t e = 0; e < per; ++e) states[n * per + e] = pool[(int64_t)s * per + e];
+  }
+  const int rc = gdnref_causal_conv(channels, ksize, dilation, silu, num_seqs, cu_seqlens, x, weight,
+                                    bias, states, y, fresh);
+  if (rc == 0)
+    for (int32_t n = 0; n < num_seqs; ++n) {
+      const int32_t s = slots[n];
+      if (s >= 0 && s < num_slots)
+        for (int64_t e = 0; e < per; ++e) pool[(int64_t)s * per + e] = fresh[n * per + e];
+    }
+  free(states);
+  free(fresh);
+  return rc;
+}
+
 /* [P1] `gated_rms_norm_op`: rows of `group` elements in float, mean of the
  * squares plus epsilon, reciprocal square root, times the scale, times the
  * gate's activation (silu by default, or sigmoid). */

@@ -145,6 +145,15 @@ int gdnref_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, const doubl
                          const double* gate, const double* scale, double eps,
                          int32_t activation, double* y);
 
+/* The convolution over a state pool ([P3] `causal_conv1d_slots`): pool
+ * [num_slots, carry, C]; sequence n's state is pool[slots[n]], read and
+ * replaced by its new state; a slot outside [0, num_slots) starts from zeros
+ * and is not written back.  Returns 0, or -1 on an invalid argument. */
+int gdnref_causal_conv_slots(int32_t channels, int32_t ksize, int32_t dilation, int32_t silu,
+                             int32_t num_seqs, const int32_t* cu_seqlens, const double* x,
+                             const double* weight, const double* bias, double* pool,
+                             int32_t num_slots, const int32_t* slots, double* y);
+
 /* Threads the parallel loop over independent (sequence, head) units uses. */
 int gdnref_max_threads(void);
 

@@ -518,6 +518,34 @@ def pin_conv_special_kernels(orc):
     assert np.array_equal(y0, yz) and np.array_equal(f0, fz)
 
 
+def pin_conv_slots(orc):
+    """The pool form: gathering the states at the slots (numpy indexing), the
+    plain convolution (pinned above against torch), and scattering the new
+    states back is exactly what the slot-pool conv gives, bitwise; rows no
+    sequence names stay as they were; a padding slot (outside the pool) runs
+    from zeros and writes nothing; identity slots equal the plain call."""
+    rng, cu, x, w, b = _conv_case(51, [6, 0, 4, 3, 5])
+    C, K = w.shape
+    for dil in (1, 2):
+        carry = (K - 1) * dil
+        pool = rng.standard_normal((7, carry, C))
+        for slots in ([4, 1, -1, 6, 0], [0, 1, 2, 3, 4], [6, 5, 7, 2, -3]):
+            states = np.zeros((len(slots), carry, C))
+            for n, sl in enumerate(slots):
+                if 0 <= sl < 7:
+                    states[n] = pool[sl]
+            y_ref, f_ref = orc.causal_conv(x, w, cu, b, states, dilation=dil, silu=True)
+            pool_ref = pool.copy()
+            for n, sl in enumerate(slots):
+                if 0 <= sl < 7:
+                    pool_ref[sl] = f_ref[n]
+            y, new_pool = orc.causal_conv_slots(x, w, cu, pool, slots, b, dilation=dil, silu=True)
+            assert np.array_equal(y, y_ref) and np.array_equal(new_pool, pool_ref), (dil, slots)
+        y_id, pool_id = orc.causal_conv_slots(x, w, cu, pool[:5], [0, 1, 2, 3, 4], b, dilation=dil, silu=True)
+        y_pl, f_pl = orc.causal_conv(x, w, cu, b, pool[:5], dilation=dil, silu=True)
+        assert np.array_equal(y_id, y_pl) and np.array_equal(pool_id, f_pl), dil
+
+
 # ---------------------------------------------------------------- gated RMSNorm
 def pin_rmsnorm_library(orc):
     """Against torch's rms_norm (with the scale as its weight) times torch's
@@ -573,6 +601,6 @@ ALL_PINS = [
     pin_empty, pin_scalar_closed_form, pin_orthonormal_keys, pin_gates_library,
     pin_default_scale, pin_page_worked_example, pin_rounding_tie, pin_variants_brute_force,
     pin_variant_reductions, pin_state_history, pin_page_worked_example_window,
-    pin_conv_library, pin_conv_continuation, pin_conv_special_kernels,
+    pin_conv_library, pin_conv_continuation, pin_conv_special_kernels, pin_conv_slots,
     pin_rmsnorm_library, pin_rmsnorm_invariants,
 ]

@@ -366,3 +366,23 @@ def test_prefill_query_plan(lib):
     with pytest.raises(gdn.GdnError, match="chunked algorithm needs"):
         q(2, 2, 16, 16, f32, 1, 64, algorithm="chunked")
     assert lib.gdn_prefill_query_plan(None, 1, 8, None) == INVALID
+
+
+def test_conv_slots_validation(lib):
+    """The pool forms of the convolution check their slots like the recurrence's."""
+    prob = gdn.gdn_conv_problem(64, 4, 1, gdn.GDN_BF16, gdn.GDN_ACT_SILU, ctypes.c_void_p(FAKE), None)
+    vp = ctypes.c_void_p
+    host = (ctypes.c_int32 * 2)(3, 3)
+    cu = (ctypes.c_int32 * 3)(0, 4, 8)
+    st = lib.gdn_causal_conv_slots(ctypes.byref(prob), 2, vp(FAKE + 0x1000), cu, 8, vp(FAKE + 0x10000),
+                                   vp(FAKE + 0x20000), 5, vp(FAKE + 0x3000), host, vp(FAKE + 0x40000), None)
+    assert st == INVALID and "slot 3" in gdn.last_error()
+    st = lib.gdn_causal_conv_step_slots(ctypes.byref(prob), 2, vp(FAKE + 0x10000), vp(FAKE + 0x20000), 5,
+                                        vp(FAKE + 0x3000), host, vp(FAKE + 0x40000), None)
+    assert st == INVALID and "slot 3" in gdn.last_error()
+    st = lib.gdn_causal_conv_step_slots(ctypes.byref(prob), 2, vp(FAKE + 0x10000), vp(FAKE + 0x20000), -1,
+                                        vp(FAKE + 0x3000), None, vp(FAKE + 0x40000), None)
+    assert st == INVALID and "num_slots" in gdn.last_error()
+    st = lib.gdn_causal_conv_step_slots(ctypes.byref(prob), 2, vp(FAKE + 0x10000), vp(FAKE + 0x20000), 5,
+                                        None, None, vp(FAKE + 0x40000), None)
+    assert st == INVALID and "slots is NULL" in gdn.last_error()

@@ -171,3 +171,61 @@ def test_gated_rmsnorm_in_place_and_full_size():
     rows = torch.tensor(sorted(np.random.default_rng(6).choice(shape.rows, 512, replace=False).tolist()))
     ref = oracle.default().gated_rmsnorm(inp.x[rows], inp.gate[rows], inp.scale)
     check(x[rows.cuda()].double().cpu(), torch.from_numpy(ref), TOL[shape.io_dtype], "y (sampled rows)")
+
+
+# ------------------------------------------------------------------ the conv over a slot-indexed pool
+CONV_SLOT_CASES = [
+    # (channels, K, dilation, dtype, seqlens, slots, pool rows)
+    (8192, 4, 1, torch.bfloat16, [37, 0, 129, 64, 1, 250, 3], [9, 2, -1, 0, 5, 11, 7], 11),  # 11: padding
+    (64, 4, 1, torch.float32, [5, 9, 16], [1, 0, 2], 3),
+    (32, 3, 2, torch.bfloat16, [20, 3, 0, 8], [3, -5, 1, 6], 7),                              # generic path
+    (40, 6, 1, torch.float16, [30, 2], [0, 4], 5),
+]
+
+
+@pytest.mark.parametrize("case", CONV_SLOT_CASES, ids=lambda c: f"C{c[0]}_K{c[1]}_d{c[2]}_{str(c[3])[6:]}")
+def test_causal_conv_slots(case):
+    """gdn_causal_conv_slots against the oracle's pool form: outputs within
+    tolerance, the pool (copies of inputs) bit for bit, rows no sequence
+    names untouched."""
+    C, K, dil, dt, lens, slots, rows = case
+    shape = _conv_shape(channels=C, kernel_size=K, dilation=dil, io_dtype=dt)
+    say(f"[conv-slots] {case}")
+    inp = synth.generate_conv(shape, seqlens=lens, seed=311)
+    carry = (K - 1) * dil
+    pool0 = synth.generate_conv(dataclasses.replace(shape, num_seqs=rows), seqlens=[0] * rows, seed=312).initial_state
+    pool = to_dev(pool0).clone()
+    sl = torch.tensor(slots, dtype=torch.int32)
+    y = torch.empty_like(to_dev(inp.x))
+    gdn.gdn_causal_conv_slots(to_dev(inp.x), to_dev(inp.weight), to_dev(inp.cu_seqlens), pool, to_dev(sl), y=y,
+                              bias=to_dev(inp.bias), dilation=dil, cu_seqlens_host=inp.cu_seqlens.tolist(),
+                              slots_host=slots)
+    torch.cuda.synchronize()
+    assert pool.shape == (rows, carry, C)
+    ry, rpool = oracle.default().causal_conv_slots(inp.x, inp.weight, inp.cu_seqlens.numpy(), pool0, slots,
+                                                   inp.bias, dilation=dil, silu=True)
+    check(y.double().cpu(), torch.from_numpy(ry), TOL[dt], "y")
+    assert torch.equal(pool.double().cpu(), torch.from_numpy(rpool)), "pool differs"
+
+
+def test_causal_conv_step_slots_chain():
+    """Three one-token steps of 16 sequences over a pool of 24 rows (two
+    padding sequences), against the oracle's pool form step by step."""
+    shape = _conv_shape("conv_step_b64", channels=512, num_seqs=16)
+    slots = [23, 0, 5, -1, 7, 8, 30, 1, 2, 3, 4, 9, 10, 11, 12, 13]
+    pool0 = synth.generate_conv(dataclasses.replace(shape, num_seqs=24), seqlens=[0] * 24, seed=321).initial_state
+    pool = to_dev(pool0).clone()
+    ref_pool = pool0
+    w = synth.generate_conv(shape, seed=322)
+    say("[conv-step-slots] 3 steps")
+    for step in range(3):
+        inp = synth.generate_conv(shape, seed=4100 + step)
+        y = torch.empty_like(to_dev(inp.x))
+        gdn.gdn_causal_conv_step_slots(to_dev(inp.x), to_dev(w.weight), pool, to_dev(torch.tensor(slots, dtype=torch.int32)),
+                                       y=y, bias=to_dev(w.bias), slots_host=slots)
+        torch.cuda.synchronize()
+        ry, rp = oracle.default().causal_conv_slots(inp.x, w.weight, np.arange(17), ref_pool, slots, w.bias,
+                                                    silu=True)
+        check(y.double().cpu(), torch.from_numpy(ry), TOL[torch.bfloat16], f"y step {step}")
+        assert torch.equal(pool.double().cpu(), torch.from_numpy(rp)), f"pool step {step}"
+        ref_pool = torch.from_numpy(rp).to(torch.bfloat16)

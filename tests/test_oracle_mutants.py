@@ -40,6 +40,9 @@ MUTANTS = [
     ("conv bias dropped", "double z = bias ? bias[c] : 0.0;", "double z = 0.0;"),
     ("conv state off by one", "fs[i * channels + c] = XP(L - carry + i);", "fs[i * channels + c] = XP(L - carry + i - 1);"),
     ("conv initial state ignored", "(s0 ? s0[(carry + (p)) * channels + c] : 0.0)", "0.0"),
+    ("conv slot ignored", "states[n * per + e] = pool[(int64_t)s * per + e];",
+     "states[n * per + e] = pool[(int64_t)n * per + e];"),
+    ("conv new state not written back", "pool[(int64_t)s * per + e] = fresh[n * per + e];", ";"),
     ("rmsnorm mean over the row", "sqrt(ss / group + eps)", "sqrt(ss / width + eps)"),
     ("rmsnorm eps outside the root", "sqrt(ss / group + eps)", "(sqrt(ss / group) + eps)"),
     ("rmsnorm activations swapped", "activation == 1 ? gr[i] * s : s", "activation == 2 ? gr[i] * s : s"),
