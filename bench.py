@@ -91,11 +91,11 @@ def _manifest():
         return None
 
 
-def _traffic(name: str):
-    """HBM bytes per launch measured with rocprofv3 counters
-    (profiles/<name>_traffic.json), or None when there is no record or when
-    the machine code of a kernel it measured differs from the built one (the
-    record lists each kernel's code digest, from the build's manifest)."""
+def _record(name: str):
+    """The rocprofv3 counter record profiles/<name>_traffic.json, or None when
+    there is none or when the machine code of a kernel it measured differs
+    from the built one (the record lists each kernel's code digest, from the
+    build's manifest)."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -108,7 +108,27 @@ def _traffic(name: str):
     for kname, digest in code.items():
         if man.get(kname, {}).get("code_sha256_16") != digest:
             return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def _traffic(name: str):
+    """HBM bytes per launch from the counter record (None when stale or absent)."""
+    rec = _record(name)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def _counters(name: str):
+    """Per-kernel utilisation counters of the record (MfmaUtil, VALUBusy,
+    VALUUtilization, LDSBankConflict, in percent), keyed by kernel template
+    name; None when the record is stale or absent."""
+    rec = _record(name)
+    if rec is None or not rec.get("utilisation_pct"):
+        return None
+    out = {}
+    for k, v in rec["utilisation_pct"].items():
+        short = k.replace("gdn::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        out[short] = v
+    return out
 
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
@@ -256,7 +276,7 @@ def bench_decode(shape, steps, warmup, want_cpu):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(shape.name),
                      "kernel": "decode_kernel<bf16, d_k 128, 128 columns per workgroup, precomputed gates>",
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "algorithmic_bytes_per_launch": nbytes, "counters_pct": _counters(shape.name)},
         "config": {"workload": shape.name, "batch": shape.num_seqs, "h_qk": shape.h_qk, "h_v": shape.h_v,
                    "d_k": shape.d_k, "d_v": shape.d_v, "io_dtype": "bf16", "state_dtype": "f32",
                    "gates": "precomputed bf16", "state_buffers_rotated": DECODE_STATE_BUFFERS},
@@ -283,6 +303,7 @@ def prefill_roofline(shape, T, ms, nbytes, plan, ws_bytes):
     hbm_gbs = nbytes / (ms * 1e-3) / 1e9
     form = plan["form"]
     traffic = _traffic(f"{shape.name}_{form}")
+    counters = _counters(f"{shape.name}_{form}")
     if form.startswith("chunked"):
         # float32 I/O: three bf16 MFMA products (hi.hi + hi.lo + lo.hi) per product
         fl = chunked_flops(shape, T) * (3 if form == "chunked_f32" else 1)
@@ -290,13 +311,14 @@ def prefill_roofline(shape, T, ms, nbytes, plan, ws_bytes):
         return {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": plan["kernels"],
                 "algorithmic_bytes_per_launch": nbytes, "workspace_bytes": ws_bytes,
-                "mfma_tflops": round(tf, 2), "mfma_frac_of_bf16_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+                "mfma_tflops": round(tf, 2), "mfma_frac_of_bf16_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                "counters_pct": counters}
     fl = flops_serial(shape, T)
     tf = fl / (ms * 1e-3) / 1e12
     return {"bound": "alu", "achieved": round(tf, 2), "peak": round(FP32_VALU_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
             "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": plan["kernels"],
             "flops_per_launch": fl, "algorithmic_bytes_per_launch": nbytes,
-            "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
+            "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "counters_pct": counters}
 
 
 def bench_prefill(shape, steps, warmup, want_cpu, algorithm="auto", two_pass=True, flush=None):
