@@ -33,6 +33,7 @@ resident in device memory before the timed region starts.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -484,6 +485,86 @@ def bench_norm(shape, steps, warmup, want_cpu):
     return line
 
 
+# Shapes of the output-norm comparison: the decode step, the packed 8-sequence
+# workload (its state pass runs 64-column blocks, so AUTO keeps the norm a
+# separate pass), and the same geometry at 16 sequences of 2048 tokens (512
+# units: 128-column blocks, where AUTO fuses the norm into the state pass).
+NORM_SHAPES = {
+    "decode_b64": synth.BY_NAME["decode_b64"],
+    "varlen_prefill_8seq": synth.BY_NAME["varlen_prefill_8seq"],
+    "packed_16x2048": dataclasses.replace(synth.BY_NAME["varlen_prefill_8seq"], name="packed_16x2048", num_seqs=16,
+                                          seqlen=2048, len_range=None),
+}
+
+
+def bench_output_norm(name, steps, warmup, flush):
+    """The recurrence with its gated RMSNorm epilogue (one group per value head),
+    fused into the output store where the plan fuses it, against the unfused
+    pair: the recurrence writing o, then gdn_gated_rmsnorm over o in place.
+    Algorithmic bytes: the fused call replaces the write of o by the read of
+    the gate and the write of y; the pair adds to the recurrence's bytes a
+    read of o and of the gate and a write of y."""
+    dev = "cuda"
+    shape = NORM_SHAPES[name]
+    inp = synth.generate(shape)
+    T = inp.total_tokens
+    n = len(inp.seqlens)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    raw = shape.gate_mode == "raw"
+    decode = shape.kind == "decode"
+    if raw:
+        gates = dict(a=inp.a.to(dev), b=inp.b.to(dev), A_log=inp.A_log.to(dev), dt_bias=inp.dt_bias.to(dev))
+    else:
+        g, beta = gdn.gate_prologue(inp.a.to(dev), inp.b.to(dev), inp.A_log.to(dev), inp.dt_bias.to(dev))
+        gates = dict(g=g, beta=beta)
+    gate, scale = synth.output_norm_inputs(T, shape.h_v, shape.d_v, seed=1234 + 30, io_dtype=shape.io_dtype)
+    gate, scale = gate.to(dev), scale.to(dev)
+    out = torch.empty(T, shape.h_v, shape.d_v, dtype=shape.io_dtype, device=dev)
+    es = out.element_size()
+    if decode:
+        states = [inp.initial_state.to(dev).clone() for _ in range(DECODE_STATE_BUFFERS)]
+        it = [0]
+
+        def rec(**kw):
+            it[0] += 1
+            gdn.gdn_decode_step(q, k, v, states[it[0] % len(states)], out, **gates, **kw)
+        plan_norm = "fused"
+        fl = None
+    else:
+        cu = inp.cu_seqlens.to(dev)
+        cu_host = inp.cu_seqlens.tolist()
+        s0 = None if inp.initial_state is None else inp.initial_state.to(dev)
+        fin = torch.empty(n, shape.h_v, shape.d_k, shape.d_v, dtype=torch.float32, device=dev)
+        ws_bytes = gdn.prefill_workspace_size(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, n, T)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        plan_norm = gdn.prefill_query_plan(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, n, T,
+                                           raw_gates=raw, workspace_bytes=ws_bytes, norm=True)
+        fl = flush
+
+        def rec(**kw):
+            gdn.gdn_prefill(q, k, v, cu, out=out, final_state=fin, initial_state=s0, cu_seqlens_host=cu_host,
+                            **gates, **({"workspace": ws} if ws is not None else {}), **kw)
+    nbytes = algorithmic_bytes(shape, inp)
+    o_bytes = out.numel() * es
+    fused_bytes = nbytes + o_bytes + scale.numel() * es          # + gate read (y replaces o)
+    pair_bytes = nbytes + 3 * o_bytes + scale.numel() * es        # + o read, gate read, y write
+    if plan_norm != "fused" and plan_norm.get("norm") != "fused":
+        fused_bytes = pair_bytes  # the plan runs the norm as its own pass: the pair's traffic
+    ms_f, med_f, _ = _timed(lambda: rec(norm_gate=gate, norm_scale=scale), steps, warmup, fl)
+    o2 = out.view(T, -1)
+
+    def pair():
+        rec()
+        gdn.gdn_gated_rmsnorm(o2, gate.view(T, -1), scale, y=o2)
+    ms_p, med_p, _ = _timed(pair, steps, warmup, fl)
+    return {"tokens": T, "fused": {"ms": round(ms_f, 6), "ms_median": round(med_f, 6), "plan": plan_norm,
+                      "algorithmic_bytes": fused_bytes,
+                      "hbm_frac": round(fused_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "unfused_pair": {"ms": round(ms_p, 6), "ms_median": round(med_p, 6), "algorithmic_bytes": pair_bytes,
+                             "hbm_frac": round(pair_bytes / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "saved_ms": round(ms_p - ms_f, 6), "saved_bytes": pair_bytes - fused_bytes}
+
+
 def bench_copy(mib, steps, warmup):
     """A plain device copy of known size (dst.copy_(src), mib MiB each way): the
     reference kernel that scales the rocprofv3 HBM byte counters."""
@@ -510,7 +591,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="all",
-                    choices=["all"] + sorted(synth.BY_NAME) + sorted(synth.CONV_BY_NAME) + sorted(synth.NORM_BY_NAME))
+                    choices=["all", "output_norm"] + sorted(synth.BY_NAME) + sorted(synth.CONV_BY_NAME) +
+                    sorted(synth.NORM_BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algorithm", default="auto", choices=["auto", "serial", "chunked"],
                     help="prefill formulation (prefill workloads only)")
@@ -538,6 +620,14 @@ def main():
             line = bench_conv(synth.CONV_BY_NAME[args.workload], steps, warmup, want_cpu)
         else:
             line = bench_norm(synth.NORM_BY_NAME[args.workload], steps, warmup, want_cpu)
+    elif args.workload == "output_norm":
+        steps = args.steps if args.steps is not None else 10
+        warmup = args.warmup if args.warmup is not None else 3
+        flush = torch.zeros(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        res = {name: bench_output_norm(name, steps, warmup, flush) for name in NORM_SHAPES}
+        e = res["packed_16x2048"]
+        line = {"metric": METRIC, "value": round(e["tokens"] / (e["fused"]["ms"] * 1e-3), 1),
+                "unit": "tokens/s", "ms_per_step": e["fused"]["ms"], "output_norm": res}
     elif args.workload in ("all", "decode_b64"):
         steps = args.steps if args.steps is not None else 1000
         warmup = args.warmup if args.warmup is not None else 50
@@ -552,6 +642,13 @@ def main():
                                   flush=flush)
                 line["workloads"][name] = e
                 print(f"{name}: {e['ms']} ms ({e['plan']['form']}), HBM {100 * e['hbm_frac']:.1f} %",
+                      file=sys.stderr, flush=True)
+            # the block's output norm: fused epilogue against the unfused pair
+            line["output_norm"] = {}
+            for name in NORM_SHAPES:
+                e = bench_output_norm(name, psteps if name != "decode_b64" else min(steps, 200), pwarm, flush)
+                line["output_norm"][name] = e
+                print(f"{name} + norm: fused {e['fused']['ms']} ms, pair {e['unfused_pair']['ms']} ms",
                       file=sys.stderr, flush=True)
     else:
         shape = synth.BY_NAME[args.workload]

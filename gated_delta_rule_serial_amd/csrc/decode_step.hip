@@ -38,8 +38,11 @@ constexpr int kColsPerThread = 4;
 
 // BC: state columns per workgroup (64 or 128).  FULL: d_k == DK and d_v a
 // multiple of BC, so every thread's tile lies inside the state and the
-// accesses need no masks.
-template <typename IO, int DK, int BC, bool PERKEY, bool FULL>
+// accesses need no masks.  NORM: the workgroup owns the whole output row
+// (d_v <= BC) and writes the gated RMSNorm of o instead of o: each wave sums
+// o^2 over its 64 columns with DPP, the partials meet in LDS at the barrier
+// that publishes delta, and the first BC threads store y.
+template <typename IO, int DK, int BC, bool PERKEY, bool FULL, bool NORM>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   constexpr int kColThreads = BC / kColsPerThread;
   constexpr int kRowGroups = kThreads / kColThreads;
@@ -50,6 +53,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ float red_c[kWaves][kBlockCols];
   __shared__ float red_kq[kWaves];
   __shared__ float sh_delta[kBlockCols];
+  __shared__ float red_ss[kBlockCols / 64];
 
   const int tid = static_cast<int>(threadIdx.x);
   const int tc = tid % kColThreads;
@@ -103,6 +107,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   } else {
     rk.load_masked(kq_base_k, d_k - row0);
     rq.load_masked(kq_base_q, d_k - row0);
+  }
+
+  // ---- the norm's gate and scale of this thread's output column (the first
+  //      BC threads), issued early: they are read after the last barrier
+  float n_gate = 0.0f, n_scale = 0.0f;
+  if constexpr (NORM) {
+    if (tid < kBlockCols && (FULL || tid < d_v)) {
+      n_gate = widen(static_cast<const IO*>(p.norm.gate)[(static_cast<size_t>(b) * p.h_v + h) * d_v + tid]);
+      n_scale = widen(static_cast<const IO*>(p.norm.scale)[tid]);
+    }
   }
 
   // ---- gates: beta per (b, h) (or per b); the decay per (b, h) or, per key
@@ -195,7 +209,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // ---- the first BC threads finish the column sums, write o, publish delta
+  // ---- the first BC threads finish the column sums, write o (or keep it for
+  //      the norm), publish delta
+  float o_keep = 0.0f;
   if (tid < kBlockCols) {
     float a = 0.0f, cs = 0.0f, kq = 0.0f;
 #pragma unroll
@@ -209,12 +225,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     if (FULL || j < d_v) vv = widen(static_cast<const IO*>(p.v)[(static_cast<size_t>(b) * p.h_v + h) * d_v + j]);
     const float delta = deltas ? beta * (vv - a) : vv;
     sh_delta[tid] = delta;
-    if (FULL || j < d_v) {
+    if constexpr (NORM) {
+      // whole waves take this branch (BC is a multiple of 64): the DPP sum sees every lane
+      o_keep = (FULL || j < d_v) ? p.scale * fmaf(delta, kq, cs) : 0.0f;
+      const float sq = group_sum<64>(o_keep * o_keep);
+      if ((tid & 63) == 0) red_ss[tid >> 6] = sq;
+    } else if (FULL || j < d_v) {
       const float o = p.scale * fmaf(delta, kq, cs);
       narrow_store(static_cast<IO*>(p.out) + (static_cast<size_t>(b) * p.h_v + h) * d_v + j, o);
     }
   }
   __syncthreads();
+  if constexpr (NORM) {
+    if (tid < kBlockCols && (FULL || tid < d_v)) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kBlockCols / 64; ++w) ss += red_ss[w];
+      const float inv = __builtin_amdgcn_rsqf(fmaf(ss, p.norm.inv_n, p.norm.eps));
+      narrow_store(static_cast<IO*>(p.out) + (static_cast<size_t>(b) * p.h_v + h) * d_v + tid,
+                   gated_norm(o_keep, inv, n_scale, n_gate, p.norm.silu));
+    }
+  }
 
   // ---- S' = alpha S + k delta^T, written back in place
   float dl[kColsPerThread];
@@ -239,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <typename IO, int DK, int BC, bool PERKEY, bool FULL>
+template <typename IO, int DK, int BC, bool PERKEY, bool FULL, bool NORM>
 hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
   // grid: (column block, value head, sequence); the sequence axis is split
   // into launches of at most 65535
@@ -247,7 +278,7 @@ hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
   for (int off = 0; off < p.batch; off += kMaxZ) {
     p.b_offset = off;
     const unsigned nz = static_cast<unsigned>(p.batch - off < kMaxZ ? p.batch - off : kMaxZ);
-    hipLaunchKernelGGL((decode_kernel<IO, DK, BC, PERKEY, FULL>),
+    hipLaunchKernelGGL((decode_kernel<IO, DK, BC, PERKEY, FULL, NORM>),
                        dim3(static_cast<unsigned>(p.col_blocks), static_cast<unsigned>(p.h_v), nz),
                        dim3(kThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
@@ -256,14 +287,23 @@ hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
   return hipSuccess;
 }
 
-template <typename IO, int DK, int BC>
-hipError_t launch_bc(const DecodeParams& p, hipStream_t stream) {
+template <typename IO, int DK, int BC, bool NORM>
+hipError_t launch_norm(const DecodeParams& p, hipStream_t stream) {
   const bool full = p.d_k == DK && p.d_v % BC == 0;
   if constexpr (BC == 64) {
     if (p.gates.per_key && p.gates.decays)
-      return full ? launch_grid<IO, DK, BC, true, true>(p, stream) : launch_grid<IO, DK, BC, true, false>(p, stream);
+      return full ? launch_grid<IO, DK, BC, true, true, NORM>(p, stream)
+                  : launch_grid<IO, DK, BC, true, false, NORM>(p, stream);
   }
-  return full ? launch_grid<IO, DK, BC, false, true>(p, stream) : launch_grid<IO, DK, BC, false, false>(p, stream);
+  return full ? launch_grid<IO, DK, BC, false, true, NORM>(p, stream)
+              : launch_grid<IO, DK, BC, false, false, NORM>(p, stream);
+}
+
+template <typename IO, int DK, int BC>
+hipError_t launch_bc(const DecodeParams& p, hipStream_t stream) {
+  // the fused norm needs one column block per row (the API checks it)
+  return p.norm.gate != nullptr && p.col_blocks == 1 ? launch_norm<IO, DK, BC, true>(p, stream)
+                                                     : launch_norm<IO, DK, BC, false>(p, stream);
 }
 
 template <typename IO, int DK>
@@ -293,6 +333,8 @@ hipError_t launch_io(const DecodeParams& p, hipStream_t stream) {
 int decode_columns_per_block(int d_k, int d_v, bool per_key) {
   return (d_k <= 128 && d_v > 64 && !per_key) ? 128 : 64;
 }
+
+bool decode_fuses_norm(int d_k, int d_v, bool per_key) { return d_v <= decode_columns_per_block(d_k, d_v, per_key); }
 
 hipError_t launch_decode_step(DecodeParams p, int io_dtype, hipStream_t stream) {
   if (io_dtype == 1) return launch_io<bf16_t>(p, stream);

@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <vector>
 
 #include "gdn_launch.hpp"
@@ -99,6 +100,45 @@ gdn_status check_problem(const gdn_problem* p, const char* fn, bool has_tokens) 
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a per-key-dim decay tensor must be 16-byte aligned", fn);
   if (p->algorithm != GDN_ALGO_AUTO && p->algorithm != GDN_ALGO_SERIAL && p->algorithm != GDN_ALGO_CHUNKED)
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: unknown algorithm %d", fn, p->algorithm);
+  if (p->norm_gate != nullptr) {
+    if (!p->norm_scale) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: the output norm needs norm_scale", fn);
+    if (!aligned16(p->norm_gate) || !aligned16(p->norm_scale))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: norm_gate and norm_scale must be 16-byte aligned", fn);
+    if (!(p->norm_eps >= 0.0f) || !std::isfinite(p->norm_eps))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: norm_eps must be finite and >= 0", fn);
+    if (p->norm_activation != GDN_ACT_SILU && p->norm_activation != GDN_ACT_SIGMOID)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: norm_activation %d is not GDN_ACT_SILU or GDN_ACT_SIGMOID", fn,
+                  p->norm_activation);
+    if (!gdn::gated_rmsnorm_supported(p->io_dtype, p->d_v))
+      return fail(GDN_ERR_UNSUPPORTED, "%s: the output norm does not serve d_v=%d", fn, p->d_v);
+  }
+  return GDN_OK;
+}
+
+gdn::NormEpilogue norm_epilogue(const gdn_problem* p) {
+  gdn::NormEpilogue n{};
+  n.gate = p->norm_gate;
+  n.scale = p->norm_scale;
+  n.eps = p->norm_eps;
+  n.inv_n = 1.0f / static_cast<float>(p->d_v);
+  n.silu = p->norm_activation == GDN_ACT_SILU ? 1 : 0;
+  return n;
+}
+
+// The output norm as its own pass over out, in place: rows x h_v groups of d_v.
+gdn_status norm_pass(const gdn_problem* p, int64_t rows, void* out, const char* fn, hipStream_t stream) {
+  if (rows == 0 || out == nullptr) return GDN_OK;
+  gdn::NormParams np{};
+  np.x = out;
+  np.gate = p->norm_gate;
+  np.scale = p->norm_scale;
+  np.y = out;
+  np.groups = rows * p->h_v;
+  np.group = p->d_v;
+  np.eps = p->norm_eps;
+  np.activation = p->norm_activation;
+  const hipError_t e = gdn::launch_gated_rmsnorm(np, p->io_dtype, stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: norm launch failed: %s", fn, hipGetErrorString(e));
   return GDN_OK;
 }
 
@@ -155,6 +195,7 @@ gdn_status check_slots(const SlotArgs& sl, int32_t n, const char* fn) {
 struct Plan {
   int form = GDN_FORM_SERIAL;
   int cols = 1;
+  int norm = 0;  // 0 none, 1 fused into the output store, 2 a separate in-place pass
 };
 
 gdn::ScanParams plan_params(const gdn_problem& p, int32_t num_seqs, int32_t total_tokens) {
@@ -196,14 +237,21 @@ gdn_status plan_prefill(const gdn_problem& p, int32_t num_seqs, int32_t total_to
   const bool split = chunked && !wide && gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) &&
                      p.workspace != nullptr &&
                      p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  const bool norm = p.norm_gate != nullptr;
+  plan->norm = norm ? 2 : 0;
   if (wide) {
     plan->form = GDN_FORM_CHUNKED_F32;
     plan->cols = 16;
   } else if (split) {
     plan->form = GDN_FORM_CHUNKED_TWO_PASS;
-    plan->cols = gdn::split_takes_rows_kernel(p.d_k, p.d_v, num_seqs * p.h_v)
-                     ? 16
-                     : gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v);
+    if (norm && gdn::split_fuses_norm(p.d_v, num_seqs * p.h_v)) {
+      plan->cols = 128;
+      plan->norm = 1;
+    } else {
+      plan->cols = gdn::split_takes_rows_kernel(p.d_k, p.d_v, num_seqs * p.h_v)
+                       ? 16
+                       : gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v);
+    }
   } else if (chunked) {
     plan->form = GDN_FORM_CHUNKED_ONE_PASS;
     plan->cols = gdn::chunked_columns_per_block(p.d_k, p.d_v);
@@ -268,6 +316,8 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
   if (overlaps(out, out_bytes, q, qk_bytes) || overlaps(out, out_bytes, k, qk_bytes) ||
       overlaps(out, out_bytes, v, v_bytes) || overlaps(out, out_bytes, final_state, state_bytes))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: out overlaps an input or the final state", fn);
+  if (overlaps(p.norm_gate, out_bytes, out, out_bytes) || overlaps(p.norm_scale, p.d_v * es, out, out_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: out overlaps norm_gate or norm_scale", fn);
   const int32_t window = problem->state_window;
   const size_t hist_bytes = static_cast<size_t>(num_seqs) * window * p.h_v * p.d_k * p.d_v * sizeof(float);
   if (window > 0 && (overlaps(problem->state_history, hist_bytes, out, out_bytes) ||
@@ -309,11 +359,16 @@ gdn_status prefill_impl(const char* fn, const gdn_problem* problem, int32_t num_
                 static_cast<unsigned long long>(blocks));
   const bool wide = plan.form == GDN_FORM_CHUNKED_F32, split = plan.form == GDN_FORM_CHUNKED_TWO_PASS,
              chunked = plan.form == GDN_FORM_CHUNKED_ONE_PASS;
+  if (plan.norm == 1) sp.norm = norm_epilogue(problem);
   const hipError_t e = wide      ? gdn::launch_prefill_wide(sp, p.workspace, stream)
                        : split   ? gdn::launch_prefill_split(sp, p.workspace, stream)
                        : chunked ? gdn::launch_prefill_chunked(sp, io_bf16, stream)
                                  : gdn::launch_prefill_scan(sp, p.io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  if (plan.norm == 2) {
+    st = norm_pass(problem, total_tokens, out, fn, stream);
+    if (st != GDN_OK) return st;
+  }
   return ok();
 }
 
@@ -389,13 +444,23 @@ gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch
   dp.d_k = p.d_k;
   dp.d_v = p.d_v;
   dp.ratio = p.h_v / p.h_qk;
-  const int cpb = gdn::decode_columns_per_block(p.d_k, p.d_v, dp.gates.per_key && dp.gates.decays);
+  const bool per_key = dp.gates.per_key && dp.gates.decays;
+  const int cpb = gdn::decode_columns_per_block(p.d_k, p.d_v, per_key);
   dp.col_blocks = (p.d_v + cpb - 1) / cpb;
   dp.scale = resolved_scale(problem);
   if (p.h_v > 65535)
     return fail(GDN_ERR_UNSUPPORTED, "%s: h_v = %d exceeds the grid's head axis (65535)", fn, p.h_v);
+  if (overlaps(p.norm_gate, out_bytes, out, out_bytes) || overlaps(p.norm_scale, p.d_v * es, out, out_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: out overlaps norm_gate or norm_scale", fn);
+  const bool norm = p.norm_gate != nullptr;
+  const bool fused = norm && gdn::decode_fuses_norm(p.d_k, p.d_v, per_key);
+  if (fused) dp.norm = norm_epilogue(problem);
   const hipError_t e = gdn::launch_decode_step(dp, p.io_dtype, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  if (norm && !fused) {
+    st = norm_pass(problem, batch, out, fn, stream);
+    if (st != GDN_OK) return st;
+  }
   return ok();
 }
 
@@ -479,6 +544,7 @@ GDN_EXPORT gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t
   if (st != GDN_OK) return st;
   plan->form = pl.form;
   plan->columns_per_block = pl.cols;
+  plan->norm = pl.norm;
   const int units = num_seqs * p.h_v;
   const int units8 = (units + 7) / 8 * 8;
   char* k = plan->kernels;
@@ -497,7 +563,10 @@ GDN_EXPORT gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t
       std::snprintf(k, kn, "chunk_kernel");
       break;
     case GDN_FORM_CHUNKED_TWO_PASS:
-      if (gdn::split_takes_rows_kernel(p.d_k, p.d_v, units)) {
+      if (pl.norm == 1) {
+        plan->state_workgroups = units8;
+        std::snprintf(k, kn, "chunk_table_kernel + chunk_prep_kernel + chunk_state_kernel (gated RMSNorm fused)");
+      } else if (gdn::split_takes_rows_kernel(p.d_k, p.d_v, units)) {
         plan->state_workgroups = units8 * ((p.d_v + 15) / 16);
         std::snprintf(k, kn, "chunk_table_kernel + chunk_prep_kernel + chunk_rows_kernel");
       } else {
@@ -511,6 +580,10 @@ GDN_EXPORT gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t
       break;
     default:
       break;
+  }
+  if (pl.norm == 2) {
+    const size_t len = std::strlen(k);
+    std::snprintf(k + len, kn - len, " + rmsnorm_kernel");
   }
   return ok();
 }

@@ -368,6 +368,15 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
+// One element of the gated RMSNorm ([P1] `gated_rms_norm_op`): x times the
+// row's 1 / sqrt(mean(x^2) + eps), the per-element scale and the gate's
+// activation (silu: g sigmoid(g); else sigmoid(g)), with the epilogues'
+// hardware sigmoid.
+__device__ __forceinline__ float gated_norm(float x, float inv, float scale, float g, int silu) {
+  const float s = fast_sigmoid(g);
+  return x * inv * scale * (silu ? g * s : s);
+}
+
 // softplus(x) = max(x, 0) + log1p(exp(-|x|)), overflow-free.
 __device__ __forceinline__ float gate_softplus(float x) {
   return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));

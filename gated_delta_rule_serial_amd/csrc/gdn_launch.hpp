@@ -22,6 +22,16 @@ struct GateArgs {
   const float* dt_bias; // [h_v]
 };
 
+// Gated RMSNorm of the output rows (one group of d_v per (token, value head)),
+// applied where the kernel that forms o owns whole rows.
+struct NormEpilogue {
+  const void* gate;       // [tokens, h_v, d_v] io dtype; null: no norm
+  const void* scale;      // [d_v] io dtype
+  float eps;
+  float inv_n;            // 1 / d_v
+  int32_t silu;           // 1: gate * sigmoid(gate); 0: sigmoid(gate)
+};
+
 // Serial scan over packed sequences.
 struct ScanParams {
   const void* q;          // [T, h_qk, d_k]
@@ -45,6 +55,7 @@ struct ScanParams {
   float scale;
   int32_t window;         // > 0: history of the last `window` states per sequence
   float* history;         // [N, window, h_v, d_k, d_v]
+  NormEpilogue norm;      // the two-pass chunked form applies it when norm.gate != null
 };
 
 // One decode token per sequence, state updated in place.
@@ -63,6 +74,7 @@ struct DecodeParams {
   int32_t ratio;
   int32_t col_blocks;
   float scale;
+  NormEpilogue norm;      // applied when norm.gate != null (then col_blocks == 1)
 };
 
 struct GatePrologueParams {
@@ -134,6 +146,10 @@ hipError_t launch_prefill_chunked(ScanParams p, int io_bf16, hipStream_t stream)
 // sequential state pass) through a caller-provided workspace.
 bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window);
 int split_columns_per_block(int d_v, int units);
+// Whether the bf16 two-pass state pass applies a gated RMSNorm in its output
+// store (128-column blocks own whole rows of up to 128 columns; taken where
+// the column rule picks 128-column blocks anyway).
+bool split_fuses_norm(int d_v, int units);
 size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v);
 hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t stream);
 // The chunk table at the head of a two-pass workspace: cs [N + 1] int32 (the
@@ -180,5 +196,8 @@ hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
 hipError_t static_workspace(void** ptr, size_t* bytes);
 // Columns one decode workgroup owns.
 int decode_columns_per_block(int d_k, int d_v, bool per_key);
+// Whether the decode kernel applies a gated RMSNorm in its output store (its
+// workgroup owns whole rows: d_v at most the columns per block).
+bool decode_fuses_norm(int d_k, int d_v, bool per_key);
 
 }  // namespace gdn

@@ -502,9 +502,16 @@ constexpr int kStateWaves = 4;
 // the contraction index.  The fragments of chunk j + 1 travel straight from
 // the workspace into the second LDS buffer (global-to-LDS loads, no
 // registers) while chunk j computes, so a chunk costs one barrier.
-template <typename IO, int DK, int SL, int DVT>
+// NORM (128-column blocks, d_v <= 128): the workgroup owns whole output rows
+// and stores the gated RMSNorm of O instead of O.  Each wave sums the squares
+// of its scaled Y per token with DPP over the 16 lanes of a row and writes
+// them to a per-chunk LDS slot (double-buffered by chunk parity); after the
+// chunk's barrier the row stores of the next chunk add the four waves'
+// partials and apply the norm, with the gate rows loaded a chunk ahead.
+template <typename IO, int DK, int SL, int DVT, bool NORM>
 __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_state_kernel(
     ScanParams p, const unsigned char* ws, size_t rec_bytes, const int32_t* cs) {
+  static_assert(!NORM || SL == 2, "the fused norm needs 128-column blocks");
   constexpr int KB = DK / 32;   // key blocks of 32
   constexpr int RT = DK / 16;   // state row tiles
   constexpr int NC = kStateWaves * 16 * SL;
@@ -519,7 +526,9 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
   __shared__ __align__(16) f32x4 u_blk[kStateWaves * kUT * 64];   // each wave's U tiles of the current chunk
   __shared__ __align__(16) float gl_blk[kStateWaves * 64];        // each wave's copy of gam_last
   __shared__ __align__(16) bf16_t out_blk[kStateWaves * kC * kSO];  // each wave's output block
-  static_assert(sizeof(frag0) + sizeof(frag1) + sizeof(u_blk) + sizeof(gl_blk) + sizeof(out_blk) <= 160 * 1024,
+  __shared__ float ss_blk[NORM ? 2 * kStateWaves * kC : 1];          // [chunk parity][wave][token] sums of squares
+  static_assert(sizeof(frag0) + sizeof(frag1) + sizeof(u_blk) + sizeof(gl_blk) + sizeof(out_blk) + sizeof(ss_blk) <=
+                    160 * 1024,
                 "LDS budget of one gfx950 workgroup");
 
   const int tid = static_cast<int>(threadIdx.x);
@@ -599,6 +608,24 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
   auto out_at = [](int t, int c) __attribute__((always_inline)) {
     return t * kSO + ((((c >> 3) ^ (t >> 2)) & (2 * SL - 1)) << 3) + (c & 7);
   };
+  // the fused norm: this lane's 8-column piece of every row it stores is
+  // columns Jw + 8 (lane % 4) .. +7; their scale once, and the gate rows of
+  // the chunk in flight (loaded a chunk ahead, clamped into the sequence)
+  const int nc8 = 8 * (lane & 3);
+  const int ncol = Jw + nc8 < d_v ? Jw + nc8 : 0;
+  RawSlice<IO, 8> n_scale;
+  RawSlice<IO, 8> n_gate[4];
+  if constexpr (NORM) n_scale.load(static_cast<const IO*>(p.norm.scale) + ncol);
+  auto load_gate = [&](int j) __attribute__((always_inline)) {
+    if constexpr (NORM) {
+      const IO* gp = static_cast<const IO*>(p.norm.gate);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int t = min(t_begin + j * kC + (lane >> 2) + 16 * it, t_end - 1);
+        n_gate[it].load(gp + static_cast<size_t>(t) * v_stride + static_cast<size_t>(h) * d_v + ncol);
+      }
+    }
+  };
   // the output block of chunk j (its scaled Y, kept in registers until no
   // global-to-LDS load is in flight) through the wave's LDS block, in 16-byte rows
   f32x4 Yp[4][SL];
@@ -618,9 +645,32 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
     for (int it = 0; it < kC * VPRO / 64; ++it) {
       const int v = lane + 64 * it;
       const int t = v / VPRO, c8 = (v % VPRO) * 8;
-      if (t < Lc && Jw + c8 < d_v)
-        *reinterpret_cast<uint4*>(og + static_cast<size_t>(c0 + t) * v_stride + static_cast<size_t>(h) * d_v + Jw + c8) =
-            *reinterpret_cast<const uint4*>(Os + out_at(t, c8));
+      if constexpr (NORM) {
+        // y = o / sqrt(mean(o^2) + eps) scale act(gate) over the four waves' columns
+        const float* ssj = ss_blk + (j & 1) * kStateWaves * kC;
+        float ss = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kStateWaves; ++ww) ss += ssj[ww * kC + t];
+        const float inv = __builtin_amdgcn_rsqf(fmaf(ss, p.norm.inv_n, p.norm.eps));
+        RawSlice<IO, 8> ro;
+        const uint4 ow = *reinterpret_cast<const uint4*>(Os + out_at(t, c8));
+        ro.w[0] = ow.x;
+        ro.w[1] = ow.y;
+        ro.w[2] = ow.z;
+        ro.w[3] = ow.w;
+        float o8[8], g8[8], s8[8], y8[8];
+        ro.widen_to(o8);
+        n_gate[it].widen_to(g8);
+        n_scale.widen_to(s8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y8[e] = gated_norm(o8[e], inv, s8[e], g8[e], p.norm.silu);
+        if (t < Lc && Jw + c8 < d_v)
+          store_slice<IO, 8>(og + static_cast<size_t>(c0 + t) * v_stride + static_cast<size_t>(h) * d_v + Jw + c8, y8);
+      } else {
+        if (t < Lc && Jw + c8 < d_v)
+          *reinterpret_cast<uint4*>(og + static_cast<size_t>(c0 + t) * v_stride + static_cast<size_t>(h) * d_v + Jw + c8) =
+              *reinterpret_cast<const uint4*>(Os + out_at(t, c8));
+      }
     }
   };
   auto pack = [](f32x4 a, f32x4 b) __attribute__((always_inline)) {
@@ -644,6 +694,7 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
     // would stall the wave on the memory pipeline while its MFMAs wait)
     const bool more = j + 1 < nchunks;
     if (og != nullptr && j > 0) store_out(j - 1);
+    if (og != nullptr) load_gate(j);
 
     const bf16x8* fb = cur + lane;
     bf16x8 ring[P];
@@ -703,6 +754,21 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int sl = 0; sl < SL; ++sl) Yp[tt][sl] = p.scale * Y[tt][sl];
+    if constexpr (NORM) {
+      // per-token sums of squares over this wave's columns: lane l holds rows
+      // 4 (l / 16) + i of column l % 16 in each tile; the 16 lanes of a row group add up
+      float* ssw = ss_blk + ((j & 1) * kStateWaves + w) * kC;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float q = 0.0f;
+#pragma unroll
+          for (int sl = 0; sl < SL; ++sl) q = fmaf(Yp[tt][sl][i], Yp[tt][sl][i], q);
+          q = group_sum<16>(q);
+          if ((lane & 15) == 0) ssw[16 * tt + acc_row(lane, i)] = q;
+        }
+    }
     // the wave's U and gam_last blocks are free again (their reads have
     // returned): the next chunk's go in during the state update
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -1001,17 +1067,19 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
   const unsigned blocks = static_cast<unsigned>((units + 7) / 8) * 8u * static_cast<unsigned>(p.col_blocks);
   if (units == 0) return hipSuccess;
   if constexpr (DK == 128) {
-    if (split_rows(p.d_k, p.d_v, units)) {
+    if (split_rows(p.d_k, p.d_v, units) && !(p.norm.gate != nullptr && split_fuses_norm(p.d_v, units))) {
       const int units8 = (units + 7) / 8 * 8;
       const unsigned rblocks = static_cast<unsigned>(units8) * static_cast<unsigned>((p.d_v + 15) / 16);
       hipLaunchKernelGGL((chunk_rows_kernel<DVT>), dim3(rblocks), dim3(64 * kRowWaves), 0, stream, p, ws, rec_bytes, cs, units8);
       return hipGetLastError();
     }
   }
-  if (split_columns(p.d_v, units) == 128)
-    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, DVT>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
+  if (p.norm.gate != nullptr && split_fuses_norm(p.d_v, units))
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, DVT, true>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
+  else if (split_columns(p.d_v, units) == 128)
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, DVT, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
   else
-    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 1, DVT>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 1, DVT, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
   return hipGetLastError();
 }
 
@@ -1028,6 +1096,14 @@ bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int w
 int split_columns_per_block(int d_v, int units) { return split_columns(d_v, units); }
 
 bool split_takes_rows_kernel(int d_k, int d_v, int units) { return split_rows(d_k, d_v, units); }
+
+// The fused norm needs 128-column blocks; it is taken where the column rule
+// picks them anyway.  There it beats the separate norm pass (16 x 2048 tokens:
+// 1.093 against 1.125 ms; 32 x 1024: 1.083 against 1.094 ms); where 64-column
+// blocks or the row-split pass would run, forcing 128-column blocks costs more
+// than the pass saves (8 packed sequences: 1.26 against 1.18 ms; one
+// 4096-token sequence: 0.41 against 0.20 ms).
+bool split_fuses_norm(int d_v, int units) { return d_v <= 128 && split_columns(d_v, units) == 128; }
 
 // Workspace: cs [N + 1] int32, info [chunk bound] int2, then the records.
 static size_t table_bytes(int num_seqs, int total_tokens) {

@@ -48,13 +48,15 @@ class gdn_problem(ctypes.Structure):
         ("state_history", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_uint64),
+        ("norm_gate", ctypes.c_void_p), ("norm_scale", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float), ("norm_activation", ctypes.c_int32),
     ]
 
 
 class gdn_prefill_plan(ctypes.Structure):
     _fields_ = [
         ("form", ctypes.c_int32), ("columns_per_block", ctypes.c_int32),
-        ("state_workgroups", ctypes.c_int32), ("kernels", ctypes.c_char * 188),
+        ("state_workgroups", ctypes.c_int32), ("norm", ctypes.c_int32), ("kernels", ctypes.c_char * 184),
     ]
 
 
@@ -171,11 +173,15 @@ def make_problem(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype,
                  g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None,
                  algorithm: str = "auto", rule: str = "gated_delta", decay_per_key: bool = False,
                  beta_shared: bool = False, state_history: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> gdn_problem:
+                 workspace: Optional[torch.Tensor] = None, norm_gate: Optional[torch.Tensor] = None,
+                 norm_scale: Optional[torch.Tensor] = None, norm_eps: float = 1e-5,
+                 norm_activation: str = "silu") -> gdn_problem:
     """Fill the ``gdn_problem`` struct.  Raw gates are used when ``a`` (or, for
     rules without decay, ``b``) is given.  ``state_history`` [N, W, h_v, d_k, d_v]
     sets the state window W; ``workspace`` (a device tensor of at least
-    prefill_workspace_size bytes) enables the two-pass chunked prefill."""
+    prefill_workspace_size bytes) enables the two-pass chunked prefill;
+    ``norm_gate`` [tokens, h_v, d_v] and ``norm_scale`` [d_v] ask for the gated
+    RMSNorm of the output (per value head)."""
     if io_dtype not in _DTYPES:
         raise ValueError(f"io dtype {io_dtype} is not supported")
     raw = a is not None or (g is None and b is not None)
@@ -185,7 +191,8 @@ def make_problem(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype,
                        _ptr(g), _ptr(beta), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
                        ALGORITHMS[algorithm], RULES[rule], int(decay_per_key), int(beta_shared),
                        window, _ptr(state_history), _ptr(workspace),
-                       0 if workspace is None else workspace.numel() * workspace.element_size())
+                       0 if workspace is None else workspace.numel() * workspace.element_size(),
+                       _ptr(norm_gate), _ptr(norm_scale), float(norm_eps), ACTIVATIONS[norm_activation])
 
 
 def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
@@ -258,20 +265,23 @@ def prefill_workspace_size(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: to
 
 def prefill_query_plan(h_qk: int, h_v: int, d_k: int, d_v: int, io_dtype: torch.dtype, num_seqs: int,
                        total_tokens: int, *, algorithm: str = "auto", raw_gates: bool = False,
-                       workspace_bytes: int = 0, **variant) -> dict:
+                       workspace_bytes: int = 0, norm: bool = False, **variant) -> dict:
     """gdn_prefill_query_plan of include/gdn.h: what gdn_prefill would launch.
     ``workspace_bytes`` stands for a workspace of that size (no memory is
     touched).  Returns {"form", "columns_per_block", "state_workgroups", "kernels"}."""
     prob = make_problem(h_qk, h_v, d_k, d_v, io_dtype, algorithm=algorithm, **variant)
     if raw_gates:
         prob.gate_mode = GDN_GATES_RAW
+    if norm:
+        prob.norm_gate = prob.norm_scale = ctypes.c_void_p(512)  # stand-ins: the query reads no memory
     if workspace_bytes:
         prob.workspace = ctypes.c_void_p(256)  # a non-null, aligned stand-in: the query reads no memory
         prob.workspace_bytes = int(workspace_bytes)
     plan = gdn_prefill_plan()
     _check(load().gdn_prefill_query_plan(ctypes.byref(prob), num_seqs, total_tokens, ctypes.byref(plan)))
     return {"form": FORMS.get(plan.form, str(plan.form)), "columns_per_block": plan.columns_per_block,
-            "state_workgroups": plan.state_workgroups, "kernels": plan.kernels.decode()}
+            "state_workgroups": plan.state_workgroups, "norm": {0: "none", 1: "fused", 2: "separate pass"}[plan.norm],
+            "kernels": plan.kernels.decode()}
 
 
 def _host_i32(vals):

@@ -275,3 +275,14 @@ def positive_log_decays(g: torch.Tensor, every: int, hi: float, *, seed: int) ->
     idx = torch.arange(0, flat.numel(), every)
     flat[idx] = hi * (1.0 - torch.rand(idx.numel(), generator=gen, dtype=torch.float32))
     return flat.reshape(g.shape).to(g.dtype)
+
+
+def output_norm_inputs(T: int, h_v: int, d_v: int, *, seed: int, io_dtype: torch.dtype):
+    """Gate [T, h_v, d_v] ~ N(0, 2^2) and scale [d_v] ~ N(1, 0.1^2) of the
+    recurrence's output norm (the gated RMSNorm workload's recipe), in float32
+    then cast to the I/O dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    gate = torch.randn(T, h_v, d_v, generator=gen, dtype=torch.float32) * 2.0
+    scale = 1.0 + 0.1 * torch.randn(d_v, generator=gen, dtype=torch.float32)
+    return gate.to(io_dtype), scale.to(io_dtype)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -110,6 +110,13 @@ typedef enum gdn_rule {
   GDN_RULE_LINEAR = 3
 } gdn_rule;
 
+/* Activation applied by the convolution and the norm. */
+typedef enum gdn_activation {
+  GDN_ACT_NONE = 0,    /* convolution only                        */
+  GDN_ACT_SILU = 1,    /* x * sigmoid(x)                          */
+  GDN_ACT_SIGMOID = 2  /* gated RMSNorm only: sigmoid(gate)       */
+} gdn_activation;
+
 /* Geometry and gate inputs of one call. */
 typedef struct gdn_problem {
   int32_t h_qk;     /* query/key heads, >= 1                                  */
@@ -153,6 +160,22 @@ typedef struct gdn_problem {
    * scratch, and calls that share it must not overlap in time. */
   void* workspace;
   uint64_t workspace_bytes;
+  /* Optional gated RMSNorm of the output ([P1] `gated_rms_norm_op`), one
+   * group per value head: with norm_gate non-NULL, out receives for every
+   * (token, value head) row of d_v elements
+   *     y = o / sqrt(mean(o^2) + norm_eps) * norm_scale * act(norm_gate)
+   * in place of the readout o.  Where a workgroup owns whole output rows and
+   * that pays (the decode step with d_v <= 128 at d_k <= 128, else d_v <= 64;
+   * the bfloat16 two-pass chunked prefill with d_v <= 128 when its state pass
+   * runs 128-column blocks, about 512 or more (sequence, value head) units)
+   * the norm is applied to the float32 readout in the kernel that computes
+   * it, and o never reaches memory; elsewhere out receives o and the norm then
+   * runs over it in place, as gdn_gated_rmsnorm would.
+   * gdn_prefill_query_plan reports which.                                   */
+  const void* norm_gate;     /* [tokens, h_v, d_v] io_dtype, or NULL: no norm  */
+  const void* norm_scale;    /* [d_v] io_dtype                                 */
+  float norm_eps;            /* >= 0                                           */
+  int32_t norm_activation;   /* GDN_ACT_SILU or GDN_ACT_SIGMOID                */
 } gdn_problem;
 
 /*
@@ -232,7 +255,9 @@ typedef struct gdn_prefill_plan {
   int32_t columns_per_block;  /* state columns one workgroup of the sequential
                                  kernel owns (serial form: one wave)           */
   int32_t state_workgroups;   /* workgroups of the sequential kernel's grid    */
-  char kernels[188];          /* the kernels launched, in order, joined by
+  int32_t norm;               /* 0: no norm; 1: fused into the output store;
+                                 2: a separate in-place pass over out          */
+  char kernels[184];          /* the kernels launched, in order, joined by
                                  " + ", NUL-terminated                         */
 } gdn_prefill_plan;
 
@@ -320,13 +345,6 @@ gdn_status gdn_gate_prologue(int32_t tokens, int32_t h_v, int32_t io_dtype,
  * The block's neighbouring operations: the causal depthwise convolution in
  * front of the recurrence and the gated RMSNorm after it.
  * ---------------------------------------------------------------------- */
-
-/* Activation applied by the convolution and the norm. */
-typedef enum gdn_activation {
-  GDN_ACT_NONE = 0,    /* convolution only                        */
-  GDN_ACT_SILU = 1,    /* x * sigmoid(x)                          */
-  GDN_ACT_SIGMOID = 2  /* gated RMSNorm only: sigmoid(gate)       */
-} gdn_activation;
 
 /* Largest convolution kernel (taps per channel). */
 #define GDN_MAX_CONV_KERNEL 64

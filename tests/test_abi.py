@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 8
+    assert gdn.abi_version() == 9
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -386,3 +386,24 @@ def test_conv_slots_validation(lib):
     st = lib.gdn_causal_conv_step_slots(ctypes.byref(prob), 2, vp(FAKE + 0x10000), vp(FAKE + 0x20000), 5,
                                         None, None, vp(FAKE + 0x40000), None)
     assert st == INVALID and "slots is NULL" in gdn.last_error()
+
+
+def test_output_norm_validation(lib):
+    """The gated RMSNorm epilogue's arguments are checked before anything runs."""
+    base = dict(io_dtype=gdn.GDN_BF16, d_k=128, d_v=128, h_qk=1, h_v=2, norm_gate=FAKE + 0x80000,
+                norm_scale=FAKE + 0x90000, norm_eps=1e-5, norm_activation=gdn.GDN_ACT_SILU)
+    for kw, needle in ((dict(norm_scale=None), "norm_scale"), (dict(norm_gate=FAKE + 0x80008), "16-byte"),
+                       (dict(norm_eps=-1.0), "norm_eps"), (dict(norm_activation=gdn.GDN_ACT_NONE), "norm_activation"),
+                       (dict(norm_eps=float("inf")), "norm_eps")):
+        st = _prefill(lib, _prob(**{**base, **kw}), n=1, cu_host=[0, 8], T=8)
+        assert st == INVALID and needle in gdn.last_error(), (kw, gdn.last_error())
+    # the gate may not overlap out (out at FAKE + 0x40000, 8 x 2 x 128 bf16)
+    st = _prefill(lib, _prob(**{**base, "norm_gate": FAKE + 0x40000}), n=1, cu_host=[0, 8], T=8)
+    assert st == INVALID and "norm_gate" in gdn.last_error()
+    p = gdn.prefill_query_plan(16, 32, 128, 256, torch.bfloat16, 8, 33173, workspace_bytes=1 << 40, norm=True)
+    assert p["norm"] == "separate pass" and p["kernels"].endswith("rmsnorm_kernel")
+    p = gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 8, 33173, workspace_bytes=1 << 40, norm=True)
+    assert p["norm"] == "separate pass" and p["columns_per_block"] == 64
+    # from 512 (sequence, head) units the state pass runs 128-column blocks anyway, and fuses the norm
+    p = gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 16, 32768, workspace_bytes=1 << 40, norm=True)
+    assert p["norm"] == "fused" and p["columns_per_block"] == 128
