@@ -86,3 +86,36 @@ def test_graph_prefill_two_pass(name, over):
                         cu_seqlens_host=inp.cu_seqlens.tolist(), algorithm="chunked", workspace=ws)
 
     _replay_and_compare(run, lambda: [out, fin], lambda: None, f"{name} two-pass prefill")
+
+
+def test_graph_static_workspace_and_output_norm():
+    """gdn_prefill_static_workspace (the entry point for callers that cannot
+    allocate, such as code under graph capture) with the output norm as its own
+    pass (one sequence), and gdn_prefill with the norm fused into the state pass
+    (16 x 32 units, a caller workspace: beyond the static array), captured and
+    replayed."""
+    for lens, static in (([300], True), ([70] * 16, False)):
+        shape = W["varlen_prefill_8seq"]
+        inp = synth.generate(shape, seqlens=lens, seed=5)
+        g, beta = gates_for(inp)
+        T = inp.total_tokens
+        gate, scale = synth.output_norm_inputs(T, shape.h_v, shape.d_v, seed=6, io_dtype=shape.io_dtype)
+        args = [to_dev(t) for t in (inp.q, inp.k, inp.v, inp.cu_seqlens, g, beta, gate, scale)]
+        s0 = to_dev(inp.initial_state)
+        fin = torch.empty_like(s0)
+        out = torch.empty(T, shape.h_v, shape.d_v, dtype=shape.io_dtype, device="cuda")
+        ws = None if static else workspace_for(inp)
+        plan = gdn.prefill_query_plan(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, len(lens), T,
+                                      workspace_bytes=1 << 40, norm=True)
+        assert plan["norm"] == ("separate pass" if static else "fused"), plan
+
+        def run():
+            q, k, v, cu, gg, bb, ng, ns = args
+            kw = dict(out=out, final_state=fin, initial_state=s0, g=gg, beta=bb, norm_gate=ng, norm_scale=ns,
+                      cu_seqlens_host=inp.cu_seqlens.tolist())
+            if static:
+                gdn.gdn_prefill_static_workspace(q, k, v, cu, **kw)
+            else:
+                gdn.gdn_prefill(q, k, v, cu, workspace=ws, **kw)
+        _replay_and_compare(run, lambda: [out, fin], lambda: None,
+                            f"{'static workspace' if static else 'caller workspace'} + output norm ({plan['norm']})")
