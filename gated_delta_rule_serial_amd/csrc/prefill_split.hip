@@ -130,7 +130,7 @@ template <int DK, int DVT>
 struct PrepLds {
   static constexpr int SK = DK + 8;
   static constexpr int DVP = 16 * DVT;
-  static constexpr int kKs = 0;                          // K rows  [C][SK] bf16 (later W)
+  static constexpr int kKs = 0;                          // K rows  [C][SK] bf16
   static constexpr int kQs = kKs + kC * SK * 2;          // Q rows  [C][SK] bf16
   static constexpr int kKT = kQs + kC * SK * 2;          // K^T     [DK][SC] bf16
   static constexpr int kVt = kKT + DK * kSC * 2;         // V^T     [DVP][SC] bf16
@@ -141,7 +141,8 @@ struct PrepLds {
   static constexpr int kGd = kXs + 4 * 16 * 20 * 4;      // G       [C] f64
   static constexpr int kGam = kGd + kC * 8;              // gam     [C] f32
   static constexpr int kBet = kGam + kC * 4;             // beta    [C] f32
-  static constexpr int kBytes = kBet + kC * 4;
+  static constexpr int kKf = kBet + kC * 4;              // exp(G_last - G) [C] f32
+  static constexpr int kBytes = kKf + kC * 4;
   static_assert(2 * kC * kSC * 2 <= kC * kSA * 4, "T' and T'' must fit in the A buffer");
   static_assert(kBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
@@ -158,7 +159,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   constexpr int DVP = L_::DVP;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* Ks = reinterpret_cast<bf16_t*>(smem + L_::kKs);
-  bf16_t* Ws = Ks;
   bf16_t* Qs = reinterpret_cast<bf16_t*>(smem + L_::kQs);
   bf16_t* KT = reinterpret_cast<bf16_t*>(smem + L_::kKT);
   bf16_t* Vt = reinterpret_cast<bf16_t*>(smem + L_::kVt);
@@ -171,16 +171,17 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   double* Gd = reinterpret_cast<double*>(smem + L_::kGd);
   float* Gam = reinterpret_cast<float*>(smem + L_::kGam);
   float* Bet = reinterpret_cast<float*>(smem + L_::kBet);
+  float* Kf = reinterpret_cast<float*>(smem + L_::kKf);
 
   const int T = p.total_tokens;
   const int total = cs[p.num_seqs] * p.h_v;  // live items; the grid covers a bound
   const int n_items = items < total ? items : total;
   const int d_v = p.d_v;
   const int tid = static_cast<int>(threadIdx.x);
-  const int w = tid >> 6;
+  // wave-uniform, and the compiler is told so: branches on w must skip
+  // their MFMAs, which run whatever the execution mask
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int rb = w & 3;
-  const int chalf = w >> 2;
   const Rec rec(DK, DVP);
   const IO* qg = static_cast<const IO*>(p.q);
   const IO* kg = static_cast<const IO*>(p.k);
@@ -312,52 +313,52 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       Gd[lane] = G;
       Gam[lane] = fast_exp2(static_cast<float>(G));
       Bet[lane] = b;
+      // the state-update factor exp(G_last - G_t); gates past the chunk's end
+      // are 0, so G_last is the prefix at the last lane
+      Kf[lane] = fast_exp2(static_cast<float>(__shfl(G, kC - 1) - G));
     }
     __syncthreads();
 
-  // the next item's inputs, in flight while this one computes: issued once
-  // the staging registers are free, so they drain during the products and
-  // the solve, ahead of this item's workspace stores
-  {
-    const int next = item + static_cast<int>(gridDim.x);
-    if (next < n_items) {
-      at = locate(next, next_info);
-      fetch(at);
-      next_info = info_of(next + static_cast<int>(gridDim.x));
-    }
-  }
-
-  // ================= 2. K^T; P = K K^T, R = Q K^T -> A (f32) and M (bf16)
-  for (int ix = tid; ix < DK * (kC / 8); ix += kThreads) {
-    const int i = ix % DK;
-    const int t8 = (ix / DK) * 8;
-    uint32_t wv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      wv[e] = static_cast<uint32_t>(Ks[(t8 + 2 * e) * SK + i]) | (static_cast<uint32_t>(Ks[(t8 + 2 * e + 1) * SK + i]) << 16);
-    *reinterpret_cast<uint4*>(KT + i * kSC + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-  }
-  for (int tj = w; tj < 10; tj += kWaves) {
-    int tb = 0;
-    while ((tb + 1) * (tb + 2) / 2 <= tj) ++tb;
-    const int cs_ = tj - tb * (tb + 1) / 2;
-    f32x4 pacc = {0.0f, 0.0f, 0.0f, 0.0f}, racc = {0.0f, 0.0f, 0.0f, 0.0f};
-    pacc = mma<DK>(pacc, Ks + 16 * tb * SK, SK, Ks + 16 * cs_ * SK, SK, lane);
-    racc = mma<DK>(racc, Qs + 16 * tb * SK, SK, Ks + 16 * cs_ * SK, SK, lane);
-    const int s_ = 16 * cs_ + acc_col(lane);
+  // ================= 2. A = strictly lower (beta_t exp(G_t - G_s) k_t.k_s), M = lower (exp(G_t - G_s) q_t.k_s),
+  // K^T, and the diagonal 16 x 16 blocks of T = (I + A)^-1.  Waves 0-3 form the
+  // diagonal tile of A in block w and invert that block at once; waves 4-7
+  // transpose K and form the six tiles of A below the diagonal blocks and the
+  // ten lower tiles of M, which only later phases read.
+  // exp(G_t - G_s) for the accumulator tile (token tile tb, token tile cb), 0 where s > t
+  auto tile_decay = [&](int tb, int cb) __attribute__((always_inline)) {
+    const int s_ = 16 * cb + acc_col(lane);
     const double Gs = Gd[s_];
+    f32x4 dec;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * tb + acc_row(lane, i);
-      const float dec = (s_ <= t) ? fast_exp2(static_cast<float>(Gd[t] - Gs)) : 0.0f;
-      Af[t * kSA + s_] = (s_ < t) ? Bet[t] * dec * pacc[i] : 0.0f;
-      Ms[t * kSC + s_] = to_bf16(dec * racc[i]);
+      const float e = fast_exp2(static_cast<float>(Gd[t] - Gs));  // selected away (even if infinite) where s > t
+      dec[i] = s_ <= t ? e : 0.0f;
     }
-  }
-  __syncthreads();
-
-  // ================= 3. T = (I + A)^-1 (diagonal blocks by substitution, the rest by block substitution)
+    return dec;
+  };
+  auto store_a = [&](int tb, int cb, f32x4 pacc) __attribute__((always_inline)) {
+    const f32x4 dec = tile_decay(tb, cb);
+    const int s_ = 16 * cb + acc_col(lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + acc_row(lane, i);
+      Af[t * kSA + s_] = (s_ < t) ? Bet[t] * dec[i] * pacc[i] : 0.0f;
+    }
+  };
+  auto store_m = [&](int tb, int cb, f32x4 racc) __attribute__((always_inline)) {
+    const f32x4 dec = tile_decay(tb, cb);
+    const int s_ = 16 * cb + acc_col(lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ms[(16 * tb + acc_row(lane, i)) * kSC + s_] = to_bf16(dec[i] * racc[i]);
+  };
   if (w < 4) {
+    f32x4 pacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    pacc = mma<DK>(pacc, Ks + 16 * w * SK, SK, Ks + 16 * w * SK, SK, lane);
+    store_a(w, w, pacc);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS for this wave's reads
+    __builtin_amdgcn_wave_barrier();
+    // forward substitution, one column of the block per lane (lanes 16-63 repeat lanes 0-15)
     const int cc = lane & 15;
     const float* Ab = Af + (16 * w) * kSA + 16 * w;
     float d[16];
@@ -375,8 +376,50 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
 #pragma unroll
       for (int r = 0; r < 16; ++r) Tf[(16 * w + r) * kST + 16 * w + cc] = d[r];
     }
+  } else {
+    for (int ix = tid - 4 * 64; ix < DK * (kC / 8); ix += 4 * 64) {
+      const int i = ix % DK;
+      const int t8 = (ix / DK) * 8;
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        wv[e] = static_cast<uint32_t>(Ks[(t8 + 2 * e) * SK + i]) | (static_cast<uint32_t>(Ks[(t8 + 2 * e + 1) * SK + i]) << 16);
+      *reinterpret_cast<uint4*>(KT + i * kSC + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    // products 0-5: the tiles of A below the diagonal blocks, (1,0) (2,0) (2,1) (3,0) (3,1) (3,2);
+    // products 6-15: the lower tiles of M in the same order, diagonal tiles included
+    for (int pi = w - 4; pi < 16; pi += 4) {
+      const bool is_a = pi < 6;
+      const int q = is_a ? pi : pi - 6;
+      int tb = 0;
+      if (is_a) {
+        tb = q < 1 ? 1 : (q < 3 ? 2 : 3);
+      } else {
+        while ((tb + 1) * (tb + 2) / 2 <= q) ++tb;
+      }
+      const int cb = is_a ? q - tb * (tb - 1) / 2 : q - tb * (tb + 1) / 2;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = mma<DK>(acc, (is_a ? Ks : Qs) + 16 * tb * SK, SK, Ks + 16 * cb * SK, SK, lane);
+      if (is_a)
+        store_a(tb, cb, acc);
+      else
+        store_m(tb, cb, acc);
+    }
+  }
+  // the next item's inputs, in flight while this one computes: issued once
+  // the previous item's record stores have drained, so that the loads do not
+  // queue behind them, and well ahead of this item's own stores
+  {
+    const int next = item + static_cast<int>(gridDim.x);
+    if (next < n_items) {
+      at = locate(next, next_info);
+      fetch(at);
+      next_info = info_of(next + static_cast<int>(gridDim.x));
+    }
   }
   __syncthreads();
+
+  // ================= 3. the blocks of T below the diagonal, by block substitution
   for (int dist = 1; dist < 4; ++dist) {
     const int i = w + dist, j = w;
     if (i < 4) {
@@ -395,51 +438,79 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     }
     __syncthreads();
   }
-  for (int e = tid; e < kC * kC; e += kThreads) {
-    const int t = e >> 6, s2 = e & 63;
-    const float tv = (s2 <= t) ? Tf[t * kST + s2] : 0.0f;
-    const float bs = Bet[s2];
-    Tp[t * kSC + s2] = to_bf16(tv * bs * Gam[s2]);
-    Tpp[t * kSC + s2] = to_bf16(tv * bs);
-  }
-  __syncthreads();
-
-  // ================= 4. W = T' K (-> LDS, over K), U = T'' V (-> workspace, tile order)
-  const int kmax = (rb < 2) ? 32 : 64;  // T' and T'' vanish above the diagonal
-  constexpr int KTW = DK / 32;
+  // T' = T diag(beta gam) and T'' = T diag(beta) in bf16, lower triangle, four columns per thread
+  for (int e = tid; e < kC * kC / 4; e += kThreads) {
+    const int t = e >> 4, s4 = (e & 15) * 4;
+    const f32x4 tv = *reinterpret_cast<const f32x4*>(Tf + t * kST + s4);
+    const f32x4 bs = *reinterpret_cast<const f32x4*>(Bet + s4);
+    const f32x4 gm = *reinterpret_cast<const f32x4*>(Gam + s4);
+    uint32_t wp[2], wpp[2];
 #pragma unroll
-  for (int e = 0; e < KTW; ++e) {
-    const int ci = chalf * KTW + e;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = mma_range(acc, Tp + (16 * rb) * kSC, kSC, KT + (16 * ci) * kSC, kSC, 0, kmax, lane);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      float a2[2], b2[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Ws[(16 * rb + acc_row(lane, i)) * SK + 16 * ci + acc_col(lane)] = to_bf16(acc[i]);
-  }
-  {
-    float* ug = reinterpret_cast<float*>(base + rec.u);
-    constexpr int UTW = DVT / 2;
-#pragma unroll
-    for (int e = 0; e < UTW; ++e) {
-      const int cj = chalf * UTW + e;
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = mma_range(acc, Tpp + (16 * rb) * kSC, kSC, Vt + (16 * cj) * kSC, kSC, 0, kmax, lane);
-      f32x4* dst = reinterpret_cast<f32x4*>(ug + ((static_cast<size_t>(rb) * DVT + cj) * 64 + lane) * 4);
-      if (nt_stores)
-        __builtin_nontemporal_store(acc, dst);
-      else
-        *dst = acc;
+      for (int k = 0; k < 2; ++k) {
+        const int c = 2 * h2 + k;
+        const float x = (s4 + c <= t) ? tv[c] : 0.0f;
+        b2[k] = x * bs[c];
+        a2[k] = b2[k] * gm[c];
+      }
+      wp[h2] = static_cast<uint32_t>(to_bf16(a2[0])) | (static_cast<uint32_t>(to_bf16(a2[1])) << 16);
+      wpp[h2] = static_cast<uint32_t>(to_bf16(b2[0])) | (static_cast<uint32_t>(to_bf16(b2[1])) << 16);
     }
+    *reinterpret_cast<uint2*>(Tp + t * kSC + s4) = make_uint2(wp[0], wp[1]);
+    *reinterpret_cast<uint2*>(Tpp + t * kSC + s4) = make_uint2(wpp[0], wpp[1]);
   }
   __syncthreads();
 
-  // ================= 5. operand fragments (W, diag(gam) Q, Kt^T, M) and gam_last to the workspace
+  // ================= 4. the record: W and U from MFMA accumulators, then diag(gam) Q, Kt^T and M from LDS
   {
     typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
     constexpr int KB = DK / 32;
     constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16), NF = frags_total(DK);
     u32x4_t* fr = reinterpret_cast<u32x4_t*>(base + rec.frag);
+    auto put = [&](int f, u32x4_t piece) __attribute__((always_inline)) {
+      if (nt_stores)
+        __builtin_nontemporal_store(piece, fr + f * 64 + lane);
+      else
+        fr[f * 64 + lane] = piece;
+    };
+    auto bf2 = [](float a, float b) __attribute__((always_inline)) {
+      return static_cast<uint32_t>(to_bf16(a)) | (static_cast<uint32_t>(to_bf16(b)) << 16);
+    };
+    // W^T = K^T T'^T per (key tile, token tile tw): accumulator element i of lane l
+    // holds W[16 tw + l % 16][16 kt + 4 (l / 16) + i], so the tiles of key tiles
+    // 2 kb and 2 kb + 1 stack into the W fragment (tw, kb) as it is stored
+    const int tw = w & 3;
+    const int kmax_w = tw < 2 ? 32 : 64;  // T' vanishes above the diagonal
+#pragma unroll
+    for (int e = 0; e < KB / 2; ++e) {
+      const int kb = (w >> 2) * (KB / 2) + e;
+      f32x4 lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = {0.0f, 0.0f, 0.0f, 0.0f};
+      lo = mma_range(lo, KT + (32 * kb) * kSC, kSC, Tp + (16 * tw) * kSC, kSC, 0, kmax_w, lane);
+      hi = mma_range(hi, KT + (32 * kb + 16) * kSC, kSC, Tp + (16 * tw) * kSC, kSC, 0, kmax_w, lane);
+      put(tw * KB + kb, u32x4_t{bf2(lo[0], lo[1]), bf2(lo[2], lo[3]), bf2(hi[0], hi[1]), bf2(hi[2], hi[3])});
+    }
+    // U = T'' V in accumulator order (f32); the token tile is the mirror of tw,
+    // so that every wave has the same number of products
+    {
+      const int tu = 3 - tw;
+      const int kmax_u = tu < 2 ? 32 : 64;
+      float* ug = reinterpret_cast<float*>(base + rec.u);
+      constexpr int UTW = DVT / 2;
+#pragma unroll
+      for (int e = 0; e < UTW; ++e) {
+        const int cj = (w >> 2) * UTW + e;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mma_range(acc, Tpp + (16 * tu) * kSC, kSC, Vt + (16 * cj) * kSC, kSC, 0, kmax_u, lane);
+        f32x4* dst = reinterpret_cast<f32x4*>(ug + ((static_cast<size_t>(tu) * DVT + cj) * 64 + lane) * 4);
+        if (nt_stores)
+          __builtin_nontemporal_store(acc, dst);
+        else
+          *dst = acc;
+      }
+    }
     const int g = lane >> 4, r = lane & 15;
-    const double Glast = Gd[kC - 1];  // gates past the chunk's end are 0: G stays at its last value
     // k values of this lane's slots, relative to the block: 4 g + e (e < 4), 16 + 4 g + (e - 4)
     auto slot_k = [&](int e) __attribute__((always_inline)) { return 4 * g + (e & 3) + 16 * (e >> 2); };
     auto pick = [&](const bf16_t* row, int kb) __attribute__((always_inline)) {
@@ -450,36 +521,27 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     auto scaled = [&](u32x4_t x, auto factor) __attribute__((always_inline)) {
       u32x4_t y;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a0 = widen(static_cast<bf16_t>(x[q] & 0xffffu)) * factor(2 * q);
-        const float a1 = widen(static_cast<bf16_t>(x[q] >> 16)) * factor(2 * q + 1);
-        y[q] = static_cast<uint32_t>(to_bf16(a0)) | (static_cast<uint32_t>(to_bf16(a1)) << 16);
-      }
+      for (int q = 0; q < 4; ++q)
+        y[q] = bf2(widen(static_cast<bf16_t>(x[q] & 0xffffu)) * factor(2 * q),
+                   widen(static_cast<bf16_t>(x[q] >> 16)) * factor(2 * q + 1));
       return y;
     };
-    for (int f = w; f < NF; f += kWaves) {
+    for (int f = FQ + w; f < NF; f += kWaves) {
       u32x4_t piece;
-      if (f < FQ) {
-        piece = pick(Ws + (16 * (f / KB) + r) * SK, f % KB);
-      } else if (f < FK) {
+      if (f < FK) {
         const int t = 16 * ((f - FQ) / KB) + r;
         const float gm = Gam[t];
         piece = scaled(pick(Qs + t * SK, (f - FQ) % KB), [&](int) { return gm; });
       } else if (f < FM) {
         const int kb = (f - FK) & 1;
-        piece = scaled(pick(KT + (16 * ((f - FK) >> 1) + r) * kSC, kb), [&](int e) {
-          return fast_exp2(static_cast<float>(Glast - Gd[32 * kb + slot_k(e)]));
-        });
+        piece = scaled(pick(KT + (16 * ((f - FK) >> 1) + r) * kSC, kb), [&](int e) { return Kf[32 * kb + slot_k(e)]; });
       } else {
         const int mf = f - FM;
         const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
         const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
         piece = pick(Ms + (16 * tt + r) * kSC, kb);
       }
-      if (nt_stores)
-        __builtin_nontemporal_store(piece, fr + f * 64 + lane);
-      else
-        fr[f * 64 + lane] = piece;
+      put(f, piece);
     }
     if (tid == 0) *reinterpret_cast<float*>(base + rec.g) = Gam[kC - 1];
   }
