@@ -26,6 +26,8 @@
 // chain per chunk shrinks from the whole chunked step to those four products,
 // and pass 1 fills the whole chip however few sequences and heads there are.
 // A chunk table (chunk_table_kernel) maps the packed sequences to chunks.
+#include <type_traits>
+
 #include "chunk_mfma.hpp"
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
@@ -68,6 +70,15 @@ struct Rec {
     bytes = align256(g + 256);
   }
 };
+
+// The smaller record of the column-block state pass, which reads K, Q and V
+// itself: T' = T diag(beta gam), T'' = T diag(beta) and M, each as its six
+// lower 16 x 32 blocks (the fragment order of M above), then a 1 KiB tail with
+// gam [64] and the update factors exp(G_last - G) [64] in float32 (the last
+// 512 bytes unused).  T' and T'' stand in for W = T' K and U = T'' V.
+constexpr int kTFrags = 18;
+constexpr size_t kTRecTail = static_cast<size_t>(kTFrags) * 1024;
+constexpr size_t kTRecBytes = kTRecTail + 1024;
 
 __host__ __device__ inline int pad16(int x) { return (x + 15) & ~15; }
 
@@ -150,7 +161,7 @@ struct PrepLds {
 // Persistent: one workgroup per CU (the LDS holds one) walks the (chunk,
 // value head) items blockIdx.x, + gridDim.x, ...; the next item's K, Q, V rows
 // and gates are loaded into registers while the current one computes.
-template <typename IO, int DK, int DVT, bool RAW>
+template <typename IO, int DK, int DVT, bool RAW, bool TREC>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
                                                               const int32_t* cs, const int2* __restrict__ info, int items,
                                                               int nt_stores) {
@@ -230,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       rq[it] = *reinterpret_cast<const u32x4*>(qg + off);
     }
 #pragma unroll
-    for (int it = 0; it < V_IT; ++it) {
+    for (int it = 0; it < (TREC ? 0 : V_IT); ++it) {
       const int v = tid + (it >> 1) * kThreads;
       // rows past the chunk and columns past d_v: clamped here, zeroed when staged
       const int t = min(2 * (v % (kC / 2)) + (it & 1), at.Lc - 1), c8 = min((v / (kC / 2)) * 8, d_v - 8);
@@ -286,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     // 32 pairs of a wave fill 32 consecutive words and its two 8-column
     // groups sit 32 banks apart, so the writes are free of bank conflicts
 #pragma unroll
-    for (int it = 0; it < V_IT; it += 2) {
+    for (int it = 0; it < (TREC ? 0 : V_IT); it += 2) {
       const int v = tid + (it >> 1) * kThreads;
       const int t = 2 * (v % (kC / 2)), c8 = (v / (kC / 2)) * 8;
       const bool col_ok = c8 < d_v;
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       for (int r = 0; r < 16; ++r) Tf[(16 * w + r) * kST + 16 * w + cc] = d[r];
     }
   } else {
-    for (int ix = tid - 4 * 64; ix < DK * (kC / 8); ix += 4 * 64) {
+    for (int ix = tid - 4 * 64; ix < (TREC ? 0 : DK * (kC / 8)); ix += 4 * 64) {
       const int i = ix % DK;
       const int t8 = (ix / DK) * 8;
       uint32_t wv[4];
@@ -463,8 +474,35 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   }
   __syncthreads();
 
-  // ================= 4. the record: W and U from MFMA accumulators, then diag(gam) Q, Kt^T and M from LDS
-  {
+  // ================= 4. the record
+  if constexpr (TREC) {
+    // T', T'' and M blocks from LDS, then gam and exp(G_last - G)
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t* fr = reinterpret_cast<u32x4_t*>(base);
+    const int g = lane >> 4, r = lane & 15;
+    for (int f = w; f < kTFrags; f += kWaves) {
+      const int mf = f % 6;
+      const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
+      const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
+      const bf16_t* row = (f < 6 ? Tp : (f < 12 ? Tpp : Ms)) + (16 * tt + r) * kSC;
+      const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * g);
+      const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * g);
+      const u32x4_t piece = {lo.x, lo.y, hi.x, hi.y};
+      if (nt_stores)
+        __builtin_nontemporal_store(piece, fr + f * 64 + lane);
+      else
+        fr[f * 64 + lane] = piece;
+    }
+    if (tid < 32) {
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>((tid < 16 ? Gam : Kf) + 4 * (tid & 15));
+      f32x4* dst = reinterpret_cast<f32x4*>(base + kTRecTail) + tid;
+      if (nt_stores)
+        __builtin_nontemporal_store(v4, dst);
+      else
+        *dst = v4;
+    }
+  } else {
+    // W and U from MFMA accumulators, then diag(gam) Q, Kt^T and M from LDS
     typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
     constexpr int KB = DK / 32;
     constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16), NF = frags_total(DK);
@@ -556,55 +594,109 @@ constexpr int kStateWaves = 4;
 #define GDN_GLOBAL(ptr) ((const __attribute__((address_space(1))) void*)(ptr))
 #define GDN_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i passes the address of four consecutive 16-bit elements (piece
+// i) and receives element i % 4 of pieces i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4: when lane i points at row i / 4, columns 4 (i % 4) .. +3 of a
+// 4 x 16 block, it receives column i of the four rows (checked on the hardware).
+__device__ __forceinline__ s16x4 lds_read_tr(const bf16_t* ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<bf16_t*>(ptr)));
+}
+
+// LDS of the column-block state pass, per chunk buffer: the chunk's K and Q
+// rows (all d_k keys of the q/k head), its V rows over the block's columns
+// and its record.  Rows are stored as 16-byte pieces with piece c of row t at
+// position c ^ (t mod pieces per row), so that the column-wise reads below
+// spread over the banks.
+template <int DK, int SL>
+struct StateLds {
+  static constexpr int NC = kStateWaves * 16 * SL;  // columns per workgroup
+  static constexpr int kK = 0;                       // K rows [C][DK] bf16
+  static constexpr int kQ = kK + kC * DK * 2;        // Q rows [C][DK] bf16
+  static constexpr int kV = kQ + kC * DK * 2;        // V rows [C][NC] bf16
+  static constexpr int kF = kV + kC * NC * 2;        // record
+  static constexpr int kBytes = kF + static_cast<int>(kTRecBytes);
+  static constexpr int NK = kC * DK * 2 / 1024;      // 1 KiB global-to-LDS loads per chunk: K (and Q)
+  static constexpr int NV = kC * NC * 2 / 1024;      // V
+  static constexpr int NR = static_cast<int>(kTRecBytes / 1024);  // record
+  static constexpr int NI = 2 * NK + NV + NR;
+};
+
 // One workgroup of four waves (one per SIMD) per (sequence, value head, block
 // of 64 SL columns).  Wave w owns state columns 16 SL w .. +16 SL - 1 for all
-// DK rows, as MFMA accumulators that never leave its registers: two stacked
-// accumulator tiles, packed to bf16, are directly the B operand of the next
-// products, because the prepared fragments carry the matching permutation of
-// the contraction index.  The fragments of chunk j + 1 travel straight from
-// the workspace into the second LDS buffer (global-to-LDS loads, no
-// registers) while chunk j computes, so a chunk costs one barrier.
+// DK rows, as MFMA accumulators that never leave its registers.  Per chunk,
+// with the chunk's K, Q, V and record in LDS:
+//     U  = T'' V                       (V read transposed)
+//     X  = T' (K S)   D = U - X        (K S packed to bf16 as the B operand)
+//     O  = scale (diag(gam) (Q S) + M D)
+//     S <- gam_last S + K^T diag(exp(G_last - G)) D   (K read transposed)
+// Two stacked accumulator tiles, packed to bf16, are directly the B operand
+// of the next product: the contraction index of every A operand (the K and Q
+// rows, the record's blocks, K^T) is read in the matching permuted order.
+// The next chunk's K, Q, V and record travel straight from memory into the
+// second LDS buffer (global-to-LDS loads, no registers) while this chunk
+// computes, so a chunk costs one barrier.  The ratio value heads of a q/k head
+// and the column blocks of a head sit on one XCD and share K and Q in its L2.
 // NORM (128-column blocks, d_v <= 128): the workgroup owns whole output rows
 // and stores the gated RMSNorm of O instead of O.  Each wave sums the squares
 // of its scaled Y per token with DPP over the 16 lanes of a row and writes
 // them to a per-chunk LDS slot (double-buffered by chunk parity); after the
 // chunk's barrier the row stores of the next chunk add the four waves'
 // partials and apply the norm, with the gate rows loaded a chunk ahead.
-template <typename IO, int DK, int SL, int DVT, bool NORM>
+template <typename IO, int DK, int SL, bool NORM>
 __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_state_kernel(
-    ScanParams p, const unsigned char* ws, size_t rec_bytes, const int32_t* cs) {
+    ScanParams p, const unsigned char* ws, const int32_t* cs) {
   static_assert(!NORM || SL == 2, "the fused norm needs 128-column blocks");
+  using L_ = StateLds<DK, SL>;
   constexpr int KB = DK / 32;   // key blocks of 32
   constexpr int RT = DK / 16;   // state row tiles
-  constexpr int NC = kStateWaves * 16 * SL;
-  constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * RT, NF = frags_total(DK);
-  constexpr int STG = (NF + kStateWaves - 1) / kStateWaves;  // fragments loaded per wave
-  constexpr int kSO = 16 * SL;                                 // bf16 row stride of a wave's output block
-  constexpr int kUT = 4 * SL;                                  // U tiles of a wave
-  // two fragment buffers as distinct objects, so that loads into one are not
-  // mistaken for writes to the other
-  __shared__ __align__(16) bf16x8 frag0[NF * 64];
-  __shared__ __align__(16) bf16x8 frag1[NF * 64];
-  __shared__ __align__(16) f32x4 u_blk[kStateWaves * kUT * 64];   // each wave's U tiles of the current chunk
-  __shared__ __align__(16) float gl_blk[kStateWaves * 64];        // each wave's copy of gam_last
+  constexpr int NC = L_::NC;
+  constexpr int CPK = DK / 8;   // 16-byte pieces per K / Q row
+  constexpr int CPV = NC / 8;   // 16-byte pieces per V row
+  constexpr int kSO = 16 * SL;  // bf16 row stride of a wave's output block
+  constexpr int ISS = (L_::NI + kStateWaves - 1) / kStateWaves;  // loads issued per wave and chunk
+  // two chunk buffers, each region a distinct object, so that the compiler
+  // keeps the loads into one buffer apart from the reads of the other (and
+  // puts no wait for them before those reads)
+  __shared__ __align__(16) bf16_t k0[kC * DK], k1[kC * DK], q0[kC * DK], q1[kC * DK];
+  __shared__ __align__(16) bf16_t v0[kC * NC], v1[kC * NC];
+  __shared__ __align__(16) bf16x8 f0[kTRecBytes / 16], f1[kTRecBytes / 16];
+  struct Buf {
+    bf16_t *k, *q, *v;
+    bf16x8* f;
+  };
+  auto buf_of = [&](auto par) __attribute__((always_inline)) {
+    if constexpr (decltype(par)::value == 0)
+      return Buf{k0, q0, v0, f0};
+    else
+      return Buf{k1, q1, v1, f1};
+  };
   __shared__ __align__(16) bf16_t out_blk[kStateWaves * kC * kSO];  // each wave's output block
   __shared__ float ss_blk[NORM ? 2 * kStateWaves * kC : 1];          // [chunk parity][wave][token] sums of squares
-  static_assert(sizeof(frag0) + sizeof(frag1) + sizeof(u_blk) + sizeof(gl_blk) + sizeof(out_blk) + sizeof(ss_blk) <=
-                    160 * 1024,
-                "LDS budget of one gfx950 workgroup");
+  static_assert(2 * L_::kBytes + sizeof(out_blk) + sizeof(ss_blk) <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+  static_assert(sizeof(k0) + sizeof(q0) + sizeof(v0) + sizeof(f0) == L_::kBytes, "buffer layout");
 
   const int tid = static_cast<int>(threadIdx.x);
-  const int w = tid >> 6;
+  // wave-uniform, and the compiler is told so
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  const int g = lane >> 4;
   bf16_t* Os = out_blk + w * kC * kSO;
-  // blocks go round-robin over the 8 XCDs: the column blocks of one (sequence,
-  // head) unit are placed 8 apart, on one XCD, so they share its L2
+  // blocks go round-robin over the 8 XCDs: the ratio value heads of a q/k head
+  // and their column blocks are placed 8 apart, on one XCD
   const int xcd = static_cast<int>(blockIdx.x) % 8, r = static_cast<int>(blockIdx.x) / 8;
-  const int unit = (r / p.col_blocks) * 8 + xcd;
+  const int per_group = p.ratio * p.col_blocks;
+  const int group = (r / per_group) * 8 + xcd;  // (sequence, q/k head)
+  if (group >= p.num_seqs * p.h_qk) return;     // the grid is padded to whole rounds of 8 groups
+  const int unit = group * p.ratio + (r % per_group) / p.col_blocks;
   const int cb = r % p.col_blocks;
-  if (unit >= p.num_seqs * p.h_v) return;  // the grid is padded to whole rounds of 8 units
   const int h = unit % p.h_v;
   const int n = unit / p.h_v;
+  const int hq = h / p.ratio;
   const int d_v = p.d_v;
   const int T = p.total_tokens;
   const int t_begin = seq_lo(p.cu, n, T);
@@ -615,7 +707,6 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
   bool has_state;
   const int sidx = state_slot(p.slots, p.num_slots, n, &has_state);
   const size_t sbase = (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(DK) * d_v;
-  const Rec rec(DK, 16 * DVT);
 
   // ---- the wave's state slice: row tile ri, column tile sl
   f32x4 S[RT][SL];
@@ -631,40 +722,73 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
       }
     }
 
+  const IO* kg = static_cast<const IO*>(p.k);
+  const IO* qg = static_cast<const IO*>(p.q);
+  const IO* vg = static_cast<const IO*>(p.v);
   IO* og = static_cast<IO*>(p.out);
+  const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
   const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
-  auto record = [&](int j) __attribute__((always_inline)) {
-    return ws + (static_cast<size_t>(c_first + j) * p.h_v + h) * rec_bytes;
-  };
-  // the shared fragments of chunk j into an LDS buffer, a quarter per wave;
-  // load_frag(e) issues the wave's e-th one
-  auto load_frag = [&](int j, bf16x8* dst, int e) __attribute__((always_inline)) {
-    const int f = w + kStateWaves * e;
-    if (f < NF)
-      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(record(j) + rec.frag + (static_cast<size_t>(f) * 64 + lane) * 16),
-                                       GDN_LDS(dst + f * 64), 16, 0, 0);
-  };
-  auto load_frags = [&](int j, bf16x8* dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < STG; ++e) load_frag(j, dst, e);
-  };
-  // this wave's U tiles and gam_last of chunk j into its LDS blocks; load_u1(e)
-  // issues the e-th of the 4 SL + 1 loads
-  f32x4* Uw = u_blk + w * kUT * 64;
-  float* Gw = gl_blk + w * 64;
-  auto load_u1 = [&](int j, int e) __attribute__((always_inline)) {
-    if (e < kUT) {
-      const int tt = e / SL, sl = e % SL;
-      const int cj = min(Jw / 16 + sl, DVT - 1);  // column tile of the whole head (past d_v: U is 0 there anyway)
-      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(record(j) + rec.u + ((static_cast<size_t>(tt) * DVT + cj) * 64 + lane) * 16),
-                                       GDN_LDS(Uw + e * 64), 16, 0, 0);
-    } else {
-      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(record(j) + rec.g + lane * 4), GDN_LDS(Gw), 4, 0, 0);
+  // global-to-LDS load e (< NI) of chunk j into buffer dst: 1 KiB, lane l
+  // writing bytes 16 l .. +15; rows past the sequence repeat its last row
+  // (their contributions vanish: beta = 0 there), columns past d_v repeat the
+  // last 8 (their reads are zeroed below)
+  auto issue = [&](int j, const Buf& dst, int e) __attribute__((always_inline)) {
+    const int c0 = t_begin + j * kC;
+    const int last = t_end - 1 - c0;
+    if (e < 2 * L_::NK) {
+      const bool is_q = e >= L_::NK;
+      const int s = 64 * (e - (is_q ? L_::NK : 0)) + lane;
+      const int t = s / CPK, c = (s % CPK) ^ (t % CPK);
+      const IO* src = (is_q ? qg : kg) + static_cast<size_t>(c0 + min(t, last)) * qk_stride +
+                      static_cast<size_t>(hq) * DK + 8 * c;
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(src), GDN_LDS((is_q ? dst.q : dst.k) + (s - lane) * 8), 16, 0, 0);
+    } else if (e < 2 * L_::NK + L_::NV) {
+      const int s = 64 * (e - 2 * L_::NK) + lane;
+      const int t = s / CPV, c = (s % CPV) ^ (t % CPV);
+      const int col = min(cb * NC + 8 * c, d_v - 8);
+      const IO* src = vg + static_cast<size_t>(c0 + min(t, last)) * v_stride + static_cast<size_t>(h) * d_v + col;
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(src), GDN_LDS(dst.v + (s - lane) * 8), 16, 0, 0);
+    } else if (e < L_::NI) {
+      const int f = e - 2 * L_::NK - L_::NV;
+      const unsigned char* rec = ws + (static_cast<size_t>(c_first + j) * p.h_v + h) * kTRecBytes;
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(rec + (static_cast<size_t>(f) * 64 + lane) * 16),
+                                       GDN_LDS(dst.f + f * 64), 16, 0, 0);
     }
   };
-  auto load_u = [&](int j) __attribute__((always_inline)) {
+  auto issue_all = [&](int j, const Buf& dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e <= kUT; ++e) load_u1(j, e);
+    for (int e = 0; e < ISS; ++e) issue(j, dst, w + kStateWaves * e);
+  };
+  // A operand of rows 16 tt + (l % 16) of a K or Q buffer, keys 32 kb + 4 g .. +3
+  // and 32 kb + 16 + 4 g .. +3 (g = l / 16)
+  auto rows_frag = [&](const bf16_t* X, int tt, int kb) __attribute__((always_inline)) {
+    const int t = 16 * tt + (lane & 15);
+    const int sw = t % CPK;
+    const int c0 = 4 * kb + (g >> 1), half = 4 * (g & 1);
+    const uint2 lo = *reinterpret_cast<const uint2*>(X + t * DK + 8 * (c0 ^ sw) + half);
+    const uint2 hi = *reinterpret_cast<const uint2*>(X + t * DK + 8 * ((c0 + 2) ^ sw) + half);
+    return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+  };
+  // operand over tokens, read transposed: lane l gets column col0 + l % 16 of
+  // token rows 32 kb + 4 g .. +3 (elements 0-3) and 32 kb + 16 + 4 g .. +3
+  auto tr_frag = [&](const bf16_t* X, int row_elems, int pieces, int col0, int kb) __attribute__((always_inline)) {
+    const int i = lane & 15;
+    const int col = col0 + 4 * (i & 3);
+    const int c = col >> 3, half = col & 7;
+    const int t0 = 32 * kb + 4 * g + (i >> 2);
+    const s16x4 a = lds_read_tr(X + t0 * row_elems + 8 * (c ^ (t0 % pieces)) + half);
+    const s16x4 b = lds_read_tr(X + (t0 + 16) * row_elems + 8 * (c ^ ((t0 + 16) % pieces)) + half);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(bf16x8, s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+  };
+  auto pack = [](f32x4 a, f32x4 b) __attribute__((always_inline)) {
+    bf16x8 rr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rr[i] = static_cast<__bf16>(a[i]);
+      rr[4 + i] = static_cast<__bf16>(b[i]);
+    }
+    return rr;
   };
   // swizzled output block: the 8-column piece pc of row t sits at piece pc ^ ((t / 4) % (2 SL))
   auto out_at = [](int t, int c) __attribute__((always_inline)) {
@@ -735,40 +859,46 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
       }
     }
   };
-  auto pack = [](f32x4 a, f32x4 b) __attribute__((always_inline)) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r[i] = static_cast<__bf16>(a[i]);
-      r[4 + i] = static_cast<__bf16>(b[i]);
-    }
-    return r;
-  };
-  // fragments in the order a chunk consumes them: W and diag(gam) Q per
-  // (token tile, key block), then M, then Kt^T per (key tile, token block)
-  auto frag_at = [](int q) constexpr {
-    return q < 8 * KB ? ((q & 1) ? FQ : 0) + (q >> 1) : (q < 8 * KB + 6 ? FM + (q - 8 * KB) : FK + (q - 8 * KB - 6));
-  };
-  constexpr int P = 6;  // fragment reads in flight
 
-  auto chunk = [&](int j, const bf16x8* cur, bf16x8* nxt) __attribute__((always_inline)) {
+  auto chunk = [&](int j, auto par) __attribute__((always_inline)) {
+    const Buf cur = buf_of(par);
+    const Buf nxt = buf_of(std::integral_constant<int, 1 - decltype(par)::value>{});
     // the next chunk's loads are spread over this chunk's products (a burst
     // would stall the wave on the memory pipeline while its MFMAs wait)
     const bool more = j + 1 < nchunks;
     if (og != nullptr && j > 0) store_out(j - 1);
     if (og != nullptr) load_gate(j);
+    const bf16_t* Kc = cur.k;
+    const bf16_t* Qc = cur.q;
+    const bf16_t* Vc = cur.v;
+    const bf16x8* Fc = cur.f + lane;
+    const float* tail = reinterpret_cast<const float*>(cur.f + kTRecTail / 16);
 
-    const bf16x8* fb = cur + lane;
-    bf16x8 ring[P];
+    // ================= a. U = T'' V, V over tokens as the B operand (columns past d_v read as 0)
+    f32x4 U[4][SL];
+    {
+      bf16x8 VB[2][SL];
 #pragma unroll
-    for (int q = 0; q < P; ++q) ring[q] = fb[frag_at(q) * 64];
-    auto take = [&](int q) __attribute__((always_inline)) {
-      const bf16x8 v = ring[q % P];
-      if (q + P < NF) ring[q % P] = fb[frag_at(q + P) * 64];
-      return v;
-    };
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) {
+          VB[kb][sl] = tr_frag(Vc, NC, CPV, 16 * (SL * w + sl), kb);
+          if (Jw + 16 * sl + (lane & 15) >= d_v) VB[kb][sl] = bf16x8{};
+        }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) U[tt][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb <= tt / 2; ++kb) {
+          const bf16x8 a = Fc[(6 + m_frag(tt, kb)) * 64];
+#pragma unroll
+          for (int sl = 0; sl < SL; ++sl) U[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, VB[kb][sl], U[tt][sl], 0, 0, 0);
+        }
+      }
+    }
 
-    // ================= a. X = W S and Y = diag(gam) Q S, the state (bf16) as B operand from registers
+    // ================= b. K S and Q S, the state (bf16) as the B operand from registers
     bf16x8 SB[KB][SL];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -781,37 +911,67 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
       for (int sl = 0; sl < SL; ++sl) X[tt][sl] = Y[tt][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int step = tt * KB + kb;  // 4 KB steps; the STG fragment loads are spread over them
+        const int step = tt * KB + kb;  // 4 KB steps; the ISS loads are spread over them
 #pragma unroll
-        for (int e = (step * STG) / (4 * KB); e < ((step + 1) * STG) / (4 * KB); ++e)
-          if (more) load_frag(j + 1, nxt, e);
-        const bf16x8 aw = take(2 * step);
-        const bf16x8 aq = take(2 * step + 1);
+        for (int e = (step * ISS) / (4 * KB); e < ((step + 1) * ISS) / (4 * KB); ++e)
+          if (more) issue(j + 1, nxt, w + kStateWaves * e);
+        const bf16x8 ak = rows_frag(Kc, tt, kb);
+        const bf16x8 aq = rows_frag(Qc, tt, kb);
 #pragma unroll
         for (int sl = 0; sl < SL; ++sl) {
-          X[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, SB[kb][sl], X[tt][sl], 0, 0, 0);
+          X[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, SB[kb][sl], X[tt][sl], 0, 0, 0);
           Y[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, SB[kb][sl], Y[tt][sl], 0, 0, 0);
         }
       }
     }
-    // ================= b. D = U - X, packed as the B operand over tokens
-    bf16x8 DB[2][SL];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int sl = 0; sl < SL; ++sl)
-        DB[kb][sl] = pack(Uw[((2 * kb) * SL + sl) * 64 + lane] - X[2 * kb][sl], Uw[((2 * kb + 1) * SL + sl) * 64 + lane] - X[2 * kb + 1][sl]);
-    const float gl = Gw[0];
 
-    // ================= c. O = scale (Y + M D), stored at the start of the next chunk
+    // ================= c. D = U - T' (K S), packed as the B operand over tokens, plain and scaled by exp(G_last - G)
+    bf16x8 DB[2][SL], DW[2][SL];
+    {
+      bf16x8 XB[2][SL];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) XB[kb][sl] = pack(X[2 * kb][sl], X[2 * kb + 1][sl]);
+      f32x4 D[4][SL];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) D[tt][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb <= tt / 2; ++kb) {
+          const bf16x8 a = Fc[m_frag(tt, kb) * 64];
+#pragma unroll
+          for (int sl = 0; sl < SL; ++sl) D[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, XB[kb][sl], D[tt][sl], 0, 0, 0);
+        }
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) D[tt][sl] = U[tt][sl] - D[tt][sl];
+      }
+      f32x4 kf[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) kf[tt] = *reinterpret_cast<const f32x4*>(tail + 64 + 16 * tt + 4 * g);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) {
+          DB[kb][sl] = pack(D[2 * kb][sl], D[2 * kb + 1][sl]);
+          DW[kb][sl] = pack(D[2 * kb][sl] * kf[2 * kb], D[2 * kb + 1][sl] * kf[2 * kb + 1]);
+        }
+    }
+
+    // ================= d. O = scale (diag(gam) Q S + M D), stored at the start of the next chunk
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(tail + 16 * tt + 4 * g);
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) Y[tt][sl] = Y[tt][sl] * gm;
 #pragma unroll
       for (int kb = 0; kb <= tt / 2; ++kb) {
-        const bf16x8 am = take(8 * KB + m_frag(tt, kb));
+        const bf16x8 am = Fc[(12 + m_frag(tt, kb)) * 64];
 #pragma unroll
         for (int sl = 0; sl < SL; ++sl) Y[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, DB[kb][sl], Y[tt][sl], 0, 0, 0);
       }
+    }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -831,24 +991,18 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
           if ((lane & 15) == 0) ssw[16 * tt + acc_row(lane, i)] = q;
         }
     }
-    // the wave's U and gam_last blocks are free again (their reads have
-    // returned): the next chunk's go in during the state update
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
 
-    // ================= d. S <- gam_last S + Kt^T D
+    // ================= e. S <- gam_last S + K^T (exp(G_last - G) D), K over tokens as the A operand
+    const float gl = tail[kC - 1];
 #pragma unroll
     for (int ri = 0; ri < RT; ++ri) {
-#pragma unroll
-      for (int e = (ri * (kUT + 1)) / RT; e < ((ri + 1) * (kUT + 1)) / RT; ++e)
-        if (more) load_u1(j + 1, e);
 #pragma unroll
       for (int sl = 0; sl < SL; ++sl) S[ri][sl] = S[ri][sl] * gl;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ak = take(8 * KB + 6 + 2 * ri + kb);
+        const bf16x8 ak = tr_frag(Kc, DK, CPK, 16 * ri, kb);
 #pragma unroll
-        for (int sl = 0; sl < SL; ++sl) S[ri][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, DB[kb][sl], S[ri][sl], 0, 0, 0);
+        for (int sl = 0; sl < SL; ++sl) S[ri][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, DW[kb][sl], S[ri][sl], 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's share of the next buffer has landed
@@ -856,14 +1010,13 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
   };
 
   if (nchunks > 0) {
-    load_frags(0, frag0);
-    load_u(0);
+    issue_all(0, buf_of(std::integral_constant<int, 0>{}));
     __builtin_amdgcn_s_waitcnt(0x0f70);
   }
   __syncthreads();
   for (int j = 0; j < nchunks; j += 2) {
-    chunk(j, frag0, frag1);
-    if (j + 1 < nchunks) chunk(j + 1, frag1, frag0);
+    chunk(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nchunks) chunk(j + 1, std::integral_constant<int, 1>{});
   }
   if (og != nullptr && nchunks > 0) store_out(nchunks - 1);
 
@@ -1100,49 +1253,68 @@ int split_columns(int d_v, int units) {
 }
 
 
+template <typename IO, int DK, int DVT, bool TREC>
+hipError_t launch_prep(const ScanParams& p, unsigned char* ws, size_t rec_bytes, const int32_t* cs, const int2* info,
+                       int items, int nt, hipStream_t stream) {
+  constexpr int bytes = PrepLds<DK, DVT>::kBytes;
+  const unsigned grid = static_cast<unsigned>(items < prep_workgroups() ? items : prep_workgroups());
+  if (p.gates.raw) {
+    auto kern = chunk_prep_kernel<IO, DK, DVT, true, TREC>;
+    hipError_t e = set_lds(kern, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
+  } else {
+    auto kern = chunk_prep_kernel<IO, DK, DVT, false, TREC>;
+    hipError_t e = set_lds(kern, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
+  }
+  return hipGetLastError();
+}
+
+// The row-split state pass reads the full record (W, diag(gam) Q, Kt^T, M,
+// U); the column-block pass reads K, Q and V itself and the T', T'', M record.
 template <typename IO, int DK, int DVT>
 hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, int32_t* cs, const int2* info,
                       int chunk_bound, hipStream_t stream) {
+  const int units = p.num_seqs * p.h_v;
+  const bool rows = DK == 128 && split_rows(p.d_k, p.d_v, units);
   if (chunk_bound > 0 && p.h_v > 0) {
-    constexpr int bytes = PrepLds<DK, DVT>::kBytes;
     const int items = chunk_bound * p.h_v;
-    const unsigned grid = static_cast<unsigned>(items < prep_workgroups() ? items : prep_workgroups());
     // Nontemporal record stores ahead of the column-block state pass (the
     // 8-sequence packed workload 1.07-1.08 against 1.09-1.10 ms); ahead of
     // the row-split pass they cost about 1 % (one 4096-token sequence).
-    const int nt = DK == 128 && split_rows(p.d_k, p.d_v, p.num_seqs * p.h_v) ? 0 : 1;
-    if (p.gates.raw) {
-      auto kern = chunk_prep_kernel<IO, DK, DVT, true>;
-      hipError_t e = set_lds(kern, bytes);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
-    } else {
-      auto kern = chunk_prep_kernel<IO, DK, DVT, false>;
-      hipError_t e = set_lds(kern, bytes);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
-    }
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = rows ? launch_prep<IO, DK, DVT, false>(p, ws, rec_bytes, cs, info, items, 0, stream)
+                              : launch_prep<IO, DK, 8, true>(p, ws, rec_bytes, cs, info, items, 1, stream);
     if (e != hipSuccess) return e;
   }
-  const int units = p.num_seqs * p.h_v;
-  const unsigned blocks = static_cast<unsigned>((units + 7) / 8) * 8u * static_cast<unsigned>(p.col_blocks);
   if (units == 0) return hipSuccess;
   if constexpr (DK == 128) {
-    if (split_rows(p.d_k, p.d_v, units) && !(p.norm.gate != nullptr && split_fuses_norm(p.d_v, units))) {
+    if (rows) {
       const int units8 = (units + 7) / 8 * 8;
       const unsigned rblocks = static_cast<unsigned>(units8) * static_cast<unsigned>((p.d_v + 15) / 16);
       hipLaunchKernelGGL((chunk_rows_kernel<DVT>), dim3(rblocks), dim3(64 * kRowWaves), 0, stream, p, ws, rec_bytes, cs, units8);
       return hipGetLastError();
     }
   }
+  const unsigned groups8 = static_cast<unsigned>((p.num_seqs * p.h_qk + 7) / 8 * 8);
+  const unsigned blocks = groups8 * static_cast<unsigned>(p.ratio) * static_cast<unsigned>(p.col_blocks);
   if (p.norm.gate != nullptr && split_fuses_norm(p.d_v, units))
-    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, DVT, true>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, true>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
   else if (split_columns(p.d_v, units) == 128)
-    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, DVT, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
   else
-    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 1, DVT, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, rec_bytes, cs);
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 1, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
   return hipGetLastError();
+}
+
+// Bytes of one (chunk, value head) record for the state pass that runs.
+size_t record_bytes(int d_k, int d_v, int units) {
+  if (split_rows(d_k, d_v, units)) {
+    const int dvt = pad16(d_v) > 128 ? 16 : 8;
+    return Rec(d_k, 16 * dvt).bytes;
+  }
+  return kTRecBytes;
 }
 
 int chunk_bound_of(int num_seqs, int total_tokens) {
@@ -1185,16 +1357,14 @@ hipError_t launch_chunk_table(const int32_t* cu, int num_seqs, int total_tokens,
 
 size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v) {
   if (num_seqs <= 0) return 0;
-  const int dvt = pad16(d_v) > 128 ? 16 : 8;
-  const Rec rec(d_k, 16 * dvt);
   return table_bytes(num_seqs, total_tokens) +
-         static_cast<size_t>(chunk_bound_of(num_seqs, total_tokens)) * h_v * rec.bytes;
+         static_cast<size_t>(chunk_bound_of(num_seqs, total_tokens)) * h_v * record_bytes(d_k, d_v, num_seqs * h_v);
 }
 
 hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t stream) {
   if (p.num_seqs <= 0) return hipSuccess;
   const int dvt = pad16(p.d_v) > 128 ? 16 : 8;
-  const Rec rec(p.d_k, 16 * dvt);
+  const size_t rec_bytes = record_bytes(p.d_k, p.d_v, p.num_seqs * p.h_v);
   // total tokens: the caller's count (the kernels clamp the sequences to it)
   const int T = p.total_tokens;
   int32_t* cs = static_cast<int32_t*>(workspace);
@@ -1206,10 +1376,9 @@ hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t strea
   if (e != hipSuccess) return e;
   const int bound = chunk_bound_of(p.num_seqs, T);
   if (p.d_k == 128)
-    return dvt == 16 ? launch_dvt<bf16_t, 128, 16>(p, recs, rec.bytes, cs, info, bound, stream)
-                     : launch_dvt<bf16_t, 128, 8>(p, recs, rec.bytes, cs, info, bound, stream);
-  return dvt == 16 ? launch_dvt<bf16_t, 64, 16>(p, recs, rec.bytes, cs, info, bound, stream)
-                   : launch_dvt<bf16_t, 64, 8>(p, recs, rec.bytes, cs, info, bound, stream);
+    return dvt == 16 ? launch_dvt<bf16_t, 128, 16>(p, recs, rec_bytes, cs, info, bound, stream)
+                     : launch_dvt<bf16_t, 128, 8>(p, recs, rec_bytes, cs, info, bound, stream);
+  return launch_dvt<bf16_t, 64, 8>(p, recs, rec_bytes, cs, info, bound, stream);
 }
 
 }  // namespace gdn
