@@ -728,36 +728,56 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
   IO* og = static_cast<IO*>(p.out);
   const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
   const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
-  // global-to-LDS load e (< NI) of chunk j into buffer dst: 1 KiB, lane l
-  // writing bytes 16 l .. +15; rows past the sequence repeat its last row
-  // (their contributions vanish: beta = 0 there), columns past d_v repeat the
-  // last 8 (their reads are zeroed below)
+  // This wave's loads of a chunk, e = 0 .. ISS - 1, each 1 KiB with lane l
+  // writing bytes 16 l .. +15: K pieces w + 4 e (e < EQ), Q pieces, V pieces,
+  // then record pieces, so that the kind of load e is fixed at compile time.
+  // The row in the chunk and the offset of each lane's 16 bytes are the same
+  // for every chunk.  Rows past the sequence repeat its last row (their
+  // contributions vanish: beta = 0 there); columns past d_v repeat the last 8
+  // (their reads are zeroed below).
+  constexpr int EQ = L_::NK / kStateWaves, EV = 2 * EQ, ER = EV + L_::NV / kStateWaves;
+  static_assert(L_::NK % kStateWaves == 0 && L_::NV % kStateWaves == 0, "whole loads per wave");
+  static_assert(ISS == ER + (L_::NR + kStateWaves - 1) / kStateWaves, "loads per wave");
+  int ld_row[ISS], ld_off[ISS];
+#pragma unroll
+  for (int e = 0; e < ISS; ++e) {
+    ld_row[e] = 0;
+    if (e < EV) {
+      const int s = 64 * (w + kStateWaves * (e < EQ ? e : e - EQ)) + lane;
+      const int t = s / CPK, c = (s % CPK) ^ (t % CPK);
+      ld_row[e] = t;
+      ld_off[e] = hq * DK + 8 * c;  // elements
+    } else if (e < ER) {
+      const int s = 64 * (w + kStateWaves * (e - EV)) + lane;
+      const int t = s / CPV, c = (s % CPV) ^ (t % CPV);
+      ld_row[e] = t;
+      ld_off[e] = h * d_v + min(cb * NC + 8 * c, d_v - 8);  // elements
+    } else {
+      ld_off[e] = (64 * (w + kStateWaves * (e - ER)) + lane) * 16;  // bytes of the record
+    }
+  }
   auto issue = [&](int j, const Buf& dst, int e) __attribute__((always_inline)) {
     const int c0 = t_begin + j * kC;
-    const int last = t_end - 1 - c0;
-    if (e < 2 * L_::NK) {
-      const bool is_q = e >= L_::NK;
-      const int s = 64 * (e - (is_q ? L_::NK : 0)) + lane;
-      const int t = s / CPK, c = (s % CPK) ^ (t % CPK);
-      const IO* src = (is_q ? qg : kg) + static_cast<size_t>(c0 + min(t, last)) * qk_stride +
-                      static_cast<size_t>(hq) * DK + 8 * c;
-      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(src), GDN_LDS((is_q ? dst.q : dst.k) + (s - lane) * 8), 16, 0, 0);
-    } else if (e < 2 * L_::NK + L_::NV) {
-      const int s = 64 * (e - 2 * L_::NK) + lane;
-      const int t = s / CPV, c = (s % CPV) ^ (t % CPV);
-      const int col = min(cb * NC + 8 * c, d_v - 8);
-      const IO* src = vg + static_cast<size_t>(c0 + min(t, last)) * v_stride + static_cast<size_t>(h) * d_v + col;
-      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(src), GDN_LDS(dst.v + (s - lane) * 8), 16, 0, 0);
-    } else if (e < L_::NI) {
-      const int f = e - 2 * L_::NK - L_::NV;
+    const size_t row = static_cast<size_t>(c0 + min(ld_row[e], t_end - 1 - c0));
+    if (e < EQ) {
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(kg + row * qk_stride + ld_off[e]),
+                                       GDN_LDS(dst.k + 512 * (w + kStateWaves * e)), 16, 0, 0);
+    } else if (e < EV) {
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(qg + row * qk_stride + ld_off[e]),
+                                       GDN_LDS(dst.q + 512 * (w + kStateWaves * (e - EQ))), 16, 0, 0);
+    } else if (e < ER) {
+      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(vg + row * v_stride + ld_off[e]),
+                                       GDN_LDS(dst.v + 512 * (w + kStateWaves * (e - EV))), 16, 0, 0);
+    } else {
+      const int f = w + kStateWaves * (e - ER);
       const unsigned char* rec = ws + (static_cast<size_t>(c_first + j) * p.h_v + h) * kTRecBytes;
-      __builtin_amdgcn_global_load_lds(GDN_GLOBAL(rec + (static_cast<size_t>(f) * 64 + lane) * 16),
-                                       GDN_LDS(dst.f + f * 64), 16, 0, 0);
+      if (e + 1 < ISS || f < L_::NR)
+        __builtin_amdgcn_global_load_lds(GDN_GLOBAL(rec + ld_off[e]), GDN_LDS(dst.f + 64 * f), 16, 0, 0);
     }
   };
   auto issue_all = [&](int j, const Buf& dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < ISS; ++e) issue(j, dst, w + kStateWaves * e);
+    for (int e = 0; e < ISS; ++e) issue(j, dst, e);
   };
   // A operand of rows 16 tt + (l % 16) of a K or Q buffer, keys 32 kb + 4 g .. +3
   // and 32 kb + 16 + 4 g .. +3 (g = l / 16)
@@ -904,24 +924,36 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int sl = 0; sl < SL; ++sl) SB[kb][sl] = pack(S[2 * kb][sl], S[2 * kb + 1][sl]);
+    // the next chunk's loads (the last chunk reloads itself into the idle
+    // buffer) are spread over the 4 KB steps; the K and Q operands are read P
+    // steps ahead
+    const int jn = more ? j + 1 : j;
+    constexpr int NSTEP = 4 * KB, P = 4;
+    bf16x8 rk[P], rq[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      rk[q] = rows_frag(Kc, q / KB, q % KB);
+      rq[q] = rows_frag(Qc, q / KB, q % KB);
+    }
     f32x4 X[4][SL], Y[4][SL];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int step = 0; step < NSTEP; ++step) {
+      const int tt = step / KB, kb = step % KB;
+      if (kb == 0) {
 #pragma unroll
-      for (int sl = 0; sl < SL; ++sl) X[tt][sl] = Y[tt][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int sl = 0; sl < SL; ++sl) X[tt][sl] = Y[tt][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int step = tt * KB + kb;  // 4 KB steps; the ISS loads are spread over them
+      for (int e = (step * ISS) / NSTEP; e < ((step + 1) * ISS) / NSTEP; ++e) issue(jn, nxt, e);
+      const bf16x8 ak = rk[step % P], aq = rq[step % P];
+      if (step + P < NSTEP) {
+        rk[step % P] = rows_frag(Kc, (step + P) / KB, (step + P) % KB);
+        rq[step % P] = rows_frag(Qc, (step + P) / KB, (step + P) % KB);
+      }
 #pragma unroll
-        for (int e = (step * ISS) / (4 * KB); e < ((step + 1) * ISS) / (4 * KB); ++e)
-          if (more) issue(j + 1, nxt, w + kStateWaves * e);
-        const bf16x8 ak = rows_frag(Kc, tt, kb);
-        const bf16x8 aq = rows_frag(Qc, tt, kb);
-#pragma unroll
-        for (int sl = 0; sl < SL; ++sl) {
-          X[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, SB[kb][sl], X[tt][sl], 0, 0, 0);
-          Y[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, SB[kb][sl], Y[tt][sl], 0, 0, 0);
-        }
+      for (int sl = 0; sl < SL; ++sl) {
+        X[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, SB[kb][sl], X[tt][sl], 0, 0, 0);
+        Y[tt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, SB[kb][sl], Y[tt][sl], 0, 0, 0);
       }
     }
 
