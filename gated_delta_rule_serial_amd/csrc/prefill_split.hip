@@ -330,11 +330,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     }
     __syncthreads();
 
-  // ================= 2. A = strictly lower (beta_t exp(G_t - G_s) k_t.k_s), M = lower (exp(G_t - G_s) q_t.k_s),
-  // K^T, and the diagonal 16 x 16 blocks of T = (I + A)^-1.  Waves 0-3 form the
-  // diagonal tile of A in block w and invert that block at once; waves 4-7
-  // transpose K and form the six tiles of A below the diagonal blocks and the
-  // ten lower tiles of M, which only later phases read.
+  // ================= 2. A = strictly lower (beta_t exp(G_t - G_s) k_t.k_s), K^T, and the
+  // diagonal 16 x 16 blocks of T = (I + A)^-1.  Waves 0-3 form the diagonal
+  // tile of A in block w and invert that block at once; waves 4-7 transpose K
+  // and form the six tiles of A below the diagonal blocks.  The ten lower
+  // tiles of M = lower (exp(G_t - G_s) q_t.k_s), which only the record reads,
+  // are formed by the waves that the block substitution leaves idle.
   // exp(G_t - G_s) for the accumulator tile (token tile tb, token tile cb), 0 where s > t
   auto tile_decay = [&](int tb, int cb) __attribute__((always_inline)) {
     const int s_ = 16 * cb + acc_col(lane);
@@ -397,24 +398,13 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
         wv[e] = static_cast<uint32_t>(Ks[(t8 + 2 * e) * SK + i]) | (static_cast<uint32_t>(Ks[(t8 + 2 * e + 1) * SK + i]) << 16);
       *reinterpret_cast<uint4*>(KT + i * kSC + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
-    // products 0-5: the tiles of A below the diagonal blocks, (1,0) (2,0) (2,1) (3,0) (3,1) (3,2);
-    // products 6-15: the lower tiles of M in the same order, diagonal tiles included
-    for (int pi = w - 4; pi < 16; pi += 4) {
-      const bool is_a = pi < 6;
-      const int q = is_a ? pi : pi - 6;
-      int tb = 0;
-      if (is_a) {
-        tb = q < 1 ? 1 : (q < 3 ? 2 : 3);
-      } else {
-        while ((tb + 1) * (tb + 2) / 2 <= q) ++tb;
-      }
-      const int cb = is_a ? q - tb * (tb - 1) / 2 : q - tb * (tb + 1) / 2;
+    // the tiles of A below the diagonal blocks, (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    for (int q = w - 4; q < 6; q += 4) {
+      const int tb = q < 1 ? 1 : (q < 3 ? 2 : 3);
+      const int cb = q - tb * (tb - 1) / 2;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = mma<DK>(acc, (is_a ? Ks : Qs) + 16 * tb * SK, SK, Ks + 16 * cb * SK, SK, lane);
-      if (is_a)
-        store_a(tb, cb, acc);
-      else
-        store_m(tb, cb, acc);
+      acc = mma<DK>(acc, Ks + 16 * tb * SK, SK, Ks + 16 * cb * SK, SK, lane);
+      store_a(tb, cb, acc);
     }
   }
   // the next item's inputs, in flight while this one computes: issued once
@@ -430,9 +420,20 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   }
   __syncthreads();
 
-  // ================= 3. the blocks of T below the diagonal, by block substitution
+  // ================= 3. the blocks of T below the diagonal, by block substitution;
+  // beside the first two steps, waves 3-7 form the lower tiles of M
+  // ((0,0) (1,0) (1,1) (2,0) .. (3,3), five per step)
   for (int dist = 1; dist < 4; ++dist) {
     const int i = w + dist, j = w;
+    const int mq = 5 * (dist - 1) + (w - 3);
+    if (w >= 3 && mq < 10) {
+      int tb = 0;
+      while ((tb + 1) * (tb + 2) / 2 <= mq) ++tb;
+      const int cb = mq - tb * (tb + 1) / 2;
+      f32x4 racc = {0.0f, 0.0f, 0.0f, 0.0f};
+      racc = mma<DK>(racc, Qs + 16 * tb * SK, SK, Ks + 16 * cb * SK, SK, lane);
+      store_m(tb, cb, racc);
+    }
     if (i < 4) {
       f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int k = j; k < i; ++k)
