@@ -336,26 +336,32 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   // and form the six tiles of A below the diagonal blocks.  The ten lower
   // tiles of M = lower (exp(G_t - G_s) q_t.k_s), which only the record reads,
   // are formed by the waves that the block substitution leaves idle.
-  // exp(G_t - G_s) for the accumulator tile (token tile tb, token tile cb), 0 where s > t
+  // exp(G_t - G_s) for the accumulator tile (token tile tb, token tile cb), 0 where s > t;
+  // the lane's four rows are 16 tb + 4 g + i, read at once (no load waits inside a branch)
   auto tile_decay = [&](int tb, int cb) __attribute__((always_inline)) {
     const int s_ = 16 * cb + acc_col(lane);
+    const int t0 = 16 * tb + acc_row(lane, 0);
     const double Gs = Gd[s_];
+    const double2 ga = *reinterpret_cast<const double2*>(Gd + t0);
+    const double2 gb = *reinterpret_cast<const double2*>(Gd + t0 + 2);
+    const double gt[4] = {ga.x, ga.y, gb.x, gb.y};
     f32x4 dec;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 16 * tb + acc_row(lane, i);
-      const float e = fast_exp2(static_cast<float>(Gd[t] - Gs));  // selected away (even if infinite) where s > t
-      dec[i] = s_ <= t ? e : 0.0f;
+      const float e = fast_exp2(static_cast<float>(gt[i] - Gs));  // selected away (even if infinite) where s > t
+      dec[i] = s_ <= t0 + i ? e : 0.0f;
     }
     return dec;
   };
   auto store_a = [&](int tb, int cb, f32x4 pacc) __attribute__((always_inline)) {
     const f32x4 dec = tile_decay(tb, cb);
     const int s_ = 16 * cb + acc_col(lane);
+    const int t0 = 16 * tb + acc_row(lane, 0);
+    const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + t0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 16 * tb + acc_row(lane, i);
-      Af[t * kSA + s_] = (s_ < t) ? Bet[t] * dec[i] * pacc[i] : 0.0f;
+      const float a = bt[i] * dec[i] * pacc[i];
+      Af[(t0 + i) * kSA + s_] = (s_ < t0 + i) ? a : 0.0f;
     }
   };
   auto store_m = [&](int tb, int cb, f32x4 racc) __attribute__((always_inline)) {
