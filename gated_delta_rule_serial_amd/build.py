@@ -118,8 +118,10 @@ def _kernels_of(co: str) -> dict:
             kernels[parts[7]]["code_sha256_16"] = hashlib.sha256(code).hexdigest()[:16]
     for k in kernels.values():
         k.pop("name", None)
-        total = (k.get("vgprs", 0) + 3) // 4 * 4 + k.get("agprs", 0)
-        # waves per SIMD that the register file allows (512 registers per lane, granule 8)
+        # waves per SIMD that the register file allows (512 registers per lane,
+        # granule 8); on gfx950 the vgpr count is already the unified total,
+        # the architectural registers (aligned to 4) plus the accumulation ones
+        total = k.get("vgprs", 0)
         k["waves_per_simd_by_registers"] = min(8, 512 // max(8, (total + 7) // 8 * 8))
     return kernels
 

@@ -654,10 +654,15 @@ struct StateLds {
 // them to a per-chunk LDS slot (double-buffered by chunk parity); after the
 // chunk's barrier the row stores of the next chunk add the four waves'
 // partials and apply the norm, with the gate rows loaded a chunk ahead.
-template <typename IO, int DK, int SL, bool NORM>
-__global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_state_kernel(
-    ScanParams p, const unsigned char* ws, const int32_t* cs) {
+// ONE (64-column blocks, no norm): one chunk buffer, and two workgroups per
+// compute unit, so that one's loads and barriers overlap the other's products:
+// each chunk ends with a barrier, the next chunk's loads, the output stores
+// of this one and a second barrier.
+template <typename IO, int DK, int SL, bool NORM, bool ONE>
+__global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_eu(ONE ? 2 : 1, ONE ? 2 : 1))) void
+chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
   static_assert(!NORM || SL == 2, "the fused norm needs 128-column blocks");
+  static_assert(!ONE || (SL == 1 && !NORM), "one buffer: 64-column blocks without the norm");
   using L_ = StateLds<DK, SL>;
   constexpr int KB = DK / 32;   // key blocks of 32
   constexpr int RT = DK / 16;   // state row tiles
@@ -669,22 +674,23 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
   // two chunk buffers, each region a distinct object, so that the compiler
   // keeps the loads into one buffer apart from the reads of the other (and
   // puts no wait for them before those reads)
-  __shared__ __align__(16) bf16_t k0[kC * DK], k1[kC * DK], q0[kC * DK], q1[kC * DK];
-  __shared__ __align__(16) bf16_t v0[kC * NC], v1[kC * NC];
-  __shared__ __align__(16) bf16x8 f0[kTRecBytes / 16], f1[kTRecBytes / 16];
+  __shared__ __align__(16) bf16_t k0[kC * DK], k1[ONE ? 8 : kC * DK], q0[kC * DK], q1[ONE ? 8 : kC * DK];
+  __shared__ __align__(16) bf16_t v0[kC * NC], v1[ONE ? 8 : kC * NC];
+  __shared__ __align__(16) bf16x8 f0[kTRecBytes / 16], f1[ONE ? 1 : kTRecBytes / 16];
   struct Buf {
     bf16_t *k, *q, *v;
     bf16x8* f;
   };
   auto buf_of = [&](auto par) __attribute__((always_inline)) {
-    if constexpr (decltype(par)::value == 0)
+    if constexpr (ONE || decltype(par)::value == 0)
       return Buf{k0, q0, v0, f0};
     else
       return Buf{k1, q1, v1, f1};
   };
   __shared__ __align__(16) bf16_t out_blk[kStateWaves * kC * kSO];  // each wave's output block
   __shared__ float ss_blk[NORM ? 2 * kStateWaves * kC : 1];          // [chunk parity][wave][token] sums of squares
-  static_assert(2 * L_::kBytes + sizeof(out_blk) + sizeof(ss_blk) <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+  static_assert((ONE ? 1 : 2) * L_::kBytes + sizeof(out_blk) + sizeof(ss_blk) <= (ONE ? 80 : 160) * 1024,
+                "LDS budget of one gfx950 compute unit");
   static_assert(sizeof(k0) + sizeof(q0) + sizeof(v0) + sizeof(f0) == L_::kBytes, "buffer layout");
 
   const int tid = static_cast<int>(threadIdx.x);
@@ -893,7 +899,7 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
     // the next chunk's loads are spread over this chunk's products (a burst
     // would stall the wave on the memory pipeline while its MFMAs wait)
     const bool more = j + 1 < nchunks;
-    if (og != nullptr && j > 0) store_out(j - 1);
+    if (!ONE && og != nullptr && j > 0) store_out(j - 1);
     if (og != nullptr) load_gate(j);
     const bf16_t* Kc = cur.k;
     const bf16_t* Qc = cur.q;
@@ -950,8 +956,10 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int sl = 0; sl < SL; ++sl) X[tt][sl] = Y[tt][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
+      if constexpr (!ONE) {
 #pragma unroll
-      for (int e = (step * ISS) / NSTEP; e < ((step + 1) * ISS) / NSTEP; ++e) issue(jn, nxt, e);
+        for (int e = (step * ISS) / NSTEP; e < ((step + 1) * ISS) / NSTEP; ++e) issue(jn, nxt, e);
+      }
       const bf16x8 ak = rk[step % P], aq = rq[step % P];
       if (step + P < NSTEP) {
         rk[step % P] = rows_frag(Kc, (step + P) / KB, (step + P) % KB);
@@ -1044,6 +1052,11 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
         for (int sl = 0; sl < SL; ++sl) S[ri][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, DW[kb][sl], S[ri][sl], 0, 0, 0);
       }
     }
+    if constexpr (ONE) {
+      __syncthreads();  // every wave is done with this chunk's K, Q, V and record
+      if (more) issue_all(j + 1, nxt);
+      if (og != nullptr) store_out(j);
+    }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's share of the next buffer has landed
     __syncthreads();                     // the next buffer is complete; this one may be refilled
   };
@@ -1057,7 +1070,7 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
     chunk(j, std::integral_constant<int, 0>{});
     if (j + 1 < nchunks) chunk(j + 1, std::integral_constant<int, 1>{});
   }
-  if (og != nullptr && nchunks > 0) store_out(nchunks - 1);
+  if (!ONE && og != nullptr && nchunks > 0) store_out(nchunks - 1);
 
   // ---- final state
   if (p.sN != nullptr && has_state) {
@@ -1339,11 +1352,11 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
   const unsigned groups8 = static_cast<unsigned>((p.num_seqs * p.h_qk + 7) / 8 * 8);
   const unsigned blocks = groups8 * static_cast<unsigned>(p.ratio) * static_cast<unsigned>(p.col_blocks);
   if (p.norm.gate != nullptr && split_fuses_norm(p.d_v, units))
-    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, true>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, true, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
   else if (split_columns(p.d_v, units) == 128)
-    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 2, false, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
   else
-    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 1, false>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
+    hipLaunchKernelGGL((chunk_state_kernel<IO, DK, 1, false, true>), dim3(blocks), dim3(64 * kStateWaves), 0, stream, p, ws, cs);
   return hipGetLastError();
 }
 
