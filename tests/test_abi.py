@@ -278,11 +278,20 @@ def test_prefill_workspace_size(lib):
     size = ctypes.c_uint64(123)
     chunky = dict(io_dtype=gdn.GDN_BF16, d_k=128, d_v=128, h_qk=16, h_v=32)
     assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), 8, 33173, ctypes.byref(size)) == gdn.GDN_OK
-    # the chunk table, then one record per (chunk, head) for ceil(T / 64) + N chunks
+    # the chunk table, then one record per (chunk, head) for ceil(T / 64) + N chunks.
+    # 256 (sequence, head) units take the column-block state pass: the six lower
+    # blocks of T diag(beta gam), T diag(beta) and M (1 KiB each), then gam and
+    # exp(G_last - G) in a 1 KiB tail
+    per_rec = 18 * 1024 + 1024
+    bound = 33173 // 64 + 1 + 8
+    assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * per_rec
+    # one sequence of 32 heads (32 x 8 16-column tiles fill the 256 compute units
+    # assumed without a device) takes the row-split pass and the full record:
     # operand fragments (W, diag(gam) Q: 16 each; Kt^T: 16; M: 6) of 1 KiB, U in f32, gam_last
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), 1, 4096, ctypes.byref(size)) == gdn.GDN_OK
     per_rec = (16 + 16 + 16 + 6) * 1024 + 64 * 128 * 4 + 16
     per_rec = (per_rec + 255) // 256 * 256
-    bound = 33173 // 64 + 1 + 8
+    bound = 4096 // 64 + 1
     assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * per_rec
     for kw in (dict(algorithm=gdn.GDN_ALGO_SERIAL), dict(io_dtype=gdn.GDN_F16), dict(d_k=96), dict(rule=2),
                dict(decay_per_key=1), dict(state_window=2)):
