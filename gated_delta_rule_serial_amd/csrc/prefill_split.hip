@@ -274,7 +274,17 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     Ms[t * kSC + s] = 0;
   }
 
+  // Blocks go round-robin over the 8 XCDs.  Where the grid allows, the ratio
+  // value heads of one (chunk, q/k head) go to blocks 8 apart, on one XCD,
+  // which run them at about the same time and read K and Q once through its L2.
   int item = static_cast<int>(blockIdx.x);
+  {
+    const int R = p.ratio, G = static_cast<int>(gridDim.x);
+    if (R > 1 && G % (8 * R) == 0) {
+      const int xcd = item % 8, j = item / 8;
+      item = (j / R) * (8 * R) + xcd * R + j % R;
+    }
+  }
   if (item >= n_items) return;
   Where at = locate(item, info[item / p.h_v]);
   fetch(at);
