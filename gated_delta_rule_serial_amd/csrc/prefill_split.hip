@@ -161,7 +161,7 @@ struct PrepLds {
 // Persistent: one workgroup per CU (the LDS holds one) walks the (chunk,
 // value head) items blockIdx.x, + gridDim.x, ...; the next item's K, Q, V rows
 // and gates are loaded into registers while the current one computes.
-template <typename IO, int DK, int DVT, bool RAW, bool TREC>
+template <typename IO, int DK, int DVT, bool RAW>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
                                                               const int32_t* cs, const int2* __restrict__ info, int items,
                                                               int nt_stores) {
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       rq[it] = *reinterpret_cast<const u32x4*>(qg + off);
     }
 #pragma unroll
-    for (int it = 0; it < (TREC ? 0 : V_IT); ++it) {
+    for (int it = 0; it < V_IT; ++it) {
       const int v = tid + (it >> 1) * kThreads;
       // rows past the chunk and columns past d_v: clamped here, zeroed when staged
       const int t = min(2 * (v % (kC / 2)) + (it & 1), at.Lc - 1), c8 = min((v / (kC / 2)) * 8, d_v - 8);
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     // 32 pairs of a wave fill 32 consecutive words and its two 8-column
     // groups sit 32 banks apart, so the writes are free of bank conflicts
 #pragma unroll
-    for (int it = 0; it < (TREC ? 0 : V_IT); it += 2) {
+    for (int it = 0; it < V_IT; it += 2) {
       const int v = tid + (it >> 1) * kThreads;
       const int t = 2 * (v % (kC / 2)), c8 = (v / (kC / 2)) * 8;
       const bool col_ok = c8 < d_v;
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       for (int r = 0; r < 16; ++r) Tf[(16 * w + r) * kST + 16 * w + cc] = d[r];
     }
   } else {
-    for (int ix = tid - 4 * 64; ix < (TREC ? 0 : DK * (kC / 8)); ix += 4 * 64) {
+    for (int ix = tid - 4 * 64; ix < DK * (kC / 8); ix += 4 * 64) {
       const int i = ix % DK;
       const int t8 = (ix / DK) * 8;
       uint32_t wv[4];
@@ -491,35 +491,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   }
   __syncthreads();
 
-  // ================= 4. the record
-  if constexpr (TREC) {
-    // T', T'' and M blocks from LDS, then gam and exp(G_last - G)
-    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-    u32x4_t* fr = reinterpret_cast<u32x4_t*>(base);
-    const int g = lane >> 4, r = lane & 15;
-    for (int f = w; f < kTFrags; f += kWaves) {
-      const int mf = f % 6;
-      const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
-      const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
-      const bf16_t* row = (f < 6 ? Tp : (f < 12 ? Tpp : Ms)) + (16 * tt + r) * kSC;
-      const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * g);
-      const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * g);
-      const u32x4_t piece = {lo.x, lo.y, hi.x, hi.y};
-      if (nt_stores)
-        __builtin_nontemporal_store(piece, fr + f * 64 + lane);
-      else
-        fr[f * 64 + lane] = piece;
-    }
-    if (tid < 32) {
-      const f32x4 v4 = *reinterpret_cast<const f32x4*>((tid < 16 ? Gam : Kf) + 4 * (tid & 15));
-      f32x4* dst = reinterpret_cast<f32x4*>(base + kTRecTail) + tid;
-      if (nt_stores)
-        __builtin_nontemporal_store(v4, dst);
-      else
-        *dst = v4;
-    }
-  } else {
-    // W and U from MFMA accumulators, then diag(gam) Q, Kt^T and M from LDS
+  // ================= 4. the record: W and U from MFMA accumulators, then diag(gam) Q, Kt^T and M from LDS
+  {
     typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
     constexpr int KB = DK / 32;
     constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16), NF = frags_total(DK);
@@ -601,6 +574,331 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     if (tid == 0) *reinterpret_cast<float*>(base + rec.g) = Gam[kC - 1];
   }
   __syncthreads();  // the LDS is restaged for the next item
+  }
+}
+
+// ---------------------------------------------------------------- pass 1, small record
+// The preparation pass of the column-block state pass (T', T'' and M
+// record): four waves per workgroup and two workgroups per compute unit, so
+// that one's barriers and the latency of the substitution overlap the other's
+// products.  Two fit in the LDS because Q's rows hold the substitution's
+// scratch once M is formed.
+constexpr int kTWaves = 4;
+constexpr int kTThreads = 64 * kTWaves;
+
+template <int DK>
+struct TPrepLds {
+  static constexpr int SK = DK + 8;
+  static constexpr int kKs = 0;                      // K rows [C][SK] bf16
+  static constexpr int kQs = kKs + kC * SK * 2;      // Q rows [C][SK] bf16, later the scratch [4][16][20] f32
+  static constexpr int kAf = kQs + kC * SK * 2;      // A [C][SA] f32, later T' and T'' in bf16
+  static constexpr int kTf = kAf + kC * kSA * 4;     // T [C][ST] f32
+  static constexpr int kMs = kTf + kC * kST * 4;     // M [C][SC] bf16
+  static constexpr int kGd = kMs + kC * kSC * 2;     // G [C] f64
+  static constexpr int kGam = kGd + kC * 8;          // gam [C] f32
+  static constexpr int kBet = kGam + kC * 4;         // beta [C] f32
+  static constexpr int kKf = kBet + kC * 4;          // exp(G_last - G) [C] f32
+  static constexpr int kBytes = kKf + kC * 4;
+  static_assert(4 * 16 * 20 * 4 <= kC * SK * 2, "the scratch fits in Q's rows");
+  static_assert(2 * kC * kSC * 2 <= kC * kSA * 4, "T' and T'' fit in the A buffer");
+  static_assert(2 * kBytes <= 160 * 1024, "two workgroups per gfx950 compute unit");
+};
+
+// Persistent: the workgroups walk the (chunk, value head) items blockIdx.x,
+// + gridDim.x, ...; the next item's K and Q rows and gates are loaded into
+// registers while the current one computes.
+template <typename IO, int DK, bool RAW>
+__global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, unsigned char* ws, const int32_t* cs,
+                                                               const int2* __restrict__ info, int items) {
+  using L_ = TPrepLds<DK>;
+  constexpr int SK = L_::SK;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem + L_::kKs);
+  bf16_t* Qs = reinterpret_cast<bf16_t*>(smem + L_::kQs);
+  float* Xs = reinterpret_cast<float*>(smem + L_::kQs);
+  float* Af = reinterpret_cast<float*>(smem + L_::kAf);
+  bf16_t* Tp = reinterpret_cast<bf16_t*>(smem + L_::kAf);
+  bf16_t* Tpp = reinterpret_cast<bf16_t*>(smem + L_::kAf + kC * kSC * 2);
+  float* Tf = reinterpret_cast<float*>(smem + L_::kTf);
+  bf16_t* Ms = reinterpret_cast<bf16_t*>(smem + L_::kMs);
+  double* Gd = reinterpret_cast<double*>(smem + L_::kGd);
+  float* Gam = reinterpret_cast<float*>(smem + L_::kGam);
+  float* Bet = reinterpret_cast<float*>(smem + L_::kBet);
+  float* Kf = reinterpret_cast<float*>(smem + L_::kKf);
+
+  const int total = cs[p.num_seqs] * p.h_v;  // live items; the grid covers a bound
+  const int n_items = items < total ? items : total;
+  const int tid = static_cast<int>(threadIdx.x);
+  // wave-uniform, and the compiler is told so: branches on w must skip
+  // their MFMAs, which run whatever the execution mask
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, r = lane & 15;
+  const IO* qg = static_cast<const IO*>(p.q);
+  const IO* kg = static_cast<const IO*>(p.k);
+  const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
+
+  // item i is chunk c = i / h_v (first token, tokens from the chunk table), head h = i % h_v
+  struct Where {
+    int c, h, t0, Lc;
+  };
+  auto locate = [&](int item, int2 ci) __attribute__((always_inline)) {
+    Where at;
+    at.c = item / p.h_v;
+    at.h = item % p.h_v;
+    at.t0 = ci.x;
+    at.Lc = ci.y;
+    return at;
+  };
+  // unconditional (clamped) loads, so that no wait for them falls right after they are issued
+  auto info_of = [&](int item) __attribute__((always_inline)) { return info[min(item, n_items - 1) / p.h_v]; };
+
+  // ---- register staging of one item's K and Q rows and gate inputs
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int VPR = DK / 8;
+  constexpr int KQ_IT = kC * VPR / kTThreads;
+  static_assert(KQ_IT >= 1, "block shape");
+  u32x4_t rk[KQ_IT], rq[KQ_IT];
+  uint32_t rg = 0u, rbt = 0u;
+  float rAl = 0.0f, rdt = 0.0f;
+  auto fetch = [&](const Where& at) __attribute__((always_inline)) {
+    const int hq = at.h / p.ratio;
+#pragma unroll
+    for (int it = 0; it < KQ_IT; ++it) {
+      const int v = tid + it * kTThreads;
+      const int t = min(v / VPR, at.Lc - 1), c8 = (v % VPR) * 8;  // rows past the chunk: zeroed when staged
+      const size_t off = static_cast<size_t>(at.t0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
+      rk[it] = *reinterpret_cast<const u32x4_t*>(kg + off);
+      rq[it] = *reinterpret_cast<const u32x4_t*>(qg + off);
+    }
+    // gate inputs of token (chunk start + lane), clamped into the chunk
+    const int tl = at.t0 + min(lane, max(at.Lc - 1, 0));
+    const size_t gi = static_cast<size_t>(tl) * p.h_v + at.h;
+    const size_t bi = p.gates.beta_shared ? static_cast<size_t>(tl) : gi;
+    const IO* bsrc = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
+    const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : bsrc;
+    rg = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : bi];
+    rbt = reinterpret_cast<const uint16_t*>(bsrc)[bi];
+    if constexpr (RAW) {
+      rAl = p.gates.A_log[at.h];
+      rdt = p.gates.dt_bias[at.h];
+    }
+  };
+
+  // the upper tiles of M stay zero for every item
+  for (int e = tid; e < 6 * 256; e += kTThreads) {
+    const int tile = e >> 8;
+    const int tb = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+    const int cs_ = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+    const int t = 16 * tb + ((e & 255) >> 4), s = 16 * cs_ + (e & 15);
+    Ms[t * kSC + s] = 0;
+  }
+
+  // exp(G_t - G_s) for the accumulator tile (token tile tb, token tile cb), 0 where s > t;
+  // the lane's four rows are 16 tb + 4 g + i, read at once
+  auto tile_decay = [&](int tb, int cb) __attribute__((always_inline)) {
+    const int s_ = 16 * cb + acc_col(lane);
+    const int t0 = 16 * tb + acc_row(lane, 0);
+    const double Gs = Gd[s_];
+    const double2 ga = *reinterpret_cast<const double2*>(Gd + t0);
+    const double2 gb = *reinterpret_cast<const double2*>(Gd + t0 + 2);
+    const double gt[4] = {ga.x, ga.y, gb.x, gb.y};
+    f32x4 dec;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(static_cast<float>(gt[i] - Gs));  // selected away (even if infinite) where s > t
+      dec[i] = s_ <= t0 + i ? e : 0.0f;
+    }
+    return dec;
+  };
+  // product q of a workgroup's twenty: the diagonal tiles of A (q < 4), the
+  // tiles of A below them ((1,0) (2,0) (2,1) (3,0) (3,1) (3,2)), the lower
+  // tiles of M ((0,0) (1,0) (1,1) .. (3,3)); A with beta and the decay, M with the decay
+  auto product = [&](int q) __attribute__((always_inline)) {
+    int tb, cb;
+    bool is_a = true;
+    if (q < 4) {
+      tb = cb = q;
+    } else if (q < 10) {
+      const int a = q - 4;
+      tb = a < 1 ? 1 : (a < 3 ? 2 : 3);
+      cb = a - tb * (tb - 1) / 2;
+    } else {
+      const int m = q - 10;
+      tb = 0;
+      while ((tb + 1) * (tb + 2) / 2 <= m) ++tb;
+      cb = m - tb * (tb + 1) / 2;
+      is_a = false;
+    }
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = mma<DK>(acc, (is_a ? Ks : Qs) + 16 * tb * SK, SK, Ks + 16 * cb * SK, SK, lane);
+    const f32x4 dec = tile_decay(tb, cb);
+    const int s_ = 16 * cb + acc_col(lane);
+    const int t0 = 16 * tb + acc_row(lane, 0);
+    if (is_a) {
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + t0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = bt[i] * dec[i] * acc[i];
+        Af[(t0 + i) * kSA + s_] = (s_ < t0 + i) ? a : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ms[(t0 + i) * kSC + s_] = to_bf16(dec[i] * acc[i]);
+    }
+  };
+
+  // Blocks go round-robin over the 8 XCDs.  Where the grid allows, the ratio
+  // value heads of one (chunk, q/k head) go to blocks 8 apart, on one XCD,
+  // which run them at about the same time and read K and Q once through its L2.
+  int item = static_cast<int>(blockIdx.x);
+  {
+    const int R = p.ratio, G = static_cast<int>(gridDim.x);
+    if (R > 1 && G % (8 * R) == 0) {
+      const int xcd = item % 8, j = item / 8;
+      item = (j / R) * (8 * R) + xcd * R + j % R;
+    }
+  }
+  if (item >= n_items) return;
+  Where at = locate(item, info[item / p.h_v]);
+  fetch(at);
+  int2 next_info = info_of(item + static_cast<int>(gridDim.x));  // one item ahead of the fetch
+  for (; item < n_items; item += static_cast<int>(gridDim.x)) {
+    const int h = at.h;
+    const int Lc = at.Lc;
+    unsigned char* base = ws + (static_cast<size_t>(at.c) * p.h_v + h) * kTRecBytes;
+
+    // ================= 1. stage K and Q rows; gates and the prefix sum of the log-decay
+#pragma unroll
+    for (int it = 0; it < KQ_IT; ++it) {
+      const int v = tid + it * kTThreads;
+      const int t = v / VPR, c8 = (v % VPR) * 8;
+      const u32x4_t zero = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(Ks + t * SK + c8) = t < Lc ? rk[it] : zero;
+      *reinterpret_cast<u32x4_t*>(Qs + t * SK + c8) = t < Lc ? rq[it] : zero;
+    }
+    if (w == 0) {
+      float gv = 0.0f, b = 0.0f;
+      if (lane < Lc) {
+        if constexpr (RAW) {
+          gv = p.gates.decays ? gate_log_decay(widen_bits16<IO>(rg), rAl, rdt) : 0.0f;
+          b = gate_sigmoid(widen_bits16<IO>(rbt));
+        } else {
+          gv = p.gates.decays ? widen_bits16<IO>(rg) : 0.0f;
+          b = widen_bits16<IO>(rbt);
+        }
+        gv = fmaxf(gv, kMinLogDecay);
+      }
+      const double G = wave_prefix_sum(static_cast<double>(gv) * kLog2e, lane);
+      Gd[lane] = G;
+      Gam[lane] = fast_exp2(static_cast<float>(G));
+      Bet[lane] = b;
+      // the state-update factor exp(G_last - G_t); gates past the chunk's end
+      // are 0, so G_last is the prefix at the last lane
+      Kf[lane] = fast_exp2(static_cast<float>(__shfl(G, kC - 1) - G));
+    }
+    __syncthreads();
+
+    // ================= 2. the twenty tile products, five per wave, then the
+    // diagonal 16 x 16 block w of T = (I + A)^-1 by forward substitution (one
+    // column per lane; lanes 16-63 repeat lanes 0-15)
+#pragma unroll
+    for (int e = 0; e < 5; ++e) product(e == 0 ? w : 4 + 4 * w + (e - 1));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the diagonal block is in LDS for this wave's reads
+    __builtin_amdgcn_wave_barrier();
+    {
+      const int cc = lane & 15;
+      const float* Ab = Af + (16 * w) * kSA + 16 * w;
+      float d[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        float x0 = (rr == cc) ? 1.0f : 0.0f, x1 = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < rr; s2 += 2) {
+          x0 = fmaf(-Ab[rr * kSA + s2], d[s2], x0);
+          if (s2 + 1 < rr) x1 = fmaf(-Ab[rr * kSA + s2 + 1], d[s2 + 1], x1);
+        }
+        d[rr] = x0 + x1;
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) Tf[(16 * w + rr) * kST + 16 * w + cc] = d[rr];
+      }
+    }
+    // the next item's inputs, in flight while this one computes
+    {
+      const int next = item + static_cast<int>(gridDim.x);
+      if (next < n_items) {
+        at = locate(next, next_info);
+        fetch(at);
+        next_info = info_of(next + static_cast<int>(gridDim.x));
+      }
+    }
+    __syncthreads();
+
+    // ================= 3. the blocks of T below the diagonal, by block
+    // substitution: T_ij = -T_ii sum_{k = j .. i-1} A_ik T_kj
+    for (int dist = 1; dist < 4; ++dist) {
+      const int i = w + dist, j = w;
+      if (i < 4) {
+        f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k = j; k < i; ++k)
+          x = mma_f32(x, Af + (16 * i) * kSA + 16 * k, kSA, Tf + (16 * k) * kST + 16 * j, kST, lane);
+        float* xs = Xs + w * 16 * 20;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[acc_row(lane, e) * 20 + acc_col(lane)] = x[e];
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+        y = mma_f32(y, Tf + (16 * i) * kST + 16 * i, kST, xs, 20, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Tf[(16 * i + acc_row(lane, e)) * kST + 16 * j + acc_col(lane)] = -y[e];
+      }
+      __syncthreads();
+    }
+    // T' = T diag(beta gam) and T'' = T diag(beta) in bf16, lower triangle, four columns per thread
+    for (int e = tid; e < kC * kC / 4; e += kTThreads) {
+      const int t = e >> 4, s4 = (e & 15) * 4;
+      const f32x4 tv = *reinterpret_cast<const f32x4*>(Tf + t * kST + s4);
+      const f32x4 bs = *reinterpret_cast<const f32x4*>(Bet + s4);
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(Gam + s4);
+      uint32_t wp[2], wpp[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float a2[2], b2[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int c = 2 * h2 + k;
+          const float x = (s4 + c <= t) ? tv[c] : 0.0f;
+          b2[k] = x * bs[c];
+          a2[k] = b2[k] * gm[c];
+        }
+        wp[h2] = static_cast<uint32_t>(to_bf16(a2[0])) | (static_cast<uint32_t>(to_bf16(a2[1])) << 16);
+        wpp[h2] = static_cast<uint32_t>(to_bf16(b2[0])) | (static_cast<uint32_t>(to_bf16(b2[1])) << 16);
+      }
+      *reinterpret_cast<uint2*>(Tp + t * kSC + s4) = make_uint2(wp[0], wp[1]);
+      *reinterpret_cast<uint2*>(Tpp + t * kSC + s4) = make_uint2(wpp[0], wpp[1]);
+    }
+    __syncthreads();
+
+    // ================= 4. the record: T', T'' and M blocks, then gam and exp(G_last - G)
+    {
+      u32x4_t* fr = reinterpret_cast<u32x4_t*>(base);
+      for (int f = w; f < kTFrags; f += kTWaves) {
+        const int mf = f % 6;
+        const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
+        const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
+        const bf16_t* row = (f < 6 ? Tp : (f < 12 ? Tpp : Ms)) + (16 * tt + r) * kSC;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * g);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * g);
+        __builtin_nontemporal_store(u32x4_t{lo.x, lo.y, hi.x, hi.y}, fr + f * 64 + lane);
+      }
+      if (tid < 32) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>((tid < 16 ? Gam : Kf) + 4 * (tid & 15));
+        __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(base + kTRecTail) + tid);
+      }
+    }
+    __syncthreads();  // the LDS is restaged for the next item
   }
 }
 
@@ -1315,22 +1613,36 @@ int split_columns(int d_v, int units) {
 }
 
 
-template <typename IO, int DK, int DVT, bool TREC>
+template <typename IO, int DK, int DVT>
 hipError_t launch_prep(const ScanParams& p, unsigned char* ws, size_t rec_bytes, const int32_t* cs, const int2* info,
                        int items, int nt, hipStream_t stream) {
   constexpr int bytes = PrepLds<DK, DVT>::kBytes;
   const unsigned grid = static_cast<unsigned>(items < prep_workgroups() ? items : prep_workgroups());
   if (p.gates.raw) {
-    auto kern = chunk_prep_kernel<IO, DK, DVT, true, TREC>;
+    auto kern = chunk_prep_kernel<IO, DK, DVT, true>;
     hipError_t e = set_lds(kern, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
   } else {
-    auto kern = chunk_prep_kernel<IO, DK, DVT, false, TREC>;
+    auto kern = chunk_prep_kernel<IO, DK, DVT, false>;
     hipError_t e = set_lds(kern, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
   }
+  return hipGetLastError();
+}
+
+// The small-record preparation pass: two workgroups per compute unit.
+template <typename IO, int DK>
+hipError_t launch_trec(const ScanParams& p, unsigned char* ws, const int32_t* cs, const int2* info, int items,
+                       hipStream_t stream) {
+  constexpr int bytes = TPrepLds<DK>::kBytes;
+  const int slots = 2 * prep_workgroups();
+  const unsigned grid = static_cast<unsigned>(items < slots ? items : slots);
+  auto kern = p.gates.raw ? chunk_trec_kernel<IO, DK, true> : chunk_trec_kernel<IO, DK, false>;
+  hipError_t e = set_lds(kern, bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kTThreads), bytes, stream, p, ws, cs, info, items);
   return hipGetLastError();
 }
 
@@ -1346,8 +1658,8 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
     // Nontemporal record stores ahead of the column-block state pass (the
     // 8-sequence packed workload 1.07-1.08 against 1.09-1.10 ms); ahead of
     // the row-split pass they cost about 1 % (one 4096-token sequence).
-    const hipError_t e = rows ? launch_prep<IO, DK, DVT, false>(p, ws, rec_bytes, cs, info, items, 0, stream)
-                              : launch_prep<IO, DK, 8, true>(p, ws, rec_bytes, cs, info, items, 1, stream);
+    const hipError_t e = rows ? launch_prep<IO, DK, DVT>(p, ws, rec_bytes, cs, info, items, 0, stream)
+                              : launch_trec<IO, DK>(p, ws, cs, info, items, stream);
     if (e != hipSuccess) return e;
   }
   if (units == 0) return hipSuccess;
