@@ -399,6 +399,32 @@ def _timed(one, steps, warmup, flush=None):
     return sum(ms_list) / len(ms_list), ms_list[len(ms_list) // 2], wall
 
 
+def _timed_ab(one_a, one_b, steps, warmup, flush=None):
+    """_timed for two variants of the same work, their steps interleaved (a, b,
+    a, b, ...) so that clock and cache drift over the run falls on both alike."""
+    for _ in range(warmup):
+        one_a()
+        one_b()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = ([], [])
+    for _ in range(steps):
+        for i, one in enumerate((one_a, one_b)):
+            if flush is not None:
+                _flush(flush)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            one()
+            e1.record(stream)
+            times[i].append((e0, e1))
+    torch.cuda.synchronize()
+    out = []
+    for t in times:
+        ms_list = sorted(a.elapsed_time(b) for a, b in t)
+        out.append((sum(ms_list) / len(ms_list), ms_list[len(ms_list) // 2]))
+    return out
+
+
 def bench_conv(shape, steps, warmup, want_cpu):
     """gdn_causal_conv over packed sequences, or gdn_causal_conv_step for the
     one-token workload.  HBM-bound: x and y once, the states in and out once,
@@ -550,13 +576,12 @@ def bench_output_norm(name, steps, warmup, flush):
     pair_bytes = nbytes + 3 * o_bytes + scale.numel() * es        # + o read, gate read, y write
     if plan_norm != "fused" and plan_norm.get("norm") != "fused":
         fused_bytes = pair_bytes  # the plan runs the norm as its own pass: the pair's traffic
-    ms_f, med_f, _ = _timed(lambda: rec(norm_gate=gate, norm_scale=scale), steps, warmup, fl)
     o2 = out.view(T, -1)
 
     def pair():
         rec()
         gdn.gdn_gated_rmsnorm(o2, gate.view(T, -1), scale, y=o2)
-    ms_p, med_p, _ = _timed(pair, steps, warmup, fl)
+    (ms_f, med_f), (ms_p, med_p) = _timed_ab(lambda: rec(norm_gate=gate, norm_scale=scale), pair, steps, warmup, fl)
     return {"tokens": T, "fused": {"ms": round(ms_f, 6), "ms_median": round(med_f, 6), "plan": plan_norm,
                       "algorithmic_bytes": fused_bytes,
                       "hbm_frac": round(fused_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
