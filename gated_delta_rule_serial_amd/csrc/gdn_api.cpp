@@ -565,13 +565,13 @@ GDN_EXPORT gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t
     case GDN_FORM_CHUNKED_TWO_PASS:
       if (pl.norm == 1) {
         plan->state_workgroups = units8;
-        std::snprintf(k, kn, "chunk_table_kernel + chunk_prep_kernel + chunk_state_kernel (gated RMSNorm fused)");
+        std::snprintf(k, kn, "chunk_table_kernel + chunk_trec_kernel + chunk_state_kernel (gated RMSNorm fused)");
       } else if (gdn::split_takes_rows_kernel(p.d_k, p.d_v, units)) {
         plan->state_workgroups = units8 * ((p.d_v + 15) / 16);
         std::snprintf(k, kn, "chunk_table_kernel + chunk_prep_kernel + chunk_rows_kernel");
       } else {
         plan->state_workgroups = units8 * ((p.d_v + pl.cols - 1) / pl.cols);
-        std::snprintf(k, kn, "chunk_table_kernel + chunk_prep_kernel + chunk_state_kernel");
+        std::snprintf(k, kn, "chunk_table_kernel + chunk_trec_kernel + chunk_state_kernel");
       }
       break;
     case GDN_FORM_CHUNKED_F32:

@@ -360,6 +360,7 @@ def test_prefill_query_plan(lib):
     assert p["state_workgroups"] == 32 * 8
     p = q(16, 32, 128, 128, bf16, 8, 33173, workspace_bytes=ws)
     assert p["form"] == "chunked_two_pass" and p["kernels"].endswith("chunk_state_kernel")
+    assert "chunk_trec_kernel" in p["kernels"]  # the small record's preparation pass
     assert p["columns_per_block"] == 64
     p = q(16, 32, 128, 128, bf16, 8, 33173)
     assert p["form"] == "chunked_one_pass" and p["kernels"] == "chunk_kernel"

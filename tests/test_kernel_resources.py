@@ -46,7 +46,7 @@ def manifest(tmp_path_factory):
 
 def test_every_kernel_is_described(manifest):
     families = {libbuild.kernel_base_name(n) for n in manifest}
-    for k in ("decode_kernel", "scan_kernel", "scan_plain_kernel", "chunk_kernel", "chunk_prep_kernel",
+    for k in ("decode_kernel", "scan_kernel", "scan_plain_kernel", "chunk_kernel", "chunk_prep_kernel", "chunk_trec_kernel",
               "chunk_state_kernel", "chunk_rows_kernel", "chunk_table_kernel", "wide_prep_kernel",
               "wide_state_kernel", "gate_kernel", "conv_window_kernel", "conv_generic_kernel",
               "conv_state_kernel", "conv_step_kernel", "rmsnorm_kernel"):
