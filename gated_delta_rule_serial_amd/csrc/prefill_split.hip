@@ -16,16 +16,21 @@
 //     S  <- gam_last S + Kt^T D
 // carry the state S from chunk to chunk.
 //
-// Pass 1 (chunk_prep_kernel): one workgroup per (chunk, value head) computes
-// W, Kt^T, M, U and gam into a caller-provided workspace; all chunks of all
-// sequences run at once.  Pass 2 (chunk_state_kernel): one workgroup per
-// (sequence, value head, column block) walks its sequence's chunks, doing only
-// the four products above with the state in MFMA accumulators; for few units
-// at d_k = 128, chunk_rows_kernel splits each 16-column tile's state rows over
-// four waves instead.  The serial
-// chain per chunk shrinks from the whole chunked step to those four products,
-// and pass 1 fills the whole chip however few sequences and heads there are.
-// A chunk table (chunk_table_kernel) maps the packed sequences to chunks.
+// A chunk table (chunk_table_kernel) maps the packed sequences to chunks.  A
+// preparation pass then forms, for all chunks of all sequences at once, what
+// depends on one chunk alone, into a record per (chunk, value head) in a
+// caller-provided workspace; a state pass walks each sequence's chunks with
+// the state in MFMA accumulators.  The preparation pass fills the whole chip
+// however few sequences and heads there are, and the serial chain per chunk
+// shrinks to the products that involve S.  Two pairs of passes:
+//   - chunk_trec_kernel + chunk_state_kernel (one workgroup per (sequence,
+//     value head, block of 64 or 128 columns)): the record holds only T' =
+//     T diag(beta gam), T'' = T diag(beta), M, gam and exp(G_last - G); the
+//     state pass reads K, Q and V itself and forms U = T'' V, W S = T' (K S),
+//     diag(gam) Q S and Kt^T D = K^T diag(exp(G_last - G)) D;
+//   - chunk_prep_kernel + chunk_rows_kernel (few units at d_k = 128: each
+//     16-column tile's state rows split over four waves): the record holds W,
+//     diag(gam) Q, Kt^T, M, U and gam_last.
 #include <type_traits>
 
 #include "chunk_mfma.hpp"
