@@ -594,10 +594,11 @@ constexpr int kTThreads = 64 * kTWaves;
 template <int DK>
 struct TPrepLds {
   static constexpr int SK = DK + 8;
+  static constexpr int SA = kC + 4;                  // f32 row stride of A: 4 rows of a tile 16 banks apart
   static constexpr int kKs = 0;                      // K rows [C][SK] bf16
-  static constexpr int kQs = kKs + kC * SK * 2;      // Q rows [C][SK] bf16, later the scratch [4][16][20] f32
-  static constexpr int kAf = kQs + kC * SK * 2;      // A [C][SA] f32, later T' and T'' in bf16
-  static constexpr int kTf = kAf + kC * kSA * 4;     // T [C][ST] f32
+  static constexpr int kQs = kKs + kC * SK * 2;      // Q rows [C][SK] bf16, later the scratch [4][16][20] f32, then T''
+  static constexpr int kAf = kQs + kC * SK * 2;      // A [C][SA] f32, later T' in bf16
+  static constexpr int kTf = kAf + kC * SA * 4;      // T [C][ST] f32
   static constexpr int kMs = kTf + kC * kST * 4;     // M [C][SC] bf16
   static constexpr int kGd = kMs + kC * kSC * 2;     // G [C] f64
   static constexpr int kGam = kGd + kC * 8;          // gam [C] f32
@@ -605,7 +606,7 @@ struct TPrepLds {
   static constexpr int kKf = kBet + kC * 4;          // exp(G_last - G) [C] f32
   static constexpr int kBytes = kKf + kC * 4;
   static_assert(4 * 16 * 20 * 4 <= kC * SK * 2, "the scratch fits in Q's rows");
-  static_assert(2 * kC * kSC * 2 <= kC * kSA * 4, "T' and T'' fit in the A buffer");
+  static_assert(kC * kSC * 2 <= kC * SA * 4 && kC * kSC * 2 <= kC * SK * 2, "T' and T'' fit in the A and Q buffers");
   static_assert(2 * kBytes <= 160 * 1024, "two workgroups per gfx950 compute unit");
 };
 
@@ -621,9 +622,10 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
   bf16_t* Ks = reinterpret_cast<bf16_t*>(smem + L_::kKs);
   bf16_t* Qs = reinterpret_cast<bf16_t*>(smem + L_::kQs);
   float* Xs = reinterpret_cast<float*>(smem + L_::kQs);
+  constexpr int kSA = L_::SA;  // this kernel's stride of A
   float* Af = reinterpret_cast<float*>(smem + L_::kAf);
   bf16_t* Tp = reinterpret_cast<bf16_t*>(smem + L_::kAf);
-  bf16_t* Tpp = reinterpret_cast<bf16_t*>(smem + L_::kAf + kC * kSC * 2);
+  bf16_t* Tpp = reinterpret_cast<bf16_t*>(smem + L_::kQs);
   float* Tf = reinterpret_cast<float*>(smem + L_::kTf);
   bf16_t* Ms = reinterpret_cast<bf16_t*>(smem + L_::kMs);
   double* Gd = reinterpret_cast<double*>(smem + L_::kGd);
@@ -929,9 +931,16 @@ __device__ __forceinline__ s16x4 lds_read_tr(const bf16_t* ptr) {
 
 // LDS of the column-block state pass, per chunk buffer: the chunk's K and Q
 // rows (all d_k keys of the q/k head), its V rows over the block's columns
-// and its record.  Rows are stored as 16-byte pieces with piece c of row t at
-// position c ^ (t mod pieces per row), so that the column-wise reads below
-// spread over the banks.
+// and its record.  Rows are stored as 16-byte pieces, piece c of row t at
+// position c ^ row_swizzle(t).  The swizzle is a permutation of t's low four
+// bits (t1 t0 into bits 2-1, t2 into bit 0, t3 kept), so that both kinds of
+// read below touch distinct banks: 16 consecutive rows at one piece (the
+// operand rows of K and Q) and 4 consecutive rows at two neighbouring pieces
+// (the transposing reads).
+__device__ __forceinline__ int row_swizzle(int t, int pieces) {
+  return (((t & 3) << 1) | ((t >> 2) & 1) | (t & 8)) & (pieces - 1);
+}
+
 template <int DK, int SL>
 struct StateLds {
   static constexpr int NC = kStateWaves * 16 * SL;  // columns per workgroup
@@ -1070,12 +1079,12 @@ chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
     ld_row[e] = 0;
     if (e < EV) {
       const int s = 64 * (w + kStateWaves * (e < EQ ? e : e - EQ)) + lane;
-      const int t = s / CPK, c = (s % CPK) ^ (t % CPK);
+      const int t = s / CPK, c = (s % CPK) ^ row_swizzle(t, CPK);
       ld_row[e] = t;
       ld_off[e] = hq * DK + 8 * c;  // elements
     } else if (e < ER) {
       const int s = 64 * (w + kStateWaves * (e - EV)) + lane;
-      const int t = s / CPV, c = (s % CPV) ^ (t % CPV);
+      const int t = s / CPV, c = (s % CPV) ^ row_swizzle(t, CPV);
       ld_row[e] = t;
       ld_off[e] = h * d_v + min(cb * NC + 8 * c, d_v - 8);  // elements
     } else {
@@ -1109,7 +1118,7 @@ chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
   // and 32 kb + 16 + 4 g .. +3 (g = l / 16)
   auto rows_frag = [&](const bf16_t* X, int tt, int kb) __attribute__((always_inline)) {
     const int t = 16 * tt + (lane & 15);
-    const int sw = t % CPK;
+    const int sw = row_swizzle(t, CPK);
     const int c0 = 4 * kb + (g >> 1), half = 4 * (g & 1);
     const uint2 lo = *reinterpret_cast<const uint2*>(X + t * DK + 8 * (c0 ^ sw) + half);
     const uint2 hi = *reinterpret_cast<const uint2*>(X + t * DK + 8 * ((c0 + 2) ^ sw) + half);
@@ -1122,8 +1131,8 @@ chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
     const int col = col0 + 4 * (i & 3);
     const int c = col >> 3, half = col & 7;
     const int t0 = 32 * kb + 4 * g + (i >> 2);
-    const s16x4 a = lds_read_tr(X + t0 * row_elems + 8 * (c ^ (t0 % pieces)) + half);
-    const s16x4 b = lds_read_tr(X + (t0 + 16) * row_elems + 8 * (c ^ ((t0 + 16) % pieces)) + half);
+    const s16x4 a = lds_read_tr(X + t0 * row_elems + 8 * (c ^ row_swizzle(t0, pieces)) + half);
+    const s16x4 b = lds_read_tr(X + (t0 + 16) * row_elems + 8 * (c ^ row_swizzle(t0 + 16, pieces)) + half);
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     return __builtin_bit_cast(bf16x8, s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
   };
