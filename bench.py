@@ -17,9 +17,13 @@ events after a 1 GiB read that flushes the L2 and the Infinity Cache.  Each
 entry has its mean and median time, tokens/s, the plan the library reports,
 its own roofline and the oracle's CPU baseline.  Prints ONE JSON line.
 
---workload NAME times one workload alone (any prefill workload, or the
-block's neighbouring operations: conv_step_b64, conv_varlen_8seq,
-gated_rmsnorm_t33173), for profiling.
+The line also carries the block's neighbouring operations fused into the
+recurrence against their unfused pairs: "output_norm" (the gated RMSNorm
+epilogue) and "decode_conv" (the conv step as the decode step's prologue).
+
+--workload NAME times one workload alone (any prefill workload, the block's
+neighbouring operations conv_step_b64, conv_varlen_8seq, gated_rmsnorm_t33173,
+or the fused pairs output_norm and decode_conv), for profiling.
 
 CPU baseline: the oracle's float32 build (the same C source with a float32
 working state, gcc -O3 -march=native, OpenMP over independent (sequence,
@@ -590,6 +594,73 @@ def bench_output_norm(name, steps, warmup, flush):
             "saved_ms": round(ms_p - ms_f, 6), "saved_bytes": pair_bytes - fused_bytes}
 
 
+def bench_decode_conv(steps, warmup):
+    """The decode step fed by the block's conv (gdn_decode_step_conv: the conv
+    step and the decode step in one launch) against the unfused pair
+    (gdn_causal_conv_step writing y, then gdn_decode_step), at the decode
+    workload (B = 64, H 16/32, d 128, bf16) and its conv (8192 channels, 4
+    taps, silu).  The pair's decode reads q, k, v buffers of y's size: the
+    split of y into them is not charged to it.  Each form runs `steps` steps
+    back to back between events, in four alternating blocks, and the
+    recurrent state rotates over 4 buffers as in the headline; the fused form
+    alternates its two conv-state buffers.  Algorithmic bytes: the fused call
+    reads x, the carried inputs, taps and bias in place of q, k and v; the
+    pair adds y's write and its read as q, k, v."""
+    dev = "cuda"
+    shape = synth.BY_NAME["decode_b64"]
+    inp = synth.generate(shape)
+    cin = synth.generate_conv(synth.CONV_BY_NAME["conv_step_b64"])
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    g, beta = gdn.gate_prologue(inp.a.to(dev), inp.b.to(dev), inp.A_log.to(dev), inp.dt_bias.to(dev))
+    states = [inp.initial_state.to(dev).clone() for _ in range(DECODE_STATE_BUFFERS)]
+    out = torch.empty(shape.num_seqs, shape.h_v, shape.d_v, dtype=shape.io_dtype, device=dev)
+    x, w, bias = cin.x.to(dev), cin.weight.to(dev), cin.bias.to(dev)
+    cs = [cin.initial_state.to(dev).clone() for _ in range(2)]
+    y = torch.empty_like(x)
+    it = [0]
+
+    def fused():
+        i = it[0] = it[0] + 1
+        gdn.gdn_decode_step_conv(x, w, cs[i % 2], cs[1 - i % 2], states[i % len(states)], out, h_qk=shape.h_qk,
+                                 d_k=shape.d_k, conv_bias=bias, g=g, beta=beta)
+
+    def pair():
+        i = it[0] = it[0] + 1
+        gdn.gdn_causal_conv_step(x, w, cs[0], y=y, bias=bias)
+        gdn.gdn_decode_step(q, k, v, states[i % len(states)], out, g=g, beta=beta)
+
+    def block(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for fn in (fused, pair):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    tf, tp = [], []
+    for _ in range(4):
+        tf.append(block(fused, steps))
+        tp.append(block(pair, steps))
+    ms_f, ms_p = sum(tf) / len(tf), sum(tp) / len(tp)
+    es = x.element_size()
+    rec = algorithmic_bytes(shape, inp)                   # state in/out, q, k, v, gates, out
+    qkv = x.numel() * es
+    conv_extra = 2 * cs[0].numel() * es + (w.numel() + bias.numel()) * es   # carried inputs in/out, taps
+    fused_bytes = rec + conv_extra                        # x (the size of q, k, v) read in their place
+    pair_bytes = rec + 2 * qkv + conv_extra               # + the conv's x read and y write
+    return {"fused": {"us": round(ms_f * 1e3, 3), "algorithmic_bytes": fused_bytes,
+                      "hbm_frac": round(fused_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "unfused_pair": {"us": round(ms_p * 1e3, 3), "algorithmic_bytes": pair_bytes,
+                             "hbm_frac": round(pair_bytes / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "saved_us": round((ms_p - ms_f) * 1e3, 3), "saved_bytes": pair_bytes - fused_bytes,
+            "steps_per_block": steps, "blocks": 4}
+
+
 def bench_copy(mib, steps, warmup):
     """A plain device copy of known size (dst.copy_(src), mib MiB each way): the
     reference kernel that scales the rocprofv3 HBM byte counters."""
@@ -616,7 +687,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "output_norm"] + sorted(synth.BY_NAME) + sorted(synth.CONV_BY_NAME) +
+                    choices=["all", "output_norm", "decode_conv"] + sorted(synth.BY_NAME) + sorted(synth.CONV_BY_NAME) +
                     sorted(synth.NORM_BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algorithm", default="auto", choices=["auto", "serial", "chunked"],
@@ -653,6 +724,12 @@ def main():
         e = res["packed_16x2048"]
         line = {"metric": METRIC, "value": round(e["tokens"] / (e["fused"]["ms"] * 1e-3), 1),
                 "unit": "tokens/s", "ms_per_step": e["fused"]["ms"], "output_norm": res}
+    elif args.workload == "decode_conv":
+        steps = args.steps if args.steps is not None else 250
+        warmup = args.warmup if args.warmup is not None else 20
+        e = bench_decode_conv(steps, warmup)
+        line = {"metric": METRIC, "value": round(64 / (e["fused"]["us"] * 1e-6), 1), "unit": "tokens/s",
+                "ms_per_step": round(e["fused"]["us"] * 1e-3, 6), "decode_conv": e}
     elif args.workload in ("all", "decode_b64"):
         steps = args.steps if args.steps is not None else 1000
         warmup = args.warmup if args.warmup is not None else 50
@@ -675,6 +752,11 @@ def main():
                 line["output_norm"][name] = e
                 print(f"{name} + norm: fused {e['fused']['ms']} ms, pair {e['unfused_pair']['ms']} ms",
                       file=sys.stderr, flush=True)
+            # the block's conv feeding the decode step: fused prologue against the unfused pair
+            e = bench_decode_conv(min(steps, 250), min(warmup, 20))
+            line["decode_conv"] = e
+            print(f"decode_b64 + conv: fused {e['fused']['us']} us, pair {e['unfused_pair']['us']} us",
+                  file=sys.stderr, flush=True)
     else:
         shape = synth.BY_NAME[args.workload]
         steps = args.steps if args.steps is not None else 10

@@ -25,6 +25,18 @@
 // then writes its tile.  The state traffic (read + write once) is the
 // kernel's HBM cost; it uses non-temporal 16-byte accesses, since no state
 // byte is reused.
+//
+// With the conv prologue (CONV), q, k and v are not read: they are the
+// outputs of the causal depthwise conv (and silu) over one token row x = [q |
+// k | v] and the carried inputs of each channel, z = bias + sum_j w_j xp_j
+// with the last tap on x ([P1] `causal_conv_op` with a one-token time axis).
+// Each is rounded to the I/O dtype, as the conv would store it, and then
+// widened: the result is that of the conv step followed by the decode step.
+// The workgroup computes the 2 d_k q and k channels of its head once (one per
+// thread) and shares them through LDS; the first BC threads compute their own
+// v column.  The shifted carried inputs go to a second buffer, written for a
+// q/k channel by the head group's first workgroup and for a v channel by the
+// workgroup that owns its column.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -36,20 +48,72 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kColsPerThread = 4;
 
+// One conv channel of one token: its input, up to three carried inputs, its
+// taps and bias.  The loads are unconditional (indices clamped into the
+// buffers, x standing in for absent ones), so that they issue as one batch
+// with no branch and one wait covers them.
+template <typename IO>
+struct ConvChannel {
+  static constexpr int kMaxTaps = 4;
+  IO x, s[kMaxTaps - 1], w[kMaxTaps], bias;
+
+  __device__ __forceinline__ void load(const ConvPrologue& cv, int b, int ch) {
+    const int C = cv.channels, K = cv.ksize, carry = K - 1;
+    const IO* xp = static_cast<const IO*>(cv.x) + static_cast<size_t>(b) * C + ch;
+    const IO* st = carry > 0 ? static_cast<const IO*>(cv.state) + static_cast<size_t>(b) * carry * C + ch : xp;
+    const IO* wt = static_cast<const IO*>(cv.weight) + static_cast<size_t>(ch) * K;
+    const IO* bp = cv.bias != nullptr ? static_cast<const IO*>(cv.bias) + ch : xp;
+    x = *xp;
+#pragma unroll
+    for (int j = 0; j < kMaxTaps - 1; ++j) s[j] = st[static_cast<size_t>(min(j, max(carry - 1, 0))) * C];
+#pragma unroll
+    for (int j = 0; j < kMaxTaps; ++j) w[j] = wt[min(j, K - 1)];
+    bias = *bp;
+  }
+
+  // z = bias + sum_j w_j xp_j in tap order (the last tap meets x), then silu,
+  // rounded to IO and widened back
+  __device__ __forceinline__ float out(const ConvPrologue& cv) const {
+    const int K = cv.ksize;
+    float z = cv.bias != nullptr ? widen(bias) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxTaps; ++j)
+      if (j < K) z = fmaf(widen(w[j]), j == K - 1 ? widen(x) : widen(s[j < kMaxTaps - 1 ? j : 0]), z);
+    if (cv.silu) z = z * fast_sigmoid(z);
+    IO r;
+    narrow_store(&r, z);
+    return widen(r);
+  }
+
+  // the carried inputs one token later: rows 1 .. K - 2, then x
+  __device__ __forceinline__ void keep(const ConvPrologue& cv, int b, int ch) const {
+    const int C = cv.channels, carry = cv.ksize - 1;
+    IO* st = static_cast<IO*>(cv.state_out) + static_cast<size_t>(b) * carry * C + ch;
+#pragma unroll
+    for (int j = 0; j + 1 < kMaxTaps - 1; ++j)
+      if (j + 1 < carry) st[static_cast<size_t>(j) * C] = s[j + 1];
+    if (carry > 0) st[static_cast<size_t>(carry - 1) * C] = x;
+  }
+};
+
 // BC: state columns per workgroup (64 or 128).  FULL: d_k == DK and d_v a
 // multiple of BC, so every thread's tile lies inside the state and the
 // accesses need no masks.  NORM: the workgroup owns the whole output row
 // (d_v <= BC) and writes the gated RMSNorm of o instead of o: each wave sums
 // o^2 over its 64 columns with DPP, the partials meet in LDS at the barrier
-// that publishes delta, and the first BC threads store y.
-template <typename IO, int DK, int BC, bool PERKEY, bool FULL, bool NORM>
+// that publishes delta, and the first BC threads store y.  CONV: the inputs
+// come through the conv prologue (FULL shapes with a per-head decay only).
+template <typename IO, int DK, int BC, bool PERKEY, bool FULL, bool NORM, bool CONV>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   constexpr int kColThreads = BC / kColsPerThread;
   constexpr int kRowGroups = kThreads / kColThreads;
   constexpr int kBlockCols = BC;
   constexpr int RPT = DK / kRowGroups;
   static_assert(RPT >= 1 && RPT * kRowGroups == DK, "row groups must tile d_k");
+  static_assert(!CONV || (FULL && !PERKEY), "the conv prologue serves whole tiles with a per-head decay");
+  constexpr int kConvQK = CONV ? (2 * DK + kThreads - 1) / kThreads : 0;  // q/k channels per thread
   __shared__ float red_a[kWaves][kBlockCols];
+  __shared__ float sh_qk[CONV ? 2 * DK : 1];
   __shared__ float red_c[kWaves][kBlockCols];
   __shared__ float red_kq[kWaves];
   __shared__ float sh_delta[kBlockCols];
@@ -71,8 +135,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int sidx = state_slot(p.slots, p.num_slots, b, &has_state);
   float* __restrict__ Sg = p.state + (static_cast<size_t>(sidx) * p.h_v + h) * static_cast<size_t>(d_k) * d_v;
 
-  // ---- state tile (issued first: it is the long-latency traffic); a padding
-  //      slot starts from zeros
+  // ---- conv prologue inputs (CONV), then its gate inputs, issued ahead of the
+  //      state tile in one batch with no branch: a load under a branch is
+  //      waited for where the branch joins, so every index is clamped into its
+  //      buffer (x stands in for an absent one) and unused values are dropped
+  ConvChannel<IO> cqk[kConvQK > 0 ? kConvQK : 1], cv_v;
+  IO beta_c{}, g_c{};
+  if constexpr (CONV) {
+#pragma unroll
+    for (int u = 0; u < kConvQK; ++u) {
+      const int c = min(tid + u * kThreads, 2 * DK - 1);  // past 2 d_k: loaded, not used
+      cqk[u].load(p.conv, b, (c < DK ? hq : p.h_qk + hq - 1) * DK + c);
+    }
+    cv_v.load(p.conv, b, 2 * p.h_qk * DK + h * d_v + cb * kBlockCols + tid % kBlockCols);
+    const IO* x0 = static_cast<const IO*>(p.conv.x);
+    const size_t gi = static_cast<size_t>(b) * p.h_v + h;
+    const bool dl = p.gates.deltas != 0, dc = p.gates.decays != 0;
+    beta_c = (dl ? static_cast<const IO*>(p.gates.raw ? p.gates.b : p.gates.beta) : x0)
+        [dl ? (p.gates.beta_shared ? static_cast<size_t>(b) : gi) : 0];
+    g_c = (dc ? static_cast<const IO*>(p.gates.raw ? p.gates.a : p.gates.g) : x0)[dc ? gi : 0];
+  }
+
+  // ---- state tile (the plain kernel issues it first: it is the long-latency
+  //      traffic); a padding slot starts from zeros
   float S[RPT][kColsPerThread];
   if (!has_state) {
 #pragma unroll
@@ -97,16 +182,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
   }
 
-  // ---- k, q rows of this thread
-  const IO* kq_base_k = static_cast<const IO*>(p.k) + (static_cast<size_t>(b) * p.h_qk + hq) * d_k + row0;
-  const IO* kq_base_q = static_cast<const IO*>(p.q) + (static_cast<size_t>(b) * p.h_qk + hq) * d_k + row0;
+  // ---- conv outputs (while the tile is in flight): q and k of the head to
+  //      LDS, this thread's v column to a register; then the carried inputs,
+  //      one token later, to conv.state_out
+  float v_conv = 0.0f;
+  if constexpr (CONV) {
+    float zqk[kConvQK > 0 ? kConvQK : 1];
+#pragma unroll
+    for (int u = 0; u < kConvQK; ++u) zqk[u] = cqk[u].out(p.conv);
+    v_conv = cv_v.out(p.conv);
+#pragma unroll
+    for (int u = 0; u < kConvQK; ++u)
+      if (tid + u * kThreads < 2 * DK) sh_qk[tid + u * kThreads] = zqk[u];
+    if (cb == 0 && h == hq * p.ratio) {  // the head group's first workgroup keeps q and k
+#pragma unroll
+      for (int u = 0; u < kConvQK; ++u) {
+        const int c = tid + u * kThreads;
+        if (c < 2 * DK) cqk[u].keep(p.conv, b, (c < DK ? hq : p.h_qk + hq - 1) * DK + c);
+      }
+    }
+    if (tid < kBlockCols) cv_v.keep(p.conv, b, 2 * p.h_qk * DK + h * d_v + cb * kBlockCols + tid);
+  }
+
+  // ---- k, q rows of this thread (from LDS with the conv prologue, below)
   RawSlice<IO, RPT> rk, rq;
-  if (FULL || d_k == DK) {
-    rk.load(kq_base_k);
-    rq.load(kq_base_q);
-  } else {
-    rk.load_masked(kq_base_k, d_k - row0);
-    rq.load_masked(kq_base_q, d_k - row0);
+  if constexpr (!CONV) {
+    const IO* kq_base_k = static_cast<const IO*>(p.k) + (static_cast<size_t>(b) * p.h_qk + hq) * d_k + row0;
+    const IO* kq_base_q = static_cast<const IO*>(p.q) + (static_cast<size_t>(b) * p.h_qk + hq) * d_k + row0;
+    if (FULL || d_k == DK) {
+      rk.load(kq_base_k);
+      rq.load(kq_base_q);
+    } else {
+      rk.load_masked(kq_base_k, d_k - row0);
+      rq.load_masked(kq_base_q, d_k - row0);
+    }
   }
 
   // ---- the norm's gate and scale of this thread's output column (the first
@@ -124,7 +233,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const size_t gidx = static_cast<size_t>(b) * p.h_v + h;
   const bool decays = p.gates.decays != 0, deltas = p.gates.deltas != 0;
   float beta = 0.0f;
-  if (deltas) {
+  if constexpr (CONV) {
+    if (deltas) beta = p.gates.raw ? gate_sigmoid(widen(beta_c)) : widen(beta_c);
+  } else if (deltas) {
     const size_t bi = p.gates.beta_shared ? static_cast<size_t>(b) : gidx;
     if (p.gates.raw) beta = gate_sigmoid(widen(static_cast<const IO*>(p.gates.b)[bi]));
     else beta = widen(static_cast<const IO*>(p.gates.beta)[bi]);
@@ -150,7 +261,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
   } else if (decays) {
     float lg;
-    if (p.gates.raw)
+    if constexpr (CONV)
+      lg = p.gates.raw ? gate_log_decay(widen(g_c), p.gates.A_log[h], p.gates.dt_bias[h]) : widen(g_c);
+    else if (p.gates.raw)
       lg = gate_log_decay(widen(static_cast<const IO*>(p.gates.a)[gidx]), p.gates.A_log[h], p.gates.dt_bias[h]);
     else
       lg = widen(static_cast<const IO*>(p.gates.g)[gidx]);
@@ -158,8 +271,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 
   float kf[RPT], qf[RPT];
-  rk.widen_to(kf);
-  rq.widen_to(qf);
+  if constexpr (CONV) {
+    __syncthreads();  // q and k of the head are in LDS
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      qf[m] = sh_qk[row0 + m];
+      kf[m] = sh_qk[DK + row0 + m];
+    }
+  } else {
+    rk.widen_to(kf);
+    rq.widen_to(qf);
+  }
   // the decayed state's retrieval and readout sums: (diag(alpha) S)^T x = S^T (alpha x)
   float ka[PERKEY ? RPT : 1], qa[PERKEY ? RPT : 1];
   if constexpr (PERKEY) {
@@ -222,7 +344,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     const int j = cb * kBlockCols + tid;
     float vv = 0.0f;
-    if (FULL || j < d_v) vv = widen(static_cast<const IO*>(p.v)[(static_cast<size_t>(b) * p.h_v + h) * d_v + j]);
+    if constexpr (CONV) vv = v_conv;
+    else if (FULL || j < d_v) vv = widen(static_cast<const IO*>(p.v)[(static_cast<size_t>(b) * p.h_v + h) * d_v + j]);
     const float delta = deltas ? beta * (vv - a) : vv;
     sh_delta[tid] = delta;
     if constexpr (NORM) {
@@ -254,10 +377,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = row0 + m;
+    // with the conv prologue k is read from LDS again: the registers it held
+    // are not kept across the barriers
+    const float km = CONV ? sh_qk[DK + row0 + m] : kf[m];
     float o4[kColsPerThread];
 #pragma unroll
     for (int cc = 0; cc < kColsPerThread; ++cc)
-      o4[cc] = fmaf(S[m][cc], PERKEY ? alpha_r[PERKEY ? m : 0] : alpha, kf[m] * dl[cc]);
+      o4[cc] = fmaf(S[m][cc], PERKEY ? alpha_r[PERKEY ? m : 0] : alpha, km * dl[cc]);
     if (!has_state) {
       // padding slot: the updated state is discarded
     } else if (FULL || (i < d_k && vec_cols)) {
@@ -270,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <typename IO, int DK, int BC, bool PERKEY, bool FULL, bool NORM>
+template <typename IO, int DK, int BC, bool PERKEY, bool FULL, bool NORM, bool CONV = false>
 hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
   // grid: (column block, value head, sequence); the sequence axis is split
   // into launches of at most 65535
@@ -278,7 +404,7 @@ hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
   for (int off = 0; off < p.batch; off += kMaxZ) {
     p.b_offset = off;
     const unsigned nz = static_cast<unsigned>(p.batch - off < kMaxZ ? p.batch - off : kMaxZ);
-    hipLaunchKernelGGL((decode_kernel<IO, DK, BC, PERKEY, FULL, NORM>),
+    hipLaunchKernelGGL((decode_kernel<IO, DK, BC, PERKEY, FULL, NORM, CONV>),
                        dim3(static_cast<unsigned>(p.col_blocks), static_cast<unsigned>(p.h_v), nz),
                        dim3(kThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
@@ -290,6 +416,11 @@ hipError_t launch_grid(DecodeParams p, hipStream_t stream) {
 template <typename IO, int DK, int BC, bool NORM>
 hipError_t launch_norm(const DecodeParams& p, hipStream_t stream) {
   const bool full = p.d_k == DK && p.d_v % BC == 0;
+  if (p.conv.x != nullptr) {
+    // the API admits the conv prologue for whole tiles with a per-head decay only
+    if (!full || (p.gates.per_key && p.gates.decays)) return hipErrorInvalidValue;
+    return launch_grid<IO, DK, BC, false, true, NORM, true>(p, stream);
+  }
   if constexpr (BC == 64) {
     if (p.gates.per_key && p.gates.decays)
       return full ? launch_grid<IO, DK, BC, true, true, NORM>(p, stream)
@@ -335,6 +466,11 @@ int decode_columns_per_block(int d_k, int d_v, bool per_key) {
 }
 
 bool decode_fuses_norm(int d_k, int d_v, bool per_key) { return d_v <= decode_columns_per_block(d_k, d_v, per_key); }
+
+bool decode_takes_conv(int d_k, int d_v, bool per_key) {
+  const bool dk_bucket = d_k == 16 || d_k == 32 || d_k == 64 || d_k == 128 || d_k == 256;
+  return dk_bucket && !per_key && d_v % decode_columns_per_block(d_k, d_v, per_key) == 0;
+}
 
 hipError_t launch_decode_step(DecodeParams p, int io_dtype, hipStream_t stream) {
   if (io_dtype == 1) return launch_io<bf16_t>(p, stream);

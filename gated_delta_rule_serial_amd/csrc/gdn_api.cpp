@@ -399,8 +399,11 @@ GDN_EXPORT gdn_status gdn_prefill_slots(const gdn_problem* problem, int32_t num_
 
 namespace {
 
+// conv: the conv prologue (its x, states, taps and channels already checked
+// by the caller; then q, k and v are NULL), or NULL.
 gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch, const void* q, const void* k,
-                       const void* v, float* state, void* out, const SlotArgs* pool, hipStream_t stream) {
+                       const void* v, float* state, void* out, const SlotArgs* pool, hipStream_t stream,
+                       const gdn::ConvPrologue* conv = nullptr) {
   gdn_status st = check_problem(problem, fn, batch > 0);
   if (st != GDN_OK) return st;
   if (batch < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: batch=%d is negative", fn, batch);
@@ -411,8 +414,11 @@ gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch
   }
   // an empty pool (every sequence padding) needs no state buffer
   const bool needs_state = !(pool && pool->num_slots == 0);
-  if (!q || !k || !v || !out || (needs_state && !state))
+  if (conv) {
+    if (!out || !state) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state and out are required", fn);
+  } else if (!q || !k || !v || !out || (needs_state && !state)) {
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, state and out are required", fn);
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(out))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, state and out must be 16-byte aligned", fn);
   const gdn_problem& p = *problem;
@@ -422,6 +428,23 @@ gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch
   const size_t out_bytes = static_cast<size_t>(batch) * p.h_v * p.d_v * es;
   const size_t qk_bytes = static_cast<size_t>(batch) * p.h_qk * p.d_k * es;
   const size_t v_bytes = static_cast<size_t>(batch) * p.h_v * p.d_v * es;
+  if (conv) {
+    // every buffer the conv prologue reads or writes against out and the state
+    const size_t x_bytes = static_cast<size_t>(batch) * conv->channels * es;
+    const size_t cs_bytes = static_cast<size_t>(batch) * (conv->ksize - 1) * conv->channels * es;
+    const size_t w_bytes = static_cast<size_t>(conv->channels) * conv->ksize * es;
+    const size_t b_bytes = static_cast<size_t>(conv->channels) * es;
+    const void* ins[4] = {conv->x, conv->state, conv->weight, conv->bias};
+    const size_t in_bytes[4] = {x_bytes, cs_bytes, w_bytes, b_bytes};
+    for (int i = 0; i < 4; ++i) {
+      if (overlaps(out, out_bytes, ins[i], in_bytes[i]) || overlaps(state, state_bytes, ins[i], in_bytes[i]) ||
+          overlaps(conv->state_out, cs_bytes, ins[i], in_bytes[i]))
+        return fail(GDN_ERR_INVALID_ARGUMENT,
+                    "%s: out, state and conv_state_out must not overlap x, conv_state, weight or bias", fn);
+    }
+    if (overlaps(conv->state_out, cs_bytes, out, out_bytes) || overlaps(conv->state_out, cs_bytes, state, state_bytes))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: conv_state_out overlaps out or the state", fn);
+  }
   if (overlaps(out, out_bytes, state, state_bytes) || overlaps(out, out_bytes, q, qk_bytes) ||
       overlaps(out, out_bytes, k, qk_bytes) || overlaps(out, out_bytes, v, v_bytes))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: out overlaps the state or an input", fn);
@@ -448,6 +471,14 @@ gdn_status decode_impl(const char* fn, const gdn_problem* problem, int32_t batch
   const int cpb = gdn::decode_columns_per_block(p.d_k, p.d_v, per_key);
   dp.col_blocks = (p.d_v + cpb - 1) / cpb;
   dp.scale = resolved_scale(problem);
+  if (conv) {
+    if (!gdn::decode_takes_conv(p.d_k, p.d_v, per_key))
+      return fail(GDN_ERR_UNSUPPORTED,
+                  "%s: the conv prologue serves d_k in {16, 32, 64, 128, 256}, d_v a multiple of %d and a "
+                  "per-head decay (d_k=%d, d_v=%d%s); run gdn_causal_conv_step, then gdn_decode_step",
+                  fn, cpb, p.d_k, p.d_v, per_key ? ", per-key decay" : "");
+    dp.conv = *conv;
+  }
   if (p.h_v > 65535)
     return fail(GDN_ERR_UNSUPPORTED, "%s: h_v = %d exceeds the grid's head axis (65535)", fn, p.h_v);
   if (overlaps(p.norm_gate, out_bytes, out, out_bytes) || overlaps(p.norm_scale, p.d_v * es, out, out_bytes))
@@ -810,6 +841,48 @@ GDN_EXPORT gdn_status gdn_causal_conv_step_slots(const gdn_conv_problem* problem
   sl.slots_host = slots_host;
   sl.num_slots = num_slots;
   return conv_step_impl("gdn_causal_conv_step_slots", problem, batch, x, state_pool, y, &sl, stream);
+}
+
+GDN_EXPORT gdn_status gdn_decode_step_conv(const gdn_problem* problem, const gdn_conv_problem* conv, int32_t batch,
+                                           const void* x, const void* conv_state, void* conv_state_out, float* state,
+                                           void* out, hipStream_t stream) {
+  const char* fn = "gdn_decode_step_conv";
+  gdn_status st = check_conv(conv, fn);
+  if (st != GDN_OK) return st;
+  if (!problem) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: problem is NULL", fn);
+  const gdn_conv_problem& c = *conv;
+  if (c.io_dtype != problem->io_dtype)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: the conv's io_dtype %d differs from the problem's %d", fn, c.io_dtype,
+                problem->io_dtype);
+  const int64_t want = 2 * static_cast<int64_t>(problem->h_qk) * problem->d_k +
+                       static_cast<int64_t>(problem->h_v) * problem->d_v;
+  if (c.channels != want)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: channels=%d must be 2 h_qk d_k + h_v d_v = %lld", fn, c.channels,
+                static_cast<long long>(want));
+  if (c.dilation != 1 || c.kernel_size > 4)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "%s: the conv prologue serves dilation 1 and kernel_size <= 4 (got %d, %d); run "
+                "gdn_causal_conv_step, then gdn_decode_step",
+                fn, c.dilation, c.kernel_size);
+  if (batch < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: batch=%d is negative", fn, batch);
+  const bool carries = c.kernel_size > 1;
+  if (batch > 0 && (!x || !c.weight || (carries && (!conv_state || !conv_state_out))))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, weight, conv_state and conv_state_out are required", fn);
+  if (!aligned16(x) || !aligned16(conv_state) || !aligned16(conv_state_out))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, conv_state and conv_state_out must be 16-byte aligned", fn);
+  const size_t cs_bytes = static_cast<size_t>(batch) * (c.kernel_size - 1) * c.channels * io_size(c.io_dtype);
+  if (overlaps(conv_state_out, cs_bytes, conv_state, cs_bytes))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: conv_state_out overlaps conv_state (it cannot be updated in place)", fn);
+  gdn::ConvPrologue cp{};
+  cp.x = x;
+  cp.state = carries ? conv_state : nullptr;
+  cp.state_out = carries ? conv_state_out : nullptr;
+  cp.weight = c.weight;
+  cp.bias = c.bias;
+  cp.channels = c.channels;
+  cp.ksize = c.kernel_size;
+  cp.silu = c.activation == GDN_ACT_SILU;
+  return decode_impl(fn, problem, batch, nullptr, nullptr, nullptr, state, out, nullptr, stream, &cp);
 }
 
 GDN_EXPORT gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t width, int32_t group, int32_t io_dtype, const void* x,

@@ -58,6 +58,24 @@ struct ScanParams {
   NormEpilogue norm;      // the two-pass chunked form applies it when norm.gate != null
 };
 
+// Causal depthwise conv in front of the decode step: the step's q, k and v
+// are the conv outputs of one token row x = [q | k | v] of C = 2 h_qk d_k +
+// h_v d_v channels (dilation 1, K <= 4 taps).  Every output is narrowed to
+// the I/O dtype, as a separate conv step would store it, before the
+// recurrence reads it.  The carried inputs are read from `state` and the
+// shifted ones written to `state_out` (they may not overlap: several
+// workgroups read one q/k channel's carried inputs).
+struct ConvPrologue {
+  const void* x;          // [B, C] io dtype; null: no conv (q, k, v given)
+  const void* state;      // [B, K - 1, C] io dtype (K > 1)
+  void* state_out;        // [B, K - 1, C] io dtype (K > 1)
+  const void* weight;     // [C, K] io dtype
+  const void* bias;       // [C] io dtype or null
+  int32_t channels;       // C
+  int32_t ksize;          // K, 1 .. 4
+  int32_t silu;
+};
+
 // One decode token per sequence, state updated in place.
 struct DecodeParams {
   const void* q;          // [B, h_qk, d_k]
@@ -75,6 +93,7 @@ struct DecodeParams {
   int32_t col_blocks;
   float scale;
   NormEpilogue norm;      // applied when norm.gate != null (then col_blocks == 1)
+  ConvPrologue conv;      // applied when conv.x != null (then q, k, v are unused)
 };
 
 struct GatePrologueParams {
@@ -199,5 +218,9 @@ int decode_columns_per_block(int d_k, int d_v, bool per_key);
 // Whether the decode kernel applies a gated RMSNorm in its output store (its
 // workgroup owns whole rows: d_v at most the columns per block).
 bool decode_fuses_norm(int d_k, int d_v, bool per_key);
+// Whether the decode kernel can take its inputs through the conv prologue:
+// d_k one of 16, 32, 64, 128, 256, d_v a multiple of the columns per block,
+// a per-head (or no) decay.
+bool decode_takes_conv(int d_k, int d_v, bool per_key);
 
 }  // namespace gdn

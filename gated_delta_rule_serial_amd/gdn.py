@@ -111,6 +111,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_causal_conv_slots.restype = ctypes.c_int
     lib.gdn_causal_conv_step_slots.argtypes = [cp, i32, vp, vp, i32, vp, ip, vp, vp]
     lib.gdn_causal_conv_step_slots.restype = ctypes.c_int
+    lib.gdn_decode_step_conv.argtypes = [pp, cp, i32, vp, vp, vp, vp, vp, vp]
+    lib.gdn_decode_step_conv.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, i32, vp, vp, vp, ctypes.c_float, i32, vp, vp]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_prefill_workspace_size.argtypes = [pp, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
@@ -360,6 +362,24 @@ def gdn_causal_conv_step(x: torch.Tensor, weight: torch.Tensor, state: torch.Ten
     prob = make_conv_problem(weight, bias, dilation=dilation, activation=activation)
     _check(load().gdn_causal_conv_step(ctypes.byref(prob), x.shape[0], _ptr(x), _ptr(state), _ptr(y),
                                        _stream(stream, x.device)))
+
+
+def gdn_decode_step_conv(x: torch.Tensor, conv_weight: torch.Tensor, conv_state: Optional[torch.Tensor],
+                         conv_state_out: Optional[torch.Tensor], state: torch.Tensor, out: torch.Tensor, *,
+                         h_qk: int, d_k: int, conv_bias: Optional[torch.Tensor] = None, conv_activation: str = "silu",
+                         g=None, beta=None, a=None, b=None, A_log=None, dt_bias=None, scale: float = 0.0,
+                         stream=None, **variant) -> None:
+    """gdn_decode_step_conv of include/gdn.h: x [B, C] with C = 2 h_qk d_k + h_v d_v
+    (q | k | v); conv_state, conv_state_out [B, K - 1, C] (distinct buffers, or
+    None when K = 1); state float32 [B, h_v, d_k, d_v], updated in place; out
+    [B, h_v, d_v].  ``variant`` as in gdn_decode_step (rule, norm_gate, ...)."""
+    B = x.shape[0]
+    h_v, d_v = out.shape[1], out.shape[2]
+    prob = make_problem(h_qk, h_v, d_k, d_v, x.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
+                        A_log=A_log, dt_bias=dt_bias, **variant)
+    cprob = make_conv_problem(conv_weight, conv_bias, dilation=1, activation=conv_activation)
+    _check(load().gdn_decode_step_conv(ctypes.byref(prob), ctypes.byref(cprob), B, _ptr(x), _ptr(conv_state),
+                                       _ptr(conv_state_out), _ptr(state), _ptr(out), _stream(stream, x.device)))
 
 
 def gdn_causal_conv_slots(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor, state_pool: torch.Tensor,

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 9
+#define GDN_ABI_VERSION 10
 
 /* Largest supported head size ([P4] MAX_D_K; [P1] typed scan bound). */
 #define GDN_MAX_HEAD_DIM 256
@@ -422,6 +422,37 @@ gdn_status gdn_causal_conv_step_slots(const gdn_conv_problem* problem, int32_t b
                                       const void* x, void* state_pool, int32_t num_slots,
                                       const int32_t* slots, const int32_t* slots_host, void* y,
                                       hipStream_t stream);
+
+/*
+ * gdn_decode_step_conv -- the conv step in front of the decode step, in one
+ * launch ([P1] `causal_conv_op` feeding `linear_attention_op`, both with a
+ * one-token time axis): per sequence b, the token row x[b] holds the conv
+ * inputs of q, k and v, C = 2 h_qk d_k + h_v d_v channels in the order
+ *     q [h_qk, d_k] | k [h_qk, d_k] | v [h_v, d_v],
+ * and the step runs on the conv outputs as gdn_causal_conv_step would store
+ * them (narrowed to io_dtype).  Same result as gdn_causal_conv_step(conv, x,
+ * state = conv_state -> conv_state_out, y) followed by gdn_decode_step on the
+ * three slices of y, without y in memory.
+ *   conv            io_dtype equal to problem->io_dtype, channels = C,
+ *                   dilation 1, kernel_size 1 .. 4 (else GDN_ERR_UNSUPPORTED)
+ *   x               [batch, C] io_dtype
+ *   conv_state      [batch, K - 1, C] io_dtype, read (NULL when K = 1)
+ *   conv_state_out  [batch, K - 1, C] io_dtype, receives the carried inputs
+ *                   one token later (NULL when K = 1).  It must not overlap
+ *                   conv_state: the q and k channels are read by several
+ *                   workgroups, so the shift cannot be done in place; callers
+ *                   alternate two buffers.
+ *   state, out      as in gdn_decode_step (state updated in place)
+ * Served for d_k in {16, 32, 64, 128, 256}, d_v a multiple of the decode
+ * kernel's columns per workgroup (128 when d_k <= 128 and d_v > 64, else 64),
+ * and a per-head decay or none; other problems give GDN_ERR_UNSUPPORTED.  The
+ * problem's optional output norm applies as in gdn_decode_step.  No buffer
+ * may overlap another except the read-only inputs among themselves.
+ */
+gdn_status gdn_decode_step_conv(const gdn_problem* problem, const gdn_conv_problem* conv,
+                                int32_t batch, const void* x, const void* conv_state,
+                                void* conv_state_out, float* state, void* out,
+                                hipStream_t stream);
 
 /*
  * gdn_gated_rmsnorm -- gated RMSNorm ([P1] `gated_rms_norm_op`): each row of

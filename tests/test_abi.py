@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 9
+    assert gdn.abi_version() == 10
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
     assert gdn.status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -417,3 +417,39 @@ def test_output_norm_validation(lib):
     # from 512 (sequence, head) units the state pass runs 128-column blocks anyway, and fuses the norm
     p = gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 16, 32768, workspace_bytes=1 << 40, norm=True)
     assert p["norm"] == "fused" and p["columns_per_block"] == 128
+
+
+def test_decode_conv_validation(lib):
+    """The decode step with its conv prologue checks the conv's geometry
+    against the problem's, and its buffers, before anything runs."""
+    vp = ctypes.c_void_p
+    base = dict(io_dtype=gdn.GDN_BF16, h_qk=1, h_v=2, d_k=128, d_v=128)
+    C = 2 * 128 + 2 * 128
+
+    def call(prob_kw=None, C=C, K=4, dil=1, dtype=gdn.GDN_BF16, B=2, x=FAKE + 0x100000, cs=FAKE + 0x200000,
+             cs_out=FAKE + 0x300000, state=FAKE + 0x400000, out=FAKE + 0x500000):
+        conv = gdn.gdn_conv_problem(C, K, dil, dtype, gdn.GDN_ACT_SILU, vp(FAKE + 0x600000), None)
+        prob = _prob(**{**base, **(prob_kw or {})})
+        return lib.gdn_decode_step_conv(ctypes.byref(prob), ctypes.byref(conv), B, vp(x) if x else None,
+                                        vp(cs) if cs else None, vp(cs_out) if cs_out else None,
+                                        vp(state) if state else None, vp(out) if out else None, None)
+
+    for kw, status, needle in (
+            (dict(C=C + 1), INVALID, "channels"),
+            (dict(dtype=gdn.GDN_F32), INVALID, "io_dtype"),
+            (dict(cs_out=FAKE + 0x200000), INVALID, "in place"),
+            (dict(cs_out=None), INVALID, "required"),
+            (dict(x=FAKE + 0x100002), INVALID, "16-byte"),
+            (dict(out=FAKE + 0x100000), INVALID, "overlap"),
+            (dict(state=None), INVALID, "required"),
+            (dict(B=-1), INVALID, "negative"),
+            (dict(dil=2), UNSUPPORTED, "dilation"),
+            (dict(K=5), UNSUPPORTED, "kernel_size"),
+            (dict(prob_kw=dict(d_k=100), C=2 * 100 + 2 * 128), UNSUPPORTED, "d_k"),
+            (dict(prob_kw=dict(d_v=96), C=2 * 128 + 2 * 96), UNSUPPORTED, "multiple"),
+            (dict(prob_kw=dict(decay_per_key=1)), UNSUPPORTED, "per-key")):
+        st = call(**kw)
+        assert st == status and needle in gdn.last_error(), (kw, st, gdn.last_error())
+    # nothing to do: OK without a launch; K = 1 carries nothing, so no conv states are needed
+    assert call(B=0, x=None, cs=None, cs_out=None, state=None, out=None) == gdn.GDN_OK
+    assert gdn.last_error() == ""
