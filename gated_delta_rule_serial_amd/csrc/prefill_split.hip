@@ -596,8 +596,8 @@ struct TPrepLds {
   static constexpr int SK = DK + 8;
   static constexpr int SA = kC + 4;                  // f32 row stride of A: 4 rows of a tile 16 banks apart
   static constexpr int kKs = 0;                      // K rows [C][SK] bf16
-  static constexpr int kQs = kKs + kC * SK * 2;      // Q rows [C][SK] bf16, later the scratch [4][16][20] f32, then T''
-  static constexpr int kAf = kQs + kC * SK * 2;      // A [C][SA] f32, later T' in bf16
+  static constexpr int kQs = kKs + kC * SK * 2;      // Q rows [C][SK] bf16, later the scratch [4][16][20] f32
+  static constexpr int kAf = kQs + kC * SK * 2;      // A [C][SA] f32
   static constexpr int kTf = kAf + kC * SA * 4;      // T [C][ST] f32
   static constexpr int kMs = kTf + kC * kST * 4;     // M [C][SC] bf16
   static constexpr int kGd = kMs + kC * kSC * 2;     // G [C] f64
@@ -606,7 +606,6 @@ struct TPrepLds {
   static constexpr int kKf = kBet + kC * 4;          // exp(G_last - G) [C] f32
   static constexpr int kBytes = kKf + kC * 4;
   static_assert(4 * 16 * 20 * 4 <= kC * SK * 2, "the scratch fits in Q's rows");
-  static_assert(kC * kSC * 2 <= kC * SA * 4 && kC * kSC * 2 <= kC * SK * 2, "T' and T'' fit in the A and Q buffers");
   static_assert(2 * kBytes <= 160 * 1024, "two workgroups per gfx950 compute unit");
 };
 
@@ -624,8 +623,6 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
   float* Xs = reinterpret_cast<float*>(smem + L_::kQs);
   constexpr int kSA = L_::SA;  // this kernel's stride of A
   float* Af = reinterpret_cast<float*>(smem + L_::kAf);
-  bf16_t* Tp = reinterpret_cast<bf16_t*>(smem + L_::kAf);
-  bf16_t* Tpp = reinterpret_cast<bf16_t*>(smem + L_::kQs);
   float* Tf = reinterpret_cast<float*>(smem + L_::kTf);
   bf16_t* Ms = reinterpret_cast<bf16_t*>(smem + L_::kMs);
   double* Gd = reinterpret_cast<double*>(smem + L_::kGd);
@@ -718,27 +715,14 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
     }
     return dec;
   };
-  // product q of a workgroup's twenty: the diagonal tiles of A (q < 4), the
-  // tiles of A below them ((1,0) (2,0) (2,1) (3,0) (3,1) (3,2)), the lower
-  // tiles of M ((0,0) (1,0) (1,1) .. (3,3)); A with beta and the decay, M with the decay
-  auto product = [&](int q) __attribute__((always_inline)) {
-    int tb, cb;
-    bool is_a = true;
-    if (q < 4) {
-      tb = cb = q;
-    } else if (q < 10) {
-      const int a = q - 4;
-      tb = a < 1 ? 1 : (a < 3 ? 2 : 3);
-      cb = a - tb * (tb - 1) / 2;
-    } else {
-      const int m = q - 10;
-      tb = 0;
-      while ((tb + 1) * (tb + 2) / 2 <= m) ++tb;
-      cb = m - tb * (tb + 1) / 2;
-      is_a = false;
-    }
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = mma<DK>(acc, (is_a ? Ks : Qs) + 16 * tb * SK, SK, Ks + 16 * cb * SK, SK, lane);
+  // The twenty tile products of an item: the lower tiles of A = K K^T (with
+  // beta and the decay) and of M = Q K^T (with the decay).  Wave w forms A's
+  // tiles of token tile w (A(w, cb), cb <= w) and M's of token tile 3 - w
+  // (M(3 - w, cb), cb <= 3 - w), five each: it holds the fragments of its
+  // own K and Q rows and reads each K tile cb once for both families (K tile
+  // w is its own B operand), 18 tile reads from LDS per item instead of the
+  // 40 of one pair of operand tiles per product.
+  auto epilogue = [&](f32x4 acc, int tb, int cb, bool is_a) __attribute__((always_inline)) {
     const f32x4 dec = tile_decay(tb, cb);
     const int s_ = 16 * cb + acc_col(lane);
     const int t0 = 16 * tb + acc_row(lane, 0);
@@ -752,6 +736,35 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) Ms[(t0 + i) * kSC + s_] = to_bf16(dec[i] * acc[i]);
+    }
+  };
+  auto products = [&]() __attribute__((always_inline)) {
+    constexpr int NK = DK / 32;
+    const int wm = 3 - w;
+    bf16x8 ka[NK], qa[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      ka[kk] = frag(Ks + 16 * w * SK + 32 * kk, SK, lane);
+      qa[kk] = frag(Qs + 16 * wm * SK + 32 * kk, SK, lane);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      if (cb > w && cb > wm) break;
+      bf16x8 kb[NK];
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) kb[kk] = cb == w ? ka[kk] : frag(Ks + 16 * cb * SK + 32 * kk, SK, lane);
+      if (cb <= w) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], kb[kk], acc, 0, 0, 0);
+        epilogue(acc, w, cb, true);
+      }
+      if (cb <= wm) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kb[kk], acc, 0, 0, 0);
+        epilogue(acc, wm, cb, false);
+      }
     }
   };
 
@@ -809,8 +822,7 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
     // ================= 2. the twenty tile products, five per wave, then the
     // diagonal 16 x 16 block w of T = (I + A)^-1 by forward substitution (one
     // column per lane; lanes 16-63 repeat lanes 0-15)
-#pragma unroll
-    for (int e = 0; e < 5; ++e) product(e == 0 ? w : 4 + 4 * w + (e - 1));
+    products();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the diagonal block is in LDS for this wave's reads
     __builtin_amdgcn_wave_barrier();
     {
@@ -863,42 +875,46 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
       }
       __syncthreads();
     }
-    // T' = T diag(beta gam) and T'' = T diag(beta) in bf16, lower triangle, four columns per thread
-    for (int e = tid; e < kC * kC / 4; e += kTThreads) {
-      const int t = e >> 4, s4 = (e & 15) * 4;
-      const f32x4 tv = *reinterpret_cast<const f32x4*>(Tf + t * kST + s4);
-      const f32x4 bs = *reinterpret_cast<const f32x4*>(Bet + s4);
-      const f32x4 gm = *reinterpret_cast<const f32x4*>(Gam + s4);
-      uint32_t wp[2], wpp[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        float a2[2], b2[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int c = 2 * h2 + k;
-          const float x = (s4 + c <= t) ? tv[c] : 0.0f;
-          b2[k] = x * bs[c];
-          a2[k] = b2[k] * gm[c];
-        }
-        wp[h2] = static_cast<uint32_t>(to_bf16(a2[0])) | (static_cast<uint32_t>(to_bf16(a2[1])) << 16);
-        wpp[h2] = static_cast<uint32_t>(to_bf16(b2[0])) | (static_cast<uint32_t>(to_bf16(b2[1])) << 16);
-      }
-      *reinterpret_cast<uint2*>(Tp + t * kSC + s4) = make_uint2(wp[0], wp[1]);
-      *reinterpret_cast<uint2*>(Tpp + t * kSC + s4) = make_uint2(wpp[0], wpp[1]);
-    }
-    __syncthreads();
-
-    // ================= 4. the record: T', T'' and M blocks, then gam and exp(G_last - G)
+    // ================= 4. the record: T' = T diag(beta gam) and T'' = T diag(beta)
+    // formed in bf16 straight into their fragments (lower triangle), the M
+    // blocks, then gam and exp(G_last - G)
     {
       u32x4_t* fr = reinterpret_cast<u32x4_t*>(base);
-      for (int f = w; f < kTFrags; f += kTWaves) {
+      for (int f = w; f < 12; f += kTWaves) {
         const int mf = f % 6;
         const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
         const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
-        const bf16_t* row = (f < 6 ? Tp : (f < 12 ? Tpp : Ms)) + (16 * tt + r) * kSC;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * g);
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * g);
-        __builtin_nontemporal_store(u32x4_t{lo.x, lo.y, hi.x, hi.y}, fr + f * 64 + lane);
+        const int t = 16 * tt + r;
+        if (f < 6) {
+          uint32_t wp[4], wpp[4];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int s4 = 32 * kb + 16 * hh + 4 * g;
+            const f32x4 tv = *reinterpret_cast<const f32x4*>(Tf + t * kST + s4);
+            const f32x4 bs = *reinterpret_cast<const f32x4*>(Bet + s4);
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(Gam + s4);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              float a2[2], b2[2];
+#pragma unroll
+              for (int k = 0; k < 2; ++k) {
+                const int c = 2 * h2 + k;
+                const float x = (s4 + c <= t) ? tv[c] : 0.0f;
+                b2[k] = x * bs[c];
+                a2[k] = b2[k] * gm[c];
+              }
+              wp[2 * hh + h2] = static_cast<uint32_t>(to_bf16(a2[0])) | (static_cast<uint32_t>(to_bf16(a2[1])) << 16);
+              wpp[2 * hh + h2] = static_cast<uint32_t>(to_bf16(b2[0])) | (static_cast<uint32_t>(to_bf16(b2[1])) << 16);
+            }
+          }
+          __builtin_nontemporal_store(u32x4_t{wp[0], wp[1], wp[2], wp[3]}, fr + f * 64 + lane);
+          __builtin_nontemporal_store(u32x4_t{wpp[0], wpp[1], wpp[2], wpp[3]}, fr + (f + 6) * 64 + lane);
+        } else {
+          const bf16_t* row = Ms + t * kSC;
+          const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * g);
+          const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * g);
+          __builtin_nontemporal_store(u32x4_t{lo.x, lo.y, hi.x, hi.y}, fr + (f + 6) * 64 + lane);
+        }
       }
       if (tid < 32) {
         const f32x4 v4 = *reinterpret_cast<const f32x4*>((tid < 16 ? Gam : Kf) + 4 * (tid & 15));
