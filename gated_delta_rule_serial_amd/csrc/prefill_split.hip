@@ -591,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
 constexpr int kTWaves = 4;
 constexpr int kTThreads = 64 * kTWaves;
 
-template <int DK>
+template <int DK, int NH>
 struct TPrepLds {
   static constexpr int SK = DK + 8;
   static constexpr int SA = kC + 4;                  // f32 row stride of A: 4 rows of a tile 16 banks apart
@@ -600,22 +600,25 @@ struct TPrepLds {
   static constexpr int kAf = kQs + kC * SK * 2;      // A [C][SA] f32
   static constexpr int kTf = kAf + kC * SA * 4;      // T [C][ST] f32
   static constexpr int kMs = kTf + kC * kST * 4;     // M [C][SC] bf16
-  static constexpr int kGd = kMs + kC * kSC * 2;     // G [C] f64
-  static constexpr int kGam = kGd + kC * 8;          // gam [C] f32
-  static constexpr int kBet = kGam + kC * 4;         // beta [C] f32
-  static constexpr int kKf = kBet + kC * 4;          // exp(G_last - G) [C] f32
-  static constexpr int kBytes = kKf + kC * 4;
+  static constexpr int kGd = kMs + kC * kSC * 2;     // G [NH][C] f64, one set per value head of a unit
+  static constexpr int kGam = kGd + NH * kC * 8;     // gam [NH][C] f32
+  static constexpr int kBet = kGam + NH * kC * 4;    // beta [NH][C] f32
+  static constexpr int kKf = kBet + NH * kC * 4;     // exp(G_last - G) [NH][C] f32
+  static constexpr int kBytes = kKf + NH * kC * 4;
   static_assert(4 * 16 * 20 * 4 <= kC * SK * 2, "the scratch fits in Q's rows");
   static_assert(2 * kBytes <= 160 * 1024, "two workgroups per gfx950 compute unit");
 };
 
-// Persistent: the workgroups walk the (chunk, value head) items blockIdx.x,
-// + gridDim.x, ...; the next item's K and Q rows and gates are loaded into
-// registers while the current one computes.
-template <typename IO, int DK, bool RAW>
+// Persistent: the workgroups walk the units blockIdx.x, + gridDim.x, ...;
+// the next unit's K and Q rows and gates are loaded into registers while the
+// current one computes.  A unit is a chunk and NH value heads that read the
+// same q/k head (NH = 2 where the head ratio is even): their K K^T and Q K^T
+// are one product, formed once and kept in registers, and each head then
+// takes its own decay and gates (A, M), substitution and record in turn.
+template <typename IO, int DK, bool RAW, int NH>
 __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, unsigned char* ws, const int32_t* cs,
-                                                               const int2* __restrict__ info, int items) {
-  using L_ = TPrepLds<DK>;
+                                                               const int2* __restrict__ info, int units) {
+  using L_ = TPrepLds<DK, NH>;
   constexpr int SK = L_::SK;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* Ks = reinterpret_cast<bf16_t*>(smem + L_::kKs);
@@ -625,13 +628,10 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
   float* Af = reinterpret_cast<float*>(smem + L_::kAf);
   float* Tf = reinterpret_cast<float*>(smem + L_::kTf);
   bf16_t* Ms = reinterpret_cast<bf16_t*>(smem + L_::kMs);
-  double* Gd = reinterpret_cast<double*>(smem + L_::kGd);
-  float* Gam = reinterpret_cast<float*>(smem + L_::kGam);
-  float* Bet = reinterpret_cast<float*>(smem + L_::kBet);
-  float* Kf = reinterpret_cast<float*>(smem + L_::kKf);
 
-  const int total = cs[p.num_seqs] * p.h_v;  // live items; the grid covers a bound
-  const int n_items = items < total ? items : total;
+  const int hpu = p.h_v / NH;                       // units per chunk
+  const int total = cs[p.num_seqs] * hpu;           // live units; the grid covers a bound
+  const int n_units = units < total ? units : total;
   const int tid = static_cast<int>(threadIdx.x);
   // wave-uniform, and the compiler is told so: branches on w must skip
   // their MFMAs, which run whatever the execution mask
@@ -642,29 +642,30 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
   const IO* kg = static_cast<const IO*>(p.k);
   const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
 
-  // item i is chunk c = i / h_v (first token, tokens from the chunk table), head h = i % h_v
+  // unit u is chunk c = u / hpu (first token, tokens from the chunk table),
+  // value heads NH (u % hpu) .. + NH - 1
   struct Where {
     int c, h, t0, Lc;
   };
-  auto locate = [&](int item, int2 ci) __attribute__((always_inline)) {
+  auto locate = [&](int unit, int2 ci) __attribute__((always_inline)) {
     Where at;
-    at.c = item / p.h_v;
-    at.h = item % p.h_v;
+    at.c = unit / hpu;
+    at.h = NH * (unit % hpu);
     at.t0 = ci.x;
     at.Lc = ci.y;
     return at;
   };
   // unconditional (clamped) loads, so that no wait for them falls right after they are issued
-  auto info_of = [&](int item) __attribute__((always_inline)) { return info[min(item, n_items - 1) / p.h_v]; };
+  auto info_of = [&](int unit) __attribute__((always_inline)) { return info[min(unit, n_units - 1) / hpu]; };
 
-  // ---- register staging of one item's K and Q rows and gate inputs
+  // ---- register staging of one unit's K and Q rows and gate inputs
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   constexpr int VPR = DK / 8;
   constexpr int KQ_IT = kC * VPR / kTThreads;
   static_assert(KQ_IT >= 1, "block shape");
   u32x4_t rk[KQ_IT], rq[KQ_IT];
-  uint32_t rg = 0u, rbt = 0u;
-  float rAl = 0.0f, rdt = 0.0f;
+  uint32_t rg[NH], rbt[NH];
+  float rAl[NH], rdt[NH];
   auto fetch = [&](const Where& at) __attribute__((always_inline)) {
     const int hq = at.h / p.ratio;
 #pragma unroll
@@ -677,15 +678,21 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
     }
     // gate inputs of token (chunk start + lane), clamped into the chunk
     const int tl = at.t0 + min(lane, max(at.Lc - 1, 0));
-    const size_t gi = static_cast<size_t>(tl) * p.h_v + at.h;
-    const size_t bi = p.gates.beta_shared ? static_cast<size_t>(tl) : gi;
-    const IO* bsrc = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
-    const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : bsrc;
-    rg = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : bi];
-    rbt = reinterpret_cast<const uint16_t*>(bsrc)[bi];
-    if constexpr (RAW) {
-      rAl = p.gates.A_log[at.h];
-      rdt = p.gates.dt_bias[at.h];
+#pragma unroll
+    for (int hs = 0; hs < NH; ++hs) {
+      const int hh = at.h + hs;
+      const size_t gi = static_cast<size_t>(tl) * p.h_v + hh;
+      const size_t bi = p.gates.beta_shared ? static_cast<size_t>(tl) : gi;
+      const IO* bsrc = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
+      const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : bsrc;
+      rg[hs] = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : bi];
+      rbt[hs] = reinterpret_cast<const uint16_t*>(bsrc)[bi];
+      if constexpr (RAW) {
+        rAl[hs] = p.gates.A_log[hh];
+        rdt[hs] = p.gates.dt_bias[hh];
+      } else {
+        rAl[hs] = rdt[hs] = 0.0f;
+      }
     }
   };
 
@@ -698,9 +705,10 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
     Ms[t * kSC + s] = 0;
   }
 
-  // exp(G_t - G_s) for the accumulator tile (token tile tb, token tile cb), 0 where s > t;
-  // the lane's four rows are 16 tb + 4 g + i, read at once
-  auto tile_decay = [&](int tb, int cb) __attribute__((always_inline)) {
+  // exp(G_t - G_s) for the accumulator tile (token tile tb, token tile cb), 0
+  // where s > t, from the prefix sums Gd of one head; the lane's four rows are
+  // 16 tb + 4 g + i, read at once
+  auto tile_decay = [&](const double* Gd, int tb, int cb) __attribute__((always_inline)) {
     const int s_ = 16 * cb + acc_col(lane);
     const int t0 = 16 * tb + acc_row(lane, 0);
     const double Gs = Gd[s_];
@@ -715,29 +723,16 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
     }
     return dec;
   };
-  // The twenty tile products of an item: the lower tiles of A = K K^T (with
-  // beta and the decay) and of M = Q K^T (with the decay).  Wave w forms A's
-  // tiles of token tile w (A(w, cb), cb <= w) and M's of token tile 3 - w
-  // (M(3 - w, cb), cb <= 3 - w), five each: it holds the fragments of its
-  // own K and Q rows and reads each K tile cb once for both families (K tile
-  // w is its own B operand), 18 tile reads from LDS per item instead of the
-  // 40 of one pair of operand tiles per product.
-  auto epilogue = [&](f32x4 acc, int tb, int cb, bool is_a) __attribute__((always_inline)) {
-    const f32x4 dec = tile_decay(tb, cb);
-    const int s_ = 16 * cb + acc_col(lane);
-    const int t0 = 16 * tb + acc_row(lane, 0);
-    if (is_a) {
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + t0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = bt[i] * dec[i] * acc[i];
-        Af[(t0 + i) * kSA + s_] = (s_ < t0 + i) ? a : 0.0f;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ms[(t0 + i) * kSC + s_] = to_bf16(dec[i] * acc[i]);
-    }
-  };
+  // The twenty tile products of a unit: the lower tiles of K K^T (A, with
+  // beta and the decay) and of Q K^T (M, with the decay).  Wave w forms the
+  // K K^T tiles of token tile w ((w, cb), cb <= w) and the Q K^T tiles of
+  // token tile 3 - w ((3 - w, cb), cb <= 3 - w), five each: it holds the
+  // fragments of its own K and Q rows and reads each K tile cb once for both
+  // families (K tile w is its own B operand), 18 tile reads from LDS per unit
+  // instead of the 40 of one pair of operand tiles per product.  The raw
+  // products stay in registers, indexed by their column tile (rawA[cb] for
+  // cb <= w, rawM[cb] for cb <= 3 - w); each head's epilogue reads them.
+  f32x4 rawA[4], rawM[4];
   auto products = [&]() __attribute__((always_inline)) {
     constexpr int NK = DK / 32;
     const int wm = 3 - w;
@@ -757,38 +752,68 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], kb[kk], acc, 0, 0, 0);
-        epilogue(acc, w, cb, true);
+        rawA[cb] = acc;
       }
       if (cb <= wm) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kb[kk], acc, 0, 0, 0);
-        epilogue(acc, wm, cb, false);
+        rawM[cb] = acc;
+      }
+    }
+  };
+  // one head's A and M tiles from the raw products, in the order products() left them
+  auto epilogue = [&](int hs) __attribute__((always_inline)) {
+    const double* Gd = reinterpret_cast<const double*>(smem + L_::kGd) + hs * kC;
+    const float* Bet = reinterpret_cast<const float*>(smem + L_::kBet) + hs * kC;
+    const int wm = 3 - w;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      if (cb > w && cb > wm) break;
+#pragma unroll
+      for (int fam = 0; fam < 2; ++fam) {
+        const int tb = fam == 0 ? w : wm;
+        if (cb > tb) continue;
+        const f32x4 acc = fam == 0 ? rawA[cb] : rawM[cb];
+        const f32x4 dec = tile_decay(Gd, tb, cb);
+        const int s_ = 16 * cb + acc_col(lane);
+        const int t0 = 16 * tb + acc_row(lane, 0);
+        if (fam == 0) {
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + t0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = bt[i] * dec[i] * acc[i];
+            Af[(t0 + i) * kSA + s_] = (s_ < t0 + i) ? a : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Ms[(t0 + i) * kSC + s_] = to_bf16(dec[i] * acc[i]);
+        }
       }
     }
   };
 
-  // Blocks go round-robin over the 8 XCDs.  Where the grid allows, the ratio
-  // value heads of one (chunk, q/k head) go to blocks 8 apart, on one XCD,
-  // which run them at about the same time and read K and Q once through its L2.
-  int item = static_cast<int>(blockIdx.x);
+  // Blocks go round-robin over the 8 XCDs.  Where the grid allows, the units
+  // of one (chunk, q/k head) go to blocks 8 apart, on one XCD, which run them
+  // at about the same time and read K and Q once through its L2.
+  int unit = static_cast<int>(blockIdx.x);
   {
-    const int R = p.ratio, G = static_cast<int>(gridDim.x);
+    const int R = p.ratio / NH, G = static_cast<int>(gridDim.x);
     if (R > 1 && G % (8 * R) == 0) {
-      const int xcd = item % 8, j = item / 8;
-      item = (j / R) * (8 * R) + xcd * R + j % R;
+      const int xcd = unit % 8, j = unit / 8;
+      unit = (j / R) * (8 * R) + xcd * R + j % R;
     }
   }
-  if (item >= n_items) return;
-  Where at = locate(item, info[item / p.h_v]);
+  if (unit >= n_units) return;
+  Where at = locate(unit, info[unit / hpu]);
   fetch(at);
-  int2 next_info = info_of(item + static_cast<int>(gridDim.x));  // one item ahead of the fetch
-  for (; item < n_items; item += static_cast<int>(gridDim.x)) {
-    const int h = at.h;
+  int2 next_info = info_of(unit + static_cast<int>(gridDim.x));  // one unit ahead of the fetch
+  for (; unit < n_units; unit += static_cast<int>(gridDim.x)) {
+    const int h0 = at.h;
+    const int c = at.c;
     const int Lc = at.Lc;
-    unsigned char* base = ws + (static_cast<size_t>(at.c) * p.h_v + h) * kTRecBytes;
 
-    // ================= 1. stage K and Q rows; gates and the prefix sum of the log-decay
+    // ================= 1. stage K and Q rows; per head: gates and the prefix sum of the log-decay
 #pragma unroll
     for (int it = 0; it < KQ_IT; ++it) {
       const int v = tid + it * kTThreads;
@@ -798,130 +823,144 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
       *reinterpret_cast<u32x4_t*>(Qs + t * SK + c8) = t < Lc ? rq[it] : zero;
     }
     if (w == 0) {
-      float gv = 0.0f, b = 0.0f;
-      if (lane < Lc) {
-        if constexpr (RAW) {
-          gv = p.gates.decays ? gate_log_decay(widen_bits16<IO>(rg), rAl, rdt) : 0.0f;
-          b = gate_sigmoid(widen_bits16<IO>(rbt));
-        } else {
-          gv = p.gates.decays ? widen_bits16<IO>(rg) : 0.0f;
-          b = widen_bits16<IO>(rbt);
+#pragma unroll
+      for (int hs = 0; hs < NH; ++hs) {
+        float gv = 0.0f, b = 0.0f;
+        if (lane < Lc) {
+          if constexpr (RAW) {
+            gv = p.gates.decays ? gate_log_decay(widen_bits16<IO>(rg[hs]), rAl[hs], rdt[hs]) : 0.0f;
+            b = gate_sigmoid(widen_bits16<IO>(rbt[hs]));
+          } else {
+            gv = p.gates.decays ? widen_bits16<IO>(rg[hs]) : 0.0f;
+            b = widen_bits16<IO>(rbt[hs]);
+          }
+          gv = fmaxf(gv, kMinLogDecay);
         }
-        gv = fmaxf(gv, kMinLogDecay);
+        const double G = wave_prefix_sum(static_cast<double>(gv) * kLog2e, lane);
+        reinterpret_cast<double*>(smem + L_::kGd)[hs * kC + lane] = G;
+        reinterpret_cast<float*>(smem + L_::kGam)[hs * kC + lane] = fast_exp2(static_cast<float>(G));
+        reinterpret_cast<float*>(smem + L_::kBet)[hs * kC + lane] = b;
+        // the state-update factor exp(G_last - G_t); gates past the chunk's end
+        // are 0, so G_last is the prefix at the last lane
+        reinterpret_cast<float*>(smem + L_::kKf)[hs * kC + lane] = fast_exp2(static_cast<float>(__shfl(G, kC - 1) - G));
       }
-      const double G = wave_prefix_sum(static_cast<double>(gv) * kLog2e, lane);
-      Gd[lane] = G;
-      Gam[lane] = fast_exp2(static_cast<float>(G));
-      Bet[lane] = b;
-      // the state-update factor exp(G_last - G_t); gates past the chunk's end
-      // are 0, so G_last is the prefix at the last lane
-      Kf[lane] = fast_exp2(static_cast<float>(__shfl(G, kC - 1) - G));
     }
     __syncthreads();
 
-    // ================= 2. the twenty tile products, five per wave, then the
-    // diagonal 16 x 16 block w of T = (I + A)^-1 by forward substitution (one
-    // column per lane; lanes 16-63 repeat lanes 0-15)
+    // ================= 2. the twenty tile products (once for the unit's heads)
     products();
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the diagonal block is in LDS for this wave's reads
-    __builtin_amdgcn_wave_barrier();
-    {
-      const int cc = lane & 15;
-      const float* Ab = Af + (16 * w) * kSA + 16 * w;
-      float d[16];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        float x0 = (rr == cc) ? 1.0f : 0.0f, x1 = 0.0f;
-#pragma unroll
-        for (int s2 = 0; s2 < rr; s2 += 2) {
-          x0 = fmaf(-Ab[rr * kSA + s2], d[s2], x0);
-          if (s2 + 1 < rr) x1 = fmaf(-Ab[rr * kSA + s2 + 1], d[s2 + 1], x1);
-        }
-        d[rr] = x0 + x1;
-      }
-      if (lane < 16) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) Tf[(16 * w + rr) * kST + 16 * w + cc] = d[rr];
-      }
-    }
-    // the next item's inputs, in flight while this one computes
-    {
-      const int next = item + static_cast<int>(gridDim.x);
-      if (next < n_items) {
-        at = locate(next, next_info);
-        fetch(at);
-        next_info = info_of(next + static_cast<int>(gridDim.x));
-      }
-    }
-    __syncthreads();
+    for (int hs = 0; hs < NH; ++hs) {
+      const float* Gam = reinterpret_cast<const float*>(smem + L_::kGam) + hs * kC;
+      const float* Bet = reinterpret_cast<const float*>(smem + L_::kBet) + hs * kC;
+      const float* Kf = reinterpret_cast<const float*>(smem + L_::kKf) + hs * kC;
+      unsigned char* base = ws + (static_cast<size_t>(c) * p.h_v + h0 + hs) * kTRecBytes;
 
-    // ================= 3. the blocks of T below the diagonal, by block
-    // substitution: T_ij = -T_ii sum_{k = j .. i-1} A_ik T_kj
-    for (int dist = 1; dist < 4; ++dist) {
-      const int i = w + dist, j = w;
-      if (i < 4) {
-        f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int k = j; k < i; ++k)
-          x = mma_f32(x, Af + (16 * i) * kSA + 16 * k, kSA, Tf + (16 * k) * kST + 16 * j, kST, lane);
-        float* xs = Xs + w * 16 * 20;
+      // ---- this head's A and M tiles, then the diagonal 16 x 16 block w of
+      // T = (I + A)^-1 by forward substitution (one column per lane; lanes
+      // 16-63 repeat lanes 0-15)
+      epilogue(hs);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the diagonal block is in LDS for this wave's reads
+      __builtin_amdgcn_wave_barrier();
+      {
+        const int cc = lane & 15;
+        const float* Ab = Af + (16 * w) * kSA + 16 * w;
+        float d[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xs[acc_row(lane, e) * 20 + acc_col(lane)] = x[e];
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
-        y = mma_f32(y, Tf + (16 * i) * kST + 16 * i, kST, xs, 20, lane);
+        for (int rr = 0; rr < 16; ++rr) {
+          float x0 = (rr == cc) ? 1.0f : 0.0f, x1 = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Tf[(16 * i + acc_row(lane, e)) * kST + 16 * j + acc_col(lane)] = -y[e];
+          for (int s2 = 0; s2 < rr; s2 += 2) {
+            x0 = fmaf(-Ab[rr * kSA + s2], d[s2], x0);
+            if (s2 + 1 < rr) x1 = fmaf(-Ab[rr * kSA + s2 + 1], d[s2 + 1], x1);
+          }
+          d[rr] = x0 + x1;
+        }
+        if (lane < 16) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) Tf[(16 * w + rr) * kST + 16 * w + cc] = d[rr];
+        }
+      }
+      // the next unit's inputs, in flight while this one computes
+      if (hs == 0) {
+        const int next = unit + static_cast<int>(gridDim.x);
+        if (next < n_units) {
+          at = locate(next, next_info);
+          fetch(at);
+          next_info = info_of(next + static_cast<int>(gridDim.x));
+        }
       }
       __syncthreads();
-    }
-    // ================= 4. the record: T' = T diag(beta gam) and T'' = T diag(beta)
-    // formed in bf16 straight into their fragments (lower triangle), the M
-    // blocks, then gam and exp(G_last - G)
-    {
-      u32x4_t* fr = reinterpret_cast<u32x4_t*>(base);
-      for (int f = w; f < 12; f += kTWaves) {
-        const int mf = f % 6;
-        const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
-        const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
-        const int t = 16 * tt + r;
-        if (f < 6) {
-          uint32_t wp[4], wpp[4];
+
+      // ================= 3. the blocks of T below the diagonal, by block
+      // substitution: T_ij = -T_ii sum_{k = j .. i-1} A_ik T_kj
+      for (int dist = 1; dist < 4; ++dist) {
+        const int i = w + dist, j = w;
+        if (i < 4) {
+          f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+          for (int k = j; k < i; ++k)
+            x = mma_f32(x, Af + (16 * i) * kSA + 16 * k, kSA, Tf + (16 * k) * kST + 16 * j, kST, lane);
+          float* xs = Xs + w * 16 * 20;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int s4 = 32 * kb + 16 * hh + 4 * g;
-            const f32x4 tv = *reinterpret_cast<const f32x4*>(Tf + t * kST + s4);
-            const f32x4 bs = *reinterpret_cast<const f32x4*>(Bet + s4);
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(Gam + s4);
+          for (int e = 0; e < 4; ++e) xs[acc_row(lane, e) * 20 + acc_col(lane)] = x[e];
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+          y = mma_f32(y, Tf + (16 * i) * kST + 16 * i, kST, xs, 20, lane);
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              float a2[2], b2[2];
+          for (int e = 0; e < 4; ++e) Tf[(16 * i + acc_row(lane, e)) * kST + 16 * j + acc_col(lane)] = -y[e];
+        }
+        __syncthreads();
+      }
+
+      // ================= 4. the record: T' = T diag(beta gam) and T'' = T diag(beta)
+      // formed in bf16 straight into their fragments (lower triangle), the M
+      // blocks, then gam and exp(G_last - G)
+      {
+        u32x4_t* fr = reinterpret_cast<u32x4_t*>(base);
+        for (int f = w; f < 12; f += kTWaves) {
+          const int mf = f % 6;
+          const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
+          const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
+          const int t = 16 * tt + r;
+          if (f < 6) {
+            uint32_t wp[4], wpp[4];
 #pragma unroll
-              for (int k = 0; k < 2; ++k) {
-                const int c = 2 * h2 + k;
-                const float x = (s4 + c <= t) ? tv[c] : 0.0f;
-                b2[k] = x * bs[c];
-                a2[k] = b2[k] * gm[c];
+            for (int hh = 0; hh < 2; ++hh) {
+              const int s4 = 32 * kb + 16 * hh + 4 * g;
+              const f32x4 tv = *reinterpret_cast<const f32x4*>(Tf + t * kST + s4);
+              const f32x4 bs = *reinterpret_cast<const f32x4*>(Bet + s4);
+              const f32x4 gm = *reinterpret_cast<const f32x4*>(Gam + s4);
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                float a2[2], b2[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                  const int cix = 2 * h2 + k;
+                  const float x = (s4 + cix <= t) ? tv[cix] : 0.0f;
+                  b2[k] = x * bs[cix];
+                  a2[k] = b2[k] * gm[cix];
+                }
+                wp[2 * hh + h2] = static_cast<uint32_t>(to_bf16(a2[0])) | (static_cast<uint32_t>(to_bf16(a2[1])) << 16);
+                wpp[2 * hh + h2] = static_cast<uint32_t>(to_bf16(b2[0])) | (static_cast<uint32_t>(to_bf16(b2[1])) << 16);
               }
-              wp[2 * hh + h2] = static_cast<uint32_t>(to_bf16(a2[0])) | (static_cast<uint32_t>(to_bf16(a2[1])) << 16);
-              wpp[2 * hh + h2] = static_cast<uint32_t>(to_bf16(b2[0])) | (static_cast<uint32_t>(to_bf16(b2[1])) << 16);
             }
+            __builtin_nontemporal_store(u32x4_t{wp[0], wp[1], wp[2], wp[3]}, fr + f * 64 + lane);
+            __builtin_nontemporal_store(u32x4_t{wpp[0], wpp[1], wpp[2], wpp[3]}, fr + (f + 6) * 64 + lane);
+          } else {
+            const bf16_t* row = Ms + t * kSC;
+            const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * g);
+            const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * g);
+            __builtin_nontemporal_store(u32x4_t{lo.x, lo.y, hi.x, hi.y}, fr + (f + 6) * 64 + lane);
           }
-          __builtin_nontemporal_store(u32x4_t{wp[0], wp[1], wp[2], wp[3]}, fr + f * 64 + lane);
-          __builtin_nontemporal_store(u32x4_t{wpp[0], wpp[1], wpp[2], wpp[3]}, fr + (f + 6) * 64 + lane);
-        } else {
-          const bf16_t* row = Ms + t * kSC;
-          const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * g);
-          const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * g);
-          __builtin_nontemporal_store(u32x4_t{lo.x, lo.y, hi.x, hi.y}, fr + (f + 6) * 64 + lane);
+        }
+        if (tid < 32) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>((tid < 16 ? Gam : Kf) + 4 * (tid & 15));
+          __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(base + kTRecTail) + tid);
         }
       }
-      if (tid < 32) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>((tid < 16 ? Gam : Kf) + 4 * (tid & 15));
-        __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(base + kTRecTail) + tid);
-      }
+      __syncthreads();  // A, M and T are rewritten by the next head or unit
     }
-    __syncthreads();  // the LDS is restaged for the next item
   }
 }
 
@@ -1666,14 +1705,22 @@ hipError_t launch_prep(const ScanParams& p, unsigned char* ws, size_t rec_bytes,
 template <typename IO, int DK>
 hipError_t launch_trec(const ScanParams& p, unsigned char* ws, const int32_t* cs, const int2* info, int items,
                        hipStream_t stream) {
-  constexpr int bytes = TPrepLds<DK>::kBytes;
+  // value heads of one q/k head in pairs where the ratio is even
+  const bool pairs = p.ratio % 2 == 0;
+  const int units = pairs ? items / 2 : items;
   const int slots = 2 * prep_workgroups();
-  const unsigned grid = static_cast<unsigned>(items < slots ? items : slots);
-  auto kern = p.gates.raw ? chunk_trec_kernel<IO, DK, true> : chunk_trec_kernel<IO, DK, false>;
-  hipError_t e = set_lds(kern, bytes);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kTThreads), bytes, stream, p, ws, cs, info, items);
-  return hipGetLastError();
+  const unsigned grid = static_cast<unsigned>(units < slots ? units : slots);
+  auto launch = [&](auto kern, int bytes) {
+    hipError_t e = set_lds(kern, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kTThreads), bytes, stream, p, ws, cs, info, units);
+    return hipGetLastError();
+  };
+  if (pairs)
+    return p.gates.raw ? launch(chunk_trec_kernel<IO, DK, true, 2>, TPrepLds<DK, 2>::kBytes)
+                       : launch(chunk_trec_kernel<IO, DK, false, 2>, TPrepLds<DK, 2>::kBytes);
+  return p.gates.raw ? launch(chunk_trec_kernel<IO, DK, true, 1>, TPrepLds<DK, 1>::kBytes)
+                     : launch(chunk_trec_kernel<IO, DK, false, 1>, TPrepLds<DK, 1>::kBytes);
 }
 
 // The row-split state pass reads the full record (W, diag(gam) Q, Kt^T, M,
