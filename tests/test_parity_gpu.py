@@ -310,6 +310,10 @@ CHUNKED = [
     (1, 2, 128, 200, [130], True, True),
     (4, 4, 64, 64, [1, 2, 65, 128], True, False),
     (1, 1, 128, 8, [300], False, True),
+    # head ratio 4: value heads in pairs, 544 units, so the two pairs of a q/k
+    # head are placed on one XCD; head ratio 3: one value head per unit
+    (8, 32, 128, 64, [1500, 600], False, True),
+    (1, 3, 64, 32, [100, 37], True, False),
 ]
 
 
