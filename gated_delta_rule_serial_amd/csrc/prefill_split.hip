@@ -966,6 +966,7 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
 
 // ---------------------------------------------------------------- pass 2
 constexpr int kStateWaves = 4;
+constexpr int kStateTouchAhead = 1;  // one-buffer state pass: chunks between a line's touch and its load
 
 // Global and LDS address spaces, as the direct global-to-LDS load takes them.
 #define GDN_GLOBAL(ptr) ((const __attribute__((address_space(1))) void*)(ptr))
@@ -1033,8 +1034,10 @@ struct StateLds {
 // partials and apply the norm, with the gate rows loaded a chunk ahead.
 // ONE (64-column blocks, no norm): one chunk buffer, and two workgroups per
 // compute unit, so that one's loads and barriers overlap the other's products:
-// each chunk ends with a barrier, the next chunk's loads, the output stores
-// of this one and a second barrier.
+// each chunk starts with the output stores of the one before and a touch of
+// the next chunk's lines (into L2), and ends with a barrier, the next chunk's
+// loads and a second barrier.  The stores go first so that no output store is
+// waited for with the loads, and their LDS reads wait for no load.
 template <typename IO, int DK, int SL, bool NORM, bool ONE>
 __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_eu(ONE ? 2 : 1, ONE ? 2 : 1))) void
 chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
@@ -1169,6 +1172,44 @@ chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
 #pragma unroll
     for (int e = 0; e < ISS; ++e) issue(j, dst, e);
   };
+  // ONE: the chunk's loads are issued only after its predecessor is done, so
+  // their latency would be paid in full every chunk.  Instead, at the start of
+  // chunk j every workgroup touches its share of the 128-byte lines of chunk
+  // j + kStateTouchAhead (one 4-byte load per line and thread): the K and Q
+  // rows split over the per_group workgroups of the q/k head, the record over
+  // the column blocks of the value head, the V rows its own (at most 256 lines:
+  // any beyond are left to the loads).  The lines then come from L2 when the
+  // chunk's loads are issued.  A touch's value is used at the next touch, long
+  // after it has landed, so no early wait falls on it.
+  constexpr int kLinesKQ = kC * DK * 2 / 128;  // K lines of a chunk (as many Q lines)
+  constexpr int kLinesV = kC * NC * 2 / 128;
+  constexpr int kLinesF = static_cast<int>(kTRecBytes / 128);
+  const int member = r % per_group;
+  const int n_kq = (2 * kLinesKQ - member + per_group - 1) / per_group;
+  const int n_f = (kLinesF - cb + p.col_blocks - 1) / p.col_blocks;
+  const int n_touch = n_kq + kLinesV + n_f;
+  int tv = 0;
+  auto touch_line = [&](int j, int x) __attribute__((always_inline)) {
+    x = min(x, n_touch - 1);
+    const int c0 = t_begin + j * kC;
+    const int i = member + per_group * x;  // K then Q lines, when x < n_kq
+    const int ikq = i < kLinesKQ ? i : i - kLinesKQ;
+    const int xv = x - n_kq;              // V rows, then record lines
+    const int xf = cb + p.col_blocks * (xv - kLinesV);
+    const int row = x < n_kq ? ikq / (kLinesKQ / kC) : min(xv, kC - 1);
+    const size_t trow = static_cast<size_t>(c0 + min(row, t_end - 1 - c0));
+    const unsigned char* a =
+        x < n_kq ? reinterpret_cast<const unsigned char*>((i < kLinesKQ ? kg : qg) + trow * qk_stride + hq * DK) +
+                       128 * (ikq % (kLinesKQ / kC))
+        : xv < kLinesV ? reinterpret_cast<const unsigned char*>(vg + trow * v_stride + h * d_v + min(cb * NC, d_v - 8))
+                       : ws + (static_cast<size_t>(c_first + j) * p.h_v + h) * kTRecBytes + 128 * static_cast<size_t>(xf);
+    return *reinterpret_cast<const int*>(a);
+  };
+  auto touch = [&](int j) __attribute__((always_inline)) {
+    asm volatile("" ::"v"(tv));  // the previous touch's value, used
+    tv = touch_line(min(j, nchunks - 1), tid);
+    __builtin_amdgcn_sched_barrier(0);  // issued here, not sunk to the chunk's end
+  };
   // A operand of rows 16 tt + (l % 16) of a K or Q buffer, keys 32 kb + 4 g .. +3
   // and 32 kb + 16 + 4 g .. +3 (g = l / 16)
   auto rows_frag = [&](const bf16_t* X, int tt, int kb) __attribute__((always_inline)) {
@@ -1276,7 +1317,8 @@ chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
     // the next chunk's loads are spread over this chunk's products (a burst
     // would stall the wave on the memory pipeline while its MFMAs wait)
     const bool more = j + 1 < nchunks;
-    if (!ONE && og != nullptr && j > 0) store_out(j - 1);
+    if constexpr (ONE) touch(j + kStateTouchAhead);
+    if (og != nullptr && j > 0) store_out(j - 1);
     if (og != nullptr) load_gate(j);
     const bf16_t* Kc = cur.k;
     const bf16_t* Qc = cur.q;
@@ -1432,22 +1474,25 @@ chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
     if constexpr (ONE) {
       __syncthreads();  // every wave is done with this chunk's K, Q, V and record
       if (more) issue_all(j + 1, nxt);
-      if (og != nullptr) store_out(j);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's share of the next buffer has landed
     __syncthreads();                     // the next buffer is complete; this one may be refilled
   };
 
-  if (nchunks > 0) {
-    issue_all(0, buf_of(std::integral_constant<int, 0>{}));
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-  }
+  if (nchunks > 0) issue_all(0, buf_of(std::integral_constant<int, 0>{}));
+  // on every path, so that no load of the initial state is left in flight
+  // into the chunk loop (a wait for it there would also wait for the touches)
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
+  if constexpr (ONE) {
+    for (int j = 1; j < kStateTouchAhead && j < nchunks; ++j) touch(j);
+  }
   for (int j = 0; j < nchunks; j += 2) {
     chunk(j, std::integral_constant<int, 0>{});
     if (j + 1 < nchunks) chunk(j + 1, std::integral_constant<int, 1>{});
   }
-  if (!ONE && og != nullptr && nchunks > 0) store_out(nchunks - 1);
+  if (og != nullptr && nchunks > 0) store_out(nchunks - 1);
+  if constexpr (ONE) asm volatile("" ::"v"(tv));
 
   // ---- final state
   if (p.sN != nullptr && has_state) {
