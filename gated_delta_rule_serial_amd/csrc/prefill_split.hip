@@ -762,8 +762,17 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
       }
     }
   };
-  // one head's A and M tiles from the raw products, in the order products() left them
-  auto epilogue = [&](int hs) __attribute__((always_inline)) {
+  // No A or T tile above the diagonal is ever read (the solve reads below the
+  // diagonal of its block, the block substitution the lower blocks, the record
+  // masks the upper part), so in a pair of heads the second head's diagonal
+  // block w waits there: its A tile, formed with the first head's tiles, and
+  // its T block, solved beside the first head's, sit in the upper tile U(w) of
+  // Af and of Tf, (0,1), (0,2), (0,3) and (1,2) for w = 0 .. 3.
+  static_assert(kST == L_::SA, "A and T share the row stride");
+  const int upper_off = (w < 3 ? 0 : 16 * kSA) + 16 * (w < 3 ? w + 1 : 2);
+  // one head's A and M tiles from the raw products, in the order products() left
+  // them; with diag_next also the next head's diagonal A tile, into U(w)
+  auto epilogue = [&](int hs, bool diag_next) __attribute__((always_inline)) {
     const double* Gd = reinterpret_cast<const double*>(smem + L_::kGd) + hs * kC;
     const float* Bet = reinterpret_cast<const float*>(smem + L_::kBet) + hs * kC;
     const int wm = 3 - w;
@@ -784,6 +793,15 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
           for (int i = 0; i < 4; ++i) {
             const float a = bt[i] * dec[i] * acc[i];
             Af[(t0 + i) * kSA + s_] = (s_ < t0 + i) ? a : 0.0f;
+          }
+          if (NH == 2 && diag_next && cb == tb) {
+            const f32x4 dec1 = tile_decay(Gd + kC, tb, cb);
+            const f32x4 bt1 = *reinterpret_cast<const f32x4*>(Bet + kC + t0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float a = bt1[i] * dec1[i] * acc[i];
+              Af[upper_off + acc_row(lane, i) * kSA + acc_col(lane)] = (s_ < t0 + i) ? a : 0.0f;
+            }
           }
         } else {
 #pragma unroll
@@ -857,14 +875,23 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
       unsigned char* base = ws + (static_cast<size_t>(c) * p.h_v + h0 + hs) * kTRecBytes;
 
       // ---- this head's A and M tiles, then the diagonal 16 x 16 block w of
-      // T = (I + A)^-1 by forward substitution (one column per lane; lanes
-      // 16-63 repeat lanes 0-15)
-      epilogue(hs);
+      // T = (I + A)^-1 by forward substitution, one column per lane: lanes
+      // 0-15 this head's, lanes 16-31 in a pair the second head's (from and to
+      // the upper tiles U(w)), the other lanes repeat them.  The second head
+      // of a pair moves its solved block into place.
+      epilogue(hs, hs == 0);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the diagonal block is in LDS for this wave's reads
       __builtin_amdgcn_wave_barrier();
-      {
+      if (NH == 2 && hs == 1) {
+        if (lane < 16) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            Tf[(16 * w + rr) * kST + 16 * w + lane] = Tf[upper_off + rr * kST + lane];
+        }
+      } else {
         const int cc = lane & 15;
-        const float* Ab = Af + (16 * w) * kSA + 16 * w;
+        const int boff = NH == 2 && (lane & 16) ? upper_off : (16 * w) * kSA + 16 * w;
+        const float* Ab = Af + boff;
         float d[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
@@ -876,9 +903,9 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
           }
           d[rr] = x0 + x1;
         }
-        if (lane < 16) {
+        if (lane < (NH == 2 ? 32 : 16)) {
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) Tf[(16 * w + rr) * kST + 16 * w + cc] = d[rr];
+          for (int rr = 0; rr < 16; ++rr) Tf[boff + rr * kST + cc] = d[rr];
         }
       }
       // the next unit's inputs, in flight while this one computes
