@@ -220,23 +220,27 @@ gdn_status plan_prefill(const gdn_problem& p, int32_t num_seqs, int32_t total_to
   const bool wide_ok = gdn::wide_supported(p.io_dtype, p.d_k, p.d_v, sp.gates, window);
   const bool wide_ws = wide_ok && p.workspace != nullptr &&
                        p.workspace_bytes >= gdn::wide_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
-  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) || wide_ws;
+  // bfloat16 I/O in two passes: any rule (the gated and linear rules only there)
+  const bool split_ok = gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window);
+  const bool split_ws = split_ok && p.workspace != nullptr &&
+                        p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v,
+                                                                        sp.gates.deltas != 0);
+  const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) || wide_ws || split_ws;
   if (p.algorithm == GDN_ALGO_CHUNKED && !can_chunk)
     return fail(GDN_ERR_UNSUPPORTED,
-                "%s: the chunked algorithm needs bfloat16 I/O with d_k 64 or 128 and d_v a multiple of 8, or "
-                "float32 I/O with d_k 128 or 256, d_v a multiple of 16 up to 256 and a workspace of "
-                "gdn_prefill_workspace_size bytes; and the gated-delta or delta rule with a per-head decay "
-                "and no state history (got %s, d_k=%d, d_v=%d, rule=%d, decay_per_key=%d, state_window=%d%s)",
+                "%s: the chunked algorithm needs bfloat16 I/O with d_k 64 or 128 and d_v a multiple of 8 (the "
+                "gated and linear rules: d_v up to 256 and a workspace of gdn_prefill_workspace_size bytes), or "
+                "float32 I/O with d_k 128 or 256, d_v a multiple of 16 up to 256, a workspace and the gated-delta "
+                "or delta rule; and a per-head decay and no state history (got %s, d_k=%d, d_v=%d, rule=%d, "
+                "decay_per_key=%d, state_window=%d%s)",
                 fn, io_name(p.io_dtype), p.d_k, p.d_v, p.rule, p.decay_per_key, window,
-                wide_ok && !wide_ws ? ", no or too small a workspace" : "");
+                (wide_ok && !wide_ws) || (split_ok && !split_ws) ? ", no or too small a workspace" : "");
   const bool chunked = p.algorithm == GDN_ALGO_CHUNKED ||
                        (p.algorithm == GDN_ALGO_AUTO && can_chunk && (!wide_ws || gdn::wide_auto(p.d_k)) &&
                         static_cast<int64_t>(total_tokens) >= 64 * static_cast<int64_t>(num_seqs));
   const bool wide = chunked && wide_ws;
   // the two-pass chunked form when the caller's workspace holds it
-  const bool split = chunked && !wide && gdn::split_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) &&
-                     p.workspace != nullptr &&
-                     p.workspace_bytes >= gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  const bool split = chunked && !wide && split_ws;
   const bool norm = p.norm_gate != nullptr;
   plan->norm = norm ? 2 : 0;
   if (wide) {
@@ -248,7 +252,7 @@ gdn_status plan_prefill(const gdn_problem& p, int32_t num_seqs, int32_t total_to
       plan->cols = 128;
       plan->norm = 1;
     } else {
-      plan->cols = gdn::split_takes_rows_kernel(p.d_k, p.d_v, num_seqs * p.h_v)
+      plan->cols = gdn::split_takes_rows_kernel(p.d_k, p.d_v, num_seqs * p.h_v, sp.gates.deltas != 0)
                        ? 16
                        : gdn::split_columns_per_block(p.d_v, num_seqs * p.h_v);
     }
@@ -516,7 +520,7 @@ GDN_EXPORT gdn_status gdn_prefill_workspace_size(const gdn_problem* problem, int
     return ok();
   }
   if (!gdn::split_supported(p.io_dtype == GDN_BF16, p.d_k, p.d_v, gates, p.state_window)) return ok();
-  *bytes = gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v);
+  *bytes = gdn::split_workspace_bytes(num_seqs, total_tokens, p.h_v, p.d_k, p.d_v, gates.deltas != 0);
   return ok();
 }
 
@@ -597,7 +601,7 @@ GDN_EXPORT gdn_status gdn_prefill_query_plan(const gdn_problem* problem, int32_t
       if (pl.norm == 1) {
         plan->state_workgroups = units8;
         std::snprintf(k, kn, "chunk_table_kernel + chunk_trec_kernel + chunk_state_kernel (gated RMSNorm fused)");
-      } else if (gdn::split_takes_rows_kernel(p.d_k, p.d_v, units)) {
+      } else if (gdn::split_takes_rows_kernel(p.d_k, p.d_v, units, gate_args(problem).deltas != 0)) {
         plan->state_workgroups = units8 * ((p.d_v + 15) / 16);
         std::snprintf(k, kn, "chunk_table_kernel + chunk_prep_kernel + chunk_rows_kernel");
       } else {

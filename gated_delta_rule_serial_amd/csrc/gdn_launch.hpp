@@ -169,7 +169,7 @@ int split_columns_per_block(int d_v, int units);
 // store (128-column blocks own whole rows of up to 128 columns; taken where
 // the column rule picks 128-column blocks anyway).
 bool split_fuses_norm(int d_v, int units);
-size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v);
+size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v, bool deltas);
 hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t stream);
 // The chunk table at the head of a two-pass workspace: cs [N + 1] int32 (the
 // chunks before each sequence), then info [bound] int2 (first token, tokens of
@@ -202,7 +202,7 @@ int scan_columns_per_wave(const ScanParams& p);
 bool scan_takes_plain_kernel(const ScanParams& p);
 // Whether the bf16 two-pass state pass runs the row-split chunk_rows_kernel
 // (else chunk_state_kernel with split_columns_per_block columns).
-bool split_takes_rows_kernel(int d_k, int d_v, int units);
+bool split_takes_rows_kernel(int d_k, int d_v, int units, bool deltas);
 
 // Compute units of the current device (queried once per device; 256 when
 // there is no device to ask).  Thread-safe.

@@ -631,6 +631,9 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
 
   const int hpu = p.h_v / NH;                       // units per chunk
   const int total = cs[p.num_seqs] * hpu;           // live units; the grid covers a bound
+  // the gated and linear rules (no delta correction): the record holds T'' = I
+  // and T' = 0, so the state pass takes D = V
+  const bool plain = !p.gates.deltas;
   const int n_units = units < total ? units : total;
   const int tid = static_cast<int>(threadIdx.x);
   // wave-uniform, and the compiler is told so: branches on w must skip
@@ -683,10 +686,12 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
       const int hh = at.h + hs;
       const size_t gi = static_cast<size_t>(tl) * p.h_v + hh;
       const size_t bi = p.gates.beta_shared ? static_cast<size_t>(tl) : gi;
-      const IO* bsrc = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
-      const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : bsrc;
-      rg[hs] = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : bi];
-      rbt[hs] = reinterpret_cast<const uint16_t*>(bsrc)[bi];
+      // a rule without the decay or the delta correction reads K's first
+      // element in place of the gate it lacks (loaded, not used)
+      const IO* bsrc = p.gates.deltas ? static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta) : kg;
+      const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : kg;
+      rg[hs] = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : 0];
+      rbt[hs] = reinterpret_cast<const uint16_t*>(bsrc)[p.gates.deltas ? bi : 0];
       if constexpr (RAW) {
         rAl[hs] = p.gates.A_log[hh];
         rdt[hs] = p.gates.dt_bias[hh];
@@ -853,6 +858,7 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
             b = widen_bits16<IO>(rbt[hs]);
           }
           gv = fmaxf(gv, kMinLogDecay);
+          if (!p.gates.deltas) b = 1.0f;
         }
         const double G = wave_prefix_sum(static_cast<double>(gv) * kLog2e, lane);
         reinterpret_cast<double*>(smem + L_::kGd)[hs * kC + lane] = G;
@@ -882,7 +888,9 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
       epilogue(hs, hs == 0);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the diagonal block is in LDS for this wave's reads
       __builtin_amdgcn_wave_barrier();
-      if (NH == 2 && hs == 1) {
+      if (plain) {
+        // no delta correction: T = I, nothing to solve
+      } else if (NH == 2 && hs == 1) {
         if (lane < 16) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr)
@@ -921,7 +929,7 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
 
       // ================= 3. the blocks of T below the diagonal, by block
       // substitution: T_ij = -T_ii sum_{k = j .. i-1} A_ik T_kj
-      for (int dist = 1; dist < 4; ++dist) {
+      for (int dist = 1; dist < (plain ? 1 : 4); ++dist) {
         const int i = w + dist, j = w;
         if (i < 4) {
           f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -964,9 +972,10 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
                   const int cix = 2 * h2 + k;
-                  const float x = (s4 + cix <= t) ? tv[cix] : 0.0f;
+                  // without the delta correction T = I: T'' = I and T' = 0 (D = V)
+                  const float x = plain ? (s4 + cix == t ? 1.0f : 0.0f) : (s4 + cix <= t) ? tv[cix] : 0.0f;
                   b2[k] = x * bs[cix];
-                  a2[k] = b2[k] * gm[cix];
+                  a2[k] = plain ? 0.0f : b2[k] * gm[cix];
                 }
                 wp[2 * hh + h2] = static_cast<uint32_t>(to_bf16(a2[0])) | (static_cast<uint32_t>(to_bf16(a2[1])) << 16);
                 wpp[2 * hh + h2] = static_cast<uint32_t>(to_bf16(b2[0])) | (static_cast<uint32_t>(to_bf16(b2[1])) << 16);
@@ -1801,7 +1810,8 @@ template <typename IO, int DK, int DVT>
 hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, int32_t* cs, const int2* info,
                       int chunk_bound, hipStream_t stream) {
   const int units = p.num_seqs * p.h_v;
-  const bool rows = DK == 128 && split_rows(p.d_k, p.d_v, units);
+  // the row-split pair forms its record for the delta rules only
+  const bool rows = DK == 128 && p.gates.deltas && split_rows(p.d_k, p.d_v, units);
   if (chunk_bound > 0 && p.h_v > 0) {
     const int items = chunk_bound * p.h_v;
     // Nontemporal record stores ahead of the column-block state pass (the
@@ -1832,8 +1842,8 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
 }
 
 // Bytes of one (chunk, value head) record for the state pass that runs.
-size_t record_bytes(int d_k, int d_v, int units) {
-  if (split_rows(d_k, d_v, units)) {
+size_t record_bytes(int d_k, int d_v, int units, bool deltas) {
+  if (deltas && split_rows(d_k, d_v, units)) {
     const int dvt = pad16(d_v) > 128 ? 16 : 8;
     return Rec(d_k, 16 * dvt).bytes;
   }
@@ -1846,13 +1856,16 @@ int chunk_bound_of(int num_seqs, int total_tokens) {
 
 }  // namespace
 
+// Any of the four rules: without the delta correction the small-record
+// preparation writes T'' = I and T' = 0 (the column-block state pass then
+// takes D = V), so those rules run the column-block pair whatever the units.
 bool split_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window) {
-  return chunked_supported(io_bf16, d_k, d_v, gates, window) && d_v <= 256;
+  return io_bf16 && (d_k == 64 || d_k == 128) && d_v % 8 == 0 && d_v <= 256 && !gates.per_key && window == 0;
 }
 
 int split_columns_per_block(int d_v, int units) { return split_columns(d_v, units); }
 
-bool split_takes_rows_kernel(int d_k, int d_v, int units) { return split_rows(d_k, d_v, units); }
+bool split_takes_rows_kernel(int d_k, int d_v, int units, bool deltas) { return deltas && split_rows(d_k, d_v, units); }
 
 // The fused norm needs 128-column blocks; it is taken where the column rule
 // picks them anyway.  There it beats the separate norm pass (16 x 2048 tokens:
@@ -1878,16 +1891,16 @@ hipError_t launch_chunk_table(const int32_t* cu, int num_seqs, int total_tokens,
   return hipGetLastError();
 }
 
-size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v) {
+size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, int d_v, bool deltas) {
   if (num_seqs <= 0) return 0;
-  return table_bytes(num_seqs, total_tokens) +
-         static_cast<size_t>(chunk_bound_of(num_seqs, total_tokens)) * h_v * record_bytes(d_k, d_v, num_seqs * h_v);
+  return table_bytes(num_seqs, total_tokens) + static_cast<size_t>(chunk_bound_of(num_seqs, total_tokens)) * h_v *
+                                                   record_bytes(d_k, d_v, num_seqs * h_v, deltas);
 }
 
 hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t stream) {
   if (p.num_seqs <= 0) return hipSuccess;
   const int dvt = pad16(p.d_v) > 128 ? 16 : 8;
-  const size_t rec_bytes = record_bytes(p.d_k, p.d_v, p.num_seqs * p.h_v);
+  const size_t rec_bytes = record_bytes(p.d_k, p.d_v, p.num_seqs * p.h_v, p.gates.deltas != 0);
   // total tokens: the caller's count (the kernels clamp the sequences to it)
   const int T = p.total_tokens;
   int32_t* cs = static_cast<int32_t*>(workspace);

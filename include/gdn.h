@@ -90,9 +90,12 @@ typedef enum gdn_algorithm {
    * operand split into two bf16 parts and each product formed as
    * hi.hi + hi.lo + lo.hi (float32-class accuracy), d_k of 128 or 256, d_v a
    * multiple of 16 up to 256, and a workspace (the two-pass form only).
-   * Both need the gated-delta or delta rule with a per-head decay, no state
-   * history, and a true decay (g <= 0, as the raw-gate prologue always
-   * gives); otherwise GDN_ERR_UNSUPPORTED when requested explicitly. */
+   * Both need a per-head decay (or none), no state history and a true decay
+   * (g <= 0, as the raw-gate prologue always gives).  The gated-delta and
+   * delta rules run in every form; the gated and linear rules (no delta
+   * correction, so no triangular solve) in the bfloat16 two-pass form only,
+   * with d_v up to 256 and a workspace.  Otherwise GDN_ERR_UNSUPPORTED when
+   * requested explicitly. */
   GDN_ALGO_CHUNKED = 2
 } gdn_algorithm;
 

@@ -293,7 +293,12 @@ def test_prefill_workspace_size(lib):
     per_rec = (per_rec + 255) // 256 * 256
     bound = 4096 // 64 + 1
     assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * per_rec
-    for kw in (dict(algorithm=gdn.GDN_ALGO_SERIAL), dict(io_dtype=gdn.GDN_F16), dict(d_k=96), dict(rule=2),
+    # the gated and linear rules (no delta correction) always take the small record
+    for rule in (2, 3):
+        assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky, rule=rule, beta=None)), 1, 4096,
+                                              ctypes.byref(size)) == gdn.GDN_OK
+        assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * (18 * 1024 + 1024), rule
+    for kw in (dict(algorithm=gdn.GDN_ALGO_SERIAL), dict(io_dtype=gdn.GDN_F16), dict(d_k=96), dict(d_v=36),
                dict(decay_per_key=1), dict(state_window=2)):
         st = lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**{**chunky, **kw})), 8, 33173, ctypes.byref(size))
         assert st == gdn.GDN_OK and size.value == 0, kw

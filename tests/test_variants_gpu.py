@@ -149,6 +149,51 @@ def test_chunked_rules_and_shared_beta(rule, shared, two_pass):
     check(fin, torch.from_numpy(rf), TOL[dt], "final state")
 
 
+PLAIN_GEOMS = [
+    # (h_qk, h_v, d_k, d_v, seqlens, raw gates): head ratio 2 (paired preparation units), 3 (one head
+    # per unit), d_v 256 (four 64-column state blocks), a ragged d_v, a long sequence (the linear
+    # rule's state grows with it)
+    (16, 32, 128, 128, [150, 70, 1], True),
+    (2, 6, 64, 64, [200, 0, 65], False),
+    (1, 1, 128, 256, [300], False),
+    (2, 2, 64, 40, [129, 64], True),
+    (4, 8, 128, 128, [2048], False),
+]
+
+
+@pytest.mark.parametrize("geom", PLAIN_GEOMS, ids=lambda g: f"h{g[0]}x{g[1]}_dk{g[2]}_dv{g[3]}_T{sum(g[4])}")
+@pytest.mark.parametrize("rule", ["gated", "linear"])
+def test_chunked_two_pass_plain_rules(rule, geom):
+    """The gated and linear rules (no delta correction) in the bfloat16 two-pass chunked form,
+    as AUTO plans it with a workspace: the preparation pass writes T'' = I and T' = 0, so the
+    state pass takes D = V."""
+    h_qk, h_v, d_k, d_v, lens, raw = geom
+    dt = torch.bfloat16
+    say(f"[chunked-plain] {rule} {geom}")
+    inp, raw_in, g64, b64 = _setup(h_qk, h_v, d_k, d_v, dt, lens, seed=540)
+    gates = _gate_kwargs(raw, raw_in, g64, b64, dt)
+    if not raw:
+        g64, b64 = gates["g"].double().numpy(), gates["beta"].double().numpy()
+    n, T = len(lens), inp.total_tokens
+    ws = gdn.prefill_workspace_size(h_qk, h_v, d_k, d_v, dt, n, T, rule=rule)
+    plan = gdn.prefill_query_plan(h_qk, h_v, d_k, d_v, dt, n, T, raw_gates=raw, workspace_bytes=ws, rule=rule)
+    assert plan["form"] == "chunked_two_pass" and "chunk_trec_kernel" in plan["kernels"], plan
+    out, fin, _ = _gpu_prefill(inp, gates, raw=raw, rule=rule, per_key=False, shared=False, algorithm="auto",
+                               two_pass=True)
+    ro, rf = _oracle(inp, g64, b64, rule=rule, per_key=False, shared=False)
+    check(out, torch.from_numpy(ro), TOL[dt], "out")
+    check(fin, torch.from_numpy(rf), TOL[dt], "final state")
+
+
+def test_chunked_plain_rule_needs_workspace():
+    """Without a workspace the gated and linear rules have no chunked form: AUTO scans, CHUNKED is refused."""
+    plan = gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 2, 4096, rule="gated")
+    assert plan["form"] == "serial", plan
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 2, 4096, rule="linear", algorithm="chunked")
+    assert e.value.status == gdn.GDN_ERR_UNSUPPORTED and "workspace" in str(e.value)
+
+
 @pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("per_key,shared", [(False, False), (True, False), (False, True), (True, True)],
                          ids=["plain", "perkey", "sharedbeta", "both"])
