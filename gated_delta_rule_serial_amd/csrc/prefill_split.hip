@@ -100,9 +100,9 @@ __device__ __forceinline__ int seq_hi(const int32_t* cu, int n, int T) {
 __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int num_seqs, int T, int32_t* cs,
                                                            int2* info) {
   constexpr int kLongChunks = 16, kMaxLong = 256;
-  __shared__ int part[1024];
+  __shared__ int wsum[16];
   __shared__ int nlong;
-  __shared__ int2 longs[kMaxLong];  // (sequence, its first chunk)
+  __shared__ int4 longs[kMaxLong];  // (first token, end, first chunk) of a long sequence
   const int tid = static_cast<int>(threadIdx.x);
   if (tid == 0) nlong = 0;
   const int per = (num_seqs + 1023) / 1024;
@@ -110,22 +110,27 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
   auto chunks = [&](int n) { return (seq_hi(cu, n, T) - seq_lo(cu, n, T) + kC - 1) / kC; };
   int sum = 0;
   for (int n = a; n < b; ++n) sum += chunks(n);
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // the chunk counts' prefix over the threads: within each wave by lane
+  // shifts, then over the 16 waves' totals (one barrier)
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
   }
-  int run = part[tid] - sum;
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < wv; ++i) before += wsum[i];
+  int run = before + incl - sum;
   for (int n = a; n < b; ++n) {
     cs[n] = run;
     const int lo = seq_lo(cu, n, T), hi = seq_hi(cu, n, T);
     const int cnt = (hi - lo + kC - 1) / kC;
     const int slot = cnt > kLongChunks ? atomicAdd(&nlong, 1) : kMaxLong;
     if (slot < kMaxLong) {
-      longs[slot] = make_int2(n, run);
+      longs[slot] = make_int4(lo, hi, run, 0);
       run += cnt;
     } else {
       for (int t = lo; t < hi; t += kC) info[run++] = make_int2(t, min(kC, hi - t));
@@ -133,12 +138,12 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
   }
   __syncthreads();
   const int m = min(nlong, kMaxLong);
+  // the long sequences' bounds come from LDS: no global load waits between them
   for (int i = 0; i < m; ++i) {
-    const int n = longs[i].x, c0 = longs[i].y;
-    const int lo = seq_lo(cu, n, T), hi = seq_hi(cu, n, T);
-    for (int t = lo + kC * tid; t < hi; t += kC * 1024) info[c0 + (t - lo) / kC] = make_int2(t, min(kC, hi - t));
+    const int4 L = longs[i];
+    for (int t = L.x + kC * tid; t < L.y; t += kC * 1024) info[L.z + (t - L.x) / kC] = make_int2(t, min(kC, L.y - t));
   }
-  if (tid == 1023) cs[num_seqs] = part[1023];
+  if (tid == 1023) cs[num_seqs] = before + incl;
 }
 
 // ---------------------------------------------------------------- pass 1
@@ -615,7 +620,7 @@ struct TPrepLds {
 // same q/k head (NH = 2 where the head ratio is even): their K K^T and Q K^T
 // are one product, formed once and kept in registers, and each head then
 // takes its own decay and gates (A, M), substitution and record in turn.
-template <typename IO, int DK, bool RAW, int NH>
+template <typename IO, int DK, bool RAW, int NH, bool PLAIN>
 __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, unsigned char* ws, const int32_t* cs,
                                                                const int2* __restrict__ info, int units) {
   using L_ = TPrepLds<DK, NH>;
@@ -631,9 +636,9 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
 
   const int hpu = p.h_v / NH;                       // units per chunk
   const int total = cs[p.num_seqs] * hpu;           // live units; the grid covers a bound
-  // the gated and linear rules (no delta correction): the record holds T'' = I
-  // and T' = 0, so the state pass takes D = V
-  const bool plain = !p.gates.deltas;
+  // PLAIN, the gated and linear rules (no delta correction): the record holds
+  // T'' = I and T' = 0, so the state pass takes D = V
+  constexpr bool plain = PLAIN;
   const int n_units = units < total ? units : total;
   const int tid = static_cast<int>(threadIdx.x);
   // wave-uniform, and the compiler is told so: branches on w must skip
@@ -688,10 +693,10 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
       const size_t bi = p.gates.beta_shared ? static_cast<size_t>(tl) : gi;
       // a rule without the decay or the delta correction reads K's first
       // element in place of the gate it lacks (loaded, not used)
-      const IO* bsrc = p.gates.deltas ? static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta) : kg;
+      const IO* bsrc = PLAIN ? kg : static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
       const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : kg;
       rg[hs] = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : 0];
-      rbt[hs] = reinterpret_cast<const uint16_t*>(bsrc)[p.gates.deltas ? bi : 0];
+      rbt[hs] = reinterpret_cast<const uint16_t*>(bsrc)[PLAIN ? 0 : bi];
       if constexpr (RAW) {
         rAl[hs] = p.gates.A_log[hh];
         rdt[hs] = p.gates.dt_bias[hh];
@@ -858,7 +863,7 @@ __global__ __launch_bounds__(kTThreads) void chunk_trec_kernel(ScanParams p, uns
             b = widen_bits16<IO>(rbt[hs]);
           }
           gv = fmaxf(gv, kMinLogDecay);
-          if (!p.gates.deltas) b = 1.0f;
+          if (PLAIN) b = 1.0f;
         }
         const double G = wave_prefix_sum(static_cast<double>(gv) * kLog2e, lane);
         reinterpret_cast<double*>(smem + L_::kGd)[hs * kC + lane] = G;
@@ -1797,11 +1802,17 @@ hipError_t launch_trec(const ScanParams& p, unsigned char* ws, const int32_t* cs
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kTThreads), bytes, stream, p, ws, cs, info, units);
     return hipGetLastError();
   };
+  auto by_rule = [&](auto raw, auto nh) {
+    constexpr bool R = decltype(raw)::value;
+    constexpr int N = decltype(nh)::value;
+    return p.gates.deltas ? launch(chunk_trec_kernel<IO, DK, R, N, false>, TPrepLds<DK, N>::kBytes)
+                          : launch(chunk_trec_kernel<IO, DK, R, N, true>, TPrepLds<DK, N>::kBytes);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   if (pairs)
-    return p.gates.raw ? launch(chunk_trec_kernel<IO, DK, true, 2>, TPrepLds<DK, 2>::kBytes)
-                       : launch(chunk_trec_kernel<IO, DK, false, 2>, TPrepLds<DK, 2>::kBytes);
-  return p.gates.raw ? launch(chunk_trec_kernel<IO, DK, true, 1>, TPrepLds<DK, 1>::kBytes)
-                     : launch(chunk_trec_kernel<IO, DK, false, 1>, TPrepLds<DK, 1>::kBytes);
+    return p.gates.raw ? by_rule(T_{}, std::integral_constant<int, 2>{}) : by_rule(F_{}, std::integral_constant<int, 2>{});
+  return p.gates.raw ? by_rule(T_{}, std::integral_constant<int, 1>{}) : by_rule(F_{}, std::integral_constant<int, 1>{});
 }
 
 // The row-split state pass reads the full record (W, diag(gam) Q, Kt^T, M,

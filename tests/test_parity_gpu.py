@@ -394,6 +394,22 @@ def test_two_pass_chunk_table_many_long_sequences(dtype):
     check(fin, rf, TOL[dtype], "final state")
 
 
+def test_two_pass_chunk_table_more_sequences_than_threads():
+    """More sequences than the table kernel's 1024 threads: each thread sums
+    and writes two or three sequences, empty and 1-token ones among them."""
+    gen = torch.Generator().manual_seed(33)
+    lens = torch.randint(0, 90, (2300,), generator=gen).tolist()
+    lens[5], lens[6], lens[2299] = 0, 1, 2000  # empty, 1 token, one long sequence at the end
+    shape = _shape("varlen_prefill_8seq", h_qk=1, h_v=1, d_k=64, d_v=16, io_dtype=torch.bfloat16, init_state=True)
+    inp = synth.generate(shape, seqlens=lens, seed=22)
+    g, beta = gates_for(inp)
+    say(f"[chunk table] {len(lens)} sequences, {inp.total_tokens} tokens")
+    out, fin = gpu_prefill(inp, g, beta, algorithm="chunked", two_pass=True)
+    ro, rf = oracle_prefill(inp, g, beta)
+    check(out, ro, TOL[torch.bfloat16], "out")
+    check(fin, rf, TOL[torch.bfloat16], "final state")
+
+
 def test_chunked_unsupported_is_reported():
     shape = _shape(init_state=False)  # float32 I/O, d_k 16
     inp = synth.generate(shape, seqlens=[64])
