@@ -54,24 +54,24 @@ __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~st
 
 // Shared operand fragments of the state pass, per (chunk, value head): W and
 // diag(gam) Q as 16 x 32 blocks (4 token tiles x DK / 32 key blocks), Kt^T
-// (DK / 16 key tiles x 2 token blocks) and the six lower blocks of M.  Each is
+// (DK / 16 key tiles x 2 token blocks), the six lower blocks of M and the six
+// of T'' = T diag(beta) (the state pass forms U = T'' V itself).  Each is
 // stored as the 64 lanes x 16 bytes one wave loads for a 16x16x32 MFMA, with
 // the contraction index of a block permuted so that lane group g holds
 // k = 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3: the order in which two
 // stacked accumulator tiles already hold the other operand (state rows, or
 // the tokens of D), so that operand never leaves the registers.
 __host__ __device__ constexpr int frags_w(int dk) { return 4 * (dk / 32); }
-__host__ __device__ constexpr int frags_total(int dk) { return 2 * frags_w(dk) + 2 * (dk / 16) + 6; }
+__host__ __device__ constexpr int frags_total(int dk) { return 2 * frags_w(dk) + 2 * (dk / 16) + 12; }
 // M block (token tile tt, token block kb), kb <= tt / 2
 __host__ __device__ constexpr int m_frag(int tt, int kb) { return tt < 2 ? tt : 2 + 2 * (tt - 2) + kb; }
 
 // One (chunk, value head) record of the workspace.
 struct Rec {
-  size_t frag, u, g, bytes;
-  __host__ __device__ Rec(int dk, int dvp) {
-    frag = 0;                                               // fragments [frags_total][64 lanes] x 16 B
-    u = frag + static_cast<size_t>(frags_total(dk)) * 1024;  // U      [4][dvp / 16][64 lanes][4] f32
-    g = u + static_cast<size_t>(kC) * dvp * 4;              // gam_last f32 (a 256-byte slot)
+  size_t frag, g, bytes;
+  __host__ __device__ explicit Rec(int dk) {
+    frag = 0;                                                // fragments [frags_total][64 lanes] x 16 B
+    g = frag + static_cast<size_t>(frags_total(dk)) * 1024;  // gam_last f32 (a 256-byte slot)
     bytes = align256(g + 256);
   }
 };
@@ -85,7 +85,6 @@ constexpr int kTFrags = 18;
 constexpr size_t kTRecTail = static_cast<size_t>(kTFrags) * 1024;
 constexpr size_t kTRecBytes = kTRecTail + 1024;
 
-__host__ __device__ inline int pad16(int x) { return (x + 15) & ~15; }
 
 __device__ __forceinline__ int seq_lo(const int32_t* cu, int n, int T) { return min(max(cu[n], 0), T); }
 __device__ __forceinline__ int seq_hi(const int32_t* cu, int n, int T) {
@@ -147,15 +146,13 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
 }
 
 // ---------------------------------------------------------------- pass 1
-template <int DK, int DVT>
+template <int DK>
 struct PrepLds {
   static constexpr int SK = DK + 8;
-  static constexpr int DVP = 16 * DVT;
   static constexpr int kKs = 0;                          // K rows  [C][SK] bf16
   static constexpr int kQs = kKs + kC * SK * 2;          // Q rows  [C][SK] bf16
   static constexpr int kKT = kQs + kC * SK * 2;          // K^T     [DK][SC] bf16
-  static constexpr int kVt = kKT + DK * kSC * 2;         // V^T     [DVP][SC] bf16
-  static constexpr int kAf = kVt + DVP * kSC * 2;        // A       [C][SA] f32 (later T', T'')
+  static constexpr int kAf = kKT + DK * kSC * 2;         // A       [C][SA] f32 (later T', T'')
   static constexpr int kTf = kAf + kC * kSA * 4;         // T       [C][ST] f32
   static constexpr int kMs = kTf + kC * kST * 4;         // M       [C][SC] bf16
   static constexpr int kXs = kMs + kC * kSC * 2;         // solve scratch [4][16][20] f32
@@ -168,21 +165,19 @@ struct PrepLds {
   static_assert(kBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
-// Persistent: one workgroup per CU (the LDS holds one) walks the (chunk,
-// value head) items blockIdx.x, + gridDim.x, ...; the next item's K, Q, V rows
-// and gates are loaded into registers while the current one computes.
-template <typename IO, int DK, int DVT, bool RAW>
+// Persistent: one workgroup per CU walks the (chunk, value head) items
+// blockIdx.x, + gridDim.x, ...; the next item's K and Q rows and gates are
+// loaded into registers while the current one computes.
+template <typename IO, int DK, bool RAW>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsigned char* ws, size_t rec_bytes,
                                                               const int32_t* cs, const int2* __restrict__ info, int items,
                                                               int nt_stores) {
-  using L_ = PrepLds<DK, DVT>;
+  using L_ = PrepLds<DK>;
   constexpr int SK = L_::SK;
-  constexpr int DVP = L_::DVP;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* Ks = reinterpret_cast<bf16_t*>(smem + L_::kKs);
   bf16_t* Qs = reinterpret_cast<bf16_t*>(smem + L_::kQs);
   bf16_t* KT = reinterpret_cast<bf16_t*>(smem + L_::kKT);
-  bf16_t* Vt = reinterpret_cast<bf16_t*>(smem + L_::kVt);
   float* Af = reinterpret_cast<float*>(smem + L_::kAf);
   bf16_t* Tp = reinterpret_cast<bf16_t*>(smem + L_::kAf);
   bf16_t* Tpp = reinterpret_cast<bf16_t*>(smem + L_::kAf + kC * kSC * 2);
@@ -197,18 +192,15 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   const int T = p.total_tokens;
   const int total = cs[p.num_seqs] * p.h_v;  // live items; the grid covers a bound
   const int n_items = items < total ? items : total;
-  const int d_v = p.d_v;
   const int tid = static_cast<int>(threadIdx.x);
   // wave-uniform, and the compiler is told so: branches on w must skip
   // their MFMAs, which run whatever the execution mask
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const Rec rec(DK, DVP);
+  const Rec rec(DK);
   const IO* qg = static_cast<const IO*>(p.q);
   const IO* kg = static_cast<const IO*>(p.k);
-  const IO* vg = static_cast<const IO*>(p.v);
   const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
-  const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
 
   // item i is chunk c = i / h_v (first token, tokens from the chunk table), head h = i % h_v
   struct Where {
@@ -231,10 +223,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   constexpr int VPR = DK / 8;
   constexpr int KQ_IT = kC * VPR / kThreads;
-  constexpr int VPV = DVP / 8;
-  constexpr int V_IT = kC * VPV / kThreads;  // V rows are staged in token pairs: V_IT / 2 (pair, 8 columns) per thread
-  static_assert(KQ_IT >= 1 && V_IT >= 1, "block shape");
-  u32x4 rk[KQ_IT], rq[KQ_IT], rv[V_IT];
+  static_assert(KQ_IT >= 1, "block shape");
+  u32x4 rk[KQ_IT], rq[KQ_IT];
   // gate inputs of token (chunk start + lane) as raw 16-bit patterns, and the
   // head's A_log, dt_bias: converted where they are used, so that no
   // conversion waits for the loads right after they are issued
@@ -249,14 +239,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       const size_t off = static_cast<size_t>(at.t0 + t) * qk_stride + static_cast<size_t>(hq) * DK + c8;
       rk[it] = *reinterpret_cast<const u32x4*>(kg + off);
       rq[it] = *reinterpret_cast<const u32x4*>(qg + off);
-    }
-#pragma unroll
-    for (int it = 0; it < V_IT; ++it) {
-      const int v = tid + (it >> 1) * kThreads;
-      // rows past the chunk and columns past d_v: clamped here, zeroed when staged
-      const int t = min(2 * (v % (kC / 2)) + (it & 1), at.Lc - 1), c8 = min((v / (kC / 2)) * 8, d_v - 8);
-      rv[it] = *reinterpret_cast<const u32x4*>(vg + static_cast<size_t>(at.t0 + t) * v_stride +
-                                               static_cast<size_t>(at.h) * d_v + c8);
     }
     {
       // gate inputs of token (chunk start + lane), clamped into the chunk (wave 0
@@ -304,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
     const int Lc = at.Lc;
     unsigned char* base = ws + (static_cast<size_t>(at.c) * p.h_v + h) * rec_bytes;
 
-    // ================= 1. stage K, Q rows and V^T; gates and the prefix sum of the log-decay
+    // ================= 1. stage K and Q rows; gates and the prefix sum of the log-decay
 #pragma unroll
     for (int it = 0; it < KQ_IT; ++it) {
       const int v = tid + it * kThreads;
@@ -312,21 +294,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       const u32x4 zero = {0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(Ks + t * SK + c8) = t < Lc ? rk[it] : zero;
       *reinterpret_cast<u32x4*>(Qs + t * SK + c8) = t < Lc ? rq[it] : zero;
-    }
-    // V^T from token pairs: one 4-byte word (tokens t, t + 1) per column; the
-    // 32 pairs of a wave fill 32 consecutive words and its two 8-column
-    // groups sit 32 banks apart, so the writes are free of bank conflicts
-#pragma unroll
-    for (int it = 0; it < V_IT; it += 2) {
-      const int v = tid + (it >> 1) * kThreads;
-      const int t = 2 * (v % (kC / 2)), c8 = (v / (kC / 2)) * 8;
-      const bool col_ok = c8 < d_v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (col_ok && t < Lc) ? ((e & 1) ? (rv[it][e >> 1] >> 16) : (rv[it][e >> 1] & 0xffffu)) : 0u;
-        const uint32_t b = (col_ok && t + 1 < Lc) ? ((e & 1) ? (rv[it + 1][e >> 1] >> 16) : (rv[it + 1][e >> 1] & 0xffffu)) : 0u;
-        *reinterpret_cast<uint32_t*>(Vt + (c8 + e) * kSC + t) = a | (b << 16);
-      }
     }
     if (w == 0) {
       float g = 0.0f, b = 0.0f;
@@ -501,11 +468,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
   }
   __syncthreads();
 
-  // ================= 4. the record: W and U from MFMA accumulators, then diag(gam) Q, Kt^T and M from LDS
+  // ================= 4. the record: W from MFMA accumulators, then diag(gam) Q, Kt^T, M and T'' from LDS
   {
     typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
     constexpr int KB = DK / 32;
-    constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16), NF = frags_total(DK);
+    constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16), FT = FM + 6, NF = frags_total(DK);
     u32x4_t* fr = reinterpret_cast<u32x4_t*>(base + rec.frag);
     auto put = [&](int f, u32x4_t piece) __attribute__((always_inline)) {
       if (nt_stores)
@@ -528,25 +495,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
       lo = mma_range(lo, KT + (32 * kb) * kSC, kSC, Tp + (16 * tw) * kSC, kSC, 0, kmax_w, lane);
       hi = mma_range(hi, KT + (32 * kb + 16) * kSC, kSC, Tp + (16 * tw) * kSC, kSC, 0, kmax_w, lane);
       put(tw * KB + kb, u32x4_t{bf2(lo[0], lo[1]), bf2(lo[2], lo[3]), bf2(hi[0], hi[1]), bf2(hi[2], hi[3])});
-    }
-    // U = T'' V in accumulator order (f32); the token tile is the mirror of tw,
-    // so that every wave has the same number of products
-    {
-      const int tu = 3 - tw;
-      const int kmax_u = tu < 2 ? 32 : 64;
-      float* ug = reinterpret_cast<float*>(base + rec.u);
-      constexpr int UTW = DVT / 2;
-#pragma unroll
-      for (int e = 0; e < UTW; ++e) {
-        const int cj = (w >> 2) * UTW + e;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = mma_range(acc, Tpp + (16 * tu) * kSC, kSC, Vt + (16 * cj) * kSC, kSC, 0, kmax_u, lane);
-        f32x4* dst = reinterpret_cast<f32x4*>(ug + ((static_cast<size_t>(tu) * DVT + cj) * 64 + lane) * 4);
-        if (nt_stores)
-          __builtin_nontemporal_store(acc, dst);
-        else
-          *dst = acc;
-      }
     }
     const int g = lane >> 4, r = lane & 15;
     // k values of this lane's slots, relative to the block: 4 g + e (e < 4), 16 + 4 g + (e - 4)
@@ -574,10 +522,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanParams p, unsi
         const int kb = (f - FK) & 1;
         piece = scaled(pick(KT + (16 * ((f - FK) >> 1) + r) * kSC, kb), [&](int e) { return Kf[32 * kb + slot_k(e)]; });
       } else {
-        const int mf = f - FM;
+        // the six lower blocks of M, then of T'' (the same block order)
+        const int mf = f < FT ? f - FM : f - FT;
         const int tt = mf < 2 ? mf : 2 + ((mf - 2) >> 1);
         const int kb = mf < 2 ? 0 : ((mf - 2) & 1);
-        piece = pick(Ms + (16 * tt + r) * kSC, kb);
+        piece = pick((f < FT ? Ms : Tpp) + (16 * tt + r) * kSC, kb);
       }
       put(f, piece);
     }
@@ -1567,12 +1516,11 @@ chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
 constexpr int kRowWaves = 4;
 constexpr int kRowTouchAhead = 3;  // chunks between a record's touch and its use
 
-template <int DVT>
 __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p, const unsigned char* ws,
                                                                    size_t rec_bytes, const int32_t* cs, int units8) {
   constexpr int DK = 128;
   constexpr int KB = DK / 32;
-  constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16);
+  constexpr int FQ = frags_w(DK), FK = 2 * frags_w(DK), FM = FK + 2 * (DK / 16), FT = FM + 6;
   __shared__ __align__(16) f32x4 xpart[2][kRowWaves][4][64];  // [buffer][wave][token tile][lane]
   __shared__ __align__(16) f32x4 ypart[2][kRowWaves][4][64];
   __shared__ __align__(16) f32x4 dt[4][64];                    // D per token tile
@@ -1589,7 +1537,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = 16 * ct + acc_col(lane);
   const bool col_ok = col < d_v;
-  const Rec rec(DK, 16 * DVT);
+  const Rec rec(DK);
   bf16_t* og = static_cast<bf16_t*>(p.out);
   const size_t v_stride = static_cast<size_t>(p.h_v) * d_v;
 
@@ -1638,6 +1586,47 @@ __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) Qf[tt] = frag(rb, FQ + tt * KB + w);
   };
+  // The chunk's V rows over this column tile (64 x 16, 32-byte rows) pass
+  // through LDS, double-buffered by chunk parity: every lane loads 16 bytes at
+  // the top of the chunk before (waves 0 and 1 write them, before that chunk's
+  // second barrier), and each wave reads its B operand of U = T'' V
+  // transposed: lane l gets column l % 16 of tokens 32 kb + 4 g .. +3 and
+  // 32 kb + 16 + 4 g .. +3 (g = l / 16), the permuted order of the record's
+  // fragments.  Rows past the sequence repeat its last row (T'' is zero
+  // there); columns past d_v repeat the last 8.
+  __shared__ __align__(16) bf16_t vbuf[2][kC * 16];
+  const int v_row = 32 * (w & 1) + (lane >> 1);
+  const bf16_t* vg = static_cast<const bf16_t*>(p.v) + static_cast<size_t>(h) * d_v + min(16 * ct + 8 * (lane & 1), d_v - 8);
+  u32x4 vrow;
+  auto load_v = [&](int j) __attribute__((always_inline)) {
+    const int c0 = t_begin + kC * min(j, nchunks - 1);
+    vrow = *reinterpret_cast<const u32x4*>(vg + static_cast<size_t>(min(c0 + v_row, t_end - 1)) * v_stride);
+  };
+  auto store_v = [&](int j) __attribute__((always_inline)) {
+    if (w < 2) *reinterpret_cast<u32x4*>(vbuf[j & 1] + v_row * 16 + 8 * (lane & 1)) = vrow;
+  };
+  auto v_operand = [&](int j, int kb) __attribute__((always_inline)) {
+    const bf16_t* vb = vbuf[j & 1] + (32 * kb + 4 * (lane >> 4) + ((lane & 15) >> 2)) * 16 + 4 * (lane & 3);
+    const s16x4 a = lds_read_tr(vb);
+    const s16x4 b = lds_read_tr(vb + 16 * 16);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(bf16x8, s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+  };
+  // U of token tile w and this column tile, T'' (its lower blocks, loaded with
+  // the chunk's other operands a chunk ahead; the second block is loaded by
+  // every wave, used by waves 2 and 3) times the V rows: formed at the end of
+  // the chunk before, off the chain from S to the next S
+  bf16x8 TA[2];
+  f32x4 Uw;
+  auto load_t = [&](int j) __attribute__((always_inline)) {
+    const unsigned char* rb = record(j);
+    TA[0] = frag(rb, FT + m_frag(w, 0));
+    TA[1] = frag(rb, FT + m_frag(w, 1));
+  };
+  auto form_u = [&](int j) __attribute__((always_inline)) {
+    Uw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(TA[0], v_operand(j, 0), (f32x4{0.0f, 0.0f, 0.0f, 0.0f}), 0, 0, 0);
+    if (w >= 2) Uw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(TA[1], v_operand(j, 1), Uw, 0, 0, 0);
+  };
   // The column tiles of a unit share each chunk's record through one L2 (they
   // sit units8 blocks apart: on one XCD).  Each tile touches its share of the
   // record kRowTouchAhead chunks ahead, one 4-byte load per 128-byte line, so
@@ -1647,12 +1636,20 @@ __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p
   const int ntiles = (d_v + 15) / 16;
   const int lines = static_cast<int>(rec_bytes / 128);
   const int per_tile = (lines + ntiles - 1) / ntiles;
-  const bool touching = per_tile <= 64 * kRowWaves;
+  // Threads past the tile's record lines touch the tile's V rows of the same
+  // chunk (the line that holds its 16 columns of each row), which nothing
+  // else brings in ahead of the gathers of load_v.
+  const bool touching = per_tile + kC <= 64 * kRowWaves;
   int touched = 0, tv = 0;
   auto touch = [&](int j) __attribute__((always_inline)) {
     touched += tv;
     const int line = min(ct * per_tile + tid, lines - 1);
-    tv = *reinterpret_cast<const int*>(record(j) + static_cast<size_t>(line) * 128);
+    const int vrow = min(t_begin + kC * min(j, nchunks - 1) + (tid - per_tile), t_end - 1);
+    const unsigned char* a =
+        tid < per_tile ? record(j) + static_cast<size_t>(line) * 128
+                       : reinterpret_cast<const unsigned char*>(static_cast<const bf16_t*>(p.v) + static_cast<size_t>(vrow) * v_stride +
+                                                                static_cast<size_t>(h) * d_v + 16 * ct);
+    tv = *reinterpret_cast<const int*>(a);
   };
 
   auto chunk = [&](int j) __attribute__((always_inline)) {
@@ -1660,16 +1657,19 @@ __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p
     const int Lc = min(kC, t_end - t0);
     const unsigned char* rb = record(j);
     const int buf = j & 1;
+    load_v(j + 1);  // first: its wait, before the second barrier, then covers no later load
 
     bf16x8 KtA[2][2];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) KtA[r][kb] = frag(rb, FK + 2 * (2 * w + r) + kb);
+    // the second block of M is used by waves 2 and 3 only, but loaded by all
+    // (m_frag(w, 1) is block w itself for w < 2): a load chosen by a branch
+    // would be waited for, with every load before it, where it joins
     bf16x8 MA[2];
     MA[0] = frag(rb, FM + m_frag(w, 0));
-    MA[1] = w >= 2 ? frag(rb, FM + m_frag(w, 1)) : MA[0];
-    const f32x4 Uw = *reinterpret_cast<const f32x4*>(rb + rec.u + ((static_cast<size_t>(w) * DVT + ct) * 64 + lane) * 16);
+    MA[1] = frag(rb, FM + m_frag(w, 1));
     const float gam_last = *reinterpret_cast<const float*>(rb + rec.g);
 
     // ---- 1. partials over this wave's rows (U of token tile w folded into
@@ -1686,6 +1686,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p
     for (int tt = 0; tt < 4; ++tt)
       ypart[buf][w][tt][lane] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Qf[tt], SB, (f32x4{0.0f, 0.0f, 0.0f, 0.0f}), 0, 0, 0);
     load_q(j + 1);
+    load_t(j + 1);
     if (touching) touch(j + kRowTouchAhead);
 
     // ---- 2. D of token tile w
@@ -1695,6 +1696,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p
       for (int ww = 1; ww < kRowWaves; ++ww) x += xpart[buf][ww][w][lane];
       dt[w][lane] = -x;
     }
+    store_v(j + 1);
     __syncthreads();
 
     // ---- 3. D as the B operand over tokens; the output of tile w; the state update
@@ -1721,11 +1723,17 @@ __global__ __launch_bounds__(64 * kRowWaves) void chunk_rows_kernel(ScanParams p
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KtA[r][1], DB[1], sacc, 0, 0, 0);
       S[r] = sacc;
     }
+    form_u(j + 1);  // the next chunk's V rows are in LDS since the second barrier
   };
 
   if (nchunks > 0) {
     load_w(0);
     load_q(0);
+    load_t(0);
+    load_v(0);
+    store_v(0);
+    __syncthreads();
+    form_u(0);
     for (int j = 0; j < nchunks; ++j) chunk(j);
   }
 
@@ -1768,18 +1776,18 @@ int split_columns(int d_v, int units) {
 }
 
 
-template <typename IO, int DK, int DVT>
+template <typename IO, int DK>
 hipError_t launch_prep(const ScanParams& p, unsigned char* ws, size_t rec_bytes, const int32_t* cs, const int2* info,
                        int items, int nt, hipStream_t stream) {
-  constexpr int bytes = PrepLds<DK, DVT>::kBytes;
+  constexpr int bytes = PrepLds<DK>::kBytes;
   const unsigned grid = static_cast<unsigned>(items < prep_workgroups() ? items : prep_workgroups());
   if (p.gates.raw) {
-    auto kern = chunk_prep_kernel<IO, DK, DVT, true>;
+    auto kern = chunk_prep_kernel<IO, DK, true>;
     hipError_t e = set_lds(kern, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
   } else {
-    auto kern = chunk_prep_kernel<IO, DK, DVT, false>;
+    auto kern = chunk_prep_kernel<IO, DK, false>;
     hipError_t e = set_lds(kern, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, stream, p, ws, rec_bytes, cs, info, items, nt);
@@ -1816,9 +1824,10 @@ hipError_t launch_trec(const ScanParams& p, unsigned char* ws, const int32_t* cs
 }
 
 // The row-split state pass reads the full record (W, diag(gam) Q, Kt^T, M,
-// U); the column-block pass reads K, Q and V itself and the T', T'', M record.
-template <typename IO, int DK, int DVT>
-hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, int32_t* cs, const int2* info,
+// T'') and V; the column-block pass reads K, Q and V itself and the T', T'', M
+// record.
+template <typename IO, int DK>
+hipError_t launch_split_passes(const ScanParams& p, unsigned char* ws, size_t rec_bytes, int32_t* cs, const int2* info,
                       int chunk_bound, hipStream_t stream) {
   const int units = p.num_seqs * p.h_v;
   // the row-split pair forms its record for the delta rules only
@@ -1828,7 +1837,7 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
     // Nontemporal record stores ahead of the column-block state pass (the
     // 8-sequence packed workload 1.07-1.08 against 1.09-1.10 ms); ahead of
     // the row-split pass they cost about 1 % (one 4096-token sequence).
-    const hipError_t e = rows ? launch_prep<IO, DK, DVT>(p, ws, rec_bytes, cs, info, items, 0, stream)
+    const hipError_t e = rows ? launch_prep<IO, DK>(p, ws, rec_bytes, cs, info, items, 0, stream)
                               : launch_trec<IO, DK>(p, ws, cs, info, items, stream);
     if (e != hipSuccess) return e;
   }
@@ -1837,7 +1846,7 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
     if (rows) {
       const int units8 = (units + 7) / 8 * 8;
       const unsigned rblocks = static_cast<unsigned>(units8) * static_cast<unsigned>((p.d_v + 15) / 16);
-      hipLaunchKernelGGL((chunk_rows_kernel<DVT>), dim3(rblocks), dim3(64 * kRowWaves), 0, stream, p, ws, rec_bytes, cs, units8);
+      hipLaunchKernelGGL(chunk_rows_kernel, dim3(rblocks), dim3(64 * kRowWaves), 0, stream, p, ws, rec_bytes, cs, units8);
       return hipGetLastError();
     }
   }
@@ -1854,10 +1863,7 @@ hipError_t launch_dvt(const ScanParams& p, unsigned char* ws, size_t rec_bytes, 
 
 // Bytes of one (chunk, value head) record for the state pass that runs.
 size_t record_bytes(int d_k, int d_v, int units, bool deltas) {
-  if (deltas && split_rows(d_k, d_v, units)) {
-    const int dvt = pad16(d_v) > 128 ? 16 : 8;
-    return Rec(d_k, 16 * dvt).bytes;
-  }
+  if (deltas && split_rows(d_k, d_v, units)) return Rec(d_k).bytes;
   return kTRecBytes;
 }
 
@@ -1910,7 +1916,6 @@ size_t split_workspace_bytes(int num_seqs, int total_tokens, int h_v, int d_k, i
 
 hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t stream) {
   if (p.num_seqs <= 0) return hipSuccess;
-  const int dvt = pad16(p.d_v) > 128 ? 16 : 8;
   const size_t rec_bytes = record_bytes(p.d_k, p.d_v, p.num_seqs * p.h_v, p.gates.deltas != 0);
   // total tokens: the caller's count (the kernels clamp the sequences to it)
   const int T = p.total_tokens;
@@ -1923,9 +1928,8 @@ hipError_t launch_prefill_split(ScanParams p, void* workspace, hipStream_t strea
   if (e != hipSuccess) return e;
   const int bound = chunk_bound_of(p.num_seqs, T);
   if (p.d_k == 128)
-    return dvt == 16 ? launch_dvt<bf16_t, 128, 16>(p, recs, rec_bytes, cs, info, bound, stream)
-                     : launch_dvt<bf16_t, 128, 8>(p, recs, rec_bytes, cs, info, bound, stream);
-  return launch_dvt<bf16_t, 64, 8>(p, recs, rec_bytes, cs, info, bound, stream);
+    return launch_split_passes<bf16_t, 128>(p, recs, rec_bytes, cs, info, bound, stream);
+  return launch_split_passes<bf16_t, 64>(p, recs, rec_bytes, cs, info, bound, stream);
 }
 
 }  // namespace gdn

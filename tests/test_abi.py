@@ -287,10 +287,9 @@ def test_prefill_workspace_size(lib):
     assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * per_rec
     # one sequence of 32 heads (32 x 8 16-column tiles fill the 256 compute units
     # assumed without a device) takes the row-split pass and the full record:
-    # operand fragments (W, diag(gam) Q: 16 each; Kt^T: 16; M: 6) of 1 KiB, U in f32, gam_last
+    # operand fragments (W, diag(gam) Q: 16 each; Kt^T: 16; M: 6; T'': 6) of 1 KiB, gam_last
     assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**chunky)), 1, 4096, ctypes.byref(size)) == gdn.GDN_OK
-    per_rec = (16 + 16 + 16 + 6) * 1024 + 64 * 128 * 4 + 16
-    per_rec = (per_rec + 255) // 256 * 256
+    per_rec = (16 + 16 + 16 + 6 + 6) * 1024 + 256
     bound = 4096 // 64 + 1
     assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 32 * per_rec
     # the gated and linear rules (no delta correction) always take the small record
