@@ -56,6 +56,11 @@ struct ScanParams {
   int32_t window;         // > 0: history of the last `window` states per sequence
   float* history;         // [N, window, h_v, d_k, d_v]
   NormEpilogue norm;      // the two-pass chunked form applies it when norm.gate != null
+  // The column-block state pass's order of the sequences (position -> sequence,
+  // a permutation of [0, num_seqs)) when num_ordered = num_seqs; else the
+  // identity.  Set from the host's sequence lengths (up to 64 sequences).
+  int32_t num_ordered;
+  uint8_t seq_order[64];
 };
 
 // Causal depthwise conv in front of the decode step: the step's q, k and v

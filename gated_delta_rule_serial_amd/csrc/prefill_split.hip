@@ -1078,7 +1078,8 @@ chunk_state_kernel(ScanParams p, const unsigned char* ws, const int32_t* cs) {
   const int unit = group * p.ratio + (r % per_group) / p.col_blocks;
   const int cb = r % p.col_blocks;
   const int h = unit % p.h_v;
-  const int n = unit / p.h_v;
+  // the host's order of the sequences, where it gives one (a permutation)
+  const int n = p.num_ordered == p.num_seqs ? static_cast<int>(p.seq_order[unit / p.h_v]) : unit / p.h_v;
   const int hq = h / p.ratio;
   const int d_v = p.d_v;
   const int T = p.total_tokens;
