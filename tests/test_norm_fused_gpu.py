@@ -155,3 +155,38 @@ def test_fused_matches_separate_pair():
     pair = gdn.gated_rmsnorm(o.reshape(T, -1), to_dev(gate).reshape(T, -1), to_dev(scale)).reshape(fused.shape)
     torch.cuda.synchronize()
     check_normed(fused.double().cpu(), pair.double().cpu(), gate, scale, "silu", TOL[torch.bfloat16], "fused vs pair")
+
+
+@pytest.mark.parametrize("rule,seqlens,form", [
+    ("gated", [70, 65, 130, 0, 64, 99, 71, 66, 200, 64, 80, 65, 64, 64, 90, 64, 3], "fused"),
+    ("linear", [70, 65, 130, 0, 64, 99, 71, 66, 200, 64, 80, 65, 64, 64, 90, 64, 3], "fused"),
+    ("gated", [300, 129, 70], "separate pass"),
+    ("linear", [300, 129, 70], "separate pass"),
+], ids=["gated_fused", "linear_fused", "gated_pass", "linear_pass"])
+def test_plain_rules_with_output_norm(rule, seqlens, form):
+    """The gated and linear rules (no delta correction) in the bf16 two-pass
+    form with the output norm: from 512 (sequence, head) units the state pass
+    runs its 128-column blocks and normalises in its stores, over the records
+    of the plain rules (T'' = I, T' = 0); below that, the separate pass."""
+    shape = W["varlen_prefill_8seq"]
+    inp = synth.generate(shape, seqlens=seqlens, seed=651)
+    T, n = inp.total_tokens, len(seqlens)
+    g, _ = gates_for(inp)
+    gate, scale = synth.output_norm_inputs(T, shape.h_v, shape.d_v, seed=652, io_dtype=torch.bfloat16)
+    ws = workspace_for(inp, rule=rule)
+    plan = gdn.prefill_query_plan(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, n, T,
+                                  workspace_bytes=ws.numel(), rule=rule, norm=True)
+    say(f"[norm prefill plain] {rule} {seqlens}: {plan}")
+    assert plan["form"] == "chunked_two_pass" and plan["norm"] == form, plan
+    out = torch.full((T, shape.h_v, shape.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty(n, shape.h_v, shape.d_k, shape.d_v, dtype=torch.float32, device="cuda")
+    gates = dict(g=to_dev(g)) if rule == "gated" else {}
+    gdn.gdn_prefill(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.cu_seqlens), out=out, final_state=fin,
+                    initial_state=to_dev(inp.initial_state), cu_seqlens_host=inp.cu_seqlens.tolist(), rule=rule,
+                    workspace=ws, norm_gate=to_dev(gate), norm_scale=to_dev(scale), **gates)
+    torch.cuda.synchronize()
+    ro, rf = oracle.default().prefill(inp.q, inp.k, inp.v, g.double().numpy() if rule == "gated" else None, None,
+                                      inp.cu_seqlens.numpy(), inp.initial_state, rule=rule)
+    tol = TOL[torch.bfloat16]
+    check_normed(out.double().cpu(), _ref(ro, gate, scale, "silu"), gate, scale, "silu", tol, "normed out")
+    check(fin.double().cpu(), torch.from_numpy(rf), tol, "final state")
