@@ -297,13 +297,15 @@ def gdn_prefill_slots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seql
                       state_pool: torch.Tensor, slots: torch.Tensor, *, out: Optional[torch.Tensor], g=None,
                       beta=None, a=None, b=None, A_log=None, dt_bias=None, scale: float = 0.0,
                       cu_seqlens_host: Optional[Sequence[int]] = None, slots_host: Optional[Sequence[int]] = None,
-                      algorithm: str = "auto", workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                      algorithm: str = "auto", workspace: Optional[torch.Tensor] = None, stream=None,
+                      **variant) -> None:
     """gdn_prefill_slots of include/gdn.h: sequence i runs from and writes back
-    state_pool[slots[i]] (float32 [num_slots, h_v, d_k, d_v])."""
+    state_pool[slots[i]] (float32 [num_slots, h_v, d_k, d_v]); ``variant`` as
+    for gdn_prefill."""
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
-                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm, workspace=workspace)
+                        A_log=A_log, dt_bias=dt_bias, algorithm=algorithm, workspace=workspace, **variant)
     n = cu_seqlens.numel() - 1
     _check(load().gdn_prefill_slots(ctypes.byref(prob), n, _ptr(cu_seqlens), _host_i32(cu_seqlens_host), T,
                                     _ptr(q), _ptr(k), _ptr(v), _ptr(state_pool), state_pool.shape[0], _ptr(slots),
@@ -313,12 +315,13 @@ def gdn_prefill_slots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seql
 def gdn_decode_step_slots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state_pool: torch.Tensor,
                           slots: torch.Tensor, out: torch.Tensor, *, g=None, beta=None, a=None, b=None,
                           A_log=None, dt_bias=None, scale: float = 0.0,
-                          slots_host: Optional[Sequence[int]] = None, stream=None) -> None:
-    """gdn_decode_step_slots of include/gdn.h: sequence i updates state_pool[slots[i]] in place."""
+                          slots_host: Optional[Sequence[int]] = None, stream=None, **variant) -> None:
+    """gdn_decode_step_slots of include/gdn.h: sequence i updates state_pool[slots[i]] in place;
+    ``variant``: rule, decay_per_key, beta_shared, norm_* (see make_problem)."""
     B, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     prob = make_problem(h_qk, h_v, d_k, d_v, q.dtype, scale=scale, g=g, beta=beta, a=a, b=b,
-                        A_log=A_log, dt_bias=dt_bias)
+                        A_log=A_log, dt_bias=dt_bias, **variant)
     _check(load().gdn_decode_step_slots(ctypes.byref(prob), B, _ptr(q), _ptr(k), _ptr(v), _ptr(state_pool),
                                         state_pool.shape[0], _ptr(slots), _host_i32(slots_host), _ptr(out),
                                         _stream(stream, q.device)))

@@ -185,6 +185,62 @@ def test_chunked_two_pass_plain_rules(rule, geom):
     check(fin, torch.from_numpy(rf), TOL[dt], "final state")
 
 
+@pytest.mark.parametrize("rule", ["gated", "linear", "delta"])
+def test_rules_through_slot_pool(rule):
+    """The rules other than gated delta through the slot pool: the two-pass
+    prefill (plain rules: the small plain record) and then one decode step
+    over the same pool.  Slot -1 is padding; untouched slots stay
+    bit-identical."""
+    h_qk, h_v, d_k, d_v, dt = 16, 32, 128, 128, torch.bfloat16
+    lens, slots = [70, 0, 33, 129], [5, -1, 2, 0]
+    inp, raw_in, g64, b64 = _setup(h_qk, h_v, d_k, d_v, dt, lens, seed=560, init=False)
+    gates = _gate_kwargs(False, raw_in, g64, b64, dt)
+    g64, b64 = gates["g"].double().numpy(), gates["beta"].double().numpy()
+    uses_g, uses_b = rule == "gated", rule == "delta"
+    kw = {k: to_dev(v) for k, v in gates.items() if (k == "g" and uses_g) or (k == "beta" and uses_b)}
+    n, T = len(lens), inp.total_tokens
+    gen = torch.Generator().manual_seed(561)
+    pool = torch.randn(6, h_v, d_k, d_v, generator=gen) * 0.05
+    pool_gpu = pool.cuda()
+    ws = gdn.prefill_workspace_size(h_qk, h_v, d_k, d_v, dt, n, T, rule=rule)
+    say(f"[rules-slots] {rule} slots={slots} workspace={ws}")
+    out = torch.full((T, h_v, d_v), float("nan"), dtype=dt, device="cuda")
+    gdn.gdn_prefill_slots(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.cu_seqlens), pool_gpu,
+                          torch.tensor(slots, dtype=torch.int32, device="cuda"), out=out,
+                          cu_seqlens_host=inp.cu_seqlens.tolist(), slots_host=slots, rule=rule,
+                          workspace=torch.empty(ws, dtype=torch.uint8, device="cuda"), **kw)
+    torch.cuda.synchronize()
+    s0 = torch.stack([pool[s] if s >= 0 else torch.zeros(pool.shape[1:]) for s in slots])
+    ro, rf = _oracle(dataclasses.replace(inp, initial_state=s0), g64, b64, rule=rule, per_key=False, shared=False)
+    ref_pool = pool.double().clone()
+    for i, s in enumerate(slots):
+        if s >= 0:
+            ref_pool[s] = torch.from_numpy(rf[i])
+    check(out.double().cpu(), torch.from_numpy(ro), TOL[dt], "prefill out")
+    check(pool_gpu.double().cpu(), ref_pool, TOL[dt], "pool after prefill")
+    for s in (1, 3, 4):
+        assert torch.equal(pool_gpu[s].cpu(), pool[s]), f"untouched slot {s} changed"
+    # one decode token per sequence over the pool the prefill left
+    dinp, draw, dg, db = _setup(h_qk, h_v, d_k, d_v, dt, [1] * n, seed=562, init=False)
+    dgates = _gate_kwargs(False, draw, dg, db, dt)
+    dg, db = dgates["g"].double().numpy(), dgates["beta"].double().numpy()
+    dkw = {k: to_dev(v) for k, v in dgates.items() if (k == "g" and uses_g) or (k == "beta" and uses_b)}
+    before = pool_gpu.double().cpu()
+    dout = torch.full((n, h_v, d_v), float("nan"), dtype=dt, device="cuda")
+    gdn.gdn_decode_step_slots(to_dev(dinp.q), to_dev(dinp.k), to_dev(dinp.v), pool_gpu,
+                              torch.tensor(slots, dtype=torch.int32, device="cuda"), dout, slots_host=slots,
+                              rule=rule, **dkw)
+    torch.cuda.synchronize()
+    s1 = torch.stack([before[s] if s >= 0 else torch.zeros(pool.shape[1:], dtype=torch.float64) for s in slots])
+    do, df = _oracle(dataclasses.replace(dinp, initial_state=s1), dg, db, rule=rule, per_key=False, shared=False)
+    ref_pool = before.clone()
+    for i, s in enumerate(slots):
+        if s >= 0:
+            ref_pool[s] = torch.from_numpy(df[i])
+    check(dout.double().cpu(), torch.from_numpy(do), TOL[dt], "decode out")
+    check(pool_gpu.double().cpu(), ref_pool, TOL[dt], "pool after decode")
+
+
 def test_chunked_plain_rule_needs_workspace():
     """Without a workspace the gated and linear rules have no chunked form: AUTO scans, CHUNKED is refused."""
     plan = gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 2, 4096, rule="gated")
