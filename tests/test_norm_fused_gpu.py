@@ -190,3 +190,63 @@ def test_plain_rules_with_output_norm(rule, seqlens, form):
     tol = TOL[torch.bfloat16]
     check_normed(out.double().cpu(), _ref(ro, gate, scale, "silu"), gate, scale, "silu", tol, "normed out")
     check(fin.double().cpu(), torch.from_numpy(rf), tol, "final state")
+
+
+def test_slot_pool_with_output_norm():
+    """The output norm through the slot-pool entry points: a two-pass prefill of
+    17 sequences (544 units: the fused state pass) into a pool of 20 slots,
+    one of them padding, then one decode step over the same slots (fused)."""
+    shape = W["varlen_prefill_8seq"]
+    lens = [70, 65, 130, 0, 64, 99, 71, 66, 200, 64, 80, 65, 64, 64, 90, 64, 3]
+    slots = [19, 0, 7, 3, -1, 12, 1, 18, 5, 9, 2, 16, 11, 4, 14, 8, 6]
+    n, num_slots = len(lens), 20
+    inp = synth.generate(dataclasses.replace(shape, init_state=False), seqlens=lens, seed=661)
+    T = inp.total_tokens
+    g, beta = gates_for(inp)
+    gen = torch.Generator().manual_seed(662)
+    pool = torch.randn(num_slots, shape.h_v, shape.d_k, shape.d_v, generator=gen) * 0.05
+    pool_gpu = pool.cuda()
+    slots_dev = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    gate, scale = synth.output_norm_inputs(T, shape.h_v, shape.d_v, seed=663, io_dtype=torch.bfloat16)
+    ws = workspace_for(inp)
+    plan = gdn.prefill_query_plan(shape.h_qk, shape.h_v, shape.d_k, shape.d_v, shape.io_dtype, n, T,
+                                  workspace_bytes=ws.numel(), norm=True)
+    say(f"[norm slots] prefill {plan}")
+    assert plan["norm"] == "fused", plan
+    out = torch.full((T, shape.h_v, shape.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_prefill_slots(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.cu_seqlens), pool_gpu, slots_dev,
+                          out=out, g=to_dev(g), beta=to_dev(beta), cu_seqlens_host=inp.cu_seqlens.tolist(),
+                          slots_host=slots, workspace=ws, norm_gate=to_dev(gate), norm_scale=to_dev(scale))
+    torch.cuda.synchronize()
+    s0 = torch.stack([pool[s] if s >= 0 else torch.zeros(pool.shape[1:]) for s in slots])
+    ro, rf = oracle.default().prefill(inp.q, inp.k, inp.v, g.double().numpy(), beta.double().numpy(),
+                                      inp.cu_seqlens.numpy(), s0)
+    ref_pool = pool.double().clone()
+    for i, s in enumerate(slots):
+        if s >= 0:
+            ref_pool[s] = torch.from_numpy(rf[i])
+    tol = TOL[torch.bfloat16]
+    check_normed(out.double().cpu(), _ref(ro, gate, scale, "silu"), gate, scale, "silu", tol, "prefill normed out")
+    check(pool_gpu.double().cpu(), ref_pool, tol, "pool after prefill")
+    for s in (10, 13, 15, 17):
+        assert torch.equal(pool_gpu[s].cpu(), pool[s]), f"untouched slot {s} changed"
+    # one decode token per sequence over the same slots, the norm fused in the step
+    dinp = synth.generate(dataclasses.replace(W["decode_b64"], num_seqs=n), seed=664)
+    dg, db = gates_for(dinp)
+    dgate, dscale = synth.output_norm_inputs(n, shape.h_v, shape.d_v, seed=665, io_dtype=torch.bfloat16)
+    before = pool_gpu.double().cpu()
+    dout = torch.full((n, shape.h_v, shape.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_decode_step_slots(to_dev(dinp.q), to_dev(dinp.k), to_dev(dinp.v), pool_gpu, slots_dev, dout,
+                              g=to_dev(dg), beta=to_dev(db), slots_host=slots, norm_gate=to_dev(dgate),
+                              norm_scale=to_dev(dscale))
+    torch.cuda.synchronize()
+    st = torch.stack([before[s] if s >= 0 else torch.zeros(pool.shape[1:], dtype=torch.float64)
+                      for s in slots]).numpy().copy()
+    do = oracle.default().decode_step(dinp.q, dinp.k, dinp.v, dg.double().numpy(), db.double().numpy(), st)
+    ref_pool = before.clone()
+    for i, s in enumerate(slots):
+        if s >= 0:
+            ref_pool[s] = torch.from_numpy(st[i])
+    check_normed(dout.double().cpu(), _ref(do, dgate, dscale, "silu"), dgate, dscale, "silu", tol,
+                 "decode normed out")
+    check(pool_gpu.double().cpu(), ref_pool, tol, "pool after decode")
