@@ -11,7 +11,8 @@
 //     Kt = diag(exp(G_last - G)) K
 // depend on the chunk alone, while
 //     D = U - W S,   O = scale diag(gam) Q S + M D,   S <- gam_last S + Kt^T D
-// carry the state from chunk to chunk.
+// carry the state from chunk to chunk.  The gated and linear rules have no
+// delta correction: A = 0, W = 0 and U = V, so D = V.
 //
 // Float32 I/O asks for float32-class products, which the bfloat16 matrix
 // cores give when each operand x is split into hi = bf16(x) and
@@ -193,6 +194,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     return qg + static_cast<size_t>(t0 + min(t, Lc - 1)) * qk_stride + static_cast<size_t>(hq) * DK;
   };
 
+  // Rules without the delta correction (gated, linear) write v as it is: A = 0,
+  // so T = I, with weight 1 in U = T diag(beta) V and 0 in W, and D = V.
+  const bool delta_rule = p.gates.deltas != 0;
   // ================= 1. gates, the prefix sum of the log-decay, decay factors
   if (w == 0) {
     float gv = 0.0f, b = 0.0f;
@@ -201,10 +205,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const size_t bi = p.gates.beta_shared ? static_cast<size_t>(t0 + lane) : gi;
       if constexpr (RAW) {
         gv = p.gates.decays ? gate_log_decay(static_cast<const float*>(p.gates.a)[gi], p.gates.A_log[h], p.gates.dt_bias[h]) : 0.0f;
-        b = gate_sigmoid(static_cast<const float*>(p.gates.b)[bi]);
+        b = delta_rule ? gate_sigmoid(static_cast<const float*>(p.gates.b)[bi]) : 1.0f;
       } else {
         gv = p.gates.decays ? static_cast<const float*>(p.gates.g)[gi] : 0.0f;
-        b = static_cast<const float*>(p.gates.beta)[bi];
+        b = delta_rule ? static_cast<const float*>(p.gates.beta)[bi] : 1.0f;
       }
       gv = fmaxf(gv, kMinLogDecay);
     }
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if (st <= tt && s <= t) {
           const float dec = fast_exp2(static_cast<float>(Gd[t] - Gd[s]));
           m = p.scale * dec * racc[st][i];
-          if (s < t) a = Bet[t] * dec * pacc[st][i];
+          if (s < t && delta_rule) a = Bet[t] * dec * pacc[st][i];
         }
         Af[t * kSF + s] = a;
         Mf[t * kSF + s] = m;
@@ -362,6 +366,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     float gq[4];                     // scale gam of this lane's Q rows
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) gq[tt] = p.scale * Gam[16 * tt + r16];
+    const float wgt = delta_rule ? 1.0f : 0.0f;  // W = 0 without the delta correction
     // every load of the wave's key blocks first: K^T slots (two key tiles x
     // two token blocks each), Q rows (four token tiles each)
     float xk[PAIRS][2][2][8], xqv[PAIRS][4][8];
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           for (int e = 0; e < 8; ++e) {
             const int tok = 32 * kb + slot_k(g, e);
             xe[e] = x[half][kb][e] * Eps[tok];
-            xg[e] = x[half][kb][e] * Gam[tok];
+            xg[e] = x[half][kb][e] * Gam[tok] * wgt;
           }
           const Split8 KE = split8(xe);
           store_frag(base + rec.kt + ((r * 2 + kb) * 2) * 1024, KE.hi, lane);
@@ -765,7 +770,7 @@ hipError_t launch_dk(const ScanParams& p, unsigned char* recs, size_t rec_bytes,
 }  // namespace
 
 bool wide_supported(int io_dtype, int d_k, int d_v, const GateArgs& gates, int window) {
-  return io_dtype == 0 && (d_k == 128 || d_k == 256) && d_v >= 16 && d_v <= 256 && d_v % 16 == 0 && gates.deltas &&
+  return io_dtype == 0 && (d_k == 128 || d_k == 256) && d_v >= 16 && d_v <= 256 && d_v % 16 == 0 &&
          !gates.per_key && window == 0;
 }
 

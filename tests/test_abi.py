@@ -328,8 +328,15 @@ def test_prefill_workspace_size_f32(lib):
         assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**d128, algorithm=algo)), 3, 1000,
                                               ctypes.byref(size)) == gdn.GDN_OK
         assert size.value == 256 + (bound * 8 + 255) // 256 * 256 + bound * 8 * rec_bytes(128, 48)
+    # every rule takes the same record (the gated and linear rules write W = 0 and U = V)
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**wide)), 1, 32768, ctypes.byref(size)) == gdn.GDN_OK
+    full = size.value
+    for rule in (1, 2, 3):
+        assert lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**wide, rule=rule)), 1, 32768,
+                                              ctypes.byref(size)) == gdn.GDN_OK
+        assert size.value == full, rule
     # geometries the float32 form does not serve
-    for kw in (dict(d_k=64), dict(d_v=24), dict(rule=2), dict(decay_per_key=1), dict(state_window=1),
+    for kw in (dict(d_k=64), dict(d_v=24), dict(decay_per_key=1), dict(state_window=1),
                dict(algorithm=gdn.GDN_ALGO_SERIAL)):
         st = lib.gdn_prefill_workspace_size(ctypes.byref(_prob(**{**wide, **kw})), 1, 32768, ctypes.byref(size))
         assert st == gdn.GDN_OK and size.value == 0, kw

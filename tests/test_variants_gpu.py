@@ -241,6 +241,39 @@ def test_rules_through_slot_pool(rule):
     check(pool_gpu.double().cpu(), ref_pool, TOL[dt], "pool after decode")
 
 
+F32_PLAIN_GEOMS = [
+    # (h_qk, h_v, d_k, d_v, seqlens, raw gates): d_k 128 and 256, d_v 32 to 256, ragged tails, an
+    # empty and a one-token sequence
+    (2, 4, 128, 32, [200, 0, 70, 1], False),
+    (1, 2, 256, 64, [300], True),
+    (2, 2, 256, 256, [200, 64], False),
+]
+
+
+@pytest.mark.parametrize("geom", F32_PLAIN_GEOMS, ids=lambda g: f"h{g[0]}x{g[1]}_dk{g[2]}_dv{g[3]}_T{sum(g[4])}")
+@pytest.mark.parametrize("rule", ["gated", "linear"])
+def test_chunked_f32_plain_rules(rule, geom):
+    """The gated and linear rules in the float32 two-pass chunked form, as AUTO plans it with a
+    workspace: the preparation pass forms A = 0, so T = I, W = 0 and U = V, and the state pass
+    takes D = V."""
+    h_qk, h_v, d_k, d_v, lens, raw = geom
+    dt = torch.float32
+    say(f"[chunked-f32-plain] {rule} {geom}")
+    inp, raw_in, g64, b64 = _setup(h_qk, h_v, d_k, d_v, dt, lens, seed=570)
+    gates = _gate_kwargs(raw, raw_in, g64, b64, dt)
+    if not raw:
+        g64, b64 = gates["g"].double().numpy(), gates["beta"].double().numpy()
+    n, T = len(lens), inp.total_tokens
+    ws = gdn.prefill_workspace_size(h_qk, h_v, d_k, d_v, dt, n, T, rule=rule)
+    plan = gdn.prefill_query_plan(h_qk, h_v, d_k, d_v, dt, n, T, raw_gates=raw, workspace_bytes=ws, rule=rule)
+    assert plan["form"] == "chunked_f32", plan
+    out, fin, _ = _gpu_prefill(inp, gates, raw=raw, rule=rule, per_key=False, shared=False, algorithm="auto",
+                               two_pass=True)
+    ro, rf = _oracle(inp, g64, b64, rule=rule, per_key=False, shared=False)
+    check(out, torch.from_numpy(ro), TOL[dt], "out")
+    check(fin, torch.from_numpy(rf), TOL[dt], "final state")
+
+
 def test_chunked_plain_rule_needs_workspace():
     """Without a workspace the gated and linear rules have no chunked form: AUTO scans, CHUNKED is refused."""
     plan = gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 2, 4096, rule="gated")
