@@ -228,8 +228,7 @@ gdn_status plan_prefill(const gdn_problem& p, int32_t num_seqs, int32_t total_to
   const bool can_chunk = gdn::chunked_supported(io_bf16, p.d_k, p.d_v, sp.gates, window) || wide_ws || split_ws;
   if (p.algorithm == GDN_ALGO_CHUNKED && !can_chunk)
     return fail(GDN_ERR_UNSUPPORTED,
-                "%s: the chunked algorithm needs bfloat16 I/O with d_k 64 or 128 and d_v a multiple of 8 (the "
-                "gated and linear rules: d_v up to 256 and a workspace of gdn_prefill_workspace_size bytes), or "
+                "%s: the chunked algorithm needs bfloat16 I/O with d_k 64 or 128 and d_v a multiple of 8, or "
                 "float32 I/O with d_k 128 or 256, d_v a multiple of 16 up to 256 and a workspace; and a per-head "
                 "decay and no state history (got %s, d_k=%d, d_v=%d, rule=%d, "
                 "decay_per_key=%d, state_window=%d%s)",

@@ -19,6 +19,7 @@
 // i.e. (I + A) D = diag(beta) V - diag(beta gam) K S_0 with the strictly lower
 // A_ts = beta_t exp(G_t - G_s) k_t.k_s.  With T = (I + A)^-1:
 //     D   = U - W S_0,        U = T diag(beta) V,   W = T diag(beta gam) K
+// (the gated and linear rules have no delta correction: A = 0, U = V, W = 0)
 //     O   = scale (diag(gam) Q S_0 + M D),   M_ts = exp(G_t - G_s) q_t.k_s  (s <= t)
 //     S_C = gam_C S_0 + K^T diag(exp(G_C - G_s)) D.
 // Every exponent is a sum of log-decays over a forward range, so with g <= 0
@@ -162,6 +163,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
 
   const IO* qg = static_cast<const IO*>(p.q);
   const IO* kg = static_cast<const IO*>(p.k);
+  // Rules without the delta correction (gated, linear) write v as it is:
+  // A = 0, so T = I, with weight 1 in T'' = T diag(beta), T' = 0, and D = V.
+  const bool delta_rule = p.gates.deltas != 0;
   const IO* vg = static_cast<const IO*>(p.v);
   IO* og = static_cast<IO*>(p.out);
   const size_t qk_stride = static_cast<size_t>(p.h_qk) * DK;
@@ -226,10 +230,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       const int tl = c0 + min(lane, Ln - 1);
       const size_t gi = static_cast<size_t>(tl) * p.h_v + h;
       const size_t bi = p.gates.beta_shared ? static_cast<size_t>(tl) : gi;
-      const IO* bsrc = static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta);
+      // a gate the rule does not use reads K's first element instead (its
+      // pointer may be null), so the loads stay unconditional
+      const IO* bsrc = delta_rule ? static_cast<const IO*>(RAW ? p.gates.b : p.gates.beta) : kg;
+      const size_t bix = delta_rule ? bi : 0;
       const IO* gsrc = p.gates.decays ? static_cast<const IO*>(RAW ? p.gates.a : p.gates.g) : bsrc;
-      rg = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : bi];
-      rb_ = reinterpret_cast<const uint16_t*>(bsrc)[bi];
+      rg = reinterpret_cast<const uint16_t*>(gsrc)[p.gates.decays ? gi : bix];
+      rb_ = reinterpret_cast<const uint16_t*>(bsrc)[bix];
     }
   };
   if (t_begin < t_end) fetch(t_begin);
@@ -270,10 +277,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       if (lane < L) {
         if constexpr (RAW) {
           g = p.gates.decays ? gate_log_decay(widen_bits16<IO>(rg), A_log, dt_bias) : 0.0f;
-          b = gate_sigmoid(widen_bits16<IO>(rb_));
+          b = delta_rule ? gate_sigmoid(widen_bits16<IO>(rb_)) : 1.0f;
         } else {
           g = p.gates.decays ? widen_bits16<IO>(rg) : 0.0f;
-          b = widen_bits16<IO>(rb_);
+          b = delta_rule ? widen_bits16<IO>(rb_) : 1.0f;
         }
         g = fmaxf(g, kMinLogDecay);
       }
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * tb + acc_row(lane, i);
         const float dec = (s_ <= t) ? fast_exp2(static_cast<float>(Gd[t] - Gs)) : 0.0f;
-        Af[t * kSA + s_] = (s_ < t) ? Bet[t] * dec * pacc[i] : 0.0f;
+        Af[t * kSA + s_] = (s_ < t && delta_rule) ? Bet[t] * dec * pacc[i] : 0.0f;
         Ms[t * kSC + s_] = to_bf16(dec * racc[i]);
       }
     }
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ScanParams p) {
       const int t = e >> 6, s2 = e & 63;
       const float tv = (s2 <= t) ? Tf[t * kST + s2] : 0.0f;
       const float bs = Bet[s2];
-      Tp[t * kSC + s2] = to_bf16(tv * bs * Gam[s2]);
+      Tp[t * kSC + s2] = to_bf16(delta_rule ? tv * bs * Gam[s2] : 0.0f);
       Tpp[t * kSC + s2] = to_bf16(tv * bs);
     }
     __syncthreads();
@@ -486,7 +493,7 @@ hipError_t launch_nc(const ScanParams& p, hipStream_t stream) {
 }  // namespace
 
 bool chunked_supported(int io_bf16, int d_k, int d_v, const GateArgs& gates, int window) {
-  return io_bf16 && (d_k == 64 || d_k == 128) && d_v % 8 == 0 && gates.deltas && !gates.per_key && window == 0;
+  return io_bf16 && (d_k == 64 || d_k == 128) && d_v % 8 == 0 && !gates.per_key && window == 0;
 }
 
 int chunked_columns_per_block(int d_k, int d_v) {

@@ -92,10 +92,10 @@ typedef enum gdn_algorithm {
    * multiple of 16 up to 256, and a workspace (the two-pass form only).
    * Both need a per-head decay (or none), no state history and a true decay
    * (g <= 0, as the raw-gate prologue always gives).  The gated-delta and
-   * delta rules run in every form; the gated and linear rules (no delta
-   * correction, so no triangular solve) in the two-pass forms only (bfloat16
-   * with d_v up to 256, or float32), with a workspace.  Otherwise
-   * GDN_ERR_UNSUPPORTED when requested explicitly. */
+   * delta rules run in every form, and so do the gated and linear rules (no
+   * delta correction: T = I, D = V), with d_v up to 256 in the bfloat16
+   * two-pass form.  Otherwise GDN_ERR_UNSUPPORTED when requested
+   * explicitly. */
   GDN_ALGO_CHUNKED = 2
 } gdn_algorithm;
 

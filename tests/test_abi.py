@@ -92,7 +92,7 @@ INVALID, UNSUPPORTED = gdn.GDN_ERR_INVALID_ARGUMENT, gdn.GDN_ERR_UNSUPPORTED
     ("negative window", dict(state_window=-1), {}, INVALID, "negative"),
     ("chunked per-key", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_BF16, d_k=64, d_v=64,
                              decay_per_key=1), {}, UNSUPPORTED, "chunked algorithm needs"),
-    ("chunked gated rule", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_BF16, d_k=64, d_v=64, rule=2),
+    ("chunked gated rule", dict(algorithm=gdn.GDN_ALGO_CHUNKED, io_dtype=gdn.GDN_BF16, d_k=64, d_v=12, rule=2),
      {}, UNSUPPORTED, "chunked algorithm needs"),
     ("negative seqs", {}, dict(n=-1), INVALID, "negative"),
     ("negative tokens", {}, dict(T=-1), INVALID, "negative"),

@@ -274,13 +274,26 @@ def test_chunked_f32_plain_rules(rule, geom):
     check(fin, torch.from_numpy(rf), TOL[dt], "final state")
 
 
-def test_chunked_plain_rule_needs_workspace():
-    """Without a workspace the gated and linear rules have no chunked form: AUTO scans, CHUNKED is refused."""
-    plan = gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 2, 4096, rule="gated")
-    assert plan["form"] == "serial", plan
-    with pytest.raises(gdn.GdnError) as e:
-        gdn.prefill_query_plan(16, 32, 128, 128, torch.bfloat16, 2, 4096, rule="linear", algorithm="chunked")
-    assert e.value.status == gdn.GDN_ERR_UNSUPPORTED and "workspace" in str(e.value)
+@pytest.mark.parametrize("geom", [(16, 32, 128, 128, [300, 0, 70, 1], True), (2, 6, 64, 40, [200, 65], False)],
+                         ids=["h16x32_dk128_dv128", "h2x6_dk64_dv40"])
+@pytest.mark.parametrize("rule", ["gated", "linear"])
+def test_chunked_one_pass_plain_rules(rule, geom):
+    """Without a workspace the gated and linear rules take the one-pass chunked form, as AUTO
+    plans it: A = 0, so T = I, T' = 0 and T'' = I, and D = V."""
+    h_qk, h_v, d_k, d_v, lens, raw = geom
+    dt = torch.bfloat16
+    say(f"[chunked-one-pass-plain] {rule} {geom}")
+    inp, raw_in, g64, b64 = _setup(h_qk, h_v, d_k, d_v, dt, lens, seed=580)
+    gates = _gate_kwargs(raw, raw_in, g64, b64, dt)
+    if not raw:
+        g64, b64 = gates["g"].double().numpy(), gates["beta"].double().numpy()
+    n, T = len(lens), inp.total_tokens
+    plan = gdn.prefill_query_plan(h_qk, h_v, d_k, d_v, dt, n, T, raw_gates=raw, rule=rule)
+    assert plan["form"] == "chunked_one_pass", plan
+    out, fin, _ = _gpu_prefill(inp, gates, raw=raw, rule=rule, per_key=False, shared=False, algorithm="auto")
+    ro, rf = _oracle(inp, g64, b64, rule=rule, per_key=False, shared=False)
+    check(out, torch.from_numpy(ro), TOL[dt], "out")
+    check(fin, torch.from_numpy(rf), TOL[dt], "final state")
 
 
 @pytest.mark.parametrize("rule", RULES)
